@@ -1,0 +1,408 @@
+"""CPU oracle of the LLaTTE target-aware MLA sequence-module forward.
+
+TEST INFRASTRUCTURE ONLY. This module is the slow, plain reference that the
+GPU library is checked against. Only the tests, the package smoke check and
+the CPU-baseline leg of the benchmark may import it; the product path never
+does. It shares no code with the HIP library.
+
+Sources (cited by page title and section):
+  [LLaTTE]  "LLaTTE: Scaling Laws for Multi-Stage Sequence Modeling in
+            Large-Scale Ads Recommendation" (annotated translation):
+            section 1.3.2 (five-step sequence module), Appendix A.2 (query
+            tokens and fusion, the layer equations, the pyramidal schedule
+            and its cost, the three attention modes, sequence summaries),
+            Appendix A.3 (MLA, non-absorbed and absorbed forms).
+  [Repro]   "LLaTTE: Multi-stage sequence scaling" (reproduction note),
+            section "core formula" (target-aware query q = W_Q [x; c]).
+
+Readings taken where the pages are silent or disagree (each is also listed
+with its reason in the design notes):
+  * pre-norm layer by default (the A.2 layer equation is written post-norm;
+    both placements are implemented, 'post' follows A.2 literally);
+  * RMSNorm on the latent C (A.3) on by default, switchable off;
+  * full-rank per-layer query projection W_uq (no low-rank query path);
+  * softmax scale 1/sqrt(head_dim) in both MLA forms (A.3's absorbed form
+    writes sqrt(d_c); the two forms are only equal with one common scale);
+  * candidate query tokens attend every history key and nothing else;
+    history rows attend causally and never see candidates;
+  * the pyramid keeps history rows only; candidates are always kept; layer
+    l's keys are all rows kept by layer l-1, its queries the last n_l rows
+    (output extraction; equal to computing all rows then slicing, A.2);
+  * GELU with the exact erf, FFN width 4d, no biases; RMSNorm eps inside the
+    square root; no final norm after the stack;
+  * readout: one more layer in cross-attention mode whose queries are the
+    learned seeds, flattened seed-major and multiplied by W_p (the A.2
+    summary with a plain linear map in place of the low-rank MLP).
+
+Numbers are fp64 by default; ``dtype=np.float32`` gives the same code in
+single precision (used only as the timed CPU baseline).
+"""
+import math
+
+import numpy as np
+from scipy.special import erf as _erf
+
+__all__ = [
+    "rmsnorm", "gelu", "softmax_masked", "pyramid_list", "pyramid_counts",
+    "compact", "history_query_mask", "mla_layer", "fuse_queries", "forward",
+    "token_embed", "latent_attention", "unmasked_pairs", "flop_count",
+]
+
+
+# ---------------------------------------------------------------- primitives
+
+def rmsnorm(x, g, eps=1e-6):
+    """RMS normalisation over the last axis, times the gain g.
+
+    [LLaTTE] A.2 layer equations use RMSNorm (Root Mean Square Layer
+    Normalization): x / sqrt(mean(x^2) + eps) * g.
+    """
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * g
+
+
+def gelu(x):
+    """Exact GELU, x * Phi(x) with Phi the standard normal CDF (erf form).
+
+    The FFN of the [LLaTTE] A.2 layer equation has no stated activation; the
+    exact-erf GELU is the reading used throughout.
+    """
+    return 0.5 * x * (1.0 + _erf(x / math.sqrt(2.0)))
+
+
+def softmax_masked(s, allowed):
+    """Row softmax over the last axis of s, with disallowed entries removed.
+
+    [LLaTTE] A.3: softmax(Q K^T / sqrt(d_k)); masked entries get probability 0.
+    The row maximum is subtracted before exponentiation. Every row must have
+    at least one allowed entry.
+    """
+    z = np.where(allowed, s, -np.inf)
+    m = np.max(z, axis=-1, keepdims=True)
+    e = np.where(allowed, np.exp(z - m), 0.0)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+# ---------------------------------------------------------------- pyramid
+
+def pyramid_list(rule, n_layers):
+    """Per-layer keep list of a 'fixed' or 'geometric' rule.
+
+    [LLaTTE] A.2 pyramidal schedule: T_{l+1} <= T_l. A geometric rule runs
+    from rule.start to rule.end over the layers, rounded half up.
+    """
+    if rule.kind == "fixed":
+        assert len(rule.values) == n_layers
+        return [int(v) for v in rule.values]
+    if rule.kind == "geometric":
+        if n_layers == 1:
+            return [int(rule.start)]
+        out = []
+        for l in range(n_layers):
+            v = rule.start * (rule.end / rule.start) ** (l / (n_layers - 1))
+            out.append(int(math.floor(v + 0.5)))
+        return out
+    raise ValueError(rule.kind)
+
+
+def pyramid_counts(rule, lengths, n_layers):
+    """keep[l, u]: history rows of user u kept as queries/outputs at layer l+1.
+
+    [LLaTTE] A.2 pyramidal schedule: the next layer works on the most recent
+    T_{l+1} <= T_l rows. Counts never exceed the previous layer's count.
+    'halving': keep = max(min(floor, L_u), L_u >> l) for the 0-based layer l.
+    """
+    lengths = np.asarray(lengths, dtype=np.int64)
+    keep = np.zeros((n_layers, lengths.size), dtype=np.int64)
+    prev = lengths.copy()
+    if rule.kind == "halving":
+        for l in range(n_layers):
+            keep[l] = np.maximum(np.minimum(rule.floor, lengths), lengths >> l)
+            keep[l] = np.minimum(keep[l], prev)
+            prev = keep[l]
+        return keep
+    lst = pyramid_list(rule, n_layers)
+    for l in range(n_layers):
+        keep[l] = np.minimum(lst[l], prev)
+        prev = keep[l]
+    return keep
+
+
+def compact(values, offsets, keep):
+    """Keep the last keep[u] rows of each user's segment, in order.
+
+    [LLaTTE] A.2: R^{(l+1)} = X^{(l)}[:, -T_{l+1}:, :]. Returns the kept rows,
+    the exclusive scan of keep as new offsets, and the global source row of
+    every kept row.
+    """
+    offsets = np.asarray(offsets, dtype=np.int64)
+    keep = np.asarray(keep, dtype=np.int64)
+    B = keep.size
+    lens = offsets[1:] - offsets[:-1]
+    if np.any(keep < 0) or np.any(keep > lens):
+        raise ValueError("keep must lie in [0, L_u]")
+    src = []
+    for u in range(B):
+        src.extend(range(offsets[u + 1] - keep[u], offsets[u + 1]))
+    src = np.asarray(src, dtype=np.int64)
+    new_off = np.zeros(B + 1, dtype=np.int64)
+    new_off[1:] = np.cumsum(keep)
+    return values[src], new_off, src
+
+
+def history_query_mask(K, n, n_c):
+    """Allowed (query, key) pairs of one user at one layer, shape [n+n_c, K].
+
+    Query rows 0..n-1 are the last n history rows (key positions K-n .. K-1)
+    and attend causally ([LLaTTE] A.2 causal transformer). Rows n..n+n_c-1
+    are candidate tokens and attend every history key (reading of the
+    target-aware query of [Repro], core formula).
+    """
+    j = np.arange(K)[None, :]
+    pos = (K - n + np.arange(n))[:, None]
+    hist = j <= pos
+    cand = np.ones((n_c, K), dtype=bool)
+    return np.concatenate([hist, cand], axis=0)
+
+
+# ---------------------------------------------------------------- one layer
+
+def _split_heads(x, h):
+    M = x.shape[0]
+    return x.reshape(M, h, -1)
+
+
+def mla_layer(Rh, Rc, n, W, cfg, absorbed=False, return_probs=False):
+    """One transformer layer with MLA on one user.
+
+    Rh: the K history rows entering the layer (oldest first); Rc: the n_c
+    candidate/seed rows; n: history rows kept as queries (0 <= n <= K).
+    Returns (Rh_out [n, d], Rc_out [n_c, d]) and, on request, the attention
+    probabilities [h, n+n_c, K].
+
+    [LLaTTE] A.3 non-absorbed MLA: C = RMSNorm(H W_down^KV) (the latent),
+    K, V = split(C W_up^KV), attention softmax(Q K^T / sqrt(d_k)) V W_out.
+    With ``absorbed`` the A.3 rewritten form is used instead: per head the
+    query is moved into latent space (q W_uk^T), scores are taken against C
+    itself and the output is mapped back through W_uv.
+    [LLaTTE] A.2 layer equation (post-norm) or its pre-norm reading.
+    """
+    d, h, dk = cfg.d, cfg.h, cfg.dk
+    eps = cfg.eps
+    K = Rh.shape[0]
+    n_c = Rc.shape[0]
+    if K < 1 or not (0 <= n <= K):
+        raise ValueError("need K >= 1 and 0 <= n <= K")
+    pre = cfg.norm_mode == "pre"
+    Hh = rmsnorm(Rh, W["g1"], eps) if pre else Rh
+    Hc = rmsnorm(Rc, W["g1"], eps) if pre else Rc
+
+    C = Hh @ W["W_dkv"]
+    if cfg.latent_norm:
+        C = rmsnorm(C, W["g_c"], eps)
+
+    Hq = np.concatenate([Hh[K - n:], Hc], axis=0)
+    Rq = np.concatenate([Rh[K - n:], Rc], axis=0)
+    M = Hq.shape[0]
+    q = _split_heads(Hq @ W["W_uq"], h)              # [M, h, dk]
+    allowed = history_query_mask(K, n, n_c)          # [M, K]
+    scale = 1.0 / math.sqrt(dk)
+
+    Wuk = W["W_uk"].reshape(cfg.r, h, dk)
+    Wuv = W["W_uv"].reshape(cfg.r, h, dk)
+    o = np.empty((M, h, dk), dtype=Rh.dtype)
+    probs = np.empty((h, M, K), dtype=Rh.dtype) if return_probs else None
+    for hh in range(h):
+        if absorbed:
+            q_lat = q[:, hh, :] @ Wuk[:, hh, :].T    # [M, r]
+            s = (q_lat @ C.T) * scale
+            p = softmax_masked(s, allowed)
+            o[:, hh, :] = (p @ C) @ Wuv[:, hh, :]
+        else:
+            Kh = C @ Wuk[:, hh, :]                   # [K, dk]
+            Vh = C @ Wuv[:, hh, :]
+            s = (q[:, hh, :] @ Kh.T) * scale
+            p = softmax_masked(s, allowed)
+            o[:, hh, :] = p @ Vh
+        if return_probs:
+            probs[hh] = p
+    A = o.reshape(M, h * dk) @ W["W_o"]
+
+    if pre:
+        R1 = Rq + A
+        R2 = R1 + gelu(rmsnorm(R1, W["g2"], eps) @ W["W1"]) @ W["W2"]
+    else:
+        R1 = rmsnorm(Rq + A, W["g1"], eps)
+        R2 = rmsnorm(R1 + gelu(R1 @ W["W1"]) @ W["W2"], W["g2"], eps)
+    out = (R2[:n], R2[n:])
+    return (out, probs) if return_probs else out
+
+
+# ---------------------------------------------------------------- the stack
+
+def fuse_queries(cand, ctx, W_q):
+    """Candidate query tokens Q0 = [x_j ; c_u] W_q for one user.
+
+    [Repro] core formula q = W_Q [x; c]; [LLaTTE] A.2 query tokens appended
+    after the history (Concat(X_seq, Q)). cand: [n_q, d]; ctx: [d_c] or None.
+    """
+    if ctx is None or ctx.size == 0:
+        xc = cand
+    else:
+        xc = np.concatenate([cand, np.broadcast_to(ctx, (cand.shape[0], ctx.size))],
+                            axis=1)
+    return xc @ W_q
+
+
+def forward(cfg, W, hist, offsets, cand=None, ctx=None, users=None,
+            absorbed=False, dtype=np.float64):
+    """The sequence-module forward for each user in ``users`` (all if None).
+
+    [LLaTTE] section 1.3.2: fusion of the query tokens, N layers of MLA with
+    the pyramidal schedule, then the readout. Returns a dict with per-user
+    lists 'hist' ([n_N(u), d]), 'cand' ([n_q, d]) and, with a readout,
+    'emb' ([d_out]).
+    """
+    offsets = np.asarray(offsets, dtype=np.int64)
+    lengths = offsets[1:] - offsets[:-1]
+    B = lengths.size
+    if np.any(lengths < 1):
+        raise ValueError("every user needs at least one history row")
+    keep = pyramid_counts(cfg.pyramid, lengths, cfg.N)
+    users = range(B) if users is None else users
+    cast = lambda a: None if a is None else np.asarray(a, dtype=dtype)
+    Wc = {k: (v if k == "layers" or k == "readout" else cast(v))
+          for k, v in W.items()}
+    layers = [{k: cast(v) for k, v in lw.items()} for lw in W["layers"]]
+    readout = ({k: cast(v) for k, v in W["readout"].items()}
+               if cfg.n_seeds > 0 else None)
+    res = {"users": list(users), "hist": [], "cand": [], "emb": []}
+    for u in users:
+        Rh = cast(hist[offsets[u]:offsets[u + 1]])
+        if cfg.n_q > 0:
+            cu = cast(cand[u * cfg.n_q:(u + 1) * cfg.n_q])
+            xu = cast(ctx[u]) if (ctx is not None and cfg.d_c > 0) else None
+            Rc = fuse_queries(cu, xu, Wc["W_q"])
+        else:
+            Rc = np.zeros((0, cfg.d), dtype=dtype)
+        for l in range(cfg.N):
+            Rh, Rc = mla_layer(Rh, Rc, int(keep[l, u]), layers[l], cfg, absorbed)
+        res["hist"].append(Rh)
+        res["cand"].append(Rc)
+        if readout is not None:
+            _, S = mla_layer(Rh, Wc["seeds"], 0, readout, cfg, absorbed)
+            res["emb"].append(S.reshape(-1) @ Wc["W_p"])
+    return res
+
+
+def token_embed(table_rows, sem, W_s):
+    """Token = hashed-ID table row + semantic vector times W_s.
+
+    [LLaTTE] section 1.3 features: sparse-ID embeddings plus dense content
+    embeddings per event (section 1.5.3 content-aware scaling adds the
+    semantic representation to the token).
+    """
+    return table_rows + sem @ W_s
+
+
+# ------------------------------------------------- the exported latent core
+
+def latent_attention(q_lat, c_lat, kv_offsets, hq_offsets, n_cand, scale):
+    """Attention in latent space, the core of the absorbed MLA form.
+
+    [LLaTTE] A.3 absorbed form: queries already multiplied into latent space
+    (q_lat [Mtot, h, r]) score against the shared latent C ([Ktot, r]) and the
+    output is sum_j softmax_j(scale * q_lat . C_j) * C_j, per head.
+    History query rows of user u are hq_offsets[u] .. hq_offsets[u+1]-1; row t
+    sits at key position K_u - n_u + t and sees keys 0..that position.
+    Candidate rows of user u follow all history rows, at
+    hq_offsets[B] + u*n_cand + j, and see all K_u keys.
+    Returns (out [Mtot, h, r], lse [Mtot, h]) with lse the natural-log
+    log-sum-exp of the scaled scores.
+    """
+    kv_offsets = np.asarray(kv_offsets, dtype=np.int64)
+    hq_offsets = np.asarray(hq_offsets, dtype=np.int64)
+    B = kv_offsets.size - 1
+    Mtot = int(hq_offsets[-1]) + B * n_cand
+    h, r = q_lat.shape[1], q_lat.shape[2]
+    out = np.zeros((Mtot, h, r), dtype=q_lat.dtype)
+    lse = np.zeros((Mtot, h), dtype=q_lat.dtype)
+    base_c = int(hq_offsets[-1])
+    for u in range(B):
+        C = c_lat[kv_offsets[u]:kv_offsets[u + 1]]
+        K = C.shape[0]
+        n = int(hq_offsets[u + 1] - hq_offsets[u])
+        rows = list(range(hq_offsets[u], hq_offsets[u + 1])) + \
+            list(range(base_c + u * n_cand, base_c + (u + 1) * n_cand))
+        allowed = history_query_mask(K, n, n_cand)
+        for hh in range(h):
+            s = (q_lat[rows, hh, :] @ C.T) * scale
+            z = np.where(allowed, s, -np.inf)
+            m = np.max(z, axis=1, keepdims=True)
+            e = np.where(allowed, np.exp(z - m), 0.0)
+            tot = e.sum(axis=1, keepdims=True)
+            out[rows, hh, :] = (e / tot) @ C
+            lse[rows, hh] = (m + np.log(tot))[:, 0]
+    return out, lse
+
+
+# ---------------------------------------------------------------- counting
+
+def unmasked_pairs(cfg, lengths):
+    """Allowed (query, key) pairs per layer, counted from the explicit masks."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    keep = pyramid_counts(cfg.pyramid, lengths, cfg.N)
+    per_layer = np.zeros(cfg.N + (1 if cfg.n_seeds else 0), dtype=np.int64)
+    for u, Lu in enumerate(lengths):
+        K = int(Lu)
+        for l in range(cfg.N):
+            n = int(keep[l, u])
+            per_layer[l] += int(history_query_mask(K, n, cfg.n_q).sum())
+            K = n
+        if cfg.n_seeds:
+            per_layer[cfg.N] += int(history_query_mask(K, 0, cfg.n_seeds).sum())
+    return per_layer
+
+
+def flop_count(cfg, lengths, absorbed=True):
+    """Algorithmic FLOPs of one batch: 2mnk per matrix product, plus per
+    allowed (query, key) pair 4*r*h (absorbed) or 4*d_k*h (non-absorbed).
+
+    Matrix products per layer, with K history rows in and M = n + n_q query
+    rows: W_dkv (K x d x r), W_uq (M x d x h*dk), then absorbed W_uk and W_uv
+    on the queries (M x dk x r per head, each) or non-absorbed W_uk and W_uv on
+    the keys (K x r x h*dk, each), W_o (M x h*dk x d), W1 and W2 (M x d x 4d).
+    Plus the fusion (B*n_q x (d+d_c) x d), the readout projection
+    (B x n_s*d x d_out) and the W_s token build (rows x d_sem x d).
+    """
+    lengths = np.asarray(lengths, dtype=np.int64)
+    keep = pyramid_counts(cfg.pyramid, lengths, cfg.N)
+    d, h, dk, r = cfg.d, cfg.h, cfg.dk, cfg.r
+    pairs = unmasked_pairs(cfg, lengths)
+    total = 0
+    Ks = lengths.copy()
+    nl = cfg.N + (1 if cfg.n_seeds else 0)
+    for l in range(nl):
+        if l < cfg.N:
+            n = keep[l]
+            nq = cfg.n_q
+        else:
+            n = np.zeros_like(Ks)
+            nq = cfg.n_seeds
+        Kt = int(Ks.sum())
+        Mt = int(n.sum()) + nq * cfg.B
+        total += 2 * Kt * d * r + 2 * Mt * d * h * dk
+        if absorbed:
+            total += 2 * (2 * Mt * h * dk * r) + 4 * r * h * int(pairs[l])
+        else:
+            total += 2 * (2 * Kt * r * h * dk) + 4 * dk * h * int(pairs[l])
+        total += 2 * Mt * h * dk * d + 2 * (2 * Mt * d * cfg.d_ff)
+        Ks = n
+    if cfg.n_q > 0:
+        total += 2 * cfg.B * cfg.n_q * (d + cfg.d_c) * d
+    if cfg.n_seeds:
+        total += 2 * cfg.B * cfg.n_seeds * d * cfg.d_out
+    if cfg.semantic is not None:
+        rows = int(lengths.sum()) + cfg.B * cfg.n_q
+        total += 2 * rows * cfg.semantic.d_sem * d
+    return total

@@ -1,0 +1,302 @@
+/*
+ * llatte.h -- C ABI of the MI355X (gfx950) library for the forward pass of
+ * LLaTTE's target-aware sequence transformer with Multi-head Latent Attention.
+ *
+ * Sources, cited by page title and section:
+ *   [LLaTTE] "LLaTTE: Scaling Laws for Multi-Stage Sequence Modeling in
+ *            Large-Scale Ads Recommendation" (annotated translation):
+ *            section 1.3.2 (the five steps of the sequence module),
+ *            Appendix A.2 (query tokens and fusion; layer equations; the
+ *            pyramidal schedule, its cost and the three attention modes;
+ *            sequence summaries), Appendix A.3 (MLA and its absorbed form).
+ *   [Repro]  "LLaTTE: Multi-stage sequence scaling" (reproduction note),
+ *            core formula: target-aware query q = W_Q [x; c].
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless marked "host". Buffers are
+ *     caller-owned, contiguous and row-major; matrices are [in, out] so that
+ *     y = x W. Activation/weight matrices use the descriptor's dtype (F32 or
+ *     BF16); gains, residual-stream inputs and all outputs are float32.
+ *   - Alignment: every device pointer must be 16-byte aligned.
+ *   - The library never allocates, frees or retains a pointer after it
+ *     returns. Scratch memory is passed in as a caller-owned workspace whose
+ *     size the matching *_workspace_size function returns.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and the call returns without synchronising. Inputs must stay
+ *     alive until the stream work completes.
+ *   - Errors: every function returns LLATTE_OK (0) or a negative status.
+ *     Host-side validation happens before anything is enqueued; on a
+ *     validation error nothing is launched. llatte_last_error() gives a
+ *     message for the last failing call on the calling thread. Malformed
+ *     device-side offsets (non-monotone, or inconsistent with the host
+ *     totals) are undefined behaviour.
+ *   - Re-entrant; no global mutable state besides the per-thread message.
+ */
+#ifndef LLATTE_H
+#define LLATTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t llatte_status;
+#define LLATTE_OK 0
+#define LLATTE_ERR_INVALID_ARG (-1) /* bad pointer, size or shape          */
+#define LLATTE_ERR_UNSUPPORTED (-2) /* valid but not implemented (e.g. r)  */
+#define LLATTE_ERR_WORKSPACE (-3)   /* workspace too small                 */
+#define LLATTE_ERR_HIP (-4)         /* a HIP runtime call or launch failed */
+
+#define LLATTE_F32 0
+#define LLATTE_BF16 1
+
+#define LLATTE_NORM_PRE 0  /* pre-norm layer (default)                     */
+#define LLATTE_NORM_POST 1 /* post-norm, as written in [LLaTTE] A.2        */
+
+#define LLATTE_PYR_FIXED 0     /* values[l] per layer, capped by layer l-1  */
+#define LLATTE_PYR_HALVING 1   /* max(min(floor, L_u), L_u >> l)            */
+#define LLATTE_PYR_GEOMETRIC 2 /* start -> end geometric, rounded half up   */
+
+#define LLATTE_MAX_LAYERS 64
+
+/* Pyramidal schedule ([LLaTTE] A.2): how many of the most recent history rows
+ * stay as queries/outputs at each layer. The count for user u at layer l
+ * (0-based) is capped by the count at layer l-1 (layer -1 = L_u). A count of
+ * 0 is cross-attention mode (only the query tokens stay), allowed only at
+ * the last layer of the stack. */
+typedef struct {
+  int32_t kind;                       /* LLATTE_PYR_*                        */
+  int32_t floor;                      /* HALVING: the floor (>= 1)           */
+  int32_t start, end;                 /* GEOMETRIC: endpoints (>= 1)         */
+  int32_t values[LLATTE_MAX_LAYERS];  /* FIXED: per-layer counts (>= 0)      */
+} llatte_pyramid_rule;
+
+/* Model shape and options. d_ff must be 4*d. head_dim*n_heads is the query
+ * width. rank is the latent width r of C = H W_dkv ([LLaTTE] A.3). */
+typedef struct {
+  int32_t d;           /* model width                                       */
+  int32_t n_heads;     /* h                                                 */
+  int32_t head_dim;    /* d_k; the softmax scale is 1/sqrt(d_k)             */
+  int32_t rank;        /* r                                                 */
+  int32_t d_ff;        /* FFN hidden width (= 4d)                           */
+  int32_t n_layers;    /* N, 1 .. LLATTE_MAX_LAYERS                         */
+  int32_t n_q;         /* candidate query tokens per user (>= 0)            */
+  int32_t d_ctx;       /* per-user context width d_c (>= 0)                 */
+  int32_t dtype;       /* LLATTE_F32 or LLATTE_BF16                         */
+  int32_t norm_mode;   /* LLATTE_NORM_PRE or LLATTE_NORM_POST               */
+  int32_t latent_norm; /* 1: RMSNorm on the latent C ([LLaTTE] A.3); 0: off */
+  float eps;           /* RMSNorm epsilon, inside the square root           */
+  llatte_pyramid_rule pyramid;
+  int32_t n_seeds;     /* readout seed queries (0 = no readout)             */
+  int32_t d_out;       /* readout embedding width                           */
+  uint32_t flags;      /* reserved, must be 0                               */
+} llatte_model_desc;
+
+/* Weights of one layer (device pointers). g* are float32 gains; the
+ * matrices have the descriptor's dtype:
+ *   W_dkv [d, r], W_uq [d, h*dk], W_uk [r, h*dk], W_uv [r, h*dk],
+ *   W_o [h*dk, d], W1 [d, d_ff], W2 [d_ff, d].
+ * Head j of W_uk / W_uv is the column slice j*dk .. (j+1)*dk-1. */
+typedef struct {
+  const float* g1;
+  const void* W_dkv;
+  const float* g_c;
+  const void* W_uq;
+  const void* W_uk;
+  const void* W_uv;
+  const void* W_o;
+  const float* g2;
+  const void* W1;
+  const void* W2;
+} llatte_layer_weights;
+
+/* All weights. `layers` is a HOST array of n_layers structs.
+ *   W_q   [d + d_ctx, d]  fusion projection of [x_j ; c_u] (needed if n_q>0)
+ *   seeds [n_seeds, d]    float32 learned readout queries   (if n_seeds>0)
+ *   readout               weights of the readout layer       (if n_seeds>0)
+ *   W_p   [n_seeds*d, d_out] readout projection              (if n_seeds>0) */
+typedef struct {
+  const llatte_layer_weights* layers;
+  const void* W_q;
+  const float* seeds;
+  llatte_layer_weights readout;
+  const void* W_p;
+} llatte_weights;
+
+/* ------------------------------------------------------------------------
+ * llatte_mla_forward -- the whole sequence-module forward ([LLaTTE] 1.3.2):
+ * fusion of the query tokens, N layers of MLA with the pyramidal schedule,
+ * then the optional readout.
+ *
+ * Per user u the history is rows hist_offsets[u] .. hist_offsets[u+1]-1 of
+ * hist_values (oldest first, L_u >= 1 rows). The n_q candidate tokens of
+ * user u are rows u*n_q .. of cand_x, each fused with the user's context as
+ * Q0 = [x_j ; c_u] W_q ([Repro] core formula; [LLaTTE] A.2 fusion).
+ * Layer l (0-based) takes K = n_{l-1}(u) history rows as keys/values
+ * (n_{-1} = L_u) and the last n_l(u) of them plus the candidates as queries.
+ * History queries attend causally; candidates attend every history key.
+ * Each layer is (PRE) R1 = R + MLA(RMSNorm(R)); R2 = R1 + FFN(RMSNorm(R1))
+ * or (POST) R1 = RMSNorm(R + MLA(R)); R2 = RMSNorm(R1 + FFN(R1)), with
+ * FFN(x) = GELU(x W1) W2 (exact erf GELU) ([LLaTTE] A.2, A.3).
+ * The readout runs one more layer with n = 0 whose queries are the seeds,
+ * then emb_u = flatten(seed outputs of u, seed-major) W_p ([LLaTTE] A.2
+ * sequence summaries, with a linear map).
+ *
+ *   desc, w            host pointers
+ *   hist_values        [total_rows, d] float32
+ *   hist_offsets       [B+1] int32, hist_offsets[0] = 0, strictly increasing
+ *   B                  users (>= 1)
+ *   total_rows         host copy of hist_offsets[B]
+ *   max_len            host upper bound of every L_u
+ *   cand_x             [B*n_q, d] float32 (NULL iff n_q == 0)
+ *   ctx                [B, d_ctx] float32 (NULL iff d_ctx == 0 or n_q == 0)
+ *   out_cand           [B*n_q, d] float32 (NULL iff n_q == 0)
+ *   out_hist           [sum_u n_{N-1}(u), d] float32, or NULL; rows ordered
+ *                      by user, oldest first; llatte_pyramid_counts_host
+ *                      gives the row count
+ *   out_hist_offsets   [B+1] int32 or NULL: offsets of out_hist
+ *   out_emb            [B, d_out] float32 (NULL iff n_seeds == 0)
+ *   workspace          >= llatte_mla_forward_workspace_size(...) bytes,
+ *                      256-byte aligned
+ * ---------------------------------------------------------------------- */
+llatte_status llatte_mla_forward(
+    const llatte_model_desc* desc, const llatte_weights* w,
+    const float* hist_values, const int32_t* hist_offsets, int32_t B,
+    int32_t total_rows, int32_t max_len, const float* cand_x,
+    const float* ctx, float* out_cand, float* out_hist,
+    int32_t* out_hist_offsets, float* out_emb, void* workspace,
+    size_t workspace_bytes, void* stream);
+
+/* Workspace bytes needed by llatte_mla_forward for these sizes (host only;
+ * returns 0 if the arguments are invalid). */
+size_t llatte_mla_forward_workspace_size(const llatte_model_desc* desc,
+                                         int32_t B, int32_t total_rows,
+                                         int32_t max_len);
+
+/* ------------------------------------------------------------------------
+ * llatte_mla_attention -- the attention core of the absorbed MLA form
+ * ([LLaTTE] A.3, "MQA on the latent"): queries already moved into latent
+ * space score against the shared latent C and average C itself.
+ *
+ *   out[i, j, :] = sum_k softmax_k(scale * q_lat[i, j, :] . C_k) * C_k
+ *   lse[i, j]    = log(sum_k exp(scale * q_lat[i, j, :] . C_k))  (natural log)
+ * over the keys k allowed to query row i (head j).
+ *
+ * Rows of q_lat / out: first the candidate rows, user-major
+ * (user u's candidates are rows u*n_cand .. u*n_cand+n_cand-1), then the
+ * history query rows: user u's are rows B*n_cand + hq_offsets[u] ..
+ * B*n_cand + hq_offsets[u+1]-1. With n_u = hq_offsets[u+1]-hq_offsets[u]
+ * <= K_u = kv_offsets[u+1]-kv_offsets[u], history row t sits at key position
+ * K_u - n_u + t and attends keys 0 .. K_u - n_u + t (causal, [LLaTTE] A.2);
+ * candidate rows attend all K_u keys. Every user needs K_u >= 1.
+ *
+ *   a                  host descriptor
+ *   q_lat              [Mtot, h, r] dtype
+ *   c_lat              [Ktot, r] dtype, user u's keys at kv_offsets[u]..
+ *   kv_offsets         [B+1] int32;  hq_offsets [B+1] int32 (device)
+ *   Mtot               host: B*n_cand + hq_offsets[B]
+ *   Ktot               host: kv_offsets[B]
+ *   out                [Mtot, h, r] dtype (normalised output)
+ *   lse                [Mtot, h] float32 or NULL
+ *   workspace          >= llatte_mla_attention_workspace_size(...) bytes
+ * BF16 requires r in {64, 128, 256}; F32 accepts 1 <= r <= 256.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t n_heads; /* h                                      */
+  int32_t rank;    /* r                                      */
+  int32_t n_cand;  /* candidate rows per user (>= 0)         */
+  int32_t dtype;   /* LLATTE_F32 or LLATTE_BF16              */
+  float scale;     /* softmax scale, e.g. 1/sqrt(head_dim)   */
+} llatte_attn_desc;
+
+llatte_status llatte_mla_attention(
+    const llatte_attn_desc* a, const void* q_lat, const void* c_lat,
+    const int32_t* kv_offsets, const int32_t* hq_offsets, int32_t B,
+    int32_t Mtot, int32_t Ktot, void* out, float* lse, void* workspace,
+    size_t workspace_bytes, void* stream);
+
+size_t llatte_mla_attention_workspace_size(const llatte_attn_desc* a,
+                                           int32_t B, int32_t Mtot,
+                                           int32_t Ktot);
+
+/* ------------------------------------------------------------------------
+ * llatte_pyramid_compact -- keep the last keep[u] rows of every user's
+ * segment, in order ([LLaTTE] A.2: the next layer works on
+ * X[:, -T_{l+1}:, :]).
+ *
+ *   values             [total_rows, row_elems] of dtype dt (F32 or BF16)
+ *   offsets_in         [B+1] int32 (device); total_rows = offsets_in[B] (host)
+ *   keep               [B] int32, 0 <= keep[u] <= L_u
+ *   values_out         [>= sum keep, row_elems]
+ *   offsets_out        [B+1] int32: exclusive scan of keep
+ *   src_index          [sum keep] int32 or NULL: global source row of each
+ *                      kept row, offsets_in[u] + L_u - keep[u] + t
+ * Integer-exact; rows are copied bit for bit.
+ * ---------------------------------------------------------------------- */
+llatte_status llatte_pyramid_compact(const void* values, int32_t row_elems,
+                                     int32_t dt, const int32_t* offsets_in,
+                                     int32_t B, int32_t total_rows,
+                                     const int32_t* keep, void* values_out,
+                                     int32_t* offsets_out, int32_t* src_index,
+                                     void* stream);
+
+/* ------------------------------------------------------------------------
+ * llatte_pyramid_counts -- evaluate a pyramid rule on the device:
+ * keep_out[l*B + u] = n_l(u) for l < n_layers ([LLaTTE] A.2).
+ *   rule (host), offsets_in [B+1] (device), keep_out [n_layers*B] (device)
+ * llatte_pyramid_counts_host is the same on host arrays (lengths [B]).
+ * ---------------------------------------------------------------------- */
+llatte_status llatte_pyramid_counts(const llatte_pyramid_rule* rule,
+                                    int32_t n_layers,
+                                    const int32_t* offsets_in, int32_t B,
+                                    int32_t* keep_out, void* stream);
+
+llatte_status llatte_pyramid_counts_host(const llatte_pyramid_rule* rule,
+                                         int32_t n_layers,
+                                         const int32_t* lengths, int32_t B,
+                                         int32_t* keep_out);
+
+/* ------------------------------------------------------------------------
+ * llatte_token_embed -- event tokens from a hashed-ID table plus a
+ * projected semantic vector ([LLaTTE] section 1.3 features: sparse-ID
+ * embeddings and dense content embeddings per event):
+ *   out[i, :] = table[rows[i], :] + sem[i, :] W_s
+ *
+ *   table [V, d] dtype; rows [n] int32 in [0, V); sem [n, d_sem] dtype;
+ *   W_s [d_sem, d] dtype; out [n, d] float32.
+ *   workspace >= llatte_token_embed_workspace_size(d, d_sem, dt) bytes.
+ * ---------------------------------------------------------------------- */
+llatte_status llatte_token_embed(const void* table, int32_t V,
+                                 const int32_t* rows, const void* sem,
+                                 const void* W_s, int32_t n, int32_t d,
+                                 int32_t d_sem, int32_t dt, float* out,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+size_t llatte_token_embed_workspace_size(int32_t d, int32_t d_sem,
+                                         int32_t dt);
+
+/* ------------------------------------------------------------------------
+ * Diagnostics.
+ *   llatte_last_error   message of the last non-OK status on this thread
+ *   llatte_version      library version (major*10000 + minor*100 + patch)
+ *   llatte_kernel_timing_enable(1) makes later calls on this thread record
+ *   HIP events around every kernel launch; llatte_kernel_timing_read then
+ *   synchronises those events and fills, per kernel name (up to `cap`
+ *   entries), the launch count and summed milliseconds. Returns the number
+ *   of entries. Timing adds one event pair per launch; leave it off for
+ *   throughput runs.
+ * ---------------------------------------------------------------------- */
+const char* llatte_last_error(void);
+int32_t llatte_version(void);
+void llatte_kernel_timing_enable(int32_t on);
+int32_t llatte_kernel_timing_read(char* names, int32_t name_stride,
+                                  int32_t* counts, double* ms, int32_t cap);
+void llatte_kernel_timing_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LLATTE_H */

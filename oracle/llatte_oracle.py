@@ -313,27 +313,27 @@ def latent_attention(q_lat, c_lat, kv_offsets, hq_offsets, n_cand, scale):
     [LLaTTE] A.3 absorbed form: queries already multiplied into latent space
     (q_lat [Mtot, h, r]) score against the shared latent C ([Ktot, r]) and the
     output is sum_j softmax_j(scale * q_lat . C_j) * C_j, per head.
-    History query rows of user u are hq_offsets[u] .. hq_offsets[u+1]-1; row t
-    sits at key position K_u - n_u + t and sees keys 0..that position.
-    Candidate rows of user u follow all history rows, at
-    hq_offsets[B] + u*n_cand + j, and see all K_u keys.
+    Candidate rows come first: user u's are rows u*n_cand + j, and see all
+    K_u keys. History query rows of user u follow at
+    B*n_cand + hq_offsets[u] .. B*n_cand + hq_offsets[u+1]-1; row t sits at
+    key position K_u - n_u + t and sees keys 0..that position.
     Returns (out [Mtot, h, r], lse [Mtot, h]) with lse the natural-log
     log-sum-exp of the scaled scores.
     """
     kv_offsets = np.asarray(kv_offsets, dtype=np.int64)
     hq_offsets = np.asarray(hq_offsets, dtype=np.int64)
     B = kv_offsets.size - 1
-    Mtot = int(hq_offsets[-1]) + B * n_cand
+    nc = B * n_cand
+    Mtot = nc + int(hq_offsets[-1])
     h, r = q_lat.shape[1], q_lat.shape[2]
     out = np.zeros((Mtot, h, r), dtype=q_lat.dtype)
     lse = np.zeros((Mtot, h), dtype=q_lat.dtype)
-    base_c = int(hq_offsets[-1])
     for u in range(B):
         C = c_lat[kv_offsets[u]:kv_offsets[u + 1]]
         K = C.shape[0]
         n = int(hq_offsets[u + 1] - hq_offsets[u])
-        rows = list(range(hq_offsets[u], hq_offsets[u + 1])) + \
-            list(range(base_c + u * n_cand, base_c + (u + 1) * n_cand))
+        rows = list(range(nc + hq_offsets[u], nc + hq_offsets[u + 1])) + \
+            list(range(u * n_cand, (u + 1) * n_cand))
         allowed = history_query_mask(K, n, n_cand)
         for hh in range(h):
             s = (q_lat[rows, hh, :] @ C.T) * scale

@@ -180,8 +180,8 @@ def test_latent_attention_matches_torch_sdpa():
     scale = 0.37
     out, lse = O.latent_attention(q, C, kv_off, hq_off, nc, scale)
     for u in range(B):
-        rows = list(range(hq_off[u], hq_off[u + 1])) + \
-            list(range(hq_off[-1] + u * nc, hq_off[-1] + (u + 1) * nc))
+        rows = list(range(B * nc + hq_off[u], B * nc + hq_off[u + 1])) + \
+            list(range(u * nc, (u + 1) * nc))
         Cu = torch.tensor(C[kv_off[u]:kv_off[u + 1]])
         allowed = torch.tensor(O.history_query_mask(K[u], n[u], nc))
         for hh in range(h):
@@ -217,9 +217,10 @@ def test_identical_keys_long_history_return_that_row():
     q = rng.standard_normal((n + 2, 3, 8)) * 4
     out, lse = O.latent_attention(q, C, [0, 1600], [0, n], 2, 1.0 / 8)
     assert np.max(np.abs(out - row)) < 1e-12
-    # lse = s + log(number of allowed keys) since all scores are equal
+    # lse = s + log(number of allowed keys) since all scores are equal;
+    # rows: the 2 candidates first, then the n history queries
     s = (q @ row) / 8
-    cnt = np.concatenate([1600 - n + np.arange(n) + 1, [1600, 1600]])
+    cnt = np.concatenate([[1600, 1600], 1600 - n + np.arange(n) + 1])
     assert rel(lse, s + np.log(cnt)[:, None]) < 1e-12
 
 

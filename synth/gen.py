@@ -78,10 +78,17 @@ def _zipf_rows(rng, spec, n):
     return rows.astype(np.int32)
 
 
-def generate(cfg, seed=0):
-    """All lengths, weights and inputs of one workload, in the fixed order."""
+def generate(cfg, seed=0, lengths=None):
+    """All lengths, weights and inputs of one workload, in the fixed order.
+
+    ``lengths`` replaces the workload's own per-user lengths (used for edge
+    cases); when given, no lengths are drawn."""
     rng = np.random.default_rng(seed)
-    lengths = _lengths(rng, cfg)
+    if lengths is None:
+        lengths = _lengths(rng, cfg)
+    else:
+        lengths = np.asarray(lengths, dtype=np.int64)
+        assert lengths.size == cfg.B
     offsets = np.zeros(cfg.B + 1, dtype=np.int32)
     offsets[1:] = np.cumsum(lengths)
     W = {"layers": [_layer(rng, cfg) for _ in range(cfg.N)]}

@@ -1,0 +1,849 @@
+// C ABI of the library: argument validation, workspace layout, and the
+// composition of the forward pass from the kernels.
+//
+// Forward pass of one layer (LLaTTE Appendix A.2 layer equation and A.3
+// MLA, absorbed form), rows of the layer's row space ordered as
+// [candidate/seed rows (B*n_q) ; history rows (sum_u K_u, user-major)] and
+// query rows as [candidates ; last n_u history rows of each user]:
+//   H   = RMSNorm(R) (pre) or R (post), as the compute dtype
+//   C   = H_hist W_dkv, then RMSNorm(C) g_c          (latent, [sum K, r])
+//   q   = H[qmap] W_uq                               ([M, h*dk])
+//   ql  = q_j W_uk_j^T per head j                    ([M, h, r], absorbed)
+//   ol  = latent attention(ql, C)                    ([M, h, r])
+//   o   = ol_j W_uv_j per head                       ([M, h*dk])
+//   R1  = R[qmap] + o W_o              (post: then RMSNorm with g1)
+//   R2  = R1 + GELU(RMSNorm(R1) W1) W2 (post: GELU(R1 W1) W2, then RMSNorm g2)
+// The output rows are exactly the next layer's row space, so the pyramidal
+// output extraction costs no copy.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/llatte.h"
+#include "kernels.hpp"
+
+namespace llatte {
+
+// ------------------------------------------------------------------ errors
+static thread_local std::string t_err;
+
+static llatte_status fail(llatte_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  t_err = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                        \
+  do {                                                                       \
+    hipError_t e_ = (expr);                                                  \
+    if (e_ != hipSuccess)                                                    \
+      return fail(LLATTE_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+// ------------------------------------------------------------------ timing
+struct PendingEv {
+  const char* name;
+  hipEvent_t a, b;
+};
+static thread_local bool t_timing = false;
+static thread_local std::vector<PendingEv> t_pending;
+static thread_local std::map<std::string, std::pair<int, double>> t_acc;
+
+void timing_begin(const char* name, hipStream_t s) {
+  if (!t_timing) return;
+  PendingEv p{name, nullptr, nullptr};
+  if (hipEventCreate(&p.a) != hipSuccess || hipEventCreate(&p.b) != hipSuccess) return;
+  hipEventRecord(p.a, s);
+  t_pending.push_back(p);
+}
+void timing_end(hipStream_t s) {
+  if (!t_timing || t_pending.empty()) return;
+  hipEventRecord(t_pending.back().b, s);
+}
+
+static void timing_collect() {
+  for (auto& p : t_pending) {
+    float ms = 0.f;
+    hipEventSynchronize(p.b);
+    if (hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+      auto& e = t_acc[p.name];
+      e.first += 1;
+      e.second += ms;
+    }
+    hipEventDestroy(p.a);
+    hipEventDestroy(p.b);
+  }
+  t_pending.clear();
+}
+
+// ------------------------------------------------------------------ workspace
+// Bump allocator: a dry run (base == nullptr) measures, a real run carves.
+struct Arena {
+  char* base;
+  size_t off = 0;
+  explicit Arena(void* b) : base((char*)b) {}
+  template <typename T> T* take(size_t count) {
+    off = (off + 255) & ~(size_t)255;
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+static PlanBase carve_plan(Arena& ar, int n_plans, int B, int qcap, int icap) {
+  PlanBase pb;
+  pb.B = B;
+  pb.qcap = qcap;
+  pb.icap = icap;
+  pb.kv_len = ar.take<int>((size_t)n_plans * B);
+  pb.keep = ar.take<int>((size_t)n_plans * B);
+  pb.kv_off = ar.take<int>((size_t)n_plans * (B + 1));
+  pb.hq_off = ar.take<int>((size_t)n_plans * (B + 1));
+  pb.counts = ar.take<int>((size_t)n_plans * 4);
+  pb.qmap = ar.take<int>((size_t)n_plans * qcap);
+  pb.qinfo = ar.take<int2>((size_t)n_plans * qcap);
+  pb.items = ar.take<i32x4>((size_t)n_plans * icap);
+  pb.n_items = ar.take<int>((size_t)n_plans);
+  return pb;
+}
+
+// ------------------------------------------------------------------ shapes
+struct Shapes {
+  int B, total, max_len;
+  int d, h, dk, hd, r, dff, N, nq, dc, ns, dout;
+  bool bf16, pre, lnorm;
+  float eps;
+  int NP;                     // plans: N layers (+ readout)
+  RuleDev rule;
+  std::vector<long long> UBn, UBK, UBM, UBrows;
+  int qcap = 0, icap = 1, bq = 0;
+  size_t esz;                 // bytes per dtype element
+};
+
+static long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
+
+static llatte_status expand_rule(const llatte_pyramid_rule* pr, int N,
+                                 RuleDev* out) {
+  memset(out, 0, sizeof *out);
+  out->n_layers = N;
+  if (pr->kind == LLATTE_PYR_HALVING) {
+    if (pr->floor < 1) return fail(LLATTE_ERR_INVALID_ARG, "halving floor must be >= 1");
+    out->kind = 1;
+    out->floor = pr->floor;
+    return LLATTE_OK;
+  }
+  out->kind = 0;
+  if (pr->kind == LLATTE_PYR_FIXED) {
+    for (int l = 0; l < N; ++l) {
+      if (pr->values[l] < 0) return fail(LLATTE_ERR_INVALID_ARG, "pyramid count < 0 at layer %d", l);
+      if (pr->values[l] == 0 && l != N - 1)
+        return fail(LLATTE_ERR_INVALID_ARG, "a pyramid count of 0 is allowed only at the last layer");
+      out->values[l] = pr->values[l];
+    }
+    return LLATTE_OK;
+  }
+  if (pr->kind == LLATTE_PYR_GEOMETRIC) {
+    if (pr->start < 1 || pr->end < 1)
+      return fail(LLATTE_ERR_INVALID_ARG, "geometric endpoints must be >= 1");
+    for (int l = 0; l < N; ++l) {
+      double v = N == 1 ? (double)pr->start
+                        : (double)pr->start *
+                              pow((double)pr->end / (double)pr->start, (double)l / (N - 1));
+      out->values[l] = (int)floor(v + 0.5);
+    }
+    return LLATTE_OK;
+  }
+  return fail(LLATTE_ERR_INVALID_ARG, "unknown pyramid kind %d", pr->kind);
+}
+
+static llatte_status make_shapes(const llatte_model_desc* dsc, int B, int total,
+                                 int max_len, Shapes* S) {
+  if (!dsc) return fail(LLATTE_ERR_INVALID_ARG, "desc is NULL");
+  if (dsc->flags != 0) return fail(LLATTE_ERR_INVALID_ARG, "flags must be 0");
+  if (B < 1 || total < B || max_len < 1 || (long long)max_len * B < total)
+    return fail(LLATTE_ERR_INVALID_ARG, "need B >= 1, total_rows >= B, max_len*B >= total_rows");
+  if (dsc->dtype != LLATTE_F32 && dsc->dtype != LLATTE_BF16)
+    return fail(LLATTE_ERR_UNSUPPORTED, "dtype %d", dsc->dtype);
+  if (dsc->norm_mode != LLATTE_NORM_PRE && dsc->norm_mode != LLATTE_NORM_POST)
+    return fail(LLATTE_ERR_INVALID_ARG, "norm_mode %d", dsc->norm_mode);
+  if (dsc->n_layers < 1 || dsc->n_layers > LLATTE_MAX_LAYERS - 1)
+    return fail(LLATTE_ERR_INVALID_ARG, "n_layers must be in [1, %d]", LLATTE_MAX_LAYERS - 1);
+  S->B = B;
+  S->total = total;
+  S->max_len = max_len;
+  S->d = dsc->d;
+  S->h = dsc->n_heads;
+  S->dk = dsc->head_dim;
+  S->hd = S->h * S->dk;
+  S->r = dsc->rank;
+  S->dff = dsc->d_ff;
+  S->N = dsc->n_layers;
+  S->nq = dsc->n_q;
+  S->dc = dsc->d_ctx;
+  S->ns = dsc->n_seeds;
+  S->dout = dsc->d_out;
+  S->bf16 = dsc->dtype == LLATTE_BF16;
+  S->pre = dsc->norm_mode == LLATTE_NORM_PRE;
+  S->lnorm = dsc->latent_norm != 0;
+  S->eps = dsc->eps;
+  S->esz = S->bf16 ? 2 : 4;
+  const int al = S->bf16 ? 8 : 4;  // 16-byte vectors of the dtype
+  if (S->d < al || S->h < 1 || S->dk < 1 || S->r < 1 || S->nq < 0 || S->dc < 0 ||
+      S->ns < 0)
+    return fail(LLATTE_ERR_INVALID_ARG, "bad model dimensions");
+  if (S->d % al || S->dk % al || S->r % al || (S->d + S->dc) % al)
+    return fail(LLATTE_ERR_UNSUPPORTED, "d, head_dim, rank and d+d_ctx must be multiples of %d", al);
+  if (S->d > 1024 || S->r > 1024)
+    return fail(LLATTE_ERR_UNSUPPORTED, "d and rank must be <= 1024");
+  if (S->dff != 4 * S->d) return fail(LLATTE_ERR_INVALID_ARG, "d_ff must be 4*d");
+  if (!(S->eps >= 0.f)) return fail(LLATTE_ERR_INVALID_ARG, "eps must be >= 0");
+  if (S->nq == 0 && S->dc != 0) return fail(LLATTE_ERR_INVALID_ARG, "d_ctx needs n_q > 0");
+  if (S->ns > 0 && (S->dout < 1 || S->dout % 4))
+    return fail(LLATTE_ERR_INVALID_ARG, "d_out must be a positive multiple of 4");
+  if (S->bf16) {
+    if (S->r != 64 && S->r != 128 && S->r != 256)
+      return fail(LLATTE_ERR_UNSUPPORTED, "bf16 path needs rank in {64, 128, 256}");
+  } else if (S->r > 256) {
+    return fail(LLATTE_ERR_UNSUPPORTED, "f32 path needs rank <= 256");
+  }
+  llatte_status st = expand_rule(&dsc->pyramid, S->N, &S->rule);
+  if (st) return st;
+  if (S->ns > 0 && S->rule.kind == 0 && S->rule.values[S->N - 1] == 0)
+    return fail(LLATTE_ERR_INVALID_ARG, "the readout needs history rows after the last layer");
+  S->NP = S->N + (S->ns > 0 ? 1 : 0);
+  S->bq = S->bf16 ? attn_bq(S->h, S->r) : 0;
+  S->UBn.assign(S->NP, 0);
+  S->UBK.assign(S->NP, 0);
+  S->UBM.assign(S->NP, 0);
+  S->UBrows.assign(S->NP, 0);
+  long long prev = total;
+  long long icap = 1, qcap = 0;
+  for (int l = 0; l < S->NP; ++l) {
+    long long n;
+    if (l >= S->N)
+      n = 0;
+    else if (S->rule.kind == 1)
+      n = std::min<long long>(std::min<long long>((long long)B * S->rule.floor, total) +
+                                  ((long long)total >> std::min(l, 62)),
+                              total);
+    else
+      n = std::min<long long>((long long)B * S->rule.values[l], total);
+    n = std::min(n, prev);
+    const int nql = l < S->N ? S->nq : S->ns;
+    S->UBK[l] = prev;
+    S->UBn[l] = n;
+    S->UBM[l] = (long long)B * nql + n;
+    S->UBrows[l] = (long long)B * nql + prev;
+    qcap = std::max(qcap, S->UBM[l]);
+    if (S->bq > 0)
+      icap = std::max(icap, cdiv(n, S->bq) + B + (long long)B * cdiv(nql, S->bq));
+    prev = n;
+  }
+  if (qcap >= (1LL << 31) || S->UBrows[0] >= (1LL << 31))
+    return fail(LLATTE_ERR_UNSUPPORTED, "row counts exceed int32");
+  S->qcap = (int)qcap;
+  S->icap = (int)icap;
+  return LLATTE_OK;
+}
+
+// Workspace layout of the forward pass.
+struct LayerWT {
+  void *Wdkv, *Wuq, *Wuv, *Wo, *W1, *W2;  // transposed copies (K-contiguous)
+};
+struct FwdWS {
+  PlanBase plan;
+  std::vector<LayerWT> wt;
+  void *WqT, *WpT;
+  void* H;      // [max rows, d]
+  float* Cf;    // [max K, r] latent before its norm
+  void* Cl;     // [max K, r]
+  void* q;      // [qcap, hd]
+  void* ql;     // [qcap, h, r]
+  void* ol;     // [qcap, h, r]
+  void* o;      // [qcap, hd]
+  float* R1;    // [qcap, d]
+  void* H2;     // [qcap, d]
+  void* F;      // [qcap, dff]
+  float* Rb[2]; // [qcap, d]
+  float* Q0;    // [B*nq, d]
+  void* XC;     // [B*nq, d+dc]
+  float* S;     // [B*ns, d]
+  void* E;      // [B*ns*d]
+};
+
+static size_t layout_forward(const Shapes& S, void* base, FwdWS* w) {
+  Arena ar(base);
+  const size_t e = S.esz;
+  long long maxrows = 0, maxK = 0;
+  for (int l = 0; l < S.NP; ++l) {
+    maxrows = std::max(maxrows, S.UBrows[l]);
+    maxK = std::max(maxK, S.UBK[l]);
+  }
+  w->plan = carve_plan(ar, S.NP, S.B, S.qcap, S.icap);
+  w->wt.resize(S.NP);
+  for (int l = 0; l < S.NP; ++l) {
+    w->wt[l].Wdkv = ar.take<char>((size_t)S.d * S.r * e);
+    w->wt[l].Wuq = ar.take<char>((size_t)S.d * S.hd * e);
+    w->wt[l].Wuv = ar.take<char>((size_t)S.r * S.hd * e);
+    w->wt[l].Wo = ar.take<char>((size_t)S.hd * S.d * e);
+    w->wt[l].W1 = ar.take<char>((size_t)S.d * S.dff * e);
+    w->wt[l].W2 = ar.take<char>((size_t)S.dff * S.d * e);
+  }
+  w->WqT = S.nq ? ar.take<char>((size_t)(S.d + S.dc) * S.d * e) : nullptr;
+  w->WpT = S.ns ? ar.take<char>((size_t)S.ns * S.d * S.dout * e) : nullptr;
+  w->H = ar.take<char>((size_t)maxrows * S.d * e);
+  w->Cf = S.lnorm ? ar.take<float>((size_t)maxK * S.r) : nullptr;
+  w->Cl = ar.take<char>((size_t)maxK * S.r * e);
+  w->q = ar.take<char>((size_t)S.qcap * S.hd * e);
+  w->ql = ar.take<char>((size_t)S.qcap * S.h * S.r * e);
+  w->ol = ar.take<char>((size_t)S.qcap * S.h * S.r * e);
+  w->o = ar.take<char>((size_t)S.qcap * S.hd * e);
+  w->R1 = ar.take<float>((size_t)S.qcap * S.d);
+  w->H2 = ar.take<char>((size_t)S.qcap * S.d * e);
+  w->F = ar.take<char>((size_t)S.qcap * S.dff * e);
+  w->Rb[0] = ar.take<float>((size_t)S.qcap * S.d);
+  w->Rb[1] = ar.take<float>((size_t)S.qcap * S.d);
+  w->Q0 = S.nq ? ar.take<float>((size_t)S.B * S.nq * S.d) : nullptr;
+  w->XC = S.nq ? ar.take<char>((size_t)S.B * S.nq * (S.d + S.dc) * e) : nullptr;
+  w->S = S.ns ? ar.take<float>((size_t)S.B * S.ns * S.d) : nullptr;
+  w->E = S.ns ? ar.take<char>((size_t)S.B * S.ns * S.d * e) : nullptr;
+  return ar.off + 256;
+}
+
+static llatte_status check_layer(const llatte_layer_weights* L, int l) {
+  if (!L->g1 || !L->W_dkv || !L->W_uq || !L->W_uk || !L->W_uv || !L->W_o ||
+      !L->g2 || !L->W1 || !L->W2)
+    return fail(LLATTE_ERR_INVALID_ARG, "layer %d: NULL weight pointer", l);
+  return LLATTE_OK;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Transposed copies of one layer's matrices into the workspace.
+static hipError_t prep_layer(const Shapes& S, const llatte_layer_weights* L,
+                             const LayerWT& T, hipStream_t s) {
+  const bool b = S.bf16;
+  hipError_t e;
+  if ((e = transpose(L->W_dkv, S.d, S.r, S.r, 0, T.Wdkv, S.d, 0, 1, b, s))) return e;
+  if ((e = transpose(L->W_uq, S.d, S.hd, S.hd, 0, T.Wuq, S.d, 0, 1, b, s))) return e;
+  // per head: W_uv[:, j*dk:(j+1)*dk] ([r, dk]) -> [dk, r]
+  if ((e = transpose(L->W_uv, S.r, S.dk, S.hd, S.dk, T.Wuv, S.r,
+                     (long long)S.dk * S.r, S.h, b, s)))
+    return e;
+  if ((e = transpose(L->W_o, S.hd, S.d, S.d, 0, T.Wo, S.hd, 0, 1, b, s))) return e;
+  if ((e = transpose(L->W1, S.d, S.dff, S.dff, 0, T.W1, S.d, 0, 1, b, s))) return e;
+  if ((e = transpose(L->W2, S.dff, S.d, S.d, 0, T.W2, S.dff, 0, 1, b, s))) return e;
+  return hipSuccess;
+}
+
+// One layer (plan index l) from row space `src` into `out` ([UBM, d] float).
+static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
+                            const llatte_layer_weights* L, RowSrc src,
+                            float* out, hipStream_t s) {
+  const LayerPlan P = w.plan.layer(l);
+  const bool b = S.bf16;
+  const int nql = l < S.N ? S.nq : S.ns;
+  const long long nc = (long long)S.B * nql;
+  const int UBrows = (int)S.UBrows[l], UBK = (int)S.UBK[l], UBM = (int)S.UBM[l];
+  const size_t e = S.esz;
+  hipError_t err;
+
+  // 1. H = RMSNorm(R) g1 (pre) or R (post), all rows of the row space
+  if ((err = norm_rows(src, UBrows, P.counts + 2, S.pre ? L->g1 : nullptr, S.eps,
+                       nullptr, 0, w.H, S.d, S.d, b, s)))
+    return err;
+  // 2. latent C = H_hist W_dkv (+ RMSNorm g_c)
+  {
+    GemmParams g;
+    g.name = "gemm_down";
+    g.A = (const char*)w.H + (size_t)nc * S.d * e;
+    g.lda = S.d;
+    g.B = w.wt[l].Wdkv;
+    g.ldb = S.d;
+    g.M_cap = UBK;
+    g.M_dev = P.counts + 0;
+    g.N = S.r;
+    g.K = S.d;
+    if (S.lnorm) {
+      g.epi = EPI_STORE_F32;
+      g.C = w.Cf;
+    } else {
+      g.epi = EPI_STORE;
+      g.C = w.Cl;
+    }
+    g.ldc = S.r;
+    if ((err = gemm(g, b, s))) return err;
+    if (S.lnorm &&
+        (err = norm_rows(RowSrc{w.Cf, w.Cf, 0, S.r}, UBK, P.counts + 0, L->g_c,
+                         S.eps, nullptr, 0, w.Cl, S.r, S.r, b, s)))
+      return err;
+  }
+  // 3. q = H[qmap] W_uq
+  {
+    GemmParams g;
+    g.name = "gemm_q";
+    g.A = w.H;
+    g.lda = S.d;
+    g.a_rows = P.qmap;
+    g.B = w.wt[l].Wuq;
+    g.ldb = S.d;
+    g.M_cap = UBM;
+    g.M_dev = P.counts + 3;
+    g.N = S.hd;
+    g.K = S.d;
+    g.C = w.q;
+    g.ldc = S.hd;
+    if ((err = gemm(g, b, s))) return err;
+  }
+  // 4. latent queries per head: ql_j = q_j W_uk_j^T
+  {
+    GemmParams g;
+    g.name = "gemm_absorb_uk";
+    g.A = w.q;
+    g.lda = S.hd;
+    g.sA = S.dk;
+    g.B = L->W_uk;
+    g.ldb = S.hd;
+    g.sB = S.dk;
+    g.batch = S.h;
+    g.M_cap = UBM;
+    g.M_dev = P.counts + 3;
+    g.N = S.r;
+    g.K = S.dk;
+    g.C = w.ql;
+    g.ldc = S.h * S.r;
+    g.sC = S.r;
+    if ((err = gemm(g, b, s))) return err;
+  }
+  // 5. attention in latent space
+  {
+    AttnParams a;
+    a.q = w.ql;
+    a.c = w.Cl;
+    a.out = w.ol;
+    a.lse = nullptr;
+    a.h = S.h;
+    a.r = S.r;
+    a.scale = 1.f / sqrtf((float)S.dk);
+    a.items = P.items;
+    a.n_items = P.n_items;
+    a.items_cap = S.icap;
+    a.qinfo = P.qinfo;
+    a.M_cap = UBM;
+    a.M_dev = P.counts + 3;
+    if ((err = attention(a, b, s))) return err;
+  }
+  // 6. o_j = ol_j W_uv_j
+  {
+    GemmParams g;
+    g.name = "gemm_absorb_uv";
+    g.A = w.ol;
+    g.lda = S.h * S.r;
+    g.sA = S.r;
+    g.B = w.wt[l].Wuv;
+    g.ldb = S.r;
+    g.sB = (long long)S.dk * S.r;
+    g.batch = S.h;
+    g.M_cap = UBM;
+    g.M_dev = P.counts + 3;
+    g.N = S.dk;
+    g.K = S.r;
+    g.C = w.o;
+    g.ldc = S.hd;
+    g.sC = S.dk;
+    if ((err = gemm(g, b, s))) return err;
+  }
+  // 7. R1 = R[qmap] + o W_o
+  {
+    GemmParams g;
+    g.name = "gemm_out";
+    g.A = w.o;
+    g.lda = S.hd;
+    g.B = w.wt[l].Wo;
+    g.ldb = S.hd;
+    g.M_cap = UBM;
+    g.M_dev = P.counts + 3;
+    g.N = S.d;
+    g.K = S.hd;
+    g.epi = EPI_RESID_F32;
+    g.C = w.R1;
+    g.ldc = S.d;
+    g.res = src;
+    g.res_rows = P.qmap;
+    if ((err = gemm(g, b, s))) return err;
+  }
+  // 8. H2 = RMSNorm(R1) g2 (pre); post: R1 = RMSNorm(R1) g1, H2 = R1
+  if (S.pre)
+    err = norm_rows(RowSrc{w.R1, w.R1, 0, S.d}, UBM, P.counts + 3, L->g2, S.eps,
+                    nullptr, 0, w.H2, S.d, S.d, b, s);
+  else
+    err = norm_rows(RowSrc{w.R1, w.R1, 0, S.d}, UBM, P.counts + 3, L->g1, S.eps,
+                    w.R1, S.d, w.H2, S.d, S.d, b, s);
+  if (err) return err;
+  // 9. F = GELU(H2 W1)
+  {
+    GemmParams g;
+    g.name = "gemm_ffn1";
+    g.A = w.H2;
+    g.lda = S.d;
+    g.B = w.wt[l].W1;
+    g.ldb = S.d;
+    g.M_cap = UBM;
+    g.M_dev = P.counts + 3;
+    g.N = S.dff;
+    g.K = S.d;
+    g.epi = EPI_GELU;
+    g.C = w.F;
+    g.ldc = S.dff;
+    if ((err = gemm(g, b, s))) return err;
+  }
+  // 10. out = R1 + F W2 (post: then RMSNorm g2)
+  {
+    GemmParams g;
+    g.name = "gemm_ffn2";
+    g.A = w.F;
+    g.lda = S.dff;
+    g.B = w.wt[l].W2;
+    g.ldb = S.dff;
+    g.M_cap = UBM;
+    g.M_dev = P.counts + 3;
+    g.N = S.d;
+    g.K = S.dff;
+    g.epi = EPI_RESID_F32;
+    g.C = out;
+    g.ldc = S.d;
+    g.res = RowSrc{w.R1, w.R1, 0, S.d};
+    if ((err = gemm(g, b, s))) return err;
+  }
+  if (!S.pre &&
+      (err = norm_rows(RowSrc{out, out, 0, S.d}, UBM, P.counts + 3, L->g2, S.eps,
+                       out, S.d, nullptr, 0, S.d, b, s)))
+    return err;
+  return hipSuccess;
+}
+
+}  // namespace llatte
+
+using namespace llatte;
+
+extern "C" {
+
+const char* llatte_last_error(void) { return t_err.c_str(); }
+int32_t llatte_version(void) { return 100; }
+
+void llatte_kernel_timing_enable(int32_t on) { t_timing = on != 0; }
+
+void llatte_kernel_timing_reset(void) {
+  timing_collect();
+  t_acc.clear();
+}
+
+int32_t llatte_kernel_timing_read(char* names, int32_t name_stride,
+                                  int32_t* counts, double* ms, int32_t cap) {
+  timing_collect();
+  int32_t i = 0;
+  for (auto& kv : t_acc) {
+    if (i >= cap) break;
+    if (names && name_stride > 0) {
+      strncpy(names + (size_t)i * name_stride, kv.first.c_str(), name_stride - 1);
+      names[(size_t)i * name_stride + name_stride - 1] = 0;
+    }
+    if (counts) counts[i] = kv.second.first;
+    if (ms) ms[i] = kv.second.second;
+    ++i;
+  }
+  return i;
+}
+
+size_t llatte_mla_forward_workspace_size(const llatte_model_desc* desc,
+                                         int32_t B, int32_t total_rows,
+                                         int32_t max_len) {
+  Shapes S;
+  if (make_shapes(desc, B, total_rows, max_len, &S) != LLATTE_OK) return 0;
+  FwdWS w;
+  return layout_forward(S, nullptr, &w);
+}
+
+llatte_status llatte_mla_forward(
+    const llatte_model_desc* desc, const llatte_weights* wts,
+    const float* hist_values, const int32_t* hist_offsets, int32_t B,
+    int32_t total_rows, int32_t max_len, const float* cand_x,
+    const float* ctx, float* out_cand, float* out_hist,
+    int32_t* out_hist_offsets, float* out_emb, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  Shapes S;
+  llatte_status st = make_shapes(desc, B, total_rows, max_len, &S);
+  if (st) return st;
+  if (!wts || !wts->layers) return fail(LLATTE_ERR_INVALID_ARG, "weights are NULL");
+  for (int l = 0; l < S.N; ++l)
+    if ((st = check_layer(&wts->layers[l], l))) return st;
+  if (!hist_values || !hist_offsets)
+    return fail(LLATTE_ERR_INVALID_ARG, "hist_values/hist_offsets are NULL");
+  if (S.nq > 0 && (!cand_x || !out_cand || !wts->W_q))
+    return fail(LLATTE_ERR_INVALID_ARG, "n_q > 0 needs cand_x, out_cand and W_q");
+  if (S.nq > 0 && S.dc > 0 && !ctx)
+    return fail(LLATTE_ERR_INVALID_ARG, "d_ctx > 0 needs ctx");
+  if (S.ns > 0) {
+    if (!wts->seeds || !wts->W_p || !out_emb)
+      return fail(LLATTE_ERR_INVALID_ARG, "readout needs seeds, W_p and out_emb");
+    if ((st = check_layer(&wts->readout, -1))) return st;
+  }
+  const void* ptrs[] = {hist_values, cand_x, ctx, out_cand, out_hist, out_emb, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(LLATTE_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (!workspace) return fail(LLATTE_ERR_INVALID_ARG, "workspace is NULL");
+  FwdWS w;
+  const size_t need = layout_forward(S, nullptr, &w);
+  if (workspace_bytes < need)
+    return fail(LLATTE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  layout_forward(S, workspace, &w);
+  hipStream_t s = (hipStream_t)stream;
+  const bool b = S.bf16;
+
+  HIP_TRY(build_plan(hist_offsets, B, S.rule, S.nq, S.ns, w.plan, S.NP, S.bq,
+                     kAttnBN, s));
+  for (int l = 0; l < S.N; ++l) HIP_TRY(prep_layer(S, &wts->layers[l], w.wt[l], s));
+  if (S.ns) HIP_TRY(prep_layer(S, &wts->readout, w.wt[S.N], s));
+  if (S.nq) {
+    HIP_TRY(transpose(wts->W_q, S.d + S.dc, S.d, S.d, 0, w.WqT, S.d + S.dc, 0, 1, b, s));
+    HIP_TRY(concat_queries(cand_x, ctx, B, S.nq, S.d, S.dc, w.XC, b, s));
+    GemmParams g;
+    g.name = "gemm_fusion";
+    g.A = w.XC;
+    g.lda = S.d + S.dc;
+    g.B = w.WqT;
+    g.ldb = S.d + S.dc;
+    g.M_cap = B * S.nq;
+    g.N = S.d;
+    g.K = S.d + S.dc;
+    g.epi = EPI_STORE_F32;
+    g.C = w.Q0;
+    g.ldc = S.d;
+    HIP_TRY(gemm(g, b, s));
+  }
+  const long long nc = (long long)B * S.nq;
+  float* last = nullptr;
+  for (int l = 0; l < S.N; ++l) {
+    RowSrc src;
+    if (l == 0)
+      src = RowSrc{w.Q0, hist_values, (int)nc, S.d};
+    else
+      src = RowSrc{last, last + nc * S.d, (int)nc, S.d};
+    float* out = w.Rb[l & 1];
+    HIP_TRY(run_layer(S, w, l, &wts->layers[l], src, out, s));
+    last = out;
+  }
+  const LayerPlan PN = w.plan.layer(S.N - 1);
+  if (S.nq) HIP_TRY(copy_rows_f32(last, S.d, out_cand, (int)nc, nullptr, S.d, s));
+  if (out_hist)
+    HIP_TRY(copy_rows_f32(last + nc * S.d, S.d, out_hist, (int)S.UBn[S.N - 1],
+                          PN.counts + 1, S.d, s));
+  if (out_hist_offsets)
+    HIP_TRY(hipMemcpyAsync(out_hist_offsets, PN.hq_off, sizeof(int) * (B + 1),
+                           hipMemcpyDeviceToDevice, s));
+  if (S.ns) {
+    HIP_TRY(broadcast_rows(wts->seeds, S.ns, S.d, B, w.S, s));
+    float* ro = w.Rb[S.N & 1];
+    RowSrc src{w.S, last + nc * S.d, B * S.ns, S.d};
+    HIP_TRY(run_layer(S, w, S.N, &wts->readout, src, ro, s));
+    HIP_TRY(norm_rows(RowSrc{ro, ro, 0, S.d}, B * S.ns, nullptr, nullptr, 0.f,
+                      nullptr, 0, w.E, S.d, S.d, b, s));
+    HIP_TRY(transpose(wts->W_p, S.ns * S.d, S.dout, S.dout, 0, w.WpT, S.ns * S.d,
+                      0, 1, b, s));
+    GemmParams g;
+    g.name = "gemm_readout";
+    g.A = w.E;
+    g.lda = S.ns * S.d;
+    g.B = w.WpT;
+    g.ldb = S.ns * S.d;
+    g.M_cap = B;
+    g.N = S.dout;
+    g.K = S.ns * S.d;
+    g.epi = EPI_STORE_F32;
+    g.C = out_emb;
+    g.ldc = S.dout;
+    HIP_TRY(gemm(g, b, s));
+  }
+  return LLATTE_OK;
+}
+
+size_t llatte_mla_attention_workspace_size(const llatte_attn_desc* a,
+                                           int32_t B, int32_t Mtot,
+                                           int32_t Ktot) {
+  if (!a || B < 1 || Mtot < 0 || Ktot < B) return 0;
+  const bool b = a->dtype == LLATTE_BF16;
+  const int bq = b ? attn_bq(a->n_heads, a->rank) : 0;
+  const long long nh = (long long)Mtot - (long long)B * a->n_cand;
+  if (nh < 0) return 0;
+  const long long icap =
+      bq > 0 ? cdiv(nh, bq) + B + (long long)B * cdiv(a->n_cand, bq) : 1;
+  Arena ar(nullptr);
+  carve_plan(ar, 1, B, std::max(Mtot, 1), (int)icap);
+  return ar.off + 256;
+}
+
+llatte_status llatte_mla_attention(
+    const llatte_attn_desc* a, const void* q_lat, const void* c_lat,
+    const int32_t* kv_offsets, const int32_t* hq_offsets, int32_t B,
+    int32_t Mtot, int32_t Ktot, void* out, float* lse, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  if (!a) return fail(LLATTE_ERR_INVALID_ARG, "desc is NULL");
+  if (a->dtype != LLATTE_F32 && a->dtype != LLATTE_BF16)
+    return fail(LLATTE_ERR_UNSUPPORTED, "dtype %d", a->dtype);
+  const bool b = a->dtype == LLATTE_BF16;
+  if (a->n_heads < 1 || a->rank < 1 || a->n_cand < 0 || B < 1 || Ktot < B ||
+      Mtot < (long long)B * a->n_cand)
+    return fail(LLATTE_ERR_INVALID_ARG, "bad sizes");
+  if (b && attn_bq(a->n_heads, a->rank) == 0)
+    return fail(LLATTE_ERR_UNSUPPORTED, "bf16 attention needs rank in {64, 128, 256}");
+  if (!b && a->rank > 256) return fail(LLATTE_ERR_UNSUPPORTED, "f32 attention needs rank <= 256");
+  if (!(a->scale > 0.f)) return fail(LLATTE_ERR_INVALID_ARG, "scale must be > 0");
+  if (!q_lat || !c_lat || !kv_offsets || !hq_offsets || !out || !workspace)
+    return fail(LLATTE_ERR_INVALID_ARG, "NULL pointer");
+  const void* ptrs[] = {q_lat, c_lat, out, lse, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(LLATTE_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  const size_t need = llatte_mla_attention_workspace_size(a, B, Mtot, Ktot);
+  if (workspace_bytes < need)
+    return fail(LLATTE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  if (Mtot == 0) return LLATTE_OK;
+  const int bq = b ? attn_bq(a->n_heads, a->rank) : 0;
+  const long long nh = (long long)Mtot - (long long)B * a->n_cand;
+  const int icap = bq > 0 ? (int)(cdiv(nh, bq) + B + (long long)B * cdiv(a->n_cand, bq)) : 1;
+  Arena ar(workspace);
+  PlanBase pb = carve_plan(ar, 1, B, Mtot, icap);
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(build_attn_plan(kv_offsets, hq_offsets, B, a->n_cand, bq, kAttnBN, pb, s));
+  const LayerPlan P = pb.layer(0);
+  AttnParams ap;
+  ap.q = q_lat;
+  ap.c = c_lat;
+  ap.out = out;
+  ap.lse = lse;
+  ap.h = a->n_heads;
+  ap.r = a->rank;
+  ap.scale = a->scale;
+  ap.items = P.items;
+  ap.n_items = P.n_items;
+  ap.items_cap = icap;
+  ap.qinfo = P.qinfo;
+  ap.M_cap = Mtot;
+  ap.M_dev = P.counts + 3;
+  HIP_TRY(attention(ap, b, s));
+  return LLATTE_OK;
+}
+
+llatte_status llatte_pyramid_compact(const void* values, int32_t row_elems,
+                                     int32_t dt, const int32_t* offsets_in,
+                                     int32_t B, int32_t total_rows,
+                                     const int32_t* keep, void* values_out,
+                                     int32_t* offsets_out, int32_t* src_index,
+                                     void* stream) {
+  if (dt != LLATTE_F32 && dt != LLATTE_BF16) return fail(LLATTE_ERR_UNSUPPORTED, "dtype %d", dt);
+  if (B < 1 || total_rows < 0 || row_elems < 1)
+    return fail(LLATTE_ERR_INVALID_ARG, "bad sizes");
+  if (!values || !offsets_in || !keep || !values_out || !offsets_out)
+    return fail(LLATTE_ERR_INVALID_ARG, "NULL pointer");
+  const int row_bytes = row_elems * (dt == LLATTE_BF16 ? 2 : 4);
+  if ((row_bytes & 3) || !aligned16(values) || !aligned16(values_out))
+    return fail(LLATTE_ERR_INVALID_ARG, "rows must be a multiple of 4 bytes, pointers 16-byte aligned");
+  HIP_TRY(pyramid_compact(values, row_bytes, offsets_in, B, total_rows, keep,
+                          values_out, offsets_out, src_index, (hipStream_t)stream));
+  return LLATTE_OK;
+}
+
+llatte_status llatte_pyramid_counts(const llatte_pyramid_rule* rule,
+                                    int32_t n_layers,
+                                    const int32_t* offsets_in, int32_t B,
+                                    int32_t* keep_out, void* stream) {
+  if (!rule || !offsets_in || !keep_out || B < 1 || n_layers < 1 ||
+      n_layers > LLATTE_MAX_LAYERS)
+    return fail(LLATTE_ERR_INVALID_ARG, "bad arguments");
+  RuleDev rd;
+  llatte_status st = expand_rule(rule, n_layers, &rd);
+  if (st) return st;
+  HIP_TRY(pyramid_counts_dev(rd, offsets_in, B, keep_out, (hipStream_t)stream));
+  return LLATTE_OK;
+}
+
+llatte_status llatte_pyramid_counts_host(const llatte_pyramid_rule* rule,
+                                         int32_t n_layers,
+                                         const int32_t* lengths, int32_t B,
+                                         int32_t* keep_out) {
+  if (!rule || !lengths || !keep_out || B < 1 || n_layers < 1 ||
+      n_layers > LLATTE_MAX_LAYERS)
+    return fail(LLATTE_ERR_INVALID_ARG, "bad arguments");
+  RuleDev rd;
+  llatte_status st = expand_rule(rule, n_layers, &rd);
+  if (st) return st;
+  for (int u = 0; u < B; ++u) {
+    const int L = lengths[u];
+    if (L < 1) return fail(LLATTE_ERR_INVALID_ARG, "length of user %d is < 1", u);
+    int prev = L;
+    for (int l = 0; l < n_layers; ++l) {
+      int k = rd.kind == 1 ? std::max(std::min(rd.floor, L), L >> std::min(l, 30))
+                           : rd.values[l];
+      prev = std::min(k, prev);
+      keep_out[(size_t)l * B + u] = prev;
+    }
+  }
+  return LLATTE_OK;
+}
+
+size_t llatte_token_embed_workspace_size(int32_t d, int32_t d_sem, int32_t dt) {
+  if (d < 1 || d_sem < 1) return 0;
+  return (size_t)d * d_sem * (dt == LLATTE_BF16 ? 2 : 4) + 256;
+}
+
+llatte_status llatte_token_embed(const void* table, int32_t V,
+                                 const int32_t* rows, const void* sem,
+                                 const void* W_s, int32_t n, int32_t d,
+                                 int32_t d_sem, int32_t dt, float* out,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (dt != LLATTE_F32 && dt != LLATTE_BF16) return fail(LLATTE_ERR_UNSUPPORTED, "dtype %d", dt);
+  const bool b = dt == LLATTE_BF16;
+  const int al = b ? 8 : 4;
+  if (V < 1 || n < 0 || d < 1 || d_sem < 1) return fail(LLATTE_ERR_INVALID_ARG, "bad sizes");
+  if (d % al || d_sem % al)
+    return fail(LLATTE_ERR_UNSUPPORTED, "d and d_sem must be multiples of %d", al);
+  if (!table || !rows || !sem || !W_s || !out || !workspace)
+    return fail(LLATTE_ERR_INVALID_ARG, "NULL pointer");
+  const void* ptrs[] = {table, sem, W_s, out, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(LLATTE_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (workspace_bytes < llatte_token_embed_workspace_size(d, d_sem, dt))
+    return fail(LLATTE_ERR_WORKSPACE, "workspace too small");
+  if (n == 0) return LLATTE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(transpose(W_s, d_sem, d, d, 0, workspace, d_sem, 0, 1, b, s));
+  GemmParams g;
+  g.name = "gemm_token_embed";
+  g.A = sem;
+  g.lda = d_sem;
+  g.B = workspace;
+  g.ldb = d_sem;
+  g.M_cap = n;
+  g.N = d;
+  g.K = d_sem;
+  g.epi = EPI_GATHER_ADD_F32;
+  g.C = out;
+  g.ldc = d;
+  g.table = table;
+  g.ld_table = d;
+  g.g_rows = rows;
+  HIP_TRY(gemm(g, b, s));
+  return LLATTE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,244 @@
+// Tiled matrix product on the gfx950 matrix cores, with fused epilogues.
+//
+// Both operands are K-contiguous (A [M, K], B [N, K]); weights are brought to
+// this layout once per call by the transpose kernel. A workgroup of four
+// waves computes a BM x BN tile; K advances in BK steps through a
+// double-buffered LDS stage (rows padded by 16 bytes so that the 16-byte
+// fragment reads of 8 consecutive rows fall in distinct banks). The MFMA is
+// issued with the operands swapped (B fragment first) so that each lane ends
+// up holding four consecutive output columns of one row: the epilogue then
+// reads residuals and writes results as 8- or 16-byte vectors.
+//
+// bf16 operands use v_mfma_f32_16x16x32_bf16; fp32 operands use
+// v_mfma_f32_16x16x4_f32. Accumulation is fp32 in both cases.
+#include "kernels.hpp"
+
+namespace llatte {
+
+template <typename T> struct Mfma;
+template <> struct Mfma<bf16> {
+  static constexpr int KSTEP = 32;   // k per instruction
+  static constexpr int VEC = 8;      // k values per lane
+  typedef bf16x8 frag;
+  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<float> {
+  static constexpr int KSTEP = 4;
+  static constexpr int VEC = 1;
+  typedef float frag;
+  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ float gelu_erf(float x) {
+  return 0.5f * x * (1.f + erff(x * 0.70710678118654752f));
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *(f32x4*)p = f32x4{a, b, c, d};
+}
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16* p, float a, float b, float c, float d) {
+  *(bf16x4*)p = bf16x4{to_bf16(a), to_bf16(b), to_bf16(c), to_bf16(d)};
+}
+template <typename T> __device__ __forceinline__ f32x4 load4(const T* p);
+template <> __device__ __forceinline__ f32x4 load4<float>(const float* p) {
+  return *(const f32x4*)p;
+}
+template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
+  bf16x4 v = *(const bf16x4*)p;
+  return f32x4{from_bf16(v[0]), from_bf16(v[1]), from_bf16(v[2]), from_bf16(v[3])};
+}
+
+template <typename T, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
+  using MF = Mfma<T>;
+  constexpr int CE = 16 / sizeof(T);       // elements per 16-byte chunk
+  constexpr int BK = 8 * CE;               // 8 chunks per tile row
+  constexpr int LDK = BK + CE;             // padded LDS row (elements)
+  constexpr int WAVES_N = BN / WN;
+  static_assert((BM / WM) * (BN / WN) == 4, "four waves");
+  constexpr int AI = BM * 8 / 256;         // A chunks per thread
+  constexpr int BI = BN * 8 / 256;
+  constexpr int TM = WM / 16, TN = WN / 16;
+
+  __shared__ __attribute__((aligned(16))) T As[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) T Bs[2][BN * LDK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int M = dev_count(p.M_dev, p.M_cap);
+
+  // Tile index, regrouped so that consecutive tiles of one XCD (workgroups
+  // are dealt to the eight XCDs round-robin) share the same A rows.
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int tiles_m = (p.M_cap + BM - 1) / BM;
+  const int G = tiles_n * tiles_m;
+  int bid = blockIdx.x;
+  const int per = G / 8;
+  if (bid < per * 8) bid = (bid & 7) * per + (bid >> 3);
+  const int tm = bid / tiles_n, tn = bid % tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  if (m0 >= M) return;
+
+  const T* A = (const T*)p.A + (size_t)blockIdx.z * p.sA;
+  const T* Bm = (const T*)p.B + (size_t)blockIdx.z * p.sB;
+
+  // Per-thread global source rows (fixed across the K loop).
+  const T* arow[AI];
+  bool aok[AI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    int c = tid + i * 256;
+    int r = m0 + c / 8;
+    aok[i] = r < M;
+    int src = aok[i] ? (p.a_rows ? p.a_rows[r] : r) : 0;
+    arow[i] = A + (size_t)src * p.lda + (c % 8) * CE;
+  }
+  const T* brow[BI];
+  bool bok[BI];
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    int c = tid + i * 256;
+    int r = n0 + c / 8;
+    bok[i] = r < p.N;
+    brow[i] = Bm + (size_t)(bok[i] ? r : 0) * p.ldb + (c % 8) * CE;
+  }
+
+  i32x4 ra[AI], rb[BI];
+  auto load_tile = [&](int kt) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+      int kc = ((tid + i * 256) % 8) * CE;
+      bool ok = aok[i] && (k0 + kc < p.K);
+      ra[i] = ok ? *(const i32x4*)(arow[i] + k0) : i32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      int kc = ((tid + i * 256) % 8) * CE;
+      bool ok = bok[i] && (k0 + kc < p.K);
+      rb[i] = ok ? *(const i32x4*)(brow[i] + k0) : i32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_lds = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+      int c = tid + i * 256;
+      *(i32x4*)&As[buf][(c / 8) * LDK + (c % 8) * CE] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      int c = tid + i * 256;
+      *(i32x4*)&Bs[buf][(c / 8) * LDK + (c % 8) * CE] = rb[i];
+    }
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int wm0 = (wave / WAVES_N) * WM;
+  const int wn0 = (wave % WAVES_N) * WN;
+  const int lr = lane & 15;                 // fragment row
+  const int lk = (lane >> 4) * MF::VEC;     // fragment k offset
+
+  const int nk = (p.K + BK - 1) / BK;
+  load_tile(0);
+  store_lds(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_tile(kt + 1);
+    const T* as = As[cur];
+    const T* bs = Bs[cur];
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += MF::KSTEP) {
+      typename MF::frag fa[TM], fb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        fa[i] = *(const typename MF::frag*)&as[(wm0 + i * 16 + lr) * LDK + kk + lk];
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        fb[j] = *(const typename MF::frag*)&bs[(wn0 + j * 16 + lr) * LDK + kk + lk];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(fb[j], fa[i], acc[i][j]);
+    }
+    if (kt + 1 < nk) store_lds(cur ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: lane holds C[m][n .. n+3] of each 16x16 block.
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int m = m0 + wm0 + i * 16 + lr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + wn0 + j * 16 + (lane >> 4) * 4;
+      if (n >= p.N) continue;
+      f32x4 v = acc[i][j];
+      const size_t off = (size_t)blockIdx.z * p.sC + (size_t)m * p.ldc + n;
+      switch (p.epi) {
+        case EPI_STORE:
+          store4<T>((T*)p.C + off, p.alpha * v[0], p.alpha * v[1], p.alpha * v[2],
+                    p.alpha * v[3]);
+          break;
+        case EPI_STORE_F32:
+          store4<float>((float*)p.C + off, p.alpha * v[0], p.alpha * v[1],
+                        p.alpha * v[2], p.alpha * v[3]);
+          break;
+        case EPI_GELU:
+          store4<T>((T*)p.C + off, gelu_erf(v[0]), gelu_erf(v[1]), gelu_erf(v[2]),
+                    gelu_erf(v[3]));
+          break;
+        case EPI_RESID_F32: {
+          const float* rr = p.res.row(p.res_rows ? p.res_rows[m] : m) + n;
+          f32x4 r = *(const f32x4*)rr;
+          store4<float>((float*)p.C + off, v[0] + r[0], v[1] + r[1], v[2] + r[2],
+                        v[3] + r[3]);
+        } break;
+        case EPI_GATHER_ADD_F32: {
+          const T* tr = (const T*)p.table + (size_t)p.g_rows[m] * p.ld_table + n;
+          f32x4 r = load4<T>(tr);
+          store4<float>((float*)p.C + off, v[0] + r[0], v[1] + r[1], v[2] + r[2],
+                        v[3] + r[3]);
+        } break;
+      }
+    }
+  }
+}
+
+template <typename T, int BM, int BN, int WM, int WN>
+static hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
+  const int tiles = ((p.M_cap + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  if (tiles == 0 || p.batch == 0) return hipSuccess;
+  timing_begin(p.name, s);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN>), dim3(tiles, 1, p.batch),
+                     dim3(256), 0, s, p);
+  timing_end(s);
+  return hipGetLastError();
+}
+
+hipError_t gemm(const GemmParams& p, bool is_bf16, hipStream_t s) {
+  if (p.M_cap <= 0 || p.N <= 0) return hipSuccess;
+  if (is_bf16) {
+    if (p.N <= 64) return launch_gemm<bf16, 128, 64, 64, 32>(p, s);
+    return launch_gemm<bf16, 128, 128, 64, 64>(p, s);
+  }
+  if (p.N <= 64) return launch_gemm<float, 128, 64, 64, 32>(p, s);
+  return launch_gemm<float, 128, 128, 64, 64>(p, s);
+}
+
+}  // namespace llatte

@@ -1,0 +1,179 @@
+// Internal launcher interfaces between the C-ABI layer and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace llatte {
+
+// ------------------------------------------------------------------ timing
+// Optional per-launch HIP-event timing (off by default). `name` must be a
+// string literal.
+void timing_begin(const char* name, hipStream_t s);
+void timing_end(hipStream_t s);
+
+// ------------------------------------------------------------------ GEMM
+// C[m, n] = sum_k A[m, k] * B[n, k]  (A row-major [M, K], B row-major [N, K],
+// i.e. both operands K-contiguous), fp32 accumulation, then an epilogue.
+enum GemmEpi {
+  EPI_STORE = 0,       // C (dtype) = alpha * acc
+  EPI_STORE_F32 = 1,   // C (float) = alpha * acc
+  EPI_GELU = 2,        // C (dtype) = gelu(acc)
+  EPI_RESID_F32 = 3,   // C (float) = acc + res.row(res_rows ? res_rows[m] : m)
+  EPI_GATHER_ADD_F32 = 4,  // C (float) = acc + table[g_rows[m]]
+};
+
+struct GemmParams {
+  const void* A = nullptr;
+  int lda = 0;
+  const int* a_rows = nullptr;  // optional gather: A row m is A[a_rows[m]]
+  const void* B = nullptr;
+  int ldb = 0;
+  int M_cap = 0;
+  const int* M_dev = nullptr;   // optional device-side row count (<= M_cap)
+  int N = 0, K = 0;
+  int batch = 1;                // grid.z; operands advance by the strides
+  long long sA = 0, sB = 0, sC = 0;
+  int epi = EPI_STORE;
+  const char* name = "gemm";    // label for the optional kernel timing
+  void* C = nullptr;
+  int ldc = 0;
+  float alpha = 1.f;
+  RowSrc res{};                 // EPI_RESID_F32
+  const int* res_rows = nullptr;
+  const void* table = nullptr;  // EPI_GATHER_ADD_F32 (dtype of A)
+  int ld_table = 0;
+  const int* g_rows = nullptr;
+};
+
+hipError_t gemm(const GemmParams& p, bool bf16, hipStream_t s);
+
+// ------------------------------------------------------------------ row ops
+// One wave per row (d <= 1024): out = gain ? x / sqrt(mean(x^2) + eps) * gain : x, where
+// x = src.row(i); written as float to out_f32 (may alias the source) and/or
+// as dtype to out_t. Rows i >= *rows_dev (if given) are skipped.
+hipError_t norm_rows(RowSrc src, int rows_cap, const int* rows_dev,
+                     const float* gain, float eps, float* out_f32, int ld_f32,
+                     void* out_t, int ld_t, int d, bool bf16, hipStream_t s);
+
+// dst (dtype) [rows, cols] = transpose(src (dtype) [cols, rows]) for a batch
+// of `batch` matrices laid out with the given element strides.
+hipError_t transpose(const void* src, int src_rows, int src_cols, int ld_src,
+                     long long s_src, void* dst, int ld_dst, long long s_dst,
+                     int batch, bool bf16, hipStream_t s);
+
+// xc (dtype) [B*n_q, d + d_c]: row u*n_q + j = [cand[u*n_q+j] ; ctx[u]].
+hipError_t concat_queries(const float* cand, const float* ctx, int B, int n_q,
+                          int d, int d_c, void* xc, bool bf16, hipStream_t s);
+
+// out (float) [B*n_s, d]: row u*n_s + j = seeds[j].
+hipError_t broadcast_rows(const float* seeds, int n_s, int d, int B,
+                          float* out, hipStream_t s);
+
+// Copy float rows [row0, row0 + count) of src into dst (count from device if
+// count_dev is given, else count_cap).
+hipError_t copy_rows_f32(const float* src, int ld, float* dst, int count_cap,
+                         const int* count_dev, int d, hipStream_t s);
+
+// ------------------------------------------------------------------ plan
+// Per-layer device plan built from the history offsets.
+struct LayerPlan {
+  int* kv_len;     // [B]   keys per user at this layer (K_u)
+  int* keep;       // [B]   history queries per user (n_u)
+  int* kv_off;     // [B+1] exclusive scan of kv_len
+  int* hq_off;     // [B+1] exclusive scan of keep
+  int* counts;     // [4]   {sum K, sum n, rows = nc + sum K, M = nc + sum n}
+  int* qmap;       // [qcap] query row -> row of the layer's row space
+  int2* qinfo;     // [qcap] query row -> {kv base row, key position}
+  i32x4* items;    // [icap] attention work items, heaviest first
+  int* n_items;    // [1]
+};
+
+// All layers' plans in one block of device memory with fixed strides.
+struct PlanBase {
+  int* kv_len;   // [n_plans][B]
+  int* keep;     // [n_plans][B]
+  int* kv_off;   // [n_plans][B+1]
+  int* hq_off;   // [n_plans][B+1]
+  int* counts;   // [n_plans][4]
+  int* qmap;     // [n_plans][qcap]
+  int2* qinfo;   // [n_plans][qcap]
+  i32x4* items;  // [n_plans][icap]
+  int* n_items;  // [n_plans]
+  int B, qcap, icap;
+  __host__ __device__ LayerPlan layer(int l) const {
+    LayerPlan p;
+    p.kv_len = kv_len + (size_t)l * B;
+    p.keep = keep + (size_t)l * B;
+    p.kv_off = kv_off + (size_t)l * (B + 1);
+    p.hq_off = hq_off + (size_t)l * (B + 1);
+    p.counts = counts + (size_t)l * 4;
+    p.qmap = qmap + (size_t)l * qcap;
+    p.qinfo = qinfo + (size_t)l * qcap;
+    p.items = items + (size_t)l * icap;
+    p.n_items = n_items + l;
+    return p;
+  }
+  // bytes of device memory for n_plans layers
+  static size_t bytes(int n_plans, int B, int qcap, int icap) {
+    size_t n = (size_t)n_plans;
+    return n * (2 * (size_t)B + 2 * ((size_t)B + 1) + 4 + 1) * sizeof(int) +
+           n * (size_t)qcap * (sizeof(int) + sizeof(int2)) +
+           n * (size_t)icap * sizeof(i32x4) + 64 * 9;
+  }
+};
+
+// A pyramid rule with the per-layer list already expanded on the host
+// (FIXED and GEOMETRIC: kind 0 with values; HALVING: kind 1 with floor).
+struct RuleDev {
+  int kind;
+  int floor;
+  int n_layers;
+  int values[64];
+};
+
+// Builds the plans of layers 0..rule.n_layers-1, plus one readout plan
+// (no history queries, n_seeds query tokens) when n_plans > n_layers.
+// bq/bn: query rows and keys per attention tile (bq = 0: no work items).
+hipError_t build_plan(const int* offsets, int B, const RuleDev& rule, int n_q,
+                      int n_seeds, const PlanBase& base, int n_plans, int bq,
+                      int bn, hipStream_t s);
+
+// One-layer plan for the standalone attention entry from given offsets.
+hipError_t build_attn_plan(const int* kv_off, const int* hq_off, int B,
+                           int n_cand, int bq, int bn, const PlanBase& base,
+                           hipStream_t s);
+
+hipError_t pyramid_counts_dev(const RuleDev& rule, const int* offsets, int B,
+                              int* keep_out, hipStream_t s);
+
+hipError_t pyramid_compact(const void* values, int row_bytes,
+                           const int* offsets_in, int B, int total_rows,
+                           const int* keep, void* values_out,
+                           int* offsets_out, int* src_index, hipStream_t s);
+
+// ------------------------------------------------------------------ attention
+struct AttnParams {
+  const void* q;      // [M, h, r]
+  const void* c;      // [Ktot, r]
+  void* out;          // [M, h, r]
+  float* lse;         // [M, h] or null
+  int h, r;
+  float scale;
+  const i32x4* items; // bf16 path
+  const int* n_items;
+  int items_cap;
+  const int2* qinfo;  // f32 path: per query row {kv base, key position}
+  int M_cap;
+  const int* M_dev;
+};
+
+// Query rows per work item for the bf16 kernel at these sizes (0 if the
+// shape is not supported by the MFMA kernel).
+int attn_bq(int h, int r);
+constexpr int kAttnBN = 64;
+hipError_t attention(const AttnParams& p, bool bf16, hipStream_t s);
+
+}  // namespace llatte

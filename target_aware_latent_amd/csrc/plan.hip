@@ -1,0 +1,310 @@
+// Device-side planning of the jagged, pyramidal layer stack.
+//
+// Everything that depends on the per-user history lengths is computed on the
+// GPU from the offsets, so the forward pass never waits for the host: per
+// layer the key and query counts of every user (pyramidal schedule of
+// LLaTTE, Appendix A.2), their exclusive scans, the query-row gather map,
+// and the attention work items sorted by decreasing cost (longest-processing-
+// time order, so that the heaviest query blocks start first and the tail of
+// the grid holds the light ones).
+#include "kernels.hpp"
+
+namespace llatte {
+
+constexpr int kPlanThreads = 1024;
+constexpr int kMaxBuckets = 4096;  // cost buckets: KV tiles per work item
+constexpr unsigned kCandFlag = 0x80000000u;
+
+// Count of user u at layer l (0-based) under the rule, capped by `prev`
+// (the count at layer l-1, or L_u at layer 0).
+__device__ __forceinline__ int rule_eval(const RuleDev& r, int l, int L,
+                                         int prev) {
+  int k;
+  if (r.kind == 1)  // halving with floor
+    k = max(min(r.floor, L), L >> min(l, 30));
+  else
+    k = r.values[l];
+  return min(k, prev);
+}
+
+// Exclusive scan of in[0..B) into out[0..B], out[B] = total, by one block of
+// kPlanThreads threads; each thread owns a contiguous chunk of users.
+__device__ void block_scan(const int* in, int* out, int B, int* sh) {
+  const int t = threadIdx.x;
+  const int chunk = (B + kPlanThreads - 1) / kPlanThreads;
+  const int u0 = min(B, t * chunk), u1 = min(B, u0 + chunk);
+  int s = 0;
+  for (int u = u0; u < u1; ++u) s += in[u];
+  sh[t] = s;
+  __syncthreads();
+  for (int o = 1; o < kPlanThreads; o <<= 1) {
+    int v = t >= o ? sh[t - o] : 0;
+    __syncthreads();
+    sh[t] += v;
+    __syncthreads();
+  }
+  int run = sh[t] - s;  // exclusive prefix of this chunk
+  for (int u = u0; u < u1; ++u) {
+    out[u] = run;
+    run += in[u];
+  }
+  if (t == kPlanThreads - 1) out[B] = sh[t];
+  __syncthreads();
+}
+
+struct PlanArgs {
+  PlanBase base;
+  int n_plans;
+  int n_layers;      // layers of the stack (plans beyond are the readout)
+  int nq[65];        // query tokens per user, per plan
+};
+
+// Counts and offsets of every layer; one block.
+__global__ __launch_bounds__(kPlanThreads) void plan_counts_kernel(
+    const int* offsets, int B, RuleDev rule, PlanArgs a) {
+  __shared__ int sh[kPlanThreads];
+  for (int l = 0; l < a.n_plans; ++l) {
+    const LayerPlan P = a.base.layer(l);
+    for (int u = threadIdx.x; u < B; u += kPlanThreads) {
+      const int L = offsets[u + 1] - offsets[u];
+      const int K = l == 0 ? L : a.base.layer(l - 1).keep[u];
+      const int n = l < a.n_layers ? rule_eval(rule, l, L, K) : 0;
+      P.kv_len[u] = K;
+      P.keep[u] = n;
+    }
+    __syncthreads();
+    block_scan(P.kv_len, P.kv_off, B, sh);
+    block_scan(P.keep, P.hq_off, B, sh);
+    if (threadIdx.x == 0) {
+      const int nc = B * a.nq[l];
+      P.counts[0] = P.kv_off[B];
+      P.counts[1] = P.hq_off[B];
+      P.counts[2] = nc + P.kv_off[B];
+      P.counts[3] = nc + P.hq_off[B];
+    }
+    __syncthreads();
+  }
+}
+
+// Attention work items of one layer (blockIdx.x = plan), counting-sorted by
+// cost (KV tiles) in decreasing order. Item = {first query row, kv base row,
+// rows | candidate flag, key position of the first row}.
+__global__ __launch_bounds__(kPlanThreads) void plan_items_kernel(
+    PlanArgs a, int B, int bq, int bn, int items_cap) {
+  __shared__ int hist[kMaxBuckets];
+  const int l = blockIdx.x;
+  const LayerPlan P = a.base.layer(l);
+  const int nq = a.nq[l];
+  const int nc = B * nq;
+  for (int i = threadIdx.x; i < kMaxBuckets; i += kPlanThreads) hist[i] = 0;
+  __syncthreads();
+  const int ncb = (nq + bq - 1) / bq;
+  // pass 0 counts items per cost bucket, pass 1 places them
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int u = threadIdx.x; u < B; u += kPlanThreads) {
+      const int K = P.kv_len[u], n = P.keep[u];
+      const int kvb = P.kv_off[u];
+      const int nhb = (n + bq - 1) / bq;
+      for (int b = 0; b < nhb + ncb; ++b) {
+        i32x4 it;
+        int cost;
+        if (b < nhb) {
+          const int t0 = b * bq, nr = min(bq, n - t0);
+          const int pos0 = K - n + t0;
+          it = i32x4{nc + P.hq_off[u] + t0, kvb, nr, pos0};
+          cost = (pos0 + nr + bn - 1) / bn;
+        } else {
+          const int j0 = (b - nhb) * bq, nr = min(bq, nq - j0);
+          it = i32x4{u * nq + j0, kvb, (int)(kCandFlag | (unsigned)nr), K - 1};
+          cost = (K + bn - 1) / bn;
+        }
+        const int bucket = kMaxBuckets - 1 - min(cost, kMaxBuckets - 1);
+        if (pass == 0) {
+          atomicAdd(&hist[bucket], 1);
+        } else {
+          const int slot = atomicAdd(&hist[bucket], 1);
+          if (slot < items_cap) P.items[slot] = it;
+        }
+      }
+    }
+    __syncthreads();
+    if (pass == 0) {
+      // exclusive scan of the bucket counts (buckets ordered heaviest first)
+      __shared__ int part[kPlanThreads];
+      const int per = kMaxBuckets / kPlanThreads;
+      int s = 0;
+      for (int i = 0; i < per; ++i) s += hist[threadIdx.x * per + i];
+      part[threadIdx.x] = s;
+      __syncthreads();
+      for (int o = 1; o < kPlanThreads; o <<= 1) {
+        int v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+        __syncthreads();
+        part[threadIdx.x] += v;
+        __syncthreads();
+      }
+      int run = part[threadIdx.x] - s;
+      for (int i = 0; i < per; ++i) {
+        const int c = hist[threadIdx.x * per + i];
+        hist[threadIdx.x * per + i] = run;
+        run += c;
+      }
+      if (threadIdx.x == kPlanThreads - 1) *P.n_items = min(part[threadIdx.x], items_cap);
+      __syncthreads();
+    }
+  }
+}
+
+// Query gather map and per-row attention info; grid (B, n_plans).
+__global__ void plan_qmap_kernel(PlanArgs a, int B) {
+  const int u = blockIdx.x, l = blockIdx.y;
+  const LayerPlan P = a.base.layer(l);
+  const int nq = a.nq[l];
+  const int nc = B * nq;
+  const int K = P.kv_len[u], n = P.keep[u];
+  const int kvb = P.kv_off[u];
+  for (int j = threadIdx.x; j < nq; j += blockDim.x) {
+    const int i = u * nq + j;
+    P.qmap[i] = i;
+    P.qinfo[i] = int2{kvb, K - 1};
+  }
+  for (int t = threadIdx.x; t < n; t += blockDim.x) {
+    const int i = nc + P.hq_off[u] + t;
+    P.qmap[i] = nc + kvb + K - n + t;
+    P.qinfo[i] = int2{kvb, K - n + t};
+  }
+}
+
+hipError_t build_plan(const int* offsets, int B, const RuleDev& rule, int n_q,
+                      int n_seeds, const PlanBase& base, int n_plans, int bq,
+                      int bn, hipStream_t s) {
+  PlanArgs a;
+  a.base = base;
+  a.n_plans = n_plans;
+  a.n_layers = rule.n_layers;
+  for (int l = 0; l < n_plans; ++l) a.nq[l] = l < rule.n_layers ? n_q : n_seeds;
+  timing_begin("plan", s);
+  hipLaunchKernelGGL(plan_counts_kernel, dim3(1), dim3(kPlanThreads), 0, s,
+                     offsets, B, rule, a);
+  if (bq > 0)
+    hipLaunchKernelGGL(plan_items_kernel, dim3(n_plans), dim3(kPlanThreads), 0,
+                       s, a, B, bq, bn, base.icap);
+  hipLaunchKernelGGL(plan_qmap_kernel, dim3(B, n_plans), dim3(256), 0, s, a, B);
+  timing_end(s);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ counts
+__global__ __launch_bounds__(256) void pyramid_counts_kernel(
+    RuleDev rule, const int* offsets, int B, int* keep_out) {
+  const int u = blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= B) return;
+  const int L = offsets[u + 1] - offsets[u];
+  int prev = L;
+  for (int l = 0; l < rule.n_layers; ++l) {
+    prev = rule_eval(rule, l, L, prev);
+    keep_out[(size_t)l * B + u] = prev;
+  }
+}
+
+hipError_t pyramid_counts_dev(const RuleDev& rule, const int* offsets, int B,
+                              int* keep_out, hipStream_t s) {
+  hipLaunchKernelGGL(pyramid_counts_kernel, dim3((B + 255) / 256), dim3(256), 0,
+                     s, rule, offsets, B, keep_out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ compaction
+__global__ __launch_bounds__(kPlanThreads) void compact_scan_kernel(
+    const int* keep, int B, int* offsets_out) {
+  __shared__ int sh[kPlanThreads];
+  block_scan(keep, offsets_out, B, sh);
+}
+
+// One wave per output row: find the user by binary search over offsets_out,
+// copy the row's bytes in 16-byte (or 4-byte) units, record the source row.
+__global__ __launch_bounds__(256) void compact_rows_kernel(
+    const char* values, int row_bytes, const int* offsets_in, int B,
+    const int* keep, const int* offsets_out, char* values_out, int* src_index,
+    int rows_cap) {
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= rows_cap || i >= offsets_out[B]) return;
+  int lo = 0, hi = B - 1;  // largest u with offsets_out[u] <= i
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (offsets_out[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  const int u = lo;
+  const int t = i - offsets_out[u];
+  const int src = offsets_in[u + 1] - keep[u] + t;
+  if (lane == 0 && src_index) src_index[i] = src;
+  const char* s = values + (size_t)src * row_bytes;
+  char* d = values_out + (size_t)i * row_bytes;
+  if ((row_bytes & 15) == 0) {
+    for (int b = lane * 16; b < row_bytes; b += 64 * 16)
+      *(i32x4*)(d + b) = *(const i32x4*)(s + b);
+  } else {
+    for (int b = lane * 4; b < row_bytes; b += 64 * 4)
+      *(int*)(d + b) = *(const int*)(s + b);
+  }
+}
+
+hipError_t pyramid_compact(const void* values, int row_bytes,
+                           const int* offsets_in, int B, int total_rows,
+                           const int* keep, void* values_out, int* offsets_out,
+                           int* src_index, hipStream_t s) {
+  timing_begin("pyramid_compact", s);
+  hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(kPlanThreads), 0, s,
+                     keep, B, offsets_out);
+  if (total_rows > 0)
+    hipLaunchKernelGGL(compact_rows_kernel, dim3((total_rows + 3) / 4),
+                       dim3(256), 0, s, (const char*)values, row_bytes,
+                       offsets_in, B, keep, offsets_out, (char*)values_out,
+                       src_index, total_rows);
+  timing_end(s);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ standalone
+// Items and row info for llatte_mla_attention from given offsets.
+__global__ __launch_bounds__(kPlanThreads) void attn_lens_kernel(
+    const int* kv_off, const int* hq_off, int B, int* kv_len, int* keep,
+    int* kvo, int* hqo, int* counts, int n_cand) {
+  for (int u = threadIdx.x; u < B; u += kPlanThreads) {
+    kv_len[u] = kv_off[u + 1] - kv_off[u];
+    keep[u] = hq_off[u + 1] - hq_off[u];
+    kvo[u] = kv_off[u];
+    hqo[u] = hq_off[u];
+  }
+  if (threadIdx.x == 0) {
+    kvo[B] = kv_off[B];
+    hqo[B] = hq_off[B];
+    counts[0] = kv_off[B];
+    counts[1] = hq_off[B];
+    counts[2] = B * n_cand + kv_off[B];
+    counts[3] = B * n_cand + hq_off[B];
+  }
+}
+
+hipError_t build_attn_plan(const int* kv_off, const int* hq_off, int B,
+                           int n_cand, int bq, int bn, const PlanBase& base,
+                           hipStream_t s) {
+  const LayerPlan P = base.layer(0);
+  PlanArgs a;
+  a.base = base;
+  a.n_plans = 1;
+  a.n_layers = 1;
+  a.nq[0] = n_cand;
+  timing_begin("plan", s);
+  hipLaunchKernelGGL(attn_lens_kernel, dim3(1), dim3(kPlanThreads), 0, s,
+                     kv_off, hq_off, B, P.kv_len, P.keep, P.kv_off, P.hq_off,
+                     P.counts, n_cand);
+  if (bq > 0)
+    hipLaunchKernelGGL(plan_items_kernel, dim3(1), dim3(kPlanThreads), 0, s, a,
+                       B, bq, bn, base.icap);
+  hipLaunchKernelGGL(plan_qmap_kernel, dim3(B, 1), dim3(256), 0, s, a, B);
+  timing_end(s);
+  return hipGetLastError();
+}
+
+}  // namespace llatte

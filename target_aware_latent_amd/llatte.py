@@ -1,0 +1,244 @@
+"""Thin Python binding of libllatte.so (ctypes). Argument marshalling only.
+
+Every function here forwards to the C ABI declared in include/llatte.h under
+the same name; every step of the forward pass runs in the library's HIP
+kernels. PyTorch provides device memory and the stream. If the library is
+not built, or the GPU path is unavailable, calls raise: there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libllatte.so")
+
+LLATTE_OK = 0
+LLATTE_ERR_INVALID_ARG = -1
+LLATTE_ERR_UNSUPPORTED = -2
+LLATTE_ERR_WORKSPACE = -3
+LLATTE_ERR_HIP = -4
+LLATTE_F32 = 0
+LLATTE_BF16 = 1
+LLATTE_NORM_PRE = 0
+LLATTE_NORM_POST = 1
+LLATTE_PYR_FIXED = 0
+LLATTE_PYR_HALVING = 1
+LLATTE_PYR_GEOMETRIC = 2
+LLATTE_MAX_LAYERS = 64
+
+_c_int = ctypes.c_int32
+_vp = ctypes.c_void_p
+
+
+class llatte_pyramid_rule(ctypes.Structure):
+    _fields_ = [("kind", _c_int), ("floor", _c_int), ("start", _c_int),
+                ("end", _c_int), ("values", _c_int * LLATTE_MAX_LAYERS)]
+
+
+class llatte_model_desc(ctypes.Structure):
+    _fields_ = [("d", _c_int), ("n_heads", _c_int), ("head_dim", _c_int),
+                ("rank", _c_int), ("d_ff", _c_int), ("n_layers", _c_int),
+                ("n_q", _c_int), ("d_ctx", _c_int), ("dtype", _c_int),
+                ("norm_mode", _c_int), ("latent_norm", _c_int),
+                ("eps", ctypes.c_float), ("pyramid", llatte_pyramid_rule),
+                ("n_seeds", _c_int), ("d_out", _c_int),
+                ("flags", ctypes.c_uint32)]
+
+
+class llatte_layer_weights(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("g1", "W_dkv", "g_c", "W_uq", "W_uk",
+                                   "W_uv", "W_o", "g2", "W1", "W2")]
+
+
+class llatte_weights(ctypes.Structure):
+    _fields_ = [("layers", ctypes.POINTER(llatte_layer_weights)),
+                ("W_q", _vp), ("seeds", _vp),
+                ("readout", llatte_layer_weights), ("W_p", _vp)]
+
+
+class llatte_attn_desc(ctypes.Structure):
+    _fields_ = [("n_heads", _c_int), ("rank", _c_int), ("n_cand", _c_int),
+                ("dtype", _c_int), ("scale", ctypes.c_float)]
+
+
+# name -> (restype, argtypes)
+_SIGS = {
+    "llatte_mla_forward": (_c_int, [
+        ctypes.POINTER(llatte_model_desc), ctypes.POINTER(llatte_weights),
+        _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+        ctypes.c_size_t, _vp]),
+    "llatte_mla_forward_workspace_size": (ctypes.c_size_t, [
+        ctypes.POINTER(llatte_model_desc), _c_int, _c_int, _c_int]),
+    "llatte_mla_attention": (_c_int, [
+        ctypes.POINTER(llatte_attn_desc), _vp, _vp, _vp, _vp, _c_int, _c_int,
+        _c_int, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "llatte_mla_attention_workspace_size": (ctypes.c_size_t, [
+        ctypes.POINTER(llatte_attn_desc), _c_int, _c_int, _c_int]),
+    "llatte_pyramid_compact": (_c_int, [
+        _vp, _c_int, _c_int, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp]),
+    "llatte_pyramid_counts": (_c_int, [
+        ctypes.POINTER(llatte_pyramid_rule), _c_int, _vp, _c_int, _vp, _vp]),
+    "llatte_pyramid_counts_host": (_c_int, [
+        ctypes.POINTER(llatte_pyramid_rule), _c_int,
+        ctypes.POINTER(_c_int), _c_int, ctypes.POINTER(_c_int)]),
+    "llatte_token_embed": (_c_int, [
+        _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
+        ctypes.c_size_t, _vp]),
+    "llatte_token_embed_workspace_size": (ctypes.c_size_t, [
+        _c_int, _c_int, _c_int]),
+    "llatte_last_error": (ctypes.c_char_p, []),
+    "llatte_version": (_c_int, []),
+    "llatte_kernel_timing_enable": (None, [_c_int]),
+    "llatte_kernel_timing_read": (_c_int, [
+        ctypes.c_char_p, _c_int, ctypes.POINTER(_c_int),
+        ctypes.POINTER(ctypes.c_double), _c_int]),
+    "llatte_kernel_timing_reset": (None, []),
+}
+
+_lib = None
+
+
+def lib():
+    """Load libllatte.so (built in place by target_aware_latent_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run "
+                "`python -m target_aware_latent_amd.build` first")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+class LlatteError(RuntimeError):
+    def __init__(self, status, where):
+        msg = lib().llatte_last_error().decode(errors="replace")
+        super().__init__(f"{where} returned {status}: {msg}")
+        self.status = status
+
+
+def _check(status, where):
+    if status != LLATTE_OK:
+        raise LlatteError(status, where)
+
+
+def _p(t):
+    """Device pointer of a tensor (or NULL for None)."""
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ------------------------------------------------------------------ C ABI
+
+def llatte_mla_forward_workspace_size(desc, B, total_rows, max_len):
+    return lib().llatte_mla_forward_workspace_size(ctypes.byref(desc), B,
+                                                   total_rows, max_len)
+
+
+def llatte_mla_forward(desc, weights, hist_values, hist_offsets, B, total_rows,
+                       max_len, cand_x, ctx, out_cand, out_hist,
+                       out_hist_offsets, out_emb, workspace, stream=None):
+    st = lib().llatte_mla_forward(
+        ctypes.byref(desc), ctypes.byref(weights), _p(hist_values),
+        _p(hist_offsets), B, total_rows, max_len, _p(cand_x), _p(ctx),
+        _p(out_cand), _p(out_hist), _p(out_hist_offsets), _p(out_emb),
+        _p(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(st, "llatte_mla_forward")
+
+
+def llatte_mla_attention_workspace_size(adesc, B, Mtot, Ktot):
+    return lib().llatte_mla_attention_workspace_size(ctypes.byref(adesc), B,
+                                                     Mtot, Ktot)
+
+
+def llatte_mla_attention(adesc, q_lat, c_lat, kv_offsets, hq_offsets, B, Mtot,
+                         Ktot, out, lse, workspace, stream=None):
+    st = lib().llatte_mla_attention(
+        ctypes.byref(adesc), _p(q_lat), _p(c_lat), _p(kv_offsets),
+        _p(hq_offsets), B, Mtot, Ktot, _p(out), _p(lse), _p(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "llatte_mla_attention")
+
+
+def llatte_pyramid_compact(values, row_elems, dt, offsets_in, B, total_rows,
+                           keep, values_out, offsets_out, src_index,
+                           stream=None):
+    st = lib().llatte_pyramid_compact(
+        _p(values), row_elems, dt, _p(offsets_in), B, total_rows, _p(keep),
+        _p(values_out), _p(offsets_out), _p(src_index), _stream(stream))
+    _check(st, "llatte_pyramid_compact")
+
+
+def llatte_pyramid_counts(rule, n_layers, offsets_in, B, keep_out, stream=None):
+    st = lib().llatte_pyramid_counts(ctypes.byref(rule), n_layers,
+                                     _p(offsets_in), B, _p(keep_out),
+                                     _stream(stream))
+    _check(st, "llatte_pyramid_counts")
+
+
+def llatte_pyramid_counts_host(rule, n_layers, lengths):
+    """Host evaluation of a pyramid rule: returns a list of n_layers lists."""
+    B = len(lengths)
+    arr = (_c_int * B)(*[int(x) for x in lengths])
+    out = (_c_int * (B * n_layers))()
+    st = lib().llatte_pyramid_counts_host(ctypes.byref(rule), n_layers, arr, B,
+                                          out)
+    _check(st, "llatte_pyramid_counts_host")
+    return [list(out[l * B:(l + 1) * B]) for l in range(n_layers)]
+
+
+def llatte_token_embed_workspace_size(d, d_sem, dt):
+    return lib().llatte_token_embed_workspace_size(d, d_sem, dt)
+
+
+def llatte_token_embed(table, V, rows, sem, W_s, n, d, d_sem, dt, out,
+                       workspace, stream=None):
+    st = lib().llatte_token_embed(
+        _p(table), V, _p(rows), _p(sem), _p(W_s), n, d, d_sem, dt, _p(out),
+        _p(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(st, "llatte_token_embed")
+
+
+def llatte_last_error():
+    return lib().llatte_last_error().decode(errors="replace")
+
+
+def llatte_version():
+    return lib().llatte_version()
+
+
+def llatte_kernel_timing_enable(on):
+    lib().llatte_kernel_timing_enable(1 if on else 0)
+
+
+def llatte_kernel_timing_reset():
+    lib().llatte_kernel_timing_reset()
+
+
+def llatte_kernel_timing_read(cap=64):
+    """{kernel name: (launches, total ms)} of the timed launches so far."""
+    stride = 64
+    names = ctypes.create_string_buffer(stride * cap)
+    counts = (_c_int * cap)()
+    ms = (ctypes.c_double * cap)()
+    n = lib().llatte_kernel_timing_read(names, stride, counts, ms, cap)
+    out = {}
+    for i in range(n):
+        nm = names.raw[i * stride:(i + 1) * stride].split(b"\0", 1)[0].decode()
+        out[nm] = (counts[i], ms[i])
+    return out

@@ -1,0 +1,130 @@
+"""Marshalling helpers around llatte_mla_forward: descriptor, device weights,
+buffers. No arithmetic of the method happens here; it all runs in the HIP
+library behind the C ABI."""
+import ctypes
+
+import numpy as np
+import torch
+
+from . import llatte as C
+
+
+def make_desc(cfg):
+    """llatte_model_desc from a workload description with the attributes
+    d, h, dk, r, N, n_q, d_c, dtype ('f32'/'bf16'), norm_mode ('pre'/'post'),
+    latent_norm, eps, pyramid (kind/values/floor/start/end), n_seeds, d_out."""
+    d = C.llatte_model_desc()
+    d.d, d.n_heads, d.head_dim, d.rank = cfg.d, cfg.h, cfg.dk, cfg.r
+    d.d_ff = 4 * cfg.d
+    d.n_layers = cfg.N
+    d.n_q, d.d_ctx = cfg.n_q, cfg.d_c
+    d.dtype = C.LLATTE_BF16 if cfg.dtype == "bf16" else C.LLATTE_F32
+    d.norm_mode = C.LLATTE_NORM_PRE if cfg.norm_mode == "pre" else C.LLATTE_NORM_POST
+    d.latent_norm = 1 if cfg.latent_norm else 0
+    d.eps = cfg.eps
+    rule = cfg.pyramid
+    if rule.kind == "fixed":
+        d.pyramid.kind = C.LLATTE_PYR_FIXED
+        for i, v in enumerate(rule.values):
+            d.pyramid.values[i] = int(v)
+    elif rule.kind == "halving":
+        d.pyramid.kind = C.LLATTE_PYR_HALVING
+        d.pyramid.floor = int(rule.floor)
+    elif rule.kind == "geometric":
+        d.pyramid.kind = C.LLATTE_PYR_GEOMETRIC
+        d.pyramid.start, d.pyramid.end = int(rule.start), int(rule.end)
+    else:
+        raise ValueError(rule.kind)
+    d.n_seeds, d.d_out = cfg.n_seeds, cfg.d_out
+    d.flags = 0
+    return d
+
+
+def torch_dtype(cfg):
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+class DeviceModel:
+    """Weights of one model resident on the GPU plus the ctypes structs that
+    point at them (kept alive together)."""
+
+    _LAYER_KEYS = ("g1", "W_dkv", "g_c", "W_uq", "W_uk", "W_uv", "W_o", "g2",
+                   "W1", "W2")
+
+    def __init__(self, cfg, W, device="cuda"):
+        self.cfg = cfg
+        self.desc = make_desc(cfg)
+        self.device = device
+        self._keep = []
+        dt = torch_dtype(cfg)
+
+        def mat(a):
+            t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+            t = t.to(device=device).to(dt).contiguous()
+            self._keep.append(t)
+            return t
+
+        def vec(a):
+            t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+            self._keep.append(t)
+            return t
+
+        def layer(Wl):
+            s = C.llatte_layer_weights()
+            for k in self._LAYER_KEYS:
+                t = vec(Wl[k]) if k.startswith("g") else mat(Wl[k])
+                setattr(s, k, t.data_ptr())
+            return s
+
+        self._layers = (C.llatte_layer_weights * cfg.N)(
+            *[layer(Wl) for Wl in W["layers"]])
+        w = C.llatte_weights()
+        w.layers = ctypes.cast(self._layers, ctypes.POINTER(C.llatte_layer_weights))
+        if cfg.n_q > 0:
+            w.W_q = mat(W["W_q"]).data_ptr()
+        if cfg.n_seeds > 0:
+            w.seeds = vec(W["seeds"]).data_ptr()
+            w.readout = layer(W["readout"])
+            w.W_p = mat(W["W_p"]).data_ptr()
+        self.weights = w
+        self._ws = None
+
+    def workspace(self, B, total, max_len):
+        n = C.llatte_mla_forward_workspace_size(self.desc, B, total, max_len)
+        if n == 0:
+            raise C.LlatteError(-1, "llatte_mla_forward_workspace_size")
+        if self._ws is None or self._ws.numel() < n:
+            self._ws = torch.empty(n, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def out_hist_rows(self, lengths):
+        keep = C.llatte_pyramid_counts_host(self.desc.pyramid, self.cfg.N,
+                                            list(lengths))
+        return int(sum(keep[-1]))
+
+    def alloc_outputs(self, lengths):
+        cfg, dev = self.cfg, self.device
+        B = len(lengths)
+        out = {
+            "cand": (torch.empty(B * cfg.n_q, cfg.d, device=dev)
+                     if cfg.n_q else None),
+            "hist": torch.empty(max(self.out_hist_rows(lengths), 1), cfg.d, device=dev),
+            "hist_offsets": torch.empty(B + 1, dtype=torch.int32, device=dev),
+            "emb": (torch.empty(B, cfg.d_out, device=dev) if cfg.n_seeds else None),
+        }
+        return out
+
+    def forward(self, hist, offsets, lengths, cand=None, ctx=None, out=None,
+                stream=None):
+        """hist [total, d] float32 and offsets [B+1] int32 on the device;
+        lengths: host list of the per-user lengths (sizes only)."""
+        B = len(lengths)
+        total = int(sum(lengths))
+        max_len = int(max(lengths))
+        if out is None:
+            out = self.alloc_outputs(lengths)
+        ws = self.workspace(B, total, max_len)
+        C.llatte_mla_forward(self.desc, self.weights, hist, offsets, B, total,
+                             max_len, cand, ctx, out["cand"], out["hist"],
+                             out["hist_offsets"], out["emb"], ws, stream)
+        return out

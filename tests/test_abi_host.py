@@ -1,0 +1,121 @@
+"""C-ABI library checks that need no GPU: it loads, exports every symbol the
+header declares, validates arguments before launching anything, and its host
+pyramid evaluation agrees with the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import llatte_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "llatte.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from target_aware_latent_amd import llatte
+    llatte.lib()
+    return llatte
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(llatte_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for must in ("llatte_mla_forward", "llatte_mla_attention",
+                 "llatte_pyramid_compact", "llatte_pyramid_counts",
+                 "llatte_token_embed", "llatte_mla_forward_workspace_size"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    lib = L.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in L._SIGS, f"binding lacks {name}"
+
+
+def test_no_symbol_is_named_after_the_oracle():
+    so = open(os.path.join(ROOT, "target_aware_latent_amd", "libllatte.so"), "rb").read()
+    assert b"oracle" not in so
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_workspace_size_positive_for_workloads(L, name):
+    from target_aware_latent_amd.model import make_desc
+    cfg = synth.get_config(name)
+    d = make_desc(cfg)
+    L_ = cfg.L or cfg.len_range[1]
+    assert L.llatte_mla_forward_workspace_size(d, cfg.B, cfg.B * L_, L_) > 0
+
+
+def test_invalid_descriptors_rejected_on_host(L):
+    from target_aware_latent_amd.model import make_desc
+    cfg = synth.get_config("c2")
+    good = make_desc(cfg)
+    assert L.llatte_mla_forward_workspace_size(good, 4, 100, 50) > 0
+    for field, val in [("d_ff", 3 * cfg.d), ("rank", 96), ("dtype", 7),
+                       ("n_layers", 0), ("head_dim", 12), ("flags", 1)]:
+        d = make_desc(cfg)
+        setattr(d, field, val)
+        assert L.llatte_mla_forward_workspace_size(d, 4, 100, 50) == 0, field
+    d = make_desc(cfg)
+    d.pyramid.values[0] = 0     # zero before the last layer
+    assert L.llatte_mla_forward_workspace_size(d, 4, 100, 50) == 0
+    # total_rows < B (some user would be empty)
+    assert L.llatte_mla_forward_workspace_size(good, 4, 3, 50) == 0
+
+
+def test_forward_argument_errors_return_status_without_launch(L):
+    from target_aware_latent_amd.model import make_desc
+    cfg = synth.get_config("c2")
+    d = make_desc(cfg)
+    w = L.llatte_weights()
+    st = L.lib().llatte_mla_forward(ctypes.byref(d), ctypes.byref(w), None, None,
+                                    4, 100, 50, None, None, None, None, None,
+                                    None, None, 0, None)
+    assert st == L.LLATTE_ERR_INVALID_ARG
+    assert "NULL" in L.llatte_last_error()
+    ad = L.llatte_attn_desc(4, 96, 0, L.LLATTE_BF16, 0.125)
+    st = L.lib().llatte_mla_attention(ctypes.byref(ad), None, None, None, None,
+                                      2, 10, 10, None, None, None, 0, None)
+    assert st == L.LLATTE_ERR_UNSUPPORTED
+    st = L.lib().llatte_pyramid_compact(None, 8, L.LLATTE_F32, None, 2, 10,
+                                        None, None, None, None, None)
+    assert st == L.LLATTE_ERR_INVALID_ARG
+
+
+def _rule(L, r):
+    from target_aware_latent_amd.model import make_desc
+    cfg = synth.Config("x", B=1, L=1, len_range=None, d=8, h=1, dk=8, r=8,
+                       n_q=0, d_c=0, N=1, pyramid=r, dtype="f32")
+    return make_desc(cfg).pyramid
+
+
+@pytest.mark.parametrize("rule,N", [
+    (synth.PyramidRule("halving", floor=64), 4),
+    (synth.PyramidRule("halving", floor=3), 7),
+    (synth.PyramidRule("geometric", start=1600, end=50), 12),
+    (synth.PyramidRule("fixed", (1600, 800, 400, 200, 100, 50)), 6),
+    (synth.PyramidRule("fixed", (30, 30, 7, 0)), 4),
+])
+def test_host_pyramid_counts_match_oracle(L, rule, N):
+    rng = np.random.default_rng(3)
+    lengths = np.concatenate([[1, 2, 63, 64, 65, 1600], rng.integers(1, 2000, 200)])
+    got = np.array(L.llatte_pyramid_counts_host(_rule(L, rule), N, lengths))
+    assert np.array_equal(got, O.pyramid_counts(rule, lengths, N))
+
+
+def test_host_pyramid_counts_c4_lengths(L):
+    cfg = synth.get_config("c4")
+    lengths = synth.generate(cfg)["inputs"]["lengths"]
+    got = np.array(L.llatte_pyramid_counts_host(_rule(L, cfg.pyramid), cfg.N, lengths))
+    assert np.array_equal(got, O.pyramid_counts(cfg.pyramid, lengths, cfg.N))

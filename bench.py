@@ -1,0 +1,242 @@
+"""Throughput of the LLaTTE target-aware MLA forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3]
+
+One step is one llatte_mla_forward over one batch of the workload (all
+layers, the pyramid, the readout), inputs and weights already resident in
+HBM. Prints ONE JSON line: user-sequences/s as `value`, TFLOP/s of the fixed
+absorbed-form FLOP count (and its fraction of the bf16 MFMA peak), the
+roofline of the dominant kernel (HIP events around each of its launches,
+recorded by the library on the launch stream, over a second pass of the same
+K steps), and the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (vector / MFMA dense)
+PEAK_HBM_GBS = 8000.0
+
+METRIC = ("user-sequences/sec + TFLOP/s (% MFMA bf16 peak), MLA stack at "
+          "L=1600, 1 GPU")
+
+WORKLOAD_TEXT = {
+    "c1": "c1: 1 layer fp32, B=4, L=32, d=64, 2x32 heads, r=16, 4 candidates",
+    "c2": "c2: online ranker, 3 layers bf16, B=256, L=400, d=256, 4x64, r=64, "
+          "16 candidates, pyramid 400-200-100",
+    "c3": "c3: upstream user model, 6 layers bf16, B=64, L=1600, d=512, 8x64 "
+          "heads, r=128, pyramid 1600-800-400-200-100-50, 4-seed readout to 2048",
+    "c4": "c4: jagged batch, 4 layers bf16, 128 users L~U[200,1600], d=256, "
+          "4x64, r=64, 8 candidates, halving pyramid floor 64",
+}
+
+
+def layer_counts(cfg, lengths):
+    """Per layer (incl. readout): (sum K, sum n, query rows M, allowed pairs)."""
+    from target_aware_latent_amd import llatte as C
+    from target_aware_latent_amd.model import make_desc
+    keep = np.array(C.llatte_pyramid_counts_host(make_desc(cfg).pyramid, cfg.N,
+                                                 list(lengths)), dtype=np.int64)
+    out = []
+    K = np.asarray(lengths, dtype=np.int64)
+    for l in range(cfg.N + (1 if cfg.n_seeds else 0)):
+        n = keep[l] if l < cfg.N else np.zeros_like(K)
+        nq = cfg.n_q if l < cfg.N else cfg.n_seeds
+        pairs = int(np.sum(n * (K - n) + n * (n + 1) // 2 + nq * K))
+        out.append((int(K.sum()), int(n.sum()), int(n.sum()) + cfg.B * nq, pairs))
+        K = n
+    return out
+
+
+def kernel_flops(cfg, lengths):
+    """Algorithmic FLOPs per step by kernel label: 2mnk per product and
+    4*r*h per allowed (query, key) pair (absorbed form)."""
+    d, h, dk, r, dff = cfg.d, cfg.h, cfg.dk, cfg.r, 4 * cfg.d
+    f = {}
+    add = lambda k, v: f.__setitem__(k, f.get(k, 0) + v)
+    for Ks, ns, M, pairs in layer_counts(cfg, lengths):
+        add("gemm_down", 2 * Ks * d * r)
+        add("gemm_q", 2 * M * d * h * dk)
+        add("gemm_absorb_uk", 2 * M * h * dk * r)
+        add("attention_bf16" if cfg.dtype == "bf16" else "attention_f32",
+            4 * r * h * pairs)
+        add("gemm_absorb_uv", 2 * M * h * r * dk)
+        add("gemm_out", 2 * M * h * dk * d)
+        add("gemm_ffn1", 2 * M * d * dff)
+        add("gemm_ffn2", 2 * M * dff * d)
+    if cfg.n_q:
+        add("gemm_fusion", 2 * cfg.B * cfg.n_q * (d + cfg.d_c) * d)
+    if cfg.n_seeds:
+        add("gemm_readout", 2 * cfg.B * cfg.n_seeds * d * cfg.d_out)
+    return f
+
+
+def absorbed_flops(cfg, lengths):
+    return sum(kernel_flops(cfg, lengths).values())
+
+
+def non_absorbed_flops(cfg, lengths):
+    d, h, dk, r, dff = cfg.d, cfg.h, cfg.dk, cfg.r, 4 * cfg.d
+    t = 0
+    for Ks, ns, M, pairs in layer_counts(cfg, lengths):
+        t += 2 * Ks * d * r + 2 * M * d * h * dk + 2 * (2 * Ks * r * h * dk)
+        t += 4 * dk * h * pairs + 2 * M * h * dk * d + 2 * (2 * M * d * dff)
+    if cfg.n_q:
+        t += 2 * cfg.B * cfg.n_q * (d + cfg.d_c) * d
+    if cfg.n_seeds:
+        t += 2 * cfg.B * cfg.n_seeds * d * cfg.d_out
+    return t
+
+
+def cpu_baseline(prob, budget_s=12.0):
+    """The oracle as it stands, in fp32 on the host cores, on the first users
+    of the batch until about budget_s seconds of work (at least one user)."""
+    from oracle import llatte_oracle as O
+    cfg, I, W = prob["cfg"], prob["inputs"], prob["weights"]
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = sum(p.get("num_threads", 0) for p in threadpool_info()
+                      if p.get("user_api") == "blas") or None
+    except Exception:
+        pass
+    users = 0
+    t0 = time.perf_counter()
+    while users < cfg.B:
+        O.forward(cfg, W, I["hist"], I["offsets"], I.get("cand"), I.get("ctx"),
+                  users=[users], dtype=np.float32)
+        users += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": users / dt, "unit": "user-seq/s",
+            "cores": threads or len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{users} of {cfg.B} users of the same workload, fp32 "
+                      f"oracle (non-absorbed definition), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-times", action="store_true")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per launch of the "
+                         "dominant kernel ({'kernel':..., 'bytes':...})")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU "
+              "path (users shard across GPUs with no exchange; see the design "
+              "notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from target_aware_latent_amd import llatte as C
+    from target_aware_latent_amd.model import DeviceModel
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    cfg = synth.get_config(args.config)
+    if cfg.semantic is not None:
+        raise SystemExit("the token-build workload is benchmarked separately")
+    prob = synth.generate(cfg, seed=0)
+    I = prob["inputs"]
+    lengths = [int(x) for x in I["lengths"]]
+    model = DeviceModel(cfg, prob["weights"])
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    hist = dev(I["hist"])
+    offs = dev(I["offsets"].astype(np.int32))
+    cand = dev(I["cand"]) if cfg.n_q else None
+    ctx = dev(I["ctx"]) if (cfg.n_q and cfg.d_c) else None
+    out = model.alloc_outputs(lengths)
+    stream = torch.cuda.current_stream()
+    step = lambda: model.forward(hist, offs, lengths, cand, ctx, out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1)
+    ms_step = ms / args.steps
+    value = cfg.B / (ms_step / 1e3)
+    F = absorbed_flops(cfg, lengths)
+    Fna = non_absorbed_flops(cfg, lengths)
+    tflops = F / (ms_step / 1e3) / 1e12
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+
+    roofline = None
+    kernels = {}
+    if not args.no_kernel_times:
+        C.llatte_kernel_timing_reset()
+        C.llatte_kernel_timing_enable(True)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        kt = C.llatte_kernel_timing_read()
+        C.llatte_kernel_timing_enable(False)
+        kf = kernel_flops(cfg, lengths)
+        for name, (cnt, tot) in kt.items():
+            e = {"launches_per_step": cnt / args.steps, "ms_per_step": tot / args.steps}
+            if name in kf:
+                e["tflops"] = kf[name] / (tot / args.steps / 1e3) / 1e12
+            kernels[name] = e
+        dom = max((n for n in kt if n in kf), key=lambda n: kt[n][1])
+        cnt, tot = kt[dom]
+        per_launch_flops = kf[dom] * args.steps / cnt
+        avg_s = tot / cnt / 1e3
+        achieved = per_launch_flops / avg_s / 1e12
+        traffic = None
+        if args.traffic and os.path.exists(args.traffic):
+            tr = json.load(open(args.traffic))
+            if tr.get("kernel") == dom:
+                traffic = tr.get("bytes")
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                    "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4), "traffic": traffic,
+                    "flops_per_launch": per_launch_flops,
+                    "avg_launch_ms": round(tot / cnt, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(prob)
+
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "user-seq/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, N(0,1/fan_in) weights)",
+        "config": {"workload": WORKLOAD_TEXT.get(cfg.name, cfg.name),
+                   "global_batch": cfg.B, "seq_len": cfg.L or cfg.len_range[1],
+                   "parallelism": "single GPU"},
+        "tflops": round(tflops, 2), "pct_peak": round(100 * tflops / peak, 2),
+        "flops_per_step_absorbed": F, "flops_per_step_non_absorbed": Fna,
+        "tflops_non_absorbed_count": round(Fna / (ms_step / 1e3) / 1e12, 2),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+    }
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

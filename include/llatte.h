@@ -198,7 +198,7 @@ size_t llatte_mla_forward_workspace_size(const llatte_model_desc* desc,
  *   kv_offsets         [B+1] int32;  hq_offsets [B+1] int32 (device)
  *   Mtot               host: B*n_cand + hq_offsets[B]
  *   Ktot               host: kv_offsets[B]
- *   out                [Mtot, h, r] dtype (normalised output)
+ *   out                [Mtot, h, r] float32 (normalised output)
  *   lse                [Mtot, h] float32 or NULL
  *   workspace          >= llatte_mla_attention_workspace_size(...) bytes
  * BF16 requires r in {64, 128, 256}; F32 accepts 1 <= r <= 256.

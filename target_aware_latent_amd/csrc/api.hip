@@ -431,6 +431,7 @@ static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
     a.q = w.ql;
     a.c = w.Cl;
     a.out = w.ol;
+    a.out_f32 = false;
     a.lse = nullptr;
     a.h = S.h;
     a.r = S.r;
@@ -729,6 +730,7 @@ llatte_status llatte_mla_attention(
   ap.q = q_lat;
   ap.c = c_lat;
   ap.out = out;
+  ap.out_f32 = true;
   ap.lse = lse;
   ap.h = a->n_heads;
   ap.r = a->rank;

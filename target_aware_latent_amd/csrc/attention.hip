@@ -33,7 +33,7 @@ __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
 
-template <int R, int EPW>
+template <int R, int EPW, typename OutT>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnParams p, int HG,
                                                         int hg_shift) {
   constexpr int BN = kAttnBN;        // keys per tile
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnParams p, int HG,
   }
 
   // normalise and store: lane holds out[e][rb*16 + 4g .. +3]
-  bf16* O = (bf16*)p.out;
+  OutT* O = (OutT*)p.out;
 #pragma unroll
   for (int eb = 0; eb < NEB; ++eb) {
     if (!valid[eb]) continue;
@@ -230,13 +230,16 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnParams p, int HG,
     const int ql = e >> hg_shift, hl = e & (HG - 1);
     const size_t orow = (size_t)(qrow0 + ql) * p.h + h0 + hl;
     const float inv = 1.f / l_run[eb];
-    bf16* op = O + orow * R + g * 4;
+    OutT* op = O + orow * R + g * 4;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const f32x4 v = acc_o[rb][eb];
-      *(bf16x4*)(op + rb * 16) =
-          bf16x4{to_bf16(v[0] * inv), to_bf16(v[1] * inv), to_bf16(v[2] * inv),
-                 to_bf16(v[3] * inv)};
+      if constexpr (sizeof(OutT) == 2)
+        *(bf16x4*)(op + rb * 16) =
+            bf16x4{to_bf16(v[0] * inv), to_bf16(v[1] * inv), to_bf16(v[2] * inv),
+                   to_bf16(v[3] * inv)};
+      else
+        *(f32x4*)(op + rb * 16) = v * inv;
     }
     if (p.lse && g == 0) p.lse[orow] = (m_run[eb] + __log2f(l_run[eb])) * kLn2;
   }
@@ -321,8 +324,12 @@ static void launch_bf16(const AttnParams& p, hipStream_t s) {
   int shift = 0;
   while ((1 << shift) < hg) ++shift;
   dim3 grid(p.items_cap, p.h / hg);
-  hipLaunchKernelGGL((attn_bf16_kernel<R, EPW>), grid, dim3(256), 0, s, p, hg,
-                     shift);
+  if (p.out_f32)
+    hipLaunchKernelGGL((attn_bf16_kernel<R, EPW, float>), grid, dim3(256), 0, s,
+                       p, hg, shift);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<R, EPW, bf16>), grid, dim3(256), 0, s,
+                       p, hg, shift);
 }
 
 hipError_t attention(const AttnParams& p, bool is_bf16, hipStream_t s) {

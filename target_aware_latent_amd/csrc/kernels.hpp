@@ -158,7 +158,8 @@ hipError_t pyramid_compact(const void* values, int row_bytes,
 struct AttnParams {
   const void* q;      // [M, h, r]
   const void* c;      // [Ktot, r]
-  void* out;          // [M, h, r]
+  void* out;          // [M, h, r]: dtype, or float32 when out_f32
+  bool out_f32;
   float* lse;         // [M, h] or null
   int h, r;
   float scale;

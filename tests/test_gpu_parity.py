@@ -149,7 +149,7 @@ def run_attention(dt, h, r, K, n, n_cand, scale=None, seed=0, q=None, C=None):
     ad = L().llatte_attn_desc(h, r, n_cand, code, scale)
     ws = torch.empty(L().llatte_mla_attention_workspace_size(ad, B, Mtot, int(kv_off[-1])),
                      dtype=torch.uint8, device="cuda")
-    out = torch.full((max(Mtot, 1), h, r), float("nan"), dtype=tdt, device="cuda")
+    out = torch.full((max(Mtot, 1), h, r), float("nan"), device="cuda")
     lse = torch.full((max(Mtot, 1), h), float("nan"), device="cuda")
     L().llatte_mla_attention(ad, dev(q, tdt), dev(C, tdt), idev(kv_off), idev(hq_off),
                              B, Mtot, int(kv_off[-1]), out, lse, ws)

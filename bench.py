@@ -66,10 +66,14 @@ def kernel_flops(cfg, lengths):
     for Ks, ns, M, pairs in layer_counts(cfg, lengths):
         add("gemm_down", 2 * Ks * d * r)
         add("gemm_q", 2 * M * d * h * dk)
-        add("gemm_absorb_uk", 2 * M * h * dk * r)
-        add("attention_bf16" if cfg.dtype == "bf16" else "attention_f32",
-            4 * r * h * pairs)
-        add("gemm_absorb_uv", 2 * M * h * r * dk)
+        if cfg.dtype == "bf16":
+            # the attention kernel also applies W_uk (prologue) and W_uv
+            # (epilogue) of the absorbed form
+            add("attention_mfma", 4 * r * h * pairs + 2 * (2 * M * h * dk * r))
+        else:
+            add("gemm_absorb_uk", 2 * M * h * dk * r)
+            add("attention_f32", 4 * r * h * pairs)
+            add("gemm_absorb_uv", 2 * M * h * r * dk)
         add("gemm_out", 2 * M * h * dk * d)
         add("gemm_ffn1", 2 * M * d * dff)
         add("gemm_ffn2", 2 * M * dff * d)
@@ -155,6 +159,7 @@ def main():
     I = prob["inputs"]
     lengths = [int(x) for x in I["lengths"]]
     model = DeviceModel(cfg, prob["weights"])
+    model.pack()
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     hist = dev(I["hist"])
     offs = dev(I["offsets"].astype(np.int32))

@@ -144,7 +144,17 @@ typedef struct {
  * then emb_u = flatten(seed outputs of u, seed-major) W_p ([LLaTTE] A.2
  * sequence summaries, with a linear map).
  *
- *   desc, w            host pointers
+ * Precision of the BF16 path: matrices and activations entering matrix
+ * products are bf16 with fp32 accumulation, except inside the attention core
+ * where the latent C, the latent queries, the softmax weights and the latent
+ * output are fp16 (normalised values; more mantissa at the same rate); the
+ * residual stream, norms and softmax statistics are fp32.
+ *
+ *   desc               host pointer
+ *   w                  host pointer to device weights; may be NULL when
+ *                      packed_weights is given
+ *   packed_weights     NULL, or a blob written by llatte_pack_weights for
+ *                      this desc (saves re-packing the weights every call)
  *   hist_values        [total_rows, d] float32
  *   hist_offsets       [B+1] int32, hist_offsets[0] = 0, strictly increasing
  *   B                  users (>= 1)
@@ -160,14 +170,26 @@ typedef struct {
  *   out_emb            [B, d_out] float32 (NULL iff n_seeds == 0)
  *   workspace          >= llatte_mla_forward_workspace_size(...) bytes,
  *                      256-byte aligned
+ * BF16 requires rank in {64, 128, 256} and head_dim in {32, 64, 128};
+ * d and rank must be <= 1024.
  * ---------------------------------------------------------------------- */
 llatte_status llatte_mla_forward(
     const llatte_model_desc* desc, const llatte_weights* w,
-    const float* hist_values, const int32_t* hist_offsets, int32_t B,
-    int32_t total_rows, int32_t max_len, const float* cand_x,
-    const float* ctx, float* out_cand, float* out_hist,
-    int32_t* out_hist_offsets, float* out_emb, void* workspace,
-    size_t workspace_bytes, void* stream);
+    const void* packed_weights, const float* hist_values,
+    const int32_t* hist_offsets, int32_t B, int32_t total_rows,
+    int32_t max_len, const float* cand_x, const float* ctx, float* out_cand,
+    float* out_hist, int32_t* out_hist_offsets, float* out_emb,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Packed weights: every matrix of `w` transposed into the layout the kernels
+ * read (K-contiguous), W_uv per head in fp16 on the BF16 path, gains and
+ * seeds copied. The blob depends only on desc and w; write it once and pass
+ * it to every llatte_mla_forward call. `packed` is device memory of at least
+ * llatte_packed_weights_size(desc) bytes (0 = invalid desc). */
+size_t llatte_packed_weights_size(const llatte_model_desc* desc);
+llatte_status llatte_pack_weights(const llatte_model_desc* desc,
+                                  const llatte_weights* w, void* packed,
+                                  size_t packed_bytes, void* stream);
 
 /* Workspace bytes needed by llatte_mla_forward for these sizes (host only;
  * returns 0 if the arguments are invalid). */

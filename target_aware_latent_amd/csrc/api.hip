@@ -211,8 +211,9 @@ static llatte_status make_shapes(const llatte_model_desc* dsc, int B, int total,
   if (S->ns > 0 && (S->dout < 1 || S->dout % 4))
     return fail(LLATTE_ERR_INVALID_ARG, "d_out must be a positive multiple of 4");
   if (S->bf16) {
-    if (S->r != 64 && S->r != 128 && S->r != 256)
-      return fail(LLATTE_ERR_UNSUPPORTED, "bf16 path needs rank in {64, 128, 256}");
+    if (!attn_fused_supported(S->h, S->r, S->dk))
+      return fail(LLATTE_ERR_UNSUPPORTED,
+                  "bf16 path needs rank in {64, 128, 256} and head_dim in {32, 64, 128}");
   } else if (S->r > 256) {
     return fail(LLATTE_ERR_UNSUPPORTED, "f32 path needs rank <= 256");
   }
@@ -256,20 +257,53 @@ static llatte_status make_shapes(const llatte_model_desc* dsc, int B, int total,
   return LLATTE_OK;
 }
 
-// Workspace layout of the forward pass.
-struct LayerWT {
-  void *Wdkv, *Wuq, *Wuv, *Wo, *W1, *W2;  // transposed copies (K-contiguous)
+// Packed weights: matrices transposed to K-contiguous layout (the GEMM's
+// B operand), W_uv per head transposed and in fp16 for the fused attention
+// epilogue on the bf16 path, gains and seeds copied. One blob, written by
+// llatte_pack_weights (or into the workspace by every forward call).
+struct PackedLayer {
+  float *g1, *g_c, *g2;
+  void *Wdkv, *Wuq, *Wuk, *Wuv, *Wo, *W1, *W2;
 };
+struct Packed {
+  std::vector<PackedLayer> L;  // N layers (+ readout)
+  void *WqT, *WpT;
+  float* seeds;
+};
+
+static size_t layout_packed(const Shapes& S, void* base, Packed* P) {
+  Arena ar(base);
+  const size_t e = S.esz;
+  P->L.resize(S.NP);
+  for (int l = 0; l < S.NP; ++l) {
+    PackedLayer& q = P->L[l];
+    q.g1 = ar.take<float>(S.d);
+    q.g_c = ar.take<float>(S.r);
+    q.g2 = ar.take<float>(S.d);
+    q.Wdkv = ar.take<char>((size_t)S.d * S.r * e);
+    q.Wuq = ar.take<char>((size_t)S.d * S.hd * e);
+    q.Wuk = ar.take<char>((size_t)S.r * S.hd * e);
+    q.Wuv = ar.take<char>((size_t)S.r * S.hd * e);   // f16 on the bf16 path
+    q.Wo = ar.take<char>((size_t)S.hd * S.d * e);
+    q.W1 = ar.take<char>((size_t)S.d * S.dff * e);
+    q.W2 = ar.take<char>((size_t)S.dff * S.d * e);
+  }
+  P->WqT = S.nq ? ar.take<char>((size_t)(S.d + S.dc) * S.d * e) : nullptr;
+  P->WpT = S.ns ? ar.take<char>((size_t)S.ns * S.d * S.dout * e) : nullptr;
+  P->seeds = S.ns ? ar.take<float>((size_t)S.ns * S.d) : nullptr;
+  return ar.off + 256;
+}
+
+// Workspace layout of the forward pass.
 struct FwdWS {
   PlanBase plan;
-  std::vector<LayerWT> wt;
-  void *WqT, *WpT;
+  Packed pk;    // used when the caller passes no packed weights
   void* H;      // [max rows, d]
   float* Cf;    // [max K, r] latent before its norm
-  void* Cl;     // [max K, r]
+  void* Cl;     // [max K, r] (f16 on the bf16 path)
   void* q;      // [qcap, hd]
-  void* ql;     // [qcap, h, r]
-  void* ol;     // [qcap, h, r]
+  void* ql;     // [qcap, h, r]   (f32 path)
+  void* ol;     // [qcap, h, r]   (f32 path)
   void* o;      // [qcap, hd]
   float* R1;    // [qcap, d]
   void* H2;     // [qcap, d]
@@ -290,23 +324,18 @@ static size_t layout_forward(const Shapes& S, void* base, FwdWS* w) {
     maxK = std::max(maxK, S.UBK[l]);
   }
   w->plan = carve_plan(ar, S.NP, S.B, S.qcap, S.icap);
-  w->wt.resize(S.NP);
-  for (int l = 0; l < S.NP; ++l) {
-    w->wt[l].Wdkv = ar.take<char>((size_t)S.d * S.r * e);
-    w->wt[l].Wuq = ar.take<char>((size_t)S.d * S.hd * e);
-    w->wt[l].Wuv = ar.take<char>((size_t)S.r * S.hd * e);
-    w->wt[l].Wo = ar.take<char>((size_t)S.hd * S.d * e);
-    w->wt[l].W1 = ar.take<char>((size_t)S.d * S.dff * e);
-    w->wt[l].W2 = ar.take<char>((size_t)S.dff * S.d * e);
+  {
+    Packed tmp;
+    const size_t pb = layout_packed(S, nullptr, &tmp);
+    char* blob = ar.take<char>(pb);
+    layout_packed(S, blob, &w->pk);
   }
-  w->WqT = S.nq ? ar.take<char>((size_t)(S.d + S.dc) * S.d * e) : nullptr;
-  w->WpT = S.ns ? ar.take<char>((size_t)S.ns * S.d * S.dout * e) : nullptr;
   w->H = ar.take<char>((size_t)maxrows * S.d * e);
-  w->Cf = S.lnorm ? ar.take<float>((size_t)maxK * S.r) : nullptr;
+  w->Cf = ar.take<float>((size_t)maxK * S.r);
   w->Cl = ar.take<char>((size_t)maxK * S.r * e);
   w->q = ar.take<char>((size_t)S.qcap * S.hd * e);
-  w->ql = ar.take<char>((size_t)S.qcap * S.h * S.r * e);
-  w->ol = ar.take<char>((size_t)S.qcap * S.h * S.r * e);
+  w->ql = S.bf16 ? nullptr : ar.take<char>((size_t)S.qcap * S.h * S.r * e);
+  w->ol = S.bf16 ? nullptr : ar.take<char>((size_t)S.qcap * S.h * S.r * e);
   w->o = ar.take<char>((size_t)S.qcap * S.hd * e);
   w->R1 = ar.take<float>((size_t)S.qcap * S.d);
   w->H2 = ar.take<char>((size_t)S.qcap * S.d * e);
@@ -329,151 +358,176 @@ static llatte_status check_layer(const llatte_layer_weights* L, int l) {
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
-// Transposed copies of one layer's matrices into the workspace.
-static hipError_t prep_layer(const Shapes& S, const llatte_layer_weights* L,
-                             const LayerWT& T, hipStream_t s) {
-  const bool b = S.bf16;
-  hipError_t e;
-  if ((e = transpose(L->W_dkv, S.d, S.r, S.r, 0, T.Wdkv, S.d, 0, 1, b, s))) return e;
-  if ((e = transpose(L->W_uq, S.d, S.hd, S.hd, 0, T.Wuq, S.d, 0, 1, b, s))) return e;
+// Packs one layer's weights into the packed layout.
+static hipError_t pack_layer(const Shapes& S, const llatte_layer_weights* L,
+                             const PackedLayer& T, hipStream_t s) {
+  const int k = S.bf16 ? K_BF16 : K_F32;
+  const size_t e = S.esz;
+  hipError_t err;
+  if ((err = hipMemcpyAsync(T.g1, L->g1, S.d * 4, hipMemcpyDeviceToDevice, s))) return err;
+  if ((err = hipMemcpyAsync(T.g_c, L->g_c, S.r * 4, hipMemcpyDeviceToDevice, s))) return err;
+  if ((err = hipMemcpyAsync(T.g2, L->g2, S.d * 4, hipMemcpyDeviceToDevice, s))) return err;
+  if ((err = hipMemcpyAsync(T.Wuk, L->W_uk, (size_t)S.r * S.hd * e,
+                            hipMemcpyDeviceToDevice, s)))
+    return err;
+  if ((err = transpose(L->W_dkv, S.d, S.r, S.r, 0, T.Wdkv, S.d, 0, 1, k, k, s))) return err;
+  if ((err = transpose(L->W_uq, S.d, S.hd, S.hd, 0, T.Wuq, S.d, 0, 1, k, k, s))) return err;
   // per head: W_uv[:, j*dk:(j+1)*dk] ([r, dk]) -> [dk, r]
-  if ((e = transpose(L->W_uv, S.r, S.dk, S.hd, S.dk, T.Wuv, S.r,
-                     (long long)S.dk * S.r, S.h, b, s)))
-    return e;
-  if ((e = transpose(L->W_o, S.hd, S.d, S.d, 0, T.Wo, S.hd, 0, 1, b, s))) return e;
-  if ((e = transpose(L->W1, S.d, S.dff, S.dff, 0, T.W1, S.d, 0, 1, b, s))) return e;
-  if ((e = transpose(L->W2, S.dff, S.d, S.d, 0, T.W2, S.dff, 0, 1, b, s))) return e;
+  if ((err = transpose(L->W_uv, S.r, S.dk, S.hd, S.dk, T.Wuv, S.r,
+                       (long long)S.dk * S.r, S.h, k, S.bf16 ? K_F16 : K_F32, s)))
+    return err;
+  if ((err = transpose(L->W_o, S.hd, S.d, S.d, 0, T.Wo, S.hd, 0, 1, k, k, s))) return err;
+  if ((err = transpose(L->W1, S.d, S.dff, S.dff, 0, T.W1, S.d, 0, 1, k, k, s))) return err;
+  if ((err = transpose(L->W2, S.dff, S.d, S.d, 0, T.W2, S.dff, 0, 1, k, k, s))) return err;
+  return hipSuccess;
+}
+
+static hipError_t pack_all(const Shapes& S, const llatte_weights* w,
+                           const Packed& P, hipStream_t s) {
+  const int k = S.bf16 ? K_BF16 : K_F32;
+  hipError_t err;
+  for (int l = 0; l < S.N; ++l)
+    if ((err = pack_layer(S, &w->layers[l], P.L[l], s))) return err;
+  if (S.ns) {
+    if ((err = pack_layer(S, &w->readout, P.L[S.N], s))) return err;
+    if ((err = hipMemcpyAsync(P.seeds, w->seeds, (size_t)S.ns * S.d * 4,
+                              hipMemcpyDeviceToDevice, s)))
+      return err;
+    if ((err = transpose(w->W_p, S.ns * S.d, S.dout, S.dout, 0, P.WpT, S.ns * S.d,
+                         0, 1, k, k, s)))
+      return err;
+  }
+  if (S.nq &&
+      (err = transpose(w->W_q, S.d + S.dc, S.d, S.d, 0, P.WqT, S.d + S.dc, 0, 1, k, k, s)))
+    return err;
   return hipSuccess;
 }
 
 // One layer (plan index l) from row space `src` into `out` ([UBM, d] float).
 static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
-                            const llatte_layer_weights* L, RowSrc src,
-                            float* out, hipStream_t s) {
+                            const PackedLayer& L, RowSrc src, float* out,
+                            hipStream_t s) {
   const LayerPlan P = w.plan.layer(l);
   const bool b = S.bf16;
+  const int tk = b ? K_BF16 : K_F32;
   const int nql = l < S.N ? S.nq : S.ns;
   const long long nc = (long long)S.B * nql;
   const int UBrows = (int)S.UBrows[l], UBK = (int)S.UBK[l], UBM = (int)S.UBM[l];
   const size_t e = S.esz;
   hipError_t err;
+  auto gemm_base = [&](const char* name) {
+    GemmParams g;
+    g.name = name;
+    g.M_cap = UBM;
+    g.M_dev = P.counts + 3;
+    return g;
+  };
 
   // 1. H = RMSNorm(R) g1 (pre) or R (post), all rows of the row space
-  if ((err = norm_rows(src, UBrows, P.counts + 2, S.pre ? L->g1 : nullptr, S.eps,
-                       nullptr, 0, w.H, S.d, S.d, b, s)))
+  if ((err = norm_rows(src, UBrows, P.counts + 2, S.pre ? L.g1 : nullptr, S.eps,
+                       nullptr, 0, w.H, S.d, S.d, tk, s)))
     return err;
-  // 2. latent C = H_hist W_dkv (+ RMSNorm g_c)
+  // 2. latent C = H_hist W_dkv, then RMSNorm(C) g_c (f16 on the bf16 path)
   {
     GemmParams g;
     g.name = "gemm_down";
     g.A = (const char*)w.H + (size_t)nc * S.d * e;
     g.lda = S.d;
-    g.B = w.wt[l].Wdkv;
+    g.B = L.Wdkv;
     g.ldb = S.d;
     g.M_cap = UBK;
     g.M_dev = P.counts + 0;
     g.N = S.r;
     g.K = S.d;
-    if (S.lnorm) {
-      g.epi = EPI_STORE_F32;
-      g.C = w.Cf;
-    } else {
-      g.epi = EPI_STORE;
-      g.C = w.Cl;
-    }
+    g.epi = EPI_STORE_F32;
+    g.C = w.Cf;
     g.ldc = S.r;
     if ((err = gemm(g, b, s))) return err;
-    if (S.lnorm &&
-        (err = norm_rows(RowSrc{w.Cf, w.Cf, 0, S.r}, UBK, P.counts + 0, L->g_c,
-                         S.eps, nullptr, 0, w.Cl, S.r, S.r, b, s)))
+    if ((err = norm_rows(RowSrc{w.Cf, w.Cf, 0, S.r}, UBK, P.counts + 0,
+                         S.lnorm ? L.g_c : nullptr, S.eps, nullptr, 0, w.Cl, S.r,
+                         S.r, b ? K_F16 : K_F32, s)))
       return err;
   }
   // 3. q = H[qmap] W_uq
   {
-    GemmParams g;
-    g.name = "gemm_q";
+    GemmParams g = gemm_base("gemm_q");
     g.A = w.H;
     g.lda = S.d;
     g.a_rows = P.qmap;
-    g.B = w.wt[l].Wuq;
+    g.B = L.Wuq;
     g.ldb = S.d;
-    g.M_cap = UBM;
-    g.M_dev = P.counts + 3;
     g.N = S.hd;
     g.K = S.d;
     g.C = w.q;
     g.ldc = S.hd;
     if ((err = gemm(g, b, s))) return err;
   }
-  // 4. latent queries per head: ql_j = q_j W_uk_j^T
-  {
-    GemmParams g;
-    g.name = "gemm_absorb_uk";
+  AttnParams a;
+  a.c = w.Cl;
+  a.lse = nullptr;
+  a.h = S.h;
+  a.r = S.r;
+  a.dk = S.dk;
+  a.scale = 1.f / sqrtf((float)S.dk);
+  a.items = P.items;
+  a.n_items = P.n_items;
+  a.items_cap = S.icap;
+  a.qinfo = P.qinfo;
+  a.M_cap = UBM;
+  a.M_dev = P.counts + 3;
+  if (b) {
+    // 4-6. o = attention with q_lat = q W_uk^T formed in the prologue and
+    //      o_j = o_lat_j W_uv_j applied in the epilogue
+    a.fused = true;
+    a.q = w.q;
+    a.w_uk = L.Wuk;
+    a.w_uv_t = L.Wuv;
+    a.out = w.o;
+    if ((err = attention(a, true, s))) return err;
+  } else {
+    // 4. latent queries per head: ql_j = q_j W_uk_j^T
+    GemmParams g = gemm_base("gemm_absorb_uk");
     g.A = w.q;
     g.lda = S.hd;
     g.sA = S.dk;
-    g.B = L->W_uk;
+    g.B = L.Wuk;
     g.ldb = S.hd;
     g.sB = S.dk;
     g.batch = S.h;
-    g.M_cap = UBM;
-    g.M_dev = P.counts + 3;
     g.N = S.r;
     g.K = S.dk;
     g.C = w.ql;
     g.ldc = S.h * S.r;
     g.sC = S.r;
     if ((err = gemm(g, b, s))) return err;
-  }
-  // 5. attention in latent space
-  {
-    AttnParams a;
+    // 5. attention in latent space
+    a.fused = false;
     a.q = w.ql;
-    a.c = w.Cl;
     a.out = w.ol;
-    a.out_f32 = false;
-    a.lse = nullptr;
-    a.h = S.h;
-    a.r = S.r;
-    a.scale = 1.f / sqrtf((float)S.dk);
-    a.items = P.items;
-    a.n_items = P.n_items;
-    a.items_cap = S.icap;
-    a.qinfo = P.qinfo;
-    a.M_cap = UBM;
-    a.M_dev = P.counts + 3;
-    if ((err = attention(a, b, s))) return err;
-  }
-  // 6. o_j = ol_j W_uv_j
-  {
-    GemmParams g;
-    g.name = "gemm_absorb_uv";
-    g.A = w.ol;
-    g.lda = S.h * S.r;
-    g.sA = S.r;
-    g.B = w.wt[l].Wuv;
-    g.ldb = S.r;
-    g.sB = (long long)S.dk * S.r;
-    g.batch = S.h;
-    g.M_cap = UBM;
-    g.M_dev = P.counts + 3;
-    g.N = S.dk;
-    g.K = S.r;
-    g.C = w.o;
-    g.ldc = S.hd;
-    g.sC = S.dk;
-    if ((err = gemm(g, b, s))) return err;
+    if ((err = attention(a, false, s))) return err;
+    // 6. o_j = ol_j W_uv_j
+    GemmParams g2 = gemm_base("gemm_absorb_uv");
+    g2.A = w.ol;
+    g2.lda = S.h * S.r;
+    g2.sA = S.r;
+    g2.B = L.Wuv;
+    g2.ldb = S.r;
+    g2.sB = (long long)S.dk * S.r;
+    g2.batch = S.h;
+    g2.N = S.dk;
+    g2.K = S.r;
+    g2.C = w.o;
+    g2.ldc = S.hd;
+    g2.sC = S.dk;
+    if ((err = gemm(g2, b, s))) return err;
   }
   // 7. R1 = R[qmap] + o W_o
   {
-    GemmParams g;
-    g.name = "gemm_out";
+    GemmParams g = gemm_base("gemm_out");
     g.A = w.o;
     g.lda = S.hd;
-    g.B = w.wt[l].Wo;
+    g.B = L.Wo;
     g.ldb = S.hd;
-    g.M_cap = UBM;
-    g.M_dev = P.counts + 3;
     g.N = S.d;
     g.K = S.hd;
     g.epi = EPI_RESID_F32;
@@ -485,22 +539,19 @@ static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
   }
   // 8. H2 = RMSNorm(R1) g2 (pre); post: R1 = RMSNorm(R1) g1, H2 = R1
   if (S.pre)
-    err = norm_rows(RowSrc{w.R1, w.R1, 0, S.d}, UBM, P.counts + 3, L->g2, S.eps,
-                    nullptr, 0, w.H2, S.d, S.d, b, s);
+    err = norm_rows(RowSrc{w.R1, w.R1, 0, S.d}, UBM, P.counts + 3, L.g2, S.eps,
+                    nullptr, 0, w.H2, S.d, S.d, tk, s);
   else
-    err = norm_rows(RowSrc{w.R1, w.R1, 0, S.d}, UBM, P.counts + 3, L->g1, S.eps,
-                    w.R1, S.d, w.H2, S.d, S.d, b, s);
+    err = norm_rows(RowSrc{w.R1, w.R1, 0, S.d}, UBM, P.counts + 3, L.g1, S.eps,
+                    w.R1, S.d, w.H2, S.d, S.d, tk, s);
   if (err) return err;
   // 9. F = GELU(H2 W1)
   {
-    GemmParams g;
-    g.name = "gemm_ffn1";
+    GemmParams g = gemm_base("gemm_ffn1");
     g.A = w.H2;
     g.lda = S.d;
-    g.B = w.wt[l].W1;
+    g.B = L.W1;
     g.ldb = S.d;
-    g.M_cap = UBM;
-    g.M_dev = P.counts + 3;
     g.N = S.dff;
     g.K = S.d;
     g.epi = EPI_GELU;
@@ -510,14 +561,11 @@ static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
   }
   // 10. out = R1 + F W2 (post: then RMSNorm g2)
   {
-    GemmParams g;
-    g.name = "gemm_ffn2";
+    GemmParams g = gemm_base("gemm_ffn2");
     g.A = w.F;
     g.lda = S.dff;
-    g.B = w.wt[l].W2;
+    g.B = L.W2;
     g.ldb = S.dff;
-    g.M_cap = UBM;
-    g.M_dev = P.counts + 3;
     g.N = S.d;
     g.K = S.dff;
     g.epi = EPI_RESID_F32;
@@ -527,8 +575,8 @@ static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
     if ((err = gemm(g, b, s))) return err;
   }
   if (!S.pre &&
-      (err = norm_rows(RowSrc{out, out, 0, S.d}, UBM, P.counts + 3, L->g2, S.eps,
-                       out, S.d, nullptr, 0, S.d, b, s)))
+      (err = norm_rows(RowSrc{out, out, 0, S.d}, UBM, P.counts + 3, L.g2, S.eps,
+                       out, S.d, nullptr, 0, S.d, tk, s)))
     return err;
   return hipSuccess;
 }
@@ -575,31 +623,64 @@ size_t llatte_mla_forward_workspace_size(const llatte_model_desc* desc,
   return layout_forward(S, nullptr, &w);
 }
 
-llatte_status llatte_mla_forward(
-    const llatte_model_desc* desc, const llatte_weights* wts,
-    const float* hist_values, const int32_t* hist_offsets, int32_t B,
-    int32_t total_rows, int32_t max_len, const float* cand_x,
-    const float* ctx, float* out_cand, float* out_hist,
-    int32_t* out_hist_offsets, float* out_emb, void* workspace,
-    size_t workspace_bytes, void* stream) {
+size_t llatte_packed_weights_size(const llatte_model_desc* desc) {
   Shapes S;
-  llatte_status st = make_shapes(desc, B, total_rows, max_len, &S);
-  if (st) return st;
+  if (make_shapes(desc, 1, 1, 1, &S) != LLATTE_OK) return 0;
+  Packed P;
+  return layout_packed(S, nullptr, &P);
+}
+
+static llatte_status check_weights(const Shapes& S, const llatte_weights* wts) {
+  llatte_status st;
   if (!wts || !wts->layers) return fail(LLATTE_ERR_INVALID_ARG, "weights are NULL");
   for (int l = 0; l < S.N; ++l)
     if ((st = check_layer(&wts->layers[l], l))) return st;
-  if (!hist_values || !hist_offsets)
-    return fail(LLATTE_ERR_INVALID_ARG, "hist_values/hist_offsets are NULL");
-  if (S.nq > 0 && (!cand_x || !out_cand || !wts->W_q))
-    return fail(LLATTE_ERR_INVALID_ARG, "n_q > 0 needs cand_x, out_cand and W_q");
-  if (S.nq > 0 && S.dc > 0 && !ctx)
-    return fail(LLATTE_ERR_INVALID_ARG, "d_ctx > 0 needs ctx");
+  if (S.nq > 0 && !wts->W_q) return fail(LLATTE_ERR_INVALID_ARG, "n_q > 0 needs W_q");
   if (S.ns > 0) {
-    if (!wts->seeds || !wts->W_p || !out_emb)
-      return fail(LLATTE_ERR_INVALID_ARG, "readout needs seeds, W_p and out_emb");
+    if (!wts->seeds || !wts->W_p)
+      return fail(LLATTE_ERR_INVALID_ARG, "readout needs seeds and W_p");
     if ((st = check_layer(&wts->readout, -1))) return st;
   }
-  const void* ptrs[] = {hist_values, cand_x, ctx, out_cand, out_hist, out_emb, workspace};
+  return LLATTE_OK;
+}
+
+llatte_status llatte_pack_weights(const llatte_model_desc* desc,
+                                  const llatte_weights* wts, void* packed,
+                                  size_t packed_bytes, void* stream) {
+  Shapes S;
+  llatte_status st = make_shapes(desc, 1, 1, 1, &S);
+  if (st) return st;
+  if ((st = check_weights(S, wts))) return st;
+  if (!packed || !aligned16(packed)) return fail(LLATTE_ERR_INVALID_ARG, "packed must be 16-byte aligned");
+  Packed P;
+  const size_t need = layout_packed(S, nullptr, &P);
+  if (packed_bytes < need)
+    return fail(LLATTE_ERR_WORKSPACE, "packed buffer %zu bytes < %zu needed", packed_bytes, need);
+  layout_packed(S, packed, &P);
+  HIP_TRY(pack_all(S, wts, P, (hipStream_t)stream));
+  return LLATTE_OK;
+}
+
+llatte_status llatte_mla_forward(
+    const llatte_model_desc* desc, const llatte_weights* wts,
+    const void* packed_weights, const float* hist_values,
+    const int32_t* hist_offsets, int32_t B, int32_t total_rows,
+    int32_t max_len, const float* cand_x, const float* ctx, float* out_cand,
+    float* out_hist, int32_t* out_hist_offsets, float* out_emb,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  Shapes S;
+  llatte_status st = make_shapes(desc, B, total_rows, max_len, &S);
+  if (st) return st;
+  if (!packed_weights && (st = check_weights(S, wts))) return st;
+  if (!hist_values || !hist_offsets)
+    return fail(LLATTE_ERR_INVALID_ARG, "hist_values/hist_offsets are NULL");
+  if (S.nq > 0 && (!cand_x || !out_cand))
+    return fail(LLATTE_ERR_INVALID_ARG, "n_q > 0 needs cand_x and out_cand");
+  if (S.nq > 0 && S.dc > 0 && !ctx)
+    return fail(LLATTE_ERR_INVALID_ARG, "d_ctx > 0 needs ctx");
+  if (S.ns > 0 && !out_emb) return fail(LLATTE_ERR_INVALID_ARG, "readout needs out_emb");
+  const void* ptrs[] = {hist_values, cand_x, ctx, out_cand, out_hist, out_emb,
+                        workspace, packed_weights};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(LLATTE_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   if (!workspace) return fail(LLATTE_ERR_INVALID_ARG, "workspace is NULL");
@@ -610,19 +691,23 @@ llatte_status llatte_mla_forward(
   layout_forward(S, workspace, &w);
   hipStream_t s = (hipStream_t)stream;
   const bool b = S.bf16;
+  Packed PK;
+  if (packed_weights) {
+    layout_packed(S, (void*)packed_weights, &PK);
+  } else {
+    PK = w.pk;
+    HIP_TRY(pack_all(S, wts, PK, s));
+  }
 
   HIP_TRY(build_plan(hist_offsets, B, S.rule, S.nq, S.ns, w.plan, S.NP, S.bq,
                      kAttnBN, s));
-  for (int l = 0; l < S.N; ++l) HIP_TRY(prep_layer(S, &wts->layers[l], w.wt[l], s));
-  if (S.ns) HIP_TRY(prep_layer(S, &wts->readout, w.wt[S.N], s));
   if (S.nq) {
-    HIP_TRY(transpose(wts->W_q, S.d + S.dc, S.d, S.d, 0, w.WqT, S.d + S.dc, 0, 1, b, s));
     HIP_TRY(concat_queries(cand_x, ctx, B, S.nq, S.d, S.dc, w.XC, b, s));
     GemmParams g;
     g.name = "gemm_fusion";
     g.A = w.XC;
     g.lda = S.d + S.dc;
-    g.B = w.WqT;
+    g.B = PK.WqT;
     g.ldb = S.d + S.dc;
     g.M_cap = B * S.nq;
     g.N = S.d;
@@ -641,7 +726,7 @@ llatte_status llatte_mla_forward(
     else
       src = RowSrc{last, last + nc * S.d, (int)nc, S.d};
     float* out = w.Rb[l & 1];
-    HIP_TRY(run_layer(S, w, l, &wts->layers[l], src, out, s));
+    HIP_TRY(run_layer(S, w, l, PK.L[l], src, out, s));
     last = out;
   }
   const LayerPlan PN = w.plan.layer(S.N - 1);
@@ -653,19 +738,17 @@ llatte_status llatte_mla_forward(
     HIP_TRY(hipMemcpyAsync(out_hist_offsets, PN.hq_off, sizeof(int) * (B + 1),
                            hipMemcpyDeviceToDevice, s));
   if (S.ns) {
-    HIP_TRY(broadcast_rows(wts->seeds, S.ns, S.d, B, w.S, s));
+    HIP_TRY(broadcast_rows(PK.seeds, S.ns, S.d, B, w.S, s));
     float* ro = w.Rb[S.N & 1];
     RowSrc src{w.S, last + nc * S.d, B * S.ns, S.d};
-    HIP_TRY(run_layer(S, w, S.N, &wts->readout, src, ro, s));
+    HIP_TRY(run_layer(S, w, S.N, PK.L[S.N], src, ro, s));
     HIP_TRY(norm_rows(RowSrc{ro, ro, 0, S.d}, B * S.ns, nullptr, nullptr, 0.f,
-                      nullptr, 0, w.E, S.d, S.d, b, s));
-    HIP_TRY(transpose(wts->W_p, S.ns * S.d, S.dout, S.dout, 0, w.WpT, S.ns * S.d,
-                      0, 1, b, s));
+                      nullptr, 0, w.E, S.d, S.d, b ? K_BF16 : K_F32, s));
     GemmParams g;
     g.name = "gemm_readout";
     g.A = w.E;
     g.lda = S.ns * S.d;
-    g.B = w.WpT;
+    g.B = PK.WpT;
     g.ldb = S.ns * S.d;
     g.M_cap = B;
     g.N = S.dout;
@@ -730,8 +813,11 @@ llatte_status llatte_mla_attention(
   ap.q = q_lat;
   ap.c = c_lat;
   ap.out = out;
-  ap.out_f32 = true;
   ap.lse = lse;
+  ap.fused = false;
+  ap.w_uk = nullptr;
+  ap.w_uv_t = nullptr;
+  ap.dk = 0;
   ap.h = a->n_heads;
   ap.r = a->rank;
   ap.scale = a->scale;
@@ -828,7 +914,8 @@ llatte_status llatte_token_embed(const void* table, int32_t V,
     return fail(LLATTE_ERR_WORKSPACE, "workspace too small");
   if (n == 0) return LLATTE_OK;
   hipStream_t s = (hipStream_t)stream;
-  HIP_TRY(transpose(W_s, d_sem, d, d, 0, workspace, d_sem, 0, 1, b, s));
+  HIP_TRY(transpose(W_s, d_sem, d, d, 0, workspace, d_sem, 0, 1,
+                    b ? K_BF16 : K_F32, b ? K_BF16 : K_F32, s));
   GemmParams g;
   g.name = "gemm_token_embed";
   g.A = sem;

@@ -3,22 +3,38 @@
 // scores its latent query against the same latent rows C and averages C
 // itself, so one C tile in LDS serves all heads of a query block.
 //
-// bf16 kernel (MFMA), one workgroup per work item (a block of query rows of
-// one user, all heads of a head group), four waves, each wave owning EPW
-// (query row, head) pairs ("effective rows"):
-//   S^T = C_tile . Q^T          v_mfma_f32_16x16x32_bf16, A = C rows from LDS,
-//                               B = latent queries held in registers
-//   online softmax per column   (fp32, exp2, max/sum over the four lane
-//                               groups of a column with two xor shuffles)
-//   O^T += C_tile^T . P^T       A = C^T from a transposed LDS copy, B = P^T
-//                               straight from the S^T accumulators
-// Computing the transposed products keeps each lane's softmax column and its
-// output column the same effective row, so the rescale needs no shuffles,
-// and P never goes through LDS. The C tile is staged twice per step
-// (row-major for S^T, transposed for O^T), double-buffered; the transpose is
-// done while writing LDS from registers. Masks: history rows attend keys up
-// to their own position (causal, LLaTTE Appendix A.2); candidate rows attend
-// every key of their user.
+// MFMA kernel: one workgroup (8 waves) per work item (a block of BQ query
+// rows of one user, for HG heads). Each wave owns EPW (head, query row)
+// pairs, "effective rows", head-major, so every 16-row MFMA block belongs
+// to one head. Per 64-key tile of C:
+//   S^T = C_tile . Qlat^T        v_mfma_f32_16x16x32_f16; A = C rows (LDS),
+//                                B = latent queries held in registers
+//   online softmax per column    fp32, exp2 (the softmax scale and log2(e)
+//                                are folded into the latent queries); max and
+//                                sum over a column's four lane groups with
+//                                two xor shuffles
+//   O^T += C_tile^T . P^T        A = C^T from a transposed LDS copy, B = P^T
+//                                straight from the S^T accumulators
+// Working on the transposed products keeps each lane's softmax column and
+// output column the same effective row: the rescale needs no shuffles and P
+// never goes through LDS. The tile is staged twice (row-major for S^T,
+// transposed for O^T), double-buffered. Operand k-order: both MFMA operands
+// of a product use the same permutation of the contraction index (lane group
+// g holds k = 4g..4g+3 and 16+4g..16+4g+3 of each 32-wide step), which is
+// what the S^T accumulator layout hands to the P^T operand.
+//
+// Operands are fp16 (the latent C and queries are RMS-normalised, well
+// inside fp16 range, and P lies in [0, 1]): 11 mantissa bits instead of 8,
+// at the same MFMA rate. Accumulation and softmax are fp32.
+//
+// Fused mode (the forward pass): the prologue forms the latent queries from
+// the query projection, q_lat_j = q_j W_uk_j^T (bf16 MFMA), and the epilogue
+// maps the normalised output back, o_j = o_lat_j W_uv_j (fp16 MFMA), writing
+// o [M, h*dk] in bf16 for the output projection. Neither q_lat nor o_lat
+// touches HBM.
+//
+// Masks: history rows see keys up to their own position (causal, LLaTTE
+// Appendix A.2); candidate rows see every key of their user.
 //
 // fp32 kernel: one wave per (query row, head), keys 64 at a time, plain
 // online softmax. It serves the fp32 path only.
@@ -29,23 +45,54 @@ namespace llatte {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
+__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// Values k = 4g..4g+3 and 16+4g..16+4g+3 of two 16-wide accumulator blocks.
+__device__ __forceinline__ f16x8 pack8(f32x4 lo, f32x4 hi, float s) {
+  return f16x8{(f16)(lo[0] * s), (f16)(lo[1] * s), (f16)(lo[2] * s), (f16)(lo[3] * s),
+               (f16)(hi[0] * s), (f16)(hi[1] * s), (f16)(hi[2] * s), (f16)(hi[3] * s)};
+}
+__device__ __forceinline__ f16x8 cat(f16x4 lo, f16x4 hi) {
+  return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ f16x8 to_f16x8(i32x4 raw, bool is_bf16) {
+  if (!is_bf16) return __builtin_bit_cast(f16x8, raw);
+  const bf16x8 b = __builtin_bit_cast(bf16x8, raw);
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (f16)from_bf16(b[i]);
+  return r;
+}
 
-template <int R, int EPW, typename OutT>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnParams p, int HG,
-                                                        int hg_shift) {
+struct AttnCfg {
+  int HG;  // heads per workgroup
+  int BQ;  // query rows per workgroup (multiple of 16)
+};
+
+template <int R, int EPW, int DK, bool FUSED, typename CT>
+__global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams p, AttnCfg cfg) {
   constexpr int BN = kAttnBN;        // keys per tile
-  constexpr int LDC = R + 8;         // row-major C tile pitch (elements)
-  constexpr int LDT = BN + 8;        // transposed C tile pitch
+  constexpr int LDC = R + 8;         // row-major tile pitch (f16)
+  constexpr int LDT = BN + 8;        // transposed tile pitch (f16)
   constexpr int NEB = EPW / 16;      // effective-row blocks per wave
-  constexpr int NKS = R / 32;        // 32-wide r steps
-  constexpr int NRB = R / 16;        // 16-wide r blocks of the output
-  constexpr int NLD = (2 * R + 255) / 256;  // 4-key x 8-r load blocks/thread
+  constexpr int NKS = R / 32;        // 32-wide steps over r
+  constexpr int NRB = R / 16;        // 16-wide blocks over r
+  constexpr int NLD = (2 * R + 511) / 512;  // 4-key x 8-r blocks per thread
+  constexpr bool C_BF16 = __is_same(CT, bf16);
 
-  __shared__ __attribute__((aligned(16))) bf16 Cs[2][BN * LDC];
-  __shared__ __attribute__((aligned(16))) bf16 Ct[2][R * LDT];
+  __shared__ __attribute__((aligned(16))) f16 Cs[2][BN * LDC];
+  __shared__ __attribute__((aligned(16))) f16 Ct[2][R * LDT];
 
   const int nitems = min(*p.n_items, p.items_cap);
   if ((int)blockIdx.x >= nitems) return;
@@ -54,7 +101,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnParams p, int HG,
   const bool cand = it[2] < 0;
   const int nr = it[2] & 0x7fffffff;
   const int pos0 = it[3];
-  const int h0 = blockIdx.y * HG;
+  const int h0 = blockIdx.y * cfg.HG;
   const int max_pos = cand ? pos0 : pos0 + nr - 1;
   const int nkeys = max_pos + 1;
   const int ntiles = (nkeys + BN - 1) / BN;
@@ -62,38 +109,69 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnParams p, int HG,
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, l16 = lane & 15;
+  const float sc = p.scale * kLog2e;   // scores in log2 units
+  const CT* Cg = (const CT*)p.c + (size_t)kvb * R;
 
-  const bf16* Q = (const bf16*)p.q;
-  const bf16* Cg = (const bf16*)p.c + (size_t)kvb * R;
-
-  // Effective rows of this lane (one per block eb): e = wave*EPW + eb*16 + l16
-  // -> query row ql = e >> hg_shift, head h0 + (e & (HG-1)).
-  int pos[NEB];
+  // this lane's effective rows: one per block (head uniform per block)
+  int head[NEB], qrow[NEB], pos[NEB];
   bool valid[NEB];
-  bf16x8 qf[NEB][NKS];
   int pmin = 0x7fffffff;
 #pragma unroll
   for (int eb = 0; eb < NEB; ++eb) {
-    const int e = wave * EPW + eb * 16 + l16;
-    const int ql = e >> hg_shift, hl = e & (HG - 1);
+    const int e0 = wave * EPW + eb * 16;
+    const int ql = e0 % cfg.BQ + l16;
+    head[eb] = h0 + e0 / cfg.BQ;
     valid[eb] = ql < nr;
     const int qc = min(ql, nr - 1);
+    qrow[eb] = qrow0 + qc;
     pos[eb] = cand ? pos0 : pos0 + qc;
     pmin = min(pmin, pos[eb]);
-    const bf16* qp = Q + ((size_t)(qrow0 + qc) * p.h + h0 + hl) * R + g * 8;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[eb][ks] = *(const bf16x8*)(qp + ks * 32);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) pmin = min(pmin, __shfl_xor(pmin, o, 64));
 
-  // Tile loads: block b covers keys 4*kq .. 4*kq+3 and r 8*rc .. 8*rc+7.
+  // latent queries, B operand of S^T, scaled into log2 units
+  f16x8 qf[NEB][NKS];
+#pragma unroll
+  for (int eb = 0; eb < NEB; ++eb) {
+    if constexpr (FUSED) {
+      // q_lat^T[r][e] = sum_k W_uk[r][head*DK + k] * q[e][head*DK + k]
+      const int hd = p.h * DK;
+      const bf16* qp = (const bf16*)p.q + (size_t)qrow[eb] * hd + head[eb] * DK + g * 8;
+      const bf16* wp = (const bf16*)p.w_uk + (size_t)l16 * hd + head[eb] * DK + g * 8;
+      f32x4 acc[NRB];
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kd = 0; kd < DK / 32; ++kd) {
+        const bf16x8 bq = *(const bf16x8*)(qp + kd * 32);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          const bf16x8 a = *(const bf16x8*)(wp + (size_t)rb * 16 * hd + kd * 32);
+          acc[rb] = mfma_bf16(a, bq, acc[rb]);
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qf[eb][ks] = pack8(acc[2 * ks], acc[2 * ks + 1], sc);
+    } else {
+      const bf16* qp = (const bf16*)p.q + ((size_t)qrow[eb] * p.h + head[eb]) * R + g * 4;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x4 lo = *(const bf16x4*)(qp + ks * 32);
+        const bf16x4 hi = *(const bf16x4*)(qp + ks * 32 + 16);
+        qf[eb][ks] = pack8(f32x4{from_bf16(lo[0]), from_bf16(lo[1]), from_bf16(lo[2]), from_bf16(lo[3])},
+                           f32x4{from_bf16(hi[0]), from_bf16(hi[1]), from_bf16(hi[2]), from_bf16(hi[3])}, sc);
+      }
+    }
+  }
+
+  // C tile staging: block b covers keys 4*kq .. 4*kq+3 and r 8*rc .. 8*rc+7
   i32x4 ld[NLD][4];
   auto load_tile = [&](int t) {
     const int k0 = t * BN;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int b = tid + i * 256;
+      const int b = tid + i * 512;
       const int rc = b % (R / 8), kq = b / (R / 8);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -107,20 +185,18 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnParams p, int HG,
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int b = tid + i * 256;
+      const int b = tid + i * 512;
       if (b >= 2 * R) continue;
       const int rc = b % (R / 8), kq = b / (R / 8);
+      f16x8 v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *(i32x4*)&Cs[buf][(kq * 4 + j) * LDC + rc * 8] = ld[i][j];
-      bf16x8 v0 = __builtin_bit_cast(bf16x8, ld[i][0]);
-      bf16x8 v1 = __builtin_bit_cast(bf16x8, ld[i][1]);
-      bf16x8 v2 = __builtin_bit_cast(bf16x8, ld[i][2]);
-      bf16x8 v3 = __builtin_bit_cast(bf16x8, ld[i][3]);
+      for (int j = 0; j < 4; ++j) {
+        v[j] = to_f16x8(ld[i][j], C_BF16);
+        *(f16x8*)&Cs[buf][(kq * 4 + j) * LDC + rc * 8] = v[j];
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        *(bf16x4*)&Ct[buf][(rc * 8 + e) * LDT + kq * 4] =
-            bf16x4{v0[e], v1[e], v2[e], v3[e]};
+        *(f16x4*)&Ct[buf][(rc * 8 + e) * LDT + kq * 4] = f16x4{v[0][e], v[1][e], v[2][e], v[3][e]};
     }
   };
 
@@ -135,7 +211,6 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnParams p, int HG,
     m_run[eb] = -INFINITY;
     l_run[eb] = 0.f;
   }
-  const float sc = p.scale * kLog2e;
 
   load_tile(0);
   store_tile(0);
@@ -143,10 +218,10 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnParams p, int HG,
   for (int t = 0; t < ntiles; ++t) {
     const int cur = t & 1;
     if (t + 1 < ntiles) load_tile(t + 1);
-    const bf16* cs = Cs[cur];
-    const bf16* ct = Ct[cur];
+    const f16* cs = Cs[cur];
+    const f16* ct = Ct[cur];
 
-    // S^T[key][e] for the 64 keys of this tile
+    // S^T[key][e], 64 keys
     f32x4 s[4][NEB];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -154,31 +229,30 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnParams p, int HG,
       for (int eb = 0; eb < NEB; ++eb) s[kb][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 a = *(const bf16x8*)&cs[(kb * 16 + l16) * LDC + ks * 32 + g * 8];
+        const f16* row = &cs[(kb * 16 + l16) * LDC + ks * 32 + g * 4];
+        const f16x8 a = cat(*(const f16x4*)row, *(const f16x4*)(row + 16));
 #pragma unroll
-        for (int eb = 0; eb < NEB; ++eb)
-          s[kb][eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[eb][ks], s[kb][eb], 0, 0, 0);
+        for (int eb = 0; eb < NEB; ++eb) s[kb][eb] = mfma_f16(a, qf[eb][ks], s[kb][eb]);
       }
     }
 
     // online softmax per effective row (this lane's column of S^T)
     const bool need_mask = t * BN + BN - 1 > pmin;
-    bf16x8 pf[2][NEB];
+    f16x8 pf[2][NEB];
 #pragma unroll
     for (int eb = 0; eb < NEB; ++eb) {
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (t * BN + kb * 16 + g * 4 + v > pos[eb]) s[kb][eb][v] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float x = s[kb][eb][v] * sc;
-          if (need_mask) {
-            const int key = t * BN + kb * 16 + g * 4 + v;
-            if (key > pos[eb]) x = -INFINITY;
-          }
-          s[kb][eb][v] = x;
-          mx = fmaxf(mx, x);
-        }
+        for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[kb][eb][v]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m_run[eb], mx);
@@ -190,9 +264,11 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnParams p, int HG,
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const float e = fast_exp2(s[kb][eb][v] - m_new);
+          s[kb][eb][v] = e;
           rs += e;
-          pf[kb >> 1][eb][(kb & 1) * 4 + v] = to_bf16(e);
         }
+      pf[0][eb] = pack8(s[0][eb], s[1][eb], 1.f);
+      pf[1][eb] = pack8(s[2][eb], s[3][eb], 1.f);
       rs += __shfl_xor(rs, 16, 64);
       rs += __shfl_xor(rs, 32, 64);
       l_run[eb] = l_run[eb] * alpha + rs;
@@ -207,13 +283,10 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnParams p, int HG,
     for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16* row = &ct[(rb * 16 + l16) * LDT + kk * 32 + g * 4];
-        const bf16x4 lo = *(const bf16x4*)row;
-        const bf16x4 hi = *(const bf16x4*)(row + 16);
-        const bf16x8 a = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const f16* row = &ct[(rb * 16 + l16) * LDT + kk * 32 + g * 4];
+        const f16x8 a = cat(*(const f16x4*)row, *(const f16x4*)(row + 16));
 #pragma unroll
-        for (int eb = 0; eb < NEB; ++eb)
-          acc_o[rb][eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[kk][eb], acc_o[rb][eb], 0, 0, 0);
+        for (int eb = 0; eb < NEB; ++eb) acc_o[rb][eb] = mfma_f16(a, pf[kk][eb], acc_o[rb][eb]);
       }
     }
 
@@ -221,27 +294,36 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnParams p, int HG,
     __syncthreads();
   }
 
-  // normalise and store: lane holds out[e][rb*16 + 4g .. +3]
-  OutT* O = (OutT*)p.out;
 #pragma unroll
   for (int eb = 0; eb < NEB; ++eb) {
-    if (!valid[eb]) continue;
-    const int e = wave * EPW + eb * 16 + l16;
-    const int ql = e >> hg_shift, hl = e & (HG - 1);
-    const size_t orow = (size_t)(qrow0 + ql) * p.h + h0 + hl;
     const float inv = 1.f / l_run[eb];
-    OutT* op = O + orow * R + g * 4;
+    if constexpr (FUSED) {
+      // o^T[k][e] = sum_r W_uv^T[head][k][r] * o_lat^T[r][e]
+      f16x8 ob[NKS];
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      const f32x4 v = acc_o[rb][eb];
-      if constexpr (sizeof(OutT) == 2)
-        *(bf16x4*)(op + rb * 16) =
-            bf16x4{to_bf16(v[0] * inv), to_bf16(v[1] * inv), to_bf16(v[2] * inv),
-                   to_bf16(v[3] * inv)};
-      else
-        *(f32x4*)(op + rb * 16) = v * inv;
+      for (int kk = 0; kk < NKS; ++kk)
+        ob[kk] = pack8(acc_o[2 * kk][eb], acc_o[2 * kk + 1][eb], inv);
+      const f16* wv = (const f16*)p.w_uv_t + ((size_t)head[eb] * DK + l16) * R + g * 4;
+      bf16* op = (bf16*)p.out + (size_t)qrow[eb] * (p.h * DK) + head[eb] * DK + g * 4;
+#pragma unroll
+      for (int nb = 0; nb < DK / 16; ++nb) {
+        f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NKS; ++kk) {
+          const f16* w = wv + (size_t)nb * 16 * R + kk * 32;
+          o = mfma_f16(cat(*(const f16x4*)w, *(const f16x4*)(w + 16)), ob[kk], o);
+        }
+        if (valid[eb])
+          *(bf16x4*)(op + nb * 16) = bf16x4{(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};
+      }
+    } else {
+      if (!valid[eb]) continue;
+      const size_t orow = (size_t)qrow[eb] * p.h + head[eb];
+      float* op = (float*)p.out + orow * R + g * 4;
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) *(f32x4*)(op + rb * 16) = acc_o[rb][eb] * inv;
+      if (p.lse && g == 0) p.lse[orow] = (m_run[eb] + log2f(l_run[eb])) * kLn2;
     }
-    if (p.lse && g == 0) p.lse[orow] = (m_run[eb] + __log2f(l_run[eb])) * kLn2;
   }
 }
 
@@ -301,53 +383,66 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
   if (p.lse && lane == 0) p.lse[(size_t)i * p.h + hh] = m + logf(l);
 }
 
-// Effective rows per wave and query rows per item of the bf16 kernel.
-static int attn_epw(int r) { return r == 256 ? 32 : 64; }
+// Effective rows per wave: register budget of the O accumulator.
+static int attn_epw(int r) { return r == 256 ? 16 : (r == 128 ? 32 : 64); }
 
-static int heads_per_group(int h, int r) {
-  // all heads of a query row in one workgroup when at least one query row
-  // fits; otherwise the largest power-of-two divisor of h that fits
-  const int eff = 4 * attn_epw(r);
-  int hg = 1;
-  while (hg * 2 <= h && h % (hg * 2) == 0 && hg * 2 <= eff) hg *= 2;
-  return hg;
+static AttnCfg attn_cfg(int h, int r) {
+  const int eff = 8 * attn_epw(r);  // effective rows per workgroup
+  int hg = 1;                       // power-of-two divisor of h, BQ >= 16
+  while (h % (hg * 2) == 0 && eff / (hg * 2) >= 16) hg *= 2;
+  return AttnCfg{hg, eff / hg};
 }
 
 int attn_bq(int h, int r) {
   if (r != 64 && r != 128 && r != 256) return 0;
-  return 4 * attn_epw(r) / heads_per_group(h, r);
+  return attn_cfg(h, r).BQ;
+}
+
+bool attn_fused_supported(int h, int r, int dk) {
+  return attn_bq(h, r) > 0 && (dk == 32 || dk == 64 || dk == 128);
+}
+
+template <int R, int EPW, int DK, bool FUSED, typename CT>
+static void launch_mfma(const AttnParams& p, hipStream_t s) {
+  const AttnCfg c = attn_cfg(p.h, R);
+  dim3 grid(p.items_cap, p.h / c.HG);
+  hipLaunchKernelGGL((attn_mfma_kernel<R, EPW, DK, FUSED, CT>), grid, dim3(512),
+                     0, s, p, c);
 }
 
 template <int R, int EPW>
-static void launch_bf16(const AttnParams& p, hipStream_t s) {
-  const int hg = heads_per_group(p.h, R);
-  int shift = 0;
-  while ((1 << shift) < hg) ++shift;
-  dim3 grid(p.items_cap, p.h / hg);
-  if (p.out_f32)
-    hipLaunchKernelGGL((attn_bf16_kernel<R, EPW, float>), grid, dim3(256), 0, s,
-                       p, hg, shift);
-  else
-    hipLaunchKernelGGL((attn_bf16_kernel<R, EPW, bf16>), grid, dim3(256), 0, s,
-                       p, hg, shift);
+static hipError_t launch_r(const AttnParams& p, hipStream_t s) {
+  if (!p.fused) {
+    launch_mfma<R, EPW, 64, false, bf16>(p, s);
+    return hipSuccess;
+  }
+  switch (p.dk) {
+    case 32: launch_mfma<R, EPW, 32, true, f16>(p, s); break;
+    case 64: launch_mfma<R, EPW, 64, true, f16>(p, s); break;
+    case 128: launch_mfma<R, EPW, 128, true, f16>(p, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipSuccess;
 }
 
 hipError_t attention(const AttnParams& p, bool is_bf16, hipStream_t s) {
   if (p.M_cap <= 0) return hipSuccess;
-  timing_begin(is_bf16 ? "attention_bf16" : "attention_f32", s);
+  hipError_t e = hipSuccess;
+  timing_begin(is_bf16 ? "attention_mfma" : "attention_f32", s);
   if (is_bf16) {
     if (p.items_cap > 0) {
       switch (p.r) {
-        case 64: launch_bf16<64, 64>(p, s); break;
-        case 128: launch_bf16<128, 64>(p, s); break;
-        case 256: launch_bf16<256, 32>(p, s); break;
-        default: timing_end(s); return hipErrorInvalidValue;
+        case 64: e = launch_r<64, 64>(p, s); break;
+        case 128: e = launch_r<128, 32>(p, s); break;
+        case 256: e = launch_r<256, 16>(p, s); break;
+        default: e = hipErrorInvalidValue;
       }
     }
   } else {
     hipLaunchKernelGGL(attn_f32_kernel, dim3(p.M_cap, p.h), dim3(64), 0, s, p);
   }
   timing_end(s);
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

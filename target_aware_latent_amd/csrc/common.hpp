@@ -13,12 +13,10 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
-// float -> bf16, round to nearest even (finite inputs).
-__device__ __forceinline__ bf16 to_bf16(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return __builtin_bit_cast(bf16, (uint16_t)(u >> 16));
-}
+typedef _Float16 f16;
+
+// float -> bf16 with the hardware conversion (round to nearest even).
+__device__ __forceinline__ bf16 to_bf16(float f) { return (bf16)f; }
 __device__ __forceinline__ float from_bf16(bf16 b) {
   return __builtin_bit_cast(float, ((uint32_t)__builtin_bit_cast(uint16_t, b)) << 16);
 }
@@ -26,6 +24,7 @@ __device__ __forceinline__ float from_bf16(bf16 b) {
 template <typename T> __device__ __forceinline__ T cvt(float f);
 template <> __device__ __forceinline__ float cvt<float>(float f) { return f; }
 template <> __device__ __forceinline__ bf16 cvt<bf16>(float f) { return to_bf16(f); }
+template <> __device__ __forceinline__ f16 cvt<f16>(float f) { return (f16)f; }
 __device__ __forceinline__ float tof(float f) { return f; }
 __device__ __forceinline__ float tof(bf16 b) { return from_bf16(b); }
 

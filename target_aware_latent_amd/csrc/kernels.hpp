@@ -51,18 +51,22 @@ struct GemmParams {
 hipError_t gemm(const GemmParams& p, bool bf16, hipStream_t s);
 
 // ------------------------------------------------------------------ row ops
+// Element kinds of buffers whose type is chosen at run time.
+enum Kind { K_F32 = 0, K_BF16 = 1, K_F16 = 2 };
+
 // One wave per row (d <= 1024): out = gain ? x / sqrt(mean(x^2) + eps) * gain : x, where
 // x = src.row(i); written as float to out_f32 (may alias the source) and/or
-// as dtype to out_t. Rows i >= *rows_dev (if given) are skipped.
+// as `t_kind` to out_t. Rows i >= *rows_dev (if given) are skipped.
 hipError_t norm_rows(RowSrc src, int rows_cap, const int* rows_dev,
                      const float* gain, float eps, float* out_f32, int ld_f32,
-                     void* out_t, int ld_t, int d, bool bf16, hipStream_t s);
+                     void* out_t, int ld_t, int d, int t_kind, hipStream_t s);
 
-// dst (dtype) [rows, cols] = transpose(src (dtype) [cols, rows]) for a batch
-// of `batch` matrices laid out with the given element strides.
+// dst [cols, rows] = transpose(src [rows, cols]) for a batch of `batch`
+// matrices laid out with the given element strides; src has kind s_kind,
+// dst kind d_kind (bf16 -> f16 and same-kind copies).
 hipError_t transpose(const void* src, int src_rows, int src_cols, int ld_src,
                      long long s_src, void* dst, int ld_dst, long long s_dst,
-                     int batch, bool bf16, hipStream_t s);
+                     int batch, int s_kind, int d_kind, hipStream_t s);
 
 // xc (dtype) [B*n_q, d + d_c]: row u*n_q + j = [cand[u*n_q+j] ; ctx[u]].
 hipError_t concat_queries(const float* cand, const float* ctx, int B, int n_q,
@@ -156,11 +160,20 @@ hipError_t pyramid_compact(const void* values, int row_bytes,
 
 // ------------------------------------------------------------------ attention
 struct AttnParams {
-  const void* q;      // [M, h, r]
-  const void* c;      // [Ktot, r]
-  void* out;          // [M, h, r]: dtype, or float32 when out_f32
-  bool out_f32;
-  float* lse;         // [M, h] or null
+  // fused (forward pass): q = query projection [M, h*dk] bf16, c = latent
+  //   [Ktot, r] f16, w_uk [r, h*dk] bf16, w_uv_t [h][dk][r] f16,
+  //   out = o [M, h*dk] bf16.
+  // standalone (bf16): q = latent queries [M, h, r] bf16, c [Ktot, r] bf16,
+  //   out [M, h, r] float32, lse [M, h] float32 or null.
+  // f32 kernel: q [M, h, r], c [Ktot, r], out [M, h, r], all float32.
+  const void* q;
+  const void* c;
+  void* out;
+  float* lse;
+  bool fused;
+  const void* w_uk;
+  const void* w_uv_t;
+  int dk;
   int h, r;
   float scale;
   const i32x4* items; // bf16 path
@@ -174,6 +187,7 @@ struct AttnParams {
 // Query rows per work item for the bf16 kernel at these sizes (0 if the
 // shape is not supported by the MFMA kernel).
 int attn_bq(int h, int r);
+bool attn_fused_supported(int h, int r, int dk);
 constexpr int kAttnBN = 64;
 hipError_t attention(const AttnParams& p, bool bf16, hipStream_t s);
 

@@ -57,14 +57,18 @@ __global__ __launch_bounds__(256) void norm_rows_kernel(
 
 hipError_t norm_rows(RowSrc src, int rows_cap, const int* rows_dev,
                      const float* gain, float eps, float* out_f32, int ld_f32,
-                     void* out_t, int ld_t, int d, bool is_bf16, hipStream_t s) {
+                     void* out_t, int ld_t, int d, int t_kind, hipStream_t s) {
   if (rows_cap <= 0) return hipSuccess;
   dim3 grid((rows_cap + 3) / 4);
   timing_begin("norm_rows", s);
-  if (is_bf16)
+  if (t_kind == K_BF16)
     hipLaunchKernelGGL(norm_rows_kernel<bf16>, grid, dim3(256), 0, s, src,
                        rows_cap, rows_dev, gain, eps, out_f32, ld_f32,
                        (bf16*)out_t, ld_t, d);
+  else if (t_kind == K_F16)
+    hipLaunchKernelGGL(norm_rows_kernel<f16>, grid, dim3(256), 0, s, src,
+                       rows_cap, rows_dev, gain, eps, out_f32, ld_f32,
+                       (f16*)out_t, ld_t, d);
   else
     hipLaunchKernelGGL(norm_rows_kernel<float>, grid, dim3(256), 0, s, src,
                        rows_cap, rows_dev, gain, eps, out_f32, ld_f32,
@@ -74,9 +78,9 @@ hipError_t norm_rows(RowSrc src, int rows_cap, const int* rows_dev,
 }
 
 // 32x32 tiles through LDS (one padding column against bank conflicts).
-template <typename T>
+template <typename S, typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(
-    const T* src, int rows, int cols, int ld_src, long long s_src, T* dst,
+    const S* src, int rows, int cols, int ld_src, long long s_src, T* dst,
     int ld_dst, long long s_dst) {
   __shared__ T tile[32][33];
   src += (size_t)blockIdx.z * s_src;
@@ -85,7 +89,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   for (int i = ty; i < 32; i += 8) {
     int r = r0 + i, c = c0 + tx;
-    if (r < rows && c < cols) tile[i][tx] = src[(size_t)r * ld_src + c];
+    if (r < rows && c < cols) tile[i][tx] = cvt<T>(tof(src[(size_t)r * ld_src + c]));
   }
   __syncthreads();
   for (int i = ty; i < 32; i += 8) {
@@ -96,18 +100,24 @@ __global__ __launch_bounds__(256) void transpose_kernel(
 
 hipError_t transpose(const void* src, int rows, int cols, int ld_src,
                      long long s_src, void* dst, int ld_dst, long long s_dst,
-                     int batch, bool is_bf16, hipStream_t s) {
+                     int batch, int s_kind, int d_kind, hipStream_t s) {
   if (rows <= 0 || cols <= 0 || batch <= 0) return hipSuccess;
   dim3 grid((cols + 31) / 32, (rows + 31) / 32, batch);
   timing_begin("transpose", s);
-  if (is_bf16)
-    hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(256), 0, s,
+  if (s_kind == K_BF16 && d_kind == K_BF16)
+    hipLaunchKernelGGL((transpose_kernel<bf16, bf16>), grid, dim3(256), 0, s,
                        (const bf16*)src, rows, cols, ld_src, s_src, (bf16*)dst,
                        ld_dst, s_dst);
-  else
-    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, s,
+  else if (s_kind == K_BF16 && d_kind == K_F16)
+    hipLaunchKernelGGL((transpose_kernel<bf16, f16>), grid, dim3(256), 0, s,
+                       (const bf16*)src, rows, cols, ld_src, s_src, (f16*)dst,
+                       ld_dst, s_dst);
+  else if (s_kind == K_F32 && d_kind == K_F32)
+    hipLaunchKernelGGL((transpose_kernel<float, float>), grid, dim3(256), 0, s,
                        (const float*)src, rows, cols, ld_src, s_src,
                        (float*)dst, ld_dst, s_dst);
+  else
+    return hipErrorInvalidValue;
   timing_end(s);
   return hipGetLastError();
 }

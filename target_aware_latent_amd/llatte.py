@@ -66,7 +66,12 @@ class llatte_attn_desc(ctypes.Structure):
 _SIGS = {
     "llatte_mla_forward": (_c_int, [
         ctypes.POINTER(llatte_model_desc), ctypes.POINTER(llatte_weights),
-        _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+        _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp,
+        _vp, ctypes.c_size_t, _vp]),
+    "llatte_packed_weights_size": (ctypes.c_size_t, [
+        ctypes.POINTER(llatte_model_desc)]),
+    "llatte_pack_weights": (_c_int, [
+        ctypes.POINTER(llatte_model_desc), ctypes.POINTER(llatte_weights), _vp,
         ctypes.c_size_t, _vp]),
     "llatte_mla_forward_workspace_size": (ctypes.c_size_t, [
         ctypes.POINTER(llatte_model_desc), _c_int, _c_int, _c_int]),
@@ -148,16 +153,28 @@ def llatte_mla_forward_workspace_size(desc, B, total_rows, max_len):
                                                    total_rows, max_len)
 
 
-def llatte_mla_forward(desc, weights, hist_values, hist_offsets, B, total_rows,
-                       max_len, cand_x, ctx, out_cand, out_hist,
-                       out_hist_offsets, out_emb, workspace, stream=None):
+def llatte_mla_forward(desc, weights, packed_weights, hist_values,
+                       hist_offsets, B, total_rows, max_len, cand_x, ctx,
+                       out_cand, out_hist, out_hist_offsets, out_emb,
+                       workspace, stream=None):
     st = lib().llatte_mla_forward(
-        ctypes.byref(desc), ctypes.byref(weights), _p(hist_values),
-        _p(hist_offsets), B, total_rows, max_len, _p(cand_x), _p(ctx),
-        _p(out_cand), _p(out_hist), _p(out_hist_offsets), _p(out_emb),
-        _p(workspace), workspace.numel() * workspace.element_size(),
-        _stream(stream))
+        ctypes.byref(desc), None if weights is None else ctypes.byref(weights),
+        _p(packed_weights), _p(hist_values), _p(hist_offsets), B, total_rows,
+        max_len, _p(cand_x), _p(ctx), _p(out_cand), _p(out_hist),
+        _p(out_hist_offsets), _p(out_emb), _p(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "llatte_mla_forward")
+
+
+def llatte_packed_weights_size(desc):
+    return lib().llatte_packed_weights_size(ctypes.byref(desc))
+
+
+def llatte_pack_weights(desc, weights, packed, stream=None):
+    st = lib().llatte_pack_weights(
+        ctypes.byref(desc), ctypes.byref(weights), _p(packed),
+        packed.numel() * packed.element_size(), _stream(stream))
+    _check(st, "llatte_pack_weights")
 
 
 def llatte_mla_attention_workspace_size(adesc, B, Mtot, Ktot):

@@ -88,6 +88,16 @@ class DeviceModel:
             w.W_p = mat(W["W_p"]).data_ptr()
         self.weights = w
         self._ws = None
+        self.packed = None
+
+    def pack(self, stream=None):
+        """Write the packed-weight blob once; later forwards reuse it."""
+        n = C.llatte_packed_weights_size(self.desc)
+        if n == 0:
+            raise C.LlatteError(-1, "llatte_packed_weights_size")
+        self.packed = torch.empty(n, dtype=torch.uint8, device=self.device)
+        C.llatte_pack_weights(self.desc, self.weights, self.packed, stream)
+        return self.packed
 
     def workspace(self, B, total, max_len):
         n = C.llatte_mla_forward_workspace_size(self.desc, B, total, max_len)
@@ -124,7 +134,8 @@ class DeviceModel:
         if out is None:
             out = self.alloc_outputs(lengths)
         ws = self.workspace(B, total, max_len)
-        C.llatte_mla_forward(self.desc, self.weights, hist, offsets, B, total,
-                             max_len, cand, ctx, out["cand"], out["hist"],
-                             out["hist_offsets"], out["emb"], ws, stream)
+        C.llatte_mla_forward(self.desc, self.weights, self.packed, hist,
+                             offsets, B, total, max_len, cand, ctx,
+                             out["cand"], out["hist"], out["hist_offsets"],
+                             out["emb"], ws, stream)
         return out

@@ -63,7 +63,8 @@ def test_invalid_descriptors_rejected_on_host(L):
     good = make_desc(cfg)
     assert L.llatte_mla_forward_workspace_size(good, 4, 100, 50) > 0
     for field, val in [("d_ff", 3 * cfg.d), ("rank", 96), ("dtype", 7),
-                       ("n_layers", 0), ("head_dim", 12), ("flags", 1)]:
+                       ("n_layers", 0), ("head_dim", 12), ("head_dim", 48),
+                       ("flags", 1)]:
         d = make_desc(cfg)
         setattr(d, field, val)
         assert L.llatte_mla_forward_workspace_size(d, 4, 100, 50) == 0, field
@@ -72,6 +73,7 @@ def test_invalid_descriptors_rejected_on_host(L):
     assert L.llatte_mla_forward_workspace_size(d, 4, 100, 50) == 0
     # total_rows < B (some user would be empty)
     assert L.llatte_mla_forward_workspace_size(good, 4, 3, 50) == 0
+    assert L.llatte_packed_weights_size(good) > 0
 
 
 def test_forward_argument_errors_return_status_without_launch(L):
@@ -79,9 +81,9 @@ def test_forward_argument_errors_return_status_without_launch(L):
     cfg = synth.get_config("c2")
     d = make_desc(cfg)
     w = L.llatte_weights()
-    st = L.lib().llatte_mla_forward(ctypes.byref(d), ctypes.byref(w), None, None,
-                                    4, 100, 50, None, None, None, None, None,
-                                    None, None, 0, None)
+    st = L.lib().llatte_mla_forward(ctypes.byref(d), ctypes.byref(w), None,
+                                    None, None, 4, 100, 50, None, None, None,
+                                    None, None, None, None, 0, None)
     assert st == L.LLATTE_ERR_INVALID_ARG
     assert "NULL" in L.llatte_last_error()
     ad = L.llatte_attn_desc(4, 96, 0, L.LLATTE_BF16, 0.125)

@@ -246,11 +246,13 @@ def test_token_embed_matches_oracle(dt):
 
 # ---------------------------------------------------------------- whole stack
 
-def gpu_forward(prob, hist=None, cand=None):
+def gpu_forward(prob, hist=None, cand=None, packed=True):
     from target_aware_latent_amd.model import DeviceModel
     cfg = prob["cfg"]
     I = prob["inputs"]
     model = DeviceModel(cfg, prob["weights"])
+    if packed:
+        model.pack()
     lengths = [int(x) for x in I["lengths"]]
     h = dev(I["hist"] if hist is None else hist)
     c = None
@@ -332,7 +334,7 @@ def test_forward_small_matches_oracle(name):
 def test_forward_is_deterministic():
     prob = small("c4", [1, 64, 65, 129, 300, 513, 200])
     a = gpu_forward(prob)
-    b = gpu_forward(prob)
+    b = gpu_forward(prob, packed=False)   # weights packed inside the call
     for k in a:
         if a[k] is not None:
             assert np.array_equal(a[k], b[k]), k
@@ -351,4 +353,68 @@ def test_forward_full_size(name, users):
     B = prob["cfg"].B
     users = list(range(B)) if users is None else users
     ref = oracle_forward(prob, users=users)
+    compare_stack(prob, got, ref, users)
+
+
+def build_semantic_tokens(cfg, prob, seed=0):
+    """Device table (streamed block by block) and the GPU token build of the
+    history and candidate tokens through llatte_token_embed."""
+    sp = cfg.semantic
+    I, W = prob["inputs"], prob["weights"]
+    table = torch.empty(sp.vocab, cfg.d, dtype=torch.bfloat16, device="cuda")
+    for row0, blk in synth.full_table(cfg, seed):
+        table[row0:row0 + blk.shape[0]] = torch.from_numpy(blk).to("cuda").to(torch.bfloat16)
+    Ws = dev(W["W_s"], torch.bfloat16)
+    ws = torch.empty(L().llatte_token_embed_workspace_size(cfg.d, sp.d_sem, L().LLATTE_BF16),
+                     dtype=torch.uint8, device="cuda")
+    out = {}
+    for key in ("hist", "cand"):
+        ids, sem = I[f"{key}_ids"], I[f"{key}_sem"]
+        o = torch.empty(ids.size, cfg.d, device="cuda")
+        L().llatte_token_embed(table, sp.vocab, idev(ids), dev(sem, torch.bfloat16), Ws,
+                               ids.size, cfg.d, sp.d_sem, L().LLATTE_BF16, o, ws)
+        out[key] = o
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.timeout(900)
+def test_forward_full_size_semantic_tokens():
+    """12 layers, d=1024, r=256, 16 candidates: token build from the 1M x 1024
+    hashed-ID table plus W_s times the semantic vector, then the stack; the
+    token build is checked on sampled rows and the stack on sampled users."""
+    print("forward full c5", flush=True)
+    cfg = synth.get_config("c5")
+    prob = synth.generate(cfg)
+    I, W = prob["inputs"], prob["weights"]
+    tok = build_semantic_tokens(cfg, prob)
+    users = [0, 17, 31]
+    off = I["offsets"]
+    # token build, sampled users' rows, against the oracle's token build
+    hist_ref, cand_ref = {}, {}
+    for u in users:
+        rows = I["hist_ids"][off[u]:off[u + 1]]
+        hist_ref[u] = O.token_embed(synth.table_rows(cfg, 0, rows).astype(np.float64),
+                                    I["hist_sem"][off[u]:off[u + 1]].astype(np.float64),
+                                    W["W_s"].astype(np.float64))
+        crow = I["cand_ids"][u * cfg.n_q:(u + 1) * cfg.n_q]
+        cand_ref[u] = O.token_embed(synth.table_rows(cfg, 0, crow).astype(np.float64),
+                                    I["cand_sem"][u * cfg.n_q:(u + 1) * cfg.n_q].astype(np.float64),
+                                    W["W_s"].astype(np.float64))
+        check(tok["hist"][off[u]:off[u + 1]].cpu().numpy(), hist_ref[u], "bf16",
+              f"token_embed user {u}")
+    from target_aware_latent_amd.model import DeviceModel
+    model = DeviceModel(cfg, W)
+    model.pack()
+    lengths = [int(x) for x in I["lengths"]]
+    got = model.forward(tok["hist"], idev(off), lengths, tok["cand"], dev(I["ctx"]))
+    torch.cuda.synchronize()
+    got = {k: (None if v is None else v.cpu().numpy()) for k, v in got.items()}
+    # oracle on the oracle's own tokens for the sampled users
+    hist_o = np.zeros((off[-1], cfg.d))
+    cand_o = np.zeros((cfg.B * cfg.n_q, cfg.d))
+    for u in users:
+        hist_o[off[u]:off[u + 1]] = hist_ref[u]
+        cand_o[u * cfg.n_q:(u + 1) * cfg.n_q] = cand_ref[u]
+    ref = O.forward(cfg, W, hist_o, off, cand_o, I["ctx"], users=users)
     compare_stack(prob, got, ref, users)

@@ -136,6 +136,9 @@ def main():
     ap.add_argument("--config", default="c3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-times", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain 256 MiB device-to-device copy first, "
+                         "as the reference for HBM byte counters")
     ap.add_argument("--traffic", default=None,
                     help="JSON file with measured HBM bytes per launch of the "
                          "dominant kernel ({'kernel':..., 'bytes':...})")
@@ -167,6 +170,13 @@ def main():
     ctx = dev(I["ctx"]) if (cfg.n_q and cfg.d_c) else None
     out = model.alloc_outputs(lengths)
     stream = torch.cuda.current_stream()
+    if args.calibrate_copy:
+        src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     step = lambda: model.forward(hist, offs, lengths, cand, ctx, out=out, stream=stream)
 
     for _ in range(args.warmup):

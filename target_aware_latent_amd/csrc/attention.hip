@@ -17,11 +17,19 @@
 //                                straight from the S^T accumulators
 // Working on the transposed products keeps each lane's softmax column and
 // output column the same effective row: the rescale needs no shuffles and P
-// never goes through LDS. The tile is staged twice (row-major for S^T,
-// transposed for O^T), double-buffered. Operand k-order: both MFMA operands
-// of a product use the same permutation of the contraction index (lane group
-// g holds k = 4g..4g+3 and 16+4g..16+4g+3 of each 32-wide step), which is
-// what the S^T accumulator layout hands to the P^T operand.
+// never goes through LDS. The tile is staged once, row-major and
+// double-buffered; the C^T operand is read from it with the gfx950 transpose
+// load (ds_read_b64_tr_b16: within each 16-lane group, lane i receives column
+// i of the 4x16 block whose rows the group's lanes address). The 8-byte
+// chunks of each tile row are XOR-swizzled by a function of the key's low
+// nibble, chosen so that with 64 four-byte LDS banks every 32-lane pass of
+// the three access patterns (S^T reads: 16 keys x 2 chunks; transpose reads:
+// 8 keys x 4 chunks; staging writes) touches 32 distinct 8-byte bank slots
+// (for r = 256 the staging writes keep a 2-way conflict). The swizzled
+// offsets are lane constants, computed once. Operand k-order: both MFMA operands of a product
+// use the same permutation of the contraction index (lane group g holds
+// k = 4g..4g+3 and 16+4g..16+4g+3 of each 32-wide step), which is what the
+// S^T accumulator layout hands to the P^T operand.
 //
 // Operands are fp16 (the latent C and queries are RMS-normalised, well
 // inside fp16 range, and P lies in [0, 1]): 11 mantissa bits instead of 8,
@@ -63,6 +71,10 @@ __device__ __forceinline__ f16x8 pack8(f32x4 lo, f32x4 hi, float s) {
   return f16x8{(f16)(lo[0] * s), (f16)(lo[1] * s), (f16)(lo[2] * s), (f16)(lo[3] * s),
                (f16)(hi[0] * s), (f16)(hi[1] * s), (f16)(hi[2] * s), (f16)(hi[3] * s)};
 }
+__device__ __forceinline__ f16x8 pack8(f32x4 lo, f32x4 hi) {
+  return f16x8{(f16)lo[0], (f16)lo[1], (f16)lo[2], (f16)lo[3],
+               (f16)hi[0], (f16)hi[1], (f16)hi[2], (f16)hi[3]};
+}
 __device__ __forceinline__ f16x8 cat(f16x4 lo, f16x4 hi) {
   return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
@@ -75,6 +87,31 @@ __device__ __forceinline__ f16x8 to_f16x8(i32x4 raw, bool is_bf16) {
   return r;
 }
 
+typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 hx4_t;
+typedef __attribute__((address_space(3))) hx4_t lds_hx4;
+typedef __attribute__((address_space(3))) f16 lds_f16;
+
+// Transposed 4x16 read (see the header comment); p points into LDS.
+__device__ __forceinline__ f16x4 lds_read_tr(const f16* p) {
+  auto q = (lds_hx4*)((lds_f16*)(f16*)p);
+  return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(q));
+}
+
+// XOR mask of the 8-byte chunks of tile row `key` (physical = logical ^ mask).
+template <int R>
+__device__ __forceinline__ int swz_key(int key) {
+  const int k = key & 15;
+  if constexpr (R == 64) {
+    // masks for keys 0..15, one nibble each (key 0 in the low nibble):
+    // 7 2 2 7 15 11 8 14 4 9 13 0 11 13 0 4 (found by exhaustive checking of
+    // the three access patterns; rows are half a bank window wide)
+    constexpr unsigned long long tab = 0x40db0d94e8bf7227ull;
+    return (int)((tab >> (4 * k)) & 15);
+  } else {
+    return 4 * (k & 7) + 2 * (k >> 3) + (k & 1);
+  }
+}
+
 struct AttnCfg {
   int HG;  // heads per workgroup
   int BQ;  // query rows per workgroup (multiple of 16)
@@ -83,16 +120,14 @@ struct AttnCfg {
 template <int R, int EPW, int DK, bool FUSED, typename CT>
 __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams p, AttnCfg cfg) {
   constexpr int BN = kAttnBN;        // keys per tile
-  constexpr int LDC = R + 8;         // row-major tile pitch (f16)
-  constexpr int LDT = BN + 8;        // transposed tile pitch (f16)
   constexpr int NEB = EPW / 16;      // effective-row blocks per wave
   constexpr int NKS = R / 32;        // 32-wide steps over r
   constexpr int NRB = R / 16;        // 16-wide blocks over r
-  constexpr int NLD = (2 * R + 511) / 512;  // 4-key x 8-r blocks per thread
+  constexpr int NLD = BN * R / 8 / 512;  // 16-byte chunks per thread and tile
+  static_assert(NLD >= 1, "tile too small for the staging map");
   constexpr bool C_BF16 = __is_same(CT, bf16);
 
-  __shared__ __attribute__((aligned(16))) f16 Cs[2][BN * LDC];
-  __shared__ __attribute__((aligned(16))) f16 Ct[2][R * LDT];
+  __shared__ __attribute__((aligned(16))) f16 Cs[2][BN * R];
 
   const int nitems = min(*p.n_items, p.items_cap);
   if ((int)blockIdx.x >= nitems) return;
@@ -165,40 +200,54 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams p, AttnCfg cf
     }
   }
 
-  // C tile staging: block b covers keys 4*kq .. 4*kq+3 and r 8*rc .. 8*rc+7
-  i32x4 ld[NLD][4];
+  // C tile staging: chunk idx covers key idx / (R/8), r 8*(idx % (R/8)) .. +7.
+  // Global offsets and swizzled LDS offsets (in halves) are fixed per thread.
+  i32x4 ld[NLD];
+  int ld_src[NLD], st_off0[NLD], st_off1[NLD], ld_key[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int idx = tid + i * 512;
+    const int key = idx / (R / 8), j = idx % (R / 8);
+    const int kv = swz_key<R>(key);
+    ld_key[i] = key;
+    ld_src[i] = key * R + j * 8;
+    st_off0[i] = key * R + ((2 * j) ^ kv) * 4;
+    st_off1[i] = key * R + ((2 * j + 1) ^ kv) * 4;
+  }
   auto load_tile = [&](int t) {
     const int k0 = t * BN;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int b = tid + i * 512;
-      const int rc = b % (R / 8), kq = b / (R / 8);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = k0 + kq * 4 + j;
-        ld[i][j] = (b < 2 * R && key < nkeys)
-                       ? *(const i32x4*)(Cg + (size_t)key * R + rc * 8)
-                       : i32x4{0, 0, 0, 0};
-      }
-    }
+    for (int i = 0; i < NLD; ++i)
+      ld[i] = (k0 + ld_key[i] < nkeys) ? *(const i32x4*)(Cg + (size_t)k0 * R + ld_src[i])
+                                       : i32x4{0, 0, 0, 0};
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int b = tid + i * 512;
-      if (b >= 2 * R) continue;
-      const int rc = b % (R / 8), kq = b / (R / 8);
-      f16x8 v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[j] = to_f16x8(ld[i][j], C_BF16);
-        *(f16x8*)&Cs[buf][(kq * 4 + j) * LDC + rc * 8] = v[j];
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *(f16x4*)&Ct[buf][(rc * 8 + e) * LDT + kq * 4] = f16x4{v[0][e], v[1][e], v[2][e], v[3][e]};
+      const f16x8 v = to_f16x8(ld[i], C_BF16);
+      *(f16x4*)&Cs[buf][st_off0[i]] = f16x4{v[0], v[1], v[2], v[3]};
+      *(f16x4*)&Cs[buf][st_off1[i]] = f16x4{v[4], v[5], v[6], v[7]};
     }
   };
+
+  // S^T operand reads: row kb*16 + l16, chunk c = 4x + g with x = 2*ks (+1);
+  // the mask depends on l16 only and is below 32, so chunks 32 apart differ
+  // by a constant: 8 lane-constant offsets cover every x.
+  constexpr int NOS = 2 * NKS < 8 ? 2 * NKS : 8;
+  constexpr int NOT = NRB < 8 ? NRB : 8;
+  int offS[NOS], offT[NOT];
+  {
+    const int kv = swz_key<R>(l16);
+#pragma unroll
+    for (int x = 0; x < NOS; ++x) offS[x] = l16 * R + ((x * 4 + g) ^ kv) * 4;
+    // transpose reads: rows kk*32 (+16) + 4g + (l16 >> 2), chunk rb*4 + (l16 & 3)
+    const int tk = 4 * g + (l16 >> 2);
+    const int kt = swz_key<R>(tk);
+#pragma unroll
+    for (int rb = 0; rb < NOT; ++rb) offT[rb] = tk * R + ((rb * 4 + (l16 & 3)) ^ kt) * 4;
+  }
+  auto off_s = [&](int x) { return offS[x % 8] + (x / 8) * 128; };
+  auto off_t = [&](int rb) { return offT[rb % 8] + (rb / 8) * 128; };
 
   f32x4 acc_o[NRB][NEB];
 #pragma unroll
@@ -219,7 +268,6 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams p, AttnCfg cf
     const int cur = t & 1;
     if (t + 1 < ntiles) load_tile(t + 1);
     const f16* cs = Cs[cur];
-    const f16* ct = Ct[cur];
 
     // S^T[key][e], 64 keys
     f32x4 s[4][NEB];
@@ -227,10 +275,11 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams p, AttnCfg cf
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) s[kb][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const f16* rowb = cs + kb * 16 * R;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const f16* row = &cs[(kb * 16 + l16) * LDC + ks * 32 + g * 4];
-        const f16x8 a = cat(*(const f16x4*)row, *(const f16x4*)(row + 16));
+        const f16x8 a = cat(*(const f16x4*)&rowb[off_s(2 * ks)],
+                            *(const f16x4*)&rowb[off_s(2 * ks + 1)]);
 #pragma unroll
         for (int eb = 0; eb < NEB; ++eb) s[kb][eb] = mfma_f16(a, qf[eb][ks], s[kb][eb]);
       }
@@ -267,8 +316,8 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams p, AttnCfg cf
           s[kb][eb][v] = e;
           rs += e;
         }
-      pf[0][eb] = pack8(s[0][eb], s[1][eb], 1.f);
-      pf[1][eb] = pack8(s[2][eb], s[3][eb], 1.f);
+      pf[0][eb] = pack8(s[0][eb], s[1][eb]);
+      pf[1][eb] = pack8(s[2][eb], s[3][eb]);
       rs += __shfl_xor(rs, 16, 64);
       rs += __shfl_xor(rs, 32, 64);
       l_run[eb] = l_run[eb] * alpha + rs;
@@ -278,13 +327,14 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams p, AttnCfg cf
       }
     }
 
-    // O^T[r][e] += sum over keys of C^T[r][key] * P^T[key][e]
+    // O^T[r][e] += sum over keys of C^T[r][key] * P^T[key][e]; the C^T
+    // operand comes from the row-major tile through the transpose load
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const f16* row = &ct[(rb * 16 + l16) * LDT + kk * 32 + g * 4];
-        const f16x8 a = cat(*(const f16x4*)row, *(const f16x4*)(row + 16));
+        const f16x8 a = cat(lds_read_tr(cs + kk * 32 * R + off_t(rb)),
+                            lds_read_tr(cs + (kk * 32 + 16) * R + off_t(rb)));
 #pragma unroll
         for (int eb = 0; eb < NEB; ++eb) acc_o[rb][eb] = mfma_f16(a, pf[kk][eb], acc_o[rb][eb]);
       }

@@ -1,10 +1,12 @@
 // Tiled matrix product on the gfx950 matrix cores, with fused epilogues.
 //
 // Both operands are K-contiguous (A [M, K], B [N, K]); weights are brought to
-// this layout once per call by the transpose kernel. A workgroup of four
-// waves computes a BM x BN tile; K advances in BK steps through a
-// double-buffered LDS stage (rows padded by 16 bytes so that the 16-byte
-// fragment reads of 8 consecutive rows fall in distinct banks). The MFMA is
+// this layout once by the packing step. A workgroup of four waves computes a
+// BM x BN tile; K advances in BK steps through a double-buffered LDS stage.
+// A tile row is 128 bytes (eight 16-byte chunks) with chunk c of row r
+// stored at c ^ ((r >> 1) & 7): with 64 four-byte banks, a 16-lane pass of
+// fragment reads (16 rows, one chunk) and of staging writes (2 rows, 8
+// chunks) each covers all 64 banks once. The MFMA is
 // issued with the operands swapped (B fragment first) so that each lane ends
 // up holding four consecutive output columns of one row: the epilogue then
 // reads residuals and writes results as 8- or 16-byte vectors.
@@ -33,8 +35,22 @@ template <> struct Mfma<float> {
   }
 };
 
+// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26 (|error| <= 1.5e-7): for z >= 0, erf(z) = 1 - t (a1 + t (a2 + t (a3
+// + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 + p z); odd in z.
+__device__ __forceinline__ float erf_as(float z) {
+  const float az = fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(1.f + 0.3275911f * az);
+  const float poly =
+      t * (0.254829592f +
+           t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  const float e = __builtin_amdgcn_exp2f(-az * az * 1.4426950408889634f);
+  return copysignf(1.f - poly * e, z);
+}
+
+// GELU with the exact (erf) form, x * Phi(x).
 __device__ __forceinline__ float gelu_erf(float x) {
-  return 0.5f * x * (1.f + erff(x * 0.70710678118654752f));
+  return 0.5f * x * (1.f + erf_as(x * 0.70710678118654752f));
 }
 
 template <typename T>
@@ -61,7 +77,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   using MF = Mfma<T>;
   constexpr int CE = 16 / sizeof(T);       // elements per 16-byte chunk
   constexpr int BK = 8 * CE;               // 8 chunks per tile row
-  constexpr int LDK = BK + CE;             // padded LDS row (elements)
+  constexpr int LDK = BK;                  // LDS row (elements), swizzled
   constexpr int WAVES_N = BN / WN;
   static_assert((BM / WM) * (BN / WN) == 4, "four waves");
   constexpr int AI = BM * 8 / 256;         // A chunks per thread
@@ -128,16 +144,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
       rb[i] = ok ? *(const i32x4*)(brow[i] + k0) : i32x4{0, 0, 0, 0};
     }
   };
+  auto sw = [](int row, int chunk) { return row * LDK + ((chunk ^ ((row >> 1) & 7)) * CE); };
   auto store_lds = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       int c = tid + i * 256;
-      *(i32x4*)&As[buf][(c / 8) * LDK + (c % 8) * CE] = ra[i];
+      *(i32x4*)&As[buf][sw(c / 8, c % 8)] = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
       int c = tid + i * 256;
-      *(i32x4*)&Bs[buf][(c / 8) * LDK + (c % 8) * CE] = rb[i];
+      *(i32x4*)&Bs[buf][sw(c / 8, c % 8)] = rb[i];
     }
   };
 
@@ -151,6 +168,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   const int wn0 = (wave % WAVES_N) * WN;
   const int lr = lane & 15;                 // fragment row
   const int lk = (lane >> 4) * MF::VEC;     // fragment k offset
+  // swizzled in-row offset of each k step (fragment rows are 16-aligned, so
+  // the swizzle depends on lr only)
+  constexpr int NKK = BK / MF::KSTEP;
+  int koff[NKK];
+#pragma unroll
+  for (int x = 0; x < NKK; ++x) {
+    const int e = x * MF::KSTEP + lk;
+    koff[x] = ((e / CE) ^ ((lr >> 1) & 7)) * CE + e % CE;
+  }
 
   const int nk = (p.K + BK - 1) / BK;
   load_tile(0);
@@ -162,14 +188,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
     const T* as = As[cur];
     const T* bs = Bs[cur];
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += MF::KSTEP) {
+    for (int x = 0; x < NKK; ++x) {
       typename MF::frag fa[TM], fb[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        fa[i] = *(const typename MF::frag*)&as[(wm0 + i * 16 + lr) * LDK + kk + lk];
+        fa[i] = *(const typename MF::frag*)&as[(wm0 + i * 16 + lr) * LDK + koff[x]];
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        fb[j] = *(const typename MF::frag*)&bs[(wn0 + j * 16 + lr) * LDK + kk + lk];
+        fb[j] = *(const typename MF::frag*)&bs[(wn0 + j * 16 + lr) * LDK + koff[x]];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll

@@ -13,6 +13,8 @@
 //
 // bf16 operands use v_mfma_f32_16x16x32_bf16; fp32 operands use
 // v_mfma_f32_16x16x4_f32. Accumulation is fp32 in both cases.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace llatte {
@@ -72,16 +74,17 @@ template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
   return f32x4{from_bf16(v[0]), from_bf16(v[1]), from_bf16(v[2]), from_bf16(v[3])};
 }
 
-template <typename T, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
+template <typename T, int BM, int BN, int WM, int WN, int NW, int PF>
+__global__ __launch_bounds__(64 * NW) void gemm_kernel(GemmParams p) {
   using MF = Mfma<T>;
+  constexpr int NT = 64 * NW;              // threads
   constexpr int CE = 16 / sizeof(T);       // elements per 16-byte chunk
   constexpr int BK = 8 * CE;               // 8 chunks per tile row
   constexpr int LDK = BK;                  // LDS row (elements), swizzled
   constexpr int WAVES_N = BN / WN;
-  static_assert((BM / WM) * (BN / WN) == 4, "four waves");
-  constexpr int AI = BM * 8 / 256;         // A chunks per thread
-  constexpr int BI = BN * 8 / 256;
+  static_assert((BM / WM) * (BN / WN) == NW, "wave grid");
+  constexpr int AI = BM * 8 / NT;          // A chunks per thread
+  constexpr int BI = BN * 8 / NT;
   constexpr int TM = WM / 16, TN = WN / 16;
 
   __shared__ __attribute__((aligned(16))) T As[2][BM * LDK];
@@ -112,7 +115,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   bool aok[AI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
-    int c = tid + i * 256;
+    int c = tid + i * NT;
     int r = m0 + c / 8;
     aok[i] = r < M;
     int src = aok[i] ? (p.a_rows ? p.a_rows[r] : r) : 0;
@@ -122,39 +125,44 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   bool bok[BI];
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
-    int c = tid + i * 256;
+    int c = tid + i * NT;
     int r = n0 + c / 8;
     bok[i] = r < p.N;
     brow[i] = Bm + (size_t)(bok[i] ? r : 0) * p.ldb + (c % 8) * CE;
   }
 
-  i32x4 ra[AI], rb[BI];
-  auto load_tile = [&](int kt) {
+  // Two register sets: the loads of K step k+2 are issued while step k is
+  // computed from LDS and step k+1 waits in the other set, so each load has
+  // two compute phases to arrive.
+  i32x4 ra[PF][AI], rb[PF][BI];
+  auto load_tile = [&](int kt, auto set) {
+    constexpr int S = decltype(set)::value;
     const int k0 = kt * BK;
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
-      int kc = ((tid + i * 256) % 8) * CE;
+      int kc = ((tid + i * NT) % 8) * CE;
       bool ok = aok[i] && (k0 + kc < p.K);
-      ra[i] = ok ? *(const i32x4*)(arow[i] + k0) : i32x4{0, 0, 0, 0};
+      ra[S][i] = ok ? *(const i32x4*)(arow[i] + k0) : i32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
-      int kc = ((tid + i * 256) % 8) * CE;
+      int kc = ((tid + i * NT) % 8) * CE;
       bool ok = bok[i] && (k0 + kc < p.K);
-      rb[i] = ok ? *(const i32x4*)(brow[i] + k0) : i32x4{0, 0, 0, 0};
+      rb[S][i] = ok ? *(const i32x4*)(brow[i] + k0) : i32x4{0, 0, 0, 0};
     }
   };
   auto sw = [](int row, int chunk) { return row * LDK + ((chunk ^ ((row >> 1) & 7)) * CE); };
-  auto store_lds = [&](int buf) {
+  auto store_lds = [&](int buf, auto set) {
+    constexpr int S = decltype(set)::value;
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
-      int c = tid + i * 256;
-      *(i32x4*)&As[buf][sw(c / 8, c % 8)] = ra[i];
+      int c = tid + i * NT;
+      *(i32x4*)&As[buf][sw(c / 8, c % 8)] = ra[S][i];
     }
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
-      int c = tid + i * 256;
-      *(i32x4*)&Bs[buf][sw(c / 8, c % 8)] = rb[i];
+      int c = tid + i * NT;
+      *(i32x4*)&Bs[buf][sw(c / 8, c % 8)] = rb[S][i];
     }
   };
 
@@ -179,14 +187,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   }
 
   const int nk = (p.K + BK - 1) / BK;
-  load_tile(0);
-  store_lds(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_tile(kt + 1);
-    const T* as = As[cur];
-    const T* bs = Bs[cur];
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  auto compute = [&](int buf) {
+    const T* as = As[buf];
+    const T* bs = Bs[buf];
 #pragma unroll
     for (int x = 0; x < NKK; ++x) {
       typename MF::frag fa[TM], fb[TN];
@@ -201,9 +206,36 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(fb[j], fa[i], acc[i][j]);
     }
-    if (kt + 1 < nk) store_lds(cur ^ 1);
+  };
+  // one K step: prefetch kt+2 into the set that held kt, compute kt, stage kt+1
+  // PF == 2: two register sets (prefetch distance 2); PF == 1: one set,
+  // loads of step k+1 issued while step k is computed.
+  auto step = [&](int kt, auto set) {
+    constexpr int S = decltype(set)::value;
+    if constexpr (PF == 2) {
+      using Sn = std::integral_constant<int, S ^ 1>;
+      if (kt + 2 < nk) load_tile(kt + 2, set);
+      compute(kt & 1);
+      if (kt + 1 < nk) store_lds((kt + 1) & 1, Sn{});
+    } else {
+      if (kt + 1 < nk) load_tile(kt + 1, S0{});
+      compute(kt & 1);
+      if (kt + 1 < nk) store_lds((kt + 1) & 1, S0{});
+    }
     __syncthreads();
+  };
+  load_tile(0, S0{});
+  if constexpr (PF == 2) {
+    if (nk > 1) load_tile(1, S1{});
   }
+  store_lds(0, S0{});
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, S0{});
+    step(kt + 1, S1{});
+  }
+  if (kt < nk) step(kt, S0{});
 
   // Epilogue: lane holds C[m][n .. n+3] of each 16x16 block.
 #pragma unroll
@@ -246,25 +278,33 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   }
 }
 
-template <typename T, int BM, int BN, int WM, int WN>
+template <typename T, int BM, int BN, int WM, int WN, int NW, int PF = 1>
 static hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   const int tiles = ((p.M_cap + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   if (tiles == 0 || p.batch == 0) return hipSuccess;
   timing_begin(p.name, s);
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN>), dim3(tiles, 1, p.batch),
-                     dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, NW, PF>), dim3(tiles, 1, p.batch),
+                     dim3(64 * NW), 0, s, p);
   timing_end(s);
   return hipGetLastError();
 }
 
+static long long ntiles(const GemmParams& p, int bm, int bn) {
+  return (long long)((p.M_cap + bm - 1) / bm) * ((p.N + bn - 1) / bn) * p.batch;
+}
+
+// Tile choice: 128x128 with eight waves (32x64 each) when that gives the
+// GPU (256 CUs) enough workgroups; 64x64 tiles for the small products
+// (readout layer, last pyramid layers) that would otherwise occupy a few CUs.
 hipError_t gemm(const GemmParams& p, bool is_bf16, hipStream_t s) {
   if (p.M_cap <= 0 || p.N <= 0) return hipSuccess;
   if (is_bf16) {
-    if (p.N <= 64) return launch_gemm<bf16, 128, 64, 64, 32>(p, s);
-    return launch_gemm<bf16, 128, 128, 64, 64>(p, s);
+    if (ntiles(p, 128, 128) < 256) return launch_gemm<bf16, 64, 64, 32, 32, 4>(p, s);
+    if (p.N <= 64) return launch_gemm<bf16, 128, 64, 64, 32, 4>(p, s);
+    return launch_gemm<bf16, 128, 128, 32, 64, 8>(p, s);
   }
-  if (p.N <= 64) return launch_gemm<float, 128, 64, 64, 32>(p, s);
-  return launch_gemm<float, 128, 128, 64, 64>(p, s);
+  if (p.N <= 64) return launch_gemm<float, 128, 64, 64, 32, 4>(p, s);
+  return launch_gemm<float, 128, 128, 64, 64, 4>(p, s);
 }
 
 }  // namespace llatte

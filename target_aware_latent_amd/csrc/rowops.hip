@@ -46,11 +46,9 @@ __global__ __launch_bounds__(256) void norm_rows_kernel(
     }
     if (out_f32) *(f32x4*)(out_f32 + (size_t)row * ld_f32 + idx) = y;
     if (out_t) {
-      T* o = out_t + (size_t)row * ld_t + idx;
-      o[0] = cvt<T>(y[0]);
-      o[1] = cvt<T>(y[1]);
-      o[2] = cvt<T>(y[2]);
-      o[3] = cvt<T>(y[3]);
+      typedef T T4 __attribute__((ext_vector_type(4)));
+      *(T4*)(out_t + (size_t)row * ld_t + idx) =
+          T4{cvt<T>(y[0]), cvt<T>(y[1]), cvt<T>(y[2]), cvt<T>(y[3])};
     }
   }
 }

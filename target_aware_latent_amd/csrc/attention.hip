@@ -10,9 +10,10 @@
 //   S^T = C_tile . Qlat^T        v_mfma_f32_16x16x32_f16; A = C rows (LDS),
 //                                B = latent queries held in registers
 //   online softmax per column    fp32, exp2 (the softmax scale and log2(e)
-//                                are folded into the latent queries); max and
-//                                sum over a column's four lane groups with
-//                                two xor shuffles
+//                                are folded into the latent queries); the
+//                                column max over the four lane groups with
+//                                two permlane swaps, the column sums on the
+//                                matrix cores (ones operand)
 //   O^T += C_tile^T . P^T        A = C^T from a transposed LDS copy, B = P^T
 //                                straight from the S^T accumulators
 // Working on the transposed products keeps each lane's softmax column and
@@ -52,6 +53,7 @@ namespace llatte {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.f;  // running-max slack, log2 units
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
@@ -59,6 +61,19 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
+}
+// Max over the four lanes l, l^16, l^32, l^48 (a column of an MFMA
+// accumulator block spans the four 16-lane groups). Each permlane swap hands
+// a lane its own value and its partner's, in an order that differs between
+// the two lanes of a pair; the max of the two is order-free. Runs on the VALU,
+// no LDS round trip.
+__device__ __forceinline__ float max_across_groups(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+  const unsigned w = __float_as_uint(x);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
 }
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -202,31 +217,30 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams p, AttnCfg cf
 
   // C tile staging: chunk idx covers key idx / (R/8), r 8*(idx % (R/8)) .. +7.
   // Global offsets and swizzled LDS offsets (in halves) are fixed per thread.
+  // (the second 8-byte chunk of a pair sits at the first's offset XOR 4
+  // halves: the mask flips at most bit 0 of the chunk index)
   i32x4 ld[NLD];
-  int ld_src[NLD], st_off0[NLD], st_off1[NLD], ld_key[NLD];
+  int ld_src[NLD], st_off[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
     const int idx = tid + i * 512;
     const int key = idx / (R / 8), j = idx % (R / 8);
-    const int kv = swz_key<R>(key);
-    ld_key[i] = key;
     ld_src[i] = key * R + j * 8;
-    st_off0[i] = key * R + ((2 * j) ^ kv) * 4;
-    st_off1[i] = key * R + ((2 * j + 1) ^ kv) * 4;
+    st_off[i] = key * R + ((2 * j) ^ swz_key<R>(key)) * 4;
   }
   auto load_tile = [&](int t) {
     const int k0 = t * BN;
 #pragma unroll
     for (int i = 0; i < NLD; ++i)
-      ld[i] = (k0 + ld_key[i] < nkeys) ? *(const i32x4*)(Cg + (size_t)k0 * R + ld_src[i])
-                                       : i32x4{0, 0, 0, 0};
+      ld[i] = (k0 + ld_src[i] / R < nkeys) ? *(const i32x4*)(Cg + (size_t)k0 * R + ld_src[i])
+                                           : i32x4{0, 0, 0, 0};
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const f16x8 v = to_f16x8(ld[i], C_BF16);
-      *(f16x4*)&Cs[buf][st_off0[i]] = f16x4{v[0], v[1], v[2], v[3]};
-      *(f16x4*)&Cs[buf][st_off1[i]] = f16x4{v[4], v[5], v[6], v[7]};
+      *(f16x4*)&Cs[buf][st_off[i]] = f16x4{v[0], v[1], v[2], v[3]};
+      *(f16x4*)&Cs[buf][st_off[i] ^ 4] = f16x4{v[4], v[5], v[6], v[7]};
     }
   };
 
@@ -234,58 +248,66 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams p, AttnCfg cf
   // the mask depends on l16 only and is below 32, so chunks 32 apart differ
   // by a constant: 8 lane-constant offsets cover every x.
   constexpr int NOS = 2 * NKS < 8 ? 2 * NKS : 8;
-  constexpr int NOT = NRB < 8 ? NRB : 8;
-  int offS[NOS], offT[NOT];
+  int offS[NOS];
   {
     const int kv = swz_key<R>(l16);
 #pragma unroll
     for (int x = 0; x < NOS; ++x) offS[x] = l16 * R + ((x * 4 + g) ^ kv) * 4;
-    // transpose reads: rows kk*32 (+16) + 4g + (l16 >> 2), chunk rb*4 + (l16 & 3)
-    const int tk = 4 * g + (l16 >> 2);
-    const int kt = swz_key<R>(tk);
-#pragma unroll
-    for (int rb = 0; rb < NOT; ++rb) offT[rb] = tk * R + ((rb * 4 + (l16 & 3)) ^ kt) * 4;
   }
   auto off_s = [&](int x) { return offS[x % 8] + (x / 8) * 128; };
-  auto off_t = [&](int rb) { return offT[rb % 8] + (rb / 8) * 128; };
+  // transpose reads: rows kk*32 (+16) + 4g + (l16 >> 2), chunk rb*4 + (l16 & 3);
+  // with the mask kt below 32, (4rb + j) ^ kt = 4 (rb ^ (kt >> 2)) + (j ^ (kt & 3))
+  const int tk = 4 * g + (l16 >> 2);
+  const int kt = swz_key<R>(tk);
+  const int baseT = tk * R + 4 * ((l16 & 3) ^ (kt & 3));
+  const int maskT = 16 * (kt >> 2);
+  auto off_t = [&](int rb) { return baseT + (((rb % 8) * 16) ^ maskT) + (rb / 8) * 128; };
 
   f32x4 acc_o[NRB][NEB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
     for (int eb = 0; eb < NEB; ++eb) acc_o[rb][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[NEB], l_run[NEB];
+  float m_run[NEB];
+  f32x4 acc_l[NEB];   // every element holds the row sum of P
 #pragma unroll
   for (int eb = 0; eb < NEB; ++eb) {
     m_run[eb] = -INFINITY;
-    l_run[eb] = 0.f;
+    acc_l[eb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const f16x8 kOnes = f16x8{(f16)1.f, (f16)1.f, (f16)1.f, (f16)1.f,
+                            (f16)1.f, (f16)1.f, (f16)1.f, (f16)1.f};
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-    const f16* cs = Cs[cur];
-
-    // S^T[key][e], 64 keys
-    f32x4 s[4][NEB];
+  // S^T[key][e] of the 64-key tile in LDS buffer cs
+  auto scores = [&](const f16* cs, f32x4 (&sc)[4][NEB]) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-      for (int eb = 0; eb < NEB; ++eb) s[kb][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int eb = 0; eb < NEB; ++eb) sc[kb][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
       const f16* rowb = cs + kb * 16 * R;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const f16x8 a = cat(*(const f16x4*)&rowb[off_s(2 * ks)],
                             *(const f16x4*)&rowb[off_s(2 * ks + 1)]);
 #pragma unroll
-        for (int eb = 0; eb < NEB; ++eb) s[kb][eb] = mfma_f16(a, qf[eb][ks], s[kb][eb]);
+        for (int eb = 0; eb < NEB; ++eb) sc[kb][eb] = mfma_f16(a, qf[eb][ks], sc[kb][eb]);
       }
     }
+    // issue order: operand reads run two steps ahead of the MFMAs using them
+#pragma unroll
+    for (int i = 0; i < 4 * NKS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, NEB, 0);  // NEB MFMAs
+    }
+  };
 
-    // online softmax per effective row (this lane's column of S^T)
+  // Online softmax of tile t's scores (this lane's column of S^T per block),
+  // then O^T += C^T P^T from the tile in LDS buffer cs. The running max only
+  // moves when a tile's max exceeds it by more than kLazy (log2 units):
+  // P = exp2(s - m_run) then stays <= 2^kLazy, exact enough in fp16, and the
+  // accumulators are rescaled only on those tiles. Row sums of the fp16 P
+  // are accumulated on the matrix cores with an all-ones A operand.
+  auto softmax_pv = [&](int t, f32x4 (&sc)[4][NEB], const f16* cs) {
     const bool need_mask = t * BN + BN - 1 > pmin;
     f16x8 pf[2][NEB];
 #pragma unroll
@@ -295,38 +317,30 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams p, AttnCfg cf
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            if (t * BN + kb * 16 + g * 4 + v > pos[eb]) s[kb][eb][v] = -INFINITY;
+            if (t * BN + kb * 16 + g * 4 + v > pos[eb]) sc[kb][eb][v] = -INFINITY;
       }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[kb][eb][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[eb], mx);
-      const float alpha = fast_exp2(m_run[eb] - m_new);
-      m_run[eb] = m_new;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float e = fast_exp2(s[kb][eb][v] - m_new);
-          s[kb][eb][v] = e;
-          rs += e;
-        }
-      pf[0][eb] = pack8(s[0][eb], s[1][eb]);
-      pf[1][eb] = pack8(s[2][eb], s[3][eb]);
-      rs += __shfl_xor(rs, 16, 64);
-      rs += __shfl_xor(rs, 32, 64);
-      l_run[eb] = l_run[eb] * alpha + rs;
-      if (__ballot(alpha != 1.f)) {
+      float mx = fmaxf(fmaxf(fmaxf(sc[0][eb][0], sc[0][eb][1]), fmaxf(sc[0][eb][2], sc[0][eb][3])),
+                       fmaxf(fmaxf(sc[1][eb][0], sc[1][eb][1]), fmaxf(sc[1][eb][2], sc[1][eb][3])));
+      mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sc[2][eb][0], sc[2][eb][1]), fmaxf(sc[2][eb][2], sc[2][eb][3])),
+                           fmaxf(fmaxf(sc[3][eb][0], sc[3][eb][1]), fmaxf(sc[3][eb][2], sc[3][eb][3]))));
+      mx = max_across_groups(mx);
+      const bool bump = mx > m_run[eb] + kLazy;   // true on the first tile (m_run = -inf)
+      if (__ballot(bump)) {
+        const float m_new = bump ? mx : m_run[eb];
+        const float alpha = fast_exp2(m_run[eb] - m_new);
+        m_run[eb] = m_new;
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) acc_o[rb][eb] *= alpha;
+        acc_l[eb] *= alpha;
       }
+      const float m = m_run[eb];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sc[kb][eb][v] = fast_exp2(sc[kb][eb][v] - m);
+      pf[0][eb] = pack8(sc[0][eb], sc[1][eb]);
+      pf[1][eb] = pack8(sc[2][eb], sc[3][eb]);
     }
-
     // O^T[r][e] += sum over keys of C^T[r][key] * P^T[key][e]; the C^T
     // operand comes from the row-major tile through the transpose load
 #pragma unroll
@@ -339,14 +353,35 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams p, AttnCfg cf
         for (int eb = 0; eb < NEB; ++eb) acc_o[rb][eb] = mfma_f16(a, pf[kk][eb], acc_o[rb][eb]);
       }
     }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int eb = 0; eb < NEB; ++eb) acc_l[eb] = mfma_f16(kOnes, pf[kk][eb], acc_l[eb]);
+#pragma unroll
+    for (int i = 0; i < 2 * NRB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // 2 transposed LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, NEB, 1);  // NEB MFMAs
+    }
+  };
 
+  // Double-buffered tiles: the next tile's global loads are in flight while
+  // this one is computed; one barrier per tile.
+  f32x4 st[4][NEB];
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1);
+    scores(&Cs[cur][0], st);
+    softmax_pv(t, st, &Cs[cur][0]);
     if (t + 1 < ntiles) store_tile(cur ^ 1);
     __syncthreads();
   }
 
 #pragma unroll
   for (int eb = 0; eb < NEB; ++eb) {
-    const float inv = 1.f / l_run[eb];
+    const float inv = 1.f / acc_l[eb][0];
     if constexpr (FUSED) {
       // o^T[k][e] = sum_r W_uv^T[head][k][r] * o_lat^T[r][e]
       f16x8 ob[NKS];
@@ -372,7 +407,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams p, AttnCfg cf
       float* op = (float*)p.out + orow * R + g * 4;
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) *(f32x4*)(op + rb * 16) = acc_o[rb][eb] * inv;
-      if (p.lse && g == 0) p.lse[orow] = (m_run[eb] + log2f(l_run[eb])) * kLn2;
+      if (p.lse && g == 0) p.lse[orow] = (m_run[eb] + log2f(acc_l[eb][0])) * kLn2;
     }
   }
 }
@@ -434,7 +469,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
 }
 
 // Effective rows per wave: register budget of the O accumulator.
-static int attn_epw(int r) { return r == 256 ? 16 : (r == 128 ? 32 : 64); }
+static int attn_epw(int r) { return r == 256 ? 16 : 32; }
 
 static AttnCfg attn_cfg(int h, int r) {
   const int eff = 8 * attn_epw(r);  // effective rows per workgroup
@@ -482,7 +517,7 @@ hipError_t attention(const AttnParams& p, bool is_bf16, hipStream_t s) {
   if (is_bf16) {
     if (p.items_cap > 0) {
       switch (p.r) {
-        case 64: e = launch_r<64, 64>(p, s); break;
+        case 64: e = launch_r<64, 32>(p, s); break;
         case 128: e = launch_r<128, 32>(p, s); break;
         case 256: e = launch_r<256, 16>(p, s); break;
         default: e = hipErrorInvalidValue;

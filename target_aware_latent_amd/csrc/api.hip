@@ -15,6 +15,14 @@
 //   R2  = R1 + GELU(RMSNorm(R1) W1) W2 (post: GELU(R1 W1) W2, then RMSNorm g2)
 // The output rows are exactly the next layer's row space, so the pyramidal
 // output extraction costs no copy.
+//
+// bf16 pre-norm path: the three RMSNorms run inside the GEMMs. A norm's row
+// scale s(x) = 1/sqrt(mean(x^2) + eps) commutes with the product that
+// follows it, RMSNorm(x) g W = s(x) * (x (diag(g) W)), so the gains are
+// folded into W_dkv, W_uq (g1) and W1 (g2) at packing, the producer of x (the
+// residual epilogues) also writes x as bf16 with per-row partial sums of
+// squares, and the consumer GEMM scales its rows in the epilogue. The latent
+// norm is the down-projection's epilogue (one tile spans the r columns).
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -122,6 +130,7 @@ struct Shapes {
   int B, total, max_len;
   int d, h, dk, hd, r, dff, N, nq, dc, ns, dout;
   bool bf16, pre, lnorm;
+  bool fnorm;                 // norms fused into the GEMMs (bf16, pre-norm)
   float eps;
   int NP;                     // plans: N layers (+ readout)
   RuleDev rule;
@@ -195,6 +204,7 @@ static llatte_status make_shapes(const llatte_model_desc* dsc, int B, int total,
   S->bf16 = dsc->dtype == LLATTE_BF16;
   S->pre = dsc->norm_mode == LLATTE_NORM_PRE;
   S->lnorm = dsc->latent_norm != 0;
+  S->fnorm = S->bf16 && S->pre;
   S->eps = dsc->eps;
   S->esz = S->bf16 ? 2 : 4;
   const int al = S->bf16 ? 8 : 4;  // 16-byte vectors of the dtype
@@ -294,6 +304,10 @@ static size_t layout_packed(const Shapes& S, void* base, Packed* P) {
   return ar.off + 256;
 }
 
+// Partial sums of squares per row written by a residual epilogue over d
+// columns (one per 32-column strip at most).
+static int kMaxSlots(const Shapes& S) { return (S.d + 31) / 32; }
+
 // Workspace layout of the forward pass.
 struct FwdWS {
   PlanBase plan;
@@ -309,6 +323,9 @@ struct FwdWS {
   void* H2;     // [qcap, d]
   void* F;      // [qcap, dff]
   float* Rb[2]; // [qcap, d]
+  float* SSin;  // [kMaxSlots, ss_ld_in] partial sums of squares, layer input
+  long long ss_ld_in;  // max rows
+  float* SS2;   // [kMaxSlots, qcap] partial sums of squares of R1
   float* Q0;    // [B*nq, d]
   void* XC;     // [B*nq, d+dc]
   float* S;     // [B*ns, d]
@@ -331,7 +348,7 @@ static size_t layout_forward(const Shapes& S, void* base, FwdWS* w) {
     layout_packed(S, blob, &w->pk);
   }
   w->H = ar.take<char>((size_t)maxrows * S.d * e);
-  w->Cf = ar.take<float>((size_t)maxK * S.r);
+  w->Cf = S.fnorm ? nullptr : ar.take<float>((size_t)maxK * S.r);
   w->Cl = ar.take<char>((size_t)maxK * S.r * e);
   w->q = ar.take<char>((size_t)S.qcap * S.hd * e);
   w->ql = S.bf16 ? nullptr : ar.take<char>((size_t)S.qcap * S.h * S.r * e);
@@ -342,6 +359,9 @@ static size_t layout_forward(const Shapes& S, void* base, FwdWS* w) {
   w->F = ar.take<char>((size_t)S.qcap * S.dff * e);
   w->Rb[0] = ar.take<float>((size_t)S.qcap * S.d);
   w->Rb[1] = ar.take<float>((size_t)S.qcap * S.d);
+  w->ss_ld_in = maxrows;
+  w->SSin = S.fnorm ? ar.take<float>((size_t)maxrows * kMaxSlots(S)) : nullptr;
+  w->SS2 = S.fnorm ? ar.take<float>((size_t)S.qcap * kMaxSlots(S)) : nullptr;
   w->Q0 = S.nq ? ar.take<float>((size_t)S.B * S.nq * S.d) : nullptr;
   w->XC = S.nq ? ar.take<char>((size_t)S.B * S.nq * (S.d + S.dc) * e) : nullptr;
   w->S = S.ns ? ar.take<float>((size_t)S.B * S.ns * S.d) : nullptr;
@@ -370,14 +390,17 @@ static hipError_t pack_layer(const Shapes& S, const llatte_layer_weights* L,
   if ((err = hipMemcpyAsync(T.Wuk, L->W_uk, (size_t)S.r * S.hd * e,
                             hipMemcpyDeviceToDevice, s)))
     return err;
-  if ((err = transpose(L->W_dkv, S.d, S.r, S.r, 0, T.Wdkv, S.d, 0, 1, k, k, s))) return err;
-  if ((err = transpose(L->W_uq, S.d, S.hd, S.hd, 0, T.Wuq, S.d, 0, 1, k, k, s))) return err;
+  // fused norms: diag(g1) W_dkv, diag(g1) W_uq, diag(g2) W1
+  const float* g1 = S.fnorm ? L->g1 : nullptr;
+  const float* g2 = S.fnorm ? L->g2 : nullptr;
+  if ((err = transpose(L->W_dkv, S.d, S.r, S.r, 0, T.Wdkv, S.d, 0, 1, k, k, s, g1))) return err;
+  if ((err = transpose(L->W_uq, S.d, S.hd, S.hd, 0, T.Wuq, S.d, 0, 1, k, k, s, g1))) return err;
   // per head: W_uv[:, j*dk:(j+1)*dk] ([r, dk]) -> [dk, r]
   if ((err = transpose(L->W_uv, S.r, S.dk, S.hd, S.dk, T.Wuv, S.r,
                        (long long)S.dk * S.r, S.h, k, S.bf16 ? K_F16 : K_F32, s)))
     return err;
   if ((err = transpose(L->W_o, S.hd, S.d, S.d, 0, T.Wo, S.hd, 0, 1, k, k, s))) return err;
-  if ((err = transpose(L->W1, S.d, S.dff, S.dff, 0, T.W1, S.d, 0, 1, k, k, s))) return err;
+  if ((err = transpose(L->W1, S.d, S.dff, S.dff, 0, T.W1, S.d, 0, 1, k, k, s, g2))) return err;
   if ((err = transpose(L->W2, S.dff, S.d, S.d, 0, T.W2, S.dff, 0, 1, k, k, s))) return err;
   return hipSuccess;
 }
@@ -403,10 +426,19 @@ static hipError_t pack_all(const Shapes& S, const llatte_weights* w,
   return hipSuccess;
 }
 
+// Hand-over between layers on the fused-norm path.
+struct LayerIO {
+  bool in_ready = false;  // w.H / w.SSin hold this layer's rows as bf16 and
+                          // their partial sums of squares
+  int np_in = 0;          // slots per row in w.SSin
+  bool next = false;      // write them for the next layer (from the FFN)
+  int np_out = 0;         // slots written
+};
+
 // One layer (plan index l) from row space `src` into `out` ([UBM, d] float).
 static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
                             const PackedLayer& L, RowSrc src, float* out,
-                            hipStream_t s) {
+                            LayerIO& io, hipStream_t s) {
   const LayerPlan P = w.plan.layer(l);
   const bool b = S.bf16;
   const int tk = b ? K_BF16 : K_F32;
@@ -415,6 +447,7 @@ static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
   const int UBrows = (int)S.UBrows[l], UBK = (int)S.UBK[l], UBM = (int)S.UBM[l];
   const size_t e = S.esz;
   hipError_t err;
+  int np2 = 0;
   auto gemm_base = [&](const char* name) {
     GemmParams g;
     g.name = name;
@@ -423,10 +456,20 @@ static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
     return g;
   };
 
-  // 1. H = RMSNorm(R) g1 (pre) or R (post), all rows of the row space
-  if ((err = norm_rows(src, UBrows, P.counts + 2, S.pre ? L.g1 : nullptr, S.eps,
-                       nullptr, 0, w.H, S.d, S.d, tk, s)))
-    return err;
+  // 1. H = RMSNorm(R) g1 (pre) or R (post), all rows of the row space.
+  //    Fused norms: H = R as bf16 plus sum(R^2) per row, unless the previous
+  //    layer's FFN epilogue has written them already.
+  if (!S.fnorm) {
+    if ((err = norm_rows(src, UBrows, P.counts + 2, S.pre ? L.g1 : nullptr, S.eps,
+                         nullptr, 0, w.H, S.d, S.d, tk, s)))
+      return err;
+  } else if (!io.in_ready) {
+    if ((err = norm_rows(src, UBrows, P.counts + 2, nullptr, 0.f, nullptr, 0, w.H,
+                         S.d, S.d, K_BF16, s, w.SSin)))
+      return err;
+    io.np_in = 1;
+  }
+  const RowScale rs_in{w.SSin, io.np_in, w.ss_ld_in, S.d, S.eps};
   // 2. latent C = H_hist W_dkv, then RMSNorm(C) g_c (f16 on the bf16 path)
   {
     GemmParams g;
@@ -439,18 +482,31 @@ static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
     g.M_dev = P.counts + 0;
     g.N = S.r;
     g.K = S.d;
-    g.epi = EPI_STORE_F32;
-    g.C = w.Cf;
-    g.ldc = S.r;
-    if ((err = gemm(g, b, s))) return err;
-    if ((err = norm_rows(RowSrc{w.Cf, w.Cf, 0, S.r}, UBK, P.counts + 0,
-                         S.lnorm ? L.g_c : nullptr, S.eps, nullptr, 0, w.Cl, S.r,
-                         S.r, b ? K_F16 : K_F32, s)))
-      return err;
+    if (S.fnorm) {
+      g.rs = rs_in;
+      g.rs.ss = w.SSin + nc;
+      g.epi = EPI_ROWNORM;
+      g.gain = S.lnorm ? L.g_c : nullptr;
+      g.eps = S.eps;
+      g.out_kind = K_F16;
+      g.C = w.Cl;
+      g.ldc = S.r;
+      if ((err = gemm(g, b, s))) return err;
+    } else {
+      g.epi = EPI_STORE_F32;
+      g.C = w.Cf;
+      g.ldc = S.r;
+      if ((err = gemm(g, b, s))) return err;
+      if ((err = norm_rows(RowSrc{w.Cf, w.Cf, 0, S.r}, UBK, P.counts + 0,
+                           S.lnorm ? L.g_c : nullptr, S.eps, nullptr, 0, w.Cl, S.r,
+                           S.r, b ? K_F16 : K_F32, s)))
+        return err;
+    }
   }
   // 3. q = H[qmap] W_uq
   {
     GemmParams g = gemm_base("gemm_q");
+    if (S.fnorm) g.rs = rs_in;
     g.A = w.H;
     g.lda = S.d;
     g.a_rows = P.qmap;
@@ -535,10 +591,19 @@ static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
     g.ldc = S.d;
     g.res = src;
     g.res_rows = P.qmap;
+    if (S.fnorm) {  // H2 = R1 as bf16, sum(R1^2) per row
+      g.cast_out = w.H2;
+      g.ld_cast = S.d;
+      g.ss_out = w.SS2;
+      g.ss_ld = S.qcap;
+      np2 = gemm_ss_slots(g, b);
+    }
     if ((err = gemm(g, b, s))) return err;
   }
   // 8. H2 = RMSNorm(R1) g2 (pre); post: R1 = RMSNorm(R1) g1, H2 = R1
-  if (S.pre)
+  if (S.fnorm)
+    err = hipSuccess;
+  else if (S.pre)
     err = norm_rows(RowSrc{w.R1, w.R1, 0, S.d}, UBM, P.counts + 3, L.g2, S.eps,
                     nullptr, 0, w.H2, S.d, S.d, tk, s);
   else
@@ -548,6 +613,7 @@ static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
   // 9. F = GELU(H2 W1)
   {
     GemmParams g = gemm_base("gemm_ffn1");
+    if (S.fnorm) g.rs = RowScale{w.SS2, np2, S.qcap, S.d, S.eps};
     g.A = w.H2;
     g.lda = S.d;
     g.B = L.W1;
@@ -572,6 +638,13 @@ static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
     g.C = out;
     g.ldc = S.d;
     g.res = RowSrc{w.R1, w.R1, 0, S.d};
+    if (S.fnorm && io.next) {  // the next layer's H and sums of squares
+      g.cast_out = w.H;
+      g.ld_cast = S.d;
+      g.ss_out = w.SSin;
+      g.ss_ld = w.ss_ld_in;
+      io.np_out = gemm_ss_slots(g, b);
+    }
     if ((err = gemm(g, b, s))) return err;
   }
   if (!S.pre &&
@@ -719,6 +792,7 @@ llatte_status llatte_mla_forward(
   }
   const long long nc = (long long)B * S.nq;
   float* last = nullptr;
+  LayerIO io;
   for (int l = 0; l < S.N; ++l) {
     RowSrc src;
     if (l == 0)
@@ -726,7 +800,10 @@ llatte_status llatte_mla_forward(
     else
       src = RowSrc{last, last + nc * S.d, (int)nc, S.d};
     float* out = w.Rb[l & 1];
-    HIP_TRY(run_layer(S, w, l, PK.L[l], src, out, s));
+    io.next = S.fnorm && l + 1 < S.N;
+    HIP_TRY(run_layer(S, w, l, PK.L[l], src, out, io, s));
+    io.in_ready = io.next;
+    io.np_in = io.np_out;
     last = out;
   }
   const LayerPlan PN = w.plan.layer(S.N - 1);
@@ -741,7 +818,8 @@ llatte_status llatte_mla_forward(
     HIP_TRY(broadcast_rows(PK.seeds, S.ns, S.d, B, w.S, s));
     float* ro = w.Rb[S.N & 1];
     RowSrc src{w.S, last + nc * S.d, B * S.ns, S.d};
-    HIP_TRY(run_layer(S, w, S.N, PK.L[S.N], src, ro, s));
+    LayerIO rio;
+    HIP_TRY(run_layer(S, w, S.N, PK.L[S.N], src, ro, rio, s));
     HIP_TRY(norm_rows(RowSrc{ro, ro, 0, S.d}, B * S.ns, nullptr, nullptr, 0.f,
                       nullptr, 0, w.E, S.d, S.d, b ? K_BF16 : K_F32, s));
     GemmParams g;

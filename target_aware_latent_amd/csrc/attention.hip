@@ -56,7 +56,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;  // running-max slack, log2 units
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float fast_exp2(float x) {

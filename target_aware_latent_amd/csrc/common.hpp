@@ -14,6 +14,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 
 typedef _Float16 f16;
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 // float -> bf16 with the hardware conversion (round to nearest even).
 __device__ __forceinline__ bf16 to_bf16(float f) { return (bf16)f; }
@@ -38,6 +39,19 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
   return v;
+}
+
+// Sum over the four lanes l, l^16, l^32, l^48 (one column, or one row, of
+// an MFMA accumulator block across its four 16-lane groups). Each permlane
+// swap gives a lane its own value and its partner's; the two lanes of a pair
+// add the same two numbers, so all four lanes end with the same bits.
+__device__ __forceinline__ float group_sum4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Rows of a layer's row space: the first `nc` rows live at `c`, the rest at

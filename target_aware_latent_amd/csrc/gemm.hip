@@ -74,8 +74,12 @@ template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
   return f32x4{from_bf16(v[0]), from_bf16(v[1]), from_bf16(v[2]), from_bf16(v[3])};
 }
 
+// Eight-wave 128-wide tiles keep two workgroups per CU (LDS allows it): at
+// most 128 VGPRs, i.e. four waves per SIMD.
+template <int BN, int NW> constexpr int gemm_min_waves() { return NW == 8 && BN <= 128 ? 4 : 1; }
+
 template <typename T, int BM, int BN, int WM, int WN, int NW, int PF>
-__global__ __launch_bounds__(64 * NW) void gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(64 * NW, (gemm_min_waves<BN, NW>())) void gemm_kernel(GemmParams p) {
   using MF = Mfma<T>;
   constexpr int NT = 64 * NW;              // threads
   constexpr int CE = 16 / sizeof(T);       // elements per 16-byte chunk
@@ -89,6 +93,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(GemmParams p) {
 
   __shared__ __attribute__((aligned(16))) T As[2][BM * LDK];
   __shared__ __attribute__((aligned(16))) T Bs[2][BN * LDK];
+  __shared__ float rs_lds[BM];  // row scales of a fused RMSNorm of A
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -228,6 +233,38 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(GemmParams p) {
   if constexpr (PF == 2) {
     if (nk > 1) load_tile(1, S1{});
   }
+  // Source rows of the residual / gathered table rows, resolved before the
+  // main loop so the epilogue's loads do not wait on the index loads.
+  int rrow[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int m = m0 + (wave / WAVES_N) * WM + i * 16 + (lane & 15);
+    rrow[i] = 0;
+    if (m < M) {
+      if (p.epi == EPI_RESID_F32) rrow[i] = p.res_rows ? p.res_rows[m] : m;
+      else if (p.epi == EPI_GATHER_ADD_F32) rrow[i] = p.g_rows[m];
+    }
+  }
+  // Row scales of a fused RMSNorm of the A rows, one thread per tile row:
+  // their loads wait together with the first tile's.
+  if (p.rs.ss && tid < BM) {
+    const int m = m0 + tid;
+    float sc = 1.f;
+    if (m < M) {
+      // slots in batches of eight loads in flight (indexes clamped in bounds)
+      const float* ss = p.rs.ss + (p.a_rows ? p.a_rows[m] : m);
+      float t = 0.f;
+      for (int q0 = 0; q0 < p.rs.np; q0 += 8) {
+        float x[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) x[q] = ss[(size_t)min(q0 + q, p.rs.np - 1) * p.rs.ld];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) t += q0 + q < p.rs.np ? x[q] : 0.f;
+      }
+      sc = 1.f / sqrtf(t / (float)p.rs.n + p.rs.eps);
+    }
+    rs_lds[tid] = sc;
+  }
   store_lds(0, S0{});
   __syncthreads();
   int kt = 0;
@@ -238,43 +275,143 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(GemmParams p) {
   if (kt < nk) step(kt, S0{});
 
   // Epilogue: lane holds C[m][n .. n+3] of each 16x16 block.
+  // Row scale of a fused RMSNorm of the A rows (1 without one).
+  float rsc[TM];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int m = m0 + wm0 + i * 16 + lr;
-    if (m >= M) continue;
+  for (int i = 0; i < TM; ++i) rsc[i] = p.rs.ss ? rs_lds[wm0 + i * 16 + lr] : 1.f;
+
+  if (p.epi == EPI_ROWNORM) {
+    // y = rsc * acc; with a gain, RMSNorm over the row's N columns, which
+    // this tile spans: partial sums per wave, then across the WAVES_N waves
+    // of a row through LDS (free after the main loop's last barrier).
+    float scale[TM];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn0 + j * 16 + (lane >> 4) * 4;
-      if (n >= p.N) continue;
-      f32x4 v = acc[i][j];
-      const size_t off = (size_t)blockIdx.z * p.sC + (size_t)m * p.ldc + n;
-      switch (p.epi) {
-        case EPI_STORE:
-          store4<T>((T*)p.C + off, p.alpha * v[0], p.alpha * v[1], p.alpha * v[2],
-                    p.alpha * v[3]);
-          break;
-        case EPI_STORE_F32:
-          store4<float>((float*)p.C + off, p.alpha * v[0], p.alpha * v[1],
-                        p.alpha * v[2], p.alpha * v[3]);
-          break;
-        case EPI_GELU:
-          store4<T>((T*)p.C + off, gelu_erf(v[0]), gelu_erf(v[1]), gelu_erf(v[2]),
-                    gelu_erf(v[3]));
-          break;
-        case EPI_RESID_F32: {
-          const float* rr = p.res.row(p.res_rows ? p.res_rows[m] : m) + n;
-          f32x4 r = *(const f32x4*)rr;
-          store4<float>((float*)p.C + off, v[0] + r[0], v[1] + r[1], v[2] + r[2],
-                        v[3] + r[3]);
-        } break;
-        case EPI_GATHER_ADD_F32: {
-          const T* tr = (const T*)p.table + (size_t)p.g_rows[m] * p.ld_table + n;
-          f32x4 r = load4<T>(tr);
-          store4<float>((float*)p.C + off, v[0] + r[0], v[1] + r[1], v[2] + r[2],
-                        v[3] + r[3]);
-        } break;
+    for (int i = 0; i < TM; ++i) scale[i] = rsc[i];
+    if (p.gain) {
+      float* red = (float*)&As[0][0];
+      float ssr[TM];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        ssr[i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = n0 + wn0 + j * 16 + (lane >> 4) * 4;
+          if (n < p.N) {
+            const f32x4 v = acc[i][j];
+            ssr[i] += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+          }
+        }
+        ssr[i] = group_sum4(ssr[i]) * rsc[i] * rsc[i];
+      }
+      if (lane < 16) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          red[(wm0 + i * 16 + lr) * WAVES_N + wave % WAVES_N] = ssr[i];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        float t = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES_N; ++w) t += red[(wm0 + i * 16 + lr) * WAVES_N + w];
+        scale[i] = rsc[i] / sqrtf(t / (float)p.N + p.eps);
       }
     }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + wm0 + i * 16 + lr;
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn0 + j * 16 + (lane >> 4) * 4;
+        if (n >= p.N) continue;
+        f32x4 v = acc[i][j] * scale[i];
+        if (p.gain) v *= *(const f32x4*)(p.gain + n);
+        const size_t off = (size_t)m * p.ldc + n;
+        if (p.out_kind == K_F16)
+          *(f16x4*)((f16*)p.C + off) = f16x4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+        else if (p.out_kind == K_BF16)
+          store4<bf16>((bf16*)p.C + off, v[0], v[1], v[2], v[3]);
+        else
+          store4<float>((float*)p.C + off, v[0], v[1], v[2], v[3]);
+      }
+    }
+    return;
+  }
+
+  // The other epilogues: one unrolled pass per kind, with all loads of a
+  // pass (residual rows, table rows) issued before their first use.
+  auto outs = [&](auto&& f) {  // f(i, j, m, n) over this lane's valid outputs
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + wm0 + i * 16 + lr;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn0 + j * 16 + (lane >> 4) * 4;
+        if (m < M && n < p.N) f(i, j, m, n);
+      }
+    }
+  };
+  auto coff = [&](int m, int n) {
+    return (size_t)blockIdx.z * p.sC + (size_t)m * p.ldc + n;
+  };
+  switch (p.epi) {
+    case EPI_STORE:
+      outs([&](int i, int j, int m, int n) {
+        const f32x4 v = acc[i][j] * (rsc[i] * p.alpha);
+        store4<T>((T*)p.C + coff(m, n), v[0], v[1], v[2], v[3]);
+      });
+      break;
+    case EPI_STORE_F32:
+      outs([&](int i, int j, int m, int n) {
+        const f32x4 v = acc[i][j] * (rsc[i] * p.alpha);
+        store4<float>((float*)p.C + coff(m, n), v[0], v[1], v[2], v[3]);
+      });
+      break;
+    case EPI_GELU:
+      outs([&](int i, int j, int m, int n) {
+        const f32x4 v = acc[i][j] * rsc[i];
+        store4<T>((T*)p.C + coff(m, n), gelu_erf(v[0]), gelu_erf(v[1]), gelu_erf(v[2]),
+                  gelu_erf(v[3]));
+      });
+      break;
+    case EPI_RESID_F32: {
+      f32x4 r[TM][TN];
+      outs([&](int i, int j, int m, int n) {
+        r[i][j] = *(const f32x4*)(p.res.row(rrow[i]) + n);
+      });
+      float ssp[TM];  // partial sums of squares of the results
+#pragma unroll
+      for (int i = 0; i < TM; ++i) ssp[i] = 0.f;
+      outs([&](int i, int j, int m, int n) {
+        const f32x4 v = acc[i][j] * rsc[i] + r[i][j];
+        store4<float>((float*)p.C + coff(m, n), v[0], v[1], v[2], v[3]);
+        if (p.cast_out)
+          store4<T>((T*)p.cast_out + (size_t)m * p.ld_cast + n, v[0], v[1], v[2], v[3]);
+        ssp[i] += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+      });
+      if (p.ss_out) {
+        // one slot per (row, strip of WN columns); strips start below N
+        const int slots = (p.N + WN - 1) / WN;
+        const int slot = (n0 + wn0) / WN;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const float t = group_sum4(ssp[i]);
+          const int m = m0 + wm0 + i * 16 + lr;
+          if (lane < 16 && m < M && slot < slots) p.ss_out[(size_t)slot * p.ss_ld + m] = t;
+        }
+      }
+    } break;
+    case EPI_GATHER_ADD_F32: {
+      f32x4 r[TM][TN];
+      outs([&](int i, int j, int m, int n) {
+        r[i][j] = load4<T>((const T*)p.table + (size_t)rrow[i] * p.ld_table + n);
+      });
+      outs([&](int i, int j, int m, int n) {
+        const f32x4 v = acc[i][j] * rsc[i] + r[i][j];
+        store4<float>((float*)p.C + coff(m, n), v[0], v[1], v[2], v[3]);
+      });
+    } break;
   }
 }
 
@@ -296,15 +433,45 @@ static long long ntiles(const GemmParams& p, int bm, int bn) {
 // Tile choice: 128x128 with eight waves (32x64 each) when that gives the
 // GPU (256 CUs) enough workgroups; 64x64 tiles for the small products
 // (readout layer, last pyramid layers) that would otherwise occupy a few CUs.
+// A row-normalising epilogue needs one tile across all N columns.
+enum TileCfg { T64x64, T128x64, T128x128, T128x256, F128x64, F128x128, T_NONE };
+
+static TileCfg select_tile(const GemmParams& p, bool is_bf16) {
+  if (p.epi == EPI_ROWNORM && p.gain) {
+    if (!is_bf16) return p.N <= 64 ? F128x64 : p.N <= 128 ? F128x128 : T_NONE;
+    if (p.N <= 64) return ntiles(p, 128, 64) < 256 ? T64x64 : T128x64;
+    if (p.N <= 128) return T128x128;
+    if (p.N <= 256) return T128x256;
+    return T_NONE;
+  }
+  if (is_bf16) {
+    if (ntiles(p, 128, 128) < 256) return T64x64;
+    if (p.N <= 64) return T128x64;
+    return T128x128;
+  }
+  return p.N <= 64 ? F128x64 : F128x128;
+}
+
+int gemm_ss_slots(const GemmParams& p, bool is_bf16) {
+  int wn = 64;
+  switch (select_tile(p, is_bf16)) {
+    case T64x64: case T128x64: case F128x64: wn = 32; break;
+    default: break;
+  }
+  return (p.N + wn - 1) / wn;
+}
+
 hipError_t gemm(const GemmParams& p, bool is_bf16, hipStream_t s) {
   if (p.M_cap <= 0 || p.N <= 0) return hipSuccess;
-  if (is_bf16) {
-    if (ntiles(p, 128, 128) < 256) return launch_gemm<bf16, 64, 64, 32, 32, 4>(p, s);
-    if (p.N <= 64) return launch_gemm<bf16, 128, 64, 64, 32, 4>(p, s);
-    return launch_gemm<bf16, 128, 128, 32, 64, 8>(p, s);
+  switch (select_tile(p, is_bf16)) {
+    case T64x64: return launch_gemm<bf16, 64, 64, 32, 32, 4>(p, s);
+    case T128x64: return launch_gemm<bf16, 128, 64, 64, 32, 4>(p, s);
+    case T128x128: return launch_gemm<bf16, 128, 128, 32, 64, 8>(p, s);
+    case T128x256: return launch_gemm<bf16, 128, 256, 64, 64, 8>(p, s);
+    case F128x64: return launch_gemm<float, 128, 64, 64, 32, 4>(p, s);
+    case F128x128: return launch_gemm<float, 128, 128, 64, 64, 4>(p, s);
+    default: return hipErrorInvalidValue;
   }
-  if (p.N <= 64) return launch_gemm<float, 128, 64, 64, 32, 4>(p, s);
-  return launch_gemm<float, 128, 128, 64, 64, 4>(p, s);
 }
 
 }  // namespace llatte

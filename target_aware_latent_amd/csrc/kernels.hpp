@@ -15,6 +15,9 @@ void timing_begin(const char* name, hipStream_t s);
 void timing_end(hipStream_t s);
 
 // ------------------------------------------------------------------ GEMM
+// Element kinds of buffers whose type is chosen at run time.
+enum Kind { K_F32 = 0, K_BF16 = 1, K_F16 = 2 };
+
 // C[m, n] = sum_k A[m, k] * B[n, k]  (A row-major [M, K], B row-major [N, K],
 // i.e. both operands K-contiguous), fp32 accumulation, then an epilogue.
 enum GemmEpi {
@@ -23,6 +26,22 @@ enum GemmEpi {
   EPI_GELU = 2,        // C (dtype) = gelu(acc)
   EPI_RESID_F32 = 3,   // C (float) = acc + res.row(res_rows ? res_rows[m] : m)
   EPI_GATHER_ADD_F32 = 4,  // C (float) = acc + table[g_rows[m]]
+  EPI_ROWNORM = 5,     // C (out_kind) = gain ? RMSNorm(acc) * gain : acc;
+                       // with a gain the tile must span all N columns
+};
+
+// Fused RMSNorm of the A rows. A holds the rows x unscaled (cast to the
+// compute dtype) and the gain is folded into B; since the norm's row scale
+// commutes with the product, the epilogue multiplies acc by
+//   1 / sqrt(sum_p ss[p * ld + row] / n + eps),  row = a_rows ? a_rows[m] : m,
+// where ss holds partial sums of squares of x written by the producer,
+// slot-major so that consecutive rows are consecutive addresses.
+struct RowScale {
+  const float* ss = nullptr;
+  int np = 0;
+  long long ld = 0;
+  int n = 0;
+  float eps = 0.f;
 };
 
 struct GemmParams {
@@ -41,32 +60,48 @@ struct GemmParams {
   void* C = nullptr;
   int ldc = 0;
   float alpha = 1.f;
+  RowScale rs{};                // optional, applied before the epilogue
   RowSrc res{};                 // EPI_RESID_F32
   const int* res_rows = nullptr;
+  // EPI_RESID_F32 extras for a following fused RMSNorm: the result cast to
+  // the dtype ([M, ld_cast]) and per-row partial sums of its squares,
+  // ss_out[slot * ss_ld + m], one slot per wave column strip
+  // (gemm_ss_slots() of them).
+  void* cast_out = nullptr;
+  int ld_cast = 0;
+  float* ss_out = nullptr;
+  long long ss_ld = 0;
   const void* table = nullptr;  // EPI_GATHER_ADD_F32 (dtype of A)
   int ld_table = 0;
   const int* g_rows = nullptr;
+  const float* gain = nullptr;  // EPI_ROWNORM
+  float eps = 0.f;
+  int out_kind = K_BF16;
 };
 
+// Partial sums of squares per row that an EPI_RESID_F32 launch with these
+// parameters writes to ss_out.
+int gemm_ss_slots(const GemmParams& p, bool bf16);
 hipError_t gemm(const GemmParams& p, bool bf16, hipStream_t s);
 
 // ------------------------------------------------------------------ row ops
-// Element kinds of buffers whose type is chosen at run time.
-enum Kind { K_F32 = 0, K_BF16 = 1, K_F16 = 2 };
-
 // One wave per row (d <= 1024): out = gain ? x / sqrt(mean(x^2) + eps) * gain : x, where
 // x = src.row(i); written as float to out_f32 (may alias the source) and/or
-// as `t_kind` to out_t. Rows i >= *rows_dev (if given) are skipped.
+// as `t_kind` to out_t; ss_out (optional) receives sum(x^2) of each row.
+// Rows i >= *rows_dev (if given) are skipped.
 hipError_t norm_rows(RowSrc src, int rows_cap, const int* rows_dev,
                      const float* gain, float eps, float* out_f32, int ld_f32,
-                     void* out_t, int ld_t, int d, int t_kind, hipStream_t s);
+                     void* out_t, int ld_t, int d, int t_kind, hipStream_t s,
+                     float* ss_out = nullptr);
 
 // dst [cols, rows] = transpose(src [rows, cols]) for a batch of `batch`
 // matrices laid out with the given element strides; src has kind s_kind,
 // dst kind d_kind (bf16 -> f16 and same-kind copies).
+// row_scale (optional, float [src_rows]) multiplies source row i first.
 hipError_t transpose(const void* src, int src_rows, int src_cols, int ld_src,
                      long long s_src, void* dst, int ld_dst, long long s_dst,
-                     int batch, int s_kind, int d_kind, hipStream_t s);
+                     int batch, int s_kind, int d_kind, hipStream_t s,
+                     const float* row_scale = nullptr);
 
 // xc (dtype) [B*n_q, d + d_c]: row u*n_q + j = [cand[u*n_q+j] ; ctx[u]].
 hipError_t concat_queries(const float* cand, const float* ctx, int B, int n_q,

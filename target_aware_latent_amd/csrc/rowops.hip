@@ -6,12 +6,13 @@ namespace llatte {
 
 // One wave per row, four rows per workgroup. Each lane owns float4 chunks
 // lane*4 + 256*j of the row, so a row of d floats is read once, reduced with
-// wave shuffles, and written as dtype and/or float.
+// wave shuffles, and written as dtype and/or float (and its sum of squares).
 // RMSNorm (Root Mean Square Layer Normalization): x / sqrt(mean(x^2) + eps) * g.
 template <typename T>
 __global__ __launch_bounds__(256) void norm_rows_kernel(
     RowSrc src, int rows_cap, const int* rows_dev, const float* gain,
-    float eps, float* out_f32, int ld_f32, T* out_t, int ld_t, int d) {
+    float eps, float* out_f32, int ld_f32, T* out_t, int ld_t, int d,
+    float* ss_out) {
   constexpr int MAXV = 4;  // d <= 4 * 256 = 1024
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -30,9 +31,10 @@ __global__ __launch_bounds__(256) void norm_rows_kernel(
     }
   }
   float scale = 1.f;
-  if (gain) {
+  if (gain || ss_out) {
     ss = wave_sum(ss);
-    scale = 1.f / sqrtf(ss / (float)d + eps);
+    if (gain) scale = 1.f / sqrtf(ss / (float)d + eps);
+    if (ss_out && lane == 0) ss_out[row] = ss;
   }
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
@@ -55,22 +57,23 @@ __global__ __launch_bounds__(256) void norm_rows_kernel(
 
 hipError_t norm_rows(RowSrc src, int rows_cap, const int* rows_dev,
                      const float* gain, float eps, float* out_f32, int ld_f32,
-                     void* out_t, int ld_t, int d, int t_kind, hipStream_t s) {
+                     void* out_t, int ld_t, int d, int t_kind, hipStream_t s,
+                     float* ss_out) {
   if (rows_cap <= 0) return hipSuccess;
   dim3 grid((rows_cap + 3) / 4);
   timing_begin("norm_rows", s);
   if (t_kind == K_BF16)
     hipLaunchKernelGGL(norm_rows_kernel<bf16>, grid, dim3(256), 0, s, src,
                        rows_cap, rows_dev, gain, eps, out_f32, ld_f32,
-                       (bf16*)out_t, ld_t, d);
+                       (bf16*)out_t, ld_t, d, ss_out);
   else if (t_kind == K_F16)
     hipLaunchKernelGGL(norm_rows_kernel<f16>, grid, dim3(256), 0, s, src,
                        rows_cap, rows_dev, gain, eps, out_f32, ld_f32,
-                       (f16*)out_t, ld_t, d);
+                       (f16*)out_t, ld_t, d, ss_out);
   else
     hipLaunchKernelGGL(norm_rows_kernel<float>, grid, dim3(256), 0, s, src,
                        rows_cap, rows_dev, gain, eps, out_f32, ld_f32,
-                       (float*)out_t, ld_t, d);
+                       (float*)out_t, ld_t, d, ss_out);
   timing_end(s);
   return hipGetLastError();
 }
@@ -79,7 +82,7 @@ hipError_t norm_rows(RowSrc src, int rows_cap, const int* rows_dev,
 template <typename S, typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(
     const S* src, int rows, int cols, int ld_src, long long s_src, T* dst,
-    int ld_dst, long long s_dst) {
+    int ld_dst, long long s_dst, const float* row_scale) {
   __shared__ T tile[32][33];
   src += (size_t)blockIdx.z * s_src;
   dst += (size_t)blockIdx.z * s_dst;
@@ -87,7 +90,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   for (int i = ty; i < 32; i += 8) {
     int r = r0 + i, c = c0 + tx;
-    if (r < rows && c < cols) tile[i][tx] = cvt<T>(tof(src[(size_t)r * ld_src + c]));
+    if (r < rows && c < cols)
+      tile[i][tx] = cvt<T>(tof(src[(size_t)r * ld_src + c]) * (row_scale ? row_scale[r] : 1.f));
   }
   __syncthreads();
   for (int i = ty; i < 32; i += 8) {
@@ -98,22 +102,23 @@ __global__ __launch_bounds__(256) void transpose_kernel(
 
 hipError_t transpose(const void* src, int rows, int cols, int ld_src,
                      long long s_src, void* dst, int ld_dst, long long s_dst,
-                     int batch, int s_kind, int d_kind, hipStream_t s) {
+                     int batch, int s_kind, int d_kind, hipStream_t s,
+                     const float* row_scale) {
   if (rows <= 0 || cols <= 0 || batch <= 0) return hipSuccess;
   dim3 grid((cols + 31) / 32, (rows + 31) / 32, batch);
   timing_begin("transpose", s);
   if (s_kind == K_BF16 && d_kind == K_BF16)
     hipLaunchKernelGGL((transpose_kernel<bf16, bf16>), grid, dim3(256), 0, s,
                        (const bf16*)src, rows, cols, ld_src, s_src, (bf16*)dst,
-                       ld_dst, s_dst);
+                       ld_dst, s_dst, row_scale);
   else if (s_kind == K_BF16 && d_kind == K_F16)
     hipLaunchKernelGGL((transpose_kernel<bf16, f16>), grid, dim3(256), 0, s,
                        (const bf16*)src, rows, cols, ld_src, s_src, (f16*)dst,
-                       ld_dst, s_dst);
+                       ld_dst, s_dst, row_scale);
   else if (s_kind == K_F32 && d_kind == K_F32)
     hipLaunchKernelGGL((transpose_kernel<float, float>), grid, dim3(256), 0, s,
                        (const float*)src, rows, cols, ld_src, s_src,
-                       (float*)dst, ld_dst, s_dst);
+                       (float*)dst, ld_dst, s_dst, row_scale);
   else
     return hipErrorInvalidValue;
   timing_end(s);

@@ -74,6 +74,148 @@ template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
   return f32x4{from_bf16(v[0]), from_bf16(v[1]), from_bf16(v[2]), from_bf16(v[3])};
 }
 
+// Row-major epilogue. The fp32 accumulator tile goes through LDS (16-byte
+// chunk c of row r stored at chunk c ^ (r & 15), so that both the fragment
+// writes and the row reads below are free of bank conflicts) and comes back
+// with LPR lanes per row, each lane holding chunks q and q + LPR of its row:
+// every 16-lane group then reads and writes whole 256-byte runs of a row,
+// and each row's RMSNorm sums reduce within its lane group.
+template <typename T, int BM, int BN, int WM, int WN, int NW>
+__device__ __forceinline__ void epilogue_rowmajor(const GemmParams p, const f32x4 (&acc)[WM / 16][WN / 16],
+                                                  float* Cs, const float* rs_lds,
+                                                  const int (&rrow)[BM / (64 * NW / (BN / 8))],
+                                                  int m0, int n0, int M, int wm0, int wn0,
+                                                  int lane, int tid) {
+  constexpr int TM = WM / 16, TN = WN / 16;
+  constexpr int NT = 64 * NW;
+  constexpr int CPR = BN / 4;       // 16-byte chunks per row
+  constexpr int LPR = CPR / 2;      // lanes per row
+  constexpr int RPP = NT / LPR;     // rows per pass
+  constexpr int NPASS = BM / RPP;
+  static_assert(LPR <= 64 && (LPR & (LPR - 1)) == 0 && BM % RPP == 0, "row-major epilogue shape");
+  auto cidx = [](int row, int chunk) { return row * BN + ((chunk ^ (row & 15)) << 2); };
+  const int lr = lane & 15;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      *(f32x4*)&Cs[cidx(wm0 + i * 16 + lr, ((wn0 + j * 16) >> 2) + (lane >> 4))] = acc[i][j];
+  __syncthreads();
+
+  const int q = tid % LPR, rsub = tid / LPR;
+  const bool has_rs = p.rs.ss != nullptr;
+  // values of this lane, scaled by the row scale
+  f32x4 v[NPASS][2];
+#pragma unroll
+  for (int ps = 0; ps < NPASS; ++ps) {
+    const int row = ps * RPP + rsub;
+    const float sc = has_rs ? rs_lds[row] : 1.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) v[ps][h] = *(const f32x4*)&Cs[cidx(row, q + h * LPR)] * sc;
+  }
+  auto each = [&](auto&& f) {  // f(ps, h, m, n) over this lane's valid outputs
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int m = m0 + ps * RPP + rsub;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int n = n0 + (q + h * LPR) * 4;
+        if (m < M && n < p.N) f(ps, h, m, n);
+      }
+    }
+  };
+  // sum over the LPR lanes of a row (aligned groups of LPR lanes)
+  auto row_sum = [&](float x) {
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) x += __shfl_xor(x, o, 64);
+    return x;
+  };
+  auto coff = [&](int m, int n) { return (size_t)blockIdx.z * p.sC + (size_t)m * p.ldc + n; };
+  switch (p.epi) {
+    case EPI_STORE:
+      each([&](int ps, int h, int m, int n) {
+        const f32x4 x = v[ps][h] * p.alpha;
+        store4<T>((T*)p.C + coff(m, n), x[0], x[1], x[2], x[3]);
+      });
+      break;
+    case EPI_STORE_F32:
+      each([&](int ps, int h, int m, int n) {
+        const f32x4 x = v[ps][h] * p.alpha;
+        store4<float>((float*)p.C + coff(m, n), x[0], x[1], x[2], x[3]);
+      });
+      break;
+    case EPI_GELU:
+      each([&](int ps, int h, int m, int n) {
+        const f32x4 x = v[ps][h];
+        store4<T>((T*)p.C + coff(m, n), gelu_erf(x[0]), gelu_erf(x[1]), gelu_erf(x[2]),
+                  gelu_erf(x[3]));
+      });
+      break;
+    case EPI_RESID_F32: {
+      f32x4 r[NPASS][2];
+      each([&](int ps, int h, int m, int n) { r[ps][h] = *(const f32x4*)(p.res.row(rrow[ps]) + n); });
+      float ssp[NPASS];
+#pragma unroll
+      for (int ps = 0; ps < NPASS; ++ps) ssp[ps] = 0.f;
+      each([&](int ps, int h, int m, int n) {
+        const f32x4 x = v[ps][h] + r[ps][h];
+        store4<float>((float*)p.C + coff(m, n), x[0], x[1], x[2], x[3]);
+        if (p.cast_out)
+          store4<T>((T*)p.cast_out + (size_t)m * p.ld_cast + n, x[0], x[1], x[2], x[3]);
+        ssp[ps] += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+      });
+      if (p.ss_out) {
+        // one slot per (row, tile column)
+        const int slot = n0 / BN;
+#pragma unroll
+        for (int ps = 0; ps < NPASS; ++ps) {
+          const float t = row_sum(ssp[ps]);
+          const int m = m0 + ps * RPP + rsub;
+          if (q == 0 && m < M) p.ss_out[(size_t)slot * p.ss_ld + m] = t;
+        }
+      }
+    } break;
+    case EPI_GATHER_ADD_F32: {
+      f32x4 r[NPASS][2];
+      each([&](int ps, int h, int m, int n) {
+        r[ps][h] = load4<T>((const T*)p.table + (size_t)rrow[ps] * p.ld_table + n);
+      });
+      each([&](int ps, int h, int m, int n) {
+        const f32x4 x = v[ps][h] + r[ps][h];
+        store4<float>((float*)p.C + coff(m, n), x[0], x[1], x[2], x[3]);
+      });
+    } break;
+    case EPI_ROWNORM: {
+      // RMSNorm over the row's N columns (with a gain this tile spans them)
+      float sc[NPASS];
+#pragma unroll
+      for (int ps = 0; ps < NPASS; ++ps) {
+        sc[ps] = 1.f;
+        if (p.gain) {
+          float t = 0.f;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            if (n0 + (q + h * LPR) * 4 < p.N)
+              t += v[ps][h][0] * v[ps][h][0] + v[ps][h][1] * v[ps][h][1] +
+                   v[ps][h][2] * v[ps][h][2] + v[ps][h][3] * v[ps][h][3];
+          sc[ps] = 1.f / sqrtf(row_sum(t) / (float)p.N + p.eps);
+        }
+      }
+      each([&](int ps, int h, int m, int n) {
+        f32x4 x = v[ps][h] * sc[ps];
+        if (p.gain) x *= *(const f32x4*)(p.gain + n);
+        const size_t off = (size_t)m * p.ldc + n;
+        if (p.out_kind == K_F16)
+          *(f16x4*)((f16*)p.C + off) = f16x4{(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3]};
+        else if (p.out_kind == K_BF16)
+          store4<bf16>((bf16*)p.C + off, x[0], x[1], x[2], x[3]);
+        else
+          store4<float>((float*)p.C + off, x[0], x[1], x[2], x[3]);
+      });
+    } break;
+  }
+}
+
 // Eight-wave 128-wide tiles keep two workgroups per CU (LDS allows it): at
 // most 128 VGPRs, i.e. four waves per SIMD.
 template <int BN, int NW> constexpr int gemm_min_waves() { return NW == 8 && BN <= 128 ? 4 : 1; }
@@ -91,8 +233,13 @@ __global__ __launch_bounds__(64 * NW, (gemm_min_waves<BN, NW>())) void gemm_kern
   constexpr int BI = BN * 8 / NT;
   constexpr int TM = WM / 16, TN = WN / 16;
 
-  __shared__ __attribute__((aligned(16))) T As[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) T Bs[2][BN * LDK];
+  // One LDS block: the double-buffered operand tiles during the main loop,
+  // then (kShuffle) the fp32 output tile for the row-major epilogue.
+  constexpr int kOpBytes = 2 * (BM + BN) * LDK * (int)sizeof(T);
+  constexpr bool kShuffle = BM * BN * 4 <= kOpBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kOpBytes];
+  T (*As)[BM * LDK] = (T (*)[BM * LDK])smem;
+  T (*Bs)[BN * LDK] = (T (*)[BN * LDK])(smem + 2 * BM * LDK * sizeof(T));
   __shared__ float rs_lds[BM];  // row scales of a fused RMSNorm of A
 
   const int tid = threadIdx.x;
@@ -235,10 +382,15 @@ __global__ __launch_bounds__(64 * NW, (gemm_min_waves<BN, NW>())) void gemm_kern
   }
   // Source rows of the residual / gathered table rows, resolved before the
   // main loop so the epilogue's loads do not wait on the index loads.
-  int rrow[TM];
+  // Rows of this lane in the epilogue: NPASS rows of the row-major
+  // epilogue, or TM fragment rows of the direct one.
+  constexpr int RPP = NT / (BN / 8);
+  constexpr int NROW = kShuffle ? BM / RPP : TM;
+  int rrow[NROW];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int m = m0 + (wave / WAVES_N) * WM + i * 16 + (lane & 15);
+  for (int i = 0; i < NROW; ++i) {
+    const int m = kShuffle ? m0 + i * RPP + tid / (BN / 8)
+                           : m0 + (wave / WAVES_N) * WM + i * 16 + (lane & 15);
     rrow[i] = 0;
     if (m < M) {
       if (p.epi == EPI_RESID_F32) rrow[i] = p.res_rows ? p.res_rows[m] : m;
@@ -274,7 +426,17 @@ __global__ __launch_bounds__(64 * NW, (gemm_min_waves<BN, NW>())) void gemm_kern
   }
   if (kt < nk) step(kt, S0{});
 
-  // Epilogue: lane holds C[m][n .. n+3] of each 16x16 block.
+  // GELU keeps the direct epilogue: its VALU work overlaps the other
+  // resident workgroup's main loop better without the LDS round trip.
+  if constexpr (kShuffle) {
+    if (p.epi != EPI_GELU) {
+      epilogue_rowmajor<T, BM, BN, WM, WN, NW>(p, acc, (float*)smem, rs_lds, rrow, m0, n0,
+                                               M, wm0, wn0, lane, tid);
+      return;
+    }
+  }
+  // Direct epilogue (tiles whose fp32 output does not fit the LDS block):
+  // lane holds C[m][n .. n+3] of each 16x16 block.
   // Row scale of a fused RMSNorm of the A rows (1 without one).
   float rsc[TM];
 #pragma unroll
@@ -452,13 +614,16 @@ static TileCfg select_tile(const GemmParams& p, bool is_bf16) {
   return p.N <= 64 ? F128x64 : F128x128;
 }
 
+// Tiles with the row-major epilogue write one slot per tile column; the
+// 128x256 tile (direct epilogue) one per 64-column wave strip.
 int gemm_ss_slots(const GemmParams& p, bool is_bf16) {
-  int wn = 64;
+  int w = 128;
   switch (select_tile(p, is_bf16)) {
-    case T64x64: case T128x64: case F128x64: wn = 32; break;
+    case T64x64: case T128x64: case F128x64: w = 64; break;
+    case T128x256: w = 64; break;
     default: break;
   }
-  return (p.N + wn - 1) / wn;
+  return (p.N + w - 1) / w;
 }
 
 hipError_t gemm(const GemmParams& p, bool is_bf16, hipStream_t s) {

@@ -179,41 +179,6 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams p, AttnCfg cf
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) pmin = min(pmin, __shfl_xor(pmin, o, 64));
 
-  // latent queries, B operand of S^T, scaled into log2 units
-  f16x8 qf[NEB][NKS];
-#pragma unroll
-  for (int eb = 0; eb < NEB; ++eb) {
-    if constexpr (FUSED) {
-      // q_lat^T[r][e] = sum_k W_uk[r][head*DK + k] * q[e][head*DK + k]
-      const int hd = p.h * DK;
-      const bf16* qp = (const bf16*)p.q + (size_t)qrow[eb] * hd + head[eb] * DK + g * 8;
-      const bf16* wp = (const bf16*)p.w_uk + (size_t)l16 * hd + head[eb] * DK + g * 8;
-      f32x4 acc[NRB];
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kd = 0; kd < DK / 32; ++kd) {
-        const bf16x8 bq = *(const bf16x8*)(qp + kd * 32);
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          const bf16x8 a = *(const bf16x8*)(wp + (size_t)rb * 16 * hd + kd * 32);
-          acc[rb] = mfma_bf16(a, bq, acc[rb]);
-        }
-      }
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qf[eb][ks] = pack8(acc[2 * ks], acc[2 * ks + 1], sc);
-    } else {
-      const bf16* qp = (const bf16*)p.q + ((size_t)qrow[eb] * p.h + head[eb]) * R + g * 4;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x4 lo = *(const bf16x4*)(qp + ks * 32);
-        const bf16x4 hi = *(const bf16x4*)(qp + ks * 32 + 16);
-        qf[eb][ks] = pack8(f32x4{from_bf16(lo[0]), from_bf16(lo[1]), from_bf16(lo[2]), from_bf16(lo[3])},
-                           f32x4{from_bf16(hi[0]), from_bf16(hi[1]), from_bf16(hi[2]), from_bf16(hi[3])}, sc);
-      }
-    }
-  }
-
   // C tile staging: chunk idx covers key idx / (R/8), r 8*(idx % (R/8)) .. +7.
   // Global offsets and swizzled LDS offsets (in halves) are fixed per thread.
   // (the second 8-byte chunk of a pair sits at the first's offset XOR 4
@@ -242,6 +207,61 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams p, AttnCfg cf
       *(f16x4*)&Cs[buf][st_off[i] ^ 4] = f16x4{v[4], v[5], v[6], v[7]};
     }
   };
+
+  load_tile(0);  // in flight during the prologue
+
+  // latent queries, B operand of S^T, scaled into log2 units
+  f16x8 qf[NEB][NKS];
+  if constexpr (FUSED) {
+    // q_lat^T[r][e] = sum_k W_uk[r][head*DK + k] * q[e][head*DK + k]. All
+    // blocks of a wave belong to one head: each W_uk fragment is loaded once
+    // per wave, in batches of at most 16 fragments all in flight together.
+    constexpr int KD = DK / 32;
+    constexpr int RBC = NRB * KD <= 16 ? NRB : 16 / KD;
+    const int hd = p.h * DK;
+    bf16x8 bq[NEB][KD];
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb) {
+      const bf16* qp = (const bf16*)p.q + (size_t)qrow[eb] * hd + head[0] * DK + g * 8;
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd) bq[eb][kd] = *(const bf16x8*)(qp + kd * 32);
+    }
+    const bf16* wp = (const bf16*)p.w_uk + (size_t)l16 * hd + head[0] * DK + g * 8;
+    f32x4 acc[NEB][NRB];
+#pragma unroll
+    for (int rb0 = 0; rb0 < NRB; rb0 += RBC) {
+      bf16x8 a[RBC][KD];
+#pragma unroll
+      for (int r = 0; r < RBC; ++r)
+#pragma unroll
+        for (int kd = 0; kd < KD; ++kd)
+          a[r][kd] = *(const bf16x8*)(wp + (size_t)(rb0 + r) * 16 * hd + kd * 32);
+#pragma unroll
+      for (int r = 0; r < RBC; ++r)
+#pragma unroll
+        for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+          for (int kd = 0; kd < KD; ++kd)
+            acc[eb][rb0 + r] = mfma_bf16(a[r][kd], bq[eb][kd],
+                                         kd == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[eb][rb0 + r]);
+    }
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qf[eb][ks] = pack8(acc[eb][2 * ks], acc[eb][2 * ks + 1], sc);
+  } else {
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb) {
+      const bf16* qp = (const bf16*)p.q + ((size_t)qrow[eb] * p.h + head[eb]) * R + g * 4;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x4 lo = *(const bf16x4*)(qp + ks * 32);
+        const bf16x4 hi = *(const bf16x4*)(qp + ks * 32 + 16);
+        qf[eb][ks] = pack8(f32x4{from_bf16(lo[0]), from_bf16(lo[1]), from_bf16(lo[2]), from_bf16(lo[3])},
+                           f32x4{from_bf16(hi[0]), from_bf16(hi[1]), from_bf16(hi[2]), from_bf16(hi[3])}, sc);
+      }
+    }
+  }
 
   // S^T operand reads: row kb*16 + l16, chunk c = 4x + g with x = 2*ks (+1);
   // the mask depends on l16 only and is below 32, so chunks 32 apart differ
@@ -277,38 +297,54 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams p, AttnCfg cf
   const f16x8 kOnes = f16x8{(f16)1.f, (f16)1.f, (f16)1.f, (f16)1.f,
                             (f16)1.f, (f16)1.f, (f16)1.f, (f16)1.f};
 
-  // S^T[key][e] of the 64-key tile in LDS buffer cs
+  // LDS operands run kPre steps ahead of the MFMAs that use them, so each
+  // MFMA waits only for reads issued kPre steps earlier.
+  constexpr int kPre = 3;
+  constexpr int NSS = 4 * NKS;   // score steps (kb, ks), NEB MFMAs each
+  constexpr int NPS = 2 * NRB;   // PV steps (rb, kk), NEB MFMAs each
+
+  // A operand of score step i: rows kb*16.. of the tile, r = 32 ks..
+  auto rd_s = [&](const f16* cs, int i) {
+    const f16* rowb = cs + (i / NKS) * 16 * R;
+    const int ks = i % NKS;
+    return cat(*(const f16x4*)&rowb[off_s(2 * ks)], *(const f16x4*)&rowb[off_s(2 * ks + 1)]);
+  };
+  // A operand of PV step j: C^T rows rb*16.., keys 32 kk.. (transpose load)
+  auto rd_pv = [&](const f16* cs, int j) {
+    const int rb = j / 2, kk = j % 2;
+    return cat(lds_read_tr(cs + kk * 32 * R + off_t(rb)),
+               lds_read_tr(cs + (kk * 32 + 16) * R + off_t(rb)));
+  };
+
+  // S^T[key][e] of the 64-key tile in LDS buffer cs; the first k step of
+  // each block starts from a zero accumulator
   auto scores = [&](const f16* cs, f32x4 (&sc)[4][NEB]) {
+    f16x8 a[NSS];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int i = 0; i < kPre; ++i) a[i] = rd_s(cs, i);
 #pragma unroll
-      for (int eb = 0; eb < NEB; ++eb) sc[kb][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const f16* rowb = cs + kb * 16 * R;
+    for (int i = 0; i < NSS; ++i) {
+      if (i + kPre < NSS) a[i + kPre] = rd_s(cs, i + kPre);
+      const int kb = i / NKS, ks = i % NKS;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const f16x8 a = cat(*(const f16x4*)&rowb[off_s(2 * ks)],
-                            *(const f16x4*)&rowb[off_s(2 * ks + 1)]);
-#pragma unroll
-        for (int eb = 0; eb < NEB; ++eb) sc[kb][eb] = mfma_f16(a, qf[eb][ks], sc[kb][eb]);
-      }
+      for (int eb = 0; eb < NEB; ++eb)
+        sc[kb][eb] = mfma_f16(a[i], qf[eb][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sc[kb][eb]);
     }
-    // issue order: operand reads run two steps ahead of the MFMAs using them
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPre, 0);
 #pragma unroll
-    for (int i = 0; i < 4 * NKS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, NEB, 0);  // NEB MFMAs
+    for (int i = 0; i < NSS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NEB, 0);
+      if (i + kPre < NSS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
 
   // Online softmax of tile t's scores (this lane's column of S^T per block),
-  // then O^T += C^T P^T from the tile in LDS buffer cs. The running max only
-  // moves when a tile's max exceeds it by more than kLazy (log2 units):
-  // P = exp2(s - m_run) then stays <= 2^kLazy, exact enough in fp16, and the
-  // accumulators are rescaled only on those tiles. Row sums of the fp16 P
-  // are accumulated on the matrix cores with an all-ones A operand.
-  auto softmax_pv = [&](int t, f32x4 (&sc)[4][NEB], const f16* cs) {
+  // into the fp16 P^T operands. The running max only moves when a tile's max
+  // exceeds it by more than kLazy (log2 units): P = exp2(s - m_run) then
+  // stays <= 2^kLazy, exact enough in fp16, and the accumulators are
+  // rescaled only on those tiles.
+  auto softmax = [&](int t, f32x4 (&sc)[4][NEB], f16x8 (&pf)[2][NEB]) {
     const bool need_mask = t * BN + BN - 1 > pmin;
-    f16x8 pf[2][NEB];
 #pragma unroll
     for (int eb = 0; eb < NEB; ++eb) {
       if (need_mask) {
@@ -340,68 +376,96 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams p, AttnCfg cf
       pf[0][eb] = pack8(sc[0][eb], sc[1][eb]);
       pf[1][eb] = pack8(sc[2][eb], sc[3][eb]);
     }
-    // O^T[r][e] += sum over keys of C^T[r][key] * P^T[key][e]; the C^T
-    // operand comes from the row-major tile through the transpose load
+  };
+
+  // O^T[r][e] += sum over keys of C^T[r][key] * P^T[key][e]; the C^T operand
+  // comes from the row-major tile through the transpose load, its first
+  // kPre steps already in flight (pa). Row sums of the fp16 P are
+  // accumulated on the matrix cores with an all-ones A operand.
+  auto pv = [&](const f16* cs, f16x8 (&pa)[kPre], const f16x8 (&pf)[2][NEB]) {
+    f16x8 a[NPS];
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
+    for (int j = 0; j < kPre; ++j) a[j] = pa[j];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const f16x8 a = cat(lds_read_tr(cs + kk * 32 * R + off_t(rb)),
-                            lds_read_tr(cs + (kk * 32 + 16) * R + off_t(rb)));
+    for (int j = 0; j < NPS; ++j) {
+      if (j + kPre < NPS) a[j + kPre] = rd_pv(cs, j + kPre);
+      const int rb = j / 2, kk = j % 2;
 #pragma unroll
-        for (int eb = 0; eb < NEB; ++eb) acc_o[rb][eb] = mfma_f16(a, pf[kk][eb], acc_o[rb][eb]);
-      }
+      for (int eb = 0; eb < NEB; ++eb) acc_o[rb][eb] = mfma_f16(a[j], pf[kk][eb], acc_o[rb][eb]);
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) acc_l[eb] = mfma_f16(kOnes, pf[kk][eb], acc_l[eb]);
 #pragma unroll
-    for (int i = 0; i < 2 * NRB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // 2 transposed LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, NEB, 1);  // NEB MFMAs
+    for (int j = 0; j < NPS; ++j) {
+      if (j + kPre < NPS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, NEB, 1);
     }
   };
 
   // Double-buffered tiles: the next tile's global loads are in flight while
   // this one is computed; one barrier per tile.
   f32x4 st[4][NEB];
-  load_tile(0);
   store_tile(0);
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int cur = t & 1;
+    const f16* cs = &Cs[cur][0];
     if (t + 1 < ntiles) load_tile(t + 1);
-    scores(&Cs[cur][0], st);
-    softmax_pv(t, st, &Cs[cur][0]);
+    scores(cs, st);
+    f16x8 pa[kPre];
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) pa[j] = rd_pv(cs, j);
+    f16x8 pf[2][NEB];
+    softmax(t, st, pf);
+    pv(cs, pa, pf);
     if (t + 1 < ntiles) store_tile(cur ^ 1);
     __syncthreads();
   }
 
+  if constexpr (FUSED) {
+    // o^T[k][e] = sum_r W_uv^T[head][k][r] * o_lat^T[r][e]: the head's W_uv^T
+    // fragments once per wave, in batches of at most 16 in flight together
+    constexpr int NB = DK / 16;
+    constexpr int NBC = NB * NKS <= 16 ? NB : 16 / NKS;
+    const f16* wv = (const f16*)p.w_uv_t + ((size_t)head[0] * DK + l16) * R + g * 4;
+    f16x8 ob[NEB][NKS];
 #pragma unroll
-  for (int eb = 0; eb < NEB; ++eb) {
-    const float inv = 1.f / acc_l[eb][0];
-    if constexpr (FUSED) {
-      // o^T[k][e] = sum_r W_uv^T[head][k][r] * o_lat^T[r][e]
-      f16x8 ob[NKS];
+    for (int eb = 0; eb < NEB; ++eb) {
+      const float inv = 1.f / acc_l[eb][0];
 #pragma unroll
       for (int kk = 0; kk < NKS; ++kk)
-        ob[kk] = pack8(acc_o[2 * kk][eb], acc_o[2 * kk + 1][eb], inv);
-      const f16* wv = (const f16*)p.w_uv_t + ((size_t)head[eb] * DK + l16) * R + g * 4;
-      bf16* op = (bf16*)p.out + (size_t)qrow[eb] * (p.h * DK) + head[eb] * DK + g * 4;
+        ob[eb][kk] = pack8(acc_o[2 * kk][eb], acc_o[2 * kk + 1][eb], inv);
+    }
 #pragma unroll
-      for (int nb = 0; nb < DK / 16; ++nb) {
-        f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb0 = 0; nb0 < NB; nb0 += NBC) {
+      f16x8 w[NBC][NKS];
+#pragma unroll
+      for (int n = 0; n < NBC; ++n)
 #pragma unroll
         for (int kk = 0; kk < NKS; ++kk) {
-          const f16* w = wv + (size_t)nb * 16 * R + kk * 32;
-          o = mfma_f16(cat(*(const f16x4*)w, *(const f16x4*)(w + 16)), ob[kk], o);
+          const f16* q = wv + (size_t)(nb0 + n) * 16 * R + kk * 32;
+          w[n][kk] = cat(*(const f16x4*)q, *(const f16x4*)(q + 16));
         }
-        if (valid[eb])
-          *(bf16x4*)(op + nb * 16) = bf16x4{(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};
+#pragma unroll
+      for (int eb = 0; eb < NEB; ++eb) {
+        bf16* op = (bf16*)p.out + (size_t)qrow[eb] * (p.h * DK) + head[eb] * DK + g * 4;
+#pragma unroll
+        for (int n = 0; n < NBC; ++n) {
+          f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < NKS; ++kk) o = mfma_f16(w[n][kk], ob[eb][kk], o);
+          if (valid[eb])
+            *(bf16x4*)(op + (nb0 + n) * 16) = bf16x4{(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};
+        }
       }
-    } else {
+    }
+  } else {
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb) {
       if (!valid[eb]) continue;
+      const float inv = 1.f / acc_l[eb][0];
       const size_t orow = (size_t)qrow[eb] * p.h + head[eb];
       float* op = (float*)p.out + orow * R + g * 4;
 #pragma unroll
@@ -472,8 +536,8 @@ static int attn_epw(int r) { return r == 256 ? 16 : 32; }
 
 static AttnCfg attn_cfg(int h, int r) {
   const int eff = 8 * attn_epw(r);  // effective rows per workgroup
-  int hg = 1;                       // power-of-two divisor of h, BQ >= 16
-  while (h % (hg * 2) == 0 && eff / (hg * 2) >= 16) hg *= 2;
+  int hg = 1;  // power-of-two divisor of h, BQ >= 16, at most one head per wave
+  while (h % (hg * 2) == 0 && eff / (hg * 2) >= 16 && hg * 2 <= 8) hg *= 2;
   return AttnCfg{hg, eff / hg};
 }
 

@@ -3,10 +3,13 @@
 // scores its latent query against the same latent rows C and averages C
 // itself, so one C tile in LDS serves all heads of a query block.
 //
-// MFMA kernel: one workgroup (8 waves) per work item (a block of BQ query
-// rows of one user, for HG heads). Each wave owns EPW (head, query row)
-// pairs, "effective rows", head-major, so every 16-row MFMA block belongs
-// to one head. Per 64-key tile of C:
+// MFMA kernel: one workgroup per work item (a block of BQ query rows of one
+// user) and group of HG heads. Each wave owns EPW (head, query row) pairs,
+// "effective rows", all of one head. For r <= 128 a workgroup has four
+// waves and two workgroups share a CU (register budget: two waves per
+// SIMD), so one workgroup's prologue, epilogue and barrier waits overlap
+// the other's matrix work; for r = 256 eight waves fill the CU (LDS). Per
+// 64-key tile of C:
 //   S^T = C_tile . Qlat^T        v_mfma_f32_16x16x32_f16; A = C rows (LDS),
 //                                B = latent queries held in registers
 //   online softmax per column    fp32, exp2 (the softmax scale and log2(e)
@@ -131,13 +134,17 @@ struct AttnCfg {
   int BQ;  // query rows per workgroup (multiple of 16)
 };
 
+// Waves per workgroup.
+__host__ __device__ constexpr int attn_waves(int r) { return r == 256 ? 8 : 4; }
+
 template <int R, int EPW, int DK, bool FUSED, typename CT>
-__global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams p, AttnCfg cfg) {
+__global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnParams p, AttnCfg cfg) {
+  constexpr int kAttnThreads = 64 * attn_waves(R);
   constexpr int BN = kAttnBN;        // keys per tile
   constexpr int NEB = EPW / 16;      // effective-row blocks per wave
   constexpr int NKS = R / 32;        // 32-wide steps over r
   constexpr int NRB = R / 16;        // 16-wide blocks over r
-  constexpr int NLD = BN * R / 8 / 512;  // 16-byte chunks per thread and tile
+  constexpr int NLD = BN * R / 8 / kAttnThreads;  // 16-byte chunks per thread and tile
   static_assert(NLD >= 1, "tile too small for the staging map");
   constexpr bool C_BF16 = __is_same(CT, bf16);
 
@@ -187,7 +194,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams p, AttnCfg cf
   int ld_src[NLD], st_off[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
-    const int idx = tid + i * 512;
+    const int idx = tid + i * kAttnThreads;
     const int key = idx / (R / 8), j = idx % (R / 8);
     ld_src[i] = key * R + j * 8;
     st_off[i] = key * R + ((2 * j) ^ swz_key<R>(key)) * 4;
@@ -535,9 +542,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
 static int attn_epw(int r) { return r == 256 ? 16 : 32; }
 
 static AttnCfg attn_cfg(int h, int r) {
-  const int eff = 8 * attn_epw(r);  // effective rows per workgroup
+  const int nw = attn_waves(r);
+  const int eff = nw * attn_epw(r);  // effective rows per workgroup
   int hg = 1;  // power-of-two divisor of h, BQ >= 16, at most one head per wave
-  while (h % (hg * 2) == 0 && eff / (hg * 2) >= 16 && hg * 2 <= 8) hg *= 2;
+  while (h % (hg * 2) == 0 && eff / (hg * 2) >= 16 && hg * 2 <= nw) hg *= 2;
   return AttnCfg{hg, eff / hg};
 }
 
@@ -554,7 +562,7 @@ template <int R, int EPW, int DK, bool FUSED, typename CT>
 static void launch_mfma(const AttnParams& p, hipStream_t s) {
   const AttnCfg c = attn_cfg(p.h, R);
   dim3 grid(p.items_cap, p.h / c.HG);
-  hipLaunchKernelGGL((attn_mfma_kernel<R, EPW, DK, FUSED, CT>), grid, dim3(512),
+  hipLaunchKernelGGL((attn_mfma_kernel<R, EPW, DK, FUSED, CT>), grid, dim3(64 * attn_waves(R)),
                      0, s, p, c);
 }
 

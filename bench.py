@@ -101,6 +101,27 @@ def non_absorbed_flops(cfg, lengths):
     return t
 
 
+def kernel_source(label):
+    """Source file of the kernel behind a timing label."""
+    name = "attention.hip" if label.startswith("attention") else "gemm.hip"
+    return os.path.join(ROOT, "target_aware_latent_amd", "csrc", name)
+
+
+def read_traffic(path, label):
+    """HBM bytes per launch of `label` from a profile summary's RECORD line,
+    or None when there is none or the kernel changed since it was taken."""
+    if not path or not os.path.exists(path):
+        return None
+    from target_aware_latent_amd.profsum import fingerprint
+    for line in open(path):
+        if line.startswith("RECORD "):
+            rec = json.loads(line[len("RECORD "):])
+            if rec.get("kernel") == label and \
+                    rec.get("fingerprint") == fingerprint(kernel_source(label)):
+                return rec.get("bytes")
+    return None
+
+
 def cpu_baseline(prob, budget_s=12.0):
     """The oracle as it stands, in fp32 on the host cores, on the first users
     of the batch until about budget_s seconds of work (at least one user)."""
@@ -139,9 +160,11 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 256 MiB device-to-device copy first, "
                          "as the reference for HBM byte counters")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per launch of the "
-                         "dominant kernel ({'kernel':..., 'bytes':...})")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles",
+                                                      "c3_attention_hbm_traffic.txt"),
+                    help="profile summary whose RECORD line holds the measured "
+                         "HBM bytes per launch of the dominant kernel (written "
+                         "by target_aware_latent_amd.profsum traffic)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
@@ -220,11 +243,7 @@ def main():
         per_launch_flops = kf[dom] * args.steps / cnt
         avg_s = tot / cnt / 1e3
         achieved = per_launch_flops / avg_s / 1e12
-        traffic = None
-        if args.traffic and os.path.exists(args.traffic):
-            tr = json.load(open(args.traffic))
-            if tr.get("kernel") == dom:
-                traffic = tr.get("bytes")
+        traffic = read_traffic(args.traffic, dom)
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                     "peak": peak, "unit": "TFLOP/s",
                     "frac": round(achieved / peak, 4), "traffic": traffic,

@@ -70,7 +70,10 @@ def _layer(Rh, Rc, n, W, cfg):
     qrows += [(Hc[j], Rc[j], K - 1) for j in range(nc)]
     out = []
     for Hx, Rx, pos in qrows:
-        q = _matvec_row(Hx, Wuq)
+        if "W_dq" in W:  # low-rank query path: RMSNorm(x W_dq) g_q W_uq
+            q = _matvec_row(_rms(_matvec_row(Hx, _mat(W["W_dq"])), _vec(W["g_q"]), eps), Wuq)
+        else:
+            q = _matvec_row(Hx, Wuq)
         o = [0.0] * (h * dk)
         for hh in range(h):
             sc = []

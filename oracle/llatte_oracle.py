@@ -20,7 +20,9 @@ with its reason in the design notes):
   * pre-norm layer by default (the A.2 layer equation is written post-norm;
     both placements are implemented, 'post' follows A.2 literally);
   * RMSNorm on the latent C (A.3) on by default, switchable off;
-  * full-rank per-layer query projection W_uq (no low-rank query path);
+  * queries: a full-rank per-layer W_uq by default, or the A.3 low-rank path
+    RMSNorm(H W_dq) g_q W_uq when the layer carries W_dq (the pages give no
+    query rank; it is a workload parameter);
   * softmax scale 1/sqrt(head_dim) in both MLA forms (A.3's absorbed form
     writes sqrt(d_c); the two forms are only equal with one common scale);
   * candidate query tokens attend every history key and nothing else;
@@ -182,6 +184,8 @@ def mla_layer(Rh, Rc, n, W, cfg, absorbed=False, return_probs=False):
 
     [LLaTTE] A.3 non-absorbed MLA: C = RMSNorm(H W_down^KV) (the latent),
     K, V = split(C W_up^KV), attention softmax(Q K^T / sqrt(d_k)) V W_out.
+    Queries: Q = H W_uq (full rank), or, when the layer has W_dq, the A.3
+    low-rank path Q = RMSNorm(H W_down^Q) W_up^Q with gain g_q.
     With ``absorbed`` the A.3 rewritten form is used instead: per head the
     query is moved into latent space (q W_uk^T), scores are taken against C
     itself and the output is mapped back through W_uv.
@@ -204,7 +208,10 @@ def mla_layer(Rh, Rc, n, W, cfg, absorbed=False, return_probs=False):
     Hq = np.concatenate([Hh[K - n:], Hc], axis=0)
     Rq = np.concatenate([Rh[K - n:], Rc], axis=0)
     M = Hq.shape[0]
-    q = _split_heads(Hq @ W["W_uq"], h)              # [M, h, dk]
+    if "W_dq" in W:                                  # low-rank query path
+        q = _split_heads(rmsnorm(Hq @ W["W_dq"], W["g_q"], eps) @ W["W_uq"], h)
+    else:
+        q = _split_heads(Hq @ W["W_uq"], h)          # [M, h, dk]
     allowed = history_query_mask(K, n, n_c)          # [M, K]
     scale = 1.0 / math.sqrt(dk)
 
@@ -369,7 +376,8 @@ def flop_count(cfg, lengths, absorbed=True):
     allowed (query, key) pair 4*r*h (absorbed) or 4*d_k*h (non-absorbed).
 
     Matrix products per layer, with K history rows in and M = n + n_q query
-    rows: W_dkv (K x d x r), W_uq (M x d x h*dk), then absorbed W_uk and W_uv
+    rows: W_dkv (K x d x r), W_uq (M x d x h*dk; low-rank: W_dq M x d x r_q
+    and W_uq M x r_q x h*dk), then absorbed W_uk and W_uv
     on the queries (M x dk x r per head, each) or non-absorbed W_uk and W_uv on
     the keys (K x r x h*dk, each), W_o (M x h*dk x d), W1 and W2 (M x d x 4d).
     Plus the fusion (B*n_q x (d+d_c) x d), the readout projection
@@ -391,7 +399,10 @@ def flop_count(cfg, lengths, absorbed=True):
             nq = cfg.n_seeds
         Kt = int(Ks.sum())
         Mt = int(n.sum()) + nq * cfg.B
-        total += 2 * Kt * d * r + 2 * Mt * d * h * dk
+        if getattr(cfg, "r_q", 0):
+            total += 2 * Kt * d * r + 2 * Mt * d * cfg.r_q + 2 * Mt * cfg.r_q * h * dk
+        else:
+            total += 2 * Kt * d * r + 2 * Mt * d * h * dk
         if absorbed:
             total += 2 * (2 * Mt * h * dk * r) + 4 * r * h * int(pairs[l])
         else:

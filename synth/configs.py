@@ -63,6 +63,8 @@ class Config:
     d_out: int = 0                   # readout: embedding width
     semantic: Optional[SemanticSpec] = None
     gain_jitter: float = 0.0         # gains = 1 + jitter * N(0,1)
+    r_q: int = 0                     # query rank: 0 = full-rank W_uq [d, h*dk];
+                                     # > 0 = RMSNorm(H W_dq) g_q W_uq [r_q, h*dk]
 
     @property
     def d_ff(self) -> int:

@@ -45,12 +45,13 @@ def _gain(rng, cfg, n):
 
 
 def _layer(rng, cfg):
-    d, hd, r = cfg.d, cfg.h * cfg.dk, cfg.r
-    return {
+    d, hd, r, rq = cfg.d, cfg.h * cfg.dk, cfg.r, cfg.r_q
+    qin = rq if rq else d  # input width of W_uq
+    L = {
         "g1": _gain(rng, cfg, d),
         "W_dkv": _w(rng, cfg, d, (d, r)),
         "g_c": _gain(rng, cfg, r),
-        "W_uq": _w(rng, cfg, d, (d, hd)),
+        "W_uq": _w(rng, cfg, qin, (qin, hd)),
         "W_uk": _w(rng, cfg, r, (r, hd)),
         "W_uv": _w(rng, cfg, r, (r, hd)),
         "W_o": _w(rng, cfg, hd, (hd, d)),
@@ -58,6 +59,10 @@ def _layer(rng, cfg):
         "W1": _w(rng, cfg, d, (d, cfg.d_ff)),
         "W2": _w(rng, cfg, cfg.d_ff, (cfg.d_ff, d)),
     }
+    if rq:  # low-rank query path, drawn after the rest of the layer
+        L["W_dq"] = _w(rng, cfg, d, (d, rq))
+        L["g_q"] = _gain(rng, cfg, rq)
+    return L
 
 
 def _lengths(rng, cfg):

@@ -30,13 +30,18 @@ def tiny_cfg(**kw):
 
 
 def rand_layer(rng, cfg):
-    d, hd, r = cfg.d, cfg.h * cfg.dk, cfg.r
+    d, hd, r, rq = cfg.d, cfg.h * cfg.dk, cfg.r, cfg.r_q
+    qin = rq if rq else d
     n = lambda *s: rng.standard_normal(s)
-    return {"g1": 1 + 0.1 * n(d), "W_dkv": n(d, r) / math.sqrt(d),
-            "g_c": 1 + 0.1 * n(r), "W_uq": n(d, hd) / math.sqrt(d),
-            "W_uk": n(r, hd) / math.sqrt(r), "W_uv": n(r, hd) / math.sqrt(r),
-            "W_o": n(hd, d) / math.sqrt(hd), "g2": 1 + 0.1 * n(d),
-            "W1": n(d, 4 * d) / math.sqrt(d), "W2": n(4 * d, d) / math.sqrt(4 * d)}
+    L = {"g1": 1 + 0.1 * n(d), "W_dkv": n(d, r) / math.sqrt(d),
+         "g_c": 1 + 0.1 * n(r), "W_uq": n(qin, hd) / math.sqrt(qin),
+         "W_uk": n(r, hd) / math.sqrt(r), "W_uv": n(r, hd) / math.sqrt(r),
+         "W_o": n(hd, d) / math.sqrt(hd), "g2": 1 + 0.1 * n(d),
+         "W1": n(d, 4 * d) / math.sqrt(d), "W2": n(4 * d, d) / math.sqrt(4 * d)}
+    if rq:
+        L["W_dq"] = n(d, rq) / math.sqrt(d)
+        L["g_q"] = 1 + 0.1 * n(rq)
+    return L
 
 
 def rel(a, b):
@@ -92,12 +97,21 @@ def torch_layer(Rh, Rc, n, W, cfg):
     mha = torch.nn.MultiheadAttention(d, h, bias=False, kdim=cfg.r, vdim=cfg.r,
                                       batch_first=True, dtype=torch.float64)
     with torch.no_grad():
-        mha.q_proj_weight.copy_(t(W["W_uq"]).T)
+        if "W_dq" not in W:
+            mha.q_proj_weight.copy_(t(W["W_uq"]).T)
         mha.k_proj_weight.copy_(t(W["W_uk"]).T)
         mha.v_proj_weight.copy_(t(W["W_uv"]).T)
         mha.out_proj.weight.copy_(t(W["W_o"]).T)
-    mha.eval()
     Hq = torch.cat([Hh[K - n:], Hc])
+    if "W_dq" in W:
+        # low-rank query path: the query enters already projected,
+        # RMSNorm(Hq W_dq) g_q W_uq, through an identity q_proj (h*dk == d)
+        with torch.no_grad():
+            mha.q_proj_weight.copy_(torch.eye(d, dtype=torch.float64))
+        Qin = norm(Hq @ t(W["W_dq"]), W["g_q"]) @ t(W["W_uq"])
+    else:
+        Qin = Hq
+    mha.eval()
     Rq = torch.cat([Rh_t[K - n:], Rc_t])
     M = Hq.shape[0]
     blocked = torch.ones(M, K, dtype=torch.bool)
@@ -105,7 +119,7 @@ def torch_layer(Rh, Rc, n, W, cfg):
         blocked[i, :K - n + i + 1] = False
     blocked[n:, :] = False
     with torch.no_grad():
-        A = mha(Hq[None], C[None], C[None], attn_mask=blocked,
+        A = mha(Qin[None], C[None], C[None], attn_mask=blocked,
                 need_weights=False)[0][0]
     gelu = lambda x: F.gelu(x, approximate="none")
     if pre:
@@ -135,6 +149,41 @@ def test_layer_matches_torch_nn(norm_mode, latent_norm, K, n, nc):
         assert rel(ah, bh) < 1e-12
     if nc:
         assert rel(ac, bc) < 1e-12
+
+
+@pytest.mark.parametrize("norm_mode", ["pre", "post"])
+@pytest.mark.parametrize("K,n,nc,rq", [(9, 9, 3, 5), (9, 4, 2, 24), (6, 0, 4, 3)])
+def test_low_rank_query_layer_matches_torch_nn(norm_mode, K, n, nc, rq):
+    cfg = tiny_cfg(d=16, h=4, dk=4, r=6, norm_mode=norm_mode, r_q=rq)
+    rng = np.random.default_rng(K * 100 + n * 10 + nc + rq)
+    W = rand_layer(rng, cfg)
+    Rh = rng.standard_normal((K, cfg.d))
+    Rc = rng.standard_normal((nc, cfg.d))
+    ah, ac = O.mla_layer(Rh, Rc, n, W, cfg)
+    bh, bc = torch_layer(Rh, Rc, n, W, cfg)
+    if n:
+        assert rel(ah, bh) < 1e-12
+    if nc:
+        assert rel(ac, bc) < 1e-12
+
+
+def test_low_rank_query_with_identity_down_projection_is_full_rank():
+    # With eps = 0, g1 = 1, W_dq = I and g_q = 1 the query norm acts on rows
+    # that are already unit-RMS, so the low-rank path returns H W_uq exactly
+    # (up to rounding) and the layer equals the full-rank layer.
+    cfg = tiny_cfg(d=16, h=4, dk=4, r=6, eps=0.0, r_q=16)
+    cfg_full = dataclasses.replace(cfg, r_q=0)
+    rng = np.random.default_rng(77)
+    W = rand_layer(rng, cfg)
+    W["g1"] = np.ones(cfg.d)
+    W["W_dq"] = np.eye(cfg.d)
+    W["g_q"] = np.ones(cfg.d)
+    Wf = {k: v for k, v in W.items() if k not in ("W_dq", "g_q")}
+    Rh = rng.standard_normal((7, cfg.d))
+    Rc = rng.standard_normal((2, cfg.d))
+    ah, ac = O.mla_layer(Rh, Rc, 4, W, cfg)
+    bh, bc = O.mla_layer(Rh, Rc, 4, Wf, cfg_full)
+    assert rel(ah, bh) < 1e-12 and rel(ac, bc) < 1e-12
 
 
 # ------------------------------------------------------- MLA invariants
@@ -351,6 +400,10 @@ BRUTE_CASES = [
          n_seeds=2, d_out=5),
     dict(N=2, n_q=2, d_c=3, pyramid=synth.PyramidRule("fixed", (4, 2)), L=(6, 4, 3),
          norm_mode="post", latent_norm=False),
+    dict(N=2, n_q=2, d_c=3, pyramid=synth.PyramidRule("fixed", (5, 3)), L=(5, 2, 8),
+         r_q=5),
+    dict(N=2, n_q=1, d_c=3, pyramid=synth.PyramidRule("fixed", (4, 2)), L=(5, 4, 2),
+         n_seeds=2, d_out=5, r_q=3, norm_mode="post"),
 ]
 
 

@@ -65,7 +65,11 @@ def kernel_flops(cfg, lengths):
     add = lambda k, v: f.__setitem__(k, f.get(k, 0) + v)
     for Ks, ns, M, pairs in layer_counts(cfg, lengths):
         add("gemm_down", 2 * Ks * d * r)
-        add("gemm_q", 2 * M * d * h * dk)
+        if cfg.r_q:  # low-rank query path
+            add("gemm_qdown", 2 * M * d * cfg.r_q)
+            add("gemm_q", 2 * M * cfg.r_q * h * dk)
+        else:
+            add("gemm_q", 2 * M * d * h * dk)
         if cfg.dtype == "bf16":
             # the attention kernel also applies W_uk (prologue) and W_uv
             # (epilogue) of the absorbed form
@@ -92,7 +96,8 @@ def non_absorbed_flops(cfg, lengths):
     d, h, dk, r, dff = cfg.d, cfg.h, cfg.dk, cfg.r, 4 * cfg.d
     t = 0
     for Ks, ns, M, pairs in layer_counts(cfg, lengths):
-        t += 2 * Ks * d * r + 2 * M * d * h * dk + 2 * (2 * Ks * r * h * dk)
+        qproj = (2 * M * d * cfg.r_q + 2 * M * cfg.r_q * h * dk) if cfg.r_q else 2 * M * d * h * dk
+        t += 2 * Ks * d * r + qproj + 2 * (2 * Ks * r * h * dk)
         t += 4 * dk * h * pairs + 2 * M * h * dk * d + 2 * (2 * M * d * dff)
     if cfg.n_q:
         t += 2 * cfg.B * cfg.n_q * (d + cfg.d_c) * d

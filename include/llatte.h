@@ -74,7 +74,11 @@ typedef struct {
 } llatte_pyramid_rule;
 
 /* Model shape and options. d_ff must be 4*d. head_dim*n_heads is the query
- * width. rank is the latent width r of C = H W_dkv ([LLaTTE] A.3). */
+ * width. rank is the latent width r of C = H W_dkv ([LLaTTE] A.3).
+ * q_rank selects the query path of [LLaTTE] A.3: 0 = one full-rank W_uq
+ * [d, h*dk]; > 0 = the low-rank path q = RMSNorm(H W_dq) g_q W_uq with
+ * W_dq [d, q_rank] and W_uq [q_rank, h*dk] (q_rank a multiple of 8 on the
+ * bf16 path, of 4 on the fp32 path, at most 1024). */
 typedef struct {
   int32_t d;           /* model width                                       */
   int32_t n_heads;     /* h                                                 */
@@ -92,12 +96,14 @@ typedef struct {
   int32_t n_seeds;     /* readout seed queries (0 = no readout)             */
   int32_t d_out;       /* readout embedding width                           */
   uint32_t flags;      /* reserved, must be 0                               */
+  int32_t q_rank;      /* 0: full-rank queries; > 0: low-rank query width   */
 } llatte_model_desc;
 
 /* Weights of one layer (device pointers). g* are float32 gains; the
  * matrices have the descriptor's dtype:
- *   W_dkv [d, r], W_uq [d, h*dk], W_uk [r, h*dk], W_uv [r, h*dk],
- *   W_o [h*dk, d], W1 [d, d_ff], W2 [d_ff, d].
+ *   W_dkv [d, r], W_uq [d, h*dk] (q_rank = 0) or [q_rank, h*dk],
+ *   W_uk [r, h*dk], W_uv [r, h*dk], W_o [h*dk, d], W1 [d, d_ff], W2 [d_ff, d];
+ *   with q_rank > 0 also W_dq [d, q_rank] and g_q [q_rank] (NULL otherwise).
  * Head j of W_uk / W_uv is the column slice j*dk .. (j+1)*dk-1. */
 typedef struct {
   const float* g1;
@@ -110,6 +116,8 @@ typedef struct {
   const float* g2;
   const void* W1;
   const void* W2;
+  const void* W_dq;    /* low-rank query path only */
+  const float* g_q;
 } llatte_layer_weights;
 
 /* All weights. `layers` is a HOST array of n_layers structs.

@@ -129,6 +129,7 @@ static PlanBase carve_plan(Arena& ar, int n_plans, int B, int qcap, int icap) {
 struct Shapes {
   int B, total, max_len;
   int d, h, dk, hd, r, dff, N, nq, dc, ns, dout;
+  int rq, qin;                // query rank (0: full rank) and W_uq input width
   bool bf16, pre, lnorm;
   bool fnorm;                 // norms fused into the GEMMs (bf16, pre-norm)
   float eps;
@@ -201,6 +202,8 @@ static llatte_status make_shapes(const llatte_model_desc* dsc, int B, int total,
   S->dc = dsc->d_ctx;
   S->ns = dsc->n_seeds;
   S->dout = dsc->d_out;
+  S->rq = dsc->q_rank;
+  S->qin = S->rq > 0 ? S->rq : dsc->d;
   S->bf16 = dsc->dtype == LLATTE_BF16;
   S->pre = dsc->norm_mode == LLATTE_NORM_PRE;
   S->lnorm = dsc->latent_norm != 0;
@@ -215,6 +218,8 @@ static llatte_status make_shapes(const llatte_model_desc* dsc, int B, int total,
     return fail(LLATTE_ERR_UNSUPPORTED, "d, head_dim, rank and d+d_ctx must be multiples of %d", al);
   if (S->d > 1024 || S->r > 1024)
     return fail(LLATTE_ERR_UNSUPPORTED, "d and rank must be <= 1024");
+  if (S->rq < 0 || S->rq > 1024 || S->rq % al)
+    return fail(LLATTE_ERR_UNSUPPORTED, "q_rank must be 0 or a multiple of %d up to 1024", al);
   if (S->dff != 4 * S->d) return fail(LLATTE_ERR_INVALID_ARG, "d_ff must be 4*d");
   if (!(S->eps >= 0.f)) return fail(LLATTE_ERR_INVALID_ARG, "eps must be >= 0");
   if (S->nq == 0 && S->dc != 0) return fail(LLATTE_ERR_INVALID_ARG, "d_ctx needs n_q > 0");
@@ -272,8 +277,8 @@ static llatte_status make_shapes(const llatte_model_desc* dsc, int B, int total,
 // epilogue on the bf16 path, gains and seeds copied. One blob, written by
 // llatte_pack_weights (or into the workspace by every forward call).
 struct PackedLayer {
-  float *g1, *g_c, *g2;
-  void *Wdkv, *Wuq, *Wuk, *Wuv, *Wo, *W1, *W2;
+  float *g1, *g_c, *g2, *g_q;
+  void *Wdkv, *Wuq, *Wuk, *Wuv, *Wo, *W1, *W2, *Wdq;
 };
 struct Packed {
   std::vector<PackedLayer> L;  // N layers (+ readout)
@@ -291,7 +296,9 @@ static size_t layout_packed(const Shapes& S, void* base, Packed* P) {
     q.g_c = ar.take<float>(S.r);
     q.g2 = ar.take<float>(S.d);
     q.Wdkv = ar.take<char>((size_t)S.d * S.r * e);
-    q.Wuq = ar.take<char>((size_t)S.d * S.hd * e);
+    q.Wuq = ar.take<char>((size_t)S.qin * S.hd * e);
+    q.Wdq = S.rq ? ar.take<char>((size_t)S.d * S.rq * e) : nullptr;
+    q.g_q = S.rq ? ar.take<float>(S.rq) : nullptr;
     q.Wuk = ar.take<char>((size_t)S.r * S.hd * e);
     q.Wuv = ar.take<char>((size_t)S.r * S.hd * e);   // f16 on the bf16 path
     q.Wo = ar.take<char>((size_t)S.hd * S.d * e);
@@ -316,6 +323,8 @@ struct FwdWS {
   float* Cf;    // [max K, r] latent before its norm
   void* Cl;     // [max K, r] (f16 on the bf16 path)
   void* q;      // [qcap, hd]
+  void* Hq;     // [qcap, rq]  low-rank query path: RMSNorm(H W_dq) g_q
+  float* Qf;    // [qcap, rq]  its fp32 input when the norm is a separate pass
   void* ql;     // [qcap, h, r]   (f32 path)
   void* ol;     // [qcap, h, r]   (f32 path)
   void* o;      // [qcap, hd]
@@ -351,6 +360,8 @@ static size_t layout_forward(const Shapes& S, void* base, FwdWS* w) {
   w->Cf = S.fnorm ? nullptr : ar.take<float>((size_t)maxK * S.r);
   w->Cl = ar.take<char>((size_t)maxK * S.r * e);
   w->q = ar.take<char>((size_t)S.qcap * S.hd * e);
+  w->Hq = S.rq ? ar.take<char>((size_t)S.qcap * S.rq * e) : nullptr;
+  w->Qf = S.rq && !(S.fnorm && S.rq <= 256) ? ar.take<float>((size_t)S.qcap * S.rq) : nullptr;
   w->ql = S.bf16 ? nullptr : ar.take<char>((size_t)S.qcap * S.h * S.r * e);
   w->ol = S.bf16 ? nullptr : ar.take<char>((size_t)S.qcap * S.h * S.r * e);
   w->o = ar.take<char>((size_t)S.qcap * S.hd * e);
@@ -369,10 +380,12 @@ static size_t layout_forward(const Shapes& S, void* base, FwdWS* w) {
   return ar.off + 256;
 }
 
-static llatte_status check_layer(const llatte_layer_weights* L, int l) {
+static llatte_status check_layer(const Shapes& S, const llatte_layer_weights* L, int l) {
   if (!L->g1 || !L->W_dkv || !L->W_uq || !L->W_uk || !L->W_uv || !L->W_o ||
       !L->g2 || !L->W1 || !L->W2)
     return fail(LLATTE_ERR_INVALID_ARG, "layer %d: NULL weight pointer", l);
+  if (S.rq > 0 && (!L->W_dq || !L->g_q))
+    return fail(LLATTE_ERR_INVALID_ARG, "layer %d: q_rank > 0 needs W_dq and g_q", l);
   return LLATTE_OK;
 }
 
@@ -390,11 +403,17 @@ static hipError_t pack_layer(const Shapes& S, const llatte_layer_weights* L,
   if ((err = hipMemcpyAsync(T.Wuk, L->W_uk, (size_t)S.r * S.hd * e,
                             hipMemcpyDeviceToDevice, s)))
     return err;
-  // fused norms: diag(g1) W_dkv, diag(g1) W_uq, diag(g2) W1
+  // fused norms: diag(g1) W_dkv, diag(g1) W_uq (or W_dq), diag(g2) W1
   const float* g1 = S.fnorm ? L->g1 : nullptr;
   const float* g2 = S.fnorm ? L->g2 : nullptr;
   if ((err = transpose(L->W_dkv, S.d, S.r, S.r, 0, T.Wdkv, S.d, 0, 1, k, k, s, g1))) return err;
-  if ((err = transpose(L->W_uq, S.d, S.hd, S.hd, 0, T.Wuq, S.d, 0, 1, k, k, s, g1))) return err;
+  if ((err = transpose(L->W_uq, S.qin, S.hd, S.hd, 0, T.Wuq, S.qin, 0, 1, k, k, s,
+                       S.rq ? nullptr : g1)))
+    return err;
+  if (S.rq) {
+    if ((err = transpose(L->W_dq, S.d, S.rq, S.rq, 0, T.Wdq, S.d, 0, 1, k, k, s, g1))) return err;
+    if ((err = hipMemcpyAsync(T.g_q, L->g_q, S.rq * 4, hipMemcpyDeviceToDevice, s))) return err;
+  }
   // per head: W_uv[:, j*dk:(j+1)*dk] ([r, dk]) -> [dk, r]
   if ((err = transpose(L->W_uv, S.r, S.dk, S.hd, S.dk, T.Wuv, S.r,
                        (long long)S.dk * S.r, S.h, k, S.bf16 ? K_F16 : K_F32, s)))
@@ -503,17 +522,50 @@ static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
         return err;
     }
   }
-  // 3. q = H[qmap] W_uq
-  {
-    GemmParams g = gemm_base("gemm_q");
+  // 3. q = H[qmap] W_uq, or the low-rank path q = RMSNorm(H[qmap] W_dq) g_q W_uq
+  if (S.rq) {
+    GemmParams g = gemm_base("gemm_qdown");
     if (S.fnorm) g.rs = rs_in;
     g.A = w.H;
     g.lda = S.d;
     g.a_rows = P.qmap;
-    g.B = L.Wuq;
+    g.B = L.Wdq;
     g.ldb = S.d;
-    g.N = S.hd;
+    g.N = S.rq;
     g.K = S.d;
+    if (!w.Qf) {  // the query norm in the epilogue (one tile spans q_rank)
+      g.epi = EPI_ROWNORM;
+      g.gain = L.g_q;
+      g.eps = S.eps;
+      g.out_kind = tk;
+      g.C = w.Hq;
+      g.ldc = S.rq;
+      if ((err = gemm(g, b, s))) return err;
+    } else {
+      g.epi = EPI_STORE_F32;
+      g.C = w.Qf;
+      g.ldc = S.rq;
+      if ((err = gemm(g, b, s))) return err;
+      if ((err = norm_rows(RowSrc{w.Qf, w.Qf, 0, S.rq}, UBM, P.counts + 3, L.g_q, S.eps,
+                           nullptr, 0, w.Hq, S.rq, S.rq, tk, s)))
+        return err;
+    }
+  }
+  {
+    GemmParams g = gemm_base("gemm_q");
+    if (S.rq) {
+      g.A = w.Hq;
+      g.lda = S.rq;
+    } else {
+      if (S.fnorm) g.rs = rs_in;
+      g.A = w.H;
+      g.lda = S.d;
+      g.a_rows = P.qmap;
+    }
+    g.B = L.Wuq;
+    g.ldb = S.qin;
+    g.N = S.hd;
+    g.K = S.qin;
     g.C = w.q;
     g.ldc = S.hd;
     if ((err = gemm(g, b, s))) return err;
@@ -707,12 +759,12 @@ static llatte_status check_weights(const Shapes& S, const llatte_weights* wts) {
   llatte_status st;
   if (!wts || !wts->layers) return fail(LLATTE_ERR_INVALID_ARG, "weights are NULL");
   for (int l = 0; l < S.N; ++l)
-    if ((st = check_layer(&wts->layers[l], l))) return st;
+    if ((st = check_layer(S, &wts->layers[l], l))) return st;
   if (S.nq > 0 && !wts->W_q) return fail(LLATTE_ERR_INVALID_ARG, "n_q > 0 needs W_q");
   if (S.ns > 0) {
     if (!wts->seeds || !wts->W_p)
       return fail(LLATTE_ERR_INVALID_ARG, "readout needs seeds and W_p");
-    if ((st = check_layer(&wts->readout, -1))) return st;
+    if ((st = check_layer(S, &wts->readout, -1))) return st;
   }
   return LLATTE_OK;
 }

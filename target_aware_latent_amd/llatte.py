@@ -43,12 +43,13 @@ class llatte_model_desc(ctypes.Structure):
                 ("norm_mode", _c_int), ("latent_norm", _c_int),
                 ("eps", ctypes.c_float), ("pyramid", llatte_pyramid_rule),
                 ("n_seeds", _c_int), ("d_out", _c_int),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("q_rank", _c_int)]
 
 
 class llatte_layer_weights(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("g1", "W_dkv", "g_c", "W_uq", "W_uk",
-                                   "W_uv", "W_o", "g2", "W1", "W2")]
+                                   "W_uv", "W_o", "g2", "W1", "W2", "W_dq",
+                                   "g_q")]
 
 
 class llatte_weights(ctypes.Structure):

@@ -12,7 +12,8 @@ from . import llatte as C
 def make_desc(cfg):
     """llatte_model_desc from a workload description with the attributes
     d, h, dk, r, N, n_q, d_c, dtype ('f32'/'bf16'), norm_mode ('pre'/'post'),
-    latent_norm, eps, pyramid (kind/values/floor/start/end), n_seeds, d_out."""
+    latent_norm, eps, pyramid (kind/values/floor/start/end), n_seeds, d_out
+    and (optional) r_q."""
     d = C.llatte_model_desc()
     d.d, d.n_heads, d.head_dim, d.rank = cfg.d, cfg.h, cfg.dk, cfg.r
     d.d_ff = 4 * cfg.d
@@ -37,6 +38,7 @@ def make_desc(cfg):
         raise ValueError(rule.kind)
     d.n_seeds, d.d_out = cfg.n_seeds, cfg.d_out
     d.flags = 0
+    d.q_rank = getattr(cfg, "r_q", 0)
     return d
 
 
@@ -49,7 +51,7 @@ class DeviceModel:
     point at them (kept alive together)."""
 
     _LAYER_KEYS = ("g1", "W_dkv", "g_c", "W_uq", "W_uk", "W_uv", "W_o", "g2",
-                   "W1", "W2")
+                   "W1", "W2", "W_dq", "g_q")
 
     def __init__(self, cfg, W, device="cuda"):
         self.cfg = cfg
@@ -72,6 +74,8 @@ class DeviceModel:
         def layer(Wl):
             s = C.llatte_layer_weights()
             for k in self._LAYER_KEYS:
+                if k not in Wl:   # W_dq / g_q of the low-rank query path
+                    continue
                 t = vec(Wl[k]) if k.startswith("g") else mat(Wl[k])
                 setattr(s, k, t.data_ptr())
             return s

@@ -64,7 +64,8 @@ def test_invalid_descriptors_rejected_on_host(L):
     assert L.llatte_mla_forward_workspace_size(good, 4, 100, 50) > 0
     for field, val in [("d_ff", 3 * cfg.d), ("rank", 96), ("dtype", 7),
                        ("n_layers", 0), ("head_dim", 12), ("head_dim", 48),
-                       ("flags", 1)]:
+                       ("flags", 1), ("q_rank", 12), ("q_rank", -8),
+                       ("q_rank", 1032)]:
         d = make_desc(cfg)
         setattr(d, field, val)
         assert L.llatte_mla_forward_workspace_size(d, 4, 100, 50) == 0, field
@@ -74,6 +75,12 @@ def test_invalid_descriptors_rejected_on_host(L):
     # total_rows < B (some user would be empty)
     assert L.llatte_mla_forward_workspace_size(good, 4, 3, 50) == 0
     assert L.llatte_packed_weights_size(good) > 0
+    # a low-rank query path adds W_dq and g_q to the packed blob
+    lr = make_desc(cfg)
+    lr.q_rank = 96
+    assert L.llatte_mla_forward_workspace_size(lr, 4, 100, 50) > 0
+    assert L.llatte_packed_weights_size(lr) > L.llatte_packed_weights_size(good) - \
+        cfg.N * cfg.d * cfg.h * cfg.dk * 2
 
 
 def test_forward_argument_errors_return_status_without_launch(L):

@@ -6,10 +6,11 @@ import synth
 from oracle import llatte_oracle as O
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
-def test_bench_flop_count_matches_oracle_count(name):
+@pytest.mark.parametrize("name,r_q", [("c1", 0), ("c2", 0), ("c3", 0), ("c4", 0),
+                                      ("c3", 256), ("c2", 96)])
+def test_bench_flop_count_matches_oracle_count(name, r_q):
     import bench
-    cfg = synth.get_config(name)
+    cfg = synth.get_config(name, r_q=r_q)
     lengths = synth.generate(cfg)["inputs"]["lengths"] if cfg.len_range else \
         np.full(cfg.B, cfg.L)
     assert bench.absorbed_flops(cfg, lengths) == O.flop_count(cfg, lengths, True)

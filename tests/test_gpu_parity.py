@@ -318,6 +318,18 @@ SMALL_CASES = {
                                    pyramid=synth.PyramidRule("fixed", (200, 0))),
     "c5_small": lambda: small("c5", [200, 37], semantic=None, N=3,
                               pyramid=synth.PyramidRule("geometric", start=150, end=20)),
+    # low-rank query path (A.3): fp32; bf16 with the query norm in the GEMM
+    # epilogue for 64-, 128- and 256-wide ranks; wider ranks and post-norm
+    # through a separate norm pass
+    "c1_lowrank_f32": lambda: small("c1", [9, 32, 21], r_q=24, gain_jitter=0.1),
+    "c2_lowrank_64": lambda: small("c2", [70, 130, 1], r_q=64, gain_jitter=0.1),
+    "c3_small_lowrank": lambda: small("c3", [300, 150, 64, 1], r_q=128,
+                                      pyramid=synth.PyramidRule("fixed", (300, 129, 64, 33, 17, 5))),
+    "c5_small_lowrank": lambda: small("c5", [200, 37], semantic=None, N=3, r_q=256,
+                                      pyramid=synth.PyramidRule("geometric", start=150, end=20)),
+    "c4_lowrank_wide": lambda: small("c4", [65, 300, 129], r_q=384, gain_jitter=0.1),
+    "c2_post_lowrank": lambda: small("c2", [33, 257, 4], norm_mode="post", r_q=96,
+                                     gain_jitter=0.1),
 }
 
 
@@ -340,15 +352,16 @@ def test_forward_is_deterministic():
             assert np.array_equal(a[k], b[k]), k
 
 
-@pytest.mark.parametrize("name,users", [
-    ("c1", None),
-    ("c2", None),
-    ("c3", [0, 7, 31, 63]),
-    ("c4", None),
+@pytest.mark.parametrize("name,users,over", [
+    ("c1", None, {}),
+    ("c2", None, {}),
+    ("c3", [0, 7, 31, 63], {}),
+    ("c4", None, {}),
+    ("c3", [0, 40], {"r_q": 256}),
 ])
-def test_forward_full_size(name, users):
-    print(f"forward full {name}", flush=True)
-    prob = synth.generate(synth.get_config(name))
+def test_forward_full_size(name, users, over):
+    print(f"forward full {name} {over}", flush=True)
+    prob = synth.generate(synth.get_config(name, **over))
     got = gpu_forward(prob)
     B = prob["cfg"].B
     users = list(range(B)) if users is None else users

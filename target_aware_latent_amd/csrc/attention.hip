@@ -50,6 +50,8 @@
 //
 // fp32 kernel: one wave per (query row, head), keys 64 at a time, plain
 // online softmax. It serves the fp32 path only.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace llatte {
@@ -199,12 +201,16 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
     ld_src[i] = key * R + j * 8;
     st_off[i] = key * R + ((2 * j) ^ swz_key<R>(key)) * 4;
   }
+  // Chunk i of tile t. Keys past the end read the last key's row instead
+  // (finite data; their scores are masked to -inf, so P = 0 there): no
+  // branch, and a tile past the last one is a harmless load.
+  auto load_chunk = [&](int t, int i) {
+    const int key = min(t * BN + ld_src[i] / R, nkeys - 1);
+    ld[i] = *(const i32x4*)(Cg + (size_t)key * R + ld_src[i] % R);
+  };
   auto load_tile = [&](int t) {
-    const int k0 = t * BN;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i)
-      ld[i] = (k0 + ld_src[i] / R < nkeys) ? *(const i32x4*)(Cg + (size_t)k0 * R + ld_src[i])
-                                           : i32x4{0, 0, 0, 0};
+    for (int i = 0; i < NLD; ++i) load_chunk(t, i);
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
@@ -310,36 +316,51 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
   constexpr int NSS = 4 * NKS;   // score steps (kb, ks), NEB MFMAs each
   constexpr int NPS = 2 * NRB;   // PV steps (rb, kk), NEB MFMAs each
 
-  // A operand of score step i: rows kb*16.. of the tile, r = 32 ks..
+  // A operand of score step i: rows kb*16.. of the tile, r = 32 ks.. (k
+  // step outermost: an accumulator's next step comes 4 * NEB MFMAs later)
   auto rd_s = [&](const f16* cs, int i) {
-    const f16* rowb = cs + (i / NKS) * 16 * R;
-    const int ks = i % NKS;
+    const f16* rowb = cs + (i % 4) * 16 * R;
+    const int ks = i / 4;
     return cat(*(const f16x4*)&rowb[off_s(2 * ks)], *(const f16x4*)&rowb[off_s(2 * ks + 1)]);
   };
-  // A operand of PV step j: C^T rows rb*16.., keys 32 kk.. (transpose load)
+  // A operand of PV step j: C^T rows rb*16.., keys 32 kk.. (transpose load;
+  // key half outermost: an accumulator's second step comes NRB * NEB MFMAs
+  // after its first)
   auto rd_pv = [&](const f16* cs, int j) {
-    const int rb = j / 2, kk = j % 2;
+    const int rb = j % NRB, kk = j / NRB;
     return cat(lds_read_tr(cs + kk * 32 * R + off_t(rb)),
                lds_read_tr(cs + (kk * 32 + 16) * R + off_t(rb)));
   };
 
   // S^T[key][e] of the 64-key tile in LDS buffer cs; the first k step of
   // each block starts from a zero accumulator
-  auto scores = [&](const f16* cs, f32x4 (&sc)[4][NEB]) {
+  // The global loads of tile tn are spread over the score steps, one chunk
+  // every NSS / NLD steps, so that the waves of the CU do not issue them in
+  // one burst after the barrier.
+  constexpr int kLdEvery = NSS / NLD > 0 ? NSS / NLD : 1;
+  // The accumulators start at -m_run (m0[eb], 0 on an item's first tile), so
+  // the MFMAs produce s - m_run directly.
+  auto scores = [&](const f16* cs, f32x4 (&sc)[4][NEB], int tn, const float (&m0)[NEB]) {
     f16x8 a[NSS];
 #pragma unroll
     for (int i = 0; i < kPre; ++i) a[i] = rd_s(cs, i);
 #pragma unroll
     for (int i = 0; i < NSS; ++i) {
+      if (i % kLdEvery == 0 && i / kLdEvery < NLD) load_chunk(tn, i / kLdEvery);
       if (i + kPre < NSS) a[i + kPre] = rd_s(cs, i + kPre);
-      const int kb = i / NKS, ks = i % NKS;
+      const int kb = i % 4, ks = i / 4;
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb)
-        sc[kb][eb] = mfma_f16(a[i], qf[eb][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sc[kb][eb]);
+        sc[kb][eb] = mfma_f16(a[i], qf[eb][ks],
+                              ks == 0 ? f32x4{-m0[eb], -m0[eb], -m0[eb], -m0[eb]} : sc[kb][eb]);
     }
+#pragma unroll
+    for (int i = NSS / kLdEvery; i < NLD; ++i) load_chunk(tn, i);
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPre, 0);
 #pragma unroll
     for (int i = 0; i < NSS; ++i) {
+      if (i % kLdEvery == 0 && i / kLdEvery < NLD)
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load
       __builtin_amdgcn_sched_group_barrier(0x008, NEB, 0);
       if (i + kPre < NSS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
@@ -350,6 +371,8 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
   // exceeds it by more than kLazy (log2 units): P = exp2(s - m_run) then
   // stays <= 2^kLazy, exact enough in fp16, and the accumulators are
   // rescaled only on those tiles.
+  // The scores arrive shifted by the running max (s - m_run; on the first
+  // tile s itself, m_run then starts at that tile's max).
   auto softmax = [&](int t, f32x4 (&sc)[4][NEB], f16x8 (&pf)[2][NEB]) {
     const bool need_mask = t * BN + BN - 1 > pmin;
 #pragma unroll
@@ -366,20 +389,28 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
       mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sc[2][eb][0], sc[2][eb][1]), fmaxf(sc[2][eb][2], sc[2][eb][3])),
                            fmaxf(fmaxf(sc[3][eb][0], sc[3][eb][1]), fmaxf(sc[3][eb][2], sc[3][eb][3]))));
       mx = max_across_groups(mx);
-      const bool bump = mx > m_run[eb] + kLazy;   // true on the first tile (m_run = -inf)
-      if (__ballot(bump)) {
-        const float m_new = bump ? mx : m_run[eb];
-        const float alpha = fast_exp2(m_run[eb] - m_new);
-        m_run[eb] = m_new;
+      if (t == 0) {
+        // first tile: m_run = its max (the first key is never masked)
+        m_run[eb] = mx;
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) acc_o[rb][eb] *= alpha;
-        acc_l[eb] *= alpha;
+        for (int kb = 0; kb < 4; ++kb) sc[kb][eb] -= mx;
+      } else {
+        const bool bump = mx > kLazy;
+        if (__ballot(bump)) {
+          const float dm = bump ? mx : 0.f;
+          const float alpha = fast_exp2(-dm);
+          m_run[eb] += dm;
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) acc_o[rb][eb] *= alpha;
+          acc_l[eb] *= alpha;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) sc[kb][eb] -= dm;
+        }
       }
-      const float m = m_run[eb];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) sc[kb][eb][v] = fast_exp2(sc[kb][eb][v] - m);
+        for (int v = 0; v < 4; ++v) sc[kb][eb][v] = fast_exp2(sc[kb][eb][v]);
       pf[0][eb] = pack8(sc[0][eb], sc[1][eb]);
       pf[1][eb] = pack8(sc[2][eb], sc[3][eb]);
     }
@@ -396,7 +427,7 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
 #pragma unroll
     for (int j = 0; j < NPS; ++j) {
       if (j + kPre < NPS) a[j + kPre] = rd_pv(cs, j + kPre);
-      const int rb = j / 2, kk = j % 2;
+      const int rb = j % NRB, kk = j / NRB;
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) acc_o[rb][eb] = mfma_f16(a[j], pf[kk][eb], acc_o[rb][eb]);
     }
@@ -413,23 +444,33 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
 
   // Double-buffered tiles: the next tile's global loads are in flight while
   // this one is computed; one barrier per tile.
+  // (two iterations per loop trip, so that each LDS buffer's address is a
+  // constant folded into the instructions' offsets)
   f32x4 st[4][NEB];
   store_tile(0);
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
-    const f16* cs = &Cs[cur][0];
-    if (t + 1 < ntiles) load_tile(t + 1);
-    scores(cs, st);
+  auto iter = [&](int t, auto cur) {
+    constexpr int CUR = decltype(cur)::value;
+    const f16* cs = &Cs[CUR][0];
+    float m0[NEB];
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb) m0[eb] = t == 0 ? 0.f : m_run[eb];
+    scores(cs, st, t + 1, m0);
     f16x8 pa[kPre];
 #pragma unroll
     for (int j = 0; j < kPre; ++j) pa[j] = rd_pv(cs, j);
     f16x8 pf[2][NEB];
     softmax(t, st, pf);
     pv(cs, pa, pf);
-    if (t + 1 < ntiles) store_tile(cur ^ 1);
+    if (t + 1 < ntiles) store_tile(CUR ^ 1);
     __syncthreads();
+  };
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    iter(t, std::integral_constant<int, 0>{});
+    iter(t + 1, std::integral_constant<int, 1>{});
   }
+  if (t < ntiles) iter(t, std::integral_constant<int, 0>{});
 
   if constexpr (FUSED) {
     // o^T[k][e] = sum_r W_uv^T[head][k][r] * o_lat^T[r][e]: the head's W_uv^T

@@ -414,9 +414,11 @@ static hipError_t pack_layer(const Shapes& S, const llatte_layer_weights* L,
     if ((err = transpose(L->W_dq, S.d, S.rq, S.rq, 0, T.Wdq, S.d, 0, 1, k, k, s, g1))) return err;
     if ((err = hipMemcpyAsync(T.g_q, L->g_q, S.rq * 4, hipMemcpyDeviceToDevice, s))) return err;
   }
-  // per head: W_uv[:, j*dk:(j+1)*dk] ([r, dk]) -> [dk, r]
+  // per head: W_uv[:, j*dk:(j+1)*dk] ([r, dk]) -> [dk, r]; on the bf16 path
+  // the r columns in the attention kernel's stored order
   if ((err = transpose(L->W_uv, S.r, S.dk, S.hd, S.dk, T.Wuv, S.r,
-                       (long long)S.dk * S.r, S.h, k, S.bf16 ? K_F16 : K_F32, s)))
+                       (long long)S.dk * S.r, S.h, k, S.bf16 ? K_F16 : K_F32, s, nullptr,
+                       S.bf16)))
     return err;
   if ((err = transpose(L->W_o, S.hd, S.d, S.d, 0, T.Wo, S.hd, 0, 1, k, k, s))) return err;
   if ((err = transpose(L->W1, S.d, S.dff, S.dff, 0, T.W1, S.d, 0, 1, k, k, s, g2))) return err;

@@ -116,18 +116,20 @@ __device__ __forceinline__ f16x4 lds_read_tr(const f16* p) {
   return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(q));
 }
 
-// XOR mask of the 8-byte chunks of tile row `key` (physical = logical ^ mask).
+// XOR mask of the 8-byte chunks of tile row `key` (physical = stored ^ mask).
+// Even, so the two halves of a score operand (stored chunks 2g, 2g+1) stay
+// one aligned 16-byte read; for the 16 keys of a 16-lane score read the
+// mask / 2 takes 16 distinct values (rows are a whole number of 256-byte
+// bank windows), and for the 8 consecutive keys of a 32-lane transposed
+// read mask / 4 takes distinct values (r = 64: per key parity, rows being
+// half a window).
 template <int R>
 __device__ __forceinline__ int swz_key(int key) {
   const int k = key & 15;
   if constexpr (R == 64) {
-    // masks for keys 0..15, one nibble each (key 0 in the low nibble):
-    // 7 2 2 7 15 11 8 14 4 9 13 0 11 13 0 4 (found by exhaustive checking of
-    // the three access patterns; rows are half a bank window wide)
-    constexpr unsigned long long tab = 0x40db0d94e8bf7227ull;
-    return (int)((tab >> (4 * k)) & 15);
+    return 4 * ((k >> 1) & 3) + 2 * ((k >> 3) & 1);
   } else {
-    return 4 * (k & 7) + 2 * (k >> 3) + (k & 1);
+    return 4 * (k & 7) + 2 * (k >> 3);
   }
 }
 
@@ -188,18 +190,20 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) pmin = min(pmin, __shfl_xor(pmin, o, 64));
 
-  // C tile staging: chunk idx covers key idx / (R/8), r 8*(idx % (R/8)) .. +7.
-  // Global offsets and swizzled LDS offsets (in halves) are fixed per thread.
-  // (the second 8-byte chunk of a pair sits at the first's offset XOR 4
-  // halves: the mask flips at most bit 0 of the chunk index)
+  // C tile staging: chunk idx covers key idx / (R/8), r 8*(idx % (R/8)) .. +7,
+  // i.e. the 4-element r-chunks 2j and 2j+1, stored at attn_chunk_slot() of
+  // their 32-element block and XOR-swizzled. Global offsets and LDS offsets
+  // (in halves) are fixed per thread.
   i32x4 ld[NLD];
-  int ld_src[NLD], st_off[NLD];
+  int ld_src[NLD], st_off[NLD], st_off2[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
     const int idx = tid + i * kAttnThreads;
     const int key = idx / (R / 8), j = idx % (R / 8);
+    const int blk = 8 * (j / 4), kv = swz_key<R>(key);
     ld_src[i] = key * R + j * 8;
-    st_off[i] = key * R + ((2 * j) ^ swz_key<R>(key)) * 4;
+    st_off[i] = key * R + ((blk + attn_chunk_slot(2 * (j % 4))) ^ kv) * 4;
+    st_off2[i] = key * R + ((blk + attn_chunk_slot(2 * (j % 4) + 1)) ^ kv) * 4;
   }
   // Chunk i of tile t. Keys past the end read the last key's row instead
   // (finite data; their scores are masked to -inf, so P = 0 there): no
@@ -217,7 +221,7 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
     for (int i = 0; i < NLD; ++i) {
       const f16x8 v = to_f16x8(ld[i], C_BF16);
       *(f16x4*)&Cs[buf][st_off[i]] = f16x4{v[0], v[1], v[2], v[3]};
-      *(f16x4*)&Cs[buf][st_off[i] ^ 4] = f16x4{v[4], v[5], v[6], v[7]};
+      *(f16x4*)&Cs[buf][st_off2[i]] = f16x4{v[4], v[5], v[6], v[7]};
     }
   };
 
@@ -276,17 +280,19 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
     }
   }
 
-  // S^T operand reads: row kb*16 + l16, chunk c = 4x + g with x = 2*ks (+1);
-  // the mask depends on l16 only and is below 32, so chunks 32 apart differ
-  // by a constant: 8 lane-constant offsets cover every x.
-  constexpr int NOS = 2 * NKS < 8 ? 2 * NKS : 8;
+  // S^T operand reads: row kb*16 + l16; lane group g takes the r-chunks g
+  // and 4 + g of k step ks, stored side by side in chunks 2g, 2g + 1 of the
+  // step's 32-element block: one 16-byte read. The mask depends on l16 only
+  // and is below 32, so blocks 32 elements apart differ by a constant: four
+  // lane-constant offsets cover every k step.
+  constexpr int NOS = NKS < 4 ? NKS : 4;
   int offS[NOS];
   {
     const int kv = swz_key<R>(l16);
 #pragma unroll
-    for (int x = 0; x < NOS; ++x) offS[x] = l16 * R + ((x * 4 + g) ^ kv) * 4;
+    for (int x = 0; x < NOS; ++x) offS[x] = l16 * R + ((8 * x + 2 * g) ^ kv) * 4;
   }
-  auto off_s = [&](int x) { return offS[x % 8] + (x / 8) * 128; };
+  auto off_s = [&](int ks) { return offS[ks % 4] + (ks / 4) * 128; };
   // transpose reads: rows kk*32 (+16) + 4g + (l16 >> 2), chunk rb*4 + (l16 & 3);
   // with the mask kt below 32, (4rb + j) ^ kt = 4 (rb ^ (kt >> 2)) + (j ^ (kt & 3))
   const int tk = 4 * g + (l16 >> 2);
@@ -321,7 +327,7 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
   auto rd_s = [&](const f16* cs, int i) {
     const f16* rowb = cs + (i % 4) * 16 * R;
     const int ks = i / 4;
-    return cat(*(const f16x4*)&rowb[off_s(2 * ks)], *(const f16x4*)&rowb[off_s(2 * ks + 1)]);
+    return *(const f16x8*)&rowb[off_s(ks)];
   };
   // A operand of PV step j: C^T rows rb*16.., keys 32 kk.. (transpose load;
   // key half outermost: an accumulator's second step comes NRB * NEB MFMAs
@@ -515,9 +521,12 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
       if (!valid[eb]) continue;
       const float inv = 1.f / acc_l[eb][0];
       const size_t orow = (size_t)qrow[eb] * p.h + head[eb];
-      float* op = (float*)p.out + orow * R + g * 4;
+      float* op = (float*)p.out + orow * R;
+      // O^T rows come in stored order: rows 16 rb + 4g .. +3 hold the chunk
+      // attn_slot_chunk(4 (rb % 2) + g) of the 32-element block rb / 2
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) *(f32x4*)(op + rb * 16) = acc_o[rb][eb] * inv;
+      for (int rb = 0; rb < NRB; ++rb)
+        *(f32x4*)(op + 32 * (rb / 2) + 4 * attn_slot_chunk(4 * (rb % 2) + g)) = acc_o[rb][eb] * inv;
       if (p.lse && g == 0) p.lse[orow] = (m_run[eb] + log2f(acc_l[eb][0])) * kLn2;
     }
   }

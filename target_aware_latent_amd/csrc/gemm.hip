@@ -647,7 +647,7 @@ int gemm_ss_slots(const GemmParams& p, bool is_bf16) {
 hipError_t gemm(const GemmParams& p, bool is_bf16, hipStream_t s) {
   if (p.M_cap <= 0 || p.N <= 0) return hipSuccess;
   switch (select_tile(p, is_bf16)) {
-    case T64x64: return launch_gemm<bf16, 64, 64, 32, 32, 4>(p, s);
+    case T64x64: return launch_gemm<bf16, 64, 64, 32, 32, 4, 2>(p, s);
     case T128x64: return launch_gemm<bf16, 128, 64, 64, 32, 4>(p, s);
     case T128x128: return launch_gemm<bf16, 128, 128, 32, 64, 8>(p, s);
     case T128x256: return launch_gemm<bf16, 128, 256, 64, 64, 8>(p, s);

@@ -97,11 +97,13 @@ hipError_t norm_rows(RowSrc src, int rows_cap, const int* rows_dev,
 // dst [cols, rows] = transpose(src [rows, cols]) for a batch of `batch`
 // matrices laid out with the given element strides; src has kind s_kind,
 // dst kind d_kind (bf16 -> f16 and same-kind copies).
-// row_scale (optional, float [src_rows]) multiplies source row i first.
+// row_scale (optional, float [src_rows]) multiplies source row i first;
+// slot_rows places source row i at dst column attn_r_slot(i) (src_rows a
+// multiple of 32).
 hipError_t transpose(const void* src, int src_rows, int src_cols, int ld_src,
                      long long s_src, void* dst, int ld_dst, long long s_dst,
                      int batch, int s_kind, int d_kind, hipStream_t s,
-                     const float* row_scale = nullptr);
+                     const float* row_scale = nullptr, bool slot_rows = false);
 
 // xc (dtype) [B*n_q, d + d_c]: row u*n_q + j = [cand[u*n_q+j] ; ctx[u]].
 hipError_t concat_queries(const float* cand, const float* ctx, int B, int n_q,
@@ -218,6 +220,19 @@ struct AttnParams {
   int M_cap;
   const int* M_dev;
 };
+
+// LDS layout of the latent rows in the MFMA attention kernel: within each
+// 32-element block of r, the 4-element chunk q (r = 4q .. 4q+3) is stored at
+// chunk position slot(q) = 2q (q < 4) or 2(q-4) + 1 (q >= 4), so that chunks
+// g and 4 + g (one lane group's k values of a 32-wide MFMA step) sit side by
+// side. The kernel's output rows come in this stored order; W_uv^T is packed
+// with its r columns in the same order.
+__host__ __device__ constexpr int attn_chunk_slot(int q) { return q < 4 ? 2 * q : 2 * (q - 4) + 1; }
+__host__ __device__ constexpr int attn_slot_chunk(int c) { return (c & 1) ? 4 + (c >> 1) : c >> 1; }
+// stored position of latent index r (r of any 32-element block)
+__host__ __device__ constexpr int attn_r_slot(int r) {
+  return (r & ~31) + 4 * attn_chunk_slot((r & 31) >> 2) + (r & 3);
+}
 
 // Query rows per work item for the bf16 kernel at these sizes (0 if the
 // shape is not supported by the MFMA kernel).

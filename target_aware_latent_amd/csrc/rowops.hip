@@ -82,7 +82,7 @@ hipError_t norm_rows(RowSrc src, int rows_cap, const int* rows_dev,
 template <typename S, typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(
     const S* src, int rows, int cols, int ld_src, long long s_src, T* dst,
-    int ld_dst, long long s_dst, const float* row_scale) {
+    int ld_dst, long long s_dst, const float* row_scale, bool slot_rows) {
   __shared__ T tile[32][33];
   src += (size_t)blockIdx.z * s_src;
   dst += (size_t)blockIdx.z * s_dst;
@@ -96,29 +96,30 @@ __global__ __launch_bounds__(256) void transpose_kernel(
   __syncthreads();
   for (int i = ty; i < 32; i += 8) {
     int c = c0 + i, r = r0 + tx;
-    if (r < rows && c < cols) dst[(size_t)c * ld_dst + r] = tile[tx][i];
+    if (r < rows && c < cols) dst[(size_t)c * ld_dst + (slot_rows ? attn_r_slot(r) : r)] = tile[tx][i];
   }
 }
 
 hipError_t transpose(const void* src, int rows, int cols, int ld_src,
                      long long s_src, void* dst, int ld_dst, long long s_dst,
                      int batch, int s_kind, int d_kind, hipStream_t s,
-                     const float* row_scale) {
+                     const float* row_scale, bool slot_rows) {
   if (rows <= 0 || cols <= 0 || batch <= 0) return hipSuccess;
+  if (slot_rows && rows % 32) return hipErrorInvalidValue;
   dim3 grid((cols + 31) / 32, (rows + 31) / 32, batch);
   timing_begin("transpose", s);
   if (s_kind == K_BF16 && d_kind == K_BF16)
     hipLaunchKernelGGL((transpose_kernel<bf16, bf16>), grid, dim3(256), 0, s,
                        (const bf16*)src, rows, cols, ld_src, s_src, (bf16*)dst,
-                       ld_dst, s_dst, row_scale);
+                       ld_dst, s_dst, row_scale, slot_rows);
   else if (s_kind == K_BF16 && d_kind == K_F16)
     hipLaunchKernelGGL((transpose_kernel<bf16, f16>), grid, dim3(256), 0, s,
                        (const bf16*)src, rows, cols, ld_src, s_src, (f16*)dst,
-                       ld_dst, s_dst, row_scale);
+                       ld_dst, s_dst, row_scale, slot_rows);
   else if (s_kind == K_F32 && d_kind == K_F32)
     hipLaunchKernelGGL((transpose_kernel<float, float>), grid, dim3(256), 0, s,
                        (const float*)src, rows, cols, ld_src, s_src,
-                       (float*)dst, ld_dst, s_dst, row_scale);
+                       (float*)dst, ld_dst, s_dst, row_scale, slot_rows);
   else
     return hipErrorInvalidValue;
   timing_end(s);

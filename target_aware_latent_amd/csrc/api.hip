@@ -677,6 +677,7 @@ static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
     g.epi = EPI_GELU;
     g.C = w.F;
     g.ldc = S.dff;
+    g.nt = true;  // the layer's largest tensor (M x d_ff): streamed, it keeps W1 and H2 cached
     if ((err = gemm(g, b, s))) return err;
   }
   // 10. out = R1 + F W2 (post: then RMSNorm g2)

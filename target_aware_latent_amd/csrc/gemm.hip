@@ -83,6 +83,18 @@ template <>
 __device__ __forceinline__ void store4<bf16>(bf16* p, float a, float b, float c, float d) {
   *(bf16x4*)p = bf16x4{to_bf16(a), to_bf16(b), to_bf16(c), to_bf16(d)};
 }
+// The same with the non-temporal hint (streamed to memory, not kept in the
+// caches); NT selects it at compile time.
+template <bool NT, typename T>
+__device__ __forceinline__ void store4h(T* p, float a, float b, float c, float d) {
+  if constexpr (!NT) {
+    store4<T>(p, a, b, c, d);
+  } else if constexpr (__is_same(T, bf16)) {
+    __builtin_nontemporal_store(bf16x4{to_bf16(a), to_bf16(b), to_bf16(c), to_bf16(d)}, (bf16x4*)p);
+  } else {
+    __builtin_nontemporal_store(f32x4{a, b, c, d}, (f32x4*)p);
+  }
+}
 template <typename T> __device__ __forceinline__ f32x4 load4(const T* p);
 template <> __device__ __forceinline__ f32x4 load4<float>(const float* p) {
   return *(const f32x4*)p;
@@ -98,7 +110,7 @@ template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
 // with LPR lanes per row, each lane holding chunks q and q + LPR of its row:
 // every 16-lane group then reads and writes whole 256-byte runs of a row,
 // and each row's RMSNorm sums reduce within its lane group.
-template <typename T, int BM, int BN, int WM, int WN, int NW>
+template <typename T, int BM, int BN, int WM, int WN, int NW, bool NTS>
 __device__ __forceinline__ void epilogue_rowmajor(const GemmParams p, const f32x4 (&acc)[WM / 16][WN / 16],
                                                   float* Cs, const float* rs_lds,
                                                   const int (&rrow)[BM / (64 * NW / (BN / 8))],
@@ -153,7 +165,7 @@ __device__ __forceinline__ void epilogue_rowmajor(const GemmParams p, const f32x
     case EPI_STORE:
       each([&](int ps, int h, int m, int n) {
         const f32x4 x = v[ps][h] * p.alpha;
-        store4<T>((T*)p.C + coff(m, n), x[0], x[1], x[2], x[3]);
+        store4h<NTS, T>((T*)p.C + coff(m, n), x[0], x[1], x[2], x[3]);
       });
       break;
     case EPI_STORE_F32:
@@ -165,8 +177,8 @@ __device__ __forceinline__ void epilogue_rowmajor(const GemmParams p, const f32x
     case EPI_GELU:
       each([&](int ps, int h, int m, int n) {
         const f32x4 x = v[ps][h];
-        store4<T>((T*)p.C + coff(m, n), gelu_t<T>(x[0]), gelu_t<T>(x[1]), gelu_t<T>(x[2]),
-                  gelu_t<T>(x[3]));
+        store4h<NTS, T>((T*)p.C + coff(m, n), gelu_t<T>(x[0]), gelu_t<T>(x[1]), gelu_t<T>(x[2]),
+                       gelu_t<T>(x[3]));
       });
       break;
     case EPI_RESID_F32: {
@@ -177,9 +189,9 @@ __device__ __forceinline__ void epilogue_rowmajor(const GemmParams p, const f32x
       for (int ps = 0; ps < NPASS; ++ps) ssp[ps] = 0.f;
       each([&](int ps, int h, int m, int n) {
         const f32x4 x = v[ps][h] + r[ps][h];
-        store4<float>((float*)p.C + coff(m, n), x[0], x[1], x[2], x[3]);
+        store4h<NTS, float>((float*)p.C + coff(m, n), x[0], x[1], x[2], x[3]);
         if (p.cast_out)
-          store4<T>((T*)p.cast_out + (size_t)m * p.ld_cast + n, x[0], x[1], x[2], x[3]);
+          store4h<NTS, T>((T*)p.cast_out + (size_t)m * p.ld_cast + n, x[0], x[1], x[2], x[3]);
         ssp[ps] += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
       });
       if (p.ss_out) {
@@ -444,14 +456,14 @@ __global__ __launch_bounds__(64 * NW, (gemm_min_waves<BN, NW>())) void gemm_kern
   }
   if (kt < nk) step(kt, S0{});
 
-  // GELU keeps the direct epilogue: its VALU work overlaps the other
-  // resident workgroup's main loop better without the LDS round trip.
   if constexpr (kShuffle) {
-    if (p.epi != EPI_GELU) {
-      epilogue_rowmajor<T, BM, BN, WM, WN, NW>(p, acc, (float*)smem, rs_lds, rrow, m0, n0,
-                                               M, wm0, wn0, lane, tid);
-      return;
-    }
+    if (p.nt)
+      epilogue_rowmajor<T, BM, BN, WM, WN, NW, true>(p, acc, (float*)smem, rs_lds, rrow, m0, n0,
+                                                     M, wm0, wn0, lane, tid);
+    else
+      epilogue_rowmajor<T, BM, BN, WM, WN, NW, false>(p, acc, (float*)smem, rs_lds, rrow, m0, n0,
+                                                      M, wm0, wn0, lane, tid);
+    return;
   }
   // Direct epilogue (tiles whose fp32 output does not fit the LDS block):
   // lane holds C[m][n .. n+3] of each 16x16 block.

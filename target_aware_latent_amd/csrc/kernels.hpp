@@ -77,6 +77,10 @@ struct GemmParams {
   const float* gain = nullptr;  // EPI_ROWNORM
   float eps = 0.f;
   int out_kind = K_BF16;
+  // Non-temporal output stores (EPI_STORE, EPI_GELU, and the float result
+  // and cast copy of EPI_RESID_F32): a large output streams to HBM without
+  // displacing the operands the tiles still read from the caches.
+  bool nt = false;
 };
 
 // Partial sums of squares per row that an EPI_RESID_F32 launch with these

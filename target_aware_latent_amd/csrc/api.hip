@@ -634,6 +634,7 @@ static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
   // 7. R1 = R[qmap] + o W_o
   {
     GemmParams g = gemm_base("gemm_out");
+    g.nt = true;  // the fp32 result is next read by the FFN epilogue
     g.A = w.o;
     g.lda = S.hd;
     g.B = L.Wo;
@@ -683,6 +684,7 @@ static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
   // 10. out = R1 + F W2 (post: then RMSNorm g2)
   {
     GemmParams g = gemm_base("gemm_ffn2");
+    g.nt = true;  // the fp32 result is next read as a residual, much later
     g.A = w.F;
     g.lda = S.dff;
     g.B = L.W2;

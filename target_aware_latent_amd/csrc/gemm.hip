@@ -191,7 +191,7 @@ __device__ __forceinline__ void epilogue_rowmajor(const GemmParams p, const f32x
         const f32x4 x = v[ps][h] + r[ps][h];
         store4h<NTS, float>((float*)p.C + coff(m, n), x[0], x[1], x[2], x[3]);
         if (p.cast_out)
-          store4h<NTS, T>((T*)p.cast_out + (size_t)m * p.ld_cast + n, x[0], x[1], x[2], x[3]);
+          store4<T>((T*)p.cast_out + (size_t)m * p.ld_cast + n, x[0], x[1], x[2], x[3]);
         ssp[ps] += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
       });
       if (p.ss_out) {

@@ -78,8 +78,9 @@ struct GemmParams {
   float eps = 0.f;
   int out_kind = K_BF16;
   // Non-temporal output stores (EPI_STORE, EPI_GELU, and the float result
-  // and cast copy of EPI_RESID_F32): a large output streams to HBM without
-  // displacing the operands the tiles still read from the caches.
+  // of EPI_RESID_F32; its cast copy, read by the next GEMM, stays cached): a
+  // large output streams to HBM without displacing the operands the tiles
+  // still read from the caches.
   bool nt = false;
 };
 

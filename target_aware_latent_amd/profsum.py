@@ -7,6 +7,12 @@
 
 `stats` prints the per-kernel table of a `--kernel-trace --stats` run.
 
+`counters` sums the SQ counters of `--pmc` runs per kernel and prints the
+derived ratios: MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES over the SIMD-cycles of
+the kernel; GRBM_GUI_ACTIVE is summed over the 8 XCDs, 1024 SIMDs in all),
+LDS bank-conflict cycles over LDS active cycles, and VALU instructions per
+MFMA instruction.
+
 `traffic` turns two `--pmc` runs (FETCH_SIZE, then WRITE_SIZE, in KiB per
 dispatch) of a program that also copied 256 MiB device to device
 (bench.py --calibrate-copy) into HBM bytes per launch of one kernel: each
@@ -60,6 +66,36 @@ def stats(path):
     return "\n".join(out)
 
 
+XCDS, SIMDS = 8, 1024   # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+
+
+def counters(paths, kernels):
+    """Per kernel (name filter): counter sums over its dispatches and ratios."""
+    tot = {k: collections.defaultdict(float) for k in kernels}
+    disp = {k: set() for k in kernels}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            for k in kernels:
+                if k in r["Kernel_Name"]:
+                    tot[k][r["Counter_Name"]] += float(r["Counter_Value"])
+                    disp[k].add((path, r["Dispatch_Id"]))
+    out = []
+    for k in kernels:
+        t = tot[k]
+        per_run = collections.Counter(path for path, _ in disp[k])
+        line = {"kernel": k, "dispatches": max(per_run.values(), default=0)}
+        if t.get("GRBM_GUI_ACTIVE") and "SQ_VALU_MFMA_BUSY_CYCLES" in t:
+            line["mfma_busy"] = round(t["SQ_VALU_MFMA_BUSY_CYCLES"] /
+                                      (t["GRBM_GUI_ACTIVE"] / XCDS * SIMDS), 4)
+        if t.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in t:
+            line["lds_conflict_cycles"] = round(t["SQ_LDS_BANK_CONFLICT"] / t["SQ_LDS_IDX_ACTIVE"], 4)
+        if t.get("SQ_INSTS_MFMA") and "SQ_INSTS_VALU" in t:
+            line["valu_per_mfma"] = round(t["SQ_INSTS_VALU"] / t["SQ_INSTS_MFMA"], 3)
+        line["sums"] = {c: v for c, v in sorted(t.items())}
+        out.append(line)
+    return out
+
+
 def _dispatches(path, counter):
     per = collections.defaultdict(dict)
     for r in csv.DictReader(open(path)):
@@ -103,6 +139,9 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     a = sub.add_parser("stats")
     a.add_argument("csv")
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--kernel", action="append", required=True)
     b = sub.add_parser("traffic")
     b.add_argument("--fetch", required=True)
     b.add_argument("--write", required=True)
@@ -113,6 +152,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         print(stats(args.csv))
+    elif args.cmd == "counters":
+        for line in counters(args.csv, args.kernel):
+            print(json.dumps(line))
     else:
         rec = traffic(args.fetch, args.write, args.kernel, args.label, args.source)
         text = json.dumps(rec)

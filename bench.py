@@ -1,6 +1,7 @@
 """Throughput of the LLaTTE target-aware MLA forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3]
+    python bench.py --workload actions     (the action tokenization)
 
 One step is one llatte_mla_forward over one batch of the workload (all
 layers, the pyramid, the readout), inputs and weights already resident in
@@ -154,6 +155,102 @@ def cpu_baseline(prob, budget_s=12.0):
                       f"oracle (non-absorbed definition), {dt:.1f} s"}
 
 
+ACTIONS_METRIC = "actions/sec + TFLOP/s (% MFMA bf16 peak), action tokenization, 1 GPU"
+ACTIONS_TEXT = ("a_c3: action tokenization, 64 users x 1600 actions, fields type 32 / item "
+                "128 (1M-row Zipf table) / surface 32 / time 32 / meta 16->32, MLP_act "
+                "256-1024-512, timestamp encoding on 64 dims")
+
+
+def action_kernel_cost(cfg, n):
+    """Per kernel label: (FLOPs, algorithmic HBM bytes) of one call."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    tables = cfg.d_type + cfg.d_item + cfg.d_surf + cfg.d_time
+    return {
+        "action_concat": (2 * n * cfg.d_meta * cfg.d_meta_emb,
+                          n * (5 * 4 + cfg.d_meta * es + tables * es + cfg.d_in * es + 4)),
+        "gemm_act_a": (2 * n * cfg.d_in * cfg.d_hidden, None),
+        "gemm_act_b": (2 * n * cfg.d_hidden * cfg.d, None),
+    }
+
+
+def bench_actions(args):
+    import torch
+    from oracle import actions as A
+    from synth.actions import generate_actions, get_action_config
+    from target_aware_latent_amd import llatte as C
+    from target_aware_latent_amd.actions import DeviceActions
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    cfg = get_action_config("a_c3")
+    p = generate_actions(cfg, 0)
+    W, I = p["weights"], p["inputs"]
+    n = len(I["tau"])
+    dev = DeviceActions(cfg, W)
+    X = dev.inputs(I)
+    out = torch.empty((n, cfg.d), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    step = lambda: dev.tokenize(X, out=out, stream=stream)
+    for _ in range(args.warmup):
+        step()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    F = A.action_flops(n, cfg.d_meta, cfg.d_meta_emb, cfg.d_in, cfg.d_hidden, cfg.d)
+    tflops = F / (ms_step / 1e3) / 1e12
+    C.llatte_kernel_timing_reset()
+    C.llatte_kernel_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = C.llatte_kernel_timing_read()
+    C.llatte_kernel_timing_enable(False)
+    cost = action_kernel_cost(cfg, n)
+    kernels = {}
+    for name, (cnt, tot) in kt.items():
+        e = {"launches_per_step": cnt / args.steps, "ms_per_step": tot / args.steps}
+        if name in cost:
+            fl, by = cost[name]
+            e["tflops"] = fl / (tot / cnt / 1e3) / 1e12
+            if by:
+                e["gb_per_s"] = by / (tot / cnt / 1e3) / 1e9
+        kernels[name] = e
+    dom = max((k for k in kt if k.startswith("gemm_act")), key=lambda k: kt[k][1])
+    cnt, tot = kt[dom]
+    achieved = cost[dom][0] / (tot / cnt / 1e3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": cost[dom][0], "avg_launch_ms": round(tot / cnt, 4)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        rows = np.arange(0, n, 4)           # every 4th action, all users
+        t0 = time.perf_counter()
+        A.action_tokens(W, I["t_req"], I["tau"], I["offsets"], I["type_id"], I["item_id"],
+                        I["surf_id"], I["meta"], cfg.n_buckets, cfg.d_enc,
+                        dtype=np.float32, rows=rows)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(len(rows) / dt, 1), "unit": "actions/s",
+               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"{len(rows)} of {n} actions (every 4th), fp32 oracle, {dt:.1f} s"}
+    rec = {
+        "metric": ACTIONS_METRIC, "value": round(n / (ms_step / 1e3), 1), "unit": "actions/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded ids, Zipf items, exponential action gaps, N(0,1) tables)",
+        "config": {"workload": ACTIONS_TEXT, "global_batch": cfg.B, "seq_len": cfg.L,
+                   "parallelism": "single GPU"},
+        "tflops": round(tflops, 2), "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+    }
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,12 +267,18 @@ def main():
                     help="profile summary whose RECORD line holds the measured "
                          "HBM bytes per launch of the dominant kernel (written "
                          "by target_aware_latent_amd.profsum traffic)")
+    ap.add_argument("--workload", default="stack", choices=["stack", "actions"],
+                    help="stack: the MLA forward (default); actions: the action "
+                         "tokenization that builds the history tokens")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
               "path (users shard across GPUs with no exchange; see the design "
               "notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "actions":
+        bench_actions(args)
+        return
 
     import torch
     import synth

@@ -309,6 +309,62 @@ size_t llatte_token_embed_workspace_size(int32_t d, int32_t d_sem,
                                          int32_t dt);
 
 /* ------------------------------------------------------------------------
+ * llatte_action_tokenize -- one d-wide token per user action ([LLaTTE]
+ * Appendix A.2, Sequence Module item 1): each action (timestamp tau, type,
+ * item, surface, meta) is embedded per field, the five embeddings pass
+ * through MLP_act, and additive timestamp encodings go on a subset of the
+ * hidden dimensions:
+ *   age   = max(0, t_req[u] - tau[i])               (u = the row's user)
+ *   U[i]  = [E_type[type_i] | E_item[item_i] | E_surf[surf_i]
+ *            | E_time[min(floor(log2(1 + age)), n_buckets - 1)]
+ *            | meta[i] W_meta]                        (d_in wide)
+ *   out[i] = GELU(U[i] W_a) W_b + enc(age)            (exact-erf GELU)
+ *   enc(age)[2j], [2j+1] = sin, cos of (age / 3600) 10000^(-2j / d_enc)
+ *   for 2j < d_enc; 0 beyond.
+ * The page fixes none of the field embeddings, MLP_act or the encoding;
+ * these are the readings the library implements (one hidden layer, no
+ * biases, log-bucketed age table, linear meta embedding, sinusoidal
+ * encoding of the age in hours on the leading d_enc dimensions).
+ *
+ *   offsets [B+1] int32 (exclusive scan; user u owns rows offsets[u] ..
+ *   offsets[u+1]-1, n = offsets[B]); t_req [B] int32 request time (s);
+ *   tau, type_id, item_id, surf_id [n] int32; meta [n, d_meta] dtype.
+ *   Tables E_type [V_type, d_type], E_item [V_item, d_item],
+ *   E_surf [V_surf, d_surf], E_time [n_buckets, d_time], W_meta
+ *   [d_meta, d_meta_emb], W_a [d_in, d_hidden], W_b [d_hidden, d], all in
+ *   dtype, d_in = d_type + d_item + d_surf + d_time + d_meta_emb.
+ *   out [n, d] float32.
+ *   Widths: d_type, d_item, d_surf, d_time, d_meta_emb, d_hidden, d and
+ *   d_meta are multiples of 8 (BF16) or 4 (F32); d_enc is even, <= d.
+ *   Ids outside their table are clamped into it (no out-of-bounds read);
+ *   timestamps after the request give age 0. n = 0 is valid and enqueues
+ *   nothing (the per-row pointers may then be NULL).
+ *   workspace >= llatte_action_tokenize_workspace_size(desc, n) bytes.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t d, d_hidden, d_enc;
+  int32_t d_type, d_item, d_surf, d_time, d_meta, d_meta_emb;
+  int32_t V_type, V_item, V_surf, n_buckets;
+  int32_t dtype; /* LLATTE_F32 or LLATTE_BF16 */
+} llatte_action_desc;
+
+typedef struct {
+  const void *E_type, *E_item, *E_surf, *E_time, *W_meta, *W_a, *W_b;
+} llatte_action_weights;
+
+llatte_status llatte_action_tokenize(const llatte_action_desc* desc /* host */,
+                                     const llatte_action_weights* w /* host */,
+                                     const int32_t* offsets, int32_t B, int32_t n,
+                                     const int32_t* t_req, const int32_t* tau,
+                                     const int32_t* type_id, const int32_t* item_id,
+                                     const int32_t* surf_id, const void* meta,
+                                     float* out, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+size_t llatte_action_tokenize_workspace_size(const llatte_action_desc* desc,
+                                             int32_t n);
+
+/* ------------------------------------------------------------------------
  * Diagnostics.
  *   llatte_last_error   message of the last non-OK status on this thread
  *   llatte_version      library version (major*10000 + minor*100 + patch)

@@ -1070,4 +1070,143 @@ llatte_status llatte_token_embed(const void* table, int32_t V,
   return LLATTE_OK;
 }
 
+
+// ---------------------------------------------------------------- actions
+// Workspace: U [n, d_in], H [n, d_hidden], age [n], W_a^T, W_b^T (the
+// products' K-contiguous operands), each 256-byte aligned.
+struct ActionWs {
+  size_t U, H, age, WaT, WbT, total;
+};
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+static ActionWs action_ws(const llatte_action_desc* a, int32_t n) {
+  const size_t es = a->dtype == LLATTE_BF16 ? 2 : 4;
+  const size_t d_in = (size_t)a->d_type + a->d_item + a->d_surf + a->d_time + a->d_meta_emb;
+  ActionWs w;
+  w.U = 0;
+  w.H = w.U + al256((size_t)n * d_in * es);
+  w.age = w.H + al256((size_t)n * a->d_hidden * es);
+  w.WaT = w.age + al256((size_t)n * 4);
+  w.WbT = w.WaT + al256((size_t)a->d_hidden * d_in * es);
+  w.total = w.WbT + al256((size_t)a->d * a->d_hidden * es) + 256;
+  return w;
+}
+
+static llatte_status check_action_desc(const llatte_action_desc* a) {
+  if (!a) return fail(LLATTE_ERR_INVALID_ARG, "NULL descriptor");
+  if (a->dtype != LLATTE_F32 && a->dtype != LLATTE_BF16)
+    return fail(LLATTE_ERR_UNSUPPORTED, "dtype %d", a->dtype);
+  const int al = a->dtype == LLATTE_BF16 ? 8 : 4;
+  const int32_t widths[] = {a->d, a->d_hidden, a->d_type, a->d_item, a->d_surf,
+                            a->d_time, a->d_meta, a->d_meta_emb};
+  for (int32_t v : widths) {
+    if (v < 1 || v > (1 << 16)) return fail(LLATTE_ERR_INVALID_ARG, "field width %d out of range", v);
+    if (v % al) return fail(LLATTE_ERR_UNSUPPORTED, "field widths must be multiples of %d", al);
+  }
+  if (a->d_enc < 0 || a->d_enc > a->d || a->d_enc % 2)
+    return fail(LLATTE_ERR_INVALID_ARG, "d_enc must be even and within [0, d]");
+  if (a->V_type < 1 || a->V_item < 1 || a->V_surf < 1 || a->n_buckets < 1 || a->n_buckets > 64)
+    return fail(LLATTE_ERR_INVALID_ARG, "table sizes must be >= 1 (n_buckets <= 64)");
+  return LLATTE_OK;
+}
+
+size_t llatte_action_tokenize_workspace_size(const llatte_action_desc* desc, int32_t n) {
+  if (!desc || n < 0 || check_action_desc(desc) != LLATTE_OK) return 0;
+  return action_ws(desc, n).total;
+}
+
+llatte_status llatte_action_tokenize(const llatte_action_desc* desc,
+                                     const llatte_action_weights* w,
+                                     const int32_t* offsets, int32_t B, int32_t n,
+                                     const int32_t* t_req, const int32_t* tau,
+                                     const int32_t* type_id, const int32_t* item_id,
+                                     const int32_t* surf_id, const void* meta,
+                                     float* out, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  llatte_status st = check_action_desc(desc);
+  if (st) return st;
+  if (!w) return fail(LLATTE_ERR_INVALID_ARG, "NULL weights");
+  if (B < 1 || n < 0) return fail(LLATTE_ERR_INVALID_ARG, "B must be >= 1 and n >= 0");
+  if (n == 0) return LLATTE_OK;  // nothing to read or write; row arrays may be NULL
+  const void* ptrs[] = {offsets, t_req, tau, type_id, item_id, surf_id, meta, out, workspace,
+                        w->E_type, w->E_item, w->E_surf, w->E_time, w->W_meta, w->W_a, w->W_b};
+  for (const void* p : ptrs) {
+    if (!p) return fail(LLATTE_ERR_INVALID_ARG, "NULL pointer");
+    if (!aligned16(p)) return fail(LLATTE_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  }
+  const ActionWs ws = action_ws(desc, n);
+  if (workspace_bytes < ws.total) return fail(LLATTE_ERR_WORKSPACE, "workspace too small");
+  const bool b = desc->dtype == LLATTE_BF16;
+  const int kind = b ? K_BF16 : K_F32;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+  const int d_in = desc->d_type + desc->d_item + desc->d_surf + desc->d_time + desc->d_meta_emb;
+
+  ActionConcat c;
+  c.offsets = offsets;
+  c.B = B;
+  c.n = n;
+  c.t_req = t_req;
+  c.tau = tau;
+  c.type_id = type_id;
+  c.item_id = item_id;
+  c.surf_id = surf_id;
+  c.meta = meta;
+  c.E_type = w->E_type;
+  c.E_item = w->E_item;
+  c.E_surf = w->E_surf;
+  c.E_time = w->E_time;
+  c.W_meta = w->W_meta;
+  c.d_type = desc->d_type;
+  c.d_item = desc->d_item;
+  c.d_surf = desc->d_surf;
+  c.d_time = desc->d_time;
+  c.d_meta = desc->d_meta;
+  c.d_meta_emb = desc->d_meta_emb;
+  c.d_in = d_in;
+  c.V_type = desc->V_type;
+  c.V_item = desc->V_item;
+  c.V_surf = desc->V_surf;
+  c.n_buckets = desc->n_buckets;
+  c.U = base + ws.U;
+  c.age = (int*)(base + ws.age);
+  HIP_TRY(transpose(w->W_a, d_in, desc->d_hidden, desc->d_hidden, 0, base + ws.WaT, d_in, 0, 1,
+                    kind, kind, s));
+  HIP_TRY(transpose(w->W_b, desc->d_hidden, desc->d, desc->d, 0, base + ws.WbT, desc->d_hidden,
+                    0, 1, kind, kind, s));
+  HIP_TRY(action_concat(c, b, s));
+  {  // H = GELU(U W_a)
+    GemmParams g;
+    g.name = "gemm_act_a";
+    g.A = c.U;
+    g.lda = d_in;
+    g.B = base + ws.WaT;
+    g.ldb = d_in;
+    g.M_cap = n;
+    g.N = desc->d_hidden;
+    g.K = d_in;
+    g.epi = EPI_GELU;
+    g.C = base + ws.H;
+    g.ldc = desc->d_hidden;
+    HIP_TRY(gemm(g, b, s));
+  }
+  {  // out = H W_b + enc(age)
+    GemmParams g;
+    g.name = "gemm_act_b";
+    g.A = base + ws.H;
+    g.lda = desc->d_hidden;
+    g.B = base + ws.WbT;
+    g.ldb = desc->d_hidden;
+    g.M_cap = n;
+    g.N = desc->d;
+    g.K = desc->d_hidden;
+    g.epi = EPI_STORE_F32;
+    g.C = out;
+    g.ldc = desc->d;
+    g.enc_age = c.age;
+    g.enc_dims = desc->d_enc;
+    HIP_TRY(gemm(g, b, s));
+  }
+  return LLATTE_OK;
+}
+
 }  // extern "C"

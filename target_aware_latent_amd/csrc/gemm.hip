@@ -104,6 +104,26 @@ template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
   return f32x4{from_bf16(v[0]), from_bf16(v[1]), from_bf16(v[2]), from_bf16(v[3])};
 }
 
+// Timestamp encoding of the action tokens ([LLaTTE] Appendix A.2, additive
+// timestamp encodings on a subset of the hidden dimensions): columns
+// 2i, 2i+1 < enc_dims of row m get sin / cos of
+// (age / 3600) * 10000^(-2i / enc_dims). The angle and the sine are computed
+// in fp64: ages span months, where an fp32 angle would be off by 1e-3 rad.
+__device__ __forceinline__ f32x4 add_time_enc(f32x4 x, const GemmParams& p, int m, int n) {
+  if (!p.enc_age || n >= p.enc_dims) return x;
+  const double age_h = (double)p.enc_age[m] / 3600.0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int col = n + c;
+    if (col < p.enc_dims) {
+      const double w = exp2(-(double)(col & ~1) / p.enc_dims * 13.287712379549449);  // log2 1e4
+      const double a = age_h * w;
+      x[c] += (float)((col & 1) ? cos(a) : sin(a));
+    }
+  }
+  return x;
+}
+
 // Row-major epilogue. The fp32 accumulator tile goes through LDS (16-byte
 // chunk c of row r stored at chunk c ^ (r & 15), so that both the fragment
 // writes and the row reads below are free of bank conflicts) and comes back
@@ -170,7 +190,7 @@ __device__ __forceinline__ void epilogue_rowmajor(const GemmParams p, const f32x
       break;
     case EPI_STORE_F32:
       each([&](int ps, int h, int m, int n) {
-        const f32x4 x = v[ps][h] * p.alpha;
+        const f32x4 x = add_time_enc(v[ps][h] * p.alpha, p, m, n);
         store4<float>((float*)p.C + coff(m, n), x[0], x[1], x[2], x[3]);
       });
       break;
@@ -556,7 +576,7 @@ __global__ __launch_bounds__(64 * NW, (gemm_min_waves<BN, NW>())) void gemm_kern
       break;
     case EPI_STORE_F32:
       outs([&](int i, int j, int m, int n) {
-        const f32x4 v = acc[i][j] * (rsc[i] * p.alpha);
+        const f32x4 v = add_time_enc(acc[i][j] * (rsc[i] * p.alpha), p, m, n);
         store4<float>((float*)p.C + coff(m, n), v[0], v[1], v[2], v[3]);
       });
       break;

@@ -82,12 +82,43 @@ struct GemmParams {
   // large output streams to HBM without displacing the operands the tiles
   // still read from the caches.
   bool nt = false;
+  // EPI_STORE_F32 extra (timestamp encoding of the action tokens): columns
+  // 2i, 2i+1 < enc_dims of row m get sin / cos of
+  // (enc_age[m] / 3600) * 10000^(-2i / enc_dims), computed in fp64.
+  const int* enc_age = nullptr;
+  int enc_dims = 0;
 };
 
 // Partial sums of squares per row that an EPI_RESID_F32 launch with these
 // parameters writes to ss_out.
 int gemm_ss_slots(const GemmParams& p, bool bf16);
 hipError_t gemm(const GemmParams& p, bool bf16, hipStream_t s);
+
+// ------------------------------------------------------------------ actions
+// U[row] = [E_type(type) | E_item(item) | E_surf(surf) | E_time(bucket) |
+// meta W_meta] in the dtype, and age[row] (seconds, >= 0), for n actions of
+// B users (rows offsets[u] .. offsets[u+1]-1 belong to user u). Field widths
+// are multiples of 16 bytes of the dtype.
+struct ActionConcat {
+  const int* offsets = nullptr;
+  int B = 0, n = 0;
+  const int* t_req = nullptr;
+  const int* tau = nullptr;
+  const int* type_id = nullptr;
+  const int* item_id = nullptr;
+  const int* surf_id = nullptr;
+  const void* meta = nullptr;
+  const void* E_type = nullptr;
+  const void* E_item = nullptr;
+  const void* E_surf = nullptr;
+  const void* E_time = nullptr;
+  const void* W_meta = nullptr;
+  int d_type = 0, d_item = 0, d_surf = 0, d_time = 0, d_meta = 0, d_meta_emb = 0, d_in = 0;
+  int V_type = 0, V_item = 0, V_surf = 0, n_buckets = 0;
+  void* U = nullptr;
+  int* age = nullptr;
+};
+hipError_t action_concat(const ActionConcat& p, bool bf16, hipStream_t s);
 
 // ------------------------------------------------------------------ row ops
 // One wave per row (d <= 1024): out = gain ? x / sqrt(mean(x^2) + eps) * gain : x, where

@@ -63,6 +63,18 @@ class llatte_attn_desc(ctypes.Structure):
                 ("dtype", _c_int), ("scale", ctypes.c_float)]
 
 
+class llatte_action_desc(ctypes.Structure):
+    _fields_ = [(n, _c_int) for n in (
+        "d", "d_hidden", "d_enc", "d_type", "d_item", "d_surf", "d_time",
+        "d_meta", "d_meta_emb", "V_type", "V_item", "V_surf", "n_buckets",
+        "dtype")]
+
+
+class llatte_action_weights(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("E_type", "E_item", "E_surf", "E_time",
+                                   "W_meta", "W_a", "W_b")]
+
+
 # name -> (restype, argtypes)
 _SIGS = {
     "llatte_mla_forward": (_c_int, [
@@ -93,6 +105,12 @@ _SIGS = {
         ctypes.c_size_t, _vp]),
     "llatte_token_embed_workspace_size": (ctypes.c_size_t, [
         _c_int, _c_int, _c_int]),
+    "llatte_action_tokenize": (_c_int, [
+        ctypes.POINTER(llatte_action_desc), ctypes.POINTER(llatte_action_weights),
+        _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+        ctypes.c_size_t, _vp]),
+    "llatte_action_tokenize_workspace_size": (ctypes.c_size_t, [
+        ctypes.POINTER(llatte_action_desc), _c_int]),
     "llatte_last_error": (ctypes.c_char_p, []),
     "llatte_version": (_c_int, []),
     "llatte_kernel_timing_enable": (None, [_c_int]),
@@ -230,6 +248,20 @@ def llatte_token_embed(table, V, rows, sem, W_s, n, d, d_sem, dt, out,
         _p(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check(st, "llatte_token_embed")
+
+
+def llatte_action_tokenize_workspace_size(desc, n):
+    return lib().llatte_action_tokenize_workspace_size(ctypes.byref(desc), n)
+
+
+def llatte_action_tokenize(desc, w, offsets, B, n, t_req, tau, type_id,
+                           item_id, surf_id, meta, out, workspace, stream=None):
+    st = lib().llatte_action_tokenize(
+        ctypes.byref(desc), ctypes.byref(w), _p(offsets), B, n, _p(t_req),
+        _p(tau), _p(type_id), _p(item_id), _p(surf_id), _p(meta), _p(out),
+        _p(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(st, "llatte_action_tokenize")
 
 
 def llatte_last_error():

@@ -128,3 +128,47 @@ def test_host_pyramid_counts_c4_lengths(L):
     lengths = synth.generate(cfg)["inputs"]["lengths"]
     got = np.array(L.llatte_pyramid_counts_host(_rule(L, cfg.pyramid), cfg.N, lengths))
     assert np.array_equal(got, O.pyramid_counts(cfg.pyramid, lengths, cfg.N))
+
+
+def test_action_tokenize_host_validation(L):
+    from synth.actions import get_action_config
+    from target_aware_latent_amd.actions import make_action_desc
+    lib = L.lib()
+    good = make_action_desc(get_action_config("a_c3"))
+    assert L.llatte_action_tokenize_workspace_size(good, 102400) > 102400 * 256 * 2
+    assert L.llatte_action_tokenize_workspace_size(
+        make_action_desc(get_action_config("a_small")), 235) > 0
+    for field, val, code in [("dtype", 5, L.LLATTE_ERR_UNSUPPORTED),
+                             ("d_item", 12, L.LLATTE_ERR_UNSUPPORTED),   # bf16: multiple of 8
+                             ("d_enc", 3, L.LLATTE_ERR_INVALID_ARG),
+                             ("d_enc", 1024, L.LLATTE_ERR_INVALID_ARG),
+                             ("V_item", 0, L.LLATTE_ERR_INVALID_ARG),
+                             ("n_buckets", 65, L.LLATTE_ERR_INVALID_ARG),
+                             ("d_meta", 0, L.LLATTE_ERR_INVALID_ARG)]:
+        d = make_action_desc(get_action_config("a_c3"))
+        setattr(d, field, val)
+        assert L.llatte_action_tokenize_workspace_size(d, 10) == 0, field
+        w = L.llatte_action_weights()
+        st = lib.llatte_action_tokenize(ctypes.byref(d), ctypes.byref(w), None, 2, 10, None,
+                                        None, None, None, None, None, None, None, 0, None)
+        assert st == code, (field, st)
+    w = L.llatte_action_weights()
+    # n = 0: valid, nothing to read, nothing launched
+    assert lib.llatte_action_tokenize(ctypes.byref(good), ctypes.byref(w), None, 2, 0, None,
+                                      None, None, None, None, None, None, None, 0, None) == 0
+    # B < 1, NULL pointers with rows to do
+    assert lib.llatte_action_tokenize(ctypes.byref(good), ctypes.byref(w), None, 0, 0, None,
+                                      None, None, None, None, None, None, None, 0,
+                                      None) == L.LLATTE_ERR_INVALID_ARG
+    assert lib.llatte_action_tokenize(ctypes.byref(good), ctypes.byref(w), None, 2, 10, None,
+                                      None, None, None, None, None, None, None, 0,
+                                      None) == L.LLATTE_ERR_INVALID_ARG
+    # every pointer present and aligned but the workspace too small: refused
+    # before anything is enqueued (the addresses are never touched)
+    fake = ctypes.c_void_p(1 << 20)
+    for k in ("E_type", "E_item", "E_surf", "E_time", "W_meta", "W_a", "W_b"):
+        setattr(w, k, 1 << 20)
+    st = lib.llatte_action_tokenize(ctypes.byref(good), ctypes.byref(w), fake, 2, 10, fake,
+                                    fake, fake, fake, fake, fake, fake, fake, 64, None)
+    assert st == L.LLATTE_ERR_WORKSPACE
+    assert "workspace" in L.llatte_last_error()

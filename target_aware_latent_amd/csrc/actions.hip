@@ -7,9 +7,8 @@
 // The age of an action is its user's request time minus its timestamp
 // (negative taken as 0), the time bucket floor(log2(1 + age)) clamped to the
 // last table row; ids outside their table are clamped into it, so a bad id
-// cannot read past a table. The thread of a row's first piece also writes
-// the row's age, which the second product's epilogue turns into the
-// timestamp encoding.
+// cannot read past a table. Each block also writes the ages of its rows,
+// which the second product's epilogue turns into the timestamp encoding.
 #include "kernels.hpp"
 
 namespace llatte {
@@ -33,19 +32,28 @@ template <typename T>
 __global__ __launch_bounds__(256) void action_concat_kernel(ActionConcat p) {
   constexpr int CE = 16 / sizeof(T);
   const int cpr = p.d_in / CE;
-  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (g >= (long long)p.n * cpr) return;
+  // The block's rows: one lane per row finds the row's user and age (the
+  // searches run side by side), shared through LDS.
+  __shared__ int s_age[258];
+  const long long g0 = (long long)blockIdx.x * 256;
+  const long long total = (long long)p.n * cpr;
+  const int r_first = (int)(g0 / cpr);
+  const int r_last = (int)((min(g0 + 256, total) - 1) / cpr);
+  if ((int)threadIdx.x <= r_last - r_first) {
+    const int r = r_first + threadIdx.x;
+    const int u = row_user(p.offsets, p.B, r);
+    long long a = (long long)p.t_req[u] - (long long)p.tau[r];
+    a = a < 0 ? 0 : (a > 0x7FFFFFFFLL ? 0x7FFFFFFFLL : a);
+    s_age[threadIdx.x] = (int)a;
+    p.age[r] = (int)a;
+  }
+  __syncthreads();
+  const long long g = g0 + threadIdx.x;
+  if (g >= total) return;
   const int row = (int)(g / cpr), c0 = (int)(g % cpr) * CE;
   const int o_item = p.d_type, o_surf = o_item + p.d_item, o_time = o_surf + p.d_surf;
   const int o_meta = o_time + p.d_time;
-  int age = 0;
-  if (c0 == 0 || (c0 >= o_time && c0 < o_meta)) {
-    const int u = row_user(p.offsets, p.B, row);
-    long long a = (long long)p.t_req[u] - (long long)p.tau[row];
-    a = a < 0 ? 0 : (a > 0x7FFFFFFFLL ? 0x7FFFFFFFLL : a);
-    age = (int)a;
-    if (c0 == 0) p.age[row] = age;
-  }
+  const int age = s_age[row - r_first];
   T* dst = (T*)p.U + (size_t)row * p.d_in + c0;
   const T* src;
   if (c0 < o_item) {
@@ -65,11 +73,18 @@ __global__ __launch_bounds__(256) void action_concat_kernel(ActionConcat p) {
     float acc[CE];
 #pragma unroll
     for (int e = 0; e < CE; ++e) acc[e] = 0.f;
-    for (int k = 0; k < p.d_meta; ++k) {
-      const float mk = tof(m[k]);
-      const T* w = (const T*)p.W_meta + (size_t)k * p.d_meta_emb + j0;
+    // meta row and W_meta rows in 16-byte pieces (widths are multiples)
+    for (int k0 = 0; k0 < p.d_meta; k0 += CE) {
+      const i32x4 mraw = *(const i32x4*)(m + k0);
+      const T* mv = (const T*)&mraw;
 #pragma unroll
-      for (int e = 0; e < CE; ++e) acc[e] = fmaf(mk, tof(w[e]), acc[e]);
+      for (int kk = 0; kk < CE; ++kk) {
+        const i32x4 wraw = *(const i32x4*)((const T*)p.W_meta + (size_t)(k0 + kk) * p.d_meta_emb + j0);
+        const T* wv = (const T*)&wraw;
+        const float mk = tof(mv[kk]);
+#pragma unroll
+        for (int e = 0; e < CE; ++e) acc[e] = fmaf(mk, tof(wv[e]), acc[e]);
+      }
     }
     if constexpr (__is_same(T, bf16)) {
       bf16x8 o;

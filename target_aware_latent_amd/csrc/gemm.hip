@@ -107,18 +107,23 @@ template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
 // Timestamp encoding of the action tokens ([LLaTTE] Appendix A.2, additive
 // timestamp encodings on a subset of the hidden dimensions): columns
 // 2i, 2i+1 < enc_dims of row m get sin / cos of
-// (age / 3600) * 10000^(-2i / enc_dims). The angle and the sine are computed
-// in fp64: ages span months, where an fp32 angle would be off by 1e-3 rad.
+// (age / 3600) * 10000^(-2i / enc_dims). Ages span months, where an fp32
+// angle would be off by 1e-3 rad: the angle is formed and reduced to a
+// fraction of a turn in fp64, and the hardware sine / cosine (argument in
+// turns) takes the reduced fp32 value.
 __device__ __forceinline__ f32x4 add_time_enc(f32x4 x, const GemmParams& p, int m, int n) {
   if (!p.enc_age || n >= p.enc_dims) return x;
-  const double age_h = (double)p.enc_age[m] / 3600.0;
+  const double turns_h = (double)p.enc_age[m] * (1.0 / (3600.0 * 6.283185307179586));
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int col = n + c;
+  for (int c = 0; c < 4; c += 2) {
+    const int col = n + c;  // even: (sin, cos) of one frequency in col, col + 1
     if (col < p.enc_dims) {
-      const double w = exp2(-(double)(col & ~1) / p.enc_dims * 13.287712379549449);  // log2 1e4
-      const double a = age_h * w;
-      x[c] += (float)((col & 1) ? cos(a) : sin(a));
+      const double w = exp2(-(double)col / p.enc_dims * 13.287712379549449);  // log2 1e4
+      double t = turns_h * w;
+      t -= floor(t);
+      const float tf = (float)t;
+      x[c] += __builtin_amdgcn_sinf(tf);
+      x[c + 1] += __builtin_amdgcn_cosf(tf);
     }
   }
   return x;

@@ -34,7 +34,10 @@ with its reason in the design notes):
     square root; no final norm after the stack;
   * readout: one more layer in cross-attention mode whose queries are the
     learned seeds, flattened seed-major and multiplied by W_p (the A.2
-    summary with a plain linear map in place of the low-rank MLP).
+    summary as a plain linear map); without W_p the flattened readout itself
+    is returned, for the low-rank adapted MLP summaries
+    (lora_mlp_summaries: one hidden layer, exact-erf GELU, no biases, base
+    weights shared by the summaries plus rank-rho adapters per summary).
 
 Numbers are fp64 by default; ``dtype=np.float32`` gives the same code in
 single precision (used only as the timed CPU baseline).
@@ -48,6 +51,7 @@ __all__ = [
     "rmsnorm", "gelu", "softmax_masked", "pyramid_list", "pyramid_counts",
     "compact", "history_query_mask", "mla_layer", "fuse_queries", "forward",
     "token_embed", "latent_attention", "unmasked_pairs", "flop_count",
+    "lora_mlp_summaries",
 ]
 
 
@@ -298,8 +302,30 @@ def forward(cfg, W, hist, offsets, cand=None, ctx=None, users=None,
         res["cand"].append(Rc)
         if readout is not None:
             _, S = mla_layer(Rh, Wc["seeds"], 0, readout, cfg, absorbed)
-            res["emb"].append(S.reshape(-1) @ Wc["W_p"])
+            flat = S.reshape(-1)   # Flatten(Z_raw), seed-major
+            res["emb"].append(flat if Wc.get("W_p") is None else flat @ Wc["W_p"])
     return res
+
+
+def lora_mlp_summaries(z, L, dtype=np.float64):
+    """Sequence summaries [K, B, d_seq] from flattened readouts z [B, d_z].
+
+    [LLaTTE] Appendix A.2 item 4: each summary k is LoRAMLP_k applied to
+    Flatten(Z_raw), a low-rank adapted MLP. Reading (the internals are not
+    given): one hidden layer, exact-erf GELU, no biases, with base weights
+    W1 [d_z, d_h], W2 [d_h, d_seq] shared by the summaries and rank-rho
+    adapters per summary on both matrices:
+        LoRAMLP_k(x) = GELU(x (W1 + A1_k B1_k)) (W2 + A2_k B2_k),
+    A1 [K, d_z, rho], B1 [K, rho, d_h], A2 [K, d_h, rho], B2 [K, rho, d_seq].
+    """
+    f = lambda a: np.asarray(a, dtype=dtype)
+    z = f(z)
+    out = []
+    for k in range(f(L["A1"]).shape[0]):
+        W1k = f(L["W1"]) + f(L["A1"][k]) @ f(L["B1"][k])
+        W2k = f(L["W2"]) + f(L["A2"][k]) @ f(L["B2"][k])
+        out.append(gelu(z @ W1k) @ W2k)
+    return np.stack(out)
 
 
 def token_embed(table_rows, sem, W_s):

@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3]
     python bench.py --workload actions     (the action tokenization)
+    python bench.py --workload summaries   (the LoRAMLP sequence summaries)
 
 One step is one llatte_mla_forward over one batch of the workload (all
 layers, the pyramid, the readout), inputs and weights already resident in
@@ -251,6 +252,88 @@ def bench_actions(args):
     print(json.dumps(rec))
 
 
+SUMMARIES_METRIC = "users/sec + TFLOP/s (% MFMA bf16 peak), sequence summaries, 1 GPU"
+SUMMARIES_TEXT = ("s_c3: LoRAMLP sequence summaries of the upstream readout, 64 users, "
+                  "Flatten(Z_raw) 2048 -> hidden 2048 -> 2048, 2 summaries, adapter rank 16")
+
+
+def bench_summaries(args):
+    import torch
+    from oracle import llatte_oracle as O
+    from synth.summaries import generate_summaries, get_summary_config
+    from target_aware_latent_amd import llatte as C
+    from target_aware_latent_amd.summaries import DeviceSummaries
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    cfg = get_summary_config("s_c3")
+    p = generate_summaries(cfg, 0)
+    L, z = p["weights"], p["inputs"]["z"]
+    ds = DeviceSummaries(cfg, L)
+    zt = torch.from_numpy(np.ascontiguousarray(z, dtype=np.float32)).cuda()
+    out = torch.empty((cfg.K, cfg.B, cfg.d_seq), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    step = lambda: ds(zt, out=out, stream=stream)
+    for _ in range(args.warmup):
+        step()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    f1 = 2 * cfg.K * cfg.B * cfg.d_z * cfg.d_hidden
+    f2 = 2 * cfg.K * cfg.B * cfg.d_hidden * cfg.d_seq
+    F = f1 + f2
+    C.llatte_kernel_timing_reset()
+    C.llatte_kernel_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = C.llatte_kernel_timing_read()
+    C.llatte_kernel_timing_enable(False)
+    flops = {"gemm_summary_1": f1, "gemm_summary_2": f2}
+    kernels = {}
+    for name, (cnt, tot) in kt.items():
+        e = {"launches_per_step": cnt / args.steps, "ms_per_step": tot / args.steps}
+        if name in flops:
+            e["tflops"] = flops[name] / (tot / cnt / 1e3) / 1e12
+        kernels[name] = e
+    dom = max(flops, key=lambda k: kt[k][1])
+    cnt, tot = kt[dom]
+    achieved = flops[dom] / (tot / cnt / 1e3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": flops[dom], "avg_launch_ms": round(tot / cnt, 4)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 5.0:
+            O.lora_mlp_summaries(z, L, dtype=np.float32)
+            reps += 1
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(reps * cfg.B / dt, 1), "unit": "users/s",
+               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"{reps} full batches of {cfg.B} users, fp32 oracle "
+                         f"(adapters merged per call), {dt:.1f} s"}
+    rec = {
+        "metric": SUMMARIES_METRIC, "value": round(cfg.B / (ms_step / 1e3), 1),
+        "unit": "users/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (N(0,1) readouts, N(0,1/fan_in) weights and adapters)",
+        "config": {"workload": SUMMARIES_TEXT, "global_batch": cfg.B, "seq_len": None,
+                   "parallelism": "single GPU"},
+        "tflops": round(F / (ms_step / 1e3) / 1e12, 2),
+        "pct_peak": round(100 * F / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+    }
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -267,9 +350,10 @@ def main():
                     help="profile summary whose RECORD line holds the measured "
                          "HBM bytes per launch of the dominant kernel (written "
                          "by target_aware_latent_amd.profsum traffic)")
-    ap.add_argument("--workload", default="stack", choices=["stack", "actions"],
+    ap.add_argument("--workload", default="stack", choices=["stack", "actions", "summaries"],
                     help="stack: the MLA forward (default); actions: the action "
-                         "tokenization that builds the history tokens")
+                         "tokenization that builds the history tokens; summaries: the "
+                         "LoRAMLP sequence summaries of the readout")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
@@ -278,6 +362,9 @@ def main():
         sys.exit(2)
     if args.workload == "actions":
         bench_actions(args)
+        return
+    if args.workload == "summaries":
+        bench_summaries(args)
         return
 
     import torch

@@ -59,6 +59,11 @@ typedef int32_t llatte_status;
 #define LLATTE_PYR_HALVING 1   /* max(min(floor, L_u), L_u >> l)            */
 #define LLATTE_PYR_GEOMETRIC 2 /* start -> end geometric, rounded half up   */
 
+/* The readout returns Flatten(Z_raw) itself in out_emb (seed-major,
+ * [B, n_seeds*d]; d_out must equal n_seeds*d and W_p is not used), as the
+ * input of llatte_summaries. */
+#define LLATTE_FLAG_RAW_READOUT 1u
+
 #define LLATTE_MAX_LAYERS 64
 
 /* Pyramidal schedule ([LLaTTE] A.2): how many of the most recent history rows
@@ -95,7 +100,7 @@ typedef struct {
   llatte_pyramid_rule pyramid;
   int32_t n_seeds;     /* readout seed queries (0 = no readout)             */
   int32_t d_out;       /* readout embedding width                           */
-  uint32_t flags;      /* reserved, must be 0                               */
+  uint32_t flags;      /* 0 or LLATTE_FLAG_RAW_READOUT                      */
   int32_t q_rank;      /* 0: full-rank queries; > 0: low-rank query width   */
 } llatte_model_desc;
 
@@ -124,7 +129,8 @@ typedef struct {
  *   W_q   [d + d_ctx, d]  fusion projection of [x_j ; c_u] (needed if n_q>0)
  *   seeds [n_seeds, d]    float32 learned readout queries   (if n_seeds>0)
  *   readout               weights of the readout layer       (if n_seeds>0)
- *   W_p   [n_seeds*d, d_out] readout projection              (if n_seeds>0) */
+ *   W_p   [n_seeds*d, d_out] readout projection              (if n_seeds>0,
+ *         unused with LLATTE_FLAG_RAW_READOUT) */
 typedef struct {
   const llatte_layer_weights* layers;
   const void* W_q;
@@ -363,6 +369,46 @@ llatte_status llatte_action_tokenize(const llatte_action_desc* desc /* host */,
 
 size_t llatte_action_tokenize_workspace_size(const llatte_action_desc* desc,
                                              int32_t n);
+
+/* ------------------------------------------------------------------------
+ * Sequence summaries ([LLaTTE] Appendix A.2 item 4): K fixed-size summaries
+ * of the flattened readout z = Flatten(Z_raw), each a low-rank adapted MLP.
+ * The page gives no internals; the library implements one hidden layer with
+ * the exact-erf GELU and no biases, base weights shared by the summaries and
+ * rank-`rank` adapters per summary on both matrices:
+ *   out[k] = GELU(z (W1 + A1[k] B1[k])) (W2 + A2[k] B2[k])
+ *
+ *   W1 [d_z, d_hidden], W2 [d_hidden, d_seq], A1 [K, d_z, rank],
+ *   B1 [K, rank, d_hidden], A2 [K, d_hidden, rank], B2 [K, rank, d_seq],
+ *   all in dtype. z [B, d_z] float32 (for instance out_emb of
+ *   llatte_mla_forward with LLATTE_FLAG_RAW_READOUT); out [K, B, d_seq]
+ *   float32. d_z, d_hidden and d_seq are multiples of 8 (BF16) or 4 (F32);
+ *   1 <= rank <= 256; 1 <= n_summaries <= 64.
+ *
+ *   llatte_summary_pack merges the adapters into the base weights once (in
+ *   dtype, transposed for the products) into caller memory of
+ *   llatte_summary_packed_size(desc) bytes; llatte_summaries then needs a
+ *   workspace of llatte_summaries_workspace_size(desc, B) bytes. B = 0 is
+ *   valid and enqueues nothing.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t d_z, d_hidden, d_seq, rank, n_summaries;
+  int32_t dtype; /* LLATTE_F32 or LLATTE_BF16 */
+} llatte_summary_desc;
+
+typedef struct {
+  const void *W1, *W2, *A1, *B1, *A2, *B2;
+} llatte_summary_weights;
+
+size_t llatte_summary_packed_size(const llatte_summary_desc* desc);
+llatte_status llatte_summary_pack(const llatte_summary_desc* desc /* host */,
+                                  const llatte_summary_weights* w /* host */,
+                                  void* packed, size_t packed_bytes, void* stream);
+size_t llatte_summaries_workspace_size(const llatte_summary_desc* desc, int32_t B);
+llatte_status llatte_summaries(const llatte_summary_desc* desc /* host */,
+                               const void* packed, const float* z, int32_t B,
+                               float* out, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /* ------------------------------------------------------------------------
  * Diagnostics.

@@ -132,6 +132,7 @@ struct Shapes {
   int rq, qin;                // query rank (0: full rank) and W_uq input width
   bool bf16, pre, lnorm;
   bool fnorm;                 // norms fused into the GEMMs (bf16, pre-norm)
+  bool raw = false;           // readout returns Flatten(Z_raw) (no W_p)
   float eps;
   int NP;                     // plans: N layers (+ readout)
   RuleDev rule;
@@ -179,7 +180,8 @@ static llatte_status expand_rule(const llatte_pyramid_rule* pr, int N,
 static llatte_status make_shapes(const llatte_model_desc* dsc, int B, int total,
                                  int max_len, Shapes* S) {
   if (!dsc) return fail(LLATTE_ERR_INVALID_ARG, "desc is NULL");
-  if (dsc->flags != 0) return fail(LLATTE_ERR_INVALID_ARG, "flags must be 0");
+  if (dsc->flags & ~LLATTE_FLAG_RAW_READOUT)
+    return fail(LLATTE_ERR_INVALID_ARG, "unknown flags 0x%x", dsc->flags);
   if (B < 1 || total < B || max_len < 1 || (long long)max_len * B < total)
     return fail(LLATTE_ERR_INVALID_ARG, "need B >= 1, total_rows >= B, max_len*B >= total_rows");
   if (dsc->dtype != LLATTE_F32 && dsc->dtype != LLATTE_BF16)
@@ -202,6 +204,7 @@ static llatte_status make_shapes(const llatte_model_desc* dsc, int B, int total,
   S->dc = dsc->d_ctx;
   S->ns = dsc->n_seeds;
   S->dout = dsc->d_out;
+  S->raw = (dsc->flags & LLATTE_FLAG_RAW_READOUT) != 0;
   S->rq = dsc->q_rank;
   S->qin = S->rq > 0 ? S->rq : dsc->d;
   S->bf16 = dsc->dtype == LLATTE_BF16;
@@ -225,6 +228,8 @@ static llatte_status make_shapes(const llatte_model_desc* dsc, int B, int total,
   if (S->nq == 0 && S->dc != 0) return fail(LLATTE_ERR_INVALID_ARG, "d_ctx needs n_q > 0");
   if (S->ns > 0 && (S->dout < 1 || S->dout % 4))
     return fail(LLATTE_ERR_INVALID_ARG, "d_out must be a positive multiple of 4");
+  if (S->raw && S->ns > 0 && S->dout != S->ns * S->d)
+    return fail(LLATTE_ERR_INVALID_ARG, "with LLATTE_FLAG_RAW_READOUT d_out must be n_seeds*d");
   if (S->bf16) {
     if (!attn_fused_supported(S->h, S->r, S->dk))
       return fail(LLATTE_ERR_UNSUPPORTED,
@@ -339,7 +344,17 @@ struct FwdWS {
   void* XC;     // [B*nq, d+dc]
   float* S;     // [B*ns, d]
   void* E;      // [B*ns*d]
+  float* sk_part;  // split-K tiles of the GEMMs (kSkPart floats)
 };
+
+// Split-K scratch of the GEMMs that leave the GPU short of workgroups (late
+// pyramid layers, readout, summaries).
+constexpr long long kSkPart = 8ll << 20;
+
+static void with_sk(GemmParams& g, float* part) {
+  g.sk_part = part;
+  g.sk_part_cap = kSkPart;
+}
 
 static size_t layout_forward(const Shapes& S, void* base, FwdWS* w) {
   Arena ar(base);
@@ -377,6 +392,7 @@ static size_t layout_forward(const Shapes& S, void* base, FwdWS* w) {
   w->XC = S.nq ? ar.take<char>((size_t)S.B * S.nq * (S.d + S.dc) * e) : nullptr;
   w->S = S.ns ? ar.take<float>((size_t)S.B * S.ns * S.d) : nullptr;
   w->E = S.ns ? ar.take<char>((size_t)S.B * S.ns * S.d * e) : nullptr;
+  w->sk_part = ar.take<float>((size_t)kSkPart);
   return ar.off + 256;
 }
 
@@ -437,7 +453,8 @@ static hipError_t pack_all(const Shapes& S, const llatte_weights* w,
     if ((err = hipMemcpyAsync(P.seeds, w->seeds, (size_t)S.ns * S.d * 4,
                               hipMemcpyDeviceToDevice, s)))
       return err;
-    if ((err = transpose(w->W_p, S.ns * S.d, S.dout, S.dout, 0, P.WpT, S.ns * S.d,
+    if (!S.raw &&
+        (err = transpose(w->W_p, S.ns * S.d, S.dout, S.dout, 0, P.WpT, S.ns * S.d,
                          0, 1, k, k, s)))
       return err;
   }
@@ -474,6 +491,7 @@ static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
     g.name = name;
     g.M_cap = UBM;
     g.M_dev = P.counts + 3;
+    with_sk(g, w.sk_part);
     return g;
   };
 
@@ -495,6 +513,7 @@ static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
   {
     GemmParams g;
     g.name = "gemm_down";
+    with_sk(g, w.sk_part);
     g.A = (const char*)w.H + (size_t)nc * S.d * e;
     g.lda = S.d;
     g.B = L.Wdkv;
@@ -767,7 +786,7 @@ static llatte_status check_weights(const Shapes& S, const llatte_weights* wts) {
     if ((st = check_layer(S, &wts->layers[l], l))) return st;
   if (S.nq > 0 && !wts->W_q) return fail(LLATTE_ERR_INVALID_ARG, "n_q > 0 needs W_q");
   if (S.ns > 0) {
-    if (!wts->seeds || !wts->W_p)
+    if (!wts->seeds || (!wts->W_p && !S.raw))
       return fail(LLATTE_ERR_INVALID_ARG, "readout needs seeds and W_p");
     if ((st = check_layer(S, &wts->readout, -1))) return st;
   }
@@ -835,6 +854,7 @@ llatte_status llatte_mla_forward(
     HIP_TRY(concat_queries(cand_x, ctx, B, S.nq, S.d, S.dc, w.XC, b, s));
     GemmParams g;
     g.name = "gemm_fusion";
+    with_sk(g, w.sk_part);
     g.A = w.XC;
     g.lda = S.d + S.dc;
     g.B = PK.WqT;
@@ -877,10 +897,15 @@ llatte_status llatte_mla_forward(
     RowSrc src{w.S, last + nc * S.d, B * S.ns, S.d};
     LayerIO rio;
     HIP_TRY(run_layer(S, w, S.N, PK.L[S.N], src, ro, rio, s));
+    if (S.raw) {  // Flatten(Z_raw): the readout rows are already seed-major per user
+      HIP_TRY(copy_rows_f32(ro, S.d, out_emb, B * S.ns, nullptr, S.d, s));
+      return LLATTE_OK;
+    }
     HIP_TRY(norm_rows(RowSrc{ro, ro, 0, S.d}, B * S.ns, nullptr, nullptr, 0.f,
                       nullptr, 0, w.E, S.d, S.d, b ? K_BF16 : K_F32, s));
     GemmParams g;
     g.name = "gemm_readout";
+    with_sk(g, w.sk_part);
     g.A = w.E;
     g.lda = S.ns * S.d;
     g.B = PK.WpT;
@@ -1204,6 +1229,131 @@ llatte_status llatte_action_tokenize(const llatte_action_desc* desc,
     g.ldc = desc->d;
     g.enc_age = c.age;
     g.enc_dims = desc->d_enc;
+    HIP_TRY(gemm(g, b, s));
+  }
+  return LLATTE_OK;
+}
+
+
+// ---------------------------------------------------------------- summaries
+static llatte_status check_summary_desc(const llatte_summary_desc* a) {
+  if (!a) return fail(LLATTE_ERR_INVALID_ARG, "NULL descriptor");
+  if (a->dtype != LLATTE_F32 && a->dtype != LLATTE_BF16)
+    return fail(LLATTE_ERR_UNSUPPORTED, "dtype %d", a->dtype);
+  const int al = a->dtype == LLATTE_BF16 ? 8 : 4;
+  const int32_t widths[] = {a->d_z, a->d_hidden, a->d_seq};
+  for (int32_t v : widths) {
+    if (v < 1 || v > (1 << 16)) return fail(LLATTE_ERR_INVALID_ARG, "width %d out of range", v);
+    if (v % al) return fail(LLATTE_ERR_UNSUPPORTED, "widths must be multiples of %d", al);
+  }
+  if (a->rank < 1 || a->rank > 256) return fail(LLATTE_ERR_INVALID_ARG, "rank must be in [1, 256]");
+  if (a->n_summaries < 1 || a->n_summaries > 64)
+    return fail(LLATTE_ERR_INVALID_ARG, "n_summaries must be in [1, 64]");
+  return LLATTE_OK;
+}
+
+// packed: W1^T merged [K, d_hidden, d_z], then W2^T merged [K, d_seq, d_hidden]
+static size_t summary_w2_offset(const llatte_summary_desc* a) {
+  const size_t es = a->dtype == LLATTE_BF16 ? 2 : 4;
+  return al256((size_t)a->n_summaries * a->d_hidden * a->d_z * es);
+}
+
+size_t llatte_summary_packed_size(const llatte_summary_desc* desc) {
+  if (check_summary_desc(desc) != LLATTE_OK) return 0;
+  const size_t es = desc->dtype == LLATTE_BF16 ? 2 : 4;
+  return summary_w2_offset(desc) + al256((size_t)desc->n_summaries * desc->d_seq * desc->d_hidden * es);
+}
+
+llatte_status llatte_summary_pack(const llatte_summary_desc* desc,
+                                  const llatte_summary_weights* w,
+                                  void* packed, size_t packed_bytes, void* stream) {
+  llatte_status st = check_summary_desc(desc);
+  if (st) return st;
+  if (!w || !w->W1 || !w->W2 || !w->A1 || !w->B1 || !w->A2 || !w->B2 || !packed)
+    return fail(LLATTE_ERR_INVALID_ARG, "NULL pointer");
+  const void* ptrs[] = {w->W1, w->W2, w->A1, w->B1, w->A2, w->B2, packed};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(LLATTE_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (packed_bytes < llatte_summary_packed_size(desc))
+    return fail(LLATTE_ERR_WORKSPACE, "packed buffer too small");
+  const bool b = desc->dtype == LLATTE_BF16;
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(lora_merge(w->W1, w->A1, w->B1, desc->d_z, desc->d_hidden, desc->rank,
+                     desc->n_summaries, packed, b, s));
+  HIP_TRY(lora_merge(w->W2, w->A2, w->B2, desc->d_hidden, desc->d_seq, desc->rank,
+                     desc->n_summaries, (char*)packed + summary_w2_offset(desc), b, s));
+  return LLATTE_OK;
+}
+
+size_t llatte_summaries_workspace_size(const llatte_summary_desc* desc, int32_t B) {
+  if (B < 0 || check_summary_desc(desc) != LLATTE_OK) return 0;
+  const size_t es = desc->dtype == LLATTE_BF16 ? 2 : 4;
+  return al256((size_t)B * desc->d_z * es) +
+         al256((size_t)desc->n_summaries * B * desc->d_hidden * es) +
+         al256((size_t)kSkPart * 4) + 256;
+}
+
+llatte_status llatte_summaries(const llatte_summary_desc* desc, const void* packed,
+                               const float* z, int32_t B, float* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  llatte_status st = check_summary_desc(desc);
+  if (st) return st;
+  if (B < 0) return fail(LLATTE_ERR_INVALID_ARG, "B must be >= 0");
+  if (B == 0) return LLATTE_OK;
+  const void* ptrs[] = {packed, z, out, workspace};
+  for (const void* p : ptrs) {
+    if (!p) return fail(LLATTE_ERR_INVALID_ARG, "NULL pointer");
+    if (!aligned16(p)) return fail(LLATTE_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  }
+  if (workspace_bytes < llatte_summaries_workspace_size(desc, B))
+    return fail(LLATTE_ERR_WORKSPACE, "workspace too small");
+  const bool b = desc->dtype == LLATTE_BF16;
+  const size_t es = b ? 2 : 4;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+  void* zc = base;
+  void* H = base + al256((size_t)B * desc->d_z * es);
+  const int K = desc->n_summaries;
+  float* sk_part = (float*)((char*)H + al256((size_t)K * B * desc->d_hidden * es));
+  HIP_TRY(cast_f32(z, zc, (long long)B * desc->d_z, b, s));
+  {  // H[k] = GELU(z W1_k), all summaries in one batched launch
+    GemmParams g;
+    g.name = "gemm_summary_1";
+    with_sk(g, sk_part);
+    g.A = zc;
+    g.lda = desc->d_z;
+    g.sA = 0;
+    g.B = packed;
+    g.ldb = desc->d_z;
+    g.sB = (long long)desc->d_hidden * desc->d_z;
+    g.M_cap = B;
+    g.N = desc->d_hidden;
+    g.K = desc->d_z;
+    g.batch = K;
+    g.epi = EPI_GELU;
+    g.C = H;
+    g.ldc = desc->d_hidden;
+    g.sC = (long long)B * desc->d_hidden;
+    HIP_TRY(gemm(g, b, s));
+  }
+  {  // out[k] = H[k] W2_k
+    GemmParams g;
+    g.name = "gemm_summary_2";
+    with_sk(g, sk_part);
+    g.A = H;
+    g.lda = desc->d_hidden;
+    g.sA = (long long)B * desc->d_hidden;
+    g.B = (const char*)packed + summary_w2_offset(desc);
+    g.ldb = desc->d_hidden;
+    g.sB = (long long)desc->d_seq * desc->d_hidden;
+    g.M_cap = B;
+    g.N = desc->d_seq;
+    g.K = desc->d_hidden;
+    g.batch = K;
+    g.epi = EPI_STORE_F32;
+    g.C = out;
+    g.ldc = desc->d_seq;
+    g.sC = (long long)B * desc->d_seq;
     HIP_TRY(gemm(g, b, s));
   }
   return LLATTE_OK;

@@ -13,6 +13,7 @@
 //
 // bf16 operands use v_mfma_f32_16x16x32_bf16; fp32 operands use
 // v_mfma_f32_16x16x4_f32. Accumulation is fp32 in both cases.
+#include <algorithm>
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -275,7 +276,12 @@ __device__ __forceinline__ void epilogue_rowmajor(const GemmParams p, const f32x
 // most 128 VGPRs, i.e. four waves per SIMD.
 template <int BN, int NW> constexpr int gemm_min_waves() { return NW == 8 && BN <= 128 ? 4 : 1; }
 
-template <typename T, int BM, int BN, int WM, int WN, int NW, int PF>
+// SK = 0: the whole product. Split K: SK = 1 computes the K steps of split
+// blockIdx.y (of gridDim.y) and stores its fp32 tile in p.sk_part; SK = 2,
+// launched after it, sums the splits' tiles in split order and runs the
+// epilogue (the kernel boundary makes the tiles visible; no cross-workgroup
+// synchronisation).
+template <typename T, int BM, int BN, int WM, int WN, int NW, int PF, int SK>
 __global__ __launch_bounds__(64 * NW, (gemm_min_waves<BN, NW>())) void gemm_kernel(GemmParams p) {
   using MF = Mfma<T>;
   constexpr int NT = 64 * NW;              // threads
@@ -313,6 +319,11 @@ __global__ __launch_bounds__(64 * NW, (gemm_min_waves<BN, NW>())) void gemm_kern
   const int tm = bid / tiles_n, tn = bid % tiles_n;
   const int m0 = tm * BM, n0 = tn * BN;
   if (m0 >= M) return;
+  // K steps [kb0, kb0 + nk) of nk_all: all of them, or split blockIdx.y's
+  const int nk_all = (p.K + BK - 1) / BK;
+  const int nsplit = SK == 1 ? (int)gridDim.y : 1;
+  const int kper = (nk_all + nsplit - 1) / nsplit;
+  const int kb0 = SK == 1 ? (int)blockIdx.y * kper : 0;
 
   const T* A = (const T*)p.A + (size_t)blockIdx.z * p.sA;
   const T* Bm = (const T*)p.B + (size_t)blockIdx.z * p.sB;
@@ -344,7 +355,7 @@ __global__ __launch_bounds__(64 * NW, (gemm_min_waves<BN, NW>())) void gemm_kern
   i32x4 ra[PF][AI], rb[PF][BI];
   auto load_tile = [&](int kt, auto set) {
     constexpr int S = decltype(set)::value;
-    const int k0 = kt * BK;
+    const int k0 = (kb0 + kt) * BK;
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       int kc = ((tid + i * NT) % 8) * CE;
@@ -393,7 +404,7 @@ __global__ __launch_bounds__(64 * NW, (gemm_min_waves<BN, NW>())) void gemm_kern
     koff[x] = ((e / CE) ^ ((lr >> 1) & 7)) * CE + e % CE;
   }
 
-  const int nk = (p.K + BK - 1) / BK;
+  const int nk = SK == 2 ? 0 : max(0, min(nk_all, kb0 + kper) - kb0);
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   auto compute = [&](int buf) {
@@ -431,9 +442,11 @@ __global__ __launch_bounds__(64 * NW, (gemm_min_waves<BN, NW>())) void gemm_kern
     }
     __syncthreads();
   };
-  load_tile(0, S0{});
-  if constexpr (PF == 2) {
-    if (nk > 1) load_tile(1, S1{});
+  if constexpr (SK != 2) {
+    load_tile(0, S0{});
+    if constexpr (PF == 2) {
+      if (nk > 1) load_tile(1, S1{});
+    }
   }
   // Source rows of the residual / gathered table rows, resolved before the
   // main loop so the epilogue's loads do not wait on the index loads.
@@ -472,7 +485,7 @@ __global__ __launch_bounds__(64 * NW, (gemm_min_waves<BN, NW>())) void gemm_kern
     }
     rs_lds[tid] = sc;
   }
-  store_lds(0, S0{});
+  if constexpr (SK != 2) store_lds(0, S0{});
   __syncthreads();
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
@@ -480,6 +493,30 @@ __global__ __launch_bounds__(64 * NW, (gemm_min_waves<BN, NW>())) void gemm_kern
     step(kt + 1, S1{});
   }
   if (kt < nk) step(kt, S0{});
+
+  if constexpr (SK != 0) {
+    // split tiles: [tile][split][thread][TM*TN f32x4], each thread's
+    // accumulators contiguous
+    const size_t tile_id = (size_t)blockIdx.z * G + bid;
+    const int S = SK == 1 ? nsplit : p.sk_splits;
+    float* part = p.sk_part + tile_id * S * (size_t)(BM * BN);
+    if constexpr (SK == 1) {
+      f32x4* mine = (f32x4*)(part + (size_t)blockIdx.y * (BM * BN)) + tid * (TM * TN);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) mine[i * TN + j] = acc[i][j];
+      return;
+    } else {
+      for (int sp = 0; sp < S; ++sp) {
+        const f32x4* src = (const f32x4*)(part + (size_t)sp * (BM * BN)) + tid * (TM * TN);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] += src[i * TN + j];
+      }
+    }
+  }
 
   if constexpr (kShuffle) {
     if (p.nt)
@@ -632,13 +669,39 @@ __global__ __launch_bounds__(64 * NW, (gemm_min_waves<BN, NW>())) void gemm_kern
   }
 }
 
+// Splits of K for a launch of `tiles` workgroups. Only launches that leave
+// most CUs idle with a long chain of K steps per workgroup gain from the
+// second pass (measured: products with K <= 512, or with 400 or more tiles,
+// got slower split): then enough splits to approach one workgroup per CU,
+// at least 4 K steps per split, within the scratch capacity; 1 without
+// scratch.
+static int k_splits(const GemmParams& p, long long tiles, int BM, int BN, int BK) {
+  if (!p.sk_part || tiles <= 0 || tiles >= 128) return 1;
+  const int nk = (p.K + BK - 1) / BK;
+  if (nk < 16) return 1;
+  long long sp = std::min<long long>({8, 256 / tiles, nk / 4});
+  while (sp > 1 && tiles * sp * BM * BN > p.sk_part_cap) --sp;
+  return (int)std::max<long long>(sp, 1);
+}
+
 template <typename T, int BM, int BN, int WM, int WN, int NW, int PF = 1>
 static hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   const int tiles = ((p.M_cap + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   if (tiles == 0 || p.batch == 0) return hipSuccess;
+  constexpr int BK = 128 / (int)sizeof(T);
+  const int splits = k_splits(p, (long long)tiles * p.batch, BM, BN, BK);
   timing_begin(p.name, s);
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, NW, PF>), dim3(tiles, 1, p.batch),
-                     dim3(64 * NW), 0, s, p);
+  if (splits == 1) {
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, NW, PF, 0>), dim3(tiles, 1, p.batch),
+                       dim3(64 * NW), 0, s, p);
+  } else {
+    GemmParams q = p;
+    q.sk_splits = splits;
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, NW, PF, 1>), dim3(tiles, splits, p.batch),
+                       dim3(64 * NW), 0, s, q);
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, NW, PF, 2>), dim3(tiles, 1, p.batch),
+                       dim3(64 * NW), 0, s, q);
+  }
   timing_end(s);
   return hipGetLastError();
 }

@@ -87,6 +87,13 @@ struct GemmParams {
   // (enc_age[m] / 3600) * 10000^(-2i / enc_dims), computed in fp64.
   const int* enc_age = nullptr;
   int enc_dims = 0;
+  // Split-K scratch (optional, sk_part_cap floats): with it, launches that
+  // leave the GPU short of workgroups split K into sk_splits parts (set by
+  // the launcher); a first launch stores each split's fp32 tile, a second
+  // sums them in split order and runs the epilogue.
+  float* sk_part = nullptr;
+  long long sk_part_cap = 0;
+  int sk_splits = 1;
 };
 
 // Partial sums of squares per row that an EPI_RESID_F32 launch with these
@@ -119,6 +126,14 @@ struct ActionConcat {
   int* age = nullptr;
 };
 hipError_t action_concat(const ActionConcat& p, bool bf16, hipStream_t s);
+
+// ------------------------------------------------------------------ summaries
+// out[k] = (W + A[k] Bm[k])^T in the dtype: W [rows, cols], A [K, rows,
+// rank], Bm [K, rank, cols], out [K, cols, rows].
+hipError_t lora_merge(const void* W, const void* A, const void* Bm, int rows, int cols,
+                      int rank, int K, void* out, bool bf16, hipStream_t s);
+// dst (dtype) = src (float32), n elements.
+hipError_t cast_f32(const float* src, void* dst, long long n, bool bf16, hipStream_t s);
 
 // ------------------------------------------------------------------ row ops
 // One wave per row (d <= 1024): out = gain ? x / sqrt(mean(x^2) + eps) * gain : x, where

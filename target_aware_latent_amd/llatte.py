@@ -26,6 +26,7 @@ LLATTE_PYR_FIXED = 0
 LLATTE_PYR_HALVING = 1
 LLATTE_PYR_GEOMETRIC = 2
 LLATTE_MAX_LAYERS = 64
+LLATTE_FLAG_RAW_READOUT = 1
 
 _c_int = ctypes.c_int32
 _vp = ctypes.c_void_p
@@ -75,6 +76,15 @@ class llatte_action_weights(ctypes.Structure):
                                    "W_meta", "W_a", "W_b")]
 
 
+class llatte_summary_desc(ctypes.Structure):
+    _fields_ = [(n, _c_int) for n in ("d_z", "d_hidden", "d_seq", "rank",
+                                      "n_summaries", "dtype")]
+
+
+class llatte_summary_weights(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("W1", "W2", "A1", "B1", "A2", "B2")]
+
+
 # name -> (restype, argtypes)
 _SIGS = {
     "llatte_mla_forward": (_c_int, [
@@ -111,6 +121,14 @@ _SIGS = {
         ctypes.c_size_t, _vp]),
     "llatte_action_tokenize_workspace_size": (ctypes.c_size_t, [
         ctypes.POINTER(llatte_action_desc), _c_int]),
+    "llatte_summary_packed_size": (ctypes.c_size_t, [ctypes.POINTER(llatte_summary_desc)]),
+    "llatte_summary_pack": (_c_int, [
+        ctypes.POINTER(llatte_summary_desc), ctypes.POINTER(llatte_summary_weights), _vp,
+        ctypes.c_size_t, _vp]),
+    "llatte_summaries_workspace_size": (ctypes.c_size_t, [
+        ctypes.POINTER(llatte_summary_desc), _c_int]),
+    "llatte_summaries": (_c_int, [
+        ctypes.POINTER(llatte_summary_desc), _vp, _vp, _c_int, _vp, _vp, ctypes.c_size_t, _vp]),
     "llatte_last_error": (ctypes.c_char_p, []),
     "llatte_version": (_c_int, []),
     "llatte_kernel_timing_enable": (None, [_c_int]),
@@ -262,6 +280,27 @@ def llatte_action_tokenize(desc, w, offsets, B, n, t_req, tau, type_id,
         _p(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check(st, "llatte_action_tokenize")
+
+
+def llatte_summary_packed_size(desc):
+    return lib().llatte_summary_packed_size(ctypes.byref(desc))
+
+
+def llatte_summary_pack(desc, w, packed, stream=None):
+    st = lib().llatte_summary_pack(ctypes.byref(desc), ctypes.byref(w), _p(packed),
+                                   packed.numel() * packed.element_size(), _stream(stream))
+    _check(st, "llatte_summary_pack")
+
+
+def llatte_summaries_workspace_size(desc, B):
+    return lib().llatte_summaries_workspace_size(ctypes.byref(desc), B)
+
+
+def llatte_summaries(desc, packed, z, B, out, workspace, stream=None):
+    st = lib().llatte_summaries(ctypes.byref(desc), _p(packed), _p(z), B, _p(out),
+                                _p(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(stream))
+    _check(st, "llatte_summaries")
 
 
 def llatte_last_error():

@@ -9,11 +9,12 @@ import torch
 from . import llatte as C
 
 
-def make_desc(cfg):
+def make_desc(cfg, raw_readout=False):
     """llatte_model_desc from a workload description with the attributes
     d, h, dk, r, N, n_q, d_c, dtype ('f32'/'bf16'), norm_mode ('pre'/'post'),
     latent_norm, eps, pyramid (kind/values/floor/start/end), n_seeds, d_out
-    and (optional) r_q."""
+    and (optional) r_q. raw_readout: the readout returns Flatten(Z_raw)
+    ([B, n_seeds*d]) instead of its W_p projection."""
     d = C.llatte_model_desc()
     d.d, d.n_heads, d.head_dim, d.rank = cfg.d, cfg.h, cfg.dk, cfg.r
     d.d_ff = 4 * cfg.d
@@ -38,6 +39,9 @@ def make_desc(cfg):
         raise ValueError(rule.kind)
     d.n_seeds, d.d_out = cfg.n_seeds, cfg.d_out
     d.flags = 0
+    if raw_readout and cfg.n_seeds > 0:
+        d.flags = C.LLATTE_FLAG_RAW_READOUT
+        d.d_out = cfg.n_seeds * cfg.d
     d.q_rank = getattr(cfg, "r_q", 0)
     return d
 
@@ -53,9 +57,10 @@ class DeviceModel:
     _LAYER_KEYS = ("g1", "W_dkv", "g_c", "W_uq", "W_uk", "W_uv", "W_o", "g2",
                    "W1", "W2", "W_dq", "g_q")
 
-    def __init__(self, cfg, W, device="cuda"):
+    def __init__(self, cfg, W, device="cuda", raw_readout=False):
         self.cfg = cfg
-        self.desc = make_desc(cfg)
+        self.desc = make_desc(cfg, raw_readout)
+        self.raw_readout = raw_readout
         self.device = device
         self._keep = []
         dt = torch_dtype(cfg)
@@ -89,7 +94,8 @@ class DeviceModel:
         if cfg.n_seeds > 0:
             w.seeds = vec(W["seeds"]).data_ptr()
             w.readout = layer(W["readout"])
-            w.W_p = mat(W["W_p"]).data_ptr()
+            if not raw_readout:
+                w.W_p = mat(W["W_p"]).data_ptr()
         self.weights = w
         self._ws = None
         self.packed = None
@@ -124,7 +130,7 @@ class DeviceModel:
                      if cfg.n_q else None),
             "hist": torch.empty(max(self.out_hist_rows(lengths), 1), cfg.d, device=dev),
             "hist_offsets": torch.empty(B + 1, dtype=torch.int32, device=dev),
-            "emb": (torch.empty(B, cfg.d_out, device=dev) if cfg.n_seeds else None),
+            "emb": (torch.empty(B, self.desc.d_out, device=dev) if cfg.n_seeds else None),
         }
         return out
 

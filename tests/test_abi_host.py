@@ -64,7 +64,7 @@ def test_invalid_descriptors_rejected_on_host(L):
     assert L.llatte_mla_forward_workspace_size(good, 4, 100, 50) > 0
     for field, val in [("d_ff", 3 * cfg.d), ("rank", 96), ("dtype", 7),
                        ("n_layers", 0), ("head_dim", 12), ("head_dim", 48),
-                       ("flags", 1), ("q_rank", 12), ("q_rank", -8),
+                       ("flags", 2), ("q_rank", 12), ("q_rank", -8),
                        ("q_rank", 1032)]:
         d = make_desc(cfg)
         setattr(d, field, val)

@@ -51,7 +51,7 @@ __all__ = [
     "rmsnorm", "gelu", "softmax_masked", "pyramid_list", "pyramid_counts",
     "compact", "history_query_mask", "mla_layer", "fuse_queries", "forward",
     "token_embed", "latent_attention", "unmasked_pairs", "flop_count",
-    "lora_mlp_summaries",
+    "lora_mlp_summaries", "latent_attention_backward",
 ]
 
 
@@ -377,6 +377,52 @@ def latent_attention(q_lat, c_lat, kv_offsets, hq_offsets, n_cand, scale):
             out[rows, hh, :] = (e / tot) @ C
             lse[rows, hh] = (m + np.log(tot))[:, 0]
     return out, lse
+
+
+def latent_attention_backward(q_lat, c_lat, kv_offsets, hq_offsets, n_cand, scale,
+                              d_out):
+    """Gradients of latent_attention's output with respect to q_lat and c_lat.
+
+    [LLaTTE] mentions training with FlashAttention; this is the backward of
+    the attention core in latent space (the derivative of the definition,
+    written out): per user and head, with p = softmax over the allowed keys
+    of s = scale * q . C_j and out = sum_j p_j C_j,
+        dp_j = d_out . C_j,   D = d_out . out,   ds_j = p_j (dp_j - D),
+        d_q  = scale * sum_j ds_j C_j,
+        d_C_j += p_j d_out + scale * ds_j q      (over every query row and
+                                                  head that sees key j; C is
+                                                  both key and value).
+    Returns (d_q [Mtot, h, r], d_c [Ktot, r]).
+    """
+    kv_offsets = np.asarray(kv_offsets, dtype=np.int64)
+    hq_offsets = np.asarray(hq_offsets, dtype=np.int64)
+    B = kv_offsets.size - 1
+    nc = B * n_cand
+    h = q_lat.shape[1]
+    d_q = np.zeros_like(q_lat)
+    d_c = np.zeros_like(c_lat)
+    for u in range(B):
+        C = c_lat[kv_offsets[u]:kv_offsets[u + 1]]
+        K = C.shape[0]
+        n = int(hq_offsets[u + 1] - hq_offsets[u])
+        rows = list(range(nc + hq_offsets[u], nc + hq_offsets[u + 1])) + \
+            list(range(u * n_cand, (u + 1) * n_cand))
+        allowed = history_query_mask(K, n, n_cand)
+        for hh in range(h):
+            q = q_lat[rows, hh, :]
+            g = d_out[rows, hh, :]
+            s = (q @ C.T) * scale
+            z = np.where(allowed, s, -np.inf)
+            m = np.max(z, axis=1, keepdims=True)
+            e = np.where(allowed, np.exp(z - m), 0.0)
+            p = e / e.sum(axis=1, keepdims=True)
+            o = p @ C
+            dp = g @ C.T
+            D = np.sum(g * o, axis=1, keepdims=True)
+            ds = p * (dp - D)
+            d_q[rows, hh, :] = scale * (ds @ C)
+            d_c[kv_offsets[u]:kv_offsets[u + 1]] += p.T @ g + scale * (ds.T @ q)
+    return d_q, d_c
 
 
 # ---------------------------------------------------------------- counting

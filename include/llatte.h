@@ -253,6 +253,34 @@ llatte_status llatte_mla_attention(
     int32_t Mtot, int32_t Ktot, void* out, float* lse, void* workspace,
     size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * llatte_mla_attention_backward -- gradients of llatte_mla_attention's
+ * output with respect to q_lat and c_lat: the training backward of the
+ * attention core of [LLaTTE] A.3 (C is both key and value), i.e. the
+ * derivative of the definition above:
+ *   p_k   = exp(scale q_lat[i,j,:] . C_k - lse[i,j])      (allowed keys)
+ *   D     = d_out[i,j,:] . out[i,j,:]
+ *   ds_k  = p_k (d_out[i,j,:] . C_k - D)
+ *   d_q[i,j,:] = scale sum_k ds_k C_k
+ *   d_c[k,:]   = sum over rows i and heads j that see key k of
+ *                (p_k d_out[i,j,:] + scale ds_k q_lat[i,j,:])
+ * Rows, masks, q_lat, c_lat, offsets, B, Mtot and Ktot as in
+ * llatte_mla_attention; out and lse are that call's outputs (lse required);
+ * d_out [Mtot, h, r] float32; d_q [Mtot, h, r] and d_c [Ktot, r] float32
+ * are overwritten (d_c rows of every user, d_q rows of every query row).
+ * max_len (host) must be >= every K_u: a smaller value leaves part of d_q
+ * and d_c unwritten (no access outside the buffers). The softmax is
+ * recomputed from lse, so no workspace is needed. Device pointers 16-byte
+ * aligned. Errors: LLATTE_ERR_UNSUPPORTED unless dtype is BF16 and r is 64
+ * or 128; LLATTE_ERR_INVALID_ARG for NULL or misaligned pointers or bad
+ * sizes; LLATTE_ERR_HIP if a launch fails. Nothing is enqueued on error.
+ * ---------------------------------------------------------------------- */
+llatte_status llatte_mla_attention_backward(
+    const llatte_attn_desc* a, const void* q_lat, const void* c_lat,
+    const int32_t* kv_offsets, const int32_t* hq_offsets, int32_t B,
+    int32_t Mtot, int32_t Ktot, int32_t max_len, const float* out,
+    const float* lse, const float* d_out, float* d_q, float* d_c, void* stream);
+
 size_t llatte_mla_attention_workspace_size(const llatte_attn_desc* a,
                                            int32_t B, int32_t Mtot,
                                            int32_t Ktot);

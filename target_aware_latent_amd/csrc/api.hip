@@ -1359,4 +1359,41 @@ llatte_status llatte_summaries(const llatte_summary_desc* desc, const void* pack
   return LLATTE_OK;
 }
 
+
+// ---------------------------------------------------------------- attention backward
+llatte_status llatte_mla_attention_backward(
+    const llatte_attn_desc* a, const void* q_lat, const void* c_lat,
+    const int32_t* kv_offsets, const int32_t* hq_offsets, int32_t B,
+    int32_t Mtot, int32_t Ktot, int32_t max_len, const float* out,
+    const float* lse, const float* d_out, float* d_q, float* d_c, void* stream) {
+  if (!a) return fail(LLATTE_ERR_INVALID_ARG, "NULL descriptor");
+  if (a->dtype != LLATTE_BF16) return fail(LLATTE_ERR_UNSUPPORTED, "the backward is BF16 only");
+  if (a->rank != 64 && a->rank != 128)
+    return fail(LLATTE_ERR_UNSUPPORTED, "the backward needs rank 64 or 128");
+  if (a->n_heads < 1 || a->n_cand < 0 || B < 1 || Ktot < B || max_len < 1 || Mtot < 0)
+    return fail(LLATTE_ERR_INVALID_ARG, "bad sizes");
+  const void* ptrs[] = {q_lat, c_lat, kv_offsets, hq_offsets, out, lse, d_out, d_q, d_c};
+  for (const void* p : ptrs) {
+    if (!p) return fail(LLATTE_ERR_INVALID_ARG, "NULL pointer");
+    if (!aligned16(p)) return fail(LLATTE_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  }
+  AttnBwdParams p;
+  p.q = q_lat;
+  p.c = c_lat;
+  p.out = out;
+  p.lse = lse;
+  p.dout = d_out;
+  p.dq = d_q;
+  p.dc = d_c;
+  p.kv_off = kv_offsets;
+  p.hq_off = hq_offsets;
+  p.B = B;
+  p.n_cand = a->n_cand;
+  p.h = a->n_heads;
+  p.r = a->rank;
+  p.scale = a->scale;
+  HIP_TRY(attention_backward(p, max_len, (hipStream_t)stream));
+  return LLATTE_OK;
+}
+
 }  // extern "C"

@@ -127,6 +127,24 @@ struct ActionConcat {
 };
 hipError_t action_concat(const ActionConcat& p, bool bf16, hipStream_t s);
 
+// ------------------------------------------------------------------ attention backward
+// Gradients of the latent attention core (bf16 q / c, fp32 out, lse, dout;
+// fp32 dq [Mtot, h, r] and dc [Ktot, r]); rows and masks as the forward.
+struct AttnBwdParams {
+  const void* q = nullptr;     // [Mtot, h, r] bf16
+  const void* c = nullptr;     // [Ktot, r] bf16
+  const float* out = nullptr;  // [Mtot, h, r]
+  const float* lse = nullptr;  // [Mtot, h] natural log
+  const float* dout = nullptr; // [Mtot, h, r]
+  float* dq = nullptr;
+  float* dc = nullptr;
+  const int* kv_off = nullptr;
+  const int* hq_off = nullptr;
+  int B = 0, n_cand = 0, h = 0, r = 0;
+  float scale = 1.f;
+};
+hipError_t attention_backward(const AttnBwdParams& p, int max_len, hipStream_t s);
+
 // ------------------------------------------------------------------ summaries
 // out[k] = (W + A[k] Bm[k])^T in the dtype: W [rows, cols], A [K, rows,
 // rank], Bm [K, rank, cols], out [K, cols, rows].

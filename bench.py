@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3]
     python bench.py --workload actions     (the action tokenization)
     python bench.py --workload summaries   (the LoRAMLP sequence summaries)
+    python bench.py --workload backward    (the attention-core backward)
 
 One step is one llatte_mla_forward over one batch of the workload (all
 layers, the pyramid, the readout), inputs and weights already resident in
@@ -334,6 +335,146 @@ def bench_summaries(args):
     print(json.dumps(rec))
 
 
+BACKWARD_METRIC = ("user-sequences/sec + TFLOP/s (% MFMA bf16 peak), attention-core backward "
+                   "of the MLA stack at L=1600, 1 GPU")
+BACKWARD_TEXT = ("c3 attention cores: d_q and d_C of the six causal layers (64 users, keys "
+                 "1600-1600-800-400-200-100, query rows 1600-800-400-200-100-50) and the "
+                 "4-seed readout over 50 keys, 8 heads, r=128, bf16")
+
+
+def backward_layers(cfg):
+    """(K per user, history query rows per user, candidate rows per user) of
+    every attention core of the stack, all users of one length."""
+    keep = [int(x) for x in cfg.pyramid.values]
+    K = cfg.L
+    out = []
+    for n in keep:
+        out.append((K, n, cfg.n_q))
+        K = n
+    if cfg.n_seeds:
+        out.append((K, 0, cfg.n_seeds))
+    return out
+
+
+def bench_backward(args):
+    import torch
+    from oracle import llatte_oracle as O
+    from target_aware_latent_amd import llatte as C
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    cfg = synth.get_config("c3")
+    h, r, B = cfg.h, cfg.r, cfg.B
+    scale = 1.0 / math.sqrt(cfg.dk)
+    rng = np.random.default_rng(0)
+    stream = torch.cuda.current_stream()
+    layers = []
+    flops = {"attn_bwd_dq": 0, "attn_bwd_dc": 0}
+    for K, n, nc in backward_layers(cfg):
+        kv = np.arange(B + 1, dtype=np.int32) * K
+        hq = np.arange(B + 1, dtype=np.int32) * n
+        Mtot, Ktot = B * (nc + n), B * K
+        ad = C.llatte_attn_desc(h, r, nc, C.LLATTE_BF16, scale)
+        q = torch.from_numpy(synth.round_bf16(rng.standard_normal((Mtot, h, r)) * 0.5)
+                             .astype(np.float32)).cuda().to(torch.bfloat16)
+        c = torch.from_numpy(synth.round_bf16(rng.standard_normal((Ktot, r)))
+                             .astype(np.float32)).cuda().to(torch.bfloat16)
+        g = torch.from_numpy(rng.standard_normal((Mtot, h, r)).astype(np.float32)).cuda()
+        kvd, hqd = torch.from_numpy(kv).cuda(), torch.from_numpy(hq).cuda()
+        out = torch.empty((Mtot, h, r), device="cuda")
+        lse = torch.empty((Mtot, h), device="cuda")
+        ws = torch.empty(C.llatte_mla_attention_workspace_size(ad, B, Mtot, Ktot),
+                         dtype=torch.uint8, device="cuda")
+        C.llatte_mla_attention(ad, q, c, kvd, hqd, B, Mtot, Ktot, out, lse, ws, stream=stream)
+        dq = torch.empty((Mtot, h, r), device="cuda")
+        dc = torch.empty((Ktot, r), device="cuda")
+        bws = torch.empty(C.llatte_mla_attention_backward_workspace_size(ad, Mtot),
+                          dtype=torch.uint8, device="cuda")
+        layers.append((ad, q, c, kvd, hqd, Mtot, Ktot, K, out, lse, g, dq, dc, bws))
+        # allowed (query row, key) pairs per user and head
+        pairs = B * (n * (K - n) + n * (n + 1) // 2 + nc * K)
+        flops["attn_bwd_dq"] += 6 * r * h * pairs   # S, dP = d_out C^T, d_q = dS C
+        flops["attn_bwd_dc"] += 4 * r * h * pairs   # P^T d_out and dS^T q
+    F = sum(flops.values())
+
+    def step():
+        for (ad, q, c, kvd, hqd, Mtot, Ktot, K, out, lse, g, dq, dc, bws) in layers:
+            C.llatte_mla_attention_backward(ad, q, c, kvd, hqd, B, Mtot, Ktot, K, out, lse,
+                                            g, dq, dc, bws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    C.llatte_kernel_timing_reset()
+    C.llatte_kernel_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = C.llatte_kernel_timing_read()
+    C.llatte_kernel_timing_enable(False)
+    kernels = {}
+    for name, (cnt, tot) in kt.items():
+        e = {"launches_per_step": cnt / args.steps, "ms_per_step": tot / args.steps}
+        if name in flops:
+            e["tflops"] = flops[name] / (tot / args.steps / 1e3) / 1e12
+        kernels[name] = e
+    dom = max(flops, key=lambda k: kt[k][1])
+    cnt, tot = kt[dom]
+    # the launches differ in size (one per layer): per launch = the step's
+    # algorithmic FLOPs of the kernel over its launches, against the mean
+    # launch duration
+    per_launch = flops[dom] / (cnt / args.steps)
+    achieved = per_launch / (tot / cnt / 1e3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": per_launch, "avg_launch_ms": round(tot / cnt, 4)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        # whole users through every attention core, fp64 oracle, until ~12 s
+        # (the rows of the first users of each layer's synthetic inputs)
+        qs, cs = [], []
+        for (ad, q, c, kvd, hqd, Mtot, Ktot, K, out, lse, g, dq, dc, bws) in layers:
+            nq = Mtot // B
+            qs.append((q[:2 * nq].float().cpu().numpy().astype(np.float64),
+                       g[:2 * nq].cpu().numpy().astype(np.float64)))
+            cs.append(c[:2 * K].float().cpu().numpy().astype(np.float64))
+        t0 = time.perf_counter()
+        users = 0
+        while time.perf_counter() - t0 < 12.0 and users < B:
+            for li, (K, n, nc) in enumerate(backward_layers(cfg)):
+                (qa, ga), ca = qs[li], cs[li]
+                # one user: its candidate rows are the first nc, history after
+                O.latent_attention_backward(qa[:nc + n], ca[:K], [0, K], [0, n], nc, scale,
+                                            ga[:nc + n])
+            users += 1
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(users / dt, 3), "unit": "user-sequences/s",
+               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"{users} of {B} users through all {len(layers)} attention-core "
+                         f"backwards, fp64 oracle, {dt:.1f} s"}
+    rec = {
+        "metric": BACKWARD_METRIC, "value": round(B / (ms_step / 1e3), 1),
+        "unit": "user-sequences/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (N(0,1/4) bf16 latent queries, N(0,1) bf16 latent, N(0,1) d_out)",
+        "config": {"workload": BACKWARD_TEXT, "global_batch": B, "seq_len": cfg.L,
+                   "parallelism": "single GPU"},
+        "tflops": round(F / (ms_step / 1e3) / 1e12, 2),
+        "pct_peak": round(100 * F / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+    }
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -350,10 +491,11 @@ def main():
                     help="profile summary whose RECORD line holds the measured "
                          "HBM bytes per launch of the dominant kernel (written "
                          "by target_aware_latent_amd.profsum traffic)")
-    ap.add_argument("--workload", default="stack", choices=["stack", "actions", "summaries"],
+    ap.add_argument("--workload", default="stack", choices=["stack", "actions", "summaries", "backward"],
                     help="stack: the MLA forward (default); actions: the action "
                          "tokenization that builds the history tokens; summaries: the "
-                         "LoRAMLP sequence summaries of the readout")
+                         "LoRAMLP sequence summaries of the readout; backward: the attention-core "
+                         "backward of every layer of the stack")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
@@ -365,6 +507,9 @@ def main():
         return
     if args.workload == "summaries":
         bench_summaries(args)
+        return
+    if args.workload == "backward":
+        bench_backward(args)
         return
 
     import torch

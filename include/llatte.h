@@ -270,16 +270,27 @@ llatte_status llatte_mla_attention(
  * are overwritten (d_c rows of every user, d_q rows of every query row).
  * max_len (host) must be >= every K_u: a smaller value leaves part of d_q
  * and d_c unwritten (no access outside the buffers). The softmax is
- * recomputed from lse, so no workspace is needed. Device pointers 16-byte
- * aligned. Errors: LLATTE_ERR_UNSUPPORTED unless dtype is BF16 and r is 64
- * or 128; LLATTE_ERR_INVALID_ARG for NULL or misaligned pointers or bad
- * sizes; LLATTE_ERR_HIP if a launch fails. Nothing is enqueued on error.
+ * recomputed from lse. workspace: device memory of at least
+ * llatte_mla_attention_backward_workspace_size(a, Mtot) bytes, caller-owned
+ * (it holds D and d_out split into two bf16 parts between the two kernels).
+ * With Mtot = 0, d_c is zeroed and q_lat, out, lse, d_out, d_q and workspace
+ * may be NULL. Device pointers 16-byte aligned. Errors:
+ * LLATTE_ERR_UNSUPPORTED unless dtype is BF16 and r is 64 or 128;
+ * LLATTE_ERR_INVALID_ARG for NULL or misaligned pointers or bad sizes;
+ * LLATTE_ERR_WORKSPACE if workspace_bytes is too small; LLATTE_ERR_HIP if a
+ * launch fails. Nothing is enqueued on an argument error.
  * ---------------------------------------------------------------------- */
 llatte_status llatte_mla_attention_backward(
     const llatte_attn_desc* a, const void* q_lat, const void* c_lat,
     const int32_t* kv_offsets, const int32_t* hq_offsets, int32_t B,
     int32_t Mtot, int32_t Ktot, int32_t max_len, const float* out,
-    const float* lse, const float* d_out, float* d_q, float* d_c, void* stream);
+    const float* lse, const float* d_out, float* d_q, float* d_c,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of llatte_mla_attention_backward (host only; 0 if the
+ * descriptor is invalid). */
+size_t llatte_mla_attention_backward_workspace_size(const llatte_attn_desc* a,
+                                                    int32_t Mtot);
 
 size_t llatte_mla_attention_workspace_size(const llatte_attn_desc* a,
                                            int32_t B, int32_t Mtot,

@@ -1365,17 +1365,23 @@ llatte_status llatte_mla_attention_backward(
     const llatte_attn_desc* a, const void* q_lat, const void* c_lat,
     const int32_t* kv_offsets, const int32_t* hq_offsets, int32_t B,
     int32_t Mtot, int32_t Ktot, int32_t max_len, const float* out,
-    const float* lse, const float* d_out, float* d_q, float* d_c, void* stream) {
+    const float* lse, const float* d_out, float* d_q, float* d_c, void* workspace,
+    size_t workspace_bytes, void* stream) {
   if (!a) return fail(LLATTE_ERR_INVALID_ARG, "NULL descriptor");
   if (a->dtype != LLATTE_BF16) return fail(LLATTE_ERR_UNSUPPORTED, "the backward is BF16 only");
   if (a->rank != 64 && a->rank != 128)
     return fail(LLATTE_ERR_UNSUPPORTED, "the backward needs rank 64 or 128");
   if (a->n_heads < 1 || a->n_cand < 0 || B < 1 || Ktot < B || max_len < 1 || Mtot < 0)
     return fail(LLATTE_ERR_INVALID_ARG, "bad sizes");
-  const void* ptrs[] = {q_lat, c_lat, kv_offsets, hq_offsets, out, lse, d_out, d_q, d_c};
-  for (const void* p : ptrs) {
-    if (!p) return fail(LLATTE_ERR_INVALID_ARG, "NULL pointer");
-    if (!aligned16(p)) return fail(LLATTE_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  // with no query rows only d_C is written (zeros): the row buffers may be NULL
+  const void* ptrs[] = {c_lat, kv_offsets, hq_offsets, d_c, q_lat, out, lse, d_out, d_q, workspace};
+  const int nreq = Mtot == 0 ? 4 : 10;
+  for (int i = 0; i < 10; ++i) {
+    if (!ptrs[i]) {
+      if (i < nreq) return fail(LLATTE_ERR_INVALID_ARG, "NULL pointer");
+      continue;
+    }
+    if (!aligned16(ptrs[i])) return fail(LLATTE_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   }
   AttnBwdParams p;
   p.q = q_lat;
@@ -1391,9 +1397,17 @@ llatte_status llatte_mla_attention_backward(
   p.n_cand = a->n_cand;
   p.h = a->n_heads;
   p.r = a->rank;
+  p.Mtot = Mtot;
   p.scale = a->scale;
-  HIP_TRY(attention_backward(p, max_len, (hipStream_t)stream));
+  if (workspace_bytes < attention_backward_workspace(Mtot, a->n_heads, a->rank))
+    return fail(LLATTE_ERR_WORKSPACE, "backward workspace too small");
+  HIP_TRY(attention_backward(p, max_len, workspace, (hipStream_t)stream));
   return LLATTE_OK;
+}
+
+size_t llatte_mla_attention_backward_workspace_size(const llatte_attn_desc* a, int32_t Mtot) {
+  if (!a || a->n_heads < 1 || a->rank < 1 || Mtot < 0) return 0;
+  return attention_backward_workspace(Mtot, a->n_heads, a->rank);
 }
 
 }  // extern "C"

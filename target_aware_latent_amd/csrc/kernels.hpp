@@ -141,9 +141,18 @@ struct AttnBwdParams {
   const int* kv_off = nullptr;
   const int* hq_off = nullptr;
   int B = 0, n_cand = 0, h = 0, r = 0;
+  long long Mtot = 0;
   float scale = 1.f;
+  // set by attention_backward from the workspace: d_out as bf16 high and
+  // low parts [Mtot, h, r], D = d_out . out [Mtot, h]
+  bf16* ws_ghi = nullptr;
+  bf16* ws_glo = nullptr;
+  float* ws_d = nullptr;
+  bool dc_accumulate = false;  // d_C from two head groups, added onto zero
 };
-hipError_t attention_backward(const AttnBwdParams& p, int max_len, hipStream_t s);
+// Workspace bytes of attention_backward.
+size_t attention_backward_workspace(long long Mtot, int h, int r);
+hipError_t attention_backward(AttnBwdParams p, int max_len, void* ws, hipStream_t s);
 
 // ------------------------------------------------------------------ summaries
 // out[k] = (W + A[k] Bm[k])^T in the dtype: W [rows, cols], A [K, rows,

@@ -131,7 +131,9 @@ _SIGS = {
         ctypes.POINTER(llatte_summary_desc), _vp, _vp, _c_int, _vp, _vp, ctypes.c_size_t, _vp]),
     "llatte_mla_attention_backward": (_c_int, [
         ctypes.POINTER(llatte_attn_desc), _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
-        _c_int, _vp, _vp, _vp, _vp, _vp, _vp]),
+        _c_int, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "llatte_mla_attention_backward_workspace_size": (ctypes.c_size_t, [
+        ctypes.POINTER(llatte_attn_desc), _c_int]),
     "llatte_last_error": (ctypes.c_char_p, []),
     "llatte_version": (_c_int, []),
     "llatte_kernel_timing_enable": (None, [_c_int]),
@@ -306,11 +308,18 @@ def llatte_summaries(desc, packed, z, B, out, workspace, stream=None):
     _check(st, "llatte_summaries")
 
 
+def llatte_mla_attention_backward_workspace_size(desc, Mtot):
+    return lib().llatte_mla_attention_backward_workspace_size(ctypes.byref(desc), Mtot)
+
+
 def llatte_mla_attention_backward(desc, q_lat, c_lat, kv_offsets, hq_offsets, B, Mtot,
-                                  Ktot, max_len, out, lse, d_out, d_q, d_c, stream=None):
+                                  Ktot, max_len, out, lse, d_out, d_q, d_c, workspace,
+                                  stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().llatte_mla_attention_backward(
         ctypes.byref(desc), _p(q_lat), _p(c_lat), _p(kv_offsets), _p(hq_offsets), B, Mtot,
-        Ktot, max_len, _p(out), _p(lse), _p(d_out), _p(d_q), _p(d_c), _stream(stream))
+        Ktot, max_len, _p(out), _p(lse), _p(d_out), _p(d_q), _p(d_c), _p(workspace), nbytes,
+        _stream(stream))
     _check(st, "llatte_mla_attention_backward")
 
 

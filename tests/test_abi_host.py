@@ -102,6 +102,30 @@ def test_forward_argument_errors_return_status_without_launch(L):
     assert st == L.LLATTE_ERR_INVALID_ARG
 
 
+def test_attention_backward_argument_errors(L):
+    # every case fails validation before anything is enqueued (fake pointers
+    # are never dereferenced on these paths)
+    bw = L.lib().llatte_mla_attention_backward
+    fake = ctypes.c_void_p(1 << 20)
+    ad = L.llatte_attn_desc(8, 96, 0, L.LLATTE_BF16, 0.125)
+    args = [fake] * 4 + [2, 10, 10, 5] + [fake] * 6
+    assert bw(ctypes.byref(ad), *args, 1 << 30, None) == L.LLATTE_ERR_UNSUPPORTED
+    ad = L.llatte_attn_desc(8, 128, 0, L.LLATTE_F32, 0.125)
+    assert bw(ctypes.byref(ad), *args, 1 << 30, None) == L.LLATTE_ERR_UNSUPPORTED
+    ad = L.llatte_attn_desc(8, 128, 0, L.LLATTE_BF16, 0.125)
+    need = L.llatte_mla_attention_backward_workspace_size(ad, 10)
+    assert need >= 10 * 8 * 128 * 4 + 10 * 8 * 4
+    assert bw(ctypes.byref(ad), *args, need - 1, None) == L.LLATTE_ERR_WORKSPACE
+    nul = [fake] * 4 + [2, 10, 10, 5] + [fake] * 4 + [None, fake]
+    assert bw(ctypes.byref(ad), *nul, need, None) == L.LLATTE_ERR_INVALID_ARG
+    assert "NULL" in L.llatte_last_error()
+    mis = [fake] * 4 + [2, 10, 10, 5] + [fake] * 5 + [ctypes.c_void_p((1 << 20) + 4)]
+    assert bw(ctypes.byref(ad), *mis, need, None) == L.LLATTE_ERR_INVALID_ARG
+    assert "aligned" in L.llatte_last_error()
+    bad = [fake] * 4 + [0, 10, 10, 5] + [fake] * 6
+    assert bw(ctypes.byref(ad), *bad, need, None) == L.LLATTE_ERR_INVALID_ARG
+
+
 def _rule(L, r):
     from target_aware_latent_amd.model import make_desc
     cfg = synth.Config("x", B=1, L=1, len_range=None, d=8, h=1, dk=8, r=8,

@@ -48,8 +48,10 @@ def run_backward(h, r, K, n, n_cand, seed=0):
     C.llatte_mla_attention(ad, qd, cd, idev(kv), idev(hq), B, Mtot, Ktot, out, lse, ws)
     d_q = torch.full((Mtot, h, r), float("nan"), device="cuda")
     d_c = torch.full((Ktot, r), float("nan"), device="cuda")
+    bws = torch.empty(C.llatte_mla_attention_backward_workspace_size(ad, Mtot), dtype=torch.uint8,
+                      device="cuda")
     C.llatte_mla_attention_backward(ad, qd, cd, idev(kv), idev(hq), B, Mtot, Ktot, int(K.max()),
-                                    out, lse, dev(g), d_q, d_c)
+                                    out, lse, dev(g), d_q, d_c, bws)
     torch.cuda.synchronize()
     rq, rc = O.latent_attention_backward(q.astype(np.float64), Cl.astype(np.float64), kv, hq,
                                          n_cand, scale, g.astype(np.float64))
@@ -62,6 +64,8 @@ CASES = [
     (8, 128, [300, 129, 1], [300, 64, 1], 0),
     (8, 128, [700, 50], [300, 50], 5),
     (2, 64, [90, 260], [90, 17], 2),
+    (3, 128, [130, 5, 257], [100, 5, 0], 3),   # odd head count: one head group
+    (1, 64, [64, 129], [64, 129], 0),
 ]
 
 
@@ -90,3 +94,19 @@ def test_upstream_layer_one_shape():
     dq, dc, rq, rc, _ = run_backward(8, 128, [1600, 1600], [1600, 1600], 0, seed=1)
     assert _err(dq, rq) <= 2e-2
     assert _err(dc, rc) <= 2e-2
+
+
+def test_no_query_rows_zero_the_latent_gradient():
+    # every user with n = 0 and no candidates: Mtot = 0, d_c = 0, and the
+    # row buffers may be NULL
+    import torch
+    from target_aware_latent_amd import llatte as C
+    ad = C.llatte_attn_desc(4, 128, 0, C.LLATTE_BF16, 0.125)
+    kv = torch.tensor([0, 5, 14], dtype=torch.int32, device="cuda")
+    hq = torch.zeros(3, dtype=torch.int32, device="cuda")
+    cl = torch.randn(14, 128, device="cuda").to(torch.bfloat16)
+    d_c = torch.full((14, 128), float("nan"), device="cuda")
+    C.llatte_mla_attention_backward(ad, None, cl, kv, hq, 2, 0, 14, 9, None, None, None, None,
+                                    d_c, None)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(d_c).item() == 0

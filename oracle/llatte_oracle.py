@@ -51,7 +51,7 @@ __all__ = [
     "rmsnorm", "gelu", "softmax_masked", "pyramid_list", "pyramid_counts",
     "compact", "history_query_mask", "mla_layer", "fuse_queries", "forward",
     "token_embed", "latent_attention", "unmasked_pairs", "flop_count",
-    "lora_mlp_summaries", "latent_attention_backward",
+    "lora_mlp_summaries", "latent_attention_backward", "ffn_block_backward",
 ]
 
 
@@ -426,6 +426,41 @@ def latent_attention_backward(q_lat, c_lat, kv_offsets, hq_offsets, n_cand, scal
 
 
 # ---------------------------------------------------------------- counting
+
+def ffn_block_backward(R1, g2, W1, W2, d_out, eps=1e-6):
+    """Gradients of the pre-norm FFN sublayer of the [LLaTTE] A.2 layer
+    equation (pre-norm reading), R2 = R1 + GELU(RMSNorm(R1) g2 W1) W2,
+    row-wise over the rows of R1 [M, d], given d_out = dL/dR2 [M, d].
+
+    [LLaTTE] trains the model (FlashAttention on H100s is mentioned); this
+    is the derivative of the definition, written out step by step:
+        s = (mean(R1^2) + eps)^-1/2 per row,  xh = R1 s,  H2 = xh g2,
+        A = H2 W1,  G = GELU(A),
+        dW2 = G^T d_out,          dG = d_out W2^T,
+        dA  = dG * GELU'(A),      GELU'(a) = Phi(a) + a phi(a),
+        dW1 = H2^T dA,            dH2 = dA W1^T,
+        dg2 = sum over rows of dH2 * xh,   dxh = dH2 * g2,
+        dR1 = d_out + s (dxh - xh mean(dxh * xh))   (per row).
+    Returns (dR1 [M, d], dg2 [d], dW1 [d, d_ff], dW2 [d_ff, d]).
+    """
+    ms = np.mean(R1 * R1, axis=-1, keepdims=True)
+    s = 1.0 / np.sqrt(ms + eps)
+    xh = R1 * s
+    H2 = xh * g2
+    A = H2 @ W1
+    G = gelu(A)
+    dW2 = G.T @ d_out
+    dG = d_out @ W2.T
+    phi = np.exp(-0.5 * A * A) / math.sqrt(2.0 * math.pi)
+    Phi = 0.5 * (1.0 + _erf(A / math.sqrt(2.0)))
+    dA = dG * (Phi + A * phi)
+    dW1 = H2.T @ dA
+    dH2 = dA @ W1.T
+    dg2 = np.sum(dH2 * xh, axis=0)
+    dxh = dH2 * g2
+    dR1 = d_out + s * (dxh - xh * np.mean(dxh * xh, axis=-1, keepdims=True))
+    return dR1, dg2, dW1, dW2
+
 
 def unmasked_pairs(cfg, lengths):
     """Allowed (query, key) pairs per layer, counted from the explicit masks."""

@@ -4,6 +4,7 @@
     python bench.py --workload actions     (the action tokenization)
     python bench.py --workload summaries   (the LoRAMLP sequence summaries)
     python bench.py --workload backward    (the attention-core backward)
+    python bench.py --workload ffn_backward (the FFN-sublayer backward)
 
 One step is one llatte_mla_forward over one batch of the workload (all
 layers, the pyramid, the readout), inputs and weights already resident in
@@ -475,6 +476,111 @@ def bench_backward(args):
     print(json.dumps(rec))
 
 
+FFN_BWD_METRIC = ("user-sequences/sec + TFLOP/s (% MFMA bf16 peak), FFN-sublayer backward of "
+                  "the MLA stack at L=1600, 1 GPU")
+FFN_BWD_TEXT = ("c3 FFN sublayers: dR1, dg2, dW1, dW2 of the six layers' pre-norm FFN "
+                "(64 users x 1600-800-400-200-100-50 rows, d=512, d_ff=2048), bf16 products")
+
+
+def bench_ffn_backward(args):
+    import torch
+    from oracle import llatte_oracle as O
+    from target_aware_latent_amd import llatte as C
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    cfg = synth.get_config("c3")
+    d, F, B = cfg.d, cfg.d_ff, cfg.B
+    rng = np.random.default_rng(0)
+    f = C.llatte_ffn_desc(d, F, C.LLATTE_BF16, cfg.eps)
+    rows = [B * int(n) for n in cfg.pyramid.values]
+    ws = torch.empty(C.llatte_ffn_backward_workspace_size(f, max(rows)), dtype=torch.uint8,
+                     device="cuda")
+    layers = []
+    for M in rows:
+        r1 = torch.from_numpy(rng.standard_normal((M, d)).astype(np.float32)).cuda()
+        g2 = torch.ones(d, device="cuda")
+        w1 = torch.from_numpy((rng.standard_normal((d, F)) / np.sqrt(d)).astype(np.float32)).cuda()
+        w2 = torch.from_numpy((rng.standard_normal((F, d)) / np.sqrt(F)).astype(np.float32)).cuda()
+        do = torch.from_numpy(rng.standard_normal((M, d)).astype(np.float32)).cuda()
+        outs = (torch.empty((M, d), device="cuda"), torch.empty(d, device="cuda"),
+                torch.empty((d, F), device="cuda"), torch.empty((F, d), device="cuda"))
+        layers.append((M, r1, g2, w1.to(torch.bfloat16), w2.to(torch.bfloat16), do, outs))
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for (M, r1, g2, w1, w2, do, (dr1, dg2, dw1, dw2)) in layers:
+            C.llatte_ffn_backward(f, r1, g2, w1, w2, do, M, dr1, dg2, dw1, dw2, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    # algorithmic FLOPs: the four gradient products (2 M d F each); the
+    # recomputed pre-activation is not counted
+    per = {k: sum(2 * M * d * F for M in rows) for k in
+           ("gemm_bwd_dg", "gemm_bwd_dh", "gemm_bwd_dw1", "gemm_bwd_dw2")}
+    Fl = sum(per.values())
+    C.llatte_kernel_timing_reset()
+    C.llatte_kernel_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = C.llatte_kernel_timing_read()
+    C.llatte_kernel_timing_enable(False)
+    kernels = {}
+    for name, (cnt, tot) in kt.items():
+        e = {"launches_per_step": cnt / args.steps, "ms_per_step": tot / args.steps}
+        if name in per:
+            e["tflops"] = per[name] / (tot / args.steps / 1e3) / 1e12
+        kernels[name] = e
+    dom = max(per, key=lambda k: kt[k][1])
+    cnt, tot = kt[dom]
+    per_launch = per[dom] / (cnt / args.steps)
+    achieved = per_launch / (tot / cnt / 1e3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": per_launch, "avg_launch_ms": round(tot / cnt, 4)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        # whole users (1600 + 800 + ... + 50 rows) through the fp64 oracle
+        W1 = layers[0][3].float().cpu().numpy().astype(np.float64)
+        W2 = layers[0][4].float().cpu().numpy().astype(np.float64)
+        g2 = np.ones(d)
+        sample = [rng.standard_normal((int(n), d)) for n in cfg.pyramid.values]
+        t0 = time.perf_counter()
+        users = 0
+        while time.perf_counter() - t0 < 12.0 and users < B:
+            for x in sample:
+                O.ffn_block_backward(x, g2, W1, W2, x)
+            users += 1
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(users / dt, 3), "unit": "user-sequences/s",
+               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"{users} of {B} users through all {len(rows)} FFN-sublayer "
+                         f"backwards, fp64 oracle, {dt:.1f} s"}
+    rec = {
+        "metric": FFN_BWD_METRIC, "value": round(B / (ms_step / 1e3), 1),
+        "unit": "user-sequences/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (N(0,1) residual rows and d_out, N(0,1/fan_in) bf16 weights, gains 1)",
+        "config": {"workload": FFN_BWD_TEXT, "global_batch": B, "seq_len": cfg.L,
+                   "parallelism": "single GPU"},
+        "tflops": round(Fl / (ms_step / 1e3) / 1e12, 2),
+        "pct_peak": round(100 * Fl / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+    }
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -491,11 +597,12 @@ def main():
                     help="profile summary whose RECORD line holds the measured "
                          "HBM bytes per launch of the dominant kernel (written "
                          "by target_aware_latent_amd.profsum traffic)")
-    ap.add_argument("--workload", default="stack", choices=["stack", "actions", "summaries", "backward"],
+    ap.add_argument("--workload", default="stack", choices=["stack", "actions", "summaries", "backward", "ffn_backward"],
                     help="stack: the MLA forward (default); actions: the action "
                          "tokenization that builds the history tokens; summaries: the "
                          "LoRAMLP sequence summaries of the readout; backward: the attention-core "
-                         "backward of every layer of the stack")
+                         "backward of every layer of the stack; ffn_backward: the FFN-sublayer "
+                         "backward (GEMM gradients) of every layer")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
@@ -510,6 +617,9 @@ def main():
         return
     if args.workload == "backward":
         bench_backward(args)
+        return
+    if args.workload == "ffn_backward":
+        bench_ffn_backward(args)
         return
 
     import torch

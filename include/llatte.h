@@ -292,6 +292,46 @@ llatte_status llatte_mla_attention_backward(
 size_t llatte_mla_attention_backward_workspace_size(const llatte_attn_desc* a,
                                                     int32_t Mtot);
 
+/* ------------------------------------------------------------------------
+ * llatte_ffn_backward -- gradients of the pre-norm FFN sublayer of the
+ * [LLaTTE] A.2 layer equation (pre-norm reading), row-wise over M rows:
+ *   R2 = R1 + GELU(RMSNorm(R1) * g2 . W1) . W2     (exact-erf GELU, no bias)
+ * Given d_out = dL/dR2 it writes
+ *   d_r1 = dL/dR1 [M, d] (residual plus the path through norm and FFN),
+ *   d_g2 [d], d_w1 [d, d_ff], d_w2 [d_ff, d]        (all float32),
+ * recomputing RMSNorm(R1) and the pre-activation. The five products take
+ * bf16 operands with fp32 accumulation: r1 and d_out are rounded to bf16
+ * where they enter a product (the norm backward itself runs in fp32).
+ *   f            host descriptor: d (multiple of 8, <= 1024), d_ff
+ *                (multiple of 8), dtype (LLATTE_BF16 only), eps
+ *   r1, d_out    [M, d] float32;  g2 [d] float32
+ *   w1           [d, d_ff] bf16 row-major;  w2 [d_ff, d] bf16 row-major
+ *   workspace    >= llatte_ffn_backward_workspace_size(f, M) bytes,
+ *                caller-owned (recomputed activations, their transposes and
+ *                the split-K scratch)
+ * With M = 0 the weight and gain gradients are zeroed and r1, d_out, d_r1
+ * and workspace may be NULL. Device pointers 16-byte aligned. Errors:
+ * LLATTE_ERR_UNSUPPORTED for a dtype other than BF16; LLATTE_ERR_INVALID_ARG
+ * for bad sizes or NULL / misaligned pointers; LLATTE_ERR_WORKSPACE if the
+ * workspace is too small; LLATTE_ERR_HIP if a launch fails. Nothing is
+ * enqueued on an argument error.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t d;      /* model width                  */
+  int32_t d_ff;   /* FFN hidden width (4d)        */
+  int32_t dtype;  /* LLATTE_BF16                  */
+  float eps;      /* RMSNorm epsilon              */
+} llatte_ffn_desc;
+
+llatte_status llatte_ffn_backward(const llatte_ffn_desc* f, const float* r1,
+                                  const float* g2, const void* w1,
+                                  const void* w2, const float* d_out,
+                                  int32_t M, float* d_r1, float* d_g2,
+                                  float* d_w1, float* d_w2, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+size_t llatte_ffn_backward_workspace_size(const llatte_ffn_desc* f,
+                                          int32_t M);
+
 size_t llatte_mla_attention_workspace_size(const llatte_attn_desc* a,
                                            int32_t B, int32_t Mtot,
                                            int32_t Ktot);

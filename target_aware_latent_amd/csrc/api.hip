@@ -1410,4 +1410,55 @@ size_t llatte_mla_attention_backward_workspace_size(const llatte_attn_desc* a, i
   return attention_backward_workspace(Mtot, a->n_heads, a->rank);
 }
 
+static const char* check_ffn_desc(const llatte_ffn_desc* f) {
+  if (!f) return "NULL descriptor";
+  if (f->dtype != LLATTE_BF16) return "the FFN backward is BF16 only";
+  if (f->d < 8 || f->d > 1024 || f->d % 8) return "d must be a multiple of 8 in [8, 1024]";
+  if (f->d_ff < 8 || f->d_ff % 8) return "d_ff must be a positive multiple of 8";
+  if (!(f->eps >= 0.f)) return "eps must be >= 0";
+  return nullptr;
+}
+
+size_t llatte_ffn_backward_workspace_size(const llatte_ffn_desc* f, int32_t M) {
+  if (check_ffn_desc(f) || M < 0) return 0;
+  return ffn_backward_workspace(M, f->d, f->d_ff);
+}
+
+llatte_status llatte_ffn_backward(const llatte_ffn_desc* f, const float* r1, const float* g2,
+                                  const void* w1, const void* w2, const float* d_out, int32_t M,
+                                  float* d_r1, float* d_g2, float* d_w1, float* d_w2,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (const char* why = check_ffn_desc(f))
+    return fail(f && f->dtype != LLATTE_BF16 ? LLATTE_ERR_UNSUPPORTED : LLATTE_ERR_INVALID_ARG, "%s", why);
+  if (M < 0) return fail(LLATTE_ERR_INVALID_ARG, "M must be >= 0");
+  // with no rows only the weight and gain gradients (zeros) are written
+  const void* ptrs[] = {g2, w1, w2, d_g2, d_w1, d_w2, r1, d_out, d_r1, workspace};
+  const int nreq = M == 0 ? 6 : 10;
+  for (int i = 0; i < 10; ++i) {
+    if (!ptrs[i]) {
+      if (i < nreq) return fail(LLATTE_ERR_INVALID_ARG, "NULL pointer");
+      continue;
+    }
+    if (!aligned16(ptrs[i])) return fail(LLATTE_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  }
+  if (M > 0 && workspace_bytes < ffn_backward_workspace(M, f->d, f->d_ff))
+    return fail(LLATTE_ERR_WORKSPACE, "FFN backward workspace too small");
+  FfnBwdParams p;
+  p.r1 = r1;
+  p.g2 = g2;
+  p.w1 = w1;
+  p.w2 = w2;
+  p.dout = d_out;
+  p.dr1 = d_r1;
+  p.dg2 = d_g2;
+  p.dW1 = d_w1;
+  p.dW2 = d_w2;
+  p.M = M;
+  p.d = f->d;
+  p.F = f->d_ff;
+  p.eps = f->eps;
+  HIP_TRY(ffn_backward(p, workspace, (hipStream_t)stream));
+  return LLATTE_OK;
+}
+
 }  // extern "C"

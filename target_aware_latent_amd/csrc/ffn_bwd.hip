@@ -1,0 +1,327 @@
+// Backward of the pre-norm FFN sublayer ([LLaTTE] Appendix A.2 layer
+// equation, pre-norm reading): R2 = R1 + GELU(RMSNorm(R1) g2 W1) W2, over M
+// independent rows. Given d_out = dL/dR2 it produces dR1, dg2, dW1 and dW2:
+//   s = (mean(R1^2) + eps)^-1/2,  xh = R1 s,  H2 = xh g2,  A = H2 W1,
+//   dW2 = GELU(A)^T d_out,   dG = d_out W2^T,   dA = dG GELU'(A),
+//   dW1 = H2^T dA,           dH2 = dA W1^T,
+//   dg2 = sum_rows dH2 xh,   dR1 = d_out + s (dH2 g2 - xh mean(dH2 g2 xh)).
+// The forward's H2 and A are recomputed (the row norm, one product). The
+// five products run on the tiled bf16 GEMM (both operands K-contiguous):
+// the input gradients take W1 [d, d_ff] and W2 [d_ff, d] in their natural
+// row-major layout, the weight gradients contract over the rows, so their
+// operands are written transposed ([cols, M] padded to a multiple of 8 with
+// zero columns) by the kernels that produce them, and split K across the
+// GPU. The elementwise steps (the GELU derivative, the norm backward) are
+// HBM-bound kernels of their own.
+#include "kernels.hpp"
+
+namespace llatte {
+
+namespace {
+constexpr int kT = 64;  // transposing tile edge
+}
+
+// dst_t [cols, ldm] = bf16(src [M, cols])^T with zero columns m in [M, ldm);
+// dst_rm (optional) = bf16(src) row-major [M, cols]. Tiles of 64 x 64
+// through LDS (rows of 66 elements against bank conflicts on the column
+// reads); each thread moves pairs of elements, along rows on the way in and
+// along columns on the way out (cols, ld_src and ldm are even).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+template <typename S>
+__device__ __forceinline__ void load2(const S* p, float& a, float& b) {
+  if constexpr (sizeof(S) == 4) {
+    const float2 v = *(const float2*)p;
+    a = v.x;
+    b = v.y;
+  } else {
+    const bf16x2 v = *(const bf16x2*)p;
+    a = from_bf16(v[0]);
+    b = from_bf16(v[1]);
+  }
+}
+
+template <typename S>
+__global__ __launch_bounds__(256) void cast_t_kernel(const S* src, int M, int cols, int ld_src,
+                                                     bf16* dst_t, int ldm, bf16* dst_rm) {
+  __shared__ bf16 tile[kT][kT + 2];
+  const int m0 = blockIdx.x * kT, c0 = blockIdx.y * kT, tid = threadIdx.x;
+#pragma unroll 4
+  for (int i = 0; i < kT * kT / 512; ++i) {
+    const int e = tid + 256 * i, r = e / (kT / 2), c = (e % (kT / 2)) * 2, m = m0 + r, cc = c0 + c;
+    bf16x2 v{to_bf16(0.f), to_bf16(0.f)};
+    if (m < M && cc < cols) {
+      float a, b;
+      load2(src + (size_t)m * ld_src + cc, a, b);
+      v = bf16x2{to_bf16(a), to_bf16(b)};
+      if (dst_rm) *(bf16x2*)(dst_rm + (size_t)m * cols + cc) = v;
+    }
+    tile[r][c] = v[0];
+    tile[r][c + 1] = v[1];
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int i = 0; i < kT * kT / 512; ++i) {
+    const int e = tid + 256 * i, c = e / (kT / 2), r = (e % (kT / 2)) * 2, m = m0 + r, cc = c0 + c;
+    if (cc < cols && m < ldm) *(bf16x2*)(dst_t + (size_t)cc * ldm + m) = bf16x2{tile[r][c], tile[r + 1][c]};
+  }
+}
+
+// From the recomputed pre-activation A and dG = d_out W2^T, both [M, F]
+// float: dA = dG * GELU'(A) as bf16 row-major [M, F] and transposed
+// [F, ldm], and GELU(A) transposed [F, ldm] (zero columns m >= M).
+// GELU(a) = a Phi(a), GELU'(a) = Phi(a) + a phi(a) (exact erf).
+__global__ __launch_bounds__(256) void gelu_bwd_kernel(const float* A, const float* dG, int M, int F,
+                                                      bf16* dA, bf16* dAT, bf16* GT, int ldm) {
+  __shared__ bf16 tA[kT][kT + 2], tG[kT][kT + 2];
+  const int m0 = blockIdx.x * kT, c0 = blockIdx.y * kT, tid = threadIdx.x;
+#pragma unroll 4
+  for (int i = 0; i < kT * kT / 512; ++i) {
+    const int e = tid + 256 * i, r = e / (kT / 2), c = (e % (kT / 2)) * 2, m = m0 + r, cc = c0 + c;
+    bf16x2 da{to_bf16(0.f), to_bf16(0.f)}, g = da;
+    if (m < M && cc < F) {
+      const size_t o = (size_t)m * F + cc;
+      const float2 a = *(const float2*)(A + o), dg = *(const float2*)(dG + o);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float x = k ? a.y : a.x;
+        const float Phi = 0.5f * (1.f + erff(x * 0.70710678118654752f));
+        const float phi = 0.39894228040143268f * expf(-0.5f * x * x);
+        da[k] = to_bf16((k ? dg.y : dg.x) * (Phi + x * phi));
+        g[k] = to_bf16(x * Phi);
+      }
+      *(bf16x2*)(dA + o) = da;
+    }
+    tA[r][c] = da[0];
+    tA[r][c + 1] = da[1];
+    tG[r][c] = g[0];
+    tG[r][c + 1] = g[1];
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int i = 0; i < kT * kT / 512; ++i) {
+    const int e = tid + 256 * i, c = e / (kT / 2), r = (e % (kT / 2)) * 2, m = m0 + r, cc = c0 + c;
+    if (cc < F && m < ldm) {
+      *(bf16x2*)(dAT + (size_t)cc * ldm + m) = bf16x2{tA[r][c], tA[r + 1][c]};
+      *(bf16x2*)(GT + (size_t)cc * ldm + m) = bf16x2{tG[r][c], tG[r + 1][c]};
+    }
+  }
+}
+
+// RMSNorm backward with the residual, one wave per row, kNormRows rows per
+// block: s = 1 / sqrt(ss / d + eps), xh = x s, dxh = dh g,
+// dx = dres + s (dxh - xh mean(dxh xh)); and the block's partial sums of
+// dh * xh per column (the gain's gradient), summed over the block's rows in
+// row order and then over its waves in wave order.
+constexpr int kNormRows = 64;
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* x, const float* ss,
+                                                         const float* dh, const float* g,
+                                                         const float* dres, float eps, int M,
+                                                         int d, float* dx, float* dg_part) {
+  constexpr int MAXV = 4;  // d <= 1024
+  __shared__ float red[4][1024];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  f32x4 acc[MAXV], gv[MAXV];
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) {
+    acc[j] = f32x4{};
+    const int idx = j * 256 + lane * 4;
+    gv[j] = idx < d ? *(const f32x4*)(g + idx) : f32x4{};
+  }
+  const int r0 = blockIdx.x * kNormRows + wave * (kNormRows / 4);
+  for (int i = 0; i < kNormRows / 4; ++i) {
+    const int row = r0 + i;
+    if (row >= M) break;
+    const float s = 1.f / sqrtf(ss[row] / (float)d + eps);
+    f32x4 xh[MAXV], dxh[MAXV], hv[MAXV];
+    float dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) {
+      const int idx = j * 256 + lane * 4;
+      xh[j] = dxh[j] = hv[j] = f32x4{};
+      if (idx < d) {
+        xh[j] = *(const f32x4*)(x + (size_t)row * d + idx) * s;
+        hv[j] = *(const f32x4*)(dh + (size_t)row * d + idx);
+        dxh[j] = hv[j] * gv[j];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dot = fmaf(dxh[j][k], xh[j][k], dot);
+      }
+    }
+    const float mean = wave_sum(dot) / (float)d;
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) {
+      const int idx = j * 256 + lane * 4;
+      if (idx >= d) continue;
+      const f32x4 r = *(const f32x4*)(dres + (size_t)row * d + idx);
+      *(f32x4*)(dx + (size_t)row * d + idx) = r + (dxh[j] - xh[j] * mean) * s;
+      acc[j] += hv[j] * xh[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) {
+    const int idx = j * 256 + lane * 4;
+    if (idx < d) *(f32x4*)&red[wave][idx] = acc[j];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < d; c += 256)
+    dg_part[(size_t)blockIdx.x * d + c] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+}
+
+// out[c] = sum over p of part[p][c]: 64 columns per block; each of sixteen
+// thread rows sums a contiguous sixteenth of the partials in order, then the
+// sixteen sums are added in order (a fixed order: the result is
+// reproducible).
+__global__ __launch_bounds__(1024) void colsum_kernel(const float* part, int np, int d, float* out) {
+  __shared__ float q[16][64];
+  const int t = threadIdx.x & 63, ty = threadIdx.x >> 6, c = blockIdx.x * 64 + t;
+  const int per = (np + 15) / 16, p0 = ty * per, p1 = min(np, p0 + per);
+  float v = 0.f;
+  if (c < d) {
+#pragma unroll 8
+    for (int p = p0; p < p1; ++p) v += part[(size_t)p * d + c];
+  }
+  q[ty][t] = v;
+  __syncthreads();
+  if (ty == 0 && c < d) {
+    float acc = 0.f;
+    for (int i = 0; i < 16; ++i) acc += q[i][t];
+    out[c] = acc;
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(float* p, long long n) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+namespace {
+
+size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+struct FfnWs {
+  bf16 *H2, *W1T, *dOb, *dOT, *dA, *dAT, *GT, *H2T;
+  float *ss, *A, *dG, *dH2, *dg_part, *sk;
+  size_t bytes;
+};
+
+FfnWs ffn_ws(char* base, long long M, int d, int F) {
+  const size_t ldm = (size_t)((M + 7) / 8 * 8);
+  const size_t nb = (size_t)((M + kNormRows - 1) / kNormRows);
+  FfnWs w{};
+  size_t o = 0;
+  auto take = [&](size_t b) {
+    char* p = base ? base + o : nullptr;
+    o += up256(b);
+    return p;
+  };
+  w.H2 = (bf16*)take((size_t)M * d * 2);
+  w.W1T = (bf16*)take((size_t)F * d * 2);
+  w.dOb = (bf16*)take((size_t)M * d * 2);
+  w.dOT = (bf16*)take((size_t)d * ldm * 2);
+  w.dA = (bf16*)take((size_t)M * F * 2);
+  w.dAT = (bf16*)take((size_t)F * ldm * 2);
+  w.GT = (bf16*)take((size_t)F * ldm * 2);
+  w.H2T = (bf16*)take((size_t)d * ldm * 2);
+  w.ss = (float*)take((size_t)M * 4);
+  w.A = (float*)take((size_t)M * F * 4);
+  w.dG = (float*)take((size_t)M * F * 4);
+  w.dH2 = (float*)take((size_t)M * d * 4);
+  w.dg_part = (float*)take(nb * d * 4);
+  w.sk = (float*)take((size_t)kFfnSkPart * 4);
+  w.bytes = o;
+  return w;
+}
+
+GemmParams plain_gemm(const void* A, int lda, const void* B, int ldb, int M, int N, int K, float* C,
+                      int ldc, const char* name, float* sk) {
+  GemmParams g;
+  g.A = A;
+  g.lda = lda;
+  g.B = B;
+  g.ldb = ldb;
+  g.M_cap = M;
+  g.N = N;
+  g.K = K;
+  g.epi = EPI_STORE_F32;
+  g.C = C;
+  g.ldc = ldc;
+  g.name = name;
+  g.sk_part = sk;
+  g.sk_part_cap = kFfnSkPart;
+  return g;
+}
+
+}  // namespace
+
+size_t ffn_backward_workspace(long long M, int d, int F) { return ffn_ws(nullptr, M, d, F).bytes; }
+
+hipError_t ffn_backward(const FfnBwdParams& p, void* ws, hipStream_t s) {
+  const long long M = p.M;
+  const int d = p.d, F = p.F;
+  if (M <= 0) {
+    // no rows: the weight gradients are zero (a fill kernel, so that the
+    // call stays capturable in a graph)
+    const long long n = (long long)d * F;
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p.dW1, n);
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p.dW2, n);
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((d + 255) / 256)), dim3(256), 0, s, p.dg2,
+                       (long long)d);
+    return hipGetLastError();
+  }
+  const int ldm = (int)((M + 7) / 8 * 8);
+  FfnWs w = ffn_ws((char*)ws, M, d, F);
+  hipError_t e;
+  // H2 = RMSNorm(R1) g2 (bf16) and the rows' sums of squares
+  if ((e = norm_rows(RowSrc{p.r1, p.r1, 0, d}, (int)M, nullptr, p.g2, p.eps, nullptr, 0, w.H2, d,
+                     d, K_BF16, s, w.ss)))
+    return e;
+  // W1^T [F, d] for the recomputed A = H2 W1
+  if ((e = transpose(p.w1, d, F, F, 0, w.W1T, d, 0, 1, K_BF16, K_BF16, s))) return e;
+  if ((e = gemm(plain_gemm(w.H2, d, w.W1T, d, (int)M, F, d, w.A, F, "gemm_bwd_a", nullptr), true, s)))
+    return e;
+  // d_out as bf16, row-major and transposed
+  {
+    const dim3 grid((ldm + kT - 1) / kT, (d + kT - 1) / kT);
+    timing_begin("cast_t", s);
+    hipLaunchKernelGGL(cast_t_kernel<float>, grid, dim3(256), 0, s, p.dout, (int)M, d, d, w.dOT,
+                       ldm, w.dOb);
+    timing_end(s);
+    if ((e = hipGetLastError())) return e;
+  }
+  // dG = d_out W2^T: B = W2 [F, d] as stored
+  if ((e = gemm(plain_gemm(w.dOb, d, p.w2, d, (int)M, F, d, w.dG, F, "gemm_bwd_dg", nullptr), true, s)))
+    return e;
+  {
+    const dim3 grid((ldm + kT - 1) / kT, (F + kT - 1) / kT);
+    timing_begin("gelu_bwd", s);
+    hipLaunchKernelGGL(gelu_bwd_kernel, grid, dim3(256), 0, s, w.A, w.dG, (int)M, F, w.dA, w.dAT,
+                       w.GT, ldm);
+    timing_end(s);
+    if ((e = hipGetLastError())) return e;
+  }
+  // dW2 [F, d] = GELU(A)^T d_out (K = the rows)
+  if ((e = gemm(plain_gemm(w.GT, ldm, w.dOT, ldm, F, d, ldm, p.dW2, d, "gemm_bwd_dw2", w.sk), true, s)))
+    return e;
+  // dW1 [d, F] = H2^T dA
+  {
+    const dim3 grid((ldm + kT - 1) / kT, (d + kT - 1) / kT);
+    timing_begin("cast_t", s);
+    hipLaunchKernelGGL(cast_t_kernel<bf16>, grid, dim3(256), 0, s, w.H2, (int)M, d, d, w.H2T, ldm,
+                       (bf16*)nullptr);
+    timing_end(s);
+    if ((e = hipGetLastError())) return e;
+  }
+  if ((e = gemm(plain_gemm(w.H2T, ldm, w.dAT, ldm, d, F, ldm, p.dW1, F, "gemm_bwd_dw1", w.sk), true, s)))
+    return e;
+  // dH2 = dA W1^T: B = W1 [d, F] as stored
+  if ((e = gemm(plain_gemm(w.dA, F, p.w1, F, (int)M, d, F, w.dH2, d, "gemm_bwd_dh", nullptr), true, s)))
+    return e;
+  const int nb = (int)((M + kNormRows - 1) / kNormRows);
+  timing_begin("rmsnorm_bwd", s);
+  hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3(nb), dim3(256), 0, s, p.r1, w.ss, w.dH2, p.g2, p.dout,
+                     p.eps, (int)M, d, p.dr1, w.dg_part);
+  hipLaunchKernelGGL(colsum_kernel, dim3((d + 63) / 64), dim3(1024), 0, s, w.dg_part, nb, d, p.dg2);
+  timing_end(s);
+  return hipGetLastError();
+}
+
+}  // namespace llatte

@@ -725,6 +725,9 @@ static TileCfg select_tile(const GemmParams& p, bool is_bf16) {
     return T_NONE;
   }
   if (is_bf16) {
+    // long contractions over few output tiles (weight gradients, K = rows):
+    // the large tile, with K split across the GPU
+    if (p.sk_part && p.K >= 4096 && p.batch == 1 && ntiles(p, 128, 128) < 128) return T128x128;
     if (ntiles(p, 128, 128) < 256) return T64x64;
     if (p.N <= 64) return T128x64;
     return T128x128;

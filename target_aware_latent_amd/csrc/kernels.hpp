@@ -154,6 +154,27 @@ struct AttnBwdParams {
 size_t attention_backward_workspace(long long Mtot, int h, int r);
 hipError_t attention_backward(AttnBwdParams p, int max_len, void* ws, hipStream_t s);
 
+// ------------------------------------------------------------------ FFN backward
+// Gradients of R2 = R1 + GELU(RMSNorm(R1) g2 W1) W2 over M rows (bf16
+// operands, fp32 accumulation and outputs).
+struct FfnBwdParams {
+  const float* r1 = nullptr;    // [M, d]
+  const float* g2 = nullptr;    // [d]
+  const void* w1 = nullptr;     // [d, F] bf16
+  const void* w2 = nullptr;     // [F, d] bf16
+  const float* dout = nullptr;  // [M, d]
+  float* dr1 = nullptr;         // [M, d]
+  float* dg2 = nullptr;         // [d]
+  float* dW1 = nullptr;         // [d, F]
+  float* dW2 = nullptr;         // [F, d]
+  long long M = 0;
+  int d = 0, F = 0;
+  float eps = 0.f;
+};
+constexpr long long kFfnSkPart = 1ll << 22;  // split-K scratch (floats)
+size_t ffn_backward_workspace(long long M, int d, int F);
+hipError_t ffn_backward(const FfnBwdParams& p, void* ws, hipStream_t s);
+
 // ------------------------------------------------------------------ summaries
 // out[k] = (W + A[k] Bm[k])^T in the dtype: W [rows, cols], A [K, rows,
 // rank], Bm [K, rank, cols], out [K, cols, rows].

@@ -64,6 +64,10 @@ class llatte_attn_desc(ctypes.Structure):
                 ("dtype", _c_int), ("scale", ctypes.c_float)]
 
 
+class llatte_ffn_desc(ctypes.Structure):
+    _fields_ = [("d", _c_int), ("d_ff", _c_int), ("dtype", _c_int), ("eps", ctypes.c_float)]
+
+
 class llatte_action_desc(ctypes.Structure):
     _fields_ = [(n, _c_int) for n in (
         "d", "d_hidden", "d_enc", "d_type", "d_item", "d_surf", "d_time",
@@ -134,6 +138,11 @@ _SIGS = {
         _c_int, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "llatte_mla_attention_backward_workspace_size": (ctypes.c_size_t, [
         ctypes.POINTER(llatte_attn_desc), _c_int]),
+    "llatte_ffn_backward": (_c_int, [
+        ctypes.POINTER(llatte_ffn_desc), _vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp,
+        _vp, ctypes.c_size_t, _vp]),
+    "llatte_ffn_backward_workspace_size": (ctypes.c_size_t, [
+        ctypes.POINTER(llatte_ffn_desc), _c_int]),
     "llatte_last_error": (ctypes.c_char_p, []),
     "llatte_version": (_c_int, []),
     "llatte_kernel_timing_enable": (None, [_c_int]),
@@ -321,6 +330,19 @@ def llatte_mla_attention_backward(desc, q_lat, c_lat, kv_offsets, hq_offsets, B,
         Ktot, max_len, _p(out), _p(lse), _p(d_out), _p(d_q), _p(d_c), _p(workspace), nbytes,
         _stream(stream))
     _check(st, "llatte_mla_attention_backward")
+
+
+def llatte_ffn_backward_workspace_size(desc, M):
+    return lib().llatte_ffn_backward_workspace_size(ctypes.byref(desc), M)
+
+
+def llatte_ffn_backward(desc, r1, g2, w1, w2, d_out, M, d_r1, d_g2, d_w1, d_w2, workspace,
+                        stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().llatte_ffn_backward(
+        ctypes.byref(desc), _p(r1), _p(g2), _p(w1), _p(w2), _p(d_out), M, _p(d_r1), _p(d_g2),
+        _p(d_w1), _p(d_w2), _p(workspace), nbytes, _stream(stream))
+    _check(st, "llatte_ffn_backward")
 
 
 def llatte_last_error():

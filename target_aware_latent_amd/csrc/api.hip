@@ -34,7 +34,7 @@
 #include <vector>
 
 #include "../../include/llatte.h"
-#include "kernels.hpp"
+#include "backward.hpp"
 
 namespace llatte {
 

@@ -36,7 +36,7 @@
 // that the 16-byte operand reads (16 rows x 4 chunks), the transpose reads
 // (8 rows x 4 eight-byte chunks per 32 lanes) and the 16-byte staging writes
 // each touch every bank of a cycle at most once.
-#include "kernels.hpp"
+#include "backward.hpp"
 
 namespace llatte {
 

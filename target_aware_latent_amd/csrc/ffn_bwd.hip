@@ -13,7 +13,7 @@
 // zero columns) by the kernels that produce them, and split K across the
 // GPU. The elementwise steps (the GELU derivative, the norm backward) are
 // HBM-bound kernels of their own.
-#include "kernels.hpp"
+#include "backward.hpp"
 
 namespace llatte {
 

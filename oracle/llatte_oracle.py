@@ -52,6 +52,7 @@ __all__ = [
     "compact", "history_query_mask", "mla_layer", "fuse_queries", "forward",
     "token_embed", "latent_attention", "unmasked_pairs", "flop_count",
     "lora_mlp_summaries", "latent_attention_backward", "ffn_block_backward",
+    "rmsnorm_backward", "attention_sublayer_backward",
 ]
 
 
@@ -460,6 +461,98 @@ def ffn_block_backward(R1, g2, W1, W2, d_out, eps=1e-6):
     dxh = dH2 * g2
     dR1 = d_out + s * (dxh - xh * np.mean(dxh * xh, axis=-1, keepdims=True))
     return dR1, dg2, dW1, dW2
+
+
+def rmsnorm_backward(x, g, dy, eps=1e-6):
+    """Gradients of y = RMSNorm(x) g (rmsnorm above) over the last axis:
+    with s = (mean(x^2) + eps)^-1/2 and xh = x s per row,
+        dg = sum over rows of dy * xh,
+        dx = s (dy g - xh mean(dy g xh))   (per row).
+    Returns (dx, dg)."""
+    s = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    xh = x * s
+    dxh = dy * g
+    dx = s * (dxh - xh * np.mean(dxh * xh, axis=-1, keepdims=True))
+    dg = np.sum((dy * xh).reshape(-1, x.shape[-1]), axis=0)
+    return dx, dg
+
+
+def attention_sublayer_backward(Rh, Rc, n, W, cfg, dRq):
+    """Gradients of the attention sublayer of one pre-norm MLA layer on one
+    user, R1 = Rq + MLA(RMSNorm(R) g1) (the first half of mla_layer, full-rank
+    queries), given dRq = dL/dR1 for the query rows (the last n history rows,
+    then the n_c candidate rows).
+
+    [LLaTTE] A.3 non-absorbed MLA: C = RMSNorm(H W_dkv) g_c (or H W_dkv
+    without the latent norm), per head K = C W_uk, V = C W_uv,
+    P = softmax(q K^T / sqrt(d_k)) over the allowed keys, o = P V, then
+    A = o W_o; A.2 layer equation (pre-norm reading) for the residual. The
+    derivative written out, per head:
+        dV = P^T do,  dP = do V^T,  dS = P (dP - rowsum(dP P)),
+        dq = dS K / sqrt(d_k),  dK = dS^T q / sqrt(d_k),
+        dW_uv += C^T dV,  dW_uk += C^T dK,  dC += dV W_uv^T + dK W_uk^T;
+    then dW_uq = Hq^T dq, dH(query rows) += dq W_uq^T, the latent norm's
+    backward, dW_dkv = H^T dC0, dH += dC0 W_dkv^T, and the pre-attention
+    norm's backward plus the residual.
+    Returns (dRh [K, d], dRc [n_c, d], grads) with grads holding g1, W_dkv,
+    g_c (when the latent norm is on), W_uq, W_uk, W_uv, W_o.
+    """
+    d, h, dk, r = cfg.d, cfg.h, cfg.dk, cfg.r
+    eps = cfg.eps
+    K = Rh.shape[0]
+    n_c = Rc.shape[0]
+    H = rmsnorm(Rh, W["g1"], eps)
+    Hc = rmsnorm(Rc, W["g1"], eps)
+    C0 = H @ W["W_dkv"]
+    C = rmsnorm(C0, W["g_c"], eps) if cfg.latent_norm else C0
+    Hq = np.concatenate([H[K - n:], Hc], axis=0)
+    M = Hq.shape[0]
+    q = (Hq @ W["W_uq"]).reshape(M, h, dk)
+    allowed = history_query_mask(K, n, n_c)
+    scale = 1.0 / math.sqrt(dk)
+    Wuk = W["W_uk"].reshape(r, h, dk)
+    Wuv = W["W_uv"].reshape(r, h, dk)
+    o = np.empty((M, h, dk))
+    P, Kh, Vh = [], [], []
+    for hh in range(h):
+        Kh.append(C @ Wuk[:, hh, :])
+        Vh.append(C @ Wuv[:, hh, :])
+        P.append(softmax_masked((q[:, hh, :] @ Kh[hh].T) * scale, allowed))
+        o[:, hh, :] = P[hh] @ Vh[hh]
+    g = {}
+    g["W_o"] = o.reshape(M, h * dk).T @ dRq
+    do = (dRq @ W["W_o"].T).reshape(M, h, dk)
+    dq = np.empty((M, h, dk))
+    dWuk = np.zeros((r, h, dk))
+    dWuv = np.zeros((r, h, dk))
+    dC = np.zeros_like(C)
+    for hh in range(h):
+        dV = P[hh].T @ do[:, hh, :]
+        dP = do[:, hh, :] @ Vh[hh].T
+        dS = P[hh] * (dP - np.sum(dP * P[hh], axis=1, keepdims=True))
+        dq[:, hh, :] = dS @ Kh[hh] * scale
+        dK = dS.T @ q[:, hh, :] * scale
+        dWuv[:, hh, :] = C.T @ dV
+        dWuk[:, hh, :] = C.T @ dK
+        dC += dV @ Wuv[:, hh, :].T + dK @ Wuk[:, hh, :].T
+    g["W_uk"] = dWuk.reshape(r, h * dk)
+    g["W_uv"] = dWuv.reshape(r, h * dk)
+    dq = dq.reshape(M, h * dk)
+    g["W_uq"] = Hq.T @ dq
+    dHq = dq @ W["W_uq"].T
+    if cfg.latent_norm:
+        dC0, g["g_c"] = rmsnorm_backward(C0, W["g_c"], dC, eps)
+    else:
+        dC0 = dC
+    g["W_dkv"] = H.T @ dC0
+    dH = dC0 @ W["W_dkv"].T
+    dH[K - n:] += dHq[:n]
+    dRh, dg1h = rmsnorm_backward(Rh, W["g1"], dH, eps)
+    dRc, dg1c = rmsnorm_backward(Rc, W["g1"], dHq[n:], eps)
+    g["g1"] = dg1h + dg1c
+    dRh[K - n:] += dRq[:n]
+    dRc = dRc + dRq[n:]
+    return dRh, dRc, g
 
 
 def unmasked_pairs(cfg, lengths):

@@ -5,6 +5,7 @@
     python bench.py --workload summaries   (the LoRAMLP sequence summaries)
     python bench.py --workload backward    (the attention-core backward)
     python bench.py --workload ffn_backward (the FFN-sublayer backward)
+    python bench.py --workload sublayer_backward (the attention-sublayer backward)
 
 One step is one llatte_mla_forward over one batch of the workload (all
 layers, the pyramid, the readout), inputs and weights already resident in
@@ -581,6 +582,133 @@ def bench_ffn_backward(args):
     print(json.dumps(rec))
 
 
+SUB_BWD_METRIC = ("user-sequences/sec + TFLOP/s (% MFMA bf16 peak), attention-sublayer backward "
+                  "of the MLA stack at L=1600, 1 GPU")
+SUB_BWD_TEXT = ("c3 attention sublayers: gradients of the layer-input rows, g1, W_dkv, g_c, W_uq, "
+                "W_uk, W_uv, W_o of the six causal layers (64 users, keys 1600-1600-800-400-200-100, "
+                "query rows 1600-800-400-200-100-50; d=512, 8x64 heads, r=128), bf16 products")
+
+
+def bench_sublayer_backward(args):
+    import torch
+    from oracle import llatte_oracle as O
+    from target_aware_latent_amd import llatte as C
+    import synth
+    from types import SimpleNamespace
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    cfg = synth.get_config("c3")
+    d, h, dk, r, B = cfg.d, cfg.h, cfg.dk, cfg.r, cfg.B
+    hd = h * dk
+    rng = np.random.default_rng(0)
+    desc = C.llatte_attn_sublayer_desc(d, h, dk, r, 0, C.LLATTE_BF16, 1, cfg.eps)
+    dev = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(dt)
+    W = {"g1": np.ones(d), "g_c": np.ones(r),
+         "W_dkv": rng.standard_normal((d, r)) / np.sqrt(d),
+         "W_uq": rng.standard_normal((d, hd)) / np.sqrt(d),
+         "W_uk": rng.standard_normal((r, hd)) / np.sqrt(r),
+         "W_uv": rng.standard_normal((r, hd)) / np.sqrt(r),
+         "W_o": rng.standard_normal((hd, d)) / np.sqrt(hd)}
+    wd = {"g1": dev(W["g1"]), "g_c": dev(W["g_c"]), "w_dkv": dev(W["W_dkv"], torch.bfloat16),
+          "w_uq": dev(W["W_uq"], torch.bfloat16), "w_uk": dev(W["W_uk"], torch.bfloat16),
+          "w_uv": dev(W["W_uv"], torch.bfloat16), "w_o": dev(W["W_o"], torch.bfloat16)}
+    flops = {}
+    add = lambda k, v: flops.__setitem__(k, flops.get(k, 0) + v)
+    layers = []
+    wsize = 0
+    for K, n, _ in backward_layers(cfg)[:cfg.N]:
+        kv = torch.from_numpy(np.arange(B + 1, dtype=np.int32) * K).cuda()
+        hq = torch.from_numpy(np.arange(B + 1, dtype=np.int32) * n).cuda()
+        Mtot, Ktot = B * n, B * K
+        r_kv = dev(rng.standard_normal((Ktot, d)))
+        dout = dev(rng.standard_normal((Mtot, d)))
+        gd = {"g1": torch.empty(d, device="cuda"), "g_c": torch.empty(r, device="cuda"),
+              "w_dkv": torch.empty((d, r), device="cuda"), "w_uq": torch.empty((d, hd), device="cuda"),
+              "w_uk": torch.empty((r, hd), device="cuda"), "w_uv": torch.empty((r, hd), device="cuda"),
+              "w_o": torch.empty((hd, d), device="cuda")}
+        d_r_kv = torch.empty((Ktot, d), device="cuda")
+        layers.append((kv, hq, Mtot, Ktot, K, r_kv, dout, d_r_kv, gd))
+        wsize = max(wsize, C.llatte_attn_sublayer_backward_workspace_size(desc, B, Mtot, Ktot))
+        pairs = B * (n * (K - n) + n * (n + 1) // 2)
+        add("attn_bwd_dq", 6 * r * h * pairs)
+        add("attn_bwd_dc", 4 * r * h * pairs)
+        for lab in ("gemm_sub_dwo", "gemm_sub_do", "gemm_sub_dwuq", "gemm_sub_dhq"):
+            add(lab, 2 * Mtot * d * hd)
+        for lab in ("gemm_sub_dwuv", "gemm_sub_dolat", "gemm_sub_dq", "gemm_sub_dwuk"):
+            add(lab, 2 * Mtot * r * hd)
+        for lab in ("gemm_sub_dwdkv", "gemm_sub_dh"):
+            add(lab, 2 * Ktot * d * r)
+    ws = torch.empty(wsize, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for (kv, hq, Mtot, Ktot, K, r_kv, dout, d_r_kv, gd) in layers:
+            C.llatte_attn_sublayer_backward(desc, wd, r_kv, None, kv, hq, B, Mtot, Ktot, K, dout,
+                                            d_r_kv, None, gd, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    Fl = sum(flops.values())
+    C.llatte_kernel_timing_reset()
+    C.llatte_kernel_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = C.llatte_kernel_timing_read()
+    C.llatte_kernel_timing_enable(False)
+    kernels = {}
+    for name, (cnt, tot) in kt.items():
+        e = {"launches_per_step": cnt / args.steps, "ms_per_step": tot / args.steps}
+        if name in flops:
+            e["tflops"] = flops[name] / (tot / args.steps / 1e3) / 1e12
+        kernels[name] = e
+    dom = max((k for k in flops if k in kt), key=lambda k: kt[k][1])
+    cnt, tot = kt[dom]
+    per_launch = flops[dom] / (cnt / args.steps)
+    achieved = per_launch / (tot / cnt / 1e3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": per_launch, "avg_launch_ms": round(tot / cnt, 4)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        ocfg = SimpleNamespace(d=d, h=h, dk=dk, r=r, eps=cfg.eps, latent_norm=True, norm_mode="pre")
+        sample = [(rng.standard_normal((K, d)), n, rng.standard_normal((n, d)))
+                  for K, n, _ in backward_layers(cfg)[:cfg.N]]
+        t0 = time.perf_counter()
+        users = 0
+        while time.perf_counter() - t0 < 12.0 and users < B:
+            for Rh, n, dq in sample:
+                O.attention_sublayer_backward(Rh, np.zeros((0, d)), n, W, ocfg, dq)
+            users += 1
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(users / dt, 3), "unit": "user-sequences/s",
+               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"{users} of {B} users through all {len(layers)} attention-sublayer "
+                         f"backwards, fp64 oracle (non-absorbed), {dt:.1f} s"}
+    rec = {
+        "metric": SUB_BWD_METRIC, "value": round(B / (ms_step / 1e3), 1),
+        "unit": "user-sequences/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (N(0,1) layer-input rows and d_out, N(0,1/fan_in) bf16 weights, gains 1)",
+        "config": {"workload": SUB_BWD_TEXT, "global_batch": B, "seq_len": cfg.L,
+                   "parallelism": "single GPU"},
+        "tflops": round(Fl / (ms_step / 1e3) / 1e12, 2),
+        "pct_peak": round(100 * Fl / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+    }
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -597,12 +725,14 @@ def main():
                     help="profile summary whose RECORD line holds the measured "
                          "HBM bytes per launch of the dominant kernel (written "
                          "by target_aware_latent_amd.profsum traffic)")
-    ap.add_argument("--workload", default="stack", choices=["stack", "actions", "summaries", "backward", "ffn_backward"],
+    ap.add_argument("--workload", default="stack", choices=["stack", "actions", "summaries", "backward", "ffn_backward",
+                             "sublayer_backward"],
                     help="stack: the MLA forward (default); actions: the action "
                          "tokenization that builds the history tokens; summaries: the "
                          "LoRAMLP sequence summaries of the readout; backward: the attention-core "
                          "backward of every layer of the stack; ffn_backward: the FFN-sublayer "
-                         "backward (GEMM gradients) of every layer")
+                         "backward (GEMM gradients) of every layer; sublayer_backward: the "
+                         "attention-sublayer backward of every layer")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
@@ -620,6 +750,9 @@ def main():
         return
     if args.workload == "ffn_backward":
         bench_ffn_backward(args)
+        return
+    if args.workload == "sublayer_backward":
+        bench_sublayer_backward(args)
         return
 
     import torch

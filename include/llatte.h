@@ -332,6 +332,81 @@ llatte_status llatte_ffn_backward(const llatte_ffn_desc* f, const float* r1,
 size_t llatte_ffn_backward_workspace_size(const llatte_ffn_desc* f,
                                           int32_t M);
 
+/* ------------------------------------------------------------------------
+ * llatte_attn_sublayer_backward -- gradients of the attention sublayer of
+ * one pre-norm MLA layer ([LLaTTE] A.3 MLA with full-rank queries; A.2
+ * layer equation, pre-norm reading), over a jagged batch of B users:
+ *   H  = RMSNorm(R) g1 (every history row of the layer input, and the
+ *        candidate rows),  C = RMSNorm(H W_dkv) g_c (or H W_dkv with
+ *        latent_norm = 0),  q = H_q W_uq (the query rows),
+ *   per head: K = C W_uk, V = C W_uv, o = softmax(q K^T / sqrt(d_k)) V
+ *        (the masks of llatte_mla_attention),
+ *   R1 = R_q + o W_o.
+ * Given d_out = dL/dR1 for the query rows it writes the gradients of the
+ * layer-input rows (history and candidate) and of g1, W_dkv, g_c, W_uq,
+ * W_uk, W_uv, W_o. The forward is recomputed (in the absorbed form, on the
+ * same kernels as llatte_mla_attention and llatte_mla_attention_backward);
+ * products take bf16 operands with fp32 accumulation.
+ *   d            host descriptor; BF16 only; rank 64 or 128; d and head_dim
+ *                multiples of 8, d <= 1024
+ *   w            host struct of device pointers: g1 [d], g_c [r] float32;
+ *                w_dkv [d, r], w_uq [d, h*dk], w_uk [r, h*dk],
+ *                w_uv [r, h*dk], w_o [h*dk, d] bf16 row-major (head j's
+ *                columns of w_uq / w_uk / w_uv are j*dk .. j*dk+dk-1)
+ *   r_kv         [Ktot, d] float32: user u's history rows at
+ *                kv_offsets[u] .. kv_offsets[u+1]-1 (oldest first)
+ *   r_cand       [B*n_cand, d] float32 (NULL if n_cand = 0)
+ *   hq_offsets   [B+1]: user u's query rows are its last n_u history rows
+ *   d_out        [Mtot, d] float32 in the attention row order (candidates
+ *                u*n_cand.., then history query rows B*n_cand + hq_offsets[u]..)
+ *   d_r_kv       [Ktot, d], d_r_cand [B*n_cand, d] float32 (overwritten)
+ *   g            host struct of device pointers to the float32 gradients,
+ *                overwritten, laid out as the weights (g_c ignored with
+ *                latent_norm = 0)
+ *   max_len      host: >= every K_u
+ *   workspace    >= llatte_attn_sublayer_backward_workspace_size(...) bytes
+ * With Mtot = 0 (no query rows) every gradient is zeroed. Device pointers
+ * 16-byte aligned. Errors: LLATTE_ERR_UNSUPPORTED (dtype, rank, latent
+ * norm flag), LLATTE_ERR_INVALID_ARG (sizes, NULL or misaligned pointers),
+ * LLATTE_ERR_WORKSPACE, LLATTE_ERR_HIP. Nothing is enqueued on an argument
+ * error.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t d, n_heads, head_dim, rank, n_cand, dtype, latent_norm;
+  float eps;
+} llatte_attn_sublayer_desc;
+
+typedef struct {
+  const float* g1;
+  const void* w_dkv;
+  const float* g_c;
+  const void* w_uq;
+  const void* w_uk;
+  const void* w_uv;
+  const void* w_o;
+} llatte_attn_sublayer_weights;
+
+typedef struct {
+  float* g1;
+  float* w_dkv;
+  float* g_c;
+  float* w_uq;
+  float* w_uk;
+  float* w_uv;
+  float* w_o;
+} llatte_attn_sublayer_grads;
+
+llatte_status llatte_attn_sublayer_backward(
+    const llatte_attn_sublayer_desc* d, const llatte_attn_sublayer_weights* w,
+    const float* r_kv, const float* r_cand, const int32_t* kv_offsets,
+    const int32_t* hq_offsets, int32_t B, int32_t Mtot, int32_t Ktot,
+    int32_t max_len, const float* d_out, float* d_r_kv, float* d_r_cand,
+    const llatte_attn_sublayer_grads* g, void* workspace,
+    size_t workspace_bytes, void* stream);
+size_t llatte_attn_sublayer_backward_workspace_size(
+    const llatte_attn_sublayer_desc* d, int32_t B, int32_t Mtot,
+    int32_t Ktot);
+
 size_t llatte_mla_attention_workspace_size(const llatte_attn_desc* a,
                                            int32_t B, int32_t Mtot,
                                            int32_t Ktot);

@@ -1410,6 +1410,235 @@ size_t llatte_mla_attention_backward_workspace_size(const llatte_attn_desc* a, i
   return attention_backward_workspace(Mtot, a->n_heads, a->rank);
 }
 
+// ------------------------------------------------------------------ attention sublayer backward
+static const char* check_sublayer_desc(const llatte_attn_sublayer_desc* D, int* code) {
+  *code = LLATTE_ERR_INVALID_ARG;
+  if (!D) return "NULL descriptor";
+  *code = LLATTE_ERR_UNSUPPORTED;
+  if (D->dtype != LLATTE_BF16) return "the sublayer backward is BF16 only";
+  if (D->rank != 64 && D->rank != 128) return "the sublayer backward needs rank 64 or 128";
+  if (D->latent_norm != 0 && D->latent_norm != 1) return "latent_norm must be 0 or 1";
+  *code = LLATTE_ERR_INVALID_ARG;
+  if (D->d < 8 || D->d > 1024 || D->d % 8) return "d must be a multiple of 8 in [8, 1024]";
+  if (D->n_heads < 1 || D->head_dim < 8 || D->head_dim % 8) return "bad heads";
+  if (D->n_cand < 0) return "n_cand must be >= 0";
+  if (!(D->eps >= 0.f)) return "eps must be >= 0";
+  return nullptr;
+}
+
+constexpr long long kSubSkPart = 1ll << 22;  // split-K scratch (floats)
+
+// Carves the workspace and, with launch set, enqueues the whole backward.
+// Returns the workspace bytes through *bytes when launch is false.
+static llatte_status sublayer_backward_run(
+    const llatte_attn_sublayer_desc* D, const llatte_attn_sublayer_weights* W, const float* r_kv,
+    const float* r_cand, const int32_t* kv_off, const int32_t* hq_off, int32_t B, int32_t Mtot,
+    int32_t Ktot, int32_t max_len, const float* d_out, float* d_r_kv, float* d_r_cand,
+    const llatte_attn_sublayer_grads* G, void* workspace, size_t* bytes, bool launch,
+    hipStream_t s) {
+  const int d = D->d, h = D->n_heads, dk = D->head_dim, r = D->rank, hd = h * dk, hr = h * r;
+  const long long M = Mtot, K = Ktot, nc = (long long)B * D->n_cand, nh = M - nc;
+  const int ldm = (int)cdiv(M, 8) * 8, ldk = (int)cdiv(K, 8) * 8;
+  const bool ln = D->latent_norm != 0;
+  const float eps = D->eps;
+  llatte_attn_desc ad{h, r, D->n_cand, LLATTE_BF16, 1.f / sqrtf((float)dk)};
+  const size_t aws = llatte_mla_attention_workspace_size(&ad, B, Mtot, Ktot);
+  const size_t bws = llatte_mla_attention_backward_workspace_size(&ad, Mtot);
+  const int pk = rmsnorm_backward_parts(K), pc = rmsnorm_backward_parts(nc);
+  Arena ar(workspace);
+  bf16* H = ar.take<bf16>(K * d);
+  float* ss_kv = ar.take<float>(K);
+  bf16* Hc = ar.take<bf16>(nc * d);
+  float* ss_c = ar.take<float>(nc);
+  bf16* WdkvT = ar.take<bf16>((size_t)r * d);
+  float* C0 = ar.take<float>(K * r);
+  bf16* Cb = ar.take<bf16>(K * r);
+  float* ss_C = ar.take<float>(K);
+  bf16* Hq = ar.take<bf16>(M * d);
+  int* hist_map = ar.take<int>(nh > 0 ? nh : 1);
+  bf16* WuqT = ar.take<bf16>((size_t)hd * d);
+  bf16* q = ar.take<bf16>(M * hd);
+  bf16* qt = ar.take<bf16>(M * hr);
+  char* attn_ws = ar.take<char>(aws);
+  float* ot = ar.take<float>(M * hr);
+  float* lse = ar.take<float>(M * h);
+  bf16* otb = ar.take<bf16>(M * hr);
+  bf16* WuvT = ar.take<bf16>((size_t)hd * r);
+  bf16* WukT = ar.take<bf16>((size_t)hd * r);
+  bf16* o = ar.take<bf16>(M * hd);
+  bf16* dRb = ar.take<bf16>(M * d);
+  bf16* dRT = ar.take<bf16>((size_t)d * ldm);
+  bf16* oT = ar.take<bf16>((size_t)hd * ldm);
+  bf16* dob = ar.take<bf16>(M * hd);
+  bf16* otT = ar.take<bf16>((size_t)hr * ldm);
+  bf16* doT = ar.take<bf16>((size_t)hd * ldm);
+  float* dot_ = ar.take<float>(M * hr);
+  char* abw_ws = ar.take<char>(bws);
+  float* dqt = ar.take<float>(M * hr);
+  bf16* dqtb = ar.take<bf16>(M * hr);
+  bf16* dqtT = ar.take<bf16>((size_t)hr * ldm);
+  bf16* dq = ar.take<bf16>(M * hd);
+  bf16* qT = ar.take<bf16>((size_t)hd * ldm);
+  bf16* HqT = ar.take<bf16>((size_t)d * ldm);
+  bf16* dqT = ar.take<bf16>((size_t)hd * ldm);
+  float* dHq = ar.take<float>(M * d);
+  float* dC = ar.take<float>(K * r);
+  float* dC0 = ln ? ar.take<float>(K * r) : dC;
+  bf16* dC0b = ar.take<bf16>(K * r);
+  bf16* dC0T = ar.take<bf16>((size_t)r * ldk);
+  bf16* HT = ar.take<bf16>((size_t)d * ldk);
+  float* dH = ar.take<float>(K * d);
+  float* dres = ar.take<float>(K * d);
+  float* dg_part = ar.take<float>((size_t)std::max((long long)(pk + pc) * d, (long long)pk * r));
+  float* sk = ar.take<float>(kSubSkPart);
+  if (!launch) {
+    *bytes = ar.off;
+    return LLATTE_OK;
+  }
+  if (M == 0) {  // no query rows: every gradient is zero
+    HIP_TRY(zero_f32(d_r_kv, K * d, s));
+    if (nc) HIP_TRY(zero_f32(d_r_cand, nc * d, s));
+    HIP_TRY(zero_f32(G->g1, d, s));
+    HIP_TRY(zero_f32(G->w_dkv, (long long)d * r, s));
+    if (ln) HIP_TRY(zero_f32(G->g_c, r, s));
+    HIP_TRY(zero_f32(G->w_uq, (long long)d * hd, s));
+    HIP_TRY(zero_f32(G->w_uk, (long long)r * hd, s));
+    HIP_TRY(zero_f32(G->w_uv, (long long)r * hd, s));
+    HIP_TRY(zero_f32(G->w_o, (long long)hd * d, s));
+    return LLATTE_OK;
+  }
+  // C = A B^T with A [Mr, Kc] (lda), B [N, Kc] (ldb), optional head batch
+  auto mm = [&](const void* A, int lda, long long sA, const void* Bm, int ldb, long long sB, long long Mr,
+                int N, int Kc, void* C, int ldc, long long sC, int batch, bool f32, bool split,
+                const char* name) {
+    GemmParams g;
+    g.A = A;
+    g.lda = lda;
+    g.sA = sA;
+    g.B = Bm;
+    g.ldb = ldb;
+    g.sB = sB;
+    g.M_cap = (int)Mr;
+    g.N = N;
+    g.K = Kc;
+    g.batch = batch;
+    g.epi = f32 ? EPI_STORE_F32 : EPI_STORE;
+    g.C = C;
+    g.ldc = ldc;
+    g.sC = sC;
+    g.name = name;
+    if (split) {
+      g.sk_part = sk;
+      g.sk_part_cap = kSubSkPart;
+    }
+    return gemm(g, true, s);
+  };
+  // ---- forward recompute
+  HIP_TRY(norm_rows(RowSrc{r_kv, r_kv, 0, d}, (int)K, nullptr, W->g1, eps, nullptr, 0, H, d, d, K_BF16,
+                    s, ss_kv));
+  if (nc)
+    HIP_TRY(norm_rows(RowSrc{r_cand, r_cand, 0, d}, (int)nc, nullptr, W->g1, eps, nullptr, 0, Hc, d, d,
+                      K_BF16, s, ss_c));
+  HIP_TRY(transpose(W->w_dkv, d, r, r, 0, WdkvT, d, 0, 1, K_BF16, K_BF16, s));
+  HIP_TRY(mm(H, d, 0, WdkvT, d, 0, K, r, d, C0, r, 0, 1, true, false, "gemm_sub_c0"));
+  HIP_TRY(norm_rows(RowSrc{C0, C0, 0, r}, (int)K, nullptr, ln ? W->g_c : nullptr, eps, nullptr, 0, Cb,
+                    r, r, K_BF16, s, ln ? ss_C : nullptr));
+  HIP_TRY(gather_query_rows(Hc, H, kv_off, hq_off, B, D->n_cand, d, Hq, hist_map, s));
+  HIP_TRY(transpose(W->w_uq, d, hd, hd, 0, WuqT, d, 0, 1, K_BF16, K_BF16, s));
+  HIP_TRY(mm(Hq, d, 0, WuqT, d, 0, M, hd, d, q, hd, 0, 1, false, false, "gemm_sub_q"));
+  HIP_TRY(mm(q, hd, dk, W->w_uk, hd, dk, M, r, dk, qt, hr, r, h, false, false, "gemm_sub_qlat"));
+  {
+    const llatte_status st = llatte_mla_attention(&ad, qt, Cb, kv_off, hq_off, B, Mtot, Ktot, ot, lse,
+                                                  attn_ws, aws, s);
+    if (st != LLATTE_OK) return st;
+  }
+  HIP_TRY(cast_f32(ot, otb, M * hr, true, s));
+  HIP_TRY(transpose(W->w_uv, r, hd, hd, 0, WuvT, r, 0, 1, K_BF16, K_BF16, s));
+  HIP_TRY(transpose(W->w_uk, r, hd, hd, 0, WukT, r, 0, 1, K_BF16, K_BF16, s));
+  HIP_TRY(mm(otb, hr, r, WuvT, r, (long long)dk * r, M, dk, r, o, hd, dk, h, false, false, "gemm_sub_o"));
+  // ---- backward
+  HIP_TRY(cast_transpose(d_out, true, M, d, d, dRT, ldm, dRb, s));
+  HIP_TRY(cast_transpose(o, false, M, hd, hd, oT, ldm, nullptr, s));
+  HIP_TRY(mm(oT, ldm, 0, dRT, ldm, 0, hd, d, ldm, G->w_o, d, 0, 1, true, true, "gemm_sub_dwo"));
+  HIP_TRY(mm(dRb, d, 0, W->w_o, d, 0, M, hd, d, dob, hd, 0, 1, false, false, "gemm_sub_do"));
+  HIP_TRY(cast_transpose(otb, false, M, hr, hr, otT, ldm, nullptr, s));
+  HIP_TRY(cast_transpose(dob, false, M, hd, hd, doT, ldm, nullptr, s));
+  HIP_TRY(mm(otT, ldm, (long long)r * ldm, doT, ldm, (long long)dk * ldm, r, dk, ldm, G->w_uv, hd, dk, h,
+             true, true, "gemm_sub_dwuv"));
+  HIP_TRY(mm(dob, hd, dk, W->w_uv, hd, dk, M, r, dk, dot_, hr, r, h, true, false, "gemm_sub_dolat"));
+  {
+    const llatte_status st = llatte_mla_attention_backward(&ad, qt, Cb, kv_off, hq_off, B, Mtot, Ktot,
+                                                           max_len, ot, lse, dot_, dqt, dC, abw_ws,
+                                                           bws, s);
+    if (st != LLATTE_OK) return st;
+  }
+  HIP_TRY(cast_transpose(dqt, true, M, hr, hr, dqtT, ldm, dqtb, s));
+  HIP_TRY(mm(dqtb, hr, r, WukT, r, (long long)dk * r, M, dk, r, dq, hd, dk, h, false, false, "gemm_sub_dq"));
+  HIP_TRY(cast_transpose(q, false, M, hd, hd, qT, ldm, nullptr, s));
+  HIP_TRY(mm(dqtT, ldm, (long long)r * ldm, qT, ldm, (long long)dk * ldm, r, dk, ldm, G->w_uk, hd, dk, h,
+             true, true, "gemm_sub_dwuk"));
+  HIP_TRY(cast_transpose(Hq, false, M, d, d, HqT, ldm, nullptr, s));
+  HIP_TRY(cast_transpose(dq, false, M, hd, hd, dqT, ldm, nullptr, s));
+  HIP_TRY(mm(HqT, ldm, 0, dqT, ldm, 0, d, hd, ldm, G->w_uq, hd, 0, 1, true, true, "gemm_sub_dwuq"));
+  HIP_TRY(mm(dq, hd, 0, W->w_uq, hd, 0, M, d, hd, dHq, d, 0, 1, true, false, "gemm_sub_dhq"));
+  if (ln) {
+    HIP_TRY(rmsnorm_backward(C0, ss_C, dC, W->g_c, nullptr, eps, K, r, dC0, dg_part, s));
+    HIP_TRY(column_sum(dg_part, pk, r, G->g_c, s));
+  }
+  HIP_TRY(cast_transpose(dC0, true, K, r, r, dC0T, ldk, dC0b, s));
+  HIP_TRY(cast_transpose(H, false, K, d, d, HT, ldk, nullptr, s));
+  HIP_TRY(mm(HT, ldk, 0, dC0T, ldk, 0, d, r, ldk, G->w_dkv, r, 0, 1, true, true, "gemm_sub_dwdkv"));
+  HIP_TRY(mm(dC0b, r, 0, W->w_dkv, r, 0, K, d, r, dH, d, 0, 1, true, false, "gemm_sub_dh"));
+  HIP_TRY(zero_f32(dres, K * d, s));
+  HIP_TRY(scatter_query_rows(dHq, d_out, hist_map, nh, nc, d, dH, dres, s));
+  HIP_TRY(rmsnorm_backward(r_kv, ss_kv, dH, W->g1, dres, eps, K, d, d_r_kv, dg_part, s));
+  if (nc)
+    HIP_TRY(rmsnorm_backward(r_cand, ss_c, dHq, W->g1, d_out, eps, nc, d, d_r_cand,
+                             dg_part + (size_t)pk * d, s));
+  HIP_TRY(column_sum(dg_part, pk + pc, d, G->g1, s));
+  return LLATTE_OK;
+}
+
+size_t llatte_attn_sublayer_backward_workspace_size(const llatte_attn_sublayer_desc* D, int32_t B,
+                                                    int32_t Mtot, int32_t Ktot) {
+  int code;
+  if (check_sublayer_desc(D, &code) || B < 1 || Mtot < 0 || Ktot < B) return 0;
+  size_t bytes = 0;
+  llatte_attn_sublayer_grads g{};
+  sublayer_backward_run(D, nullptr, nullptr, nullptr, nullptr, nullptr, B, Mtot, Ktot, 1, nullptr,
+                        nullptr, nullptr, &g, nullptr, &bytes, false, nullptr);
+  return bytes;
+}
+
+llatte_status llatte_attn_sublayer_backward(
+    const llatte_attn_sublayer_desc* D, const llatte_attn_sublayer_weights* W, const float* r_kv,
+    const float* r_cand, const int32_t* kv_offsets, const int32_t* hq_offsets, int32_t B,
+    int32_t Mtot, int32_t Ktot, int32_t max_len, const float* d_out, float* d_r_kv,
+    float* d_r_cand, const llatte_attn_sublayer_grads* G, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  int code;
+  if (const char* why = check_sublayer_desc(D, &code)) return fail(code, "%s", why);
+  if (!W || !G) return fail(LLATTE_ERR_INVALID_ARG, "NULL weights or gradients");
+  if (B < 1 || Ktot < B || max_len < 1 || Mtot < (long long)B * D->n_cand)
+    return fail(LLATTE_ERR_INVALID_ARG, "bad sizes");
+  const bool ln = D->latent_norm != 0, cand = D->n_cand > 0;
+  const void* need[] = {W->g1, W->w_dkv, W->w_uq, W->w_uk, W->w_uv, W->w_o, r_kv, kv_offsets,
+                        hq_offsets, d_r_kv, G->g1, G->w_dkv, G->w_uq, G->w_uk, G->w_uv, G->w_o,
+                        workspace, ln ? W->g_c : W->g1, ln ? G->g_c : G->g1,
+                        cand ? r_cand : r_kv, cand ? d_r_cand : d_r_kv,
+                        Mtot > 0 ? d_out : r_kv};
+  for (const void* p : need) {
+    if (!p) return fail(LLATTE_ERR_INVALID_ARG, "NULL pointer");
+    if (!aligned16(p)) return fail(LLATTE_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  }
+  const size_t bytes = llatte_attn_sublayer_backward_workspace_size(D, B, Mtot, Ktot);
+  if (workspace_bytes < bytes)
+    return fail(LLATTE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, bytes);
+  return sublayer_backward_run(D, W, r_kv, r_cand, kv_offsets, hq_offsets, B, Mtot, Ktot, max_len,
+                               d_out, d_r_kv, d_r_cand, G, workspace, nullptr, true,
+                               (hipStream_t)stream);
+}
+
 static const char* check_ffn_desc(const llatte_ffn_desc* f) {
   if (!f) return "NULL descriptor";
   if (f->dtype != LLATTE_BF16) return "the FFN backward is BF16 only";

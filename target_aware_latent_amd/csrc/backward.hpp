@@ -53,4 +53,36 @@ constexpr long long kFfnSkPart = 1ll << 22;  // split-K scratch (floats)
 size_t ffn_backward_workspace(long long M, int d, int F);
 hipError_t ffn_backward(const FfnBwdParams& p, void* ws, hipStream_t s);
 
+
+// ------------------------------------------------------------------ shared pieces
+// dst_t [cols, ldm] = bf16(src [M, cols])^T (zero columns m in [M, ldm)),
+// dst_rm (optional) = bf16(src) row-major; src float or bf16; cols, ld_src
+// and ldm even.
+hipError_t cast_transpose(const void* src, bool src_f32, long long M, int cols, int ld_src,
+                          bf16* dst_t, int ldm, bf16* dst_rm, hipStream_t s);
+// RMSNorm backward over M rows of width d (<= 1024, multiple of 4):
+// dx = dres + s (dh g - xh mean(dh g xh)) with s from ss = sum(x^2) per
+// row (dres optional), and per-block partial column sums of dh * xh in
+// dg_part [rmsnorm_backward_parts(M), d].
+int rmsnorm_backward_parts(long long M);
+hipError_t rmsnorm_backward(const float* x, const float* ss, const float* dh, const float* g,
+                            const float* dres, float eps, long long M, int d, float* dx,
+                            float* dg_part, hipStream_t s);
+// out[c] = sum over p < np of part[p][c] in a fixed order.
+hipError_t column_sum(const float* part, int np, int d, float* out, hipStream_t s);
+hipError_t zero_f32(float* p, long long n, hipStream_t s);
+
+// ------------------------------------------------------------------ attention sublayer
+// Hq [Mtot, d] (bf16) = the candidate rows Hc [B*n_cand, d], then user u's
+// last n_u rows of H (H row kv_off[u] + K_u - n_u + t goes to row
+// B*n_cand + hq_off[u] + t); hist_map[hq_off[u] + t] = that H row. d is a
+// multiple of 8.
+hipError_t gather_query_rows(const bf16* Hc, const bf16* H, const int* kv_off, const int* hq_off,
+                             int B, int n_cand, int d, bf16* Hq, int* hist_map, hipStream_t s);
+// For history query row j < nh: dH[hist_map[j]] += dHq[nc + j] and
+// dres[hist_map[j]] = dRq[nc + j] (rows of width d, a multiple of 4; the
+// mapped rows are distinct).
+hipError_t scatter_query_rows(const float* dHq, const float* dRq, const int* hist_map, long long nh,
+                              long long nc, int d, float* dH, float* dres, hipStream_t s);
+
 }  // namespace llatte

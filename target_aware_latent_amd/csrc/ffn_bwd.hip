@@ -107,8 +107,8 @@ __global__ __launch_bounds__(256) void gelu_bwd_kernel(const float* A, const flo
   }
 }
 
-// RMSNorm backward with the residual, one wave per row, kNormRows rows per
-// block: s = 1 / sqrt(ss / d + eps), xh = x s, dxh = dh g,
+// RMSNorm backward with the residual (dres, optional), one wave per row,
+// kNormRows rows per block: s = 1 / sqrt(ss / d + eps), xh = x s, dxh = dh g,
 // dx = dres + s (dxh - xh mean(dxh xh)); and the block's partial sums of
 // dh * xh per column (the gain's gradient), summed over the block's rows in
 // row order and then over its waves in wave order.
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* x, const 
     for (int j = 0; j < MAXV; ++j) {
       const int idx = j * 256 + lane * 4;
       if (idx >= d) continue;
-      const f32x4 r = *(const f32x4*)(dres + (size_t)row * d + idx);
+      const f32x4 r = dres ? *(const f32x4*)(dres + (size_t)row * d + idx) : f32x4{};
       *(f32x4*)(dx + (size_t)row * d + idx) = r + (dxh[j] - xh[j] * mean) * s;
       acc[j] += hv[j] * xh[j];
     }
@@ -253,6 +253,45 @@ GemmParams plain_gemm(const void* A, int lda, const void* B, int ldb, int M, int
 }  // namespace
 
 size_t ffn_backward_workspace(long long M, int d, int F) { return ffn_ws(nullptr, M, d, F).bytes; }
+
+hipError_t cast_transpose(const void* src, bool src_f32, long long M, int cols, int ld_src,
+                          bf16* dst_t, int ldm, bf16* dst_rm, hipStream_t s) {
+  if (ldm <= 0 || cols <= 0) return hipSuccess;
+  const dim3 grid((ldm + kT - 1) / kT, (cols + kT - 1) / kT);
+  timing_begin("cast_t", s);
+  if (src_f32)
+    hipLaunchKernelGGL(cast_t_kernel<float>, grid, dim3(256), 0, s, (const float*)src, (int)M, cols,
+                       ld_src, dst_t, ldm, dst_rm);
+  else
+    hipLaunchKernelGGL(cast_t_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)src, (int)M, cols,
+                       ld_src, dst_t, ldm, dst_rm);
+  timing_end(s);
+  return hipGetLastError();
+}
+
+int rmsnorm_backward_parts(long long M) { return (int)((M + kNormRows - 1) / kNormRows); }
+
+hipError_t rmsnorm_backward(const float* x, const float* ss, const float* dh, const float* g,
+                            const float* dres, float eps, long long M, int d, float* dx,
+                            float* dg_part, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  timing_begin("rmsnorm_bwd", s);
+  hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3(rmsnorm_backward_parts(M)), dim3(256), 0, s, x, ss, dh,
+                     g, dres, eps, (int)M, d, dx, dg_part);
+  timing_end(s);
+  return hipGetLastError();
+}
+
+hipError_t column_sum(const float* part, int np, int d, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(colsum_kernel, dim3((d + 63) / 64), dim3(1024), 0, s, part, np, d, out);
+  return hipGetLastError();
+}
+
+hipError_t zero_f32(float* p, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
 
 hipError_t ffn_backward(const FfnBwdParams& p, void* ws, hipStream_t s) {
   const long long M = p.M;

@@ -679,7 +679,10 @@ static int k_splits(const GemmParams& p, long long tiles, int BM, int BN, int BK
   if (!p.sk_part || tiles <= 0 || tiles >= 128) return 1;
   const int nk = (p.K + BK - 1) / BK;
   if (nk < 16) return 1;
-  long long sp = std::min<long long>({8, 256 / tiles, nk / 4});
+  // very long contractions (weight gradients over the rows) may split
+  // further, down to 4 K steps per split, until 256 workgroups
+  const long long cap = p.K >= 4096 ? 64 : 8;
+  long long sp = std::min<long long>({cap, 256 / tiles, nk / 4});
   while (sp > 1 && tiles * sp * BM * BN > p.sk_part_cap) --sp;
   return (int)std::max<long long>(sp, 1);
 }

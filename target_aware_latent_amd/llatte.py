@@ -68,6 +68,19 @@ class llatte_ffn_desc(ctypes.Structure):
     _fields_ = [("d", _c_int), ("d_ff", _c_int), ("dtype", _c_int), ("eps", ctypes.c_float)]
 
 
+class llatte_attn_sublayer_desc(ctypes.Structure):
+    _fields_ = [(n, _c_int) for n in ("d", "n_heads", "head_dim", "rank", "n_cand", "dtype",
+                                      "latent_norm")] + [("eps", ctypes.c_float)]
+
+
+class llatte_attn_sublayer_weights(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("g1", "w_dkv", "g_c", "w_uq", "w_uk", "w_uv", "w_o")]
+
+
+class llatte_attn_sublayer_grads(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("g1", "w_dkv", "g_c", "w_uq", "w_uk", "w_uv", "w_o")]
+
+
 class llatte_action_desc(ctypes.Structure):
     _fields_ = [(n, _c_int) for n in (
         "d", "d_hidden", "d_enc", "d_type", "d_item", "d_surf", "d_time",
@@ -143,6 +156,12 @@ _SIGS = {
         _vp, ctypes.c_size_t, _vp]),
     "llatte_ffn_backward_workspace_size": (ctypes.c_size_t, [
         ctypes.POINTER(llatte_ffn_desc), _c_int]),
+    "llatte_attn_sublayer_backward": (_c_int, [
+        ctypes.POINTER(llatte_attn_sublayer_desc), ctypes.POINTER(llatte_attn_sublayer_weights),
+        _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp,
+        ctypes.POINTER(llatte_attn_sublayer_grads), _vp, ctypes.c_size_t, _vp]),
+    "llatte_attn_sublayer_backward_workspace_size": (ctypes.c_size_t, [
+        ctypes.POINTER(llatte_attn_sublayer_desc), _c_int, _c_int, _c_int]),
     "llatte_last_error": (ctypes.c_char_p, []),
     "llatte_version": (_c_int, []),
     "llatte_kernel_timing_enable": (None, [_c_int]),
@@ -343,6 +362,25 @@ def llatte_ffn_backward(desc, r1, g2, w1, w2, d_out, M, d_r1, d_g2, d_w1, d_w2, 
         ctypes.byref(desc), _p(r1), _p(g2), _p(w1), _p(w2), _p(d_out), M, _p(d_r1), _p(d_g2),
         _p(d_w1), _p(d_w2), _p(workspace), nbytes, _stream(stream))
     _check(st, "llatte_ffn_backward")
+
+
+def llatte_attn_sublayer_backward_workspace_size(desc, B, Mtot, Ktot):
+    return lib().llatte_attn_sublayer_backward_workspace_size(ctypes.byref(desc), B, Mtot, Ktot)
+
+
+def llatte_attn_sublayer_backward(desc, weights, r_kv, r_cand, kv_offsets, hq_offsets, B, Mtot,
+                                  Ktot, max_len, d_out, d_r_kv, d_r_cand, grads, workspace,
+                                  stream=None):
+    """weights / grads: dicts of tensors keyed g1, w_dkv, g_c, w_uq, w_uk, w_uv, w_o."""
+    keys = ("g1", "w_dkv", "g_c", "w_uq", "w_uk", "w_uv", "w_o")
+    w = llatte_attn_sublayer_weights(*[_p(weights.get(k)) for k in keys])
+    g = llatte_attn_sublayer_grads(*[_p(grads.get(k)) for k in keys])
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().llatte_attn_sublayer_backward(
+        ctypes.byref(desc), ctypes.byref(w), _p(r_kv), _p(r_cand), _p(kv_offsets), _p(hq_offsets),
+        B, Mtot, Ktot, max_len, _p(d_out), _p(d_r_kv), _p(d_r_cand), ctypes.byref(g),
+        _p(workspace), nbytes, _stream(stream))
+    _check(st, "llatte_attn_sublayer_backward")
 
 
 def llatte_last_error():

@@ -126,6 +126,40 @@ def test_attention_backward_argument_errors(L):
     assert bw(ctypes.byref(ad), *bad, need, None) == L.LLATTE_ERR_INVALID_ARG
 
 
+def test_sublayer_and_ffn_backward_argument_errors(L):
+    fake = ctypes.c_void_p(1 << 20)
+    keys = ("g1", "w_dkv", "g_c", "w_uq", "w_uk", "w_uv", "w_o")
+    w = L.llatte_attn_sublayer_weights(*[fake] * 7)
+    g = L.llatte_attn_sublayer_grads(*[fake] * 7)
+    sb = L.lib().llatte_attn_sublayer_backward
+    args = lambda B=2, M=10, K=10: [fake, fake, fake, fake, B, M, K, 5, fake, fake, fake]
+    d = L.llatte_attn_sublayer_desc(64, 2, 32, 96, 0, L.LLATTE_BF16, 1, 1e-6)
+    assert sb(ctypes.byref(d), ctypes.byref(w), *args(), ctypes.byref(g), fake, 1 << 40, None) == \
+        L.LLATTE_ERR_UNSUPPORTED
+    d = L.llatte_attn_sublayer_desc(64, 2, 30, 64, 0, L.LLATTE_BF16, 1, 1e-6)
+    assert sb(ctypes.byref(d), ctypes.byref(w), *args(), ctypes.byref(g), fake, 1 << 40, None) == \
+        L.LLATTE_ERR_INVALID_ARG
+    d = L.llatte_attn_sublayer_desc(64, 2, 32, 64, 0, L.LLATTE_BF16, 1, 1e-6)
+    need = L.llatte_attn_sublayer_backward_workspace_size(d, 2, 10, 10)
+    assert need > 0
+    assert sb(ctypes.byref(d), ctypes.byref(w), *args(), ctypes.byref(g), fake, need - 1, None) == \
+        L.LLATTE_ERR_WORKSPACE
+    assert sb(ctypes.byref(d), ctypes.byref(w), *args(B=0), ctypes.byref(g), fake, need, None) == \
+        L.LLATTE_ERR_INVALID_ARG
+    w0 = L.llatte_attn_sublayer_weights(*([fake] * 6 + [None]))
+    assert sb(ctypes.byref(d), ctypes.byref(w0), *args(), ctypes.byref(g), fake, need, None) == \
+        L.LLATTE_ERR_INVALID_ARG
+    f = L.llatte_ffn_desc(64, 256, L.LLATTE_F32, 1e-6)
+    fb = L.lib().llatte_ffn_backward
+    fa = [fake] * 5 + [10] + [fake] * 5
+    assert fb(ctypes.byref(f), *fa, 1 << 40, None) == L.LLATTE_ERR_UNSUPPORTED
+    f = L.llatte_ffn_desc(60, 256, L.LLATTE_BF16, 1e-6)
+    assert fb(ctypes.byref(f), *fa, 1 << 40, None) == L.LLATTE_ERR_INVALID_ARG
+    f = L.llatte_ffn_desc(64, 256, L.LLATTE_BF16, 1e-6)
+    need = L.llatte_ffn_backward_workspace_size(f, 10)
+    assert fb(ctypes.byref(f), *fa, need - 1, None) == L.LLATTE_ERR_WORKSPACE
+
+
 def _rule(L, r):
     from target_aware_latent_amd.model import make_desc
     cfg = synth.Config("x", B=1, L=1, len_range=None, d=8, h=1, dk=8, r=8,

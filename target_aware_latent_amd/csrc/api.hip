@@ -1437,7 +1437,7 @@ static llatte_status sublayer_backward_run(
     const llatte_attn_sublayer_grads* G, void* workspace, size_t* bytes, bool launch,
     hipStream_t s) {
   const int d = D->d, h = D->n_heads, dk = D->head_dim, r = D->rank, hd = h * dk, hr = h * r;
-  const long long M = Mtot, K = Ktot, nc = (long long)B * D->n_cand, nh = M - nc;
+  const long long M = Mtot, K = Ktot, nc = (long long)B * D->n_cand;
   const int ldm = (int)cdiv(M, 8) * 8, ldk = (int)cdiv(K, 8) * 8;
   const bool ln = D->latent_norm != 0;
   const float eps = D->eps;
@@ -1455,7 +1455,7 @@ static llatte_status sublayer_backward_run(
   bf16* Cb = ar.take<bf16>(K * r);
   float* ss_C = ar.take<float>(K);
   bf16* Hq = ar.take<bf16>(M * d);
-  int* hist_map = ar.take<int>(nh > 0 ? nh : 1);
+  int* qmap = ar.take<int>(K);
   bf16* WuqT = ar.take<bf16>((size_t)hd * d);
   bf16* q = ar.take<bf16>(M * hd);
   bf16* qt = ar.take<bf16>(M * hr);
@@ -1488,7 +1488,6 @@ static llatte_status sublayer_backward_run(
   bf16* dC0T = ar.take<bf16>((size_t)r * ldk);
   bf16* HT = ar.take<bf16>((size_t)d * ldk);
   float* dH = ar.take<float>(K * d);
-  float* dres = ar.take<float>(K * d);
   float* dg_part = ar.take<float>((size_t)std::max((long long)(pk + pc) * d, (long long)pk * r));
   float* sk = ar.take<float>(kSubSkPart);
   if (!launch) {
@@ -1543,7 +1542,7 @@ static llatte_status sublayer_backward_run(
   HIP_TRY(mm(H, d, 0, WdkvT, d, 0, K, r, d, C0, r, 0, 1, true, false, "gemm_sub_c0"));
   HIP_TRY(norm_rows(RowSrc{C0, C0, 0, r}, (int)K, nullptr, ln ? W->g_c : nullptr, eps, nullptr, 0, Cb,
                     r, r, K_BF16, s, ln ? ss_C : nullptr));
-  HIP_TRY(gather_query_rows(Hc, H, kv_off, hq_off, B, D->n_cand, d, Hq, hist_map, s));
+  HIP_TRY(gather_query_rows(Hc, H, kv_off, hq_off, B, D->n_cand, d, Hq, qmap, s));
   HIP_TRY(transpose(W->w_uq, d, hd, hd, 0, WuqT, d, 0, 1, K_BF16, K_BF16, s));
   HIP_TRY(mm(Hq, d, 0, WuqT, d, 0, M, hd, d, q, hd, 0, 1, false, false, "gemm_sub_q"));
   HIP_TRY(mm(q, hd, dk, W->w_uk, hd, dk, M, r, dk, qt, hr, r, h, false, false, "gemm_sub_qlat"));
@@ -1552,7 +1551,8 @@ static llatte_status sublayer_backward_run(
                                                   attn_ws, aws, s);
     if (st != LLATTE_OK) return st;
   }
-  HIP_TRY(cast_f32(ot, otb, M * hr, true, s));
+  // õ as bf16, row-major (the W_uv product) and transposed (dW_uv)
+  HIP_TRY(cast_transpose(ot, true, M, hr, hr, otT, ldm, otb, s));
   HIP_TRY(transpose(W->w_uv, r, hd, hd, 0, WuvT, r, 0, 1, K_BF16, K_BF16, s));
   HIP_TRY(transpose(W->w_uk, r, hd, hd, 0, WukT, r, 0, 1, K_BF16, K_BF16, s));
   HIP_TRY(mm(otb, hr, r, WuvT, r, (long long)dk * r, M, dk, r, o, hd, dk, h, false, false, "gemm_sub_o"));
@@ -1561,7 +1561,6 @@ static llatte_status sublayer_backward_run(
   HIP_TRY(cast_transpose(o, false, M, hd, hd, oT, ldm, nullptr, s));
   HIP_TRY(mm(oT, ldm, 0, dRT, ldm, 0, hd, d, ldm, G->w_o, d, 0, 1, true, true, "gemm_sub_dwo"));
   HIP_TRY(mm(dRb, d, 0, W->w_o, d, 0, M, hd, d, dob, hd, 0, 1, false, false, "gemm_sub_do"));
-  HIP_TRY(cast_transpose(otb, false, M, hr, hr, otT, ldm, nullptr, s));
   HIP_TRY(cast_transpose(dob, false, M, hd, hd, doT, ldm, nullptr, s));
   HIP_TRY(mm(otT, ldm, (long long)r * ldm, doT, ldm, (long long)dk * ldm, r, dk, ldm, G->w_uv, hd, dk, h,
              true, true, "gemm_sub_dwuv"));
@@ -1589,9 +1588,9 @@ static llatte_status sublayer_backward_run(
   HIP_TRY(cast_transpose(H, false, K, d, d, HT, ldk, nullptr, s));
   HIP_TRY(mm(HT, ldk, 0, dC0T, ldk, 0, d, r, ldk, G->w_dkv, r, 0, 1, true, true, "gemm_sub_dwdkv"));
   HIP_TRY(mm(dC0b, r, 0, W->w_dkv, r, 0, K, d, r, dH, d, 0, 1, true, false, "gemm_sub_dh"));
-  HIP_TRY(zero_f32(dres, K * d, s));
-  HIP_TRY(scatter_query_rows(dHq, d_out, hist_map, nh, nc, d, dH, dres, s));
-  HIP_TRY(rmsnorm_backward(r_kv, ss_kv, dH, W->g1, dres, eps, K, d, d_r_kv, dg_part, s));
+  // the query rows' dH and residual gradient join their history rows
+  HIP_TRY(rmsnorm_backward(r_kv, ss_kv, dH, W->g1, nullptr, eps, K, d, d_r_kv, dg_part, s, qmap, dHq,
+                           d_out));
   if (nc)
     HIP_TRY(rmsnorm_backward(r_cand, ss_c, dHq, W->g1, d_out, eps, nc, d, d_r_cand,
                              dg_part + (size_t)pk * d, s));

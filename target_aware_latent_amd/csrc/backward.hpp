@@ -63,11 +63,13 @@ hipError_t cast_transpose(const void* src, bool src_f32, long long M, int cols, 
 // RMSNorm backward over M rows of width d (<= 1024, multiple of 4):
 // dx = dres + s (dh g - xh mean(dh g xh)) with s from ss = sum(x^2) per
 // row (dres optional), and per-block partial column sums of dh * xh in
-// dg_part [rmsnorm_backward_parts(M), d].
+// dg_part [rmsnorm_backward_parts(M), d]. With qmap, row i with
+// qmap[i] >= 0 adds row qmap[i] of dh_q to dh and of dres_q to dres.
 int rmsnorm_backward_parts(long long M);
 hipError_t rmsnorm_backward(const float* x, const float* ss, const float* dh, const float* g,
                             const float* dres, float eps, long long M, int d, float* dx,
-                            float* dg_part, hipStream_t s);
+                            float* dg_part, hipStream_t s, const int* qmap = nullptr,
+                            const float* dh_q = nullptr, const float* dres_q = nullptr);
 // out[c] = sum over p < np of part[p][c] in a fixed order.
 hipError_t column_sum(const float* part, int np, int d, float* out, hipStream_t s);
 hipError_t zero_f32(float* p, long long n, hipStream_t s);
@@ -75,14 +77,9 @@ hipError_t zero_f32(float* p, long long n, hipStream_t s);
 // ------------------------------------------------------------------ attention sublayer
 // Hq [Mtot, d] (bf16) = the candidate rows Hc [B*n_cand, d], then user u's
 // last n_u rows of H (H row kv_off[u] + K_u - n_u + t goes to row
-// B*n_cand + hq_off[u] + t); hist_map[hq_off[u] + t] = that H row. d is a
-// multiple of 8.
+// B*n_cand + hq_off[u] + t); qmap[H row] = that query row, or -1 for the
+// user's other rows (every H row is written). d is a multiple of 8.
 hipError_t gather_query_rows(const bf16* Hc, const bf16* H, const int* kv_off, const int* hq_off,
-                             int B, int n_cand, int d, bf16* Hq, int* hist_map, hipStream_t s);
-// For history query row j < nh: dH[hist_map[j]] += dHq[nc + j] and
-// dres[hist_map[j]] = dRq[nc + j] (rows of width d, a multiple of 4; the
-// mapped rows are distinct).
-hipError_t scatter_query_rows(const float* dHq, const float* dRq, const int* hist_map, long long nh,
-                              long long nc, int d, float* dH, float* dres, hipStream_t s);
+                             int B, int n_cand, int d, bf16* Hq, int* qmap, hipStream_t s);
 
 }  // namespace llatte

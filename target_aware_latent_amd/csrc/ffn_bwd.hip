@@ -108,7 +108,9 @@ __global__ __launch_bounds__(256) void gelu_bwd_kernel(const float* A, const flo
 }
 
 // RMSNorm backward with the residual (dres, optional), one wave per row,
-// kNormRows rows per block: s = 1 / sqrt(ss / d + eps), xh = x s, dxh = dh g,
+// kNormRows rows per block; with qmap, row i also takes dh_q and dres_q of
+// row qmap[i] when that is >= 0 (a layer's query rows feeding back into
+// its input rows): s = 1 / sqrt(ss / d + eps), xh = x s, dxh = dh g,
 // dx = dres + s (dxh - xh mean(dxh xh)); and the block's partial sums of
 // dh * xh per column (the gain's gradient), summed over the block's rows in
 // row order and then over its waves in wave order.
@@ -116,7 +118,9 @@ constexpr int kNormRows = 64;
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* x, const float* ss,
                                                          const float* dh, const float* g,
                                                          const float* dres, float eps, int M,
-                                                         int d, float* dx, float* dg_part) {
+                                                         int d, float* dx, float* dg_part,
+                                                         const int* qmap, const float* dh_q,
+                                                         const float* dres_q) {
   constexpr int MAXV = 4;  // d <= 1024
   __shared__ float red[4][1024];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -132,6 +136,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* x, const 
     const int row = r0 + i;
     if (row >= M) break;
     const float s = 1.f / sqrtf(ss[row] / (float)d + eps);
+    const int qi = qmap ? qmap[row] : -1;
     f32x4 xh[MAXV], dxh[MAXV], hv[MAXV];
     float dot = 0.f;
 #pragma unroll
@@ -141,6 +146,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* x, const 
       if (idx < d) {
         xh[j] = *(const f32x4*)(x + (size_t)row * d + idx) * s;
         hv[j] = *(const f32x4*)(dh + (size_t)row * d + idx);
+        if (qi >= 0) hv[j] += *(const f32x4*)(dh_q + (size_t)qi * d + idx);
         dxh[j] = hv[j] * gv[j];
 #pragma unroll
         for (int k = 0; k < 4; ++k) dot = fmaf(dxh[j][k], xh[j][k], dot);
@@ -151,7 +157,8 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* x, const 
     for (int j = 0; j < MAXV; ++j) {
       const int idx = j * 256 + lane * 4;
       if (idx >= d) continue;
-      const f32x4 r = dres ? *(const f32x4*)(dres + (size_t)row * d + idx) : f32x4{};
+      f32x4 r = dres ? *(const f32x4*)(dres + (size_t)row * d + idx) : f32x4{};
+      if (qi >= 0) r += *(const f32x4*)(dres_q + (size_t)qi * d + idx);
       *(f32x4*)(dx + (size_t)row * d + idx) = r + (dxh[j] - xh[j] * mean) * s;
       acc[j] += hv[j] * xh[j];
     }
@@ -273,11 +280,12 @@ int rmsnorm_backward_parts(long long M) { return (int)((M + kNormRows - 1) / kNo
 
 hipError_t rmsnorm_backward(const float* x, const float* ss, const float* dh, const float* g,
                             const float* dres, float eps, long long M, int d, float* dx,
-                            float* dg_part, hipStream_t s) {
+                            float* dg_part, hipStream_t s, const int* qmap, const float* dh_q,
+                            const float* dres_q) {
   if (M <= 0) return hipSuccess;
   timing_begin("rmsnorm_bwd", s);
   hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3(rmsnorm_backward_parts(M)), dim3(256), 0, s, x, ss, dh,
-                     g, dres, eps, (int)M, d, dx, dg_part);
+                     g, dres, eps, (int)M, d, dx, dg_part, qmap, dh_q, dres_q);
   timing_end(s);
   return hipGetLastError();
 }
@@ -357,7 +365,8 @@ hipError_t ffn_backward(const FfnBwdParams& p, void* ws, hipStream_t s) {
   const int nb = (int)((M + kNormRows - 1) / kNormRows);
   timing_begin("rmsnorm_bwd", s);
   hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3(nb), dim3(256), 0, s, p.r1, w.ss, w.dH2, p.g2, p.dout,
-                     p.eps, (int)M, d, p.dr1, w.dg_part);
+                     p.eps, (int)M, d, p.dr1, w.dg_part, (const int*)nullptr, (const float*)nullptr,
+                     (const float*)nullptr);
   hipLaunchKernelGGL(colsum_kernel, dim3((d + 63) / 64), dim3(1024), 0, s, w.dg_part, nb, d, p.dg2);
   timing_end(s);
   return hipGetLastError();

@@ -729,8 +729,12 @@ static TileCfg select_tile(const GemmParams& p, bool is_bf16) {
   }
   if (is_bf16) {
     // long contractions over few output tiles (weight gradients, K = rows):
-    // the large tile, with K split across the GPU
-    if (p.sk_part && p.K >= 4096 && p.batch == 1 && ntiles(p, 128, 128) < 128) return T128x128;
+    // the large tile, with K split across the GPU; below 16 large tiles the
+    // small one, whose split sums stay short for the reduce pass (one
+    // workgroup per output tile)
+    if (p.sk_part && p.K >= 4096 && p.batch == 1 && ntiles(p, 128, 128) >= 16 &&
+        ntiles(p, 128, 128) < 128)
+      return T128x128;
     if (ntiles(p, 128, 128) < 256) return T64x64;
     if (p.N <= 64) return T128x64;
     return T128x128;

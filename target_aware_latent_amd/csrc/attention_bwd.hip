@@ -36,6 +36,8 @@
 // that the 16-byte operand reads (16 rows x 4 chunks), the transpose reads
 // (8 rows x 4 eight-byte chunks per 32 lanes) and the 16-byte staging writes
 // each touch every bank of a cycle at most once.
+#include <type_traits>
+
 #include "backward.hpp"
 
 namespace llatte {
@@ -63,6 +65,10 @@ __device__ __forceinline__ bf16x4 lds_tr(const bf16* p) {
   auto q = (bwd_lds_hx4*)((bwd_lds_f16*)(f16*)p);
   return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(q));
 }
+
+// 2^x with the hardware instruction alone (no range scaling): arguments
+// here are x = s - lse <= ~0, and probabilities below 2^-126 flush to 0.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -126,7 +132,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdParams p) {
   if (t0 >= ur.total) return;
   const int nc = p.B * p.n_cand, h = p.h;
 
-  const int t = t0 + wave * 16 + lr;
+  const int t0w = t0 + wave * 16;  // the wave's first row
+  const int t = t0w + lr;
   const bool valid = t < ur.total;
   const size_t rowoff = valid ? ((size_t)ur.global_row(t, u, nc, p.n_cand) * h + hh) * R : 0;
   bf16x8 qf[NKS], gh[NKS], gl[NKS];
@@ -213,17 +220,24 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdParams p) {
     // kk*32 + 4 lg + e (block 2kk) and kk*32 + 16 + 4 lg + e (block 2kk+1)
     bf16x8 dsh[2], dsl[2];
     const int k0 = kt * kKeys;
+    auto make_ds = [&](auto unmasked) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = k0 + nb * 16 + lg * 4 + e;
-        const float pr = key <= pos ? exp2f(s[nb][e] * sl2 - lse2) : 0.f;
-        const float ds = pr * (dp[nb][e] - D);
-        const bf16 hi = to_bf16(ds);
-        dsh[nb >> 1][(nb & 1) * 4 + e] = hi;
-        dsl[nb >> 1][(nb & 1) * 4 + e] = to_bf16(ds - from_bf16(hi));
-      }
+        for (int e = 0; e < 4; ++e) {
+          const int key = k0 + nb * 16 + lg * 4 + e;
+          const bool ok = decltype(unmasked)::value || key <= pos;
+          const float pr = ok ? exp2_hw(s[nb][e] * sl2 - lse2) : 0.f;
+          const float ds = pr * (dp[nb][e] - D);
+          const bf16 hi = to_bf16(ds);
+          dsh[nb >> 1][(nb & 1) * 4 + e] = hi;
+          dsl[nb >> 1][(nb & 1) * 4 + e] = to_bf16(ds - from_bf16(hi));
+        }
+    };
+    // the wave's 16 rows all valid and all seeing the whole tile (positions
+    // grow with the row): no mask (a wave-uniform branch)
+    if (t0w + 16 <= ur.total && ur.pos(t0w) >= k0 + kKeys - 1) make_ds(std::true_type{});
+    else make_ds(std::false_type{});
     // d_q += dS C: A = C^T rows rb*16.. (transpose loads), keys in the same order
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -256,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dc_kernel(AttnBwdParams p) {
   constexpr int TILE = kCRows * LD;
   constexpr int NLD = 3 * kCRows * R / 8 / 256;
   __shared__ __attribute__((aligned(16))) bf16 Ts[2][3 * TILE];
-  __shared__ float s_lse2[2][kCRows], s_D[2][kCRows];
+  __shared__ __attribute__((aligned(16))) float s_lse2[2][kCRows], s_D[2][kCRows];
   const int ngroups = p.dc_accumulate ? 2 : 1;
   const int u = blockIdx.x / ngroups, grp = blockIdx.x % ngroups, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, lr = lane & 15, lg = lane >> 4;
@@ -290,19 +304,39 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dc_kernel(AttnBwdParams p) {
 
   bf16x8 stage[NLD];
   float meta = 0.f;
+  // staging piece i of a thread: tile i / (pieces per tile) (q, d_out high,
+  // d_out low), row rr, column c; its offset from the block's first row is
+  // fixed across the loop
+  constexpr int PPT = kCRows * R / 8;  // 16-byte pieces per tile (a multiple of 256)
+  int soff[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int w = (tid + 256 * i) % PPT;
+    soff[i] = (w / (R / 8)) * h * R + (w % (R / 8)) * 8;
+  }
+  auto tile_src = [&](int i) -> const bf16* {
+    const int tile = 256 * i / PPT;
+    return tile == 0 ? (const bf16*)p.q : tile == 1 ? p.ws_ghi : p.ws_glo;
+  };
   auto gload = [&](int it) {
     const int hh = h0 + it / nrb, t0 = t_first + (it % nrb) * kCRows;
+    if (t0 + kCRows <= ur.n) {
+      // 32 history rows: consecutive global rows from nc + hq0 + t0
+      const size_t base = ((size_t)(nc + ur.hq0 + t0) * h + hh) * R;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int e = tid + 256 * i, tile = e / (kCRows * R / 8), w = e % (kCRows * R / 8);
-      const int rr = w / (R / 8), c = (w % (R / 8)) * 8, t = t0 + rr;
-      bf16x8 v{};
-      if (t < ur.total) {
-        const size_t o = ((size_t)ur.global_row(t, u, nc, p.n_cand) * h + hh) * R + c;
-        const bf16* src = tile == 0 ? (const bf16*)p.q : tile == 1 ? p.ws_ghi : p.ws_glo;
-        v = *(const bf16x8*)(src + o);
+      for (int i = 0; i < NLD; ++i) stage[i] = *(const bf16x8*)(tile_src(i) + base + soff[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int w = (tid + 256 * i) % PPT;
+        const int rr = w / (R / 8), c = (w % (R / 8)) * 8, t = t0 + rr;
+        bf16x8 v{};
+        if (t < ur.total) {
+          const size_t o = ((size_t)ur.global_row(t, u, nc, p.n_cand) * h + hh) * R + c;
+          v = *(const bf16x8*)(tile_src(i) + o);
+        }
+        stage[i] = v;
       }
-      stage[i] = v;
     }
     if (tid < 2 * kCRows) {
       const int rr = tid % kCRows, t = t0 + rr;
@@ -361,25 +395,35 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dc_kernel(AttnBwdParams p) {
       }
     // P and scale * dS in two bf16 parts, rows 4 lg + e then 16 + 4 lg + e
     bf16x8 ph[2], pl[2], dh[2], dl[2];
+    auto make_p = [&](auto unmasked) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < 2; ++nb) {
+        const f32x4 lse4 = *(const f32x4*)&s_lse2[buf][nb * 16 + lg * 4];
+        const f32x4 D4 = *(const f32x4*)&s_D[buf][nb * 16 + lg * 4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int rr = nb * 16 + lg * 4 + e, t = t0 + rr;
-        const int pos = t < ur.total ? ur.pos(t) : -1;
-        const float lse2 = s_lse2[buf][rr], D = s_D[buf][rr];
+        for (int e = 0; e < 4; ++e) {
+          const int t = t0 + nb * 16 + lg * 4 + e;
+          int pos = 0;
+          if constexpr (!decltype(unmasked)::value) pos = t < ur.total ? ur.pos(t) : -1;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int key = kw + kb * 16 + lr;
-          const float pr = key <= pos ? exp2f(s[kb][nb][e] * sl2 - lse2) : 0.f;
-          const float ds = p.scale * pr * (dp[kb][nb][e] - D);
-          const bf16 a = to_bf16(pr), b = to_bf16(ds);
-          ph[kb][nb * 4 + e] = a;
-          pl[kb][nb * 4 + e] = to_bf16(pr - from_bf16(a));
-          dh[kb][nb * 4 + e] = b;
-          dl[kb][nb * 4 + e] = to_bf16(ds - from_bf16(b));
+          for (int kb = 0; kb < 2; ++kb) {
+            const int key = kw + kb * 16 + lr;
+            const bool ok = decltype(unmasked)::value || key <= pos;
+            const float pr = ok ? exp2_hw(s[kb][nb][e] * sl2 - lse4[e]) : 0.f;
+            const float ds = p.scale * pr * (dp[kb][nb][e] - D4[e]);
+            const bf16 a = to_bf16(pr), b = to_bf16(ds);
+            ph[kb][nb * 4 + e] = a;
+            pl[kb][nb * 4 + e] = to_bf16(pr - from_bf16(a));
+            dh[kb][nb * 4 + e] = b;
+            dl[kb][nb * 4 + e] = to_bf16(ds - from_bf16(b));
+          }
         }
       }
+    };
+    // all 32 rows valid and seeing all of the wave's keys (the smallest
+    // position is the first row's): no mask (a wave-uniform branch)
+    if (t0 + kCRows <= ur.total && ur.pos(t0) >= kw + 31) make_p(std::true_type{});
+    else make_p(std::false_type{});
     // d_C += P^T d_out + scale dS^T q: A = d_out^T / q^T rows rb*16..
     // (transpose loads over the tile's 32 rows), B = P^T / dS^T
 #pragma unroll

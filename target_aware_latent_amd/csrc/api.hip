@@ -1426,7 +1426,7 @@ static const char* check_sublayer_desc(const llatte_attn_sublayer_desc* D, int* 
   return nullptr;
 }
 
-constexpr long long kSubSkPart = 1ll << 22;  // split-K scratch (floats)
+constexpr long long kSubSkPart = 1ll << 23;  // split-K scratch (floats)
 
 // Carves the workspace and, with launch set, enqueues the whole backward.
 // Returns the workspace bytes through *bytes when launch is false.
@@ -1438,7 +1438,6 @@ static llatte_status sublayer_backward_run(
     hipStream_t s) {
   const int d = D->d, h = D->n_heads, dk = D->head_dim, r = D->rank, hd = h * dk, hr = h * r;
   const long long M = Mtot, K = Ktot, nc = (long long)B * D->n_cand;
-  const int ldm = (int)cdiv(M, 8) * 8, ldk = (int)cdiv(K, 8) * 8;
   const bool ln = D->latent_norm != 0;
   const float eps = D->eps;
   llatte_attn_desc ad{h, r, D->n_cand, LLATTE_BF16, 1.f / sqrtf((float)dk)};
@@ -1467,26 +1466,16 @@ static llatte_status sublayer_backward_run(
   bf16* WukT = ar.take<bf16>((size_t)hd * r);
   bf16* o = ar.take<bf16>(M * hd);
   bf16* dRb = ar.take<bf16>(M * d);
-  bf16* dRT = ar.take<bf16>((size_t)d * ldm);
-  bf16* oT = ar.take<bf16>((size_t)hd * ldm);
   bf16* dob = ar.take<bf16>(M * hd);
-  bf16* otT = ar.take<bf16>((size_t)hr * ldm);
-  bf16* doT = ar.take<bf16>((size_t)hd * ldm);
   float* dot_ = ar.take<float>(M * hr);
   char* abw_ws = ar.take<char>(bws);
   float* dqt = ar.take<float>(M * hr);
   bf16* dqtb = ar.take<bf16>(M * hr);
-  bf16* dqtT = ar.take<bf16>((size_t)hr * ldm);
   bf16* dq = ar.take<bf16>(M * hd);
-  bf16* qT = ar.take<bf16>((size_t)hd * ldm);
-  bf16* HqT = ar.take<bf16>((size_t)d * ldm);
-  bf16* dqT = ar.take<bf16>((size_t)hd * ldm);
   float* dHq = ar.take<float>(M * d);
   float* dC = ar.take<float>(K * r);
   float* dC0 = ln ? ar.take<float>(K * r) : dC;
   bf16* dC0b = ar.take<bf16>(K * r);
-  bf16* dC0T = ar.take<bf16>((size_t)r * ldk);
-  bf16* HT = ar.take<bf16>((size_t)d * ldk);
   float* dH = ar.take<float>(K * d);
   float* dg_part = ar.take<float>((size_t)std::max((long long)(pk + pc) * d, (long long)pk * r));
   float* sk = ar.take<float>(kSubSkPart);
@@ -1551,19 +1540,37 @@ static llatte_status sublayer_backward_run(
                                                   attn_ws, aws, s);
     if (st != LLATTE_OK) return st;
   }
-  // õ as bf16, row-major (the W_uv product) and transposed (dW_uv)
-  HIP_TRY(cast_transpose(ot, true, M, hr, hr, otT, ldm, otb, s));
+  HIP_TRY(cast_f32(ot, otb, M * hr, true, s));  // õ as bf16
   HIP_TRY(transpose(W->w_uv, r, hd, hd, 0, WuvT, r, 0, 1, K_BF16, K_BF16, s));
   HIP_TRY(transpose(W->w_uk, r, hd, hd, 0, WukT, r, 0, 1, K_BF16, K_BF16, s));
   HIP_TRY(mm(otb, hr, r, WuvT, r, (long long)dk * r, M, dk, r, o, hd, dk, h, false, false, "gemm_sub_o"));
   // ---- backward
-  HIP_TRY(cast_transpose(d_out, true, M, d, d, dRT, ldm, dRb, s));
-  HIP_TRY(cast_transpose(o, false, M, hd, hd, oT, ldm, nullptr, s));
-  HIP_TRY(mm(oT, ldm, 0, dRT, ldm, 0, hd, d, ldm, G->w_o, d, 0, 1, true, true, "gemm_sub_dwo"));
+  // weight gradients over the rows: C [n1, n2] (+ head batch) = X^T Y
+  auto wg = [&](const bf16* X, int ldx, long long sX, int n1, const bf16* Y, int ldy, long long sY,
+                int n2, long long rows, float* C, int ldc, long long sC, int batch, const char* name) {
+    WgradParams g;
+    g.X = X;
+    g.ldx = ldx;
+    g.sX = sX;
+    g.Y = Y;
+    g.ldy = ldy;
+    g.sY = sY;
+    g.M = rows;
+    g.N1 = n1;
+    g.N2 = n2;
+    g.batch = batch;
+    g.C = C;
+    g.ldc = ldc;
+    g.sC = sC;
+    g.part = sk;
+    g.part_cap = kSubSkPart;
+    g.name = name;
+    return wgrad(g, s);
+  };
+  HIP_TRY(cast_f32(d_out, dRb, M * d, true, s));
+  HIP_TRY(wg(o, hd, 0, hd, dRb, d, 0, d, M, G->w_o, d, 0, 1, "gemm_sub_dwo"));
   HIP_TRY(mm(dRb, d, 0, W->w_o, d, 0, M, hd, d, dob, hd, 0, 1, false, false, "gemm_sub_do"));
-  HIP_TRY(cast_transpose(dob, false, M, hd, hd, doT, ldm, nullptr, s));
-  HIP_TRY(mm(otT, ldm, (long long)r * ldm, doT, ldm, (long long)dk * ldm, r, dk, ldm, G->w_uv, hd, dk, h,
-             true, true, "gemm_sub_dwuv"));
+  HIP_TRY(wg(otb, hr, r, r, dob, hd, dk, dk, M, G->w_uv, hd, dk, h, "gemm_sub_dwuv"));
   HIP_TRY(mm(dob, hd, dk, W->w_uv, hd, dk, M, r, dk, dot_, hr, r, h, true, false, "gemm_sub_dolat"));
   {
     const llatte_status st = llatte_mla_attention_backward(&ad, qt, Cb, kv_off, hq_off, B, Mtot, Ktot,
@@ -1571,22 +1578,17 @@ static llatte_status sublayer_backward_run(
                                                            bws, s);
     if (st != LLATTE_OK) return st;
   }
-  HIP_TRY(cast_transpose(dqt, true, M, hr, hr, dqtT, ldm, dqtb, s));
+  HIP_TRY(cast_f32(dqt, dqtb, M * hr, true, s));
   HIP_TRY(mm(dqtb, hr, r, WukT, r, (long long)dk * r, M, dk, r, dq, hd, dk, h, false, false, "gemm_sub_dq"));
-  HIP_TRY(cast_transpose(q, false, M, hd, hd, qT, ldm, nullptr, s));
-  HIP_TRY(mm(dqtT, ldm, (long long)r * ldm, qT, ldm, (long long)dk * ldm, r, dk, ldm, G->w_uk, hd, dk, h,
-             true, true, "gemm_sub_dwuk"));
-  HIP_TRY(cast_transpose(Hq, false, M, d, d, HqT, ldm, nullptr, s));
-  HIP_TRY(cast_transpose(dq, false, M, hd, hd, dqT, ldm, nullptr, s));
-  HIP_TRY(mm(HqT, ldm, 0, dqT, ldm, 0, d, hd, ldm, G->w_uq, hd, 0, 1, true, true, "gemm_sub_dwuq"));
+  HIP_TRY(wg(dqtb, hr, r, r, q, hd, dk, dk, M, G->w_uk, hd, dk, h, "gemm_sub_dwuk"));
+  HIP_TRY(wg(Hq, d, 0, d, dq, hd, 0, hd, M, G->w_uq, hd, 0, 1, "gemm_sub_dwuq"));
   HIP_TRY(mm(dq, hd, 0, W->w_uq, hd, 0, M, d, hd, dHq, d, 0, 1, true, false, "gemm_sub_dhq"));
   if (ln) {
     HIP_TRY(rmsnorm_backward(C0, ss_C, dC, W->g_c, nullptr, eps, K, r, dC0, dg_part, s));
     HIP_TRY(column_sum(dg_part, pk, r, G->g_c, s));
   }
-  HIP_TRY(cast_transpose(dC0, true, K, r, r, dC0T, ldk, dC0b, s));
-  HIP_TRY(cast_transpose(H, false, K, d, d, HT, ldk, nullptr, s));
-  HIP_TRY(mm(HT, ldk, 0, dC0T, ldk, 0, d, r, ldk, G->w_dkv, r, 0, 1, true, true, "gemm_sub_dwdkv"));
+  HIP_TRY(cast_f32(dC0, dC0b, K * r, true, s));
+  HIP_TRY(wg(H, d, 0, d, dC0b, r, 0, r, K, G->w_dkv, r, 0, 1, "gemm_sub_dwdkv"));
   HIP_TRY(mm(dC0b, r, 0, W->w_dkv, r, 0, K, d, r, dH, d, 0, 1, true, false, "gemm_sub_dh"));
   // the query rows' dH and residual gradient join their history rows
   HIP_TRY(rmsnorm_backward(r_kv, ss_kv, dH, W->g1, nullptr, eps, K, d, d_r_kv, dg_part, s, qmap, dHq,

@@ -49,17 +49,12 @@ struct FfnBwdParams {
   int d = 0, F = 0;
   float eps = 0.f;
 };
-constexpr long long kFfnSkPart = 1ll << 22;  // split-K scratch (floats)
+constexpr long long kFfnSkPart = 1ll << 23;  // split-K scratch (floats)
 size_t ffn_backward_workspace(long long M, int d, int F);
 hipError_t ffn_backward(const FfnBwdParams& p, void* ws, hipStream_t s);
 
 
 // ------------------------------------------------------------------ shared pieces
-// dst_t [cols, ldm] = bf16(src [M, cols])^T (zero columns m in [M, ldm)),
-// dst_rm (optional) = bf16(src) row-major; src float or bf16; cols, ld_src
-// and ldm even.
-hipError_t cast_transpose(const void* src, bool src_f32, long long M, int cols, int ld_src,
-                          bf16* dst_t, int ldm, bf16* dst_rm, hipStream_t s);
 // RMSNorm backward over M rows of width d (<= 1024, multiple of 4):
 // dx = dres + s (dh g - xh mean(dh g xh)) with s from ss = sum(x^2) per
 // row (dres optional), and per-block partial column sums of dh * xh in
@@ -73,6 +68,30 @@ hipError_t rmsnorm_backward(const float* x, const float* ss, const float* dh, co
 // out[c] = sum over p < np of part[p][c] in a fixed order.
 hipError_t column_sum(const float* part, int np, int d, float* out, hipStream_t s);
 hipError_t zero_f32(float* p, long long n, hipStream_t s);
+
+// ------------------------------------------------------------------ weight gradients
+// C [N1, N2] (float, row stride ldc) = X^T Y over M rows, X [M, N1] and
+// Y [M, N2] bf16 row-major (row strides ldx, ldy; multiples of 8, as are N1
+// and N2), for `batch` problems whose operands advance by sX, sY, sC
+// elements. With part (part_cap floats of scratch) the rows split across
+// the GPU and the splits are added in order.
+struct WgradParams {
+  const bf16* X = nullptr;
+  int ldx = 0;
+  long long sX = 0;
+  const bf16* Y = nullptr;
+  int ldy = 0;
+  long long sY = 0;
+  long long M = 0;
+  int N1 = 0, N2 = 0, batch = 1;
+  float* C = nullptr;
+  int ldc = 0;
+  long long sC = 0;
+  float* part = nullptr;
+  long long part_cap = 0;
+  const char* name = "wgrad";
+};
+hipError_t wgrad(WgradParams p, hipStream_t s);
 
 // ------------------------------------------------------------------ attention sublayer
 // Hq [Mtot, d] (bf16) = the candidate rows Hc [B*n_cand, d], then user u's

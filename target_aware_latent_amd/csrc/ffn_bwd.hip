@@ -6,105 +6,36 @@
 //   dW1 = H2^T dA,           dH2 = dA W1^T,
 //   dg2 = sum_rows dH2 xh,   dR1 = d_out + s (dH2 g2 - xh mean(dH2 g2 xh)).
 // The forward's H2 and A are recomputed (the row norm, one product). The
-// five products run on the tiled bf16 GEMM (both operands K-contiguous):
-// the input gradients take W1 [d, d_ff] and W2 [d_ff, d] in their natural
-// row-major layout, the weight gradients contract over the rows, so their
-// operands are written transposed ([cols, M] padded to a multiple of 8 with
-// zero columns) by the kernels that produce them, and split K across the
-// GPU. The elementwise steps (the GELU derivative, the norm backward) are
-// HBM-bound kernels of their own.
+// recomputation and the input gradients run on the tiled bf16 GEMM (both
+// operands K-contiguous), the input gradients with W1 [d, d_ff] and
+// W2 [d_ff, d] in their natural row-major layout; the weight gradients
+// contract over the rows on the weight-gradient kernel, which reads the
+// row-major activations directly. The elementwise steps (the GELU
+// derivative, the norm backward) are HBM-bound kernels of their own.
 #include "backward.hpp"
 
 namespace llatte {
 
-namespace {
-constexpr int kT = 64;  // transposing tile edge
-}
-
-// dst_t [cols, ldm] = bf16(src [M, cols])^T with zero columns m in [M, ldm);
-// dst_rm (optional) = bf16(src) row-major [M, cols]. Tiles of 64 x 64
-// through LDS (rows of 66 elements against bank conflicts on the column
-// reads); each thread moves pairs of elements, along rows on the way in and
-// along columns on the way out (cols, ld_src and ldm are even).
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-template <typename S>
-__device__ __forceinline__ void load2(const S* p, float& a, float& b) {
-  if constexpr (sizeof(S) == 4) {
-    const float2 v = *(const float2*)p;
-    a = v.x;
-    b = v.y;
-  } else {
-    const bf16x2 v = *(const bf16x2*)p;
-    a = from_bf16(v[0]);
-    b = from_bf16(v[1]);
-  }
-}
-
-template <typename S>
-__global__ __launch_bounds__(256) void cast_t_kernel(const S* src, int M, int cols, int ld_src,
-                                                     bf16* dst_t, int ldm, bf16* dst_rm) {
-  __shared__ bf16 tile[kT][kT + 2];
-  const int m0 = blockIdx.x * kT, c0 = blockIdx.y * kT, tid = threadIdx.x;
-#pragma unroll 4
-  for (int i = 0; i < kT * kT / 512; ++i) {
-    const int e = tid + 256 * i, r = e / (kT / 2), c = (e % (kT / 2)) * 2, m = m0 + r, cc = c0 + c;
-    bf16x2 v{to_bf16(0.f), to_bf16(0.f)};
-    if (m < M && cc < cols) {
-      float a, b;
-      load2(src + (size_t)m * ld_src + cc, a, b);
-      v = bf16x2{to_bf16(a), to_bf16(b)};
-      if (dst_rm) *(bf16x2*)(dst_rm + (size_t)m * cols + cc) = v;
-    }
-    tile[r][c] = v[0];
-    tile[r][c + 1] = v[1];
-  }
-  __syncthreads();
-#pragma unroll 4
-  for (int i = 0; i < kT * kT / 512; ++i) {
-    const int e = tid + 256 * i, c = e / (kT / 2), r = (e % (kT / 2)) * 2, m = m0 + r, cc = c0 + c;
-    if (cc < cols && m < ldm) *(bf16x2*)(dst_t + (size_t)cc * ldm + m) = bf16x2{tile[r][c], tile[r + 1][c]};
-  }
-}
-
 // From the recomputed pre-activation A and dG = d_out W2^T, both [M, F]
-// float: dA = dG * GELU'(A) as bf16 row-major [M, F] and transposed
-// [F, ldm], and GELU(A) transposed [F, ldm] (zero columns m >= M).
-// GELU(a) = a Phi(a), GELU'(a) = Phi(a) + a phi(a) (exact erf).
-__global__ __launch_bounds__(256) void gelu_bwd_kernel(const float* A, const float* dG, int M, int F,
-                                                      bf16* dA, bf16* dAT, bf16* GT, int ldm) {
-  __shared__ bf16 tA[kT][kT + 2], tG[kT][kT + 2];
-  const int m0 = blockIdx.x * kT, c0 = blockIdx.y * kT, tid = threadIdx.x;
-#pragma unroll 4
-  for (int i = 0; i < kT * kT / 512; ++i) {
-    const int e = tid + 256 * i, r = e / (kT / 2), c = (e % (kT / 2)) * 2, m = m0 + r, cc = c0 + c;
-    bf16x2 da{to_bf16(0.f), to_bf16(0.f)}, g = da;
-    if (m < M && cc < F) {
-      const size_t o = (size_t)m * F + cc;
-      const float2 a = *(const float2*)(A + o), dg = *(const float2*)(dG + o);
+// float: dA = dG * GELU'(A) and G = GELU(A), both bf16 row-major, four
+// elements per thread. GELU(a) = a Phi(a), GELU'(a) = Phi(a) + a phi(a)
+// (exact erf).
+__global__ __launch_bounds__(256) void gelu_bwd_kernel(const float* A, const float* dG, long long n,
+                                                      bf16* dA, bf16* G) {
+  const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  const f32x4 a = *(const f32x4*)(A + i), g = *(const f32x4*)(dG + i);
+  bf16x4 da, gv;
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const float x = k ? a.y : a.x;
-        const float Phi = 0.5f * (1.f + erff(x * 0.70710678118654752f));
-        const float phi = 0.39894228040143268f * expf(-0.5f * x * x);
-        da[k] = to_bf16((k ? dg.y : dg.x) * (Phi + x * phi));
-        g[k] = to_bf16(x * Phi);
-      }
-      *(bf16x2*)(dA + o) = da;
-    }
-    tA[r][c] = da[0];
-    tA[r][c + 1] = da[1];
-    tG[r][c] = g[0];
-    tG[r][c + 1] = g[1];
+  for (int k = 0; k < 4; ++k) {
+    const float x = a[k];
+    const float Phi = 0.5f * (1.f + erff(x * 0.70710678118654752f));
+    const float phi = 0.39894228040143268f * expf(-0.5f * x * x);
+    da[k] = to_bf16(g[k] * (Phi + x * phi));
+    gv[k] = to_bf16(x * Phi);
   }
-  __syncthreads();
-#pragma unroll 4
-  for (int i = 0; i < kT * kT / 512; ++i) {
-    const int e = tid + 256 * i, c = e / (kT / 2), r = (e % (kT / 2)) * 2, m = m0 + r, cc = c0 + c;
-    if (cc < F && m < ldm) {
-      *(bf16x2*)(dAT + (size_t)cc * ldm + m) = bf16x2{tA[r][c], tA[r + 1][c]};
-      *(bf16x2*)(GT + (size_t)cc * ldm + m) = bf16x2{tG[r][c], tG[r + 1][c]};
-    }
-  }
+  *(bf16x4*)(dA + i) = da;
+  *(bf16x4*)(G + i) = gv;
 }
 
 // RMSNorm backward with the residual (dres, optional), one wave per row,
@@ -205,13 +136,12 @@ namespace {
 size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct FfnWs {
-  bf16 *H2, *W1T, *dOb, *dOT, *dA, *dAT, *GT, *H2T;
+  bf16 *H2, *W1T, *dOb, *dA, *G;
   float *ss, *A, *dG, *dH2, *dg_part, *sk;
   size_t bytes;
 };
 
 FfnWs ffn_ws(char* base, long long M, int d, int F) {
-  const size_t ldm = (size_t)((M + 7) / 8 * 8);
   const size_t nb = (size_t)((M + kNormRows - 1) / kNormRows);
   FfnWs w{};
   size_t o = 0;
@@ -223,11 +153,8 @@ FfnWs ffn_ws(char* base, long long M, int d, int F) {
   w.H2 = (bf16*)take((size_t)M * d * 2);
   w.W1T = (bf16*)take((size_t)F * d * 2);
   w.dOb = (bf16*)take((size_t)M * d * 2);
-  w.dOT = (bf16*)take((size_t)d * ldm * 2);
   w.dA = (bf16*)take((size_t)M * F * 2);
-  w.dAT = (bf16*)take((size_t)F * ldm * 2);
-  w.GT = (bf16*)take((size_t)F * ldm * 2);
-  w.H2T = (bf16*)take((size_t)d * ldm * 2);
+  w.G = (bf16*)take((size_t)M * F * 2);
   w.ss = (float*)take((size_t)M * 4);
   w.A = (float*)take((size_t)M * F * 4);
   w.dG = (float*)take((size_t)M * F * 4);
@@ -260,21 +187,6 @@ GemmParams plain_gemm(const void* A, int lda, const void* B, int ldb, int M, int
 }  // namespace
 
 size_t ffn_backward_workspace(long long M, int d, int F) { return ffn_ws(nullptr, M, d, F).bytes; }
-
-hipError_t cast_transpose(const void* src, bool src_f32, long long M, int cols, int ld_src,
-                          bf16* dst_t, int ldm, bf16* dst_rm, hipStream_t s) {
-  if (ldm <= 0 || cols <= 0) return hipSuccess;
-  const dim3 grid((ldm + kT - 1) / kT, (cols + kT - 1) / kT);
-  timing_begin("cast_t", s);
-  if (src_f32)
-    hipLaunchKernelGGL(cast_t_kernel<float>, grid, dim3(256), 0, s, (const float*)src, (int)M, cols,
-                       ld_src, dst_t, ldm, dst_rm);
-  else
-    hipLaunchKernelGGL(cast_t_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)src, (int)M, cols,
-                       ld_src, dst_t, ldm, dst_rm);
-  timing_end(s);
-  return hipGetLastError();
-}
 
 int rmsnorm_backward_parts(long long M) { return (int)((M + kNormRows - 1) / kNormRows); }
 
@@ -314,7 +226,6 @@ hipError_t ffn_backward(const FfnBwdParams& p, void* ws, hipStream_t s) {
                        (long long)d);
     return hipGetLastError();
   }
-  const int ldm = (int)((M + 7) / 8 * 8);
   FfnWs w = ffn_ws((char*)ws, M, d, F);
   hipError_t e;
   // H2 = RMSNorm(R1) g2 (bf16) and the rows' sums of squares
@@ -325,40 +236,37 @@ hipError_t ffn_backward(const FfnBwdParams& p, void* ws, hipStream_t s) {
   if ((e = transpose(p.w1, d, F, F, 0, w.W1T, d, 0, 1, K_BF16, K_BF16, s))) return e;
   if ((e = gemm(plain_gemm(w.H2, d, w.W1T, d, (int)M, F, d, w.A, F, "gemm_bwd_a", nullptr), true, s)))
     return e;
-  // d_out as bf16, row-major and transposed
-  {
-    const dim3 grid((ldm + kT - 1) / kT, (d + kT - 1) / kT);
-    timing_begin("cast_t", s);
-    hipLaunchKernelGGL(cast_t_kernel<float>, grid, dim3(256), 0, s, p.dout, (int)M, d, d, w.dOT,
-                       ldm, w.dOb);
-    timing_end(s);
-    if ((e = hipGetLastError())) return e;
-  }
-  // dG = d_out W2^T: B = W2 [F, d] as stored
+  // d_out as bf16; dG = d_out W2^T: B = W2 [F, d] as stored
+  if ((e = cast_f32(p.dout, w.dOb, M * d, true, s))) return e;
   if ((e = gemm(plain_gemm(w.dOb, d, p.w2, d, (int)M, F, d, w.dG, F, "gemm_bwd_dg", nullptr), true, s)))
     return e;
   {
-    const dim3 grid((ldm + kT - 1) / kT, (F + kT - 1) / kT);
+    const long long n = M * F;
     timing_begin("gelu_bwd", s);
-    hipLaunchKernelGGL(gelu_bwd_kernel, grid, dim3(256), 0, s, w.A, w.dG, (int)M, F, w.dA, w.dAT,
-                       w.GT, ldm);
+    hipLaunchKernelGGL(gelu_bwd_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, w.A,
+                       w.dG, n, w.dA, w.G);
     timing_end(s);
     if ((e = hipGetLastError())) return e;
   }
-  // dW2 [F, d] = GELU(A)^T d_out (K = the rows)
-  if ((e = gemm(plain_gemm(w.GT, ldm, w.dOT, ldm, F, d, ldm, p.dW2, d, "gemm_bwd_dw2", w.sk), true, s)))
-    return e;
-  // dW1 [d, F] = H2^T dA
-  {
-    const dim3 grid((ldm + kT - 1) / kT, (d + kT - 1) / kT);
-    timing_begin("cast_t", s);
-    hipLaunchKernelGGL(cast_t_kernel<bf16>, grid, dim3(256), 0, s, w.H2, (int)M, d, d, w.H2T, ldm,
-                       (bf16*)nullptr);
-    timing_end(s);
-    if ((e = hipGetLastError())) return e;
-  }
-  if ((e = gemm(plain_gemm(w.H2T, ldm, w.dAT, ldm, d, F, ldm, p.dW1, F, "gemm_bwd_dw1", w.sk), true, s)))
-    return e;
+  // dW2 [F, d] = GELU(A)^T d_out and dW1 [d, F] = H2^T dA (over the rows)
+  auto wg = [&](const bf16* X, int n1, const bf16* Y, int n2, float* C, const char* name) {
+    WgradParams g;
+    g.X = X;
+    g.ldx = n1;
+    g.Y = Y;
+    g.ldy = n2;
+    g.M = M;
+    g.N1 = n1;
+    g.N2 = n2;
+    g.C = C;
+    g.ldc = n2;
+    g.part = w.sk;
+    g.part_cap = kFfnSkPart;
+    g.name = name;
+    return wgrad(g, s);
+  };
+  if ((e = wg(w.G, F, w.dOb, d, p.dW2, "gemm_bwd_dw2"))) return e;
+  if ((e = wg(w.H2, d, w.dA, F, p.dW1, "gemm_bwd_dw1"))) return e;
   // dH2 = dA W1^T: B = W1 [d, F] as stored
   if ((e = gemm(plain_gemm(w.dA, F, p.w1, F, (int)M, d, F, w.dH2, d, "gemm_bwd_dh", nullptr), true, s)))
     return e;

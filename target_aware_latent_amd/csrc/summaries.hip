@@ -59,16 +59,33 @@ hipError_t lora_merge(const void* W, const void* A, const void* Bm, int rows, in
   return hipGetLastError();
 }
 
-// dst (dtype) = src (float32), n elements.
+// dst (dtype) = src (float32), n elements, four per thread (16-byte loads
+// where src is 16-byte aligned and n a multiple of four; one by one for the
+// tail otherwise).
 template <typename T>
 __global__ __launch_bounds__(256) void cast_kernel(const float* src, T* dst, long long n) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) dst[i] = cvt<T>(src[i]);
+  const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  if (i + 4 <= n && ((uintptr_t)(src + i) & 15) == 0) {
+    const f32x4 v = *(const f32x4*)(src + i);
+    typedef T T4 __attribute__((ext_vector_type(4)));
+    T4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = cvt<T>(v[k]);
+    if (((uintptr_t)(dst + i) & (4 * sizeof(T) - 1)) == 0) {
+      *(T4*)(dst + i) = o;
+      return;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dst[i + k] = o[k];
+    return;
+  }
+  for (long long k = i; k < n && k < i + 4; ++k) dst[k] = cvt<T>(src[k]);
 }
 
 hipError_t cast_f32(const float* src, void* dst, long long n, bool is_bf16, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  const unsigned grid = (unsigned)((n + 255) / 256);
+  const unsigned grid = (unsigned)((n + 1023) / 1024);
   timing_begin("cast", s);
   if (is_bf16)
     hipLaunchKernelGGL(cast_kernel<bf16>, dim3(grid), dim3(256), 0, s, src, (bf16*)dst, n);

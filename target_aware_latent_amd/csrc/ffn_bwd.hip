@@ -8,35 +8,14 @@
 // The forward's H2 and A are recomputed (the row norm, one product). The
 // recomputation and the input gradients run on the tiled bf16 GEMM (both
 // operands K-contiguous), the input gradients with W1 [d, d_ff] and
-// W2 [d_ff, d] in their natural row-major layout; the weight gradients
-// contract over the rows on the weight-gradient kernel, which reads the
-// row-major activations directly. The elementwise steps (the GELU
-// derivative, the norm backward) are HBM-bound kernels of their own.
+// W2 [d_ff, d] in their natural row-major layout; the product dG writes
+// dA = dG GELU'(A) and GELU(A) from its epilogue (A recomputed as bf16).
+// The weight gradients contract over the rows on the weight-gradient
+// kernel, which reads the row-major activations directly. The norm
+// backward is an HBM-bound kernel of its own.
 #include "backward.hpp"
 
 namespace llatte {
-
-// From the recomputed pre-activation A and dG = d_out W2^T, both [M, F]
-// float: dA = dG * GELU'(A) and G = GELU(A), both bf16 row-major, four
-// elements per thread. GELU(a) = a Phi(a), GELU'(a) = Phi(a) + a phi(a)
-// (exact erf).
-__global__ __launch_bounds__(256) void gelu_bwd_kernel(const float* A, const float* dG, long long n,
-                                                      bf16* dA, bf16* G) {
-  const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i >= n) return;
-  const f32x4 a = *(const f32x4*)(A + i), g = *(const f32x4*)(dG + i);
-  bf16x4 da, gv;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float x = a[k];
-    const float Phi = 0.5f * (1.f + erff(x * 0.70710678118654752f));
-    const float phi = 0.39894228040143268f * expf(-0.5f * x * x);
-    da[k] = to_bf16(g[k] * (Phi + x * phi));
-    gv[k] = to_bf16(x * Phi);
-  }
-  *(bf16x4*)(dA + i) = da;
-  *(bf16x4*)(G + i) = gv;
-}
 
 // RMSNorm backward with the residual (dres, optional), one wave per row,
 // kNormRows rows per block; with qmap, row i also takes dh_q and dres_q of
@@ -136,8 +115,8 @@ namespace {
 size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct FfnWs {
-  bf16 *H2, *W1T, *dOb, *dA, *G;
-  float *ss, *A, *dG, *dH2, *dg_part, *sk;
+  bf16 *H2, *W1T, *dOb, *A, *dA, *G;
+  float *ss, *dH2, *dg_part, *sk;
   size_t bytes;
 };
 
@@ -153,11 +132,10 @@ FfnWs ffn_ws(char* base, long long M, int d, int F) {
   w.H2 = (bf16*)take((size_t)M * d * 2);
   w.W1T = (bf16*)take((size_t)F * d * 2);
   w.dOb = (bf16*)take((size_t)M * d * 2);
+  w.A = (bf16*)take((size_t)M * F * 2);
   w.dA = (bf16*)take((size_t)M * F * 2);
   w.G = (bf16*)take((size_t)M * F * 2);
   w.ss = (float*)take((size_t)M * 4);
-  w.A = (float*)take((size_t)M * F * 4);
-  w.dG = (float*)take((size_t)M * F * 4);
   w.dH2 = (float*)take((size_t)M * d * 4);
   w.dg_part = (float*)take(nb * d * 4);
   w.sk = (float*)take((size_t)kFfnSkPart * 4);
@@ -165,7 +143,7 @@ FfnWs ffn_ws(char* base, long long M, int d, int F) {
   return w;
 }
 
-GemmParams plain_gemm(const void* A, int lda, const void* B, int ldb, int M, int N, int K, float* C,
+GemmParams plain_gemm(const void* A, int lda, const void* B, int ldb, int M, int N, int K, void* C,
                       int ldc, const char* name, float* sk) {
   GemmParams g;
   g.A = A;
@@ -234,19 +212,23 @@ hipError_t ffn_backward(const FfnBwdParams& p, void* ws, hipStream_t s) {
     return e;
   // W1^T [F, d] for the recomputed A = H2 W1
   if ((e = transpose(p.w1, d, F, F, 0, w.W1T, d, 0, 1, K_BF16, K_BF16, s))) return e;
-  if ((e = gemm(plain_gemm(w.H2, d, w.W1T, d, (int)M, F, d, w.A, F, "gemm_bwd_a", nullptr), true, s)))
-    return e;
-  // d_out as bf16; dG = d_out W2^T: B = W2 [F, d] as stored
-  if ((e = cast_f32(p.dout, w.dOb, M * d, true, s))) return e;
-  if ((e = gemm(plain_gemm(w.dOb, d, p.w2, d, (int)M, F, d, w.dG, F, "gemm_bwd_dg", nullptr), true, s)))
-    return e;
   {
-    const long long n = M * F;
-    timing_begin("gelu_bwd", s);
-    hipLaunchKernelGGL(gelu_bwd_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, w.A,
-                       w.dG, n, w.dA, w.G);
-    timing_end(s);
-    if ((e = hipGetLastError())) return e;
+    // the pre-activation A (bf16)
+    GemmParams g = plain_gemm(w.H2, d, w.W1T, d, (int)M, F, d, w.A, F, "gemm_bwd_a", nullptr);
+    g.epi = EPI_STORE;
+    if ((e = gemm(g, true, s))) return e;
+  }
+  // d_out as bf16; dG = d_out W2^T (B = W2 [F, d] as stored), whose
+  // epilogue writes dA = dG GELU'(A) and GELU(A)
+  if ((e = cast_f32(p.dout, w.dOb, M * d, true, s))) return e;
+  {
+    GemmParams g = plain_gemm(w.dOb, d, p.w2, d, (int)M, F, d, w.dA, F, "gemm_bwd_dg", nullptr);
+    g.epi = EPI_GELU_BWD;
+    g.table = w.A;
+    g.ld_table = F;
+    g.cast_out = w.G;
+    g.ld_cast = F;
+    if ((e = gemm(g, true, s))) return e;
   }
   // dW2 [F, d] = GELU(A)^T d_out and dW1 [d, F] = H2^T dA (over the rows)
   auto wg = [&](const bf16* X, int n1, const bf16* Y, int n2, float* C, const char* name) {

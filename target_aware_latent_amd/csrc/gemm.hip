@@ -74,6 +74,32 @@ template <typename T> __device__ __forceinline__ float gelu_t(float x) {
   else return gelu_erf(x);
 }
 
+// GELU(a) = a Phi(a) and its derivative Phi(a) + a phi(a) (erf form),
+// elementwise: dg = d GELU'(a), g = GELU(a). On the bf16 path the normal
+// tail Q(|a|) = q e comes from the same Abramowitz & Stegun 7.1.25 form as
+// gelu_erf_bf16, and e = exp(-a^2 / 2) also gives the density
+// phi(a) = e / sqrt(2 pi): Phi(a) = 1 - Q for a >= 0, else Q. Otherwise
+// Phi from erf_as (formula 7.1.26).
+template <typename T>
+__device__ __forceinline__ void gelu_bwd4(f32x4 d, f32x4 a, f32x4& dg, f32x4& g) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float x = a[k];
+    const float e = __builtin_amdgcn_exp2f(x * x * (-0.5f * 1.4426950408889634f));
+    float Phi;
+    if constexpr (__is_same(T, bf16)) {
+      const float ax = fabsf(x);
+      const float t = __builtin_amdgcn_rcpf(fmaf(0.47047f * 0.70710678118654752f, ax, 1.f));
+      const float Q = t * fmaf(t, fmaf(t, 0.5f * 0.7478556f, 0.5f * -0.0958798f), 0.5f * 0.3480242f) * e;
+      Phi = x >= 0.f ? 1.f - Q : Q;
+    } else {
+      Phi = 0.5f * (1.f + erf_as(x * 0.70710678118654752f));
+    }
+    dg[k] = d[k] * fmaf(x, e * 0.39894228040143268f, Phi);
+    g[k] = x * Phi;
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
 template <>
@@ -239,6 +265,18 @@ __device__ __forceinline__ void epilogue_rowmajor(const GemmParams p, const f32x
       each([&](int ps, int h, int m, int n) {
         const f32x4 x = v[ps][h] + r[ps][h];
         store4<float>((float*)p.C + coff(m, n), x[0], x[1], x[2], x[3]);
+      });
+    } break;
+    case EPI_GELU_BWD: {
+      f32x4 a[NPASS][2];
+      each([&](int ps, int h, int m, int n) {
+        a[ps][h] = load4<T>((const T*)p.table + (size_t)m * p.ld_table + n);
+      });
+      each([&](int ps, int h, int m, int n) {
+        f32x4 dg, g;
+        gelu_bwd4<T>(v[ps][h], a[ps][h], dg, g);
+        store4h<NTS, T>((T*)p.C + coff(m, n), dg[0], dg[1], dg[2], dg[3]);
+        store4<T>((T*)p.cast_out + (size_t)m * p.ld_cast + n, g[0], g[1], g[2], g[3]);
       });
     } break;
     case EPI_ROWNORM: {
@@ -666,6 +704,16 @@ __global__ __launch_bounds__(64 * NW, (gemm_min_waves<BN, NW>())) void gemm_kern
         store4<float>((float*)p.C + coff(m, n), v[0], v[1], v[2], v[3]);
       });
     } break;
+    case EPI_GELU_BWD:
+      outs([&](int i, int j, int m, int n) {
+        const f32x4 a = load4<T>((const T*)p.table + (size_t)m * p.ld_table + n);
+        const f32x4 v = acc[i][j] * rsc[i];
+        f32x4 dg, g;
+        gelu_bwd4<T>(v, a, dg, g);
+        store4<T>((T*)p.C + coff(m, n), dg[0], dg[1], dg[2], dg[3]);
+        store4<T>((T*)p.cast_out + (size_t)m * p.ld_cast + n, g[0], g[1], g[2], g[3]);
+      });
+      break;
   }
 }
 

@@ -28,6 +28,8 @@ enum GemmEpi {
   EPI_GATHER_ADD_F32 = 4,  // C (float) = acc + table[g_rows[m]]
   EPI_ROWNORM = 5,     // C (out_kind) = gain ? RMSNorm(acc) * gain : acc;
                        // with a gain the tile must span all N columns
+  EPI_GELU_BWD = 6,    // with a = table[m][n] (dtype): C (dtype) = acc GELU'(a),
+                       // cast_out (dtype) = GELU(a)  (exact erf)
 };
 
 // Fused RMSNorm of the A rows. A holds the rows x unscaled (cast to the

@@ -25,58 +25,91 @@ namespace llatte {
 // dh * xh per column (the gain's gradient), summed over the block's rows in
 // row order and then over its waves in wave order.
 constexpr int kNormRows = 64;
+// G row groups per wave (64 / G lanes per row; G = 2 for rows of at most
+// 128), two rows per group in flight at a time: a wave's 16 rows take 8 / G
+// iterations, each loading its rows before reducing them.
+template <int G>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* x, const float* ss,
                                                          const float* dh, const float* g,
                                                          const float* dres, float eps, int M,
                                                          int d, float* dx, float* dg_part,
                                                          const int* qmap, const float* dh_q,
                                                          const float* dres_q) {
-  constexpr int MAXV = 4;  // d <= 1024
+  constexpr int LG = 64 / G;               // lanes per row
+  constexpr int MAXV = G == 1 ? 4 : 1;     // d <= 1024 (G = 1) or <= 128 (G = 2)
+  constexpr int STRIDE = 4 * LG;           // columns between a lane's chunks
   __shared__ float red[4][1024];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int grp = lane / LG, gl = lane % LG;
   f32x4 acc[MAXV], gv[MAXV];
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
     acc[j] = f32x4{};
-    const int idx = j * 256 + lane * 4;
+    const int idx = j * STRIDE + gl * 4;
     gv[j] = idx < d ? *(const f32x4*)(g + idx) : f32x4{};
   }
   const int r0 = blockIdx.x * kNormRows + wave * (kNormRows / 4);
-  for (int i = 0; i < kNormRows / 4; ++i) {
-    const int row = r0 + i;
-    if (row >= M) break;
-    const float s = 1.f / sqrtf(ss[row] / (float)d + eps);
-    const int qi = qmap ? qmap[row] : -1;
-    f32x4 xh[MAXV], dxh[MAXV], hv[MAXV];
-    float dot = 0.f;
+  for (int i = 0; i < kNormRows / 4 / (2 * G); ++i) {
+    int row[2], qi[2];
+    float sc[2];
+    f32x4 xh[2][MAXV], hv[2][MAXV], rs[2][MAXV];
 #pragma unroll
-    for (int j = 0; j < MAXV; ++j) {
-      const int idx = j * 256 + lane * 4;
-      xh[j] = dxh[j] = hv[j] = f32x4{};
-      if (idx < d) {
-        xh[j] = *(const f32x4*)(x + (size_t)row * d + idx) * s;
-        hv[j] = *(const f32x4*)(dh + (size_t)row * d + idx);
-        if (qi >= 0) hv[j] += *(const f32x4*)(dh_q + (size_t)qi * d + idx);
-        dxh[j] = hv[j] * gv[j];
+    for (int u = 0; u < 2; ++u) {
+      row[u] = r0 + (2 * i + u) * G + grp;
+      const bool ok = row[u] < M;
+      sc[u] = ok ? 1.f / sqrtf(ss[row[u]] / (float)d + eps) : 0.f;
+      qi[u] = ok && qmap ? qmap[row[u]] : -1;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) dot = fmaf(dxh[j][k], xh[j][k], dot);
+      for (int j = 0; j < MAXV; ++j) {
+        const int idx = j * STRIDE + gl * 4;
+        xh[u][j] = hv[u][j] = rs[u][j] = f32x4{};
+        if (ok && idx < d) {
+          const size_t o = (size_t)row[u] * d + idx;
+          xh[u][j] = *(const f32x4*)(x + o) * sc[u];
+          hv[u][j] = *(const f32x4*)(dh + o);
+          if (dres) rs[u][j] = *(const f32x4*)(dres + o);
+          if (qi[u] >= 0) {
+            const size_t oq = (size_t)qi[u] * d + idx;
+            hv[u][j] += *(const f32x4*)(dh_q + oq);
+            rs[u][j] += *(const f32x4*)(dres_q + oq);
+          }
+        }
       }
     }
-    const float mean = wave_sum(dot) / (float)d;
 #pragma unroll
-    for (int j = 0; j < MAXV; ++j) {
-      const int idx = j * 256 + lane * 4;
-      if (idx >= d) continue;
-      f32x4 r = dres ? *(const f32x4*)(dres + (size_t)row * d + idx) : f32x4{};
-      if (qi >= 0) r += *(const f32x4*)(dres_q + (size_t)qi * d + idx);
-      *(f32x4*)(dx + (size_t)row * d + idx) = r + (dxh[j] - xh[j] * mean) * s;
-      acc[j] += hv[j] * xh[j];
+    for (int u = 0; u < 2; ++u) {
+      float dot = 0.f;
+#pragma unroll
+      for (int j = 0; j < MAXV; ++j) {
+        const f32x4 dxh = hv[u][j] * gv[j];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dot = fmaf(dxh[k], xh[u][j][k], dot);
+      }
+#pragma unroll
+      for (int o = 1; o < LG; o <<= 1) dot += __shfl_xor(dot, o, 64);
+      const float mean = dot / (float)d;
+      if (row[u] >= M) continue;
+#pragma unroll
+      for (int j = 0; j < MAXV; ++j) {
+        const int idx = j * STRIDE + gl * 4;
+        if (idx >= d) continue;
+        *(f32x4*)(dx + (size_t)row[u] * d + idx) = rs[u][j] + (hv[u][j] * gv[j] - xh[u][j] * mean) * sc[u];
+        acc[j] += hv[u][j] * xh[u][j];
+      }
     }
   }
+  if constexpr (G == 2) {
 #pragma unroll
-  for (int j = 0; j < MAXV; ++j) {
-    const int idx = j * 256 + lane * 4;
-    if (idx < d) *(f32x4*)&red[wave][idx] = acc[j];
+    for (int j = 0; j < MAXV; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[j][k] += __shfl_xor(acc[j][k], 32, 64);
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) {
+      const int idx = j * STRIDE + gl * 4;
+      if (idx < d) *(f32x4*)&red[wave][idx] = acc[j];
+    }
   }
   __syncthreads();
   for (int c = threadIdx.x; c < d; c += 256)
@@ -174,8 +207,12 @@ hipError_t rmsnorm_backward(const float* x, const float* ss, const float* dh, co
                             const float* dres_q) {
   if (M <= 0) return hipSuccess;
   timing_begin("rmsnorm_bwd", s);
-  hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3(rmsnorm_backward_parts(M)), dim3(256), 0, s, x, ss, dh,
-                     g, dres, eps, (int)M, d, dx, dg_part, qmap, dh_q, dres_q);
+  if (d <= 128)
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<2>, dim3(rmsnorm_backward_parts(M)), dim3(256), 0, s, x, ss,
+                       dh, g, dres, eps, (int)M, d, dx, dg_part, qmap, dh_q, dres_q);
+  else
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<1>, dim3(rmsnorm_backward_parts(M)), dim3(256), 0, s, x, ss,
+                       dh, g, dres, eps, (int)M, d, dx, dg_part, qmap, dh_q, dres_q);
   timing_end(s);
   return hipGetLastError();
 }
@@ -254,9 +291,14 @@ hipError_t ffn_backward(const FfnBwdParams& p, void* ws, hipStream_t s) {
     return e;
   const int nb = (int)((M + kNormRows - 1) / kNormRows);
   timing_begin("rmsnorm_bwd", s);
-  hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3(nb), dim3(256), 0, s, p.r1, w.ss, w.dH2, p.g2, p.dout,
-                     p.eps, (int)M, d, p.dr1, w.dg_part, (const int*)nullptr, (const float*)nullptr,
-                     (const float*)nullptr);
+  if (d <= 128)
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<2>, dim3(nb), dim3(256), 0, s, p.r1, w.ss, w.dH2, p.g2,
+                       p.dout, p.eps, (int)M, d, p.dr1, w.dg_part, (const int*)nullptr,
+                       (const float*)nullptr, (const float*)nullptr);
+  else
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<1>, dim3(nb), dim3(256), 0, s, p.r1, w.ss, w.dH2, p.g2,
+                       p.dout, p.eps, (int)M, d, p.dr1, w.dg_part, (const int*)nullptr,
+                       (const float*)nullptr, (const float*)nullptr);
   hipLaunchKernelGGL(colsum_kernel, dim3((d + 63) / 64), dim3(1024), 0, s, w.dg_part, nb, d, p.dg2);
   timing_end(s);
   return hipGetLastError();

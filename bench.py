@@ -6,6 +6,8 @@
     python bench.py --workload backward    (the attention-core backward)
     python bench.py --workload ffn_backward (the FFN-sublayer backward)
     python bench.py --workload sublayer_backward (the attention-sublayer backward)
+    python bench.py --workload compact     (the pyramid compaction, HBM-bound)
+    python bench.py --config c5            (the 12-layer stack with the token build)
 
 One step is one llatte_mla_forward over one batch of the workload (all
 layers, the pyramid, the readout), inputs and weights already resident in
@@ -42,6 +44,9 @@ WORKLOAD_TEXT = {
           "heads, r=128, pyramid 1600-800-400-200-100-50, 4-seed readout to 2048",
     "c4": "c4: jagged batch, 4 layers bf16, 128 users L~U[200,1600], d=256, "
           "4x64, r=64, 8 candidates, halving pyramid floor 64",
+    "c5": "c5: 12 layers bf16, B=32, L=1600, d=1024, 16x64 heads, r=256, 16 candidates, "
+          "geometric pyramid 1600->50, tokens built from a 1M x 1024 hashed-ID table + "
+          "384-d semantic vectors (in the step)",
 }
 
 
@@ -90,6 +95,8 @@ def kernel_flops(cfg, lengths):
         add("gemm_fusion", 2 * cfg.B * cfg.n_q * (d + cfg.d_c) * d)
     if cfg.n_seeds:
         add("gemm_readout", 2 * cfg.B * cfg.n_seeds * d * cfg.d_out)
+    if cfg.semantic is not None:  # token build: semantic vector times W_s
+        add("gemm_token_embed", 2 * (int(np.sum(lengths)) + cfg.B * cfg.n_q) * cfg.semantic.d_sem * d)
     return f
 
 
@@ -108,6 +115,8 @@ def non_absorbed_flops(cfg, lengths):
         t += 2 * cfg.B * cfg.n_q * (d + cfg.d_c) * d
     if cfg.n_seeds:
         t += 2 * cfg.B * cfg.n_seeds * d * cfg.d_out
+    if cfg.semantic is not None:
+        t += 2 * (int(np.sum(lengths)) + cfg.B * cfg.n_q) * cfg.semantic.d_sem * d
     return t
 
 
@@ -157,6 +166,36 @@ def cpu_baseline(prob, budget_s=12.0):
             "cores": threads or len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"{users} of {cfg.B} users of the same workload, fp32 "
                       f"oracle (non-absorbed definition), {dt:.1f} s"}
+
+
+def cpu_baseline_tokens(prob, host_table, budget_s=12.0):
+    """The same for a token-built workload: a user's table rows are gathered
+    from the host copy of the table outside the timed region; the oracle's
+    token build and forward of that user are timed."""
+    from oracle import llatte_oracle as O
+    import synth
+    cfg, I, W = prob["cfg"], prob["inputs"], prob["weights"]
+    off, nq = I["offsets"], cfg.n_q
+    hist = np.zeros((int(off[-1]), cfg.d), np.float32)
+    cand = np.zeros((cfg.B * nq, cfg.d), np.float32)
+    Ws = W["W_s"].astype(np.float32)
+    users, dt = 0, 0.0
+    while users < cfg.B and dt < budget_s:
+        u = users
+        # the rows as the device holds them (bf16-rounded)
+        hr = synth.round_bf16(host_table[I["hist_ids"][off[u]:off[u + 1]]])
+        cr = synth.round_bf16(host_table[I["cand_ids"][u * nq:(u + 1) * nq]])
+        t0 = time.perf_counter()
+        hist[off[u]:off[u + 1]] = O.token_embed(hr, I["hist_sem"][off[u]:off[u + 1]].astype(np.float32), Ws)
+        cand[u * nq:(u + 1) * nq] = O.token_embed(cr, I["cand_sem"][u * nq:(u + 1) * nq].astype(np.float32), Ws)
+        O.forward(cfg, W, hist, off, cand, I.get("ctx"), users=[u], dtype=np.float32)
+        dt += time.perf_counter() - t0
+        users += 1
+        print(f"  oracle user {users}: {dt:.1f} s", file=sys.stderr, flush=True)
+    return {"value": users / dt, "unit": "user-seq/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"{users} of {cfg.B} users of the same workload, fp32 oracle (token build "
+                      f"and non-absorbed forward; table-row gathering not timed), {dt:.1f} s"}
 
 
 ACTIONS_METRIC = "actions/sec + TFLOP/s (% MFMA bf16 peak), action tokenization, 1 GPU"
@@ -709,6 +748,80 @@ def bench_sublayer_backward(args):
     print(json.dumps(rec))
 
 
+COMPACT_METRIC = "GB/s (algorithmic), pyramid compaction, 1 GPU"
+COMPACT_TEXT = ("c3 layer-2 compaction: 64 users x 1600 fp32 rows of 512, the last 800 of each "
+                "kept (values, offsets and source indices out)")
+
+
+def bench_compact(args):
+    import torch
+    from oracle import llatte_oracle as O
+    from target_aware_latent_amd import llatte as C
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    B, Lu, d, keep_n = 64, 1600, 512, 800
+    rng = np.random.default_rng(0)
+    vals = rng.standard_normal((B * Lu, d)).astype(np.float32)
+    off_h = (np.arange(B + 1) * Lu).astype(np.int32)
+    v = torch.from_numpy(vals).cuda()
+    off = torch.from_numpy(off_h).cuda()
+    keep = torch.full((B,), keep_n, dtype=torch.int32, device="cuda")
+    out = torch.empty((B * keep_n, d), device="cuda")
+    noff = torch.empty(B + 1, dtype=torch.int32, device="cuda")
+    src = torch.empty(B * keep_n, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    step = lambda: C.llatte_pyramid_compact(v, d, C.LLATTE_F32, off, B, B * Lu, keep, out, noff,
+                                            src, stream=stream)
+    for _ in range(args.warmup):
+        step()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    # each kept row read once and written once, its source index written, the
+    # offsets and keep counts read and the new offsets written
+    nbytes = B * keep_n * (2 * 4 * d + 4) + (B + 1) * 4 * 2 + B * 4
+    gbs = nbytes / (ms_step / 1e3) / 1e9
+    C.llatte_kernel_timing_reset()
+    C.llatte_kernel_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = C.llatte_kernel_timing_read()
+    C.llatte_kernel_timing_enable(False)
+    kernels = {n: {"launches_per_step": c / args.steps, "ms_per_step": t / args.steps}
+               for n, (c, t) in kt.items()}
+    dom = max(kt, key=lambda n: kt[n][1])
+    cnt, tot = kt[dom]
+    roofline = {"bound": "hbm", "kernel": dom,
+                "achieved": round(nbytes / (tot / cnt / 1e3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(nbytes / (tot / cnt / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                "traffic": None, "bytes_per_launch": nbytes, "avg_launch_ms": round(tot / cnt, 4)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 5.0:
+            O.compact(vals, off_h, np.full(B, keep_n))
+            reps += 1
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(reps * nbytes / dt / 1e9, 2), "unit": "GB/s",
+               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"{reps} full compactions, numpy oracle, {dt:.1f} s"}
+    rec = {"metric": COMPACT_METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic (N(0,1) rows)",
+           "config": {"workload": COMPACT_TEXT, "global_batch": B, "seq_len": Lu,
+                      "parallelism": "single GPU"},
+           "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels}
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -726,13 +839,14 @@ def main():
                          "HBM bytes per launch of the dominant kernel (written "
                          "by target_aware_latent_amd.profsum traffic)")
     ap.add_argument("--workload", default="stack", choices=["stack", "actions", "summaries", "backward", "ffn_backward",
-                             "sublayer_backward"],
+                             "sublayer_backward", "compact"],
                     help="stack: the MLA forward (default); actions: the action "
                          "tokenization that builds the history tokens; summaries: the "
                          "LoRAMLP sequence summaries of the readout; backward: the attention-core "
                          "backward of every layer of the stack; ffn_backward: the FFN-sublayer "
                          "backward (GEMM gradients) of every layer; sublayer_backward: the "
-                         "attention-sublayer backward of every layer")
+                         "attention-sublayer backward of every layer; compact: the pyramid "
+                         "compaction (HBM-bound)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
@@ -754,6 +868,9 @@ def main():
     if args.workload == "sublayer_backward":
         bench_sublayer_backward(args)
         return
+    if args.workload == "compact":
+        bench_compact(args)
+        return
 
     import torch
     import synth
@@ -762,20 +879,47 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     cfg = synth.get_config(args.config)
-    if cfg.semantic is not None:
-        raise SystemExit("the token-build workload is benchmarked separately")
     prob = synth.generate(cfg, seed=0)
     I = prob["inputs"]
     lengths = [int(x) for x in I["lengths"]]
     model = DeviceModel(cfg, prob["weights"])
     model.pack()
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    hist = dev(I["hist"])
     offs = dev(I["offsets"].astype(np.int32))
-    cand = dev(I["cand"]) if cfg.n_q else None
     ctx = dev(I["ctx"]) if (cfg.n_q and cfg.d_c) else None
     out = model.alloc_outputs(lengths)
     stream = torch.cuda.current_stream()
+    build_tokens = None
+    if cfg.semantic is not None:
+        # token build (hashed-ID table row + semantic vector W_s) inside the
+        # step: the 1M-row table and the ids / semantic vectors are resident
+        sp = cfg.semantic
+        table = torch.empty(sp.vocab, cfg.d, dtype=torch.bfloat16, device="cuda")
+        host_table = None if args.no_cpu_baseline else np.empty((sp.vocab, cfg.d), np.float32)
+        print(f"building the {sp.vocab} x {cfg.d} table", file=sys.stderr, flush=True)
+        for nb, (row0, blk) in enumerate(synth.full_table(cfg, 0)):
+            table[row0:row0 + blk.shape[0]] = torch.from_numpy(blk).to("cuda").to(torch.bfloat16)
+            if host_table is not None:
+                host_table[row0:row0 + blk.shape[0]] = blk
+            if nb % 16 == 15:
+                print(f"  table rows {row0 + blk.shape[0]}", file=sys.stderr, flush=True)
+        print("table built", file=sys.stderr, flush=True)
+        Ws = dev(prob["weights"]["W_s"].astype(np.float32)).to(torch.bfloat16)
+        tws = torch.empty(C.llatte_token_embed_workspace_size(cfg.d, sp.d_sem, C.LLATTE_BF16),
+                          dtype=torch.uint8, device="cuda")
+        tok_in = [(dev(I[k + "_ids"].astype(np.int32)),
+                   dev(I[k + "_sem"].astype(np.float32)).to(torch.bfloat16), I[k + "_ids"].size)
+                  for k in ("hist", "cand")]
+        hist = torch.empty((tok_in[0][2], cfg.d), device="cuda")
+        cand = torch.empty((tok_in[1][2], cfg.d), device="cuda")
+
+        def build_tokens():
+            for (ids, sem, n), o in zip(tok_in, (hist, cand)):
+                C.llatte_token_embed(table, sp.vocab, ids, sem, Ws, n, cfg.d, sp.d_sem,
+                                     C.LLATTE_BF16, o, tws, stream=stream)
+    else:
+        hist = dev(I["hist"])
+        cand = dev(I["cand"]) if cfg.n_q else None
     if args.calibrate_copy:
         src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
@@ -783,11 +927,16 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    step = lambda: model.forward(hist, offs, lengths, cand, ctx, out=out, stream=stream)
+    def step():
+        if build_tokens is not None:
+            build_tokens()
+        model.forward(hist, offs, lengths, cand, ctx, out=out, stream=stream)
 
+    print("warm-up", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    print("timed steps", file=sys.stderr, flush=True)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -826,16 +975,33 @@ def main():
         per_launch_flops = kf[dom] * args.steps / cnt
         avg_s = tot / cnt / 1e3
         achieved = per_launch_flops / avg_s / 1e12
-        traffic = read_traffic(args.traffic, dom)
+        # the committed traffic record was measured on the c3 workload
+        default_traffic = os.path.join(ROOT, "profiles", "c3_attention_hbm_traffic.txt")
+        traffic = read_traffic(args.traffic, dom) \
+            if (args.traffic != default_traffic or cfg.name == "c3") else None
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                     "peak": peak, "unit": "TFLOP/s",
                     "frac": round(achieved / peak, 4), "traffic": traffic,
                     "flops_per_launch": per_launch_flops,
                     "avg_launch_ms": round(tot / cnt, 4)}
 
+    token_build = None
+    if build_tokens is not None and "gemm_token_embed" in kernels:
+        # HBM-bound gather-add: per token the table row (2 d bytes), the
+        # semantic vector (2 d_sem), the id (4) in, the fp32 token (4 d) out
+        e = kernels["gemm_token_embed"]
+        ntok = sum(t[2] for t in tok_in)
+        nbytes = ntok * (2 * cfg.d + 2 * cfg.semantic.d_sem + 4 + 4 * cfg.d)
+        token_build = {"ms_per_step": round(e["ms_per_step"], 4),
+                       "algorithmic_bytes_per_step": nbytes,
+                       "GB/s": round(nbytes / (e["ms_per_step"] / 1e3) / 1e9, 1),
+                       "frac_of_hbm_peak": round(nbytes / (e["ms_per_step"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                       "tflops": round(e.get("tflops", 0.0), 2)}
+
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(prob)
+        print("timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_tokens(prob, host_table) if cfg.semantic is not None else cpu_baseline(prob)
 
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "user-seq/s",
@@ -852,6 +1018,8 @@ def main():
         "wall_s_timed": round(wall, 3),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
     }
+    if token_build is not None:
+        rec["token_build"] = token_build
     print(json.dumps(rec))
 
 

@@ -122,7 +122,8 @@ def non_absorbed_flops(cfg, lengths):
 
 def kernel_source(label):
     """Source file of the kernel behind a timing label."""
-    name = "attention.hip" if label.startswith("attention") else "gemm.hip"
+    name = ("attention.hip" if label.startswith("attention") else
+            "plan.hip" if label == "pyramid_compact" else "gemm.hip")
     return os.path.join(ROOT, "target_aware_latent_amd", "csrc", name)
 
 
@@ -770,6 +771,13 @@ def bench_compact(args):
     noff = torch.empty(B + 1, dtype=torch.int32, device="cuda")
     src = torch.empty(B * keep_n, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
+    if args.calibrate_copy:
+        cs = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+        cd = torch.empty_like(cs)
+        torch.cuda.synchronize()
+        cd.copy_(cs)
+        torch.cuda.synchronize()
+        del cs, cd
     step = lambda: C.llatte_pyramid_compact(v, d, C.LLATTE_F32, off, B, B * Lu, keep, out, noff,
                                             src, stream=stream)
     for _ in range(args.warmup):
@@ -797,10 +805,14 @@ def bench_compact(args):
                for n, (c, t) in kt.items()}
     dom = max(kt, key=lambda n: kt[n][1])
     cnt, tot = kt[dom]
+    # measured HBM bytes of the row-copy kernel (the scan moves a few KB)
+    cp_traffic = os.path.join(ROOT, "profiles", "compaction_hbm_traffic.txt")
+    traffic = read_traffic(args.traffic if args.traffic.endswith("compaction_hbm_traffic.txt")
+                           else cp_traffic, dom)
     roofline = {"bound": "hbm", "kernel": dom,
                 "achieved": round(nbytes / (tot / cnt / 1e3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(nbytes / (tot / cnt / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
-                "traffic": None, "bytes_per_launch": nbytes, "avg_launch_ms": round(tot / cnt, 4)}
+                "traffic": traffic, "bytes_per_launch": nbytes, "avg_launch_ms": round(tot / cnt, 4)}
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()

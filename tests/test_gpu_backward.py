@@ -110,3 +110,42 @@ def test_no_query_rows_zero_the_latent_gradient():
                                     d_c, None)
     torch.cuda.synchronize()
     assert torch.count_nonzero(d_c).item() == 0
+
+
+def test_full_upstream_layer_one_sampled_users():
+    # the bench's launch configuration: 64 users x 1600 keys and causal query
+    # rows, 8 heads, r = 128; users are independent, so the oracle checks the
+    # d_q rows and d_C rows of sampled users one by one
+    import torch
+    from target_aware_latent_amd import llatte as C
+    B, L, h, r = 64, 1600, 8, 128
+    print("attention backward 64 x 1600 (sampled users)", flush=True)
+    rng = np.random.default_rng(21)
+    kv = (np.arange(B + 1) * L).astype(np.int32)
+    q = synth.round_bf16(rng.standard_normal((B * L, h, r)) * 0.5)
+    Cl = synth.round_bf16(rng.standard_normal((B * L, r)))
+    g = rng.standard_normal((B * L, h, r)).astype(np.float32)
+    dev = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(dt)
+    ad = C.llatte_attn_desc(h, r, 0, C.LLATTE_BF16, 0.125)
+    kvd = torch.from_numpy(kv).cuda()
+    qd, cd = dev(q, torch.bfloat16), dev(Cl, torch.bfloat16)
+    out = torch.empty((B * L, h, r), device="cuda")
+    lse = torch.empty((B * L, h), device="cuda")
+    ws = torch.empty(C.llatte_mla_attention_workspace_size(ad, B, B * L, B * L), dtype=torch.uint8,
+                     device="cuda")
+    C.llatte_mla_attention(ad, qd, cd, kvd, kvd, B, B * L, B * L, out, lse, ws)
+    d_q = torch.empty((B * L, h, r), device="cuda")
+    d_c = torch.empty((B * L, r), device="cuda")
+    bws = torch.empty(C.llatte_mla_attention_backward_workspace_size(ad, B * L), dtype=torch.uint8,
+                      device="cuda")
+    C.llatte_mla_attention_backward(ad, qd, cd, kvd, kvd, B, B * L, B * L, L, out, lse, dev(g), d_q,
+                                    d_c, bws)
+    torch.cuda.synchronize()
+    d_q, d_c = d_q.cpu().numpy(), d_c.cpu().numpy()
+    assert np.isfinite(d_q).all() and np.isfinite(d_c).all()
+    for u in (0, 29, 63):
+        s = slice(u * L, (u + 1) * L)
+        rq, rc = O.latent_attention_backward(q[s].astype(np.float64), Cl[s].astype(np.float64),
+                                             [0, L], [0, L], 0, 0.125, g[s].astype(np.float64))
+        assert _err(d_q[s], rq) <= 2e-2, f"user {u} d_q"
+        assert _err(d_c[s], rc) <= 2e-2, f"user {u} d_c"

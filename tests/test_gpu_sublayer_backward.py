@@ -151,3 +151,65 @@ def test_no_query_rows_zero_every_gradient():
     torch.cuda.synchronize()
     for t in [d_r_kv] + list(gd.values()):
         assert torch.count_nonzero(t).item() == 0
+
+
+def test_full_upstream_layer_one():
+    # the bench's launch configuration for layer 1 (64 users x 1600 rows,
+    # d = 512, 8 x 64 heads, r = 128): the input-row gradients of sampled
+    # users against the oracle one by one (users are independent), and the
+    # weight gradients, which sum over users, against the sum of the GPU's
+    # own single-user runs of every user (a property that holds at any size)
+    import torch
+    from target_aware_latent_amd import llatte as C
+    B, L, d, h, dk, r = 64, 1600, 512, 8, 64, 128
+    print("attention sublayer backward 64 x 1600", flush=True)
+    rng = np.random.default_rng(8)
+    cfg = SimpleNamespace(d=d, h=h, dk=dk, r=r, eps=1e-6, latent_norm=True, norm_mode="pre")
+    W = {"g1": (1 + 0.1 * rng.standard_normal(d)).astype(np.float32).astype(np.float64),
+         "g_c": (1 + 0.1 * rng.standard_normal(r)).astype(np.float32).astype(np.float64)}
+    for k, shp, fan in (("W_dkv", (d, r), d), ("W_uq", (d, h * dk), d), ("W_uk", (r, h * dk), r),
+                        ("W_uv", (r, h * dk), r), ("W_o", (h * dk, d), h * dk)):
+        W[k] = np.asarray(synth.round_bf16(rng.standard_normal(shp) / math.sqrt(fan)),
+                          np.float32).astype(np.float64)
+    R = rng.standard_normal((B * L, d)).astype(np.float32)
+    dout = rng.standard_normal((B * L, d)).astype(np.float32)
+    dev = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(dt)
+    desc = C.llatte_attn_sublayer_desc(d, h, dk, r, 0, C.LLATTE_BF16, 1, 1e-6)
+    wd = {"g1": dev(W["g1"]), "g_c": dev(W["g_c"])}
+    for k in ("w_dkv", "w_uq", "w_uk", "w_uv", "w_o"):
+        wd[k] = dev(W[ONAME[k]], torch.bfloat16)
+    shapes = {"g1": (d,), "w_dkv": (d, r), "g_c": (r,), "w_uq": (d, h * dk), "w_uk": (r, h * dk),
+              "w_uv": (r, h * dk), "w_o": (h * dk, d)}
+    Rd, dod = dev(R), dev(dout)
+
+    def run(b0, nb):
+        off = torch.from_numpy((np.arange(nb + 1) * L).astype(np.int32)).cuda()
+        gd = {k: torch.empty(s, device="cuda") for k, s in shapes.items()}
+        drkv = torch.empty((nb * L, d), device="cuda")
+        ws = torch.empty(C.llatte_attn_sublayer_backward_workspace_size(desc, nb, nb * L, nb * L),
+                         dtype=torch.uint8, device="cuda")
+        C.llatte_attn_sublayer_backward(desc, wd, Rd[b0 * L:(b0 + nb) * L], None, off, off, nb,
+                                        nb * L, nb * L, L, dod[b0 * L:(b0 + nb) * L], drkv, None, gd,
+                                        ws)
+        return drkv, gd
+
+    drkv, gd = run(0, B)
+    torch.cuda.synchronize()
+    drkv = drkv.cpu().numpy()
+    assert np.isfinite(drkv).all()
+    for u in (0, 41):
+        s = slice(u * L, (u + 1) * L)
+        ref, _, _ = O.attention_sublayer_backward(R[s].astype(np.float64), np.zeros((0, d)), L, W, cfg,
+                                                  dout[s].astype(np.float64))
+        e = _errs(drkv[s], ref)
+        assert e[0] <= 1.5e-2 and e[1] <= 1e-2, f"user {u} d_r_kv {e}"
+    total = {k: torch.zeros(s, device="cuda", dtype=torch.float64) for k, s in shapes.items()}
+    for u in range(B):
+        _, gu = run(u, 1)
+        for k in shapes:
+            total[k] += gu[k].double()
+    torch.cuda.synchronize()
+    for k in shapes:
+        a, b = gd[k].double().cpu().numpy(), total[k].cpu().numpy()
+        e = float(np.max(np.abs(a - b)) / np.max(np.abs(b)))
+        assert e <= 1e-5, f"{k}: batch vs sum of single-user runs {e:.2e}"

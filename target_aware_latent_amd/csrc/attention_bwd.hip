@@ -132,6 +132,30 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdParams p) {
   if (t0 >= ur.total) return;
   const int nc = p.B * p.n_cand, h = p.h;
 
+  // the last row of the block has the largest key position
+  const int last = min(ur.total, t0 + kQRows) - 1;
+  const int ntiles = ur.pos(last) / kKeys + 1;
+  const bf16* cg = (const bf16*)p.c + (size_t)ur.kv0 * R;
+  bf16x8 stage[NLD];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int e = tid + 256 * i, key = e / (R / 8), c = (e % (R / 8)) * 8;
+      const int k = kt * kKeys + key;
+      stage[i] = k < ur.K ? *(const bf16x8*)(cg + (size_t)k * R + c) : bf16x8{};
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int e = tid + 256 * i, key = e / (R / 8), c = (e % (R / 8)) * 8;
+      *(bf16x8*)&Cs[buf][key * LD + c] = stage[i];
+    }
+  };
+  // the first key tile's loads go out before the row prologue's, so the two
+  // latencies overlap
+  gload(0);
+
   const int t0w = t0 + wave * 16;  // the wave's first row
   const int t = t0w + lr;
   const bool valid = t < ur.total;
@@ -169,26 +193,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdParams p) {
   }
   const float sl2 = p.scale * kLog2e;
 
-  // the last row of the block has the largest key position
-  const int last = min(ur.total, t0 + kQRows) - 1;
-  const int ntiles = ur.pos(last) / kKeys + 1;
-  const bf16* cg = (const bf16*)p.c + (size_t)ur.kv0 * R;
-  bf16x8 stage[NLD];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int e = tid + 256 * i, key = e / (R / 8), c = (e % (R / 8)) * 8;
-      const int k = kt * kKeys + key;
-      stage[i] = k < ur.K ? *(const bf16x8*)(cg + (size_t)k * R + c) : bf16x8{};
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int e = tid + 256 * i, key = e / (R / 8), c = (e % (R / 8)) * 8;
-      *(bf16x8*)&Cs[buf][key * LD + c] = stage[i];
-    }
-  };
   // transpose-read offsets: rows 4 lg + (lr >> 2) (+16), column block rb
   const int trow = 4 * lg + (lr >> 2), tcol = (lr & 3) * 4;
 
@@ -196,7 +200,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdParams p) {
 #pragma unroll
   for (int b = 0; b < NRB; ++b) dq[b] = f32x4{};
 
-  gload(0);
   lstore(0);
   __syncthreads();
   for (int kt = 0; kt < ntiles; ++kt) {

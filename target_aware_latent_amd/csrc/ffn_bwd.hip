@@ -261,6 +261,7 @@ hipError_t ffn_backward(const FfnBwdParams& p, void* ws, hipStream_t s) {
   {
     GemmParams g = plain_gemm(w.dOb, d, p.w2, d, (int)M, F, d, w.dA, F, "gemm_bwd_dg", nullptr);
     g.epi = EPI_GELU_BWD;
+    g.nt = true;  // dA and GELU(A) stream to HBM (read by later kernels, not this one)
     g.table = w.A;
     g.ld_table = F;
     g.cast_out = w.G;

@@ -276,7 +276,7 @@ __device__ __forceinline__ void epilogue_rowmajor(const GemmParams p, const f32x
         f32x4 dg, g;
         gelu_bwd4<T>(v[ps][h], a[ps][h], dg, g);
         store4h<NTS, T>((T*)p.C + coff(m, n), dg[0], dg[1], dg[2], dg[3]);
-        store4<T>((T*)p.cast_out + (size_t)m * p.ld_cast + n, g[0], g[1], g[2], g[3]);
+        store4h<NTS, T>((T*)p.cast_out + (size_t)m * p.ld_cast + n, g[0], g[1], g[2], g[3]);
       });
     } break;
     case EPI_ROWNORM: {

@@ -142,6 +142,29 @@ def read_traffic(path, label):
     return None
 
 
+def host_desc():
+    """The host the CPU baseline ran on: CPU model and the BLAS numpy links."""
+    model = blas = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{b.get('name', '')} {b.get('version', '')}".strip() or None
+    except Exception:
+        pass
+    return {"cpu_model": model, "blas": blas}
+
+
+def emit(rec):
+    """Prints the one JSON line; a CPU baseline gets the host description."""
+    if isinstance(rec.get("cpu_baseline"), dict):
+        rec["cpu_baseline"].update(host_desc())
+    print(json.dumps(rec))
+
+
 def cpu_baseline(prob, budget_s=12.0):
     """The oracle as it stands, in fp32 on the host cores, on the first users
     of the batch until about budget_s seconds of work (at least one user)."""
@@ -292,7 +315,7 @@ def bench_actions(args):
         "tflops": round(tflops, 2), "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
     }
-    print(json.dumps(rec))
+    emit(rec)
 
 
 SUMMARIES_METRIC = "users/sec + TFLOP/s (% MFMA bf16 peak), sequence summaries, 1 GPU"
@@ -374,7 +397,7 @@ def bench_summaries(args):
         "pct_peak": round(100 * F / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
     }
-    print(json.dumps(rec))
+    emit(rec)
 
 
 BACKWARD_METRIC = ("user-sequences/sec + TFLOP/s (% MFMA bf16 peak), attention-core backward "
@@ -514,7 +537,7 @@ def bench_backward(args):
         "pct_peak": round(100 * F / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
     }
-    print(json.dumps(rec))
+    emit(rec)
 
 
 FFN_BWD_METRIC = ("user-sequences/sec + TFLOP/s (% MFMA bf16 peak), FFN-sublayer backward of "
@@ -619,7 +642,7 @@ def bench_ffn_backward(args):
         "pct_peak": round(100 * Fl / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
     }
-    print(json.dumps(rec))
+    emit(rec)
 
 
 SUB_BWD_METRIC = ("user-sequences/sec + TFLOP/s (% MFMA bf16 peak), attention-sublayer backward "
@@ -746,7 +769,7 @@ def bench_sublayer_backward(args):
         "pct_peak": round(100 * Fl / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
     }
-    print(json.dumps(rec))
+    emit(rec)
 
 
 COMPACT_METRIC = "GB/s (algorithmic), pyramid compaction, 1 GPU"
@@ -831,7 +854,7 @@ def bench_compact(args):
            "config": {"workload": COMPACT_TEXT, "global_batch": B, "seq_len": Lu,
                       "parallelism": "single GPU"},
            "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels}
-    print(json.dumps(rec))
+    emit(rec)
 
 
 def main():
@@ -1032,7 +1055,7 @@ def main():
     }
     if token_build is not None:
         rec["token_build"] = token_build
-    print(json.dumps(rec))
+    emit(rec)
 
 
 if __name__ == "__main__":

@@ -66,6 +66,18 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
+// IEEE-754 maximum (gfx950 v_maximum3_f32). Unlike fmaxf it needs no
+// quieting pass over operands the compiler cannot prove canonical (MFMA
+// results, permlane outputs), and three-way trees fuse into one instruction.
+// Scores here are finite or -inf, where both give the same value.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
+// Max of a lane's 16 scores of one accumulator column block (4 blocks of 4).
+__device__ __forceinline__ float max16(const f32x4& a, const f32x4& b, const f32x4& c, const f32x4& d) {
+  const float x = vmax3(a[0], a[1], a[2]), y = vmax3(a[3], b[0], b[1]), z = vmax3(b[2], b[3], c[0]);
+  const float u = vmax3(c[1], c[2], c[3]), w = vmax3(d[0], d[1], d[2]);
+  return vmax(vmax3(x, y, z), vmax3(u, w, d[3]));
+}
 // Max over the four lanes l, l^16, l^32, l^48 (a column of an MFMA
 // accumulator block spans the four 16-lane groups). Each permlane swap hands
 // a lane its own value and its partner's, in an order that differs between
@@ -74,10 +86,10 @@ __device__ __forceinline__ float fast_exp2(float x) {
 __device__ __forceinline__ float max_across_groups(float x) {
   const unsigned u = __float_as_uint(x);
   const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  x = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+  x = vmax(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
   const unsigned w = __float_as_uint(x);
   const auto p32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-  return fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+  return vmax(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
 }
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -389,16 +401,16 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
 #pragma unroll
     for (int eb = 0; eb < NEB; ++eb) {
       if (need_mask) {
+        // key t*BN + 16kb + 4g + v is masked past pos: compare the in-tile
+        // offset 16kb + v (an inline constant) with one per-lane limit
+        const int lim = pos[eb] - t * BN - g * 4;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            if (t * BN + kb * 16 + g * 4 + v > pos[eb]) sc[kb][eb][v] = -INFINITY;
+            if (kb * 16 + v > lim) sc[kb][eb][v] = -INFINITY;
       }
-      float mx = fmaxf(fmaxf(fmaxf(sc[0][eb][0], sc[0][eb][1]), fmaxf(sc[0][eb][2], sc[0][eb][3])),
-                       fmaxf(fmaxf(sc[1][eb][0], sc[1][eb][1]), fmaxf(sc[1][eb][2], sc[1][eb][3])));
-      mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sc[2][eb][0], sc[2][eb][1]), fmaxf(sc[2][eb][2], sc[2][eb][3])),
-                           fmaxf(fmaxf(sc[3][eb][0], sc[3][eb][1]), fmaxf(sc[3][eb][2], sc[3][eb][3]))));
+      float mx = max16(sc[0][eb], sc[1][eb], sc[2][eb], sc[3][eb]);
       mx = max_across_groups(mx);
       if (t == 0) {
         // first tile: m_run = its max (the first key is never masked)

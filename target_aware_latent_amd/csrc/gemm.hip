@@ -67,7 +67,7 @@ __device__ __forceinline__ float gelu_erf_bf16(float x) {
   const float t = __builtin_amdgcn_rcpf(fmaf(0.47047f * 0.70710678118654752f, ax, 1.f));
   const float q = t * fmaf(t, fmaf(t, 0.5f * 0.7478556f, 0.5f * -0.0958798f), 0.5f * 0.3480242f);
   const float e = __builtin_amdgcn_exp2f(x * x * (-0.5f * 1.4426950408889634f));
-  return fmaf(-(ax * q), e, fmaxf(x, 0.f));
+  return fmaf(-(ax * q), e, __builtin_elementwise_maximum(x, 0.f));  // no quieting pass
 }
 template <typename T> __device__ __forceinline__ float gelu_t(float x) {
   if constexpr (__is_same(T, bf16)) return gelu_erf_bf16(x);

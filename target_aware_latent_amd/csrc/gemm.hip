@@ -313,6 +313,10 @@ __device__ __forceinline__ void epilogue_rowmajor(const GemmParams p, const f32x
 // Eight-wave 128-wide tiles keep two workgroups per CU (LDS allows it): at
 // most 128 VGPRs, i.e. four waves per SIMD.
 template <int BN, int NW> constexpr int gemm_min_waves() { return NW == 8 && BN <= 128 ? 4 : 1; }
+// The 64x128 tile's four 32x64 waves fit the same 128 VGPRs.
+template <int BM, int BN, int NW> constexpr int gemm_min_waves3() {
+  return BM == 64 && BN == 128 && NW == 4 ? 4 : gemm_min_waves<BN, NW>();
+}
 
 // SK = 0: the whole product. Split K: SK = 1 computes the K steps of split
 // blockIdx.y (of gridDim.y) and stores its fp32 tile in p.sk_part; SK = 2,
@@ -320,7 +324,7 @@ template <int BN, int NW> constexpr int gemm_min_waves() { return NW == 8 && BN 
 // epilogue (the kernel boundary makes the tiles visible; no cross-workgroup
 // synchronisation).
 template <typename T, int BM, int BN, int WM, int WN, int NW, int PF, int SK>
-__global__ __launch_bounds__(64 * NW, (gemm_min_waves<BN, NW>())) void gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(64 * NW, (gemm_min_waves3<BM, BN, NW>())) void gemm_kernel(GemmParams p) {
   using MF = Mfma<T>;
   constexpr int NT = 64 * NW;              // threads
   constexpr int CE = 16 / sizeof(T);       // elements per 16-byte chunk
@@ -765,13 +769,15 @@ static long long ntiles(const GemmParams& p, int bm, int bn) {
 // GPU (256 CUs) enough workgroups; 64x64 tiles for the small products
 // (readout layer, last pyramid layers) that would otherwise occupy a few CUs.
 // A row-normalising epilogue needs one tile across all N columns.
-enum TileCfg { T64x64, T128x64, T128x128, T128x256, F128x64, F128x128, T_NONE };
+enum TileCfg { T64x64, T128x64, T64x128, T128x128, T128x256, F128x64, F128x128, T_NONE };
 
 static TileCfg select_tile(const GemmParams& p, bool is_bf16) {
   if (p.epi == EPI_ROWNORM && p.gain) {
     if (!is_bf16) return p.N <= 64 ? F128x64 : p.N <= 128 ? F128x128 : T_NONE;
     if (p.N <= 64) return ntiles(p, 128, 64) < 256 ? T64x64 : T128x64;
-    if (p.N <= 128) return T128x128;
+    // fewer 128-row tiles than one round of the GPU (two per CU): 64-row
+    // tiles spread the rows over more CUs
+    if (p.N <= 128) return ntiles(p, 128, 128) < 512 ? T64x128 : T128x128;
     if (p.N <= 256) return T128x256;
     return T_NONE;
   }
@@ -807,6 +813,7 @@ hipError_t gemm(const GemmParams& p, bool is_bf16, hipStream_t s) {
   switch (select_tile(p, is_bf16)) {
     case T64x64: return launch_gemm<bf16, 64, 64, 32, 32, 4, 2>(p, s);
     case T128x64: return launch_gemm<bf16, 128, 64, 64, 32, 4>(p, s);
+    case T64x128: return launch_gemm<bf16, 64, 128, 32, 64, 4>(p, s);
     case T128x128: return launch_gemm<bf16, 128, 128, 32, 64, 8>(p, s);
     case T128x256: return launch_gemm<bf16, 128, 256, 64, 64, 8>(p, s);
     case F128x64: return launch_gemm<float, 128, 64, 64, 32, 4>(p, s);

@@ -27,8 +27,10 @@ namespace llatte {
 constexpr int kNormRows = 64;
 // G row groups per wave (64 / G lanes per row; G = 2 for rows of at most
 // 128), two rows per group in flight at a time: a wave's 16 rows take 8 / G
-// iterations, each loading its rows before reducing them.
-template <int G>
+// iterations, each loading its rows before reducing them. A lane holds MAXV
+// chunks of four columns per row (rows of at most 4 MAXV 64 / G), so that
+// narrower rows keep fewer registers and more waves per SIMD.
+template <int G, int MAXV>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* x, const float* ss,
                                                          const float* dh, const float* g,
                                                          const float* dres, float eps, int M,
@@ -36,7 +38,6 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* x, const 
                                                          const int* qmap, const float* dh_q,
                                                          const float* dres_q) {
   constexpr int LG = 64 / G;               // lanes per row
-  constexpr int MAXV = G == 1 ? 4 : 1;     // d <= 1024 (G = 1) or <= 128 (G = 2)
   constexpr int STRIDE = 4 * LG;           // columns between a lane's chunks
   __shared__ float red[4][1024];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -201,18 +202,31 @@ size_t ffn_backward_workspace(long long M, int d, int F) { return ffn_ws(nullptr
 
 int rmsnorm_backward_parts(long long M) { return (int)((M + kNormRows - 1) / kNormRows); }
 
+// The instance for the row width: two row groups per wave for d <= 128,
+// else one, with the fewest column chunks per lane that cover d.
+static void launch_rmsnorm_bwd(const float* x, const float* ss, const float* dh, const float* g,
+                               const float* dres, float eps, long long M, int d, float* dx,
+                               float* dg_part, const int* qmap, const float* dh_q,
+                               const float* dres_q, hipStream_t s) {
+  const dim3 grid(rmsnorm_backward_parts(M));
+  if (d <= 128)
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<2, 1>), grid, dim3(256), 0, s, x, ss, dh, g, dres, eps,
+                       (int)M, d, dx, dg_part, qmap, dh_q, dres_q);
+  else if (d <= 512)
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<1, 2>), grid, dim3(256), 0, s, x, ss, dh, g, dres, eps,
+                       (int)M, d, dx, dg_part, qmap, dh_q, dres_q);
+  else
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<1, 4>), grid, dim3(256), 0, s, x, ss, dh, g, dres, eps,
+                       (int)M, d, dx, dg_part, qmap, dh_q, dres_q);
+}
+
 hipError_t rmsnorm_backward(const float* x, const float* ss, const float* dh, const float* g,
                             const float* dres, float eps, long long M, int d, float* dx,
                             float* dg_part, hipStream_t s, const int* qmap, const float* dh_q,
                             const float* dres_q) {
   if (M <= 0) return hipSuccess;
   timing_begin("rmsnorm_bwd", s);
-  if (d <= 128)
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<2>, dim3(rmsnorm_backward_parts(M)), dim3(256), 0, s, x, ss,
-                       dh, g, dres, eps, (int)M, d, dx, dg_part, qmap, dh_q, dres_q);
-  else
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<1>, dim3(rmsnorm_backward_parts(M)), dim3(256), 0, s, x, ss,
-                       dh, g, dres, eps, (int)M, d, dx, dg_part, qmap, dh_q, dres_q);
+  launch_rmsnorm_bwd(x, ss, dh, g, dres, eps, M, d, dx, dg_part, qmap, dh_q, dres_q, s);
   timing_end(s);
   return hipGetLastError();
 }
@@ -292,14 +306,8 @@ hipError_t ffn_backward(const FfnBwdParams& p, void* ws, hipStream_t s) {
     return e;
   const int nb = (int)((M + kNormRows - 1) / kNormRows);
   timing_begin("rmsnorm_bwd", s);
-  if (d <= 128)
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<2>, dim3(nb), dim3(256), 0, s, p.r1, w.ss, w.dH2, p.g2,
-                       p.dout, p.eps, (int)M, d, p.dr1, w.dg_part, (const int*)nullptr,
-                       (const float*)nullptr, (const float*)nullptr);
-  else
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<1>, dim3(nb), dim3(256), 0, s, p.r1, w.ss, w.dH2, p.g2,
-                       p.dout, p.eps, (int)M, d, p.dr1, w.dg_part, (const int*)nullptr,
-                       (const float*)nullptr, (const float*)nullptr);
+  launch_rmsnorm_bwd(p.r1, w.ss, w.dH2, p.g2, p.dout, p.eps, M, d, p.dr1, w.dg_part, nullptr, nullptr,
+                     nullptr, s);
   hipLaunchKernelGGL(colsum_kernel, dim3((d + 63) / 64), dim3(1024), 0, s, w.dg_part, nb, d, p.dg2);
   timing_end(s);
   return hipGetLastError();

@@ -27,6 +27,50 @@ __device__ __forceinline__ int rule_eval(const RuleDev& r, int l, int L,
   return min(k, prev);
 }
 
+// Exclusive scan of one pair of values per thread over a block of
+// kPlanThreads = 1024 threads (16 waves): inclusive scans inside each wave
+// by lane shifts, then the 16 wave totals scanned by the first wave through
+// LDS; two barriers, plus one at the end so that sh (64 ints) may be reused.
+// Returns the thread's exclusive prefixes; tot receives the block totals.
+static_assert(kPlanThreads == 1024, "the scan assumes 16 waves");
+__device__ __forceinline__ int2 block_exclusive_scan2(int2 v, int* sh, int2& tot) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int a = v.x, b = v.y;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int ya = __shfl_up(a, o, 64), yb = __shfl_up(b, o, 64);
+    if (lane >= o) {
+      a += ya;
+      b += yb;
+    }
+  }
+  if (lane == 63) {
+    sh[w] = a;
+    sh[16 + w] = b;
+  }
+  __syncthreads();
+  if (w == 0) {
+    int ta = lane < 16 ? sh[lane] : 0, tb = lane < 16 ? sh[16 + lane] : 0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int ya = __shfl_up(ta, o, 64), yb = __shfl_up(tb, o, 64);
+      if (lane >= o) {
+        ta += ya;
+        tb += yb;
+      }
+    }
+    if (lane < 16) {
+      sh[32 + lane] = ta;  // inclusive prefixes of the wave totals
+      sh[48 + lane] = tb;
+    }
+  }
+  __syncthreads();
+  const int pa = w > 0 ? sh[32 + w - 1] : 0, pb = w > 0 ? sh[48 + w - 1] : 0;
+  tot = int2{sh[47], sh[63]};
+  __syncthreads();
+  return int2{pa + a - v.x, pb + b - v.y};
+}
+
 // Exclusive scan of in[0..B) into out[0..B], out[B] = total, by one block of
 // kPlanThreads threads; each thread owns a contiguous chunk of users.
 __device__ void block_scan(const int* in, int* out, int B, int* sh) {
@@ -35,21 +79,26 @@ __device__ void block_scan(const int* in, int* out, int B, int* sh) {
   const int u0 = min(B, t * chunk), u1 = min(B, u0 + chunk);
   int s = 0;
   for (int u = u0; u < u1; ++u) s += in[u];
-  sh[t] = s;
-  __syncthreads();
-  for (int o = 1; o < kPlanThreads; o <<= 1) {
-    int v = t >= o ? sh[t - o] : 0;
-    __syncthreads();
-    sh[t] += v;
-    __syncthreads();
-  }
-  int run = sh[t] - s;  // exclusive prefix of this chunk
+  int2 tot;
+  int run = block_exclusive_scan2(int2{s, 0}, sh, tot).x;
   for (int u = u0; u < u1; ++u) {
     out[u] = run;
     run += in[u];
   }
-  if (t == kPlanThreads - 1) out[B] = sh[t];
+  if (t == kPlanThreads - 1) out[B] = tot.x;
   __syncthreads();
+}
+
+// Keys K and kept query rows n of a user with L history rows at layer l:
+// layer 0 sees all L rows, layer i + 1 the rows layer i kept; plans past the
+// stack (the readout) keep none.
+__device__ __forceinline__ int2 layer_counts(const RuleDev& rule, int n_layers, int l, int L) {
+  int K = L, n = 0;
+  for (int i = 0; i <= l; ++i) {
+    n = i < n_layers ? rule_eval(rule, i, L, K) : 0;
+    if (i < l) K = n;
+  }
+  return int2{K, n};
 }
 
 struct PlanArgs {
@@ -59,30 +108,40 @@ struct PlanArgs {
   int nq[65];        // query tokens per user, per plan
 };
 
-// Counts and offsets of every layer; one block.
+// Counts and offsets of layer blockIdx.x. A user's counts at a layer follow
+// from its history length alone, so every layer is a block of its own.
 __global__ __launch_bounds__(kPlanThreads) void plan_counts_kernel(
     const int* offsets, int B, RuleDev rule, PlanArgs a) {
-  __shared__ int sh[kPlanThreads];
-  for (int l = 0; l < a.n_plans; ++l) {
-    const LayerPlan P = a.base.layer(l);
-    for (int u = threadIdx.x; u < B; u += kPlanThreads) {
-      const int L = offsets[u + 1] - offsets[u];
-      const int K = l == 0 ? L : a.base.layer(l - 1).keep[u];
-      const int n = l < a.n_layers ? rule_eval(rule, l, L, K) : 0;
-      P.kv_len[u] = K;
-      P.keep[u] = n;
-    }
-    __syncthreads();
-    block_scan(P.kv_len, P.kv_off, B, sh);
-    block_scan(P.keep, P.hq_off, B, sh);
-    if (threadIdx.x == 0) {
-      const int nc = B * a.nq[l];
-      P.counts[0] = P.kv_off[B];
-      P.counts[1] = P.hq_off[B];
-      P.counts[2] = nc + P.kv_off[B];
-      P.counts[3] = nc + P.hq_off[B];
-    }
-    __syncthreads();
+  __shared__ int sh[64];
+  const int l = blockIdx.x, t = threadIdx.x;
+  const LayerPlan P = a.base.layer(l);
+  const int chunk = (B + kPlanThreads - 1) / kPlanThreads;
+  const int u0 = min(B, t * chunk), u1 = min(B, u0 + chunk);
+  int2 sum{0, 0};
+  for (int u = u0; u < u1; ++u) {
+    const int2 c = layer_counts(rule, a.n_layers, l, offsets[u + 1] - offsets[u]);
+    P.kv_len[u] = c.x;
+    P.keep[u] = c.y;
+    sum.x += c.x;
+    sum.y += c.y;
+  }
+  int2 tot;
+  int2 run = block_exclusive_scan2(sum, sh, tot);
+  for (int u = u0; u < u1; ++u) {
+    const int2 c = layer_counts(rule, a.n_layers, l, offsets[u + 1] - offsets[u]);
+    P.kv_off[u] = run.x;
+    P.hq_off[u] = run.y;
+    run.x += c.x;
+    run.y += c.y;
+  }
+  if (t == kPlanThreads - 1) {
+    const int nc = B * a.nq[l];
+    P.kv_off[B] = tot.x;
+    P.hq_off[B] = tot.y;
+    P.counts[0] = tot.x;
+    P.counts[1] = tot.y;
+    P.counts[2] = nc + tot.x;
+    P.counts[3] = nc + tot.y;
   }
 }
 
@@ -130,25 +189,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_items_kernel(
     __syncthreads();
     if (pass == 0) {
       // exclusive scan of the bucket counts (buckets ordered heaviest first)
-      __shared__ int part[kPlanThreads];
+      __shared__ int sh[64];
       const int per = kMaxBuckets / kPlanThreads;
       int s = 0;
       for (int i = 0; i < per; ++i) s += hist[threadIdx.x * per + i];
-      part[threadIdx.x] = s;
-      __syncthreads();
-      for (int o = 1; o < kPlanThreads; o <<= 1) {
-        int v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
-        __syncthreads();
-        part[threadIdx.x] += v;
-        __syncthreads();
-      }
-      int run = part[threadIdx.x] - s;
+      int2 tot;
+      int run = block_exclusive_scan2(int2{s, 0}, sh, tot).x;
       for (int i = 0; i < per; ++i) {
         const int c = hist[threadIdx.x * per + i];
         hist[threadIdx.x * per + i] = run;
         run += c;
       }
-      if (threadIdx.x == kPlanThreads - 1) *P.n_items = min(part[threadIdx.x], items_cap);
+      if (threadIdx.x == kPlanThreads - 1) *P.n_items = min(tot.x, items_cap);
       __syncthreads();
     }
   }
@@ -183,7 +235,7 @@ hipError_t build_plan(const int* offsets, int B, const RuleDev& rule, int n_q,
   a.n_layers = rule.n_layers;
   for (int l = 0; l < n_plans; ++l) a.nq[l] = l < rule.n_layers ? n_q : n_seeds;
   timing_begin("plan", s);
-  hipLaunchKernelGGL(plan_counts_kernel, dim3(1), dim3(kPlanThreads), 0, s,
+  hipLaunchKernelGGL(plan_counts_kernel, dim3(n_plans), dim3(kPlanThreads), 0, s,
                      offsets, B, rule, a);
   if (bq > 0)
     hipLaunchKernelGGL(plan_items_kernel, dim3(n_plans), dim3(kPlanThreads), 0,
@@ -216,7 +268,7 @@ hipError_t pyramid_counts_dev(const RuleDev& rule, const int* offsets, int B,
 // ------------------------------------------------------------------ compaction
 __global__ __launch_bounds__(kPlanThreads) void compact_scan_kernel(
     const int* keep, int B, int* offsets_out) {
-  __shared__ int sh[kPlanThreads];
+  __shared__ int sh[64];
   block_scan(keep, offsets_out, B, sh);
 }
 

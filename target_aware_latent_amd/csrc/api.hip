@@ -1361,11 +1361,12 @@ llatte_status llatte_summaries(const llatte_summary_desc* desc, const void* pack
 
 
 // ---------------------------------------------------------------- attention backward
-llatte_status llatte_mla_attention_backward(
+// d_q goes to d_q (fp32) or, when d_q_bf16 is given, there rounded to bf16.
+static llatte_status attention_backward_call(
     const llatte_attn_desc* a, const void* q_lat, const void* c_lat,
     const int32_t* kv_offsets, const int32_t* hq_offsets, int32_t B,
     int32_t Mtot, int32_t Ktot, int32_t max_len, const float* out,
-    const float* lse, const float* d_out, float* d_q, float* d_c, void* workspace,
+    const float* lse, const float* d_out, float* d_q, bf16* d_q_bf16, float* d_c, void* workspace,
     size_t workspace_bytes, void* stream) {
   if (!a) return fail(LLATTE_ERR_INVALID_ARG, "NULL descriptor");
   if (a->dtype != LLATTE_BF16) return fail(LLATTE_ERR_UNSUPPORTED, "the backward is BF16 only");
@@ -1374,7 +1375,8 @@ llatte_status llatte_mla_attention_backward(
   if (a->n_heads < 1 || a->n_cand < 0 || B < 1 || Ktot < B || max_len < 1 || Mtot < 0)
     return fail(LLATTE_ERR_INVALID_ARG, "bad sizes");
   // with no query rows only d_C is written (zeros): the row buffers may be NULL
-  const void* ptrs[] = {c_lat, kv_offsets, hq_offsets, d_c, q_lat, out, lse, d_out, d_q, workspace};
+  const void* dq_out = d_q_bf16 ? (const void*)d_q_bf16 : (const void*)d_q;
+  const void* ptrs[] = {c_lat, kv_offsets, hq_offsets, d_c, q_lat, out, lse, d_out, dq_out, workspace};
   const int nreq = Mtot == 0 ? 4 : 10;
   for (int i = 0; i < 10; ++i) {
     if (!ptrs[i]) {
@@ -1390,6 +1392,7 @@ llatte_status llatte_mla_attention_backward(
   p.lse = lse;
   p.dout = d_out;
   p.dq = d_q;
+  p.dq_bf16 = d_q_bf16;
   p.dc = d_c;
   p.kv_off = kv_offsets;
   p.hq_off = hq_offsets;
@@ -1403,6 +1406,16 @@ llatte_status llatte_mla_attention_backward(
     return fail(LLATTE_ERR_WORKSPACE, "backward workspace too small");
   HIP_TRY(attention_backward(p, max_len, workspace, (hipStream_t)stream));
   return LLATTE_OK;
+}
+
+llatte_status llatte_mla_attention_backward(
+    const llatte_attn_desc* a, const void* q_lat, const void* c_lat,
+    const int32_t* kv_offsets, const int32_t* hq_offsets, int32_t B,
+    int32_t Mtot, int32_t Ktot, int32_t max_len, const float* out,
+    const float* lse, const float* d_out, float* d_q, float* d_c, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  return attention_backward_call(a, q_lat, c_lat, kv_offsets, hq_offsets, B, Mtot, Ktot, max_len, out,
+                                 lse, d_out, d_q, nullptr, d_c, workspace, workspace_bytes, stream);
 }
 
 size_t llatte_mla_attention_backward_workspace_size(const llatte_attn_desc* a, int32_t Mtot) {
@@ -1469,7 +1482,6 @@ static llatte_status sublayer_backward_run(
   bf16* dob = ar.take<bf16>(M * hd);
   float* dot_ = ar.take<float>(M * hr);
   char* abw_ws = ar.take<char>(bws);
-  float* dqt = ar.take<float>(M * hr);
   bf16* dqtb = ar.take<bf16>(M * hr);
   bf16* dq = ar.take<bf16>(M * hd);
   float* dHq = ar.take<float>(M * d);
@@ -1573,12 +1585,12 @@ static llatte_status sublayer_backward_run(
   HIP_TRY(wg(otb, hr, r, r, dob, hd, dk, dk, M, G->w_uv, hd, dk, h, "gemm_sub_dwuv"));
   HIP_TRY(mm(dob, hd, dk, W->w_uv, hd, dk, M, r, dk, dot_, hr, r, h, true, false, "gemm_sub_dolat"));
   {
-    const llatte_status st = llatte_mla_attention_backward(&ad, qt, Cb, kv_off, hq_off, B, Mtot, Ktot,
-                                                           max_len, ot, lse, dot_, dqt, dC, abw_ws,
-                                                           bws, s);
+    // dq̃ leaves the attention core as bf16, the operand of its two products
+    const llatte_status st = attention_backward_call(&ad, qt, Cb, kv_off, hq_off, B, Mtot, Ktot,
+                                                     max_len, ot, lse, dot_, nullptr, dqtb, dC, abw_ws,
+                                                     bws, s);
     if (st != LLATTE_OK) return st;
   }
-  HIP_TRY(cast_f32(dqt, dqtb, M * hr, true, s));
   HIP_TRY(mm(dqtb, hr, r, WukT, r, (long long)dk * r, M, dk, r, dq, hd, dk, h, false, false, "gemm_sub_dq"));
   HIP_TRY(wg(dqtb, hr, r, r, q, hd, dk, dk, M, G->w_uk, hd, dk, h, "gemm_sub_dwuk"));
   HIP_TRY(wg(Hq, d, 0, d, dq, hd, 0, hd, M, G->w_uq, hd, 0, 1, "gemm_sub_dwuq"));

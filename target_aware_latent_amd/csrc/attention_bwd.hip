@@ -255,9 +255,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdParams p) {
     __syncthreads();
   }
   if (valid) {
-    float* dst = p.dq + rowoff;
+    if (p.dq_bf16) {
+      bf16* dst = p.dq_bf16 + rowoff;
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) *(f32x4*)(dst + rb * 16 + lg * 4) = dq[rb] * p.scale;
+      for (int rb = 0; rb < NRB; ++rb) {
+        const f32x4 v = dq[rb] * p.scale;
+        *(bf16x4*)(dst + rb * 16 + lg * 4) = bf16x4{to_bf16(v[0]), to_bf16(v[1]), to_bf16(v[2]), to_bf16(v[3])};
+      }
+    } else {
+      float* dst = p.dq + rowoff;
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) *(f32x4*)(dst + rb * 16 + lg * 4) = dq[rb] * p.scale;
+    }
   }
 }
 

@@ -15,6 +15,7 @@ struct AttnBwdParams {
   const float* lse = nullptr;  // [Mtot, h] natural log
   const float* dout = nullptr; // [Mtot, h, r]
   float* dq = nullptr;
+  bf16* dq_bf16 = nullptr;  // when set, d_q goes here rounded to bf16 instead of to dq
   float* dc = nullptr;
   const int* kv_off = nullptr;
   const int* hq_off = nullptr;

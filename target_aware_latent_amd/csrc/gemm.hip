@@ -130,6 +130,14 @@ template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
   bf16x4 v = *(const bf16x4*)p;
   return f32x4{from_bf16(v[0]), from_bf16(v[1]), from_bf16(v[2]), from_bf16(v[3])};
 }
+// Four elements as stored (converted only where used, so that a load can
+// stay in flight past a barrier).
+template <typename T> struct Raw4 { typedef f32x4 type; };
+template <> struct Raw4<bf16> { typedef bf16x4 type; };
+__device__ __forceinline__ f32x4 widen4(f32x4 v) { return v; }
+__device__ __forceinline__ f32x4 widen4(bf16x4 v) {
+  return f32x4{from_bf16(v[0]), from_bf16(v[1]), from_bf16(v[2]), from_bf16(v[3])};
+}
 
 // Timestamp encoding of the action tokens ([LLaTTE] Appendix A.2, additive
 // timestamp encodings on a subset of the hidden dimensions): columns
@@ -177,14 +185,46 @@ __device__ __forceinline__ void epilogue_rowmajor(const GemmParams p, const f32x
   static_assert(LPR <= 64 && (LPR & (LPR - 1)) == 0 && BM % RPP == 0, "row-major epilogue shape");
   auto cidx = [](int row, int chunk) { return row * BN + ((chunk ^ (row & 15)) << 2); };
   const int lr = lane & 15;
+  const int q = tid % LPR, rsub = tid / LPR;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
       *(f32x4*)&Cs[cidx(wm0 + i * 16 + lr, ((wn0 + j * 16) >> 2) + (lane >> 4))] = acc[i][j];
+  // Inputs the epilogue reads from memory (residual rows, gathered table
+  // rows, the stored pre-activation) are loaded once the accumulators are in
+  // LDS (their registers free) and before the barrier, so that their latency
+  // overlaps the wait for the other waves.
+  using R4 = typename Raw4<T>::type;
+  f32x4 in[NPASS][2];  // residual rows (fp32)
+  R4 tin[NPASS][2];    // table rows, as stored
+  if (p.epi == EPI_RESID_F32) {
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int m = m0 + ps * RPP + rsub;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int n = n0 + (q + h * LPR) * 4;
+        in[ps][h] = f32x4{};
+        if (m < M && n < p.N) in[ps][h] = *(const f32x4*)(p.res.row(rrow[ps]) + n);
+      }
+    }
+  } else if (p.epi == EPI_GATHER_ADD_F32 || p.epi == EPI_GELU_BWD) {
+    const bool gather = p.epi == EPI_GATHER_ADD_F32;
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int m = m0 + ps * RPP + rsub;
+      const size_t trow = (size_t)(gather ? rrow[ps] : m) * p.ld_table;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int n = n0 + (q + h * LPR) * 4;
+        tin[ps][h] = R4{};
+        if (m < M && n < p.N) tin[ps][h] = *(const R4*)((const T*)p.table + trow + n);
+      }
+    }
+  }
   __syncthreads();
 
-  const int q = tid % LPR, rsub = tid / LPR;
   const bool has_rs = p.rs.ss != nullptr;
   // values of this lane, scaled by the row scale
   f32x4 v[NPASS][2];
@@ -234,13 +274,11 @@ __device__ __forceinline__ void epilogue_rowmajor(const GemmParams p, const f32x
       });
       break;
     case EPI_RESID_F32: {
-      f32x4 r[NPASS][2];
-      each([&](int ps, int h, int m, int n) { r[ps][h] = *(const f32x4*)(p.res.row(rrow[ps]) + n); });
       float ssp[NPASS];
 #pragma unroll
       for (int ps = 0; ps < NPASS; ++ps) ssp[ps] = 0.f;
       each([&](int ps, int h, int m, int n) {
-        const f32x4 x = v[ps][h] + r[ps][h];
+        const f32x4 x = v[ps][h] + in[ps][h];
         store4h<NTS, float>((float*)p.C + coff(m, n), x[0], x[1], x[2], x[3]);
         if (p.cast_out)
           store4<T>((T*)p.cast_out + (size_t)m * p.ld_cast + n, x[0], x[1], x[2], x[3]);
@@ -258,23 +296,15 @@ __device__ __forceinline__ void epilogue_rowmajor(const GemmParams p, const f32x
       }
     } break;
     case EPI_GATHER_ADD_F32: {
-      f32x4 r[NPASS][2];
       each([&](int ps, int h, int m, int n) {
-        r[ps][h] = load4<T>((const T*)p.table + (size_t)rrow[ps] * p.ld_table + n);
-      });
-      each([&](int ps, int h, int m, int n) {
-        const f32x4 x = v[ps][h] + r[ps][h];
+        const f32x4 x = v[ps][h] + widen4(tin[ps][h]);
         store4<float>((float*)p.C + coff(m, n), x[0], x[1], x[2], x[3]);
       });
     } break;
     case EPI_GELU_BWD: {
-      f32x4 a[NPASS][2];
-      each([&](int ps, int h, int m, int n) {
-        a[ps][h] = load4<T>((const T*)p.table + (size_t)m * p.ld_table + n);
-      });
       each([&](int ps, int h, int m, int n) {
         f32x4 dg, g;
-        gelu_bwd4<T>(v[ps][h], a[ps][h], dg, g);
+        gelu_bwd4<T>(v[ps][h], widen4(tin[ps][h]), dg, g);
         store4h<NTS, T>((T*)p.C + coff(m, n), dg[0], dg[1], dg[2], dg[3]);
         store4h<NTS, T>((T*)p.cast_out + (size_t)m * p.ld_cast + n, g[0], g[1], g[2], g[3]);
       });

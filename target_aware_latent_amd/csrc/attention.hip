@@ -66,10 +66,11 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
-// IEEE-754 maximum (gfx950 v_maximum3_f32). Unlike fmaxf it needs no
-// quieting pass over operands the compiler cannot prove canonical (MFMA
-// results, permlane outputs), and three-way trees fuse into one instruction.
-// Scores here are finite or -inf, where both give the same value.
+// IEEE-754 maximum (gfx950 v_maximum3_f32): three-way trees fuse into one
+// instruction, and no quieting pass over operands the compiler cannot prove
+// canonical (MFMA results, permlane outputs) is needed whatever the NaN mode
+// the file is built with. Scores here are finite or -inf, where it equals
+// fmaxf.
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
 // Max of a lane's 16 scores of one accumulator column block (4 blocks of 4).

@@ -50,6 +50,10 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* x, const 
     gv[j] = idx < d ? *(const f32x4*)(g + idx) : f32x4{};
   }
   const int r0 = blockIdx.x * kNormRows + wave * (kNormRows / 4);
+  // the row map of the wave's 16 rows, loaded once (lane j holds row r0 + j),
+  // so that no iteration waits for it before loading the mapped rows
+  constexpr int WR = kNormRows / 4;
+  const int qm = qmap && lane < WR && r0 + lane < M ? qmap[r0 + lane] : -1;
   for (int i = 0; i < kNormRows / 4 / (2 * G); ++i) {
     int row[2], qi[2];
     float sc[2];
@@ -59,7 +63,8 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* x, const 
       row[u] = r0 + (2 * i + u) * G + grp;
       const bool ok = row[u] < M;
       sc[u] = ok ? 1.f / sqrtf(ss[row[u]] / (float)d + eps) : 0.f;
-      qi[u] = ok && qmap ? qmap[row[u]] : -1;
+      qi[u] = __shfl(qm, row[u] - r0, 64);
+      if (!ok) qi[u] = -1;
 #pragma unroll
       for (int j = 0; j < MAXV; ++j) {
         const int idx = j * STRIDE + gl * 4;

@@ -110,6 +110,27 @@ def test_pyramid_compact_bit_exact(dt, row_elems):
     assert torch.equal(out[:n].float().cpu(), torch.from_numpy(ref_vals))
 
 
+def test_pyramid_compact_many_users():
+    """3000 users: more than the offsets scan's 1024 threads, so each thread
+    scans a chunk of users; offsets, source rows and values bit-exact."""
+    rng = np.random.default_rng(7)
+    lengths = rng.integers(1, 20, 3000)
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    keep = np.array([rng.integers(0, l + 1) for l in lengths])
+    vals = rng.standard_normal((off[-1], 8)).astype(np.float32)
+    v = dev(vals, torch.float32)
+    n = int(keep.sum())
+    out = torch.zeros(n, 8, device="cuda")
+    noff = torch.empty(lengths.size + 1, dtype=torch.int32, device="cuda")
+    src = torch.empty(n, dtype=torch.int32, device="cuda")
+    L().llatte_pyramid_compact(v, 8, L().LLATTE_F32, idev(off), lengths.size, int(off[-1]),
+                               idev(keep), out, noff, src)
+    ref_vals, ref_off, ref_src = O.compact(vals, off, keep)
+    assert np.array_equal(noff.cpu().numpy(), ref_off)
+    assert np.array_equal(src.cpu().numpy(), ref_src)
+    assert torch.equal(out.cpu(), torch.from_numpy(ref_vals))
+
+
 def test_pyramid_compact_full_size_upstream():
     """Upstream shape: 64 users x 1600 rows of 512 floats, keep the last 800."""
     B, Lu, d = 64, 1600, 512
@@ -330,6 +351,11 @@ SMALL_CASES = {
     "c4_lowrank_wide": lambda: small("c4", [65, 300, 129], r_q=384, gain_jitter=0.1),
     "c2_post_lowrank": lambda: small("c2", [33, 257, 4], norm_mode="post", r_q=96,
                                      gain_jitter=0.1),
+    # more users than the planning scans' 1024 threads (several users per
+    # thread), on the fp32 and the bf16 path
+    "c1_many_users": lambda: small("c1", np.random.default_rng(5).integers(1, 13, 1100).tolist()),
+    "c2_many_users": lambda: small("c2", np.random.default_rng(6).integers(1, 17, 1100).tolist(),
+                                   pyramid=synth.PyramidRule("fixed", (12, 6, 3))),
 }
 
 

@@ -340,6 +340,22 @@ __device__ __forceinline__ void epilogue_rowmajor(const GemmParams p, const f32x
   }
 }
 
+// Operand staging without registers (bf16, PF = 0): each wave instruction
+// copies 64 x 16 bytes from global memory straight into LDS, lane i's bytes
+// landing at LDS byte address `lds` + 16 i (gfx950 LDS DMA,
+// global_load_lds_dwordx4; the LDS address travels in M0). Issued as inline
+// assembly: the compiler's own wait insertion would otherwise make every LDS
+// read wait for all outstanding copies, i.e. for the next tile's. The
+// kernel waits for its copies itself (dma_wait_all, then a barrier) before it
+// reads them. Nothing else in these kernels uses M0; the compiler's waits
+// for its own loads stay correct, since the counter retires operations in
+// issue order and extra copies only make those waits longer.
+__device__ __forceinline__ void lds_dma16(const void* g, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+               : "memory");
+}
+__device__ __forceinline__ void dma_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Eight-wave 128-wide tiles keep two workgroups per CU (LDS allows it): at
 // most 128 VGPRs, i.e. four waves per SIMD.
 template <int BN, int NW> constexpr int gemm_min_waves() { return NW == 8 && BN <= 128 ? 4 : 1; }
@@ -353,8 +369,9 @@ template <int BM, int BN, int NW> constexpr int gemm_min_waves3() {
 // launched after it, sums the splits' tiles in split order and runs the
 // epilogue (the kernel boundary makes the tiles visible; no cross-workgroup
 // synchronisation).
-template <typename T, int BM, int BN, int WM, int WN, int NW, int PF, int SK>
-__global__ __launch_bounds__(64 * NW, (gemm_min_waves3<BM, BN, NW>())) void gemm_kernel(GemmParams p) {
+template <typename T, int BM, int BN, int WM, int WN, int NW, int PF, int SK,
+          int MINW = gemm_min_waves3<BM, BN, NW>()>
+__global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
   using MF = Mfma<T>;
   constexpr int NT = 64 * NW;              // threads
   constexpr int CE = 16 / sizeof(T);       // elements per 16-byte chunk
@@ -400,6 +417,43 @@ __global__ __launch_bounds__(64 * NW, (gemm_min_waves3<BM, BN, NW>())) void gemm
   const T* A = (const T*)p.A + (size_t)blockIdx.z * p.sA;
   const T* Bm = (const T*)p.B + (size_t)blockIdx.z * p.sB;
 
+  // PF = 0: operands staged by LDS DMA (bf16, K a multiple of BK, rows of
+  // 16-byte multiples). Instruction i of a wave stages tile rows
+  // 8 (i NW + wave) .. + 7; lane l takes row + l / 8 and the global chunk that
+  // the swizzle places at physical chunk l % 8. Rows past M (N) read row
+  // M - 1 (N - 1): finite data whose results are never stored.
+  constexpr bool DMA = PF == 0;
+  static_assert(!DMA || sizeof(T) == 2, "LDS DMA staging is for 16-bit operands");
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const unsigned lds_base = (unsigned)(size_t)((__attribute__((address_space(3))) char*)smem);
+  const T* adma[DMA ? AI : 1];
+  const T* bdma[DMA ? BI : 1];
+  if constexpr (DMA) {
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+      const int row = (i * NW + wave_u) * 8 + lane / 8;
+      const int r = min(m0 + row, M - 1);
+      const int src = p.a_rows ? p.a_rows[r] : r;
+      adma[i] = A + (size_t)src * p.lda + (((lane & 7) ^ ((row >> 1) & 7)) * CE);
+    }
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const int row = (i * NW + wave_u) * 8 + lane / 8;
+      const int r = min(n0 + row, p.N - 1);
+      bdma[i] = Bm + (size_t)r * p.ldb + (((lane & 7) ^ ((row >> 1) & 7)) * CE);
+    }
+  }
+  auto dma_tile = [&](int kt, int buf) {
+    const int k0 = (kb0 + kt) * BK;
+#pragma unroll
+    for (int i = 0; i < AI; ++i)
+      lds_dma16(adma[i] + k0, lds_base + (unsigned)((buf * BM * LDK + (i * NW + wave_u) * 8 * LDK) * 2));
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
+      lds_dma16(bdma[i] + k0, lds_base + (unsigned)((2 * BM * LDK + buf * BN * LDK +
+                                                      (i * NW + wave_u) * 8 * LDK) * 2));
+  };
+
   // Per-thread global source rows (fixed across the K loop).
   const T* arow[AI];
   bool aok[AI];
@@ -424,7 +478,7 @@ __global__ __launch_bounds__(64 * NW, (gemm_min_waves3<BM, BN, NW>())) void gemm
   // Two register sets: the loads of K step k+2 are issued while step k is
   // computed from LDS and step k+1 waits in the other set, so each load has
   // two compute phases to arrive.
-  i32x4 ra[PF][AI], rb[PF][BI];
+  i32x4 ra[PF > 0 ? PF : 1][AI], rb[PF > 0 ? PF : 1][BI];
   auto load_tile = [&](int kt, auto set) {
     constexpr int S = decltype(set)::value;
     const int k0 = (kb0 + kt) * BK;
@@ -515,9 +569,13 @@ __global__ __launch_bounds__(64 * NW, (gemm_min_waves3<BM, BN, NW>())) void gemm
     __syncthreads();
   };
   if constexpr (SK != 2) {
-    load_tile(0, S0{});
-    if constexpr (PF == 2) {
-      if (nk > 1) load_tile(1, S1{});
+    if constexpr (DMA) {
+      if (nk > 0) dma_tile(0, 0);
+    } else {
+      load_tile(0, S0{});
+      if constexpr (PF == 2) {
+        if (nk > 1) load_tile(1, S1{});
+      }
     }
   }
   // Source rows of the residual / gathered table rows, resolved before the
@@ -557,14 +615,27 @@ __global__ __launch_bounds__(64 * NW, (gemm_min_waves3<BM, BN, NW>())) void gemm
     }
     rs_lds[tid] = sc;
   }
-  if constexpr (SK != 2) store_lds(0, S0{});
-  __syncthreads();
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    step(kt, S0{});
-    step(kt + 1, S1{});
+  if constexpr (DMA) {
+    // one barrier per K step: it publishes step kt's tile (every wave has
+    // waited for its own copies) and frees the other buffer, into which the
+    // copies of step kt + 1 go while step kt is computed
+    for (int kt = 0; kt < nk; ++kt) {
+      dma_wait_all();
+      __syncthreads();
+      if (kt + 1 < nk) dma_tile(kt + 1, (kt + 1) & 1);
+      compute(kt & 1);
+    }
+    __syncthreads();  // operand LDS (and rs_lds) before the epilogue reuses it
+  } else {
+    if constexpr (SK != 2) store_lds(0, S0{});
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, S0{});
+      step(kt + 1, S1{});
+    }
+    if (kt < nk) step(kt, S0{});
   }
-  if (kt < nk) step(kt, S0{});
 
   if constexpr (SK != 0) {
     // split tiles: [tile][split][thread][TM*TN f32x4], each thread's
@@ -838,14 +909,25 @@ int gemm_ss_slots(const GemmParams& p, bool is_bf16) {
   return (p.N + w - 1) / w;
 }
 
+// bf16 operands whose K is a whole number of 64-wide steps and whose rows
+// are 16-byte multiples are staged by LDS DMA (PF = 0); the others through
+// registers.
+static bool dma_ok(const GemmParams& p) { return p.K % 64 == 0 && p.lda % 8 == 0 && p.ldb % 8 == 0; }
+
 hipError_t gemm(const GemmParams& p, bool is_bf16, hipStream_t s) {
   if (p.M_cap <= 0 || p.N <= 0) return hipSuccess;
+  const bool dma = is_bf16 && dma_ok(p);
   switch (select_tile(p, is_bf16)) {
-    case T64x64: return launch_gemm<bf16, 64, 64, 32, 32, 4, 2>(p, s);
-    case T128x64: return launch_gemm<bf16, 128, 64, 64, 32, 4>(p, s);
-    case T64x128: return launch_gemm<bf16, 64, 128, 32, 64, 4>(p, s);
-    case T128x128: return launch_gemm<bf16, 128, 128, 32, 64, 8>(p, s);
-    case T128x256: return launch_gemm<bf16, 128, 256, 64, 64, 8>(p, s);
+    case T64x64:
+      return dma ? launch_gemm<bf16, 64, 64, 32, 32, 4, 0>(p, s) : launch_gemm<bf16, 64, 64, 32, 32, 4, 2>(p, s);
+    case T128x64:
+      return dma ? launch_gemm<bf16, 128, 64, 64, 32, 4, 0>(p, s) : launch_gemm<bf16, 128, 64, 64, 32, 4>(p, s);
+    case T64x128:
+      return dma ? launch_gemm<bf16, 64, 128, 32, 64, 4, 0>(p, s) : launch_gemm<bf16, 64, 128, 32, 64, 4>(p, s);
+    case T128x128:
+      return dma ? launch_gemm<bf16, 128, 128, 32, 64, 8, 0>(p, s) : launch_gemm<bf16, 128, 128, 32, 64, 8>(p, s);
+    case T128x256:
+      return dma ? launch_gemm<bf16, 128, 256, 64, 64, 8, 0>(p, s) : launch_gemm<bf16, 128, 256, 64, 64, 8>(p, s);
     case F128x64: return launch_gemm<float, 128, 64, 64, 32, 4>(p, s);
     case F128x128: return launch_gemm<float, 128, 128, 64, 64, 4>(p, s);
     default: return hipErrorInvalidValue;

@@ -254,6 +254,30 @@ llatte_status llatte_mla_attention(
     size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * llatte_mla_attention_noalloc -- llatte_mla_attention for callers that
+ * cannot allocate device memory or pass a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). Same
+ * arguments, semantics and results as llatte_mla_attention, without
+ * workspace / workspace_bytes: the attention plan lives in a fixed device
+ * array of llatte_mla_attention_noalloc_max_scratch() bytes (8 MiB) inside
+ * the library, one per GPU, held until the process ends. The call allocates
+ * nothing. Sizes whose plan exceeds the array (llatte_mla_attention_
+ * workspace_size(a, B, Mtot, Ktot) > 8 MiB, about 600 K query rows) return
+ * LLATTE_ERR_WORKSPACE before anything is enqueued. Every call on a GPU uses
+ * that GPU's one array, which keeps the last call's plan: calls that overlap
+ * on one GPU (concurrent streams, or threads that do not serialise their
+ * launches) race and must not be issued. The array's device address is
+ * looked up on the first call on each device (that device current).
+ * ---------------------------------------------------------------------- */
+llatte_status llatte_mla_attention_noalloc(
+    const llatte_attn_desc* a, const void* q_lat, const void* c_lat,
+    const int32_t* kv_offsets, const int32_t* hq_offsets, int32_t B,
+    int32_t Mtot, int32_t Ktot, void* out, float* lse, void* stream);
+
+/* Bytes of the fixed scratch of llatte_mla_attention_noalloc. */
+size_t llatte_mla_attention_noalloc_max_scratch(void);
+
+/* ------------------------------------------------------------------------
  * llatte_mla_attention_backward -- gradients of llatte_mla_attention's
  * output with respect to q_lat and c_lat: the training backward of the
  * attention core of [LLaTTE] A.3 (C is both key and value), i.e. the

@@ -30,6 +30,7 @@
 
 #include <algorithm>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -936,11 +937,20 @@ size_t llatte_mla_attention_workspace_size(const llatte_attn_desc* a,
   return ar.off + 256;
 }
 
-llatte_status llatte_mla_attention(
+}  // extern "C"
+
+namespace llatte {
+static llatte_status scratch_ptr(void** out);
+constexpr size_t kAttnScratchBytes = (size_t)8 << 20;
+
+// Validation and launch of the attention core. The plan goes into the
+// caller's workspace, or (fixed_scratch) into the library's fixed scratch,
+// whose address is fetched only after every host-side check has passed.
+static llatte_status mla_attention_impl(
     const llatte_attn_desc* a, const void* q_lat, const void* c_lat,
     const int32_t* kv_offsets, const int32_t* hq_offsets, int32_t B,
     int32_t Mtot, int32_t Ktot, void* out, float* lse, void* workspace,
-    size_t workspace_bytes, void* stream) {
+    size_t workspace_bytes, void* stream, bool fixed_scratch) {
   if (!a) return fail(LLATTE_ERR_INVALID_ARG, "desc is NULL");
   if (a->dtype != LLATTE_F32 && a->dtype != LLATTE_BF16)
     return fail(LLATTE_ERR_UNSUPPORTED, "dtype %d", a->dtype);
@@ -952,15 +962,26 @@ llatte_status llatte_mla_attention(
     return fail(LLATTE_ERR_UNSUPPORTED, "bf16 attention needs rank in {64, 128, 256}");
   if (!b && a->rank > 256) return fail(LLATTE_ERR_UNSUPPORTED, "f32 attention needs rank <= 256");
   if (!(a->scale > 0.f)) return fail(LLATTE_ERR_INVALID_ARG, "scale must be > 0");
-  if (!q_lat || !c_lat || !kv_offsets || !hq_offsets || !out || !workspace)
+  if (!q_lat || !c_lat || !kv_offsets || !hq_offsets || !out || (!fixed_scratch && !workspace))
     return fail(LLATTE_ERR_INVALID_ARG, "NULL pointer");
   const void* ptrs[] = {q_lat, c_lat, out, lse, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(LLATTE_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   const size_t need = llatte_mla_attention_workspace_size(a, B, Mtot, Ktot);
-  if (workspace_bytes < need)
+  if (fixed_scratch) {
+    if (need > kAttnScratchBytes)
+      return fail(LLATTE_ERR_WORKSPACE,
+                  "these sizes need %zu bytes of plan scratch; the fixed scratch holds %zu "
+                  "(use llatte_mla_attention with a workspace)",
+                  need, kAttnScratchBytes);
+  } else if (workspace_bytes < need) {
     return fail(LLATTE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  }
   if (Mtot == 0) return LLATTE_OK;
+  if (fixed_scratch) {
+    const llatte_status st = scratch_ptr(&workspace);
+    if (st != LLATTE_OK) return st;
+  }
   const int bq = b ? attn_bq(a->n_heads, a->rank) : 0;
   const long long nh = (long long)Mtot - (long long)B * a->n_cand;
   const int icap = bq > 0 ? (int)(cdiv(nh, bq) + B + (long long)B * cdiv(a->n_cand, bq)) : 1;
@@ -989,6 +1010,52 @@ llatte_status llatte_mla_attention(
   ap.M_dev = P.counts + 3;
   HIP_TRY(attention(ap, b, s));
   return LLATTE_OK;
+}
+
+// Fixed scratch of llatte_mla_attention_noalloc (the attention plan), one
+// copy per device, held until the process ends. In host code the array's
+// name is only a stand-in: the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) char scratch[kAttnScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+static llatte_status scratch_ptr(void** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(LLATTE_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr) return fail(LLATTE_ERR_HIP, "hipGetSymbolAddress returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LLATTE_OK;
+}
+}  // namespace llatte
+
+extern "C" {
+
+llatte_status llatte_mla_attention(
+    const llatte_attn_desc* a, const void* q_lat, const void* c_lat,
+    const int32_t* kv_offsets, const int32_t* hq_offsets, int32_t B,
+    int32_t Mtot, int32_t Ktot, void* out, float* lse, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  return mla_attention_impl(a, q_lat, c_lat, kv_offsets, hq_offsets, B, Mtot, Ktot, out, lse,
+                            workspace, workspace_bytes, stream, false);
+}
+
+size_t llatte_mla_attention_noalloc_max_scratch(void) { return kAttnScratchBytes; }
+
+llatte_status llatte_mla_attention_noalloc(
+    const llatte_attn_desc* a, const void* q_lat, const void* c_lat,
+    const int32_t* kv_offsets, const int32_t* hq_offsets, int32_t B,
+    int32_t Mtot, int32_t Ktot, void* out, float* lse, void* stream) {
+  return mla_attention_impl(a, q_lat, c_lat, kv_offsets, hq_offsets, B, Mtot, Ktot, out, lse,
+                            nullptr, 0, stream, true);
 }
 
 llatte_status llatte_pyramid_compact(const void* values, int32_t row_elems,

@@ -120,6 +120,10 @@ _SIGS = {
         _c_int, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "llatte_mla_attention_workspace_size": (ctypes.c_size_t, [
         ctypes.POINTER(llatte_attn_desc), _c_int, _c_int, _c_int]),
+    "llatte_mla_attention_noalloc": (_c_int, [
+        ctypes.POINTER(llatte_attn_desc), _vp, _vp, _vp, _vp, _c_int, _c_int,
+        _c_int, _vp, _vp, _vp]),
+    "llatte_mla_attention_noalloc_max_scratch": (ctypes.c_size_t, []),
     "llatte_pyramid_compact": (_c_int, [
         _vp, _c_int, _c_int, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp]),
     "llatte_pyramid_counts": (_c_int, [
@@ -259,6 +263,18 @@ def llatte_mla_attention(adesc, q_lat, c_lat, kv_offsets, hq_offsets, B, Mtot,
         _p(hq_offsets), B, Mtot, Ktot, _p(out), _p(lse), _p(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "llatte_mla_attention")
+
+
+def llatte_mla_attention_noalloc(adesc, q_lat, c_lat, kv_offsets, hq_offsets,
+                                 B, Mtot, Ktot, out, lse, stream=None):
+    st = lib().llatte_mla_attention_noalloc(
+        ctypes.byref(adesc), _p(q_lat), _p(c_lat), _p(kv_offsets),
+        _p(hq_offsets), B, Mtot, Ktot, _p(out), _p(lse), _stream(stream))
+    _check(st, "llatte_mla_attention_noalloc")
+
+
+def llatte_mla_attention_noalloc_max_scratch():
+    return lib().llatte_mla_attention_noalloc_max_scratch()
 
 
 def llatte_pyramid_compact(values, row_elems, dt, offsets_in, B, total_rows,

@@ -102,6 +102,28 @@ def test_forward_argument_errors_return_status_without_launch(L):
     assert st == L.LLATTE_ERR_INVALID_ARG
 
 
+def test_noalloc_attention_host_validation(L):
+    """The fixed-scratch attention entry checks everything on the host before
+    it touches the device: sizes whose plan exceeds the fixed scratch, bad
+    ranks and NULL pointers are rejected (fake pointers, never dereferenced)."""
+    fake = ctypes.c_void_p(0x100000)
+    fn = L.lib().llatte_mla_attention_noalloc
+    cap = L.llatte_mla_attention_noalloc_max_scratch()
+    assert cap == 8 << 20
+    ad = L.llatte_attn_desc(8, 128, 0, L.LLATTE_BF16, 0.125)
+    big = 1_000_000
+    assert L.llatte_mla_attention_workspace_size(ad, 1, big, big) > cap
+    st = fn(ctypes.byref(ad), fake, fake, fake, fake, 1, big, big, fake, None, None)
+    assert st == L.LLATTE_ERR_WORKSPACE
+    assert "fixed scratch" in L.llatte_last_error()
+    assert L.llatte_mla_attention_workspace_size(ad, 64, 102400, 102400) <= cap
+    bad = L.llatte_attn_desc(4, 96, 0, L.LLATTE_BF16, 0.125)
+    st = fn(ctypes.byref(bad), fake, fake, fake, fake, 2, 10, 10, fake, None, None)
+    assert st == L.LLATTE_ERR_UNSUPPORTED
+    st = fn(ctypes.byref(ad), None, fake, fake, fake, 2, 10, 10, fake, None, None)
+    assert st == L.LLATTE_ERR_INVALID_ARG
+
+
 def test_attention_backward_argument_errors(L):
     # every case fails validation before anything is enqueued (fake pointers
     # are never dereferenced on these paths)

@@ -773,20 +773,31 @@ __global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
       });
       break;
     case EPI_RESID_F32: {
-      f32x4 r[TM][TN];
-      outs([&](int i, int j, int m, int n) {
-        r[i][j] = *(const f32x4*)(p.res.row(rrow[i]) + n);
-      });
+      // one 16-row block at a time: its residual loads all in flight, then
+      // its results (registers for TN loads, not TM x TN)
       float ssp[TM];  // partial sums of squares of the results
 #pragma unroll
-      for (int i = 0; i < TM; ++i) ssp[i] = 0.f;
-      outs([&](int i, int j, int m, int n) {
-        const f32x4 v = acc[i][j] * rsc[i] + r[i][j];
-        store4<float>((float*)p.C + coff(m, n), v[0], v[1], v[2], v[3]);
-        if (p.cast_out)
-          store4<T>((T*)p.cast_out + (size_t)m * p.ld_cast + n, v[0], v[1], v[2], v[3]);
-        ssp[i] += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
-      });
+      for (int i = 0; i < TM; ++i) {
+        ssp[i] = 0.f;
+        const int m = m0 + wm0 + i * 16 + lr;
+        f32x4 r[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = n0 + wn0 + j * 16 + (lane >> 4) * 4;
+          r[j] = f32x4{};
+          if (m < M && n < p.N) r[j] = *(const f32x4*)(p.res.row(rrow[i]) + n);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = n0 + wn0 + j * 16 + (lane >> 4) * 4;
+          if (m >= M || n >= p.N) continue;
+          const f32x4 v = acc[i][j] * rsc[i] + r[j];
+          store4<float>((float*)p.C + coff(m, n), v[0], v[1], v[2], v[3]);
+          if (p.cast_out)
+            store4<T>((T*)p.cast_out + (size_t)m * p.ld_cast + n, v[0], v[1], v[2], v[3]);
+          ssp[i] += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+        }
+      }
       if (p.ss_out) {
         // one slot per (row, strip of WN columns); strips start below N
         const int slots = (p.N + WN - 1) / WN;
@@ -800,14 +811,24 @@ __global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
       }
     } break;
     case EPI_GATHER_ADD_F32: {
-      f32x4 r[TM][TN];
-      outs([&](int i, int j, int m, int n) {
-        r[i][j] = load4<T>((const T*)p.table + (size_t)rrow[i] * p.ld_table + n);
-      });
-      outs([&](int i, int j, int m, int n) {
-        const f32x4 v = acc[i][j] * rsc[i] + r[i][j];
-        store4<float>((float*)p.C + coff(m, n), v[0], v[1], v[2], v[3]);
-      });
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int m = m0 + wm0 + i * 16 + lr;
+        f32x4 r[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = n0 + wn0 + j * 16 + (lane >> 4) * 4;
+          r[j] = f32x4{};
+          if (m < M && n < p.N) r[j] = load4<T>((const T*)p.table + (size_t)rrow[i] * p.ld_table + n);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = n0 + wn0 + j * 16 + (lane >> 4) * 4;
+          if (m >= M || n >= p.N) continue;
+          const f32x4 v = acc[i][j] * rsc[i] + r[j];
+          store4<float>((float*)p.C + coff(m, n), v[0], v[1], v[2], v[3]);
+        }
+      }
     } break;
     case EPI_GELU_BWD:
       outs([&](int i, int j, int m, int n) {

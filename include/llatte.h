@@ -64,6 +64,25 @@ typedef int32_t llatte_status;
  * input of llatte_summaries. */
 #define LLATTE_FLAG_RAW_READOUT 1u
 
+/* Opt-in device check of hist_offsets before anything else runs (the S_u of
+ * [LLaTTE] A.2 are ordered, non-empty action sequences): offsets[0] == 0,
+ * every L_u = offsets[u+1] - offsets[u] in [1, max_len], offsets[B] ==
+ * total_rows. One small kernel reads only the offsets and writes an error
+ * word; the call then synchronises the stream and returns
+ * LLATTE_ERR_INVALID_ARG (with the first failing user in the message) if the
+ * check failed, before any other kernel is launched. Without the flag such
+ * offsets are undefined behaviour. For tests and debugging; it costs a sync. */
+#define LLATTE_FLAG_VALIDATE 2u
+
+/* Per-layer dump for localising a parity failure: the output rows of every
+ * layer (and of the readout layer), float32, written to desc->debug_dump.
+ * Layer l's section starts at row llatte_mla_forward_debug_layout(...)[l]
+ * (element offset row * d) and holds the layer's B*n_q candidate (or seed)
+ * rows, then its kept history rows, user-major, oldest first, i.e. the layer's
+ * query rows; the section ends at the next offset (upper bound; the rows past
+ * the layer's actual count are left untouched). */
+#define LLATTE_FLAG_DEBUG_DUMP 4u
+
 #define LLATTE_MAX_LAYERS 64
 
 /* Pyramidal schedule ([LLaTTE] A.2): how many of the most recent history rows
@@ -90,7 +109,8 @@ typedef struct {
   int32_t head_dim;    /* d_k; the softmax scale is 1/sqrt(d_k)             */
   int32_t rank;        /* r                                                 */
   int32_t d_ff;        /* FFN hidden width (= 4d)                           */
-  int32_t n_layers;    /* N, 1 .. LLATTE_MAX_LAYERS                         */
+  int32_t n_layers;    /* N, 1 .. LLATTE_MAX_LAYERS - 1 (the readout takes
+                          the last plan slot)                              */
   int32_t n_q;         /* candidate query tokens per user (>= 0)            */
   int32_t d_ctx;       /* per-user context width d_c (>= 0)                 */
   int32_t dtype;       /* LLATTE_F32 or LLATTE_BF16                         */
@@ -100,8 +120,12 @@ typedef struct {
   llatte_pyramid_rule pyramid;
   int32_t n_seeds;     /* readout seed queries (0 = no readout)             */
   int32_t d_out;       /* readout embedding width                           */
-  uint32_t flags;      /* 0 or LLATTE_FLAG_RAW_READOUT                      */
+  uint32_t flags;      /* 0 or LLATTE_FLAG_RAW_READOUT | LLATTE_FLAG_VALIDATE
+                          | LLATTE_FLAG_DEBUG_DUMP                          */
   int32_t q_rank;      /* 0: full-rank queries; > 0: low-rank query width   */
+  float* debug_dump;   /* device, with LLATTE_FLAG_DEBUG_DUMP: float32
+                          [llatte_mla_forward_debug_layout()[N_plans], d]   */
+  size_t debug_dump_bytes;  /* its size in bytes                            */
 } llatte_model_desc;
 
 /* Weights of one layer (device pointers). g* are float32 gains; the
@@ -160,9 +184,17 @@ typedef struct {
  *
  * Precision of the BF16 path: matrices and activations entering matrix
  * products are bf16 with fp32 accumulation, except inside the attention core
- * where the latent C, the latent queries, the softmax weights and the latent
- * output are fp16 (normalised values; more mantissa at the same rate); the
- * residual stream, norms and softmax statistics are fp32.
+ * where the latent C, the latent queries (times scale * log2 e), the softmax
+ * weights and the latent output are fp16 (more mantissa than bf16 at the
+ * same rate); the residual stream, norms and softmax statistics are fp32.
+ * Range precondition of that choice: every element of C and of the scaled
+ * latent queries must stay below 65504 in magnitude (fp16's largest finite
+ * value), else the outputs hold inf/NaN. With latent_norm = 1 (the
+ * default, [LLaTTE] A.3) C is RMS-normalised, |C_j| <= sqrt(r) max|g_c|, so
+ * this holds for any gains below 65504 / sqrt(r); with latent_norm = 0 it
+ * is the caller's to ensure (|RMSNorm(R) W_dkv| and |q W_uk^T| / sqrt(d_k)
+ * * 1.443 below 65504). llatte_mla_attention itself has no such limit (it
+ * rescales its inputs by powers of two). The F32 path has none.
  *
  *   desc               host pointer
  *   w                  host pointer to device weights; may be NULL when
@@ -210,6 +242,16 @@ llatte_status llatte_pack_weights(const llatte_model_desc* desc,
 size_t llatte_mla_forward_workspace_size(const llatte_model_desc* desc,
                                          int32_t B, int32_t total_rows,
                                          int32_t max_len);
+
+/* Row layout of the LLATTE_FLAG_DEBUG_DUMP buffer (host only): writes
+ * n_layers + 2 (with a readout; n_layers + 1 without) int64 row offsets
+ * to row_offsets (host array): section l = rows row_offsets[l] ..
+ * row_offsets[l+1] - 1, each row d floats. Returns the number of offsets
+ * written, 0 if the arguments are invalid. The buffer needs
+ * row_offsets[last] * d * 4 bytes. */
+int32_t llatte_mla_forward_debug_layout(const llatte_model_desc* desc,
+                                        int32_t B, int32_t total_rows,
+                                        int32_t max_len, int64_t* row_offsets);
 
 /* ------------------------------------------------------------------------
  * llatte_mla_attention -- the attention core of the absorbed MLA form

@@ -267,13 +267,16 @@ def fuse_queries(cand, ctx, W_q):
 
 
 def forward(cfg, W, hist, offsets, cand=None, ctx=None, users=None,
-            absorbed=False, dtype=np.float64):
+            absorbed=False, dtype=np.float64, trace=None):
     """The sequence-module forward for each user in ``users`` (all if None).
 
     [LLaTTE] section 1.3.2: fusion of the query tokens, N layers of MLA with
     the pyramidal schedule, then the readout. Returns a dict with per-user
     lists 'hist' ([n_N(u), d]), 'cand' ([n_q, d]) and, with a readout,
-    'emb' ([d_out]).
+    'emb' ([d_out]). With ``trace`` (a list), one entry per user is appended:
+    the list of each layer's outputs (history rows, candidate rows), then,
+    with a readout, the readout layer's seed rows (no history rows) - the
+    values only, for localising a disagreement layer by layer.
     """
     offsets = np.asarray(offsets, dtype=np.int64)
     lengths = offsets[1:] - offsets[:-1]
@@ -297,14 +300,19 @@ def forward(cfg, W, hist, offsets, cand=None, ctx=None, users=None,
             Rc = fuse_queries(cu, xu, Wc["W_q"])
         else:
             Rc = np.zeros((0, cfg.d), dtype=dtype)
+        steps = []
         for l in range(cfg.N):
             Rh, Rc = mla_layer(Rh, Rc, int(keep[l, u]), layers[l], cfg, absorbed)
+            steps.append((Rh, Rc))
         res["hist"].append(Rh)
         res["cand"].append(Rc)
         if readout is not None:
             _, S = mla_layer(Rh, Wc["seeds"], 0, readout, cfg, absorbed)
+            steps.append((Rh[:0], S))
             flat = S.reshape(-1)   # Flatten(Z_raw), seed-major
             res["emb"].append(flat if Wc.get("W_p") is None else flat @ Wc["W_p"])
+        if trace is not None:
+            trace.append(steps)
     return res
 
 

@@ -134,6 +134,8 @@ struct Shapes {
   bool bf16, pre, lnorm;
   bool fnorm;                 // norms fused into the GEMMs (bf16, pre-norm)
   bool raw = false;           // readout returns Flatten(Z_raw) (no W_p)
+  bool validate = false;      // device check of the history offsets first
+  bool dump = false;          // per-layer output rows into desc->debug_dump
   float eps;
   int NP;                     // plans: N layers (+ readout)
   RuleDev rule;
@@ -181,7 +183,7 @@ static llatte_status expand_rule(const llatte_pyramid_rule* pr, int N,
 static llatte_status make_shapes(const llatte_model_desc* dsc, int B, int total,
                                  int max_len, Shapes* S) {
   if (!dsc) return fail(LLATTE_ERR_INVALID_ARG, "desc is NULL");
-  if (dsc->flags & ~LLATTE_FLAG_RAW_READOUT)
+  if (dsc->flags & ~(LLATTE_FLAG_RAW_READOUT | LLATTE_FLAG_VALIDATE | LLATTE_FLAG_DEBUG_DUMP))
     return fail(LLATTE_ERR_INVALID_ARG, "unknown flags 0x%x", dsc->flags);
   if (B < 1 || total < B || max_len < 1 || (long long)max_len * B < total)
     return fail(LLATTE_ERR_INVALID_ARG, "need B >= 1, total_rows >= B, max_len*B >= total_rows");
@@ -206,6 +208,8 @@ static llatte_status make_shapes(const llatte_model_desc* dsc, int B, int total,
   S->ns = dsc->n_seeds;
   S->dout = dsc->d_out;
   S->raw = (dsc->flags & LLATTE_FLAG_RAW_READOUT) != 0;
+  S->validate = (dsc->flags & LLATTE_FLAG_VALIDATE) != 0;
+  S->dump = (dsc->flags & LLATTE_FLAG_DEBUG_DUMP) != 0;
   S->rq = dsc->q_rank;
   S->qin = S->rq > 0 ? S->rq : dsc->d;
   S->bf16 = dsc->dtype == LLATTE_BF16;
@@ -346,6 +350,7 @@ struct FwdWS {
   float* S;     // [B*ns, d]
   void* E;      // [B*ns*d]
   float* sk_part;  // split-K tiles of the GEMMs (kSkPart floats)
+  int* vcheck;     // [2] result of the offsets check (LLATTE_FLAG_VALIDATE)
 };
 
 // Split-K scratch of the GEMMs that leave the GPU short of workgroups (late
@@ -394,7 +399,16 @@ static size_t layout_forward(const Shapes& S, void* base, FwdWS* w) {
   w->S = S.ns ? ar.take<float>((size_t)S.B * S.ns * S.d) : nullptr;
   w->E = S.ns ? ar.take<char>((size_t)S.B * S.ns * S.d * e) : nullptr;
   w->sk_part = ar.take<float>((size_t)kSkPart);
+  w->vcheck = ar.take<int>(2);
   return ar.off + 256;
+}
+
+// First row of each layer's section of the debug dump (N layers, the readout
+// if any, then the end): the sections hold the layers' query rows.
+static std::vector<long long> dump_rows(const Shapes& S) {
+  std::vector<long long> off(S.NP + 1, 0);
+  for (int l = 0; l < S.NP; ++l) off[l + 1] = off[l] + S.UBM[l];
+  return off;
 }
 
 static llatte_status check_layer(const Shapes& S, const llatte_layer_weights* L, int l) {
@@ -773,6 +787,16 @@ size_t llatte_mla_forward_workspace_size(const llatte_model_desc* desc,
   return layout_forward(S, nullptr, &w);
 }
 
+int32_t llatte_mla_forward_debug_layout(const llatte_model_desc* desc, int32_t B,
+                                        int32_t total_rows, int32_t max_len,
+                                        int64_t* row_offsets) {
+  Shapes S;
+  if (!row_offsets || make_shapes(desc, B, total_rows, max_len, &S) != LLATTE_OK) return 0;
+  const std::vector<long long> off = dump_rows(S);
+  for (size_t i = 0; i < off.size(); ++i) row_offsets[i] = off[i];
+  return (int32_t)off.size();
+}
+
 size_t llatte_packed_weights_size(const llatte_model_desc* desc) {
   Shapes S;
   if (make_shapes(desc, 1, 1, 1, &S) != LLATTE_OK) return 0;
@@ -838,8 +862,30 @@ llatte_status llatte_mla_forward(
   const size_t need = layout_forward(S, nullptr, &w);
   if (workspace_bytes < need)
     return fail(LLATTE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  std::vector<long long> dsec;
+  if (S.dump) {
+    dsec = dump_rows(S);
+    const size_t need_dump = (size_t)dsec.back() * S.d * sizeof(float);
+    if (!desc->debug_dump || !aligned16(desc->debug_dump))
+      return fail(LLATTE_ERR_INVALID_ARG, "LLATTE_FLAG_DEBUG_DUMP needs a 16-byte aligned debug_dump");
+    if (desc->debug_dump_bytes < need_dump)
+      return fail(LLATTE_ERR_WORKSPACE, "debug_dump %zu bytes < %zu needed", desc->debug_dump_bytes,
+                  need_dump);
+  }
   layout_forward(S, workspace, &w);
   hipStream_t s = (hipStream_t)stream;
+  if (S.validate) {
+    // the only launch before the offsets are known to be well formed
+    int h[2] = {0, 0};
+    HIP_TRY(validate_offsets(hist_offsets, B, total_rows, max_len, w.vcheck, s));
+    HIP_TRY(hipMemcpyAsync(h, w.vcheck, sizeof h, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    static const char* what[] = {"", "hist_offsets[0] != 0", "an empty history (L_u < 1)",
+                                 "a history longer than max_len", "hist_offsets[B] != total_rows"};
+    if (h[0] != 0)
+      return fail(LLATTE_ERR_INVALID_ARG, "LLATTE_FLAG_VALIDATE: %s at user %d",
+                  what[h[0] >= 1 && h[0] <= 4 ? h[0] : 0], h[1]);
+  }
   const bool b = S.bf16;
   Packed PK;
   if (packed_weights) {
@@ -880,6 +926,9 @@ llatte_status llatte_mla_forward(
     float* out = w.Rb[l & 1];
     io.next = S.fnorm && l + 1 < S.N;
     HIP_TRY(run_layer(S, w, l, PK.L[l], src, out, io, s));
+    if (S.dump)
+      HIP_TRY(copy_rows_f32(out, S.d, desc->debug_dump + (size_t)dsec[l] * S.d, (int)S.UBM[l],
+                            w.plan.layer(l).counts + 3, S.d, s));
     io.in_ready = io.next;
     io.np_in = io.np_out;
     last = out;
@@ -898,6 +947,9 @@ llatte_status llatte_mla_forward(
     RowSrc src{w.S, last + nc * S.d, B * S.ns, S.d};
     LayerIO rio;
     HIP_TRY(run_layer(S, w, S.N, PK.L[S.N], src, ro, rio, s));
+    if (S.dump)
+      HIP_TRY(copy_rows_f32(ro, S.d, desc->debug_dump + (size_t)dsec[S.N] * S.d, (int)S.UBM[S.N],
+                            w.plan.layer(S.N).counts + 3, S.d, s));
     if (S.raw) {  // Flatten(Z_raw): the readout rows are already seed-major per user
       HIP_TRY(copy_rows_f32(ro, S.d, out_emb, B * S.ns, nullptr, S.d, s));
       return LLATTE_OK;
@@ -934,6 +986,7 @@ size_t llatte_mla_attention_workspace_size(const llatte_attn_desc* a,
       bq > 0 ? cdiv(nh, bq) + B + (long long)B * cdiv(a->n_cand, bq) : 1;
   Arena ar(nullptr);
   carve_plan(ar, 1, B, std::max(Mtot, 1), (int)icap);
+  ar.take<unsigned>(2);  // max magnitudes of q_lat and c_lat (bf16 range scaling)
   return ar.off + 256;
 }
 
@@ -987,8 +1040,14 @@ static llatte_status mla_attention_impl(
   const int icap = bq > 0 ? (int)(cdiv(nh, bq) + B + (long long)B * cdiv(a->n_cand, bq)) : 1;
   Arena ar(workspace);
   PlanBase pb = carve_plan(ar, 1, B, Mtot, icap);
+  unsigned* amax = ar.take<unsigned>(2);
   hipStream_t s = (hipStream_t)stream;
   HIP_TRY(build_attn_plan(kv_offsets, hq_offsets, B, a->n_cand, bq, kAttnBN, pb, s));
+  // bf16: the kernel computes in fp16 after power-of-two scalings chosen from
+  // the inputs' largest magnitudes, so any finite input stays in range
+  if (b)
+    HIP_TRY(attn_absmax(q_lat, (long long)Mtot * a->n_heads * a->rank, c_lat,
+                        (long long)Ktot * a->rank, a->scale, amax, s));
   const LayerPlan P = pb.layer(0);
   AttnParams ap;
   ap.q = q_lat;
@@ -1008,6 +1067,7 @@ static llatte_status mla_attention_impl(
   ap.qinfo = P.qinfo;
   ap.M_cap = Mtot;
   ap.M_dev = P.counts + 3;
+  ap.amax = b ? amax : nullptr;
   HIP_TRY(attention(ap, b, s));
   return LLATTE_OK;
 }

@@ -50,6 +50,7 @@
 //
 // fp32 kernel: one wave per (query row, head), keys 64 at a time, plain
 // online softmax. It serves the fp32 path only.
+#include <algorithm>
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -110,12 +111,14 @@ __device__ __forceinline__ f16x8 pack8(f32x4 lo, f32x4 hi) {
 __device__ __forceinline__ f16x8 cat(f16x4 lo, f16x4 hi) {
   return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
-__device__ __forceinline__ f16x8 to_f16x8(i32x4 raw, bool is_bf16) {
+// Eight stored values as fp16; bf16 input is scaled by `mul` (a power of
+// two, exact) before the conversion.
+__device__ __forceinline__ f16x8 to_f16x8(i32x4 raw, bool is_bf16, float mul) {
   if (!is_bf16) return __builtin_bit_cast(f16x8, raw);
   const bf16x8 b = __builtin_bit_cast(bf16x8, raw);
   f16x8 r;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (f16)from_bf16(b[i]);
+  for (int i = 0; i < 8; ++i) r[i] = (f16)(from_bf16(b[i]) * mul);
   return r;
 }
 
@@ -185,6 +188,27 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
   const int g = lane >> 4, l16 = lane & 15;
   const float sc = p.scale * kLog2e;   // scores in log2 units
   const CT* Cg = (const CT*)p.c + (size_t)kvb * R;
+  // Standalone path: C and the scaled latent queries enter fp16 as
+  // C 2^-ec and q sc 2^-eq, each exponent chosen so that the largest
+  // magnitude lies in [2^13, 2^14): far from fp16's overflow (65504) and, for
+  // all values within 2^-24 of the largest, from its subnormals. The MFMAs
+  // then give scores times 2^-(ec+eq), scaled back before the softmax, and
+  // the output is scaled by 2^ec at the end; powers of two are exact, so for
+  // values that fp16 represents either way the results equal the unscaled
+  // computation's. Exponents are clamped to +-60 (all-zero inputs).
+  int ec = 0, eq = 0;
+  if constexpr (!FUSED) {
+    if (p.amax) {
+      const auto e_of = [](unsigned bits) {  // x < 2^e for finite x > 0
+        return (int)((bits >> 23) & 0xff) - 126;
+      };
+      eq = min(max(-60, e_of(p.amax[0]) - 14), 60);
+      ec = min(max(-60, e_of(p.amax[1]) - 14), 60);
+    }
+  }
+  const float c_pre = __builtin_ldexpf(1.f, -ec);       // applied to C on staging
+  const float s_post = __builtin_ldexpf(1.f, ec + eq);  // undoes both on the scores
+  const bool rescale = ec + eq != 0;
 
   // this lane's effective rows: one per block (head uniform per block)
   int head[NEB], qrow[NEB], pos[NEB];
@@ -237,7 +261,7 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const f16x8 v = to_f16x8(ld[i], C_BF16);
+      const f16x8 v = to_f16x8(ld[i], C_BF16, c_pre);
       *(f16x4*)&Cs[buf][st_off[i]] = f16x4{v[0], v[1], v[2], v[3]};
       *(f16x4*)&Cs[buf][st_off2[i]] = f16x4{v[4], v[5], v[6], v[7]};
     }
@@ -293,7 +317,8 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
         const bf16x4 lo = *(const bf16x4*)(qp + ks * 32);
         const bf16x4 hi = *(const bf16x4*)(qp + ks * 32 + 16);
         qf[eb][ks] = pack8(f32x4{from_bf16(lo[0]), from_bf16(lo[1]), from_bf16(lo[2]), from_bf16(lo[3])},
-                           f32x4{from_bf16(hi[0]), from_bf16(hi[1]), from_bf16(hi[2]), from_bf16(hi[3])}, sc);
+                           f32x4{from_bf16(hi[0]), from_bf16(hi[1]), from_bf16(hi[2]), from_bf16(hi[3])},
+                           __builtin_ldexpf(sc, -eq));
       }
     }
   }
@@ -479,7 +504,21 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
     float m0[NEB];
 #pragma unroll
     for (int eb = 0; eb < NEB; ++eb) m0[eb] = t == 0 ? 0.f : m_run[eb];
+    if constexpr (!FUSED) {
+      if (rescale) {
+#pragma unroll
+        for (int eb = 0; eb < NEB; ++eb) m0[eb] /= s_post;
+      }
+    }
     scores(cs, st, t + 1, m0);
+    if constexpr (!FUSED) {
+      if (rescale) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int eb = 0; eb < NEB; ++eb) st[kb][eb] *= s_post;
+      }
+    }
     f16x8 pa[kPre];
 #pragma unroll
     for (int j = 0; j < kPre; ++j) pa[j] = rd_pv(cs, j);
@@ -537,7 +576,7 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
 #pragma unroll
     for (int eb = 0; eb < NEB; ++eb) {
       if (!valid[eb]) continue;
-      const float inv = 1.f / acc_l[eb][0];
+      const float inv = __builtin_ldexpf(1.f / acc_l[eb][0], ec);
       const size_t orow = (size_t)qrow[eb] * p.h + head[eb];
       float* op = (float*)p.out + orow * R;
       // O^T rows come in stored order: rows 16 rb + 4g .. +3 hold the chunk
@@ -647,6 +686,39 @@ static hipError_t launch_r(const AttnParams& p, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   return hipSuccess;
+}
+
+// Largest magnitude of bf16 arrays (float bits of non-negative values order
+// like unsigned integers): a grid-stride max per thread, a wave max, one
+// atomic per wave. amax must be zero first (attn_absmax_zero).
+__global__ void attn_absmax_zero(unsigned* amax) {
+  if (threadIdx.x < 2) amax[threadIdx.x] = 0u;
+}
+__global__ __launch_bounds__(256) void attn_absmax_kernel(const bf16* q, long long nq,
+                                                          const bf16* c, long long nc, float sc,
+                                                          unsigned* amax) {
+  float mq = 0.f, mc = 0.f;
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < nq; i += stride)
+    mq = fmaxf(mq, fabsf(from_bf16(q[i])));
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < nc; i += stride)
+    mc = fmaxf(mc, fabsf(from_bf16(c[i])));
+  mq = wave_max(mq) * sc;
+  mc = wave_max(mc);
+  if ((threadIdx.x & 63) == 0) {
+    atomicMax(&amax[0], __float_as_uint(mq));
+    atomicMax(&amax[1], __float_as_uint(mc));
+  }
+}
+
+hipError_t attn_absmax(const void* q, long long nq, const void* c, long long nc, float scale,
+                       unsigned* amax, hipStream_t s) {
+  hipLaunchKernelGGL(attn_absmax_zero, dim3(1), dim3(64), 0, s, amax);
+  const long long n = std::max(nq, nc);
+  const int blocks = (int)std::max<long long>(1, std::min<long long>((n + 255) / 256, 2048));
+  hipLaunchKernelGGL(attn_absmax_kernel, dim3(blocks), dim3(256), 0, s, (const bf16*)q, nq,
+                     (const bf16*)c, nc, scale * kLog2e, amax);
+  return hipGetLastError();
 }
 
 hipError_t attention(const AttnParams& p, bool is_bf16, hipStream_t s) {

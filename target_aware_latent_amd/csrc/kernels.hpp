@@ -243,6 +243,11 @@ hipError_t build_attn_plan(const int* kv_off, const int* hq_off, int B,
 hipError_t pyramid_counts_dev(const RuleDev& rule, const int* offsets, int B,
                               int* keep_out, hipStream_t s);
 
+// err[0..1] = {kind, user} of the first malformed history offset (0 when
+// every L_u is in [1, max_len], offsets[0] == 0 and offsets[B] == total).
+hipError_t validate_offsets(const int* offsets, int B, int total, int max_len, int* err,
+                            hipStream_t s);
+
 hipError_t pyramid_compact(const void* values, int row_bytes,
                            const int* offsets_in, int B, int total_rows,
                            const int* keep, void* values_out,
@@ -272,6 +277,10 @@ struct AttnParams {
   const int2* qinfo;  // f32 path: per query row {kv base, key position}
   int M_cap;
   const int* M_dev;
+  // standalone bf16 path: {max |q| * scale * log2 e, max |c|} as float bits
+  // (attn_absmax); the kernel scales both by powers of two into fp16 range
+  // and undoes the scaling exactly. nullptr: no scaling.
+  const unsigned* amax = nullptr;
 };
 
 // LDS layout of the latent rows in the MFMA attention kernel: within each
@@ -293,5 +302,9 @@ int attn_bq(int h, int r);
 bool attn_fused_supported(int h, int r, int dk);
 constexpr int kAttnBN = 64;
 hipError_t attention(const AttnParams& p, bool bf16, hipStream_t s);
+// amax[0] = max |q| * scale * log2 e, amax[1] = max |c| (bf16 inputs, float
+// bits, written from zero by this call: two launches, no memset).
+hipError_t attn_absmax(const void* q, long long nq, const void* c, long long nc, float scale,
+                       unsigned* amax, hipStream_t s);
 
 }  // namespace llatte

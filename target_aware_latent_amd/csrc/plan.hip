@@ -265,6 +265,57 @@ hipError_t pyramid_counts_dev(const RuleDev& rule, const int* offsets, int B,
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ validation
+// Check of the history offsets (the opt-in LLATTE_FLAG_VALIDATE): every
+// user's L_u = offsets[u+1] - offsets[u] in [1, max_len], offsets[0] == 0,
+// offsets[B] == total. One block; each thread scans a chunk of users and the
+// block keeps the smallest failing index. err[0] = kind (0: valid; 1:
+// offsets[0] != 0; 2: L_u < 1; 3: L_u > max_len; 4: offsets[B] != total),
+// err[1] = the user (or B for kind 4). Written whatever the outcome, so the
+// words need no clearing before the launch.
+__global__ __launch_bounds__(kPlanThreads) void validate_offsets_kernel(
+    const int* offsets, int B, int total, int max_len, int* err) {
+  __shared__ int first[2];
+  const int t = threadIdx.x;
+  if (t == 0) {
+    first[0] = 0x7fffffff;  // smallest failing user (kinds 2, 3)
+    first[1] = 0;           // its kind
+  }
+  __syncthreads();
+  const int chunk = (B + kPlanThreads - 1) / kPlanThreads;
+  const int u0 = min(B, t * chunk), u1 = min(B, u0 + chunk);
+  for (int u = u0; u < u1; ++u) {
+    const int L = offsets[u + 1] - offsets[u];
+    if (L < 1 || L > max_len) {
+      atomicMin(&first[0], u);
+      break;
+    }
+  }
+  __syncthreads();
+  if (t == 0) {
+    int kind = 0, who = 0;
+    if (offsets[0] != 0) {
+      kind = 1;
+    } else if (first[0] != 0x7fffffff) {
+      who = first[0];
+      const int L = offsets[who + 1] - offsets[who];
+      kind = L < 1 ? 2 : 3;
+    } else if (offsets[B] != total) {
+      kind = 4;
+      who = B;
+    }
+    err[0] = kind;
+    err[1] = who;
+  }
+}
+
+hipError_t validate_offsets(const int* offsets, int B, int total, int max_len, int* err,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(validate_offsets_kernel, dim3(1), dim3(kPlanThreads), 0, s, offsets, B, total,
+                     max_len, err);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ compaction
 __global__ __launch_bounds__(kPlanThreads) void compact_scan_kernel(
     const int* keep, int B, int* offsets_out) {

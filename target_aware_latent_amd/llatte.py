@@ -27,6 +27,8 @@ LLATTE_PYR_HALVING = 1
 LLATTE_PYR_GEOMETRIC = 2
 LLATTE_MAX_LAYERS = 64
 LLATTE_FLAG_RAW_READOUT = 1
+LLATTE_FLAG_VALIDATE = 2
+LLATTE_FLAG_DEBUG_DUMP = 4
 
 _c_int = ctypes.c_int32
 _vp = ctypes.c_void_p
@@ -44,7 +46,8 @@ class llatte_model_desc(ctypes.Structure):
                 ("norm_mode", _c_int), ("latent_norm", _c_int),
                 ("eps", ctypes.c_float), ("pyramid", llatte_pyramid_rule),
                 ("n_seeds", _c_int), ("d_out", _c_int),
-                ("flags", ctypes.c_uint32), ("q_rank", _c_int)]
+                ("flags", ctypes.c_uint32), ("q_rank", _c_int),
+                ("debug_dump", _vp), ("debug_dump_bytes", ctypes.c_size_t)]
 
 
 class llatte_layer_weights(ctypes.Structure):
@@ -115,6 +118,9 @@ _SIGS = {
         ctypes.c_size_t, _vp]),
     "llatte_mla_forward_workspace_size": (ctypes.c_size_t, [
         ctypes.POINTER(llatte_model_desc), _c_int, _c_int, _c_int]),
+    "llatte_mla_forward_debug_layout": (_c_int, [
+        ctypes.POINTER(llatte_model_desc), _c_int, _c_int, _c_int,
+        ctypes.POINTER(ctypes.c_int64)]),
     "llatte_mla_attention": (_c_int, [
         ctypes.POINTER(llatte_attn_desc), _vp, _vp, _vp, _vp, _c_int, _c_int,
         _c_int, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
@@ -225,6 +231,16 @@ def _stream(stream):
 def llatte_mla_forward_workspace_size(desc, B, total_rows, max_len):
     return lib().llatte_mla_forward_workspace_size(ctypes.byref(desc), B,
                                                    total_rows, max_len)
+
+
+def llatte_mla_forward_debug_layout(desc, B, total_rows, max_len):
+    """Row offsets of the LLATTE_FLAG_DEBUG_DUMP sections (list of ints)."""
+    buf = (ctypes.c_int64 * (LLATTE_MAX_LAYERS + 2))()
+    n = lib().llatte_mla_forward_debug_layout(ctypes.byref(desc), B, total_rows,
+                                              max_len, buf)
+    if n <= 0:
+        raise RuntimeError("llatte_mla_forward_debug_layout: invalid arguments")
+    return [int(buf[i]) for i in range(n)]
 
 
 def llatte_mla_forward(desc, weights, packed_weights, hist_values,

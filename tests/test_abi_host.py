@@ -64,7 +64,7 @@ def test_invalid_descriptors_rejected_on_host(L):
     assert L.llatte_mla_forward_workspace_size(good, 4, 100, 50) > 0
     for field, val in [("d_ff", 3 * cfg.d), ("rank", 96), ("dtype", 7),
                        ("n_layers", 0), ("head_dim", 12), ("head_dim", 48),
-                       ("flags", 2), ("q_rank", 12), ("q_rank", -8),
+                       ("flags", 8), ("q_rank", 12), ("q_rank", -8),
                        ("q_rank", 1032)]:
         d = make_desc(cfg)
         setattr(d, field, val)
@@ -100,6 +100,39 @@ def test_forward_argument_errors_return_status_without_launch(L):
     st = L.lib().llatte_pyramid_compact(None, 8, L.LLATTE_F32, None, 2, 10,
                                         None, None, None, None, None)
     assert st == L.LLATTE_ERR_INVALID_ARG
+
+
+def test_forward_flags_host_side(L):
+    """VALIDATE and DEBUG_DUMP are accepted; the dump layout has one section
+    per layer (and the readout) sized by the host row bounds; a missing or
+    short dump buffer is rejected before anything is enqueued."""
+    from target_aware_latent_amd.model import make_desc
+    cfg = synth.get_config("c3")
+    d = make_desc(cfg)
+    d.flags = L.LLATTE_FLAG_VALIDATE | L.LLATTE_FLAG_DEBUG_DUMP
+    B, total, max_len = 64, 64 * 1600, 1600
+    assert L.llatte_mla_forward_workspace_size(d, B, total, max_len) > 0
+    secs = L.llatte_mla_forward_debug_layout(d, B, total, max_len)
+    sched = [1600, 800, 400, 200, 100, 50]
+    assert secs == [0] + list(np.cumsum([B * n for n in sched] + [B * cfg.n_seeds]))
+    fake = ctypes.c_void_p(0x100000)
+    w = L.llatte_weights()
+    args = lambda: (ctypes.byref(d), ctypes.byref(w), fake, fake, fake, B, total, max_len,
+                    None, None, None, None, None, fake, fake, 1 << 40, None)
+    d.debug_dump = None
+    assert L.lib().llatte_mla_forward(*args()) == L.LLATTE_ERR_INVALID_ARG
+    assert "debug_dump" in L.llatte_last_error()
+    d.debug_dump = 0x200000
+    d.debug_dump_bytes = secs[-1] * cfg.d * 4 - 4
+    assert L.lib().llatte_mla_forward(*args()) == L.LLATTE_ERR_WORKSPACE
+    # n_layers bounds as documented: 1 .. LLATTE_MAX_LAYERS - 1
+    d2 = make_desc(cfg)
+    d2.n_layers = L.LLATTE_MAX_LAYERS
+    assert L.llatte_mla_forward_workspace_size(d2, B, total, max_len) == 0
+    d2.n_layers = L.LLATTE_MAX_LAYERS - 1
+    d2.pyramid.kind = L.LLATTE_PYR_HALVING
+    d2.pyramid.floor = 16
+    assert L.llatte_mla_forward_workspace_size(d2, B, total, max_len) > 0
 
 
 def test_noalloc_attention_host_validation(L):

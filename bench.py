@@ -100,6 +100,34 @@ def kernel_flops(cfg, lengths):
     return f
 
 
+def family_bytes(cfg, lengths):
+    """Algorithmic HBM bytes per step of the two kernel symbols (bf16 path):
+    every operand read once, every result written once. GEMM family, per
+    layer: W_dkv reads the KV rows (2d B) and writes the fp16 latent (2r B);
+    W_uq reads the gathered rows (2d) and writes q (2 h dk); W_o reads o
+    (2 h dk) and the fp32 residual (4d) and writes the fp32 result and its
+    bf16 copy (4d + 2d); W1 reads that copy (2d) and writes the hidden layer
+    (2 d_ff); W2 reads it (2 d_ff) and the fp32 residual (4d) and writes the
+    fp32 result (4d), plus its bf16 copy (2d) except at the last layer; the
+    weights once per layer; the readout's W_p product its rows, W_p and the
+    embedding. Attention: q and o rows (2 h dk each), the fp16 latent rows
+    (2r), W_uk and W_uv once per layer."""
+    d, h, dk, r, dff = cfg.d, cfg.h, cfg.dk, cfg.r, 4 * cfg.d
+    hd = h * dk
+    g = a = 0
+    layers = layer_counts(cfg, lengths)
+    for l, (Ks, ns, M, pairs) in enumerate(layers):
+        last = l == cfg.N - 1 or l >= cfg.N
+        g += Ks * (2 * d + 2 * r) + M * (2 * d + 2 * hd)
+        g += M * (2 * hd + 4 * d + 4 * d + 2 * d) + M * (2 * d + 2 * dff)
+        g += M * (2 * dff + 4 * d + 4 * d + (0 if last else 2 * d))
+        g += 2 * (d * r + d * hd + hd * d + 2 * d * dff)
+        a += M * (2 * hd + 2 * hd) + Ks * 2 * r + 2 * (2 * r * hd)
+    if cfg.n_seeds:
+        g += cfg.B * cfg.n_seeds * d * 2 + cfg.n_seeds * d * cfg.d_out * 2 + cfg.B * cfg.d_out * 4
+    return {"gemm_kernel": g, "attn_mfma_kernel": a}
+
+
 def absorbed_flops(cfg, lengths):
     return sum(kernel_flops(cfg, lengths).values())
 
@@ -120,25 +148,40 @@ def non_absorbed_flops(cfg, lengths):
     return t
 
 
+def family_of(label):
+    """Kernel symbol behind a timing label: the matrix products all run the
+    GEMM kernel template; the attention labels the attention kernel."""
+    if label.startswith("gemm_"):
+        return "gemm_kernel"
+    if label.startswith("attention_mfma"):
+        return "attn_mfma_kernel"
+    return label
+
+
 def kernel_source(label):
-    """Source file of the kernel behind a timing label."""
-    name = ("attention.hip" if label.startswith("attention") else
+    """Source file of the kernel behind a timing label or symbol."""
+    name = ("attention.hip" if label.startswith(("attention", "attn")) else
             "plan.hip" if label == "pyramid_compact" else "gemm.hip")
     return os.path.join(ROOT, "target_aware_latent_amd", "csrc", name)
 
 
 def read_traffic(path, label):
-    """HBM bytes per launch of `label` from a profile summary's RECORD line,
-    or None when there is none or the kernel changed since it was taken."""
-    if not path or not os.path.exists(path):
-        return None
+    """HBM bytes per launch of `label` from the RECORD line of a profile
+    summary (`path`, or every profiles/c3_*_hbm_traffic.txt when None), or
+    None when there is none or the kernel changed since it was taken."""
+    import glob
+    paths = [path] if path else sorted(glob.glob(os.path.join(ROOT, "profiles",
+                                                              "c3_*_hbm_traffic.txt")))
     from target_aware_latent_amd.profsum import fingerprint
-    for line in open(path):
-        if line.startswith("RECORD "):
-            rec = json.loads(line[len("RECORD "):])
-            if rec.get("kernel") == label and \
-                    rec.get("fingerprint") == fingerprint(kernel_source(label)):
-                return rec.get("bytes")
+    for p in paths:
+        if not os.path.exists(p):
+            continue
+        for line in open(p):
+            if line.startswith("RECORD "):
+                rec = json.loads(line[len("RECORD "):])
+                if rec.get("kernel") == label and \
+                        rec.get("fingerprint") == fingerprint(kernel_source(label)):
+                    return rec.get("bytes")
     return None
 
 
@@ -165,31 +208,44 @@ def emit(rec):
     print(json.dumps(rec))
 
 
-def cpu_baseline(prob, budget_s=12.0):
-    """The oracle as it stands, in fp32 on the host cores, on the first users
-    of the batch until about budget_s seconds of work (at least one user)."""
-    from oracle import llatte_oracle as O
-    cfg, I, W = prob["cfg"], prob["inputs"], prob["weights"]
-    threads = None
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = sum(p.get("num_threads", 0) for p in threadpool_info()
-                      if p.get("user_api") == "blas") or None
+        return sum(p.get("num_threads", 0) for p in threadpool_info()
+                   if p.get("user_api") == "blas") or None
     except Exception:
-        pass
-    users = 0
-    t0 = time.perf_counter()
-    while users < cfg.B:
+        return None
+
+
+def cpu_baseline(prob, budget_s=36.0):
+    """The oracle as it stands, in fp32 on the host cores: the median of
+    three passes over the whole batch when three fit in about budget_s
+    seconds, else the median of three passes over the first users whose pass
+    takes about a third of it (at least one user)."""
+    from oracle import llatte_oracle as O
+    cfg, I, W = prob["cfg"], prob["inputs"], prob["weights"]
+    threads = _blas_threads()
+
+    def one_pass(users):
+        t0 = time.perf_counter()
         O.forward(cfg, W, I["hist"], I["offsets"], I.get("cand"), I.get("ctx"),
-                  users=[users], dtype=np.float32)
-        users += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": users / dt, "unit": "user-seq/s",
+                  users=users, dtype=np.float32)
+        return time.perf_counter() - t0
+
+    # a warm pass of the first user alone sizes the sample
+    one_pass([0])
+    t1 = one_pass([0])
+    n = min(cfg.B, max(1, int(budget_s / 3 / max(t1, 1e-6))))
+    users = list(range(n))
+    times = sorted(one_pass(users) for _ in range(3))
+    med = times[1]
+    what = "the whole batch" if n == cfg.B else f"the first {n} of {cfg.B} users"
+    return {"value": n / med, "unit": "user-seq/s",
             "cores": threads or len(os.sched_getaffinity(0)), "kind": "oracle",
-            "sample": f"{users} of {cfg.B} users of the same workload, fp32 "
-                      f"oracle (non-absorbed definition), {dt:.1f} s"}
+            "affinity_cores": len(os.sched_getaffinity(0)), "blas_threads": threads,
+            "sample": f"median of 3 passes over {what} of the same workload "
+                      f"({', '.join(f'{t:.2f}' for t in times)} s), fp32 oracle "
+                      f"(non-absorbed definition)"}
 
 
 def cpu_baseline_tokens(prob, host_table, budget_s=12.0):
@@ -216,8 +272,10 @@ def cpu_baseline_tokens(prob, host_table, budget_s=12.0):
         dt += time.perf_counter() - t0
         users += 1
         print(f"  oracle user {users}: {dt:.1f} s", file=sys.stderr, flush=True)
-    return {"value": users / dt, "unit": "user-seq/s", "cores": len(os.sched_getaffinity(0)),
-            "kind": "oracle",
+    threads = _blas_threads()
+    return {"value": users / dt, "unit": "user-seq/s",
+            "cores": threads or len(os.sched_getaffinity(0)), "kind": "oracle",
+            "affinity_cores": len(os.sched_getaffinity(0)), "blas_threads": threads,
             "sample": f"{users} of {cfg.B} users of the same workload, fp32 oracle (token build "
                       f"and non-absorbed forward; table-row gathering not timed), {dt:.1f} s"}
 
@@ -314,6 +372,7 @@ def bench_actions(args):
                    "parallelism": "single GPU"},
         "tflops": round(tflops, 2), "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+        "kernel_symbols": families if not args.no_kernel_times else None,
     }
     emit(rec)
 
@@ -396,6 +455,7 @@ def bench_summaries(args):
         "tflops": round(F / (ms_step / 1e3) / 1e12, 2),
         "pct_peak": round(100 * F / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+        "kernel_symbols": families if not args.no_kernel_times else None,
     }
     emit(rec)
 
@@ -536,6 +596,7 @@ def bench_backward(args):
         "tflops": round(F / (ms_step / 1e3) / 1e12, 2),
         "pct_peak": round(100 * F / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+        "kernel_symbols": families if not args.no_kernel_times else None,
     }
     emit(rec)
 
@@ -641,6 +702,7 @@ def bench_ffn_backward(args):
         "tflops": round(Fl / (ms_step / 1e3) / 1e12, 2),
         "pct_peak": round(100 * Fl / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+        "kernel_symbols": families if not args.no_kernel_times else None,
     }
     emit(rec)
 
@@ -768,6 +830,7 @@ def bench_sublayer_backward(args):
         "tflops": round(Fl / (ms_step / 1e3) / 1e12, 2),
         "pct_peak": round(100 * Fl / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+        "kernel_symbols": families if not args.no_kernel_times else None,
     }
     emit(rec)
 
@@ -868,11 +931,11 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 256 MiB device-to-device copy first, "
                          "as the reference for HBM byte counters")
-    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles",
-                                                      "c3_attention_hbm_traffic.txt"),
+    ap.add_argument("--traffic", default=None,
                     help="profile summary whose RECORD line holds the measured "
                          "HBM bytes per launch of the dominant kernel (written "
-                         "by target_aware_latent_amd.profsum traffic)")
+                         "by target_aware_latent_amd.profsum traffic); by "
+                         "default the c3 records under profiles/")
     ap.add_argument("--workload", default="stack", choices=["stack", "actions", "summaries", "backward", "ffn_backward",
                              "sublayer_backward", "compact"],
                     help="stack: the MLA forward (default); actions: the action "
@@ -1005,15 +1068,31 @@ def main():
             if name in kf:
                 e["tflops"] = kf[name] / (tot / args.steps / 1e3) / 1e12
             kernels[name] = e
-        dom = max((n for n in kt if n in kf), key=lambda n: kt[n][1])
-        cnt, tot = kt[dom]
-        per_launch_flops = kf[dom] * args.steps / cnt
+        # by kernel symbol: every matrix product label runs the one GEMM
+        # kernel template (gemm_kernel, in several tile instances)
+        fam = {}
+        for name, (cnt, tot) in kt.items():
+            if name not in kf:
+                continue
+            f = family_of(name)
+            c0, t0, fl0 = fam.get(f, (0, 0.0, 0.0))
+            fam[f] = (c0 + cnt, t0 + tot, fl0 + kf[name] * args.steps)
+        families = {}
+        fb = family_bytes(cfg, lengths) if cfg.dtype == "bf16" else {}
+        for f, (cnt, tot, fl) in fam.items():
+            tf = fl / (tot / 1e3) / 1e12
+            families[f] = {"launches_per_step": cnt / args.steps,
+                           "ms_per_step": round(tot / args.steps, 4),
+                           "tflops": round(tf, 2), "frac": round(tf / peak, 4)}
+            if f in fb:
+                families[f]["algorithmic_bytes_per_launch"] = round(fb[f] * args.steps / cnt)
+        dom = max(fam, key=lambda f: fam[f][1])
+        cnt, tot, fl = fam[dom]
+        per_launch_flops = fl / cnt
         avg_s = tot / cnt / 1e3
         achieved = per_launch_flops / avg_s / 1e12
-        # the committed traffic record was measured on the c3 workload
-        default_traffic = os.path.join(ROOT, "profiles", "c3_attention_hbm_traffic.txt")
-        traffic = read_traffic(args.traffic, dom) \
-            if (args.traffic != default_traffic or cfg.name == "c3") else None
+        # the committed traffic records were measured on the c3 workload
+        traffic = read_traffic(args.traffic, dom) if (args.traffic or cfg.name == "c3") else None
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                     "peak": peak, "unit": "TFLOP/s",
                     "frac": round(achieved / peak, 4), "traffic": traffic,
@@ -1052,6 +1131,7 @@ def main():
         "tflops_non_absorbed_count": round(Fna / (ms_step / 1e3) / 1e12, 2),
         "wall_s_timed": round(wall, 3),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+        "kernel_symbols": families if not args.no_kernel_times else None,
     }
     if token_build is not None:
         rec["token_build"] = token_build

@@ -116,7 +116,7 @@ def _factor(disp, counter):
     return COPY_BYTES / (kib * 1024.0), kib
 
 
-def traffic(fetch_csv, write_csv, kernel, label, source):
+def traffic(fetch_csv, write_csv, kernel, label, source, launches=None):
     fd = _dispatches(fetch_csv, "FETCH_SIZE")
     wd = _dispatches(write_csv, "WRITE_SIZE")
     ff, fk = _factor(fd, "FETCH_SIZE")
@@ -125,10 +125,14 @@ def traffic(fetch_csv, write_csv, kernel, label, source):
     wsel = [d["v"] for d in wd if kernel in d["name"]]
     if not fsel or not wsel:
         raise SystemExit(f"no dispatch of {kernel}")
-    fetch = sum(fsel) / len(fsel) * 1024.0 * ff
-    write = sum(wsel) / len(wsel) * 1024.0 * wf
+    # per launch: over the dispatches, or over `launches` when one launch
+    # of the timing label takes several dispatches (split-K products)
+    nf = launches or len(fsel)
+    nw = launches or len(wsel)
+    fetch = sum(fsel) / nf * 1024.0 * ff
+    write = sum(wsel) / nw * 1024.0 * wf
     return {"kernel": label, "bytes": round(fetch + write), "fetch_bytes": round(fetch),
-            "write_bytes": round(write), "dispatches": len(fsel),
+            "write_bytes": round(write), "dispatches": len(fsel), "launches": nf,
             "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
             "copy_fetch_kib": fk, "copy_write_kib": wk,
             "fingerprint": fingerprint(source)}
@@ -148,6 +152,8 @@ def main(argv=None):
     b.add_argument("--kernel", required=True)
     b.add_argument("--label", required=True)
     b.add_argument("--source", required=True)
+    b.add_argument("--launches", type=int, default=None,
+                   help="launches the dispatches make up (default: one each)")
     b.add_argument("--out")
     args = ap.parse_args(argv)
     if args.cmd == "stats":
@@ -156,7 +162,8 @@ def main(argv=None):
         for line in counters(args.csv, args.kernel):
             print(json.dumps(line))
     else:
-        rec = traffic(args.fetch, args.write, args.kernel, args.label, args.source)
+        rec = traffic(args.fetch, args.write, args.kernel, args.label, args.source,
+                      args.launches)
         text = json.dumps(rec)
         if args.out:
             with open(args.out, "w") as f:

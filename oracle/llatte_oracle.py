@@ -52,7 +52,7 @@ __all__ = [
     "compact", "history_query_mask", "mla_layer", "fuse_queries", "forward",
     "token_embed", "latent_attention", "unmasked_pairs", "flop_count",
     "lora_mlp_summaries", "latent_attention_backward", "ffn_block_backward",
-    "rmsnorm_backward", "attention_sublayer_backward",
+    "rmsnorm_backward", "attention_sublayer_backward", "forward_backward",
 ]
 
 
@@ -179,13 +179,14 @@ def _split_heads(x, h):
     return x.reshape(M, h, -1)
 
 
-def mla_layer(Rh, Rc, n, W, cfg, absorbed=False, return_probs=False):
+def mla_layer(Rh, Rc, n, W, cfg, absorbed=False, return_probs=False, return_r1=False):
     """One transformer layer with MLA on one user.
 
     Rh: the K history rows entering the layer (oldest first); Rc: the n_c
     candidate/seed rows; n: history rows kept as queries (0 <= n <= K).
     Returns (Rh_out [n, d], Rc_out [n_c, d]) and, on request, the attention
-    probabilities [h, n+n_c, K].
+    probabilities [h, n+n_c, K] and then R1, the rows after the attention
+    sublayer ([n+n_c, d]: query history rows, then candidates).
 
     [LLaTTE] A.3 non-absorbed MLA: C = RMSNorm(H W_down^KV) (the latent),
     K, V = split(C W_up^KV), attention softmax(Q K^T / sqrt(d_k)) V W_out.
@@ -247,7 +248,8 @@ def mla_layer(Rh, Rc, n, W, cfg, absorbed=False, return_probs=False):
         R1 = rmsnorm(Rq + A, W["g1"], eps)
         R2 = rmsnorm(R1 + gelu(R1 @ W["W1"]) @ W["W2"], W["g2"], eps)
     out = (R2[:n], R2[n:])
-    return (out, probs) if return_probs else out
+    extra = ((probs,) if return_probs else ()) + ((R1,) if return_r1 else ())
+    return (out,) + extra if extra else out
 
 
 # ---------------------------------------------------------------- the stack
@@ -561,6 +563,112 @@ def attention_sublayer_backward(Rh, Rc, n, W, cfg, dRq):
     dRh[K - n:] += dRq[:n]
     dRc = dRc + dRq[n:]
     return dRh, dRc, g
+
+
+def forward_backward(cfg, W, hist, offsets, cand=None, ctx=None, d_hist=None,
+                     d_cand=None, d_emb=None):
+    """Gradients of L = sum <d_hist, out_hist> + <d_cand, out_cand> +
+    <d_emb, emb> through the whole forward above (pre-norm layers, full-rank
+    queries), for every user.
+
+    [LLaTTE] trains the sequence module end to end (section 1.5.1); this is
+    the chain rule through section 1.3.2's steps, using the sublayer
+    derivatives above ([LLaTTE] A.2 layer equation, A.3 MLA):
+      readout: emb = flatten(S) W_p, so dS = (d_emb W_p^T) reshaped and
+        dW_p = flatten(S)^T d_emb; the readout layer is a layer with n = 0
+        whose candidate rows are the seeds: its input-row gradients go to
+        the last layer's history outputs and (summed over users) the seeds;
+      layer l (last to first): the output rows are the layer's query rows
+        (last n_l history rows, then candidates); the FFN sublayer's
+        backward gives dR1, the attention sublayer's backward the gradients
+        of all K_l input rows and of the candidates. Layer l's input rows
+        are layer l-1's output rows (the pyramid keeps the last rows), so
+        they are layer l-1's output gradients; rows trimmed by the pyramid
+        get only the key/value terms of the layer that saw them last;
+      fusion: Q0 = [x ; c] W_q, so dW_q = [x ; c]^T dQ0 and d[x ; c] =
+        dQ0 W_q^T (the context part summed over the user's candidates).
+    d_hist: per-user list of [n_N(u), d] (None = zeros); d_cand [B*n_q, d];
+    d_emb [B, d_out] (or [B, n_seeds*d] without W_p). Returns a dict: 'layers'
+    (per layer: g1, W_dkv, g_c, W_uq, W_uk, W_uv, W_o, g2, W1, W2), and,
+    where present, 'readout', 'seeds', 'W_p', 'W_q', then 'hist'
+    [total_rows, d], 'cand' [B*n_q, d], 'ctx' [B, d_c].
+    """
+    if cfg.norm_mode != "pre":
+        raise ValueError("the backward follows the pre-norm layer")
+    offsets = np.asarray(offsets, dtype=np.int64)
+    lengths = offsets[1:] - offsets[:-1]
+    B = lengths.size
+    keep = pyramid_counts(cfg.pyramid, lengths, cfg.N)
+    f64 = lambda a: None if a is None else np.asarray(a, dtype=np.float64)
+    layers = [{k: f64(v) for k, v in lw.items()} for lw in W["layers"]]
+    if any("W_dq" in lw for lw in layers):
+        raise ValueError("the backward follows the full-rank query path")
+    ro = {k: f64(v) for k, v in W["readout"].items()} if cfg.n_seeds > 0 else None
+    W_q = f64(W.get("W_q"))
+    W_p = f64(W.get("W_p")) if cfg.n_seeds > 0 else None
+    seeds = f64(W.get("seeds"))
+    keys = ("g1", "W_dkv", "g_c", "W_uq", "W_uk", "W_uv", "W_o", "g2", "W1", "W2")
+    zeros_like = lambda lw: {k: np.zeros_like(lw[k]) for k in keys if k in lw}
+    g_layers = [zeros_like(lw) for lw in layers]
+    res = {"layers": g_layers, "hist": np.zeros((int(offsets[-1]), cfg.d)),
+           "cand": np.zeros((B * cfg.n_q, cfg.d)), "ctx": np.zeros((B, cfg.d_c))}
+    if ro is not None:
+        res["readout"] = zeros_like(ro)
+        res["seeds"] = np.zeros_like(seeds)
+        if W_p is not None:
+            res["W_p"] = np.zeros_like(W_p)
+    if cfg.n_q > 0:
+        res["W_q"] = np.zeros_like(W_q)
+
+    def layer_backward(Rh, Rc, n, lw, gw, dR2):
+        R1 = mla_layer(Rh, Rc, n, lw, cfg, return_r1=True)[1]
+        dR1, dg2, dW1, dW2 = ffn_block_backward(R1, lw["g2"], lw["W1"], lw["W2"], dR2, cfg.eps)
+        dRh, dRc, g = attention_sublayer_backward(Rh, Rc, n, lw, cfg, dR1)
+        g.update(g2=dg2, W1=dW1, W2=dW2)
+        for k, v in g.items():
+            gw[k] += v
+        return dRh, dRc
+
+    for u in range(B):
+        Rh = f64(hist[offsets[u]:offsets[u + 1]])
+        xc = None
+        if cfg.n_q > 0:
+            xu = f64(cand[u * cfg.n_q:(u + 1) * cfg.n_q])
+            cu = f64(ctx[u]) if (ctx is not None and cfg.d_c > 0) else None
+            xc = xu if cu is None else np.concatenate(
+                [xu, np.broadcast_to(cu, (cfg.n_q, cu.size))], axis=1)
+            Rc = xc @ W_q
+        else:
+            Rc = np.zeros((0, cfg.d))
+        ins = []
+        for l in range(cfg.N):
+            n = int(keep[l, u])
+            ins.append((Rh, Rc, n))
+            Rh, Rc = mla_layer(Rh, Rc, n, layers[l], cfg)
+        dRh = np.zeros_like(Rh) if d_hist is None else f64(d_hist[u]).copy()
+        dRc = (np.zeros((cfg.n_q, cfg.d)) if d_cand is None
+               else f64(d_cand[u * cfg.n_q:(u + 1) * cfg.n_q]).copy())
+        if ro is not None:
+            _, S = mla_layer(Rh, seeds, 0, ro, cfg)
+            de = np.zeros(S.size) if d_emb is None else f64(d_emb[u])
+            if W_p is not None:
+                res["W_p"] += np.outer(S.reshape(-1), de)
+                de = W_p @ de
+            dRh_ro, dS = layer_backward(Rh, seeds, 0, ro, res["readout"], de.reshape(S.shape))
+            dRh = dRh + dRh_ro
+            res["seeds"] += dS
+        for l in range(cfg.N - 1, -1, -1):
+            Rh_in, Rc_in, n = ins[l]
+            dRh, dRc = layer_backward(Rh_in, Rc_in, n, layers[l], g_layers[l],
+                                      np.concatenate([dRh, dRc], axis=0))
+        res["hist"][offsets[u]:offsets[u + 1]] = dRh
+        if cfg.n_q > 0:
+            res["W_q"] += xc.T @ dRc
+            dxc = dRc @ W_q.T
+            res["cand"][u * cfg.n_q:(u + 1) * cfg.n_q] = dxc[:, :cfg.d]
+            if cfg.d_c > 0:
+                res["ctx"][u] = dxc[:, cfg.d:].sum(axis=0)
+    return res
 
 
 def unmasked_pairs(cfg, lengths):

@@ -478,6 +478,98 @@ size_t llatte_mla_attention_workspace_size(const llatte_attn_desc* a,
                                            int32_t Ktot);
 
 /* ------------------------------------------------------------------------
+ * llatte_mla_backward -- the training backward of the whole sequence module
+ * of llatte_mla_forward (fusion, N layers with the pyramidal schedule, the
+ * readout; [LLaTTE] 1.3.2, trained end to end as in 1.5.1): given the
+ * gradients of a loss with respect to the forward's outputs, it writes the
+ * gradients with respect to every weight and to the inputs. The forward
+ * runs again on the same kernels as llatte_mla_forward, keeping each
+ * layer's output rows and its rows after the attention sublayer (R1); then
+ * the layers are walked back with llatte_ffn_backward and
+ * llatte_attn_sublayer_backward ([LLaTTE] A.2 layer equation, pre-norm
+ * reading; A.3 MLA):
+ *   - layer l's output rows are its query rows (the candidates, then the
+ *     last n_l(u) history rows of each user, oldest first); their gradient
+ *     gives the gradient of all of layer l's input rows, which are layer
+ *     l-1's output rows (the pyramid keeps the most recent rows), so rows
+ *     that layer l does not keep get only its key/value terms;
+ *   - the readout layer (queries = the seeds, keys = the last layer's
+ *     history outputs, n = 0) adds its key gradient to the last layer's
+ *     history output gradient; the seeds' gradient is summed over users;
+ *     emb = flatten(Z) W_p gives dZ = d_emb W_p^T and dW_p = flatten(Z)^T
+ *     d_emb (with LLATTE_FLAG_RAW_READOUT dZ = d_emb);
+ *   - the fusion Q0 = [x ; c] W_q gives dW_q = [x ; c]^T dQ0 and
+ *     d[x ; c] = dQ0 W_q^T, the context part summed over each user's
+ *     candidates.
+ * Products take bf16 operands with fp32 accumulation; gradients are fp32.
+ *   desc               as llatte_mla_forward; supported: dtype BF16,
+ *                      norm_mode PRE, q_rank 0, rank 64 or 128, d_out a
+ *                      multiple of 8 (W_p readout); flags 0 or
+ *                      LLATTE_FLAG_RAW_READOUT
+ *   w                  host pointer to the device weights (raw layout, as
+ *                      llatte_mla_forward's w; packed weights are not
+ *                      accepted: the backward reads the raw matrices)
+ *   hist_values, hist_offsets, B, total_rows, max_len, cand_x, ctx
+ *                      as llatte_mla_forward
+ *   hist_offsets_host  host copy of hist_offsets (B+1): the per-layer row
+ *                      counts are sized on the host
+ *   d_out_cand         [B*n_q, d] float32 (NULL iff n_q == 0): dL/d out_cand
+ *   d_out_hist         rows of out_hist, float32, or NULL (zero)
+ *   d_out_emb          [B, d_out] float32 (NULL iff n_seeds == 0); with
+ *                      LLATTE_FLAG_RAW_READOUT [B, n_seeds*d]
+ *   g                  host pointer to the gradients (device float32,
+ *                      each laid out as its weight, overwritten): layers
+ *                      (host array of n_layers), W_q (n_q > 0), seeds,
+ *                      readout and W_p (n_seeds > 0; W_p not with
+ *                      LLATTE_FLAG_RAW_READOUT); g_c is not written with
+ *                      latent_norm = 0
+ *   d_hist             [total_rows, d] float32, overwritten
+ *   d_cand_x           [B*n_q, d] float32 (NULL iff n_q == 0), overwritten
+ *   d_ctx              [B, d_ctx] float32 (NULL iff d_ctx == 0 or n_q == 0)
+ *   workspace          >= llatte_mla_backward_workspace_size(...) bytes,
+ *                      256-byte aligned
+ * Errors: LLATTE_ERR_UNSUPPORTED outside the supported set above;
+ * LLATTE_ERR_INVALID_ARG for NULL or misaligned pointers, bad sizes or host
+ * offsets that disagree with total_rows / max_len; LLATTE_ERR_WORKSPACE;
+ * LLATTE_ERR_HIP. Nothing is enqueued on an argument error.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  float* g1;
+  float* W_dkv;
+  float* g_c;
+  float* W_uq;
+  float* W_uk;
+  float* W_uv;
+  float* W_o;
+  float* g2;
+  float* W1;
+  float* W2;
+} llatte_layer_grads;
+
+typedef struct {
+  const llatte_layer_grads* layers;  /* HOST array of n_layers */
+  float* W_q;
+  float* seeds;
+  llatte_layer_grads readout;
+  float* W_p;
+} llatte_grads;
+
+llatte_status llatte_mla_backward(
+    const llatte_model_desc* desc, const llatte_weights* w,
+    const float* hist_values, const int32_t* hist_offsets,
+    const int32_t* hist_offsets_host, int32_t B, int32_t total_rows,
+    int32_t max_len, const float* cand_x, const float* ctx,
+    const float* d_out_cand, const float* d_out_hist, const float* d_out_emb,
+    const llatte_grads* g, float* d_hist, float* d_cand_x, float* d_ctx,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of llatte_mla_backward (host only; 0 if the descriptor is
+ * invalid or outside the supported set). */
+size_t llatte_mla_backward_workspace_size(const llatte_model_desc* desc,
+                                          int32_t B, int32_t total_rows,
+                                          int32_t max_len);
+
+/* ------------------------------------------------------------------------
  * llatte_pyramid_compact -- keep the last keep[u] rows of every user's
  * segment, in order ([LLaTTE] A.2: the next layer works on
  * X[:, -T_{l+1}:, :]).

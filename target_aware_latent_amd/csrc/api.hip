@@ -114,10 +114,11 @@ static PlanBase carve_plan(Arena& ar, int n_plans, int B, int qcap, int icap) {
   pb.B = B;
   pb.qcap = qcap;
   pb.icap = icap;
+  pb.ostride = PlanBase::offsets_stride(B);
   pb.kv_len = ar.take<int>((size_t)n_plans * B);
   pb.keep = ar.take<int>((size_t)n_plans * B);
-  pb.kv_off = ar.take<int>((size_t)n_plans * (B + 1));
-  pb.hq_off = ar.take<int>((size_t)n_plans * (B + 1));
+  pb.kv_off = ar.take<int>((size_t)n_plans * pb.ostride);
+  pb.hq_off = ar.take<int>((size_t)n_plans * pb.ostride);
   pb.counts = ar.take<int>((size_t)n_plans * 4);
   pb.qmap = ar.take<int>((size_t)n_plans * qcap);
   pb.qinfo = ar.take<int2>((size_t)n_plans * qcap);
@@ -1827,6 +1828,325 @@ llatte_status llatte_ffn_backward(const llatte_ffn_desc* f, const float* r1, con
   p.F = f->d_ff;
   p.eps = f->eps;
   HIP_TRY(ffn_backward(p, workspace, (hipStream_t)stream));
+  return LLATTE_OK;
+}
+
+}  // extern "C"
+
+namespace llatte {
+
+// ------------------------------------------------------------------ stack backward
+// Workspace of llatte_mla_backward: the forward's own, then every plan's
+// output rows and R1 rows (kept from the forward), two output-row gradient
+// buffers, the readout / fusion temporaries and one region that the
+// sublayer backward calls share (they run one after the other on the stream).
+struct StackBwdWS {
+  FwdWS fw;
+  std::vector<float*> Rout, R1;  // per plan: [UBM, d] in the layer's query-row order
+  float* gA = nullptr;           // [max rows of a layer's row space, d]
+  float* gB = nullptr;
+  float* dR1 = nullptr;          // [max UBM, d]
+  bf16* demb_b = nullptr;        // [B, d_out]
+  bf16* E = nullptr;             // [B*ns, d] the readout rows as bf16
+  float* dS = nullptr;           // [B*ns, d]
+  bf16* dq0_b = nullptr;         // [B*nq, d]
+  float* dxc = nullptr;          // [B*nq, d+dc]
+  char* sub = nullptr;
+  size_t sub_bytes = 0;
+};
+
+static llatte_attn_sublayer_desc stack_sub_desc(const Shapes& S, int n_cand) {
+  llatte_attn_sublayer_desc D;
+  D.d = S.d;
+  D.n_heads = S.h;
+  D.head_dim = S.dk;
+  D.rank = S.r;
+  D.n_cand = n_cand;
+  D.dtype = LLATTE_BF16;
+  D.latent_norm = S.lnorm ? 1 : 0;
+  D.eps = S.eps;
+  return D;
+}
+
+static const char* stack_bwd_unsupported(const Shapes& S) {
+  if (!S.bf16) return "the stack backward is BF16 only";
+  if (!S.pre) return "the stack backward follows the pre-norm layer";
+  if (S.rq) return "the stack backward follows the full-rank query path (q_rank = 0)";
+  if (S.r != 64 && S.r != 128) return "the stack backward needs rank 64 or 128";
+  if (S.validate || S.dump) return "the stack backward takes no VALIDATE or DEBUG_DUMP flag";
+  if (S.ns > 0 && !S.raw && S.dout % 8) return "the stack backward needs d_out a multiple of 8";
+  return nullptr;
+}
+
+static size_t layout_stack_bwd(const Shapes& S, void* base, StackBwdWS* b) {
+  const size_t fwd = (layout_forward(S, base, &b->fw) + 255) & ~(size_t)255;
+  Arena ar(base ? (char*)base + fwd : nullptr);
+  b->Rout.assign(S.NP, nullptr);
+  b->R1.assign(S.NP, nullptr);
+  long long maxM = 1, maxG = 1;
+  size_t sub = 0;
+  const llatte_ffn_desc fd{S.d, S.dff, LLATTE_BF16, S.eps};
+  for (int l = 0; l < S.NP; ++l) {
+    const int nql = l < S.N ? S.nq : S.ns;
+    b->Rout[l] = ar.take<float>((size_t)S.UBM[l] * S.d);
+    b->R1[l] = ar.take<float>((size_t)S.UBM[l] * S.d);
+    maxM = std::max(maxM, S.UBM[l]);
+    maxG = std::max(maxG, S.UBrows[l]);
+    const llatte_attn_sublayer_desc D = stack_sub_desc(S, nql);
+    sub = std::max(sub, llatte_attn_sublayer_backward_workspace_size(&D, S.B, (int)S.UBM[l],
+                                                                     (int)S.UBK[l]));
+    sub = std::max(sub, llatte_ffn_backward_workspace_size(&fd, (int)S.UBM[l]));
+  }
+  b->gA = ar.take<float>((size_t)maxG * S.d);
+  b->gB = ar.take<float>((size_t)maxG * S.d);
+  b->dR1 = ar.take<float>((size_t)maxM * S.d);
+  const size_t nq_rows = (size_t)S.B * S.nq, ns_rows = (size_t)S.B * S.ns;
+  if (S.ns) {
+    b->demb_b = ar.take<bf16>((size_t)S.B * std::max(S.dout, 1));
+    b->E = ar.take<bf16>(ns_rows * S.d);
+    b->dS = ar.take<float>(ns_rows * S.d);
+  }
+  if (S.nq) {
+    b->dq0_b = ar.take<bf16>(nq_rows * S.d);
+    b->dxc = ar.take<float>(nq_rows * (S.d + S.dc));
+  }
+  b->sub = ar.take<char>(sub);
+  b->sub_bytes = sub;
+  return fwd + ar.off + 256;
+}
+
+}  // namespace llatte
+
+extern "C" {
+
+size_t llatte_mla_backward_workspace_size(const llatte_model_desc* desc, int32_t B,
+                                          int32_t total_rows, int32_t max_len) {
+  Shapes S;
+  if (make_shapes(desc, B, total_rows, max_len, &S) != LLATTE_OK || stack_bwd_unsupported(S))
+    return 0;
+  StackBwdWS b;
+  return layout_stack_bwd(S, nullptr, &b);
+}
+
+llatte_status llatte_mla_backward(
+    const llatte_model_desc* desc, const llatte_weights* wts, const float* hist_values,
+    const int32_t* hist_offsets, const int32_t* hist_offsets_host, int32_t B, int32_t total_rows,
+    int32_t max_len, const float* cand_x, const float* ctx, const float* d_out_cand,
+    const float* d_out_hist, const float* d_out_emb, const llatte_grads* g, float* d_hist,
+    float* d_cand_x, float* d_ctx, void* workspace, size_t workspace_bytes, void* stream) {
+  Shapes S;
+  llatte_status st = make_shapes(desc, B, total_rows, max_len, &S);
+  if (st) return st;
+  if (const char* why = stack_bwd_unsupported(S)) return fail(LLATTE_ERR_UNSUPPORTED, "%s", why);
+  if ((st = check_weights(S, wts))) return st;
+  if (!g || !g->layers) return fail(LLATTE_ERR_INVALID_ARG, "gradients are NULL");
+  if (!hist_values || !hist_offsets || !hist_offsets_host || !d_hist || !workspace)
+    return fail(LLATTE_ERR_INVALID_ARG, "hist_values, hist_offsets, hist_offsets_host, d_hist and "
+                                        "workspace must be given");
+  const bool cand = S.nq > 0, ctxp = S.nq > 0 && S.dc > 0, ro = S.ns > 0;
+  if (cand && (!cand_x || !d_out_cand || !d_cand_x || !g->W_q))
+    return fail(LLATTE_ERR_INVALID_ARG, "n_q > 0 needs cand_x, d_out_cand, d_cand_x and g->W_q");
+  if (ctxp && (!ctx || !d_ctx)) return fail(LLATTE_ERR_INVALID_ARG, "d_ctx > 0 needs ctx and d_ctx");
+  if (ro && (!d_out_emb || !g->seeds || (!S.raw && !g->W_p)))
+    return fail(LLATTE_ERR_INVALID_ARG, "the readout needs d_out_emb, g->seeds and g->W_p");
+  std::vector<const void*> ptrs = {hist_values, d_hist, workspace, cand_x, ctx, d_out_cand,
+                                   d_out_hist, d_out_emb, d_cand_x, d_ctx, g->W_q, g->seeds,
+                                   g->W_p};
+  auto layer_ptrs = [&](const llatte_layer_grads& G, const char* what) -> llatte_status {
+    const float* need[] = {G.g1, G.W_dkv, S.lnorm ? G.g_c : G.g1, G.W_uq, G.W_uk, G.W_uv,
+                           G.W_o, G.g2, G.W1, G.W2};
+    for (const float* p : need)
+      if (!p) return fail(LLATTE_ERR_INVALID_ARG, "NULL gradient pointer (%s)", what);
+    ptrs.insert(ptrs.end(), std::begin(need), std::end(need));
+    return LLATTE_OK;
+  };
+  for (int l = 0; l < S.N; ++l)
+    if ((st = layer_ptrs(g->layers[l], "layer"))) return st;
+  if (ro && (st = layer_ptrs(g->readout, "readout"))) return st;
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(LLATTE_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  // per-plan row totals from the host offsets
+  if (hist_offsets_host[0] != 0 || hist_offsets_host[B] != total_rows)
+    return fail(LLATTE_ERR_INVALID_ARG, "hist_offsets_host must start at 0 and end at total_rows");
+  std::vector<int> len(B);
+  for (int u = 0; u < B; ++u) {
+    len[u] = hist_offsets_host[u + 1] - hist_offsets_host[u];
+    if (len[u] < 1 || len[u] > max_len)
+      return fail(LLATTE_ERR_INVALID_ARG, "user %d: history length %d outside [1, max_len]", u, len[u]);
+  }
+  std::vector<int> keep((size_t)S.N * B);
+  if ((st = llatte_pyramid_counts_host(&desc->pyramid, S.N, len.data(), B, keep.data()))) return st;
+  std::vector<long long> Ksum(S.NP, 0), nsum(S.NP, 0);
+  std::vector<int> maxK(S.NP, 1);
+  for (int l = 0; l < S.NP; ++l)
+    for (int u = 0; u < B; ++u) {
+      const int K = l == 0 ? len[u] : keep[(size_t)(l - 1) * B + u];
+      const int n = l < S.N ? keep[(size_t)l * B + u] : 0;
+      Ksum[l] += K;
+      nsum[l] += n;
+      maxK[l] = std::max(maxK[l], K);
+    }
+  StackBwdWS b;
+  const size_t need = layout_stack_bwd(S, nullptr, &b);
+  if (workspace_bytes < need)
+    return fail(LLATTE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  layout_stack_bwd(S, workspace, &b);
+  hipStream_t s = (hipStream_t)stream;
+  FwdWS& w = b.fw;
+  const int d = S.d;
+  const long long nc = (long long)B * S.nq;
+
+  // ---- the forward again, keeping each layer's output rows and R1
+  const Packed PK = w.pk;
+  HIP_TRY(pack_all(S, wts, PK, s));
+  HIP_TRY(build_plan(hist_offsets, B, S.rule, S.nq, S.ns, w.plan, S.NP, S.bq, kAttnBN, s));
+  if (cand) {
+    HIP_TRY(concat_queries(cand_x, ctx, B, S.nq, d, S.dc, w.XC, true, s));
+    GemmParams gp;
+    gp.name = "gemm_fusion";
+    with_sk(gp, w.sk_part);
+    gp.A = w.XC;
+    gp.lda = d + S.dc;
+    gp.B = PK.WqT;
+    gp.ldb = d + S.dc;
+    gp.M_cap = (int)nc;
+    gp.N = d;
+    gp.K = d + S.dc;
+    gp.epi = EPI_STORE_F32;
+    gp.C = w.Q0;
+    gp.ldc = d;
+    HIP_TRY(gemm(gp, true, s));
+  }
+  LayerIO io;
+  for (int l = 0; l < S.N; ++l) {
+    const RowSrc src = l == 0 ? RowSrc{w.Q0, hist_values, (int)nc, d}
+                              : RowSrc{b.Rout[l - 1], b.Rout[l - 1] + nc * d, (int)nc, d};
+    FwdWS wl = w;
+    wl.R1 = b.R1[l];
+    io.next = S.fnorm && l + 1 < S.N;
+    HIP_TRY(run_layer(S, wl, l, PK.L[l], src, b.Rout[l], io, s));
+    io.in_ready = io.next;
+    io.np_in = io.np_out;
+  }
+  const float* last_hist = b.Rout[S.N - 1] + nc * d;
+  if (ro) {
+    HIP_TRY(broadcast_rows(PK.seeds, S.ns, d, B, w.S, s));
+    FwdWS wl = w;
+    wl.R1 = b.R1[S.N];
+    LayerIO rio;
+    HIP_TRY(run_layer(S, wl, S.N, PK.L[S.N], RowSrc{w.S, last_hist, B * S.ns, d}, b.Rout[S.N],
+                      rio, s));
+  }
+
+  // ---- back through the stack
+  const llatte_ffn_desc fd{d, S.dff, LLATTE_BF16, S.eps};
+  auto layer_backward = [&](int l, const llatte_layer_weights& L, const llatte_layer_grads& G,
+                            int n_cand, const float* r_kv, const float* r_c, const float* dout,
+                            float* d_kv, float* d_c) -> llatte_status {
+    const long long M = (long long)B * n_cand + nsum[l];
+    llatte_status e = llatte_ffn_backward(&fd, b.R1[l], L.g2, L.W1, L.W2, dout, (int)M, b.dR1,
+                                          G.g2, G.W1, G.W2, b.sub, b.sub_bytes, s);
+    if (e) return e;
+    const llatte_attn_sublayer_desc D = stack_sub_desc(S, n_cand);
+    const llatte_attn_sublayer_weights W{L.g1, L.W_dkv, L.g_c, L.W_uq, L.W_uk, L.W_uv, L.W_o};
+    const llatte_attn_sublayer_grads Gs{G.g1, G.W_dkv, G.g_c, G.W_uq, G.W_uk, G.W_uv, G.W_o};
+    const LayerPlan P = w.plan.layer(l);
+    return llatte_attn_sublayer_backward(&D, &W, r_kv, n_cand ? r_c : nullptr, P.kv_off, P.hq_off,
+                                         B, (int)M, (int)Ksum[l], maxK[l], b.dR1, d_kv,
+                                         n_cand ? d_c : nullptr, &Gs, b.sub, b.sub_bytes, s);
+  };
+  auto wgrad_call = [&](const bf16* X, int n1, const bf16* Y, int n2, long long rows, float* C,
+                        const char* name) {
+    WgradParams p;
+    p.X = X;
+    p.ldx = n1;
+    p.Y = Y;
+    p.ldy = n2;
+    p.M = rows;
+    p.N1 = n1;
+    p.N2 = n2;
+    p.C = C;
+    p.ldc = n2;
+    p.part = w.sk_part;
+    p.part_cap = kSkPart;
+    p.name = name;
+    return wgrad(p, s);
+  };
+  float* cur = b.gA;  // gradient of the current layer's output rows
+  float* nxt = b.gB;
+  const long long nh_last = nsum[S.N - 1];
+  if (ro) {
+    // dZ: the readout rows' gradient
+    const long long nsr = (long long)B * S.ns;
+    const float* dZ = d_out_emb;
+    if (!S.raw) {
+      HIP_TRY(cast_f32(d_out_emb, b.demb_b, (long long)B * S.dout, true, s));
+      GemmParams gp;
+      gp.name = "gemm_bwd_readout";
+      with_sk(gp, w.sk_part);
+      gp.A = b.demb_b;
+      gp.lda = S.dout;
+      gp.B = wts->W_p;  // [ns*d, d_out] row-major: its rows are the products' columns
+      gp.ldb = S.dout;
+      gp.M_cap = B;
+      gp.N = S.ns * d;
+      gp.K = S.dout;
+      gp.epi = EPI_STORE_F32;
+      gp.C = b.dS;
+      gp.ldc = S.ns * d;
+      HIP_TRY(gemm(gp, true, s));
+      HIP_TRY(cast_f32(b.Rout[S.N], b.E, nsr * d, true, s));
+      HIP_TRY(wgrad_call(b.E, S.ns * d, b.demb_b, S.dout, B, g->W_p, "wgrad_readout"));
+      dZ = b.dS;
+    }
+    // the readout layer: keys = the last layer's history outputs, queries =
+    // the seeds; its key gradient is the last layer's history output
+    // gradient (plus d_out_hist), the seed rows' gradient sums into the seeds
+    if ((st = layer_backward(S.N, wts->readout, g->readout, S.ns, last_hist, w.S, dZ,
+                             cur + nc * d, nxt)))
+      return st;
+    HIP_TRY(group_sum_rows(nxt, d, 0, S.ns, 1, B, S.ns, d, g->seeds, s));
+    if (d_out_hist) HIP_TRY(add_f32(cur + nc * d, d_out_hist, nh_last * d, s));
+  } else if (d_out_hist) {
+    HIP_TRY(hipMemcpyAsync(cur + nc * d, d_out_hist, (size_t)nh_last * d * sizeof(float),
+                           hipMemcpyDeviceToDevice, s));
+  } else {
+    HIP_TRY(zero_f32(cur + nc * d, nh_last * d, s));
+  }
+  if (cand)
+    HIP_TRY(hipMemcpyAsync(cur, d_out_cand, (size_t)nc * d * sizeof(float),
+                           hipMemcpyDeviceToDevice, s));
+  for (int l = S.N - 1; l >= 0; --l) {
+    // layer l's input rows are layer l-1's output rows: candidates, then
+    // the history rows user by user
+    const float* r_kv = l == 0 ? hist_values : b.Rout[l - 1] + nc * d;
+    const float* r_c = l == 0 ? w.Q0 : b.Rout[l - 1];
+    if ((st = layer_backward(l, wts->layers[l], g->layers[l], S.nq, r_kv, r_c, cur,
+                             l == 0 ? d_hist : nxt + nc * d, nxt)))
+      return st;
+    std::swap(cur, nxt);
+  }
+  if (cand) {
+    // Q0 = [x ; c] W_q: cur holds dQ0
+    HIP_TRY(cast_f32(cur, b.dq0_b, nc * d, true, s));
+    HIP_TRY(wgrad_call((const bf16*)w.XC, d + S.dc, b.dq0_b, d, nc, g->W_q, "wgrad_fusion"));
+    GemmParams gp;
+    gp.name = "gemm_bwd_fusion";
+    with_sk(gp, w.sk_part);
+    gp.A = b.dq0_b;
+    gp.lda = d;
+    gp.B = wts->W_q;  // [d+dc, d] row-major
+    gp.ldb = d;
+    gp.M_cap = (int)nc;
+    gp.N = d + S.dc;
+    gp.K = d;
+    gp.epi = EPI_STORE_F32;
+    gp.C = b.dxc;
+    gp.ldc = d + S.dc;
+    HIP_TRY(gemm(gp, true, s));
+    HIP_TRY(copy_rows_f32(b.dxc, d + S.dc, d_cand_x, (int)nc, nullptr, d, s));
+    if (ctxp) HIP_TRY(group_sum_rows(b.dxc, d + S.dc, d, B, S.nq, S.nq, 1, S.dc, d_ctx, s));
+  }
   return LLATTE_OK;
 }
 

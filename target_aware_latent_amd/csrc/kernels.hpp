@@ -171,6 +171,13 @@ hipError_t broadcast_rows(const float* seeds, int n_s, int d, int B,
 hipError_t copy_rows_f32(const float* src, int ld, float* dst, int count_cap,
                          const int* count_dev, int d, hipStream_t s);
 
+// out [na, width] (float): out[a][c] = sum over b < nb of
+// src[(a sa + b sb) ld + col0 + c], added in increasing b.
+hipError_t group_sum_rows(const float* src, int ld, int col0, int na, int sa, int nb, int sb,
+                          int width, float* out, hipStream_t s);
+// dst[i] += src[i], i < n (float).
+hipError_t add_f32(float* dst, const float* src, long long n, hipStream_t s);
+
 // ------------------------------------------------------------------ plan
 // Per-layer device plan built from the history offsets.
 struct LayerPlan {
@@ -189,20 +196,22 @@ struct LayerPlan {
 struct PlanBase {
   int* kv_len;   // [n_plans][B]
   int* keep;     // [n_plans][B]
-  int* kv_off;   // [n_plans][B+1]
-  int* hq_off;   // [n_plans][B+1]
+  int* kv_off;   // [n_plans][ostride]: B+1 offsets, rows 16-byte aligned
+  int* hq_off;   // [n_plans][ostride]
   int* counts;   // [n_plans][4]
   int* qmap;     // [n_plans][qcap]
   int2* qinfo;   // [n_plans][qcap]
   i32x4* items;  // [n_plans][icap]
   int* n_items;  // [n_plans]
   int B, qcap, icap;
+  int ostride;   // B+1 rounded up to a multiple of 4
+  __host__ __device__ static int offsets_stride(int B) { return (B + 4) & ~3; }
   __host__ __device__ LayerPlan layer(int l) const {
     LayerPlan p;
     p.kv_len = kv_len + (size_t)l * B;
     p.keep = keep + (size_t)l * B;
-    p.kv_off = kv_off + (size_t)l * (B + 1);
-    p.hq_off = hq_off + (size_t)l * (B + 1);
+    p.kv_off = kv_off + (size_t)l * ostride;
+    p.hq_off = hq_off + (size_t)l * ostride;
     p.counts = counts + (size_t)l * 4;
     p.qmap = qmap + (size_t)l * qcap;
     p.qinfo = qinfo + (size_t)l * qcap;
@@ -213,7 +222,7 @@ struct PlanBase {
   // bytes of device memory for n_plans layers
   static size_t bytes(int n_plans, int B, int qcap, int icap) {
     size_t n = (size_t)n_plans;
-    return n * (2 * (size_t)B + 2 * ((size_t)B + 1) + 4 + 1) * sizeof(int) +
+    return n * (2 * (size_t)B + 2 * (size_t)offsets_stride(B) + 4 + 1) * sizeof(int) +
            n * (size_t)qcap * (sizeof(int) + sizeof(int2)) +
            n * (size_t)icap * sizeof(i32x4) + 64 * 9;
   }

@@ -200,4 +200,45 @@ hipError_t copy_rows_f32(const float* src, int ld, float* dst, int count_cap,
   return hipGetLastError();
 }
 
+// out[a][c] = sum over b < nb of src[(a sa + b sb) ld + col0 + c], c < width,
+// a < na, b in increasing order (one thread per output element).
+__global__ void group_sum_kernel(const float* src, int ld, int col0, int na, int sa, int nb,
+                                 int sb, int width, float* out) {
+  const long long total = (long long)na * width;
+  for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < total;
+       e += (long long)gridDim.x * blockDim.x) {
+    const long long a = e / width, c = e % width;
+    float t = 0.f;
+    for (int b = 0; b < nb; ++b) t += src[(a * sa + (long long)b * sb) * ld + col0 + c];
+    out[e] = t;
+  }
+}
+
+hipError_t group_sum_rows(const float* src, int ld, int col0, int na, int sa, int nb, int sb,
+                          int width, float* out, hipStream_t s) {
+  const long long total = (long long)na * width;
+  if (total == 0) return hipSuccess;
+  int blocks = (int)std::min<long long>((total + 255) / 256, 65536);
+  timing_begin("group_sum_rows", s);
+  hipLaunchKernelGGL(group_sum_kernel, dim3(blocks), dim3(256), 0, s, src, ld, col0, na, sa, nb,
+                     sb, width, out);
+  timing_end(s);
+  return hipGetLastError();
+}
+
+__global__ void add_kernel(float* dst, const float* src, long long n) {
+  for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < n;
+       e += (long long)gridDim.x * blockDim.x)
+    dst[e] += src[e];
+}
+
+hipError_t add_f32(float* dst, const float* src, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int blocks = (int)std::min<long long>((n + 255) / 256, 65536);
+  timing_begin("add", s);
+  hipLaunchKernelGGL(add_kernel, dim3(blocks), dim3(256), 0, s, dst, src, n);
+  timing_end(s);
+  return hipGetLastError();
+}
+
 }  // namespace llatte

@@ -84,6 +84,16 @@ class llatte_attn_sublayer_grads(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("g1", "w_dkv", "g_c", "w_uq", "w_uk", "w_uv", "w_o")]
 
 
+class llatte_layer_grads(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("g1", "W_dkv", "g_c", "W_uq", "W_uk", "W_uv", "W_o", "g2",
+                                   "W1", "W2")]
+
+
+class llatte_grads(ctypes.Structure):
+    _fields_ = [("layers", ctypes.POINTER(llatte_layer_grads)), ("W_q", _vp), ("seeds", _vp),
+                ("readout", llatte_layer_grads), ("W_p", _vp)]
+
+
 class llatte_action_desc(ctypes.Structure):
     _fields_ = [(n, _c_int) for n in (
         "d", "d_hidden", "d_enc", "d_type", "d_item", "d_surf", "d_time",
@@ -172,6 +182,12 @@ _SIGS = {
         ctypes.POINTER(llatte_attn_sublayer_grads), _vp, ctypes.c_size_t, _vp]),
     "llatte_attn_sublayer_backward_workspace_size": (ctypes.c_size_t, [
         ctypes.POINTER(llatte_attn_sublayer_desc), _c_int, _c_int, _c_int]),
+    "llatte_mla_backward": (_c_int, [
+        ctypes.POINTER(llatte_model_desc), ctypes.POINTER(llatte_weights), _vp, _vp,
+        ctypes.POINTER(_c_int), _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
+        ctypes.POINTER(llatte_grads), _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "llatte_mla_backward_workspace_size": (ctypes.c_size_t, [
+        ctypes.POINTER(llatte_model_desc), _c_int, _c_int, _c_int]),
     "llatte_last_error": (ctypes.c_char_p, []),
     "llatte_version": (_c_int, []),
     "llatte_kernel_timing_enable": (None, [_c_int]),
@@ -413,6 +429,24 @@ def llatte_attn_sublayer_backward(desc, weights, r_kv, r_cand, kv_offsets, hq_of
         B, Mtot, Ktot, max_len, _p(d_out), _p(d_r_kv), _p(d_r_cand), ctypes.byref(g),
         _p(workspace), nbytes, _stream(stream))
     _check(st, "llatte_attn_sublayer_backward")
+
+
+def llatte_mla_backward_workspace_size(desc, B, total_rows, max_len):
+    return lib().llatte_mla_backward_workspace_size(ctypes.byref(desc), B, total_rows, max_len)
+
+
+def llatte_mla_backward(desc, weights, hist_values, hist_offsets, hist_offsets_host, B,
+                        total_rows, max_len, cand_x, ctx, d_out_cand, d_out_hist, d_out_emb,
+                        grads, d_hist, d_cand_x, d_ctx, workspace, stream=None):
+    """grads: an llatte_grads struct; hist_offsets_host: host sequence of B+1 ints."""
+    off = (_c_int * (B + 1))(*[int(x) for x in hist_offsets_host])
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().llatte_mla_backward(
+        ctypes.byref(desc), ctypes.byref(weights), _p(hist_values), _p(hist_offsets), off, B,
+        total_rows, max_len, _p(cand_x), _p(ctx), _p(d_out_cand), _p(d_out_hist), _p(d_out_emb),
+        ctypes.byref(grads), _p(d_hist), _p(d_cand_x), _p(d_ctx), _p(workspace), nbytes,
+        _stream(stream))
+    _check(st, "llatte_mla_backward")
 
 
 def llatte_last_error():

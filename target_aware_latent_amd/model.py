@@ -149,3 +149,61 @@ class DeviceModel:
                              out["cand"], out["hist"], out["hist_offsets"],
                              out["emb"], ws, stream)
         return out
+
+    _GRAD_KEYS = ("g1", "W_dkv", "g_c", "W_uq", "W_uk", "W_uv", "W_o", "g2", "W1", "W2")
+
+    def backward(self, hist, offsets, lengths, cand=None, ctx=None, d_out_cand=None,
+                 d_out_hist=None, d_out_emb=None, stream=None):
+        """llatte_mla_backward: float32 gradient tensors laid out as the
+        weights ({'layers': [dict per layer], 'readout', 'seeds', 'W_q',
+        'W_p'}) and of the inputs ('hist', 'cand', 'ctx')."""
+        cfg, dev = self.cfg, self.device
+        B = len(lengths)
+        total = int(sum(lengths))
+        max_len = int(max(lengths))
+        d, hd, r, F = cfg.d, cfg.h * cfg.dk, cfg.r, 4 * cfg.d
+        shapes = {"g1": (d,), "W_dkv": (d, r), "g_c": (r,), "W_uq": (d, hd), "W_uk": (r, hd),
+                  "W_uv": (r, hd), "W_o": (hd, d), "g2": (d,), "W1": (d, F), "W2": (F, d)}
+        keep = []
+
+        def buf(*shape):
+            t = torch.empty(*shape, device=dev)
+            keep.append(t)
+            return t
+
+        def layer():
+            g = {k: buf(*shapes[k]) for k in self._GRAD_KEYS}
+            st = C.llatte_layer_grads(*[g[k].data_ptr() for k in self._GRAD_KEYS])
+            return g, st
+
+        out = {"layers": []}
+        structs = []
+        for _ in range(cfg.N):
+            g, st = layer()
+            out["layers"].append(g)
+            structs.append(st)
+        arr = (C.llatte_layer_grads * cfg.N)(*structs)
+        G = C.llatte_grads()
+        G.layers = ctypes.cast(arr, ctypes.POINTER(C.llatte_layer_grads))
+        if cfg.n_q > 0:
+            out["W_q"] = buf(d + cfg.d_c, d)
+            G.W_q = out["W_q"].data_ptr()
+        if cfg.n_seeds > 0:
+            out["seeds"] = buf(cfg.n_seeds, d)
+            G.seeds = out["seeds"].data_ptr()
+            out["readout"], G.readout = layer()
+            if not self.raw_readout:
+                out["W_p"] = buf(cfg.n_seeds * d, self.desc.d_out)
+                G.W_p = out["W_p"].data_ptr()
+        out["hist"] = buf(total, d)
+        out["cand"] = buf(B * cfg.n_q, d) if cfg.n_q else None
+        out["ctx"] = buf(B, cfg.d_c) if cfg.n_q and cfg.d_c else None
+        n = C.llatte_mla_backward_workspace_size(self.desc, B, total, max_len)
+        if n == 0:
+            raise C.LlatteError(-1, "llatte_mla_backward_workspace_size")
+        ws = torch.empty(n, dtype=torch.uint8, device=dev)
+        offs = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+        C.llatte_mla_backward(self.desc, self.weights, hist, offsets, offs, B, total, max_len,
+                              cand, ctx, d_out_cand, d_out_hist, d_out_emb, G, out["hist"],
+                              out["cand"], out["ctx"], ws, stream)
+        return out

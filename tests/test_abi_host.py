@@ -285,3 +285,55 @@ def test_action_tokenize_host_validation(L):
                                     fake, fake, fake, fake, fake, fake, fake, 64, None)
     assert st == L.LLATTE_ERR_WORKSPACE
     assert "workspace" in L.llatte_last_error()
+
+
+def test_stack_backward_host_validation(L):
+    """llatte_mla_backward: supported set (BF16, pre-norm, full-rank queries,
+    rank 64 / 128), workspace sizing, and argument errors before any launch."""
+    from target_aware_latent_amd.model import make_desc
+    for name in ("c2", "c3", "c4"):
+        cfg = synth.get_config(name)
+        L_ = cfg.L or cfg.len_range[1]
+        assert L.llatte_mla_backward_workspace_size(make_desc(cfg), cfg.B, cfg.B * L_, L_) > 0
+    cfg = synth.get_config("c2")
+    B, total, max_len = 3, 30, 20
+    for field, val in [("norm_mode", L.LLATTE_NORM_POST), ("dtype", L.LLATTE_F32),
+                       ("q_rank", 64), ("rank", 256), ("flags", L.LLATTE_FLAG_VALIDATE)]:
+        d = make_desc(cfg)
+        setattr(d, field, val)
+        assert L.llatte_mla_backward_workspace_size(d, B, total, max_len) == 0, field
+    d = make_desc(cfg)
+    fake = 0x100000
+    lw = L.llatte_layer_weights(*([fake] * 10 + [None, None]))
+    layers = (L.llatte_layer_weights * cfg.N)(*([lw] * cfg.N))
+    w = L.llatte_weights(ctypes.cast(layers, ctypes.POINTER(L.llatte_layer_weights)), fake, fake,
+                         lw, fake)
+    lg = L.llatte_layer_grads(*([fake] * 10))
+    glayers = (L.llatte_layer_grads * cfg.N)(*([lg] * cfg.N))
+    g = L.llatte_grads(ctypes.cast(glayers, ctypes.POINTER(L.llatte_layer_grads)), fake, fake, lg,
+                       fake)
+    off = (ctypes.c_int * (B + 1))(0, 10, 20, 30)
+    f = ctypes.c_void_p(fake)
+
+    def call(desc=d, weights=w, offs=off, grads=g, wsb=1 << 40, dcand=f):
+        return L.lib().llatte_mla_backward(
+            ctypes.byref(desc), ctypes.byref(weights), f, f, offs, B, total, max_len, f, f, dcand,
+            None, f, ctypes.byref(grads), f, f, f, f, wsb, None)
+
+    post = make_desc(cfg)
+    post.norm_mode = L.LLATTE_NORM_POST
+    assert call(desc=post) == L.LLATTE_ERR_UNSUPPORTED
+    assert "pre-norm" in L.llatte_last_error()
+    assert call(weights=L.llatte_weights()) == L.LLATTE_ERR_INVALID_ARG
+    assert call(dcand=None) == L.LLATTE_ERR_INVALID_ARG     # n_q > 0 needs d_out_cand
+    assert call(offs=(ctypes.c_int * (B + 1))(0, 10, 20, 29)) == L.LLATTE_ERR_INVALID_ARG
+    assert "total_rows" in L.llatte_last_error()
+    assert call(offs=(ctypes.c_int * (B + 1))(0, 25, 26, 30)) == L.LLATTE_ERR_INVALID_ARG
+    assert "max_len" in L.llatte_last_error()
+    assert call(wsb=1024) == L.LLATTE_ERR_WORKSPACE
+    nog = L.llatte_grads(ctypes.cast(glayers, ctypes.POINTER(L.llatte_layer_grads)), fake, None,
+                         lg, fake)
+    dr = make_desc(cfg)
+    dr.n_seeds, dr.d_out = 2, 64
+    assert call(desc=dr, grads=nog) == L.LLATTE_ERR_INVALID_ARG  # readout: the seeds' gradient
+    assert "seeds" in L.llatte_last_error()

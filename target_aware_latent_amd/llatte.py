@@ -11,7 +11,9 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libllatte.so")
+# LLATTE_LIBRARY selects another build of the library (the host-sanitized
+# copy of build.py --sanitize); the default is the in-place build.
+LIB_PATH = os.environ.get("LLATTE_LIBRARY") or os.path.join(HERE, "libllatte.so")
 
 LLATTE_OK = 0
 LLATTE_ERR_INVALID_ARG = -1

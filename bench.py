@@ -7,6 +7,7 @@
     python bench.py --workload ffn_backward (the FFN-sublayer backward)
     python bench.py --workload sublayer_backward (the attention-sublayer backward)
     python bench.py --workload compact     (the pyramid compaction, HBM-bound)
+    python bench.py --workload stack_backward (the whole-stack training backward)
     python bench.py --config c5            (the 12-layer stack with the token build)
 
 One step is one llatte_mla_forward over one batch of the workload (all
@@ -372,7 +373,6 @@ def bench_actions(args):
                    "parallelism": "single GPU"},
         "tflops": round(tflops, 2), "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
-        "kernel_symbols": families if not args.no_kernel_times else None,
     }
     emit(rec)
 
@@ -455,7 +455,6 @@ def bench_summaries(args):
         "tflops": round(F / (ms_step / 1e3) / 1e12, 2),
         "pct_peak": round(100 * F / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
-        "kernel_symbols": families if not args.no_kernel_times else None,
     }
     emit(rec)
 
@@ -596,7 +595,6 @@ def bench_backward(args):
         "tflops": round(F / (ms_step / 1e3) / 1e12, 2),
         "pct_peak": round(100 * F / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
-        "kernel_symbols": families if not args.no_kernel_times else None,
     }
     emit(rec)
 
@@ -702,7 +700,6 @@ def bench_ffn_backward(args):
         "tflops": round(Fl / (ms_step / 1e3) / 1e12, 2),
         "pct_peak": round(100 * Fl / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
-        "kernel_symbols": families if not args.no_kernel_times else None,
     }
     emit(rec)
 
@@ -830,7 +827,115 @@ def bench_sublayer_backward(args):
         "tflops": round(Fl / (ms_step / 1e3) / 1e12, 2),
         "pct_peak": round(100 * Fl / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
-        "kernel_symbols": families if not args.no_kernel_times else None,
+    }
+    emit(rec)
+
+
+STACK_BWD_METRIC = ("user-sequences/sec + TFLOP/s (% MFMA bf16 peak), whole-stack training "
+                    "backward (forward recomputed inside), 1 GPU")
+STACK_BWD_TEXT = ("c3: llatte_mla_backward over 64 users x 1600 rows (6 layers, pyramid "
+                  "1600-800-400-200-100-50, 4-seed readout to 2048): gradients of every weight, "
+                  "the seeds and the history rows, from N(0,1) output gradients")
+
+
+def stack_backward_flops(cfg, lengths):
+    """Algorithmic FLOPs per kernel label of one llatte_mla_backward call: the
+    forward it recomputes (absorbed count) and, per layer and the readout, the
+    gradient products of the FFN and attention sublayers (as their own
+    benches count them) and the readout's two projections."""
+    fl = dict(kernel_flops(cfg, lengths))
+    add = lambda k, v: fl.__setitem__(k, fl.get(k, 0) + v)
+    d, h, dk, r, F, B = cfg.d, cfg.h, cfg.dk, cfg.r, cfg.d_ff, len(lengths)
+    hd = h * dk
+    for K, n, nc in backward_layers(cfg):
+        M, Kt = B * (nc + n), B * K
+        pairs = B * (n * (K - n) + n * (n + 1) // 2 + nc * K)
+        add("attn_bwd_dq", 6 * r * h * pairs)
+        add("attn_bwd_dc", 4 * r * h * pairs)
+        for lab in ("gemm_sub_dwo", "gemm_sub_do", "gemm_sub_dwuq", "gemm_sub_dhq"):
+            add(lab, 2 * M * d * hd)
+        for lab in ("gemm_sub_dwuv", "gemm_sub_dolat", "gemm_sub_dq", "gemm_sub_dwuk"):
+            add(lab, 2 * M * r * hd)
+        for lab in ("gemm_sub_dwdkv", "gemm_sub_dh"):
+            add(lab, 2 * Kt * d * r)
+        for lab in ("gemm_bwd_dg", "gemm_bwd_dh", "gemm_bwd_dw1", "gemm_bwd_dw2"):
+            add(lab, 2 * M * d * F)
+    if cfg.n_seeds:
+        for lab in ("gemm_bwd_readout", "wgrad_readout"):
+            add(lab, 2 * B * cfg.d_out * cfg.n_seeds * d)
+    return fl
+
+
+def bench_stack_backward(args):
+    import torch
+    import synth
+    from target_aware_latent_amd import llatte as C
+    from target_aware_latent_amd.model import DeviceModel
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    cfg = synth.get_config("c3")
+    B = cfg.B
+    lengths = [cfg.L] * B
+    prob = synth.generate(cfg, seed=0, lengths=lengths)
+    I = prob["inputs"]
+    model = DeviceModel(cfg, prob["weights"])
+    rng = np.random.default_rng(0)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+    hist, offs = dev(I["hist"]), torch.from_numpy(I["offsets"].astype(np.int32)).cuda()
+    n_out = B * int(cfg.pyramid.values[-1])
+    d_hist = dev(rng.standard_normal((n_out, cfg.d)))
+    d_emb = dev(rng.standard_normal((B, cfg.d_out)))
+    grads = model.alloc_grads(lengths)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        model.backward(hist, offs, lengths, None, None, None, d_hist, d_emb, grads=grads,
+                       stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    per = stack_backward_flops(cfg, lengths)
+    Fl = sum(per.values())
+    C.llatte_kernel_timing_reset()
+    C.llatte_kernel_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = C.llatte_kernel_timing_read()
+    C.llatte_kernel_timing_enable(False)
+    kernels = {}
+    for name, (cnt, tot) in kt.items():
+        e = {"launches_per_step": cnt / args.steps, "ms_per_step": tot / args.steps}
+        if name in per:
+            e["tflops"] = per[name] / (tot / args.steps / 1e3) / 1e12
+        kernels[name] = e
+    dom = max((k for k in per if k in kt), key=lambda k: kt[k][1])
+    cnt, tot = kt[dom]
+    per_launch = per[dom] / (cnt / args.steps)
+    achieved = per_launch / (tot / cnt / 1e3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": per_launch, "avg_launch_ms": round(tot / cnt, 4)}
+    rec = {
+        "metric": STACK_BWD_METRIC, "value": round(B / (ms_step / 1e3), 1),
+        "unit": "user-sequences/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (the c3 workload's seeded inputs and weights, N(0,1) output gradients)",
+        "config": {"workload": STACK_BWD_TEXT, "global_batch": B, "seq_len": cfg.L,
+                   "parallelism": "single GPU"},
+        "tflops": round(Fl / (ms_step / 1e3) / 1e12, 2),
+        "pct_peak": round(100 * Fl / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline, "cpu_baseline": None, "kernels": kernels,
     }
     emit(rec)
 
@@ -893,8 +998,8 @@ def bench_compact(args):
     cnt, tot = kt[dom]
     # measured HBM bytes of the row-copy kernel (the scan moves a few KB)
     cp_traffic = os.path.join(ROOT, "profiles", "compaction_hbm_traffic.txt")
-    traffic = read_traffic(args.traffic if args.traffic.endswith("compaction_hbm_traffic.txt")
-                           else cp_traffic, dom)
+    traffic = read_traffic(args.traffic if args.traffic and
+                           args.traffic.endswith("compaction_hbm_traffic.txt") else cp_traffic, dom)
     roofline = {"bound": "hbm", "kernel": dom,
                 "achieved": round(nbytes / (tot / cnt / 1e3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(nbytes / (tot / cnt / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -937,14 +1042,15 @@ def main():
                          "by target_aware_latent_amd.profsum traffic); by "
                          "default the c3 records under profiles/")
     ap.add_argument("--workload", default="stack", choices=["stack", "actions", "summaries", "backward", "ffn_backward",
-                             "sublayer_backward", "compact"],
+                             "sublayer_backward", "stack_backward", "compact"],
                     help="stack: the MLA forward (default); actions: the action "
                          "tokenization that builds the history tokens; summaries: the "
                          "LoRAMLP sequence summaries of the readout; backward: the attention-core "
                          "backward of every layer of the stack; ffn_backward: the FFN-sublayer "
                          "backward (GEMM gradients) of every layer; sublayer_backward: the "
-                         "attention-sublayer backward of every layer; compact: the pyramid "
-                         "compaction (HBM-bound)")
+                         "attention-sublayer backward of every layer; stack_backward: the "
+                         "whole-stack training backward; compact: the pyramid compaction "
+                         "(HBM-bound)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
@@ -965,6 +1071,9 @@ def main():
         return
     if args.workload == "sublayer_backward":
         bench_sublayer_backward(args)
+        return
+    if args.workload == "stack_backward":
+        bench_stack_backward(args)
         return
     if args.workload == "compact":
         bench_compact(args)

@@ -98,6 +98,7 @@ class DeviceModel:
                 w.W_p = mat(W["W_p"]).data_ptr()
         self.weights = w
         self._ws = None
+        self._bws = None
         self.packed = None
 
     def pack(self, stream=None):
@@ -152,29 +153,20 @@ class DeviceModel:
 
     _GRAD_KEYS = ("g1", "W_dkv", "g_c", "W_uq", "W_uk", "W_uv", "W_o", "g2", "W1", "W2")
 
-    def backward(self, hist, offsets, lengths, cand=None, ctx=None, d_out_cand=None,
-                 d_out_hist=None, d_out_emb=None, stream=None):
-        """llatte_mla_backward: float32 gradient tensors laid out as the
-        weights ({'layers': [dict per layer], 'readout', 'seeds', 'W_q',
-        'W_p'}) and of the inputs ('hist', 'cand', 'ctx')."""
+    def alloc_grads(self, lengths):
+        """float32 gradient tensors laid out as the weights ({'layers': [dict
+        per layer], 'readout', 'seeds', 'W_q', 'W_p'}) and the inputs ('hist',
+        'cand', 'ctx'), plus the llatte_grads struct that points at them."""
         cfg, dev = self.cfg, self.device
-        B = len(lengths)
-        total = int(sum(lengths))
-        max_len = int(max(lengths))
+        B, total = len(lengths), int(sum(lengths))
         d, hd, r, F = cfg.d, cfg.h * cfg.dk, cfg.r, 4 * cfg.d
         shapes = {"g1": (d,), "W_dkv": (d, r), "g_c": (r,), "W_uq": (d, hd), "W_uk": (r, hd),
                   "W_uv": (r, hd), "W_o": (hd, d), "g2": (d,), "W1": (d, F), "W2": (F, d)}
-        keep = []
-
-        def buf(*shape):
-            t = torch.empty(*shape, device=dev)
-            keep.append(t)
-            return t
+        buf = lambda *shape: torch.empty(*shape, device=dev)
 
         def layer():
             g = {k: buf(*shapes[k]) for k in self._GRAD_KEYS}
-            st = C.llatte_layer_grads(*[g[k].data_ptr() for k in self._GRAD_KEYS])
-            return g, st
+            return g, C.llatte_layer_grads(*[g[k].data_ptr() for k in self._GRAD_KEYS])
 
         out = {"layers": []}
         structs = []
@@ -198,12 +190,25 @@ class DeviceModel:
         out["hist"] = buf(total, d)
         out["cand"] = buf(B * cfg.n_q, d) if cfg.n_q else None
         out["ctx"] = buf(B, cfg.d_c) if cfg.n_q and cfg.d_c else None
+        out["_struct"] = (G, arr)   # the struct and the array it points into
+        return out
+
+    def backward(self, hist, offsets, lengths, cand=None, ctx=None, d_out_cand=None,
+                 d_out_hist=None, d_out_emb=None, grads=None, stream=None):
+        """llatte_mla_backward into ``grads`` (from alloc_grads; allocated
+        when None); returns the gradients."""
+        B = len(lengths)
+        total = int(sum(lengths))
+        max_len = int(max(lengths))
+        if grads is None:
+            grads = self.alloc_grads(lengths)
         n = C.llatte_mla_backward_workspace_size(self.desc, B, total, max_len)
         if n == 0:
             raise C.LlatteError(-1, "llatte_mla_backward_workspace_size")
-        ws = torch.empty(n, dtype=torch.uint8, device=dev)
+        if self._bws is None or self._bws.numel() < n:
+            self._bws = torch.empty(n, dtype=torch.uint8, device=self.device)
         offs = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
         C.llatte_mla_backward(self.desc, self.weights, hist, offsets, offs, B, total, max_len,
-                              cand, ctx, d_out_cand, d_out_hist, d_out_emb, G, out["hist"],
-                              out["cand"], out["ctx"], ws, stream)
-        return out
+                              cand, ctx, d_out_cand, d_out_hist, d_out_emb, grads["_struct"][0],
+                              grads["hist"], grads["cand"], grads["ctx"], self._bws, stream)
+        return grads

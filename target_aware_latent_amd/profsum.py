@@ -138,6 +138,25 @@ def traffic(fetch_csv, write_csv, kernel, label, source, launches=None):
             "fingerprint": fingerprint(source)}
 
 
+def launches(path, first="plan_counts_kernel"):
+    """Median duration of each dispatch position of one forward pass, from a
+    rocprofv3 kernel-trace CSV: the passes start at each dispatch of `first`
+    and those with the most common number of dispatches are aligned by
+    position. Returns [(position, kernel symbol, grid, median us)]."""
+    import statistics
+    with open(path) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    starts = [i for i, r in enumerate(rows) if first in r["Kernel_Name"]]
+    passes = [rows[a:b] for a, b in zip(starts, starts[1:])]
+    if not passes:
+        return []
+    n = max(set(map(len, passes)), key=[len(p) for p in passes].count)
+    passes = [p for p in passes if len(p) == n]
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+    return [(j, passes[0][j]["Kernel_Name"], passes[0][j]["Grid_Size_X"],
+             statistics.median(dur(p[j]) for p in passes)) for j in range(n)]
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -146,6 +165,8 @@ def main(argv=None):
     c = sub.add_parser("counters")
     c.add_argument("csv", nargs="+")
     c.add_argument("--kernel", action="append", required=True)
+    t = sub.add_parser("launches")
+    t.add_argument("csv")
     b = sub.add_parser("traffic")
     b.add_argument("--fetch", required=True)
     b.add_argument("--write", required=True)
@@ -158,6 +179,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         print(stats(args.csv))
+    elif args.cmd == "launches":
+        for j, name, grid, us in launches(args.csv):
+            print(f"{j:4d} {us:9.1f} us  grid {grid:>9s}  {name[:100]}")
     elif args.cmd == "counters":
         for line in counters(args.csv, args.kernel):
             print(json.dumps(line))

@@ -108,13 +108,92 @@ struct PlanArgs {
   int nq[65];        // query tokens per user, per plan
 };
 
-// Counts and offsets of layer blockIdx.x. A user's counts at a layer follow
-// from its history length alone, so every layer is a block of its own.
-__global__ __launch_bounds__(kPlanThreads) void plan_counts_kernel(
-    const int* offsets, int B, RuleDev rule, PlanArgs a) {
+// Attention work items of plan P, counting-sorted by cost (KV tiles) in
+// decreasing order, by the whole block (hist: kMaxBuckets ints of LDS,
+// zeroed by the caller before a barrier). Item = {first query row, kv base
+// row, rows | candidate flag, key position of the first row}. Each wave
+// takes a contiguous range of users: it loads their counts 64 at a time, one
+// user per lane, and for each user in turn its lanes take the user's query
+// blocks, whose costs differ, so the bucket atomics of a wave rarely share an
+// address.
+__device__ void plan_items(const LayerPlan& P, int nq, int B, int bq, int bn, int items_cap,
+                           int* hist, int* sh) {
+  const int nc = B * nq;
+  const int ncb = (nq + bq - 1) / bq;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int kWaves = kPlanThreads / 64;
+  const int upw = (B + kWaves - 1) / kWaves;
+  const int uw0 = min(B, w * upw), uw1 = min(B, uw0 + upw);
+  // pass 0 counts items per cost bucket, pass 1 places them
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int ub = uw0; ub < uw1; ub += 64) {
+      const int uu = ub + lane;
+      int K = 0, n = 0, kvb = 0, hq = 0;
+      if (uu < uw1) {
+        K = P.kv_len[uu];
+        n = P.keep[uu];
+        kvb = P.kv_off[uu];
+        hq = P.hq_off[uu];
+      }
+      const int cnt = min(64, uw1 - ub);
+      for (int j = 0; j < cnt; ++j) {
+        const int Kj = __builtin_amdgcn_readlane(K, j), nj = __builtin_amdgcn_readlane(n, j);
+        const int kvj = __builtin_amdgcn_readlane(kvb, j), hqj = __builtin_amdgcn_readlane(hq, j);
+        const int u = ub + j;
+        const int nhb = (nj + bq - 1) / bq;
+        for (int b = lane; b < nhb + ncb; b += 64) {
+          i32x4 it;
+          int cost;
+          if (b < nhb) {
+            const int t0 = b * bq, nr = min(bq, nj - t0);
+            const int pos0 = Kj - nj + t0;
+            it = i32x4{nc + hqj + t0, kvj, nr, pos0};
+            cost = (pos0 + nr + bn - 1) / bn;
+          } else {
+            const int j0 = (b - nhb) * bq, nr = min(bq, nq - j0);
+            it = i32x4{u * nq + j0, kvj, (int)(kCandFlag | (unsigned)nr), Kj - 1};
+            cost = (Kj + bn - 1) / bn;
+          }
+          const int bucket = kMaxBuckets - 1 - min(cost, kMaxBuckets - 1);
+          if (pass == 0) {
+            atomicAdd(&hist[bucket], 1);
+          } else {
+            const int slot = atomicAdd(&hist[bucket], 1);
+            if (slot < items_cap) P.items[slot] = it;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (pass == 0) {
+      // exclusive scan of the bucket counts (buckets ordered heaviest first)
+      const int per = kMaxBuckets / kPlanThreads;
+      int s = 0;
+      for (int i = 0; i < per; ++i) s += hist[threadIdx.x * per + i];
+      int2 tot;
+      int run = block_exclusive_scan2(int2{s, 0}, sh, tot).x;
+      for (int i = 0; i < per; ++i) {
+        const int c = hist[threadIdx.x * per + i];
+        hist[threadIdx.x * per + i] = run;
+        run += c;
+      }
+      if (threadIdx.x == kPlanThreads - 1) *P.n_items = min(tot.x, items_cap);
+      __syncthreads();
+    }
+  }
+}
+
+// Counts, offsets and (bq > 0) attention work items of layer blockIdx.x. A
+// user's counts at a layer follow from its history length alone, so every
+// layer is a block of its own; the items read back the counts this block
+// wrote (visible to the block after the barrier).
+__global__ __launch_bounds__(kPlanThreads) void plan_layer_kernel(
+    const int* offsets, int B, RuleDev rule, PlanArgs a, int bq, int bn, int items_cap) {
   __shared__ int sh[64];
+  __shared__ int hist[kMaxBuckets];
   const int l = blockIdx.x, t = threadIdx.x;
   const LayerPlan P = a.base.layer(l);
+  for (int i = t; i < kMaxBuckets; i += kPlanThreads) hist[i] = 0;
   const int chunk = (B + kPlanThreads - 1) / kPlanThreads;
   const int u0 = min(B, t * chunk), u1 = min(B, u0 + chunk);
   int2 sum{0, 0};
@@ -143,67 +222,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_counts_kernel(
     P.counts[2] = nc + tot.x;
     P.counts[3] = nc + tot.y;
   }
+  if (bq <= 0) return;
+  __syncthreads();
+  plan_items(P, a.nq[l], B, bq, bn, items_cap, hist, sh);
 }
 
-// Attention work items of one layer (blockIdx.x = plan), counting-sorted by
-// cost (KV tiles) in decreasing order. Item = {first query row, kv base row,
-// rows | candidate flag, key position of the first row}.
+// Work items of plan blockIdx.x from counts already in place (the
+// standalone attention's plan).
 __global__ __launch_bounds__(kPlanThreads) void plan_items_kernel(
     PlanArgs a, int B, int bq, int bn, int items_cap) {
+  __shared__ int sh[64];
   __shared__ int hist[kMaxBuckets];
   const int l = blockIdx.x;
-  const LayerPlan P = a.base.layer(l);
-  const int nq = a.nq[l];
-  const int nc = B * nq;
   for (int i = threadIdx.x; i < kMaxBuckets; i += kPlanThreads) hist[i] = 0;
   __syncthreads();
-  const int ncb = (nq + bq - 1) / bq;
-  // pass 0 counts items per cost bucket, pass 1 places them
-  for (int pass = 0; pass < 2; ++pass) {
-    for (int u = threadIdx.x; u < B; u += kPlanThreads) {
-      const int K = P.kv_len[u], n = P.keep[u];
-      const int kvb = P.kv_off[u];
-      const int nhb = (n + bq - 1) / bq;
-      for (int b = 0; b < nhb + ncb; ++b) {
-        i32x4 it;
-        int cost;
-        if (b < nhb) {
-          const int t0 = b * bq, nr = min(bq, n - t0);
-          const int pos0 = K - n + t0;
-          it = i32x4{nc + P.hq_off[u] + t0, kvb, nr, pos0};
-          cost = (pos0 + nr + bn - 1) / bn;
-        } else {
-          const int j0 = (b - nhb) * bq, nr = min(bq, nq - j0);
-          it = i32x4{u * nq + j0, kvb, (int)(kCandFlag | (unsigned)nr), K - 1};
-          cost = (K + bn - 1) / bn;
-        }
-        const int bucket = kMaxBuckets - 1 - min(cost, kMaxBuckets - 1);
-        if (pass == 0) {
-          atomicAdd(&hist[bucket], 1);
-        } else {
-          const int slot = atomicAdd(&hist[bucket], 1);
-          if (slot < items_cap) P.items[slot] = it;
-        }
-      }
-    }
-    __syncthreads();
-    if (pass == 0) {
-      // exclusive scan of the bucket counts (buckets ordered heaviest first)
-      __shared__ int sh[64];
-      const int per = kMaxBuckets / kPlanThreads;
-      int s = 0;
-      for (int i = 0; i < per; ++i) s += hist[threadIdx.x * per + i];
-      int2 tot;
-      int run = block_exclusive_scan2(int2{s, 0}, sh, tot).x;
-      for (int i = 0; i < per; ++i) {
-        const int c = hist[threadIdx.x * per + i];
-        hist[threadIdx.x * per + i] = run;
-        run += c;
-      }
-      if (threadIdx.x == kPlanThreads - 1) *P.n_items = min(tot.x, items_cap);
-      __syncthreads();
-    }
-  }
+  plan_items(a.base.layer(l), a.nq[l], B, bq, bn, items_cap, hist, sh);
 }
 
 // Query gather map and per-row attention info; grid (B, n_plans).
@@ -235,11 +268,8 @@ hipError_t build_plan(const int* offsets, int B, const RuleDev& rule, int n_q,
   a.n_layers = rule.n_layers;
   for (int l = 0; l < n_plans; ++l) a.nq[l] = l < rule.n_layers ? n_q : n_seeds;
   timing_begin("plan", s);
-  hipLaunchKernelGGL(plan_counts_kernel, dim3(n_plans), dim3(kPlanThreads), 0, s,
-                     offsets, B, rule, a);
-  if (bq > 0)
-    hipLaunchKernelGGL(plan_items_kernel, dim3(n_plans), dim3(kPlanThreads), 0,
-                       s, a, B, bq, bn, base.icap);
+  hipLaunchKernelGGL(plan_layer_kernel, dim3(n_plans), dim3(kPlanThreads), 0, s,
+                     offsets, B, rule, a, bq, bn, base.icap);
   hipLaunchKernelGGL(plan_qmap_kernel, dim3(B, n_plans), dim3(256), 0, s, a, B);
   timing_end(s);
   return hipGetLastError();

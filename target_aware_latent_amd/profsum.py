@@ -138,7 +138,7 @@ def traffic(fetch_csv, write_csv, kernel, label, source, launches=None):
             "fingerprint": fingerprint(source)}
 
 
-def launches(path, first="plan_counts_kernel"):
+def launches(path, first="plan_layer_kernel"):
     """Median duration of each dispatch position of one forward pass, from a
     rocprofv3 kernel-trace CSV: the passes start at each dispatch of `first`
     and those with the most common number of dispatches are aligned by

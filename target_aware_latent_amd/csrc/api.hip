@@ -487,6 +487,7 @@ struct LayerIO {
   int np_in = 0;          // slots per row in w.SSin
   bool next = false;      // write them for the next layer (from the FFN)
   int np_out = 0;         // slots written
+  bf16* cast_to = nullptr;  // otherwise (fused norms): the output rows as bf16
 };
 
 // One layer (plan index l) from row space `src` into `out` ([UBM, d] float).
@@ -736,6 +737,9 @@ static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
       g.ss_out = w.SSin;
       g.ss_ld = w.ss_ld_in;
       io.np_out = gemm_ss_slots(g, b);
+    } else if (S.fnorm && io.cast_to) {
+      g.cast_out = io.cast_to;
+      g.ld_cast = S.d;
     }
     if ((err = gemm(g, b, s))) return err;
   }
@@ -896,8 +900,9 @@ llatte_status llatte_mla_forward(
     HIP_TRY(pack_all(S, wts, PK, s));
   }
 
+  // out_hist_offsets: the last layer's history query offsets, written by the plan
   HIP_TRY(build_plan(hist_offsets, B, S.rule, S.nq, S.ns, w.plan, S.NP, S.bq,
-                     kAttnBN, s));
+                     kAttnBN, s, out_hist_offsets, S.N - 1));
   if (S.nq) {
     HIP_TRY(concat_queries(cand_x, ctx, B, S.nq, S.d, S.dc, w.XC, b, s));
     GemmParams g;
@@ -939,14 +944,14 @@ llatte_status llatte_mla_forward(
   if (out_hist)
     HIP_TRY(copy_rows_f32(last + nc * S.d, S.d, out_hist, (int)S.UBn[S.N - 1],
                           PN.counts + 1, S.d, s));
-  if (out_hist_offsets)
-    HIP_TRY(hipMemcpyAsync(out_hist_offsets, PN.hq_off, sizeof(int) * (B + 1),
-                           hipMemcpyDeviceToDevice, s));
   if (S.ns) {
     HIP_TRY(broadcast_rows(PK.seeds, S.ns, S.d, B, w.S, s));
     float* ro = w.Rb[S.N & 1];
     RowSrc src{w.S, last + nc * S.d, B * S.ns, S.d};
     LayerIO rio;
+    // the readout rows as the W_p operand: bf16 straight from the FFN's
+    // epilogue on the fused-norm path, else a cast pass
+    if (!S.raw && S.fnorm) rio.cast_to = (bf16*)w.E;
     HIP_TRY(run_layer(S, w, S.N, PK.L[S.N], src, ro, rio, s));
     if (S.dump)
       HIP_TRY(copy_rows_f32(ro, S.d, desc->debug_dump + (size_t)dsec[S.N] * S.d, (int)S.UBM[S.N],
@@ -955,8 +960,9 @@ llatte_status llatte_mla_forward(
       HIP_TRY(copy_rows_f32(ro, S.d, out_emb, B * S.ns, nullptr, S.d, s));
       return LLATTE_OK;
     }
-    HIP_TRY(norm_rows(RowSrc{ro, ro, 0, S.d}, B * S.ns, nullptr, nullptr, 0.f,
-                      nullptr, 0, w.E, S.d, S.d, b ? K_BF16 : K_F32, s));
+    if (!rio.cast_to)
+      HIP_TRY(norm_rows(RowSrc{ro, ro, 0, S.d}, B * S.ns, nullptr, nullptr, 0.f,
+                        nullptr, 0, w.E, S.d, S.d, b ? K_BF16 : K_F32, s));
     GemmParams g;
     g.name = "gemm_readout";
     with_sk(g, w.sk_part);

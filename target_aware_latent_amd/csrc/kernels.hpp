@@ -240,9 +240,11 @@ struct RuleDev {
 // Builds the plans of layers 0..rule.n_layers-1, plus one readout plan
 // (no history queries, n_seeds query tokens) when n_plans > n_layers.
 // bq/bn: query rows and keys per attention tile (bq = 0: no work items).
+// hq_copy (optional, device, B + 1 ints) receives a copy of plan
+// copy_plan's history query offsets.
 hipError_t build_plan(const int* offsets, int B, const RuleDev& rule, int n_q,
                       int n_seeds, const PlanBase& base, int n_plans, int bq,
-                      int bn, hipStream_t s);
+                      int bn, hipStream_t s, int* hq_copy = nullptr, int copy_plan = -1);
 
 // One-layer plan for the standalone attention entry from given offsets.
 hipError_t build_attn_plan(const int* kv_off, const int* hq_off, int B,

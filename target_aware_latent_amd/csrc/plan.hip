@@ -106,6 +106,8 @@ struct PlanArgs {
   int n_plans;
   int n_layers;      // layers of the stack (plans beyond are the readout)
   int nq[65];        // query tokens per user, per plan
+  int* hq_copy = nullptr;  // optional second copy of plan copy_plan's hq_off
+  int copy_plan = -1;
 };
 
 // Attention work items of plan P, counting-sorted by cost (KV tiles) in
@@ -210,6 +212,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_layer_kernel(
     const int2 c = layer_counts(rule, a.n_layers, l, offsets[u + 1] - offsets[u]);
     P.kv_off[u] = run.x;
     P.hq_off[u] = run.y;
+    if (l == a.copy_plan) a.hq_copy[u] = run.y;
     run.x += c.x;
     run.y += c.y;
   }
@@ -217,6 +220,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_layer_kernel(
     const int nc = B * a.nq[l];
     P.kv_off[B] = tot.x;
     P.hq_off[B] = tot.y;
+    if (l == a.copy_plan) a.hq_copy[B] = tot.y;
     P.counts[0] = tot.x;
     P.counts[1] = tot.y;
     P.counts[2] = nc + tot.x;
@@ -261,11 +265,15 @@ __global__ void plan_qmap_kernel(PlanArgs a, int B) {
 
 hipError_t build_plan(const int* offsets, int B, const RuleDev& rule, int n_q,
                       int n_seeds, const PlanBase& base, int n_plans, int bq,
-                      int bn, hipStream_t s) {
+                      int bn, hipStream_t s, int* hq_copy, int copy_plan) {
   PlanArgs a;
   a.base = base;
   a.n_plans = n_plans;
   a.n_layers = rule.n_layers;
+  if (hq_copy) {
+    a.hq_copy = hq_copy;
+    a.copy_plan = copy_plan;
+  }
   for (int l = 0; l < n_plans; ++l) a.nq[l] = l < rule.n_layers ? n_q : n_seeds;
   timing_begin("plan", s);
   hipLaunchKernelGGL(plan_layer_kernel, dim3(n_plans), dim3(kPlanThreads), 0, s,

@@ -384,6 +384,11 @@ def test_forward_is_deterministic():
     ("c3", [0, 7, 31, 63], {}),
     ("c4", None, {}),
     ("c3", [0, 40], {"r_q": 256}),
+    # the upstream shape without the latent norm, under the halving rule,
+    # and with a first layer that keeps 1200 of the 1600 rows
+    ("c3", [3, 50], {"latent_norm": False}),
+    ("c3", [5, 62], {"pyramid": synth.PyramidRule("halving", floor=64)}),
+    ("c3", [1, 63], {"pyramid": synth.PyramidRule("fixed", (1200, 800, 400, 200, 100, 50))}),
 ])
 def test_forward_full_size(name, users, over):
     print(f"forward full {name} {over}", flush=True)

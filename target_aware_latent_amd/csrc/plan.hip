@@ -113,57 +113,56 @@ struct PlanArgs {
 // Attention work items of plan P, counting-sorted by cost (KV tiles) in
 // decreasing order, by the whole block (hist: kMaxBuckets ints of LDS,
 // zeroed by the caller before a barrier). Item = {first query row, kv base
-// row, rows | candidate flag, key position of the first row}. Each wave
-// takes a contiguous range of users: it loads their counts 64 at a time, one
-// user per lane, and for each user in turn its lanes take the user's query
-// blocks, whose costs differ, so the bucket atomics of a wave rarely share an
-// address.
+// row, rows | candidate flag, key position of the first row}. Lane = user
+// (users 64 k + lane), wave w = the query blocks b = w, w + 16, ... of each
+// user. When the active lanes of a wave fall in the same bucket (equal
+// history lengths: block b of every user costs the same), one atomic
+// reserves their slots and they take them in lane order, so within a bucket
+// the items are in user order: the workgroups dealt to one XCD
+// (round-robin) keep to the same users' latent rows, and the atomics of a
+// wave do not collide on one address.
+__device__ __forceinline__ int bucket_add(int* hist, int bucket) {
+  const unsigned long long act = __ballot(1);
+  const int first = __builtin_amdgcn_readfirstlane(bucket);
+  if (__ballot(bucket == first) == act) {
+    const int lane = threadIdx.x & 63;
+    const unsigned lo = (unsigned)act, hi = (unsigned)(act >> 32);
+    const int rank = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0));
+    int base = 0;
+    if (lane == __ffsll((long long)act) - 1) base = atomicAdd(&hist[bucket], __popcll(act));
+    return __builtin_amdgcn_readfirstlane(base) + rank;
+  }
+  return atomicAdd(&hist[bucket], 1);
+}
+
 __device__ void plan_items(const LayerPlan& P, int nq, int B, int bq, int bn, int items_cap,
                            int* hist, int* sh) {
   const int nc = B * nq;
   const int ncb = (nq + bq - 1) / bq;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   constexpr int kWaves = kPlanThreads / 64;
-  const int upw = (B + kWaves - 1) / kWaves;
-  const int uw0 = min(B, w * upw), uw1 = min(B, uw0 + upw);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   // pass 0 counts items per cost bucket, pass 1 places them
   for (int pass = 0; pass < 2; ++pass) {
-    for (int ub = uw0; ub < uw1; ub += 64) {
-      const int uu = ub + lane;
-      int K = 0, n = 0, kvb = 0, hq = 0;
-      if (uu < uw1) {
-        K = P.kv_len[uu];
-        n = P.keep[uu];
-        kvb = P.kv_off[uu];
-        hq = P.hq_off[uu];
-      }
-      const int cnt = min(64, uw1 - ub);
-      for (int j = 0; j < cnt; ++j) {
-        const int Kj = __builtin_amdgcn_readlane(K, j), nj = __builtin_amdgcn_readlane(n, j);
-        const int kvj = __builtin_amdgcn_readlane(kvb, j), hqj = __builtin_amdgcn_readlane(hq, j);
-        const int u = ub + j;
-        const int nhb = (nj + bq - 1) / bq;
-        for (int b = lane; b < nhb + ncb; b += 64) {
-          i32x4 it;
-          int cost;
-          if (b < nhb) {
-            const int t0 = b * bq, nr = min(bq, nj - t0);
-            const int pos0 = Kj - nj + t0;
-            it = i32x4{nc + hqj + t0, kvj, nr, pos0};
-            cost = (pos0 + nr + bn - 1) / bn;
-          } else {
-            const int j0 = (b - nhb) * bq, nr = min(bq, nq - j0);
-            it = i32x4{u * nq + j0, kvj, (int)(kCandFlag | (unsigned)nr), Kj - 1};
-            cost = (Kj + bn - 1) / bn;
-          }
-          const int bucket = kMaxBuckets - 1 - min(cost, kMaxBuckets - 1);
-          if (pass == 0) {
-            atomicAdd(&hist[bucket], 1);
-          } else {
-            const int slot = atomicAdd(&hist[bucket], 1);
-            if (slot < items_cap) P.items[slot] = it;
-          }
+    for (int u = lane; u < B; u += 64) {
+      const int K = P.kv_len[u], n = P.keep[u];
+      const int kvb = P.kv_off[u];
+      const int nhb = (n + bq - 1) / bq;
+      for (int b = w; b < nhb + ncb; b += kWaves) {
+        i32x4 it;
+        int cost;
+        if (b < nhb) {
+          const int t0 = b * bq, nr = min(bq, n - t0);
+          const int pos0 = K - n + t0;
+          it = i32x4{nc + P.hq_off[u] + t0, kvb, nr, pos0};
+          cost = (pos0 + nr + bn - 1) / bn;
+        } else {
+          const int j0 = (b - nhb) * bq, nr = min(bq, nq - j0);
+          it = i32x4{u * nq + j0, kvb, (int)(kCandFlag | (unsigned)nr), K - 1};
+          cost = (K + bn - 1) / bn;
         }
+        const int bucket = kMaxBuckets - 1 - min(cost, kMaxBuckets - 1);
+        const int slot = bucket_add(hist, bucket);
+        if (pass == 1 && slot < items_cap) P.items[slot] = it;
       }
     }
     __syncthreads();

@@ -355,6 +355,12 @@ __device__ __forceinline__ void lds_dma16(const void* g, unsigned lds) {
                : "memory");
 }
 __device__ __forceinline__ void dma_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector memory operations of this wave are in flight
+// (they retire in issue order: every older copy has landed).
+template <int N> __device__ __forceinline__ void dma_wait_but() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Eight-wave 128-wide tiles keep two workgroups per CU (LDS allows it): at
 // most 128 VGPRs, i.e. four waves per SIMD.
@@ -368,8 +374,11 @@ template <int BM, int BN, int NW> constexpr int gemm_min_waves3() {
 // blockIdx.y (of gridDim.y) and stores its fp32 tile in p.sk_part; SK = 2,
 // launched after it, sums the splits' tiles in split order and runs the
 // epilogue (the kernel boundary makes the tiles visible; no cross-workgroup
-// synchronisation).
-template <typename T, int BM, int BN, int WM, int WN, int NW, int PF, int SK,
+// synchronisation). SA: LDS stages of the A operand (DMA staging). With 3
+// the A copies run two K steps ahead of the MFMAs and B's one (A streams
+// from HBM, the weights mostly hit L2); the 128 x 128 tile's LDS is then
+// exactly half a CU's, and there is no room for fused row scales.
+template <typename T, int BM, int BN, int WM, int WN, int NW, int PF, int SK, int SA = 2,
           int MINW = gemm_min_waves3<BM, BN, NW>()>
 __global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
   using MF = Mfma<T>;
@@ -383,14 +392,16 @@ __global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
   constexpr int BI = BN * 8 / NT;
   constexpr int TM = WM / 16, TN = WN / 16;
 
-  // One LDS block: the double-buffered operand tiles during the main loop,
-  // then (kShuffle) the fp32 output tile for the row-major epilogue.
-  constexpr int kOpBytes = 2 * (BM + BN) * LDK * (int)sizeof(T);
+  // One LDS block: the operand tile stages during the main loop, then
+  // (kShuffle) the fp32 output tile for the row-major epilogue; after the
+  // operands, the row scales of a fused RMSNorm of A (not with SA = 3).
+  static_assert(SA == 2 || (SA == 3 && PF == 0), "A stages");
+  constexpr int kOpBytes = (SA * BM + 2 * BN) * LDK * (int)sizeof(T);
   constexpr bool kShuffle = BM * BN * 4 <= kOpBytes;
-  __shared__ __attribute__((aligned(16))) char smem[kOpBytes];
+  __shared__ __attribute__((aligned(16))) char smem[kOpBytes + (SA == 3 ? 0 : BM * 4)];
   T (*As)[BM * LDK] = (T (*)[BM * LDK])smem;
-  T (*Bs)[BN * LDK] = (T (*)[BN * LDK])(smem + 2 * BM * LDK * sizeof(T));
-  __shared__ float rs_lds[BM];  // row scales of a fused RMSNorm of A
+  T (*Bs)[BN * LDK] = (T (*)[BN * LDK])(smem + SA * BM * LDK * sizeof(T));
+  float* rs_lds = (float*)(smem + kOpBytes);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -450,7 +461,21 @@ __global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
       lds_dma16(adma[i] + k0, lds_base + (unsigned)((buf * BM * LDK + (i * NW + wave_u) * 8 * LDK) * 2));
 #pragma unroll
     for (int i = 0; i < BI; ++i)
-      lds_dma16(bdma[i] + k0, lds_base + (unsigned)((2 * BM * LDK + buf * BN * LDK +
+      lds_dma16(bdma[i] + k0, lds_base + (unsigned)((SA * BM * LDK + buf * BN * LDK +
+                                                      (i * NW + wave_u) * 8 * LDK) * 2));
+  };
+  // the same for one operand (SA = 3)
+  auto dma_a = [&](int kt, int buf) {
+    const int k0 = (kb0 + kt) * BK;
+#pragma unroll
+    for (int i = 0; i < AI; ++i)
+      lds_dma16(adma[i] + k0, lds_base + (unsigned)((buf * BM * LDK + (i * NW + wave_u) * 8 * LDK) * 2));
+  };
+  auto dma_b = [&](int kt, int buf) {
+    const int k0 = (kb0 + kt) * BK;
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
+      lds_dma16(bdma[i] + k0, lds_base + (unsigned)((SA * BM * LDK + buf * BN * LDK +
                                                       (i * NW + wave_u) * 8 * LDK) * 2));
   };
 
@@ -533,9 +558,9 @@ __global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
   const int nk = SK == 2 ? 0 : max(0, min(nk_all, kb0 + kper) - kb0);
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  auto compute = [&](int buf) {
-    const T* as = As[buf];
-    const T* bs = Bs[buf];
+  auto compute2 = [&](int abuf, int bbuf) {
+    const T* as = As[abuf];
+    const T* bs = Bs[bbuf];
 #pragma unroll
     for (int x = 0; x < NKK; ++x) {
       typename MF::frag fa[TM], fb[TN];
@@ -551,6 +576,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
         for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(fb[j], fa[i], acc[i][j]);
     }
   };
+  auto compute = [&](int buf) { compute2(buf, buf); };
   // one K step: prefetch kt+2 into the set that held kt, compute kt, stage kt+1
   // PF == 2: two register sets (prefetch distance 2); PF == 1: one set,
   // loads of step k+1 issued while step k is computed.
@@ -569,7 +595,14 @@ __global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
     __syncthreads();
   };
   if constexpr (SK != 2) {
-    if constexpr (DMA) {
+    if constexpr (DMA && SA == 3) {
+      // A(0), B(0), A(1)
+      if (nk > 0) {
+        dma_a(0, 0);
+        dma_b(0, 0);
+      }
+      if (nk > 1) dma_a(1, 1);
+    } else if constexpr (DMA) {
       if (nk > 0) dma_tile(0, 0);
     } else {
       load_tile(0, S0{});
@@ -597,7 +630,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
   }
   // Row scales of a fused RMSNorm of the A rows, one thread per tile row:
   // their loads wait together with the first tile's.
-  if (p.rs.ss && tid < BM) {
+  if (SA == 2 && p.rs.ss && tid < BM) {
     const int m = m0 + tid;
     float sc = 1.f;
     if (m < M) {
@@ -615,7 +648,23 @@ __global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
     }
     rs_lds[tid] = sc;
   }
-  if constexpr (DMA) {
+  if constexpr (DMA && SA == 3) {
+    // at step kt's top only A(kt + 1) may still be in flight (copies retire
+    // in issue order); after the barrier B(kt + 1) and A(kt + 2) go into the
+    // stages step kt - 1 used
+    int ac = 0, bc = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) dma_wait_but<AI>();
+      else dma_wait_all();
+      __syncthreads();
+      if (kt + 1 < nk) dma_b(kt + 1, bc ^ 1);
+      if (kt + 2 < nk) dma_a(kt + 2, ac == 0 ? 2 : ac - 1);
+      compute2(ac, bc);
+      ac = ac == 2 ? 0 : ac + 1;
+      bc ^= 1;
+    }
+    __syncthreads();  // operand LDS before the epilogue reuses it
+  } else if constexpr (DMA) {
     // one barrier per K step: it publishes step kt's tile (every wave has
     // waited for its own copies) and frees the other buffer, into which the
     // copies of step kt + 1 go while step kt is computed
@@ -861,7 +910,7 @@ static int k_splits(const GemmParams& p, long long tiles, int BM, int BN, int BK
   return (int)std::max<long long>(sp, 1);
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int NW, int PF = 1>
+template <typename T, int BM, int BN, int WM, int WN, int NW, int PF = 1, int SA = 2>
 static hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   const int tiles = ((p.M_cap + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   if (tiles == 0 || p.batch == 0) return hipSuccess;
@@ -869,7 +918,7 @@ static hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   const int splits = k_splits(p, (long long)tiles * p.batch, BM, BN, BK);
   timing_begin(p.name, s);
   if (splits == 1) {
-    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, NW, PF, 0>), dim3(tiles, 1, p.batch),
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, NW, PF, 0, SA>), dim3(tiles, 1, p.batch),
                        dim3(64 * NW), 0, s, p);
   } else {
     GemmParams q = p;
@@ -946,6 +995,11 @@ hipError_t gemm(const GemmParams& p, bool is_bf16, hipStream_t s) {
     case T64x128:
       return dma ? launch_gemm<bf16, 64, 128, 32, 64, 4, 0>(p, s) : launch_gemm<bf16, 64, 128, 32, 64, 4>(p, s);
     case T128x128:
+      // three A stages for long contractions without a fused row scale
+      // (measured on the layer-1/2 W2 products, K = 2048: 3-6 % faster;
+      // no gain at K = 512)
+      if (dma && !p.rs.ss && p.K >= 1024)
+        return launch_gemm<bf16, 128, 128, 32, 64, 8, 0, 3>(p, s);
       return dma ? launch_gemm<bf16, 128, 128, 32, 64, 8, 0>(p, s) : launch_gemm<bf16, 128, 128, 32, 64, 8>(p, s);
     case T128x256:
       return dma ? launch_gemm<bf16, 128, 256, 64, 64, 8, 0>(p, s) : launch_gemm<bf16, 128, 256, 64, 64, 8>(p, s);

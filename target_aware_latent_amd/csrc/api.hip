@@ -993,7 +993,7 @@ size_t llatte_mla_attention_workspace_size(const llatte_attn_desc* a,
       bq > 0 ? cdiv(nh, bq) + B + (long long)B * cdiv(a->n_cand, bq) : 1;
   Arena ar(nullptr);
   carve_plan(ar, 1, B, std::max(Mtot, 1), (int)icap);
-  ar.take<unsigned>(2);  // max magnitudes of q_lat and c_lat (bf16 range scaling)
+  ar.take<unsigned>(kAbsmaxWords);  // max magnitudes of q_lat and c_lat (bf16 range scaling)
   return ar.off + 256;
 }
 
@@ -1047,7 +1047,7 @@ static llatte_status mla_attention_impl(
   const int icap = bq > 0 ? (int)(cdiv(nh, bq) + B + (long long)B * cdiv(a->n_cand, bq)) : 1;
   Arena ar(workspace);
   PlanBase pb = carve_plan(ar, 1, B, Mtot, icap);
-  unsigned* amax = ar.take<unsigned>(2);
+  unsigned* amax = ar.take<unsigned>(kAbsmaxWords);
   hipStream_t s = (hipStream_t)stream;
   HIP_TRY(build_attn_plan(kv_offsets, hq_offsets, B, a->n_cand, bq, kAttnBN, pb, s));
   // bf16: the kernel computes in fp16 after power-of-two scalings chosen from

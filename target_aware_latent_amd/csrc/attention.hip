@@ -689,35 +689,83 @@ static hipError_t launch_r(const AttnParams& p, hipStream_t s) {
 }
 
 // Largest magnitude of bf16 arrays (float bits of non-negative values order
-// like unsigned integers): a grid-stride max per thread, a wave max, one
-// atomic per wave. amax must be zero first (attn_absmax_zero).
-__global__ void attn_absmax_zero(unsigned* amax) {
-  if (threadIdx.x < 2) amax[threadIdx.x] = 0u;
+// like unsigned integers). Pass 1: a grid-stride max per thread (arrays on a
+// 16-byte boundary read eight values per load, two loads in flight; the tail,
+// and any other array, one value at a time), a block max through LDS, one
+// plain store per array per block. Pass 2: one block folds the partials.
+// Thousands of atomics on the same two words would serialise at the memory
+// side and cost far more than the scan itself.
+__device__ __forceinline__ float absmax8(float m, const bf16x8& v) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(from_bf16(v[k])));
+  return m;
+}
+__device__ __forceinline__ float absmax_scan(const bf16* p, long long n, long long t,
+                                             long long stride) {
+  float m = 0.f;
+  const long long n8 = ((size_t)p & 15) == 0 ? n / 8 : 0;
+  const bf16x8* p8 = (const bf16x8*)p;
+  long long i = t;
+  for (; i + stride < n8; i += 2 * stride) {
+    const bf16x8 v0 = p8[i], v1 = p8[i + stride];
+    m = absmax8(absmax8(m, v0), v1);
+  }
+  if (i < n8) m = absmax8(m, p8[i]);
+  for (long long j = n8 * 8 + t; j < n; j += stride) m = fmaxf(m, fabsf(from_bf16(p[j])));
+  return m;
 }
 __global__ __launch_bounds__(256) void attn_absmax_kernel(const bf16* q, long long nq,
-                                                          const bf16* c, long long nc, float sc,
-                                                          unsigned* amax) {
-  float mq = 0.f, mc = 0.f;
+                                                          const bf16* c, long long nc,
+                                                          unsigned* part) {
+  __shared__ float red[2][4];
   const long long stride = (long long)gridDim.x * blockDim.x;
-  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < nq; i += stride)
-    mq = fmaxf(mq, fabsf(from_bf16(q[i])));
-  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < nc; i += stride)
-    mc = fmaxf(mc, fabsf(from_bf16(c[i])));
-  mq = wave_max(mq) * sc;
-  mc = wave_max(mc);
+  const long long t = blockIdx.x * (long long)blockDim.x + threadIdx.x;
+  float mq = wave_max(absmax_scan(q, nq, t, stride));
+  float mc = wave_max(absmax_scan(c, nc, t, stride));
+  const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
-    atomicMax(&amax[0], __float_as_uint(mq));
-    atomicMax(&amax[1], __float_as_uint(mc));
+    red[0][w] = mq;
+    red[1][w] = mc;
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    const float* r = red[threadIdx.x];
+    part[2 * blockIdx.x + threadIdx.x] = __float_as_uint(fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3])));
+  }
+}
+__global__ __launch_bounds__(256) void attn_absmax_fold(const unsigned* part, int nb, float sc,
+                                                        unsigned* amax) {
+  __shared__ float red[2][4];
+  float mq = 0.f, mc = 0.f;
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+    mq = fmaxf(mq, __uint_as_float(part[2 * b]));
+    mc = fmaxf(mc, __uint_as_float(part[2 * b + 1]));
+  }
+  mq = wave_max(mq);
+  mc = wave_max(mc);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][w] = mq;
+    red[1][w] = mc;
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    const float* r = red[threadIdx.x];
+    const float m = fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3]));
+    amax[threadIdx.x] = __float_as_uint(threadIdx.x == 0 ? m * sc : m);
   }
 }
 
 hipError_t attn_absmax(const void* q, long long nq, const void* c, long long nc, float scale,
                        unsigned* amax, hipStream_t s) {
-  hipLaunchKernelGGL(attn_absmax_zero, dim3(1), dim3(64), 0, s, amax);
-  const long long n = std::max(nq, nc);
-  const int blocks = (int)std::max<long long>(1, std::min<long long>((n + 255) / 256, 2048));
+  // two 16-byte loads per thread and iteration at the least
+  const long long n = std::max(nq, nc) / 16;
+  const int blocks = (int)std::max<long long>(1, std::min<long long>((n + 255) / 256, kAbsmaxBlocks));
+  unsigned* part = amax + 2;
   hipLaunchKernelGGL(attn_absmax_kernel, dim3(blocks), dim3(256), 0, s, (const bf16*)q, nq,
-                     (const bf16*)c, nc, scale * kLog2e, amax);
+                     (const bf16*)c, nc, part);
+  hipLaunchKernelGGL(attn_absmax_fold, dim3(1), dim3(256), 0, s, (const unsigned*)part, blocks,
+                     scale * kLog2e, amax);
   return hipGetLastError();
 }
 

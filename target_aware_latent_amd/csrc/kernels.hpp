@@ -314,7 +314,11 @@ bool attn_fused_supported(int h, int r, int dk);
 constexpr int kAttnBN = 64;
 hipError_t attention(const AttnParams& p, bool bf16, hipStream_t s);
 // amax[0] = max |q| * scale * log2 e, amax[1] = max |c| (bf16 inputs, float
-// bits, written from zero by this call: two launches, no memset).
+// bits), followed by two words per scan block for the partial maxima: the
+// buffer holds kAbsmaxWords unsigned, all written by this call (two launches,
+// no memset, no atomics).
+constexpr int kAbsmaxBlocks = 2048;
+constexpr int kAbsmaxWords = 2 + 2 * kAbsmaxBlocks;
 hipError_t attn_absmax(const void* q, long long nq, const void* c, long long nc, float scale,
                        unsigned* amax, hipStream_t s);
 

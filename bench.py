@@ -9,6 +9,7 @@
     python bench.py --workload compact     (the pyramid compaction, HBM-bound)
     python bench.py --workload stack_backward (the whole-stack training backward)
     python bench.py --config c5            (the 12-layer stack with the token build)
+    python bench.py --attn-phases          (adds the attention kernel's phase breakdown)
 
 One step is one llatte_mla_forward over one batch of the workload (all
 layers, the pyramid, the readout), inputs and weights already resident in
@@ -147,6 +148,46 @@ def non_absorbed_flops(cfg, lengths):
     if cfg.semantic is not None:
         t += 2 * (int(np.sum(lengths)) + cfg.B * cfg.n_q) * cfg.semantic.d_sem * d
     return t
+
+
+def attention_phases(cfg, lengths, step):
+    """One forward with the attention kernel's phase stamps: per launch (one
+    per layer, then the readout) the workgroups' summed time in the W_uk
+    prologue, the key loop and the W_uv epilogue, the launch span, and each
+    phase's share of workgroup time. `*_us_est` spreads the span over the
+    phases by those shares (two workgroups share a CU, so summed workgroup
+    time exceeds the span); the rates divide each phase's algorithmic FLOPs
+    by that estimate."""
+    import torch
+    from target_aware_latent_amd import llatte as C
+    h, dk, r = cfg.h, cfg.dk, cfg.r
+    torch.cuda.synchronize()
+    C.llatte_attention_phases_enable(1 << 20)
+    try:
+        step()
+        torch.cuda.synchronize()
+        recs = C.llatte_attention_phases_read()
+    finally:
+        C.llatte_attention_phases_enable(0)
+    lc = layer_counts(cfg, lengths)
+    out = []
+    for i, rc in enumerate(recs):
+        e = {k: round(v, 2) for k, v in rc.items()}
+        tot = rc["prologue_us"] + rc["loop_us"] + rc["epilogue_us"]
+        if i < len(lc) and tot > 0:
+            Ks, ns, M, pairs = lc[i]
+            e["layer"] = i + 1 if i < cfg.N else "readout"
+            e["query_rows"], e["allowed_pairs"] = M, pairs
+            fl = {"prologue": 2 * M * h * dk * r, "loop": 4 * r * h * pairs,
+                  "epilogue": 2 * M * h * dk * r}
+            for ph, f in fl.items():
+                share = rc[ph + "_us"] / tot
+                est = rc["span_us"] * share
+                e[ph + "_share"] = round(share, 4)
+                e[ph + "_us_est"] = round(est, 2)
+                e[ph + "_tflops_est"] = round(f / (est * 1e-6) / 1e12, 1) if est > 0 else None
+        out.append(e)
+    return out
 
 
 def family_of(label):
@@ -1033,6 +1074,10 @@ def main():
     ap.add_argument("--config", default="c3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-times", action="store_true")
+    ap.add_argument("--attn-phases", action="store_true",
+                    help="after the timed steps, one more forward with the attention "
+                         "kernel's phase stamps (W_uk prologue, key loop, W_uv "
+                         "epilogue) per launch; adds attention_phases to the line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 256 MiB device-to-device copy first, "
                          "as the reference for HBM byte counters")
@@ -1208,6 +1253,8 @@ def main():
                     "flops_per_launch": per_launch_flops,
                     "avg_launch_ms": round(tot / cnt, 4)}
 
+    phases = attention_phases(cfg, lengths, step) if args.attn_phases and cfg.dtype == "bf16" else None
+
     token_build = None
     if build_tokens is not None and "gemm_token_embed" in kernels:
         # HBM-bound gather-add: per token the table row (2 d bytes), the
@@ -1244,6 +1291,8 @@ def main():
     }
     if token_build is not None:
         rec["token_build"] = token_build
+    if phases is not None:
+        rec["attention_phases"] = phases
     emit(rec)
 
 

@@ -740,6 +740,30 @@ int32_t llatte_kernel_timing_read(char* names, int32_t name_stride,
                                   int32_t* counts, double* ms, int32_t cap);
 void llatte_kernel_timing_reset(void);
 
+/* Phase breakdown of the bf16 attention kernel (a diagnostic; the absorbed
+ * form's three parts, [LLaTTE] App. A.3: the W_uk absorption of the queries,
+ * the key-tile loop of latent flash attention, the W_uv map of the output).
+ *   llatte_attention_phases_enable(max_workgroups) allocates room for that
+ *   many workgroups' stamps on the current device (0 frees and turns the
+ *   diagnostic off; LLATTE_ERR_HIP if the allocation fails). While it is on,
+ *   every bf16 attention launch of this thread (forward layers, standalone
+ *   calls, the backward's recomputed forward) runs an instrumented copy of
+ *   the kernel whose workgroups stamp the 100 MHz real-time clock at their
+ *   start, after the prologue, after the key loop and after their last
+ *   store; the library then synchronises the stream and reduces the stamps.
+ *   Launches with more workgroups than the room are not instrumented. Not
+ *   for throughput runs, and not with llatte_mla_attention_noalloc (it
+ *   allocates).
+ *   llatte_attention_phases_read(out, cap) writes up to cap records of
+ *   LLATTE_ATTN_PHASE_FIELDS doubles to out (host), one per instrumented
+ *   launch in launch order: workgroups; summed prologue, key-loop and
+ *   epilogue microseconds over those workgroups; the launch span (first
+ *   start to last end, us); the longest workgroup (us). Returns the number
+ *   of records taken since the last enable (out may be NULL to count). */
+#define LLATTE_ATTN_PHASE_FIELDS 6
+llatte_status llatte_attention_phases_enable(int32_t max_workgroups);
+int32_t llatte_attention_phases_read(double* out, int32_t cap);
+
 #ifdef __cplusplus
 }
 #endif

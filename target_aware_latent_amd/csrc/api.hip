@@ -432,9 +432,13 @@ static hipError_t pack_layer(const Shapes& S, const llatte_layer_weights* L,
   if ((err = hipMemcpyAsync(T.g1, L->g1, S.d * 4, hipMemcpyDeviceToDevice, s))) return err;
   if ((err = hipMemcpyAsync(T.g_c, L->g_c, S.r * 4, hipMemcpyDeviceToDevice, s))) return err;
   if ((err = hipMemcpyAsync(T.g2, L->g2, S.d * 4, hipMemcpyDeviceToDevice, s))) return err;
-  if ((err = hipMemcpyAsync(T.Wuk, L->W_uk, (size_t)S.r * S.hd * e,
-                            hipMemcpyDeviceToDevice, s)))
+  // bf16: W_uk and W_uv in the fused attention kernel's fragment order
+  if (S.bf16) {
+    if ((err = attn_pack_weights(L->W_uk, L->W_uv, S.r, S.h, S.dk, T.Wuk, T.Wuv, s))) return err;
+  } else if ((err = hipMemcpyAsync(T.Wuk, L->W_uk, (size_t)S.r * S.hd * e,
+                                   hipMemcpyDeviceToDevice, s))) {
     return err;
+  }
   // fused norms: diag(g1) W_dkv, diag(g1) W_uq (or W_dq), diag(g2) W1
   const float* g1 = S.fnorm ? L->g1 : nullptr;
   const float* g2 = S.fnorm ? L->g2 : nullptr;
@@ -446,11 +450,9 @@ static hipError_t pack_layer(const Shapes& S, const llatte_layer_weights* L,
     if ((err = transpose(L->W_dq, S.d, S.rq, S.rq, 0, T.Wdq, S.d, 0, 1, k, k, s, g1))) return err;
     if ((err = hipMemcpyAsync(T.g_q, L->g_q, S.rq * 4, hipMemcpyDeviceToDevice, s))) return err;
   }
-  // per head: W_uv[:, j*dk:(j+1)*dk] ([r, dk]) -> [dk, r]; on the bf16 path
-  // the r columns in the attention kernel's stored order
-  if ((err = transpose(L->W_uv, S.r, S.dk, S.hd, S.dk, T.Wuv, S.r,
-                       (long long)S.dk * S.r, S.h, k, S.bf16 ? K_F16 : K_F32, s, nullptr,
-                       S.bf16)))
+  // fp32: per head W_uv[:, j*dk:(j+1)*dk] ([r, dk]) -> [dk, r]
+  if (!S.bf16 && (err = transpose(L->W_uv, S.r, S.dk, S.hd, S.dk, T.Wuv, S.r,
+                                  (long long)S.dk * S.r, S.h, k, K_F32, s)))
     return err;
   if ((err = transpose(L->W_o, S.hd, S.d, S.d, 0, T.Wo, S.hd, 0, 1, k, k, s))) return err;
   if ((err = transpose(L->W1, S.d, S.dff, S.dff, 0, T.W1, S.d, 0, 1, k, k, s, g2))) return err;
@@ -781,6 +783,16 @@ int32_t llatte_kernel_timing_read(char* names, int32_t name_stride,
     ++i;
   }
   return i;
+}
+
+llatte_status llatte_attention_phases_enable(int32_t max_workgroups) {
+  static_assert(LLATTE_ATTN_PHASE_FIELDS == kAttnPhaseFields, "phase record size");
+  HIP_TRY(attn_phases_enable(max_workgroups));
+  return LLATTE_OK;
+}
+
+int32_t llatte_attention_phases_read(double* out, int32_t cap) {
+  return attn_phases_read(out, cap < 0 ? 0 : cap);
 }
 
 size_t llatte_mla_forward_workspace_size(const llatte_model_desc* desc,

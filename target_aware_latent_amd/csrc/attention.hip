@@ -52,10 +52,20 @@
 // online softmax. It serves the fp32 path only.
 #include <algorithm>
 #include <type_traits>
+#include <vector>
 
 #include "kernels.hpp"
 
 namespace llatte {
+
+// Work-item and workgroup ids from the compiler's intrinsics. This file is
+// built with IEEE mode off, and the device library's id functions, built
+// with it on, are then not inlined: threadIdx / blockIdx would stay calls,
+// whose results the compiler must treat as per-lane values (vector
+// registers and vector loads for what is uniform).
+__device__ __forceinline__ int lid_x() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ int gid_x() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ int gid_y() { return (int)__builtin_amdgcn_workgroup_id_y(); }
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -158,7 +168,12 @@ struct AttnCfg {
 // Waves per workgroup.
 __host__ __device__ constexpr int attn_waves(int r) { return r == 256 ? 8 : 4; }
 
-template <int R, int EPW, int DK, bool FUSED, typename CT>
+// PH: the diagnostic copy. Each workgroup stamps the 100 MHz real-time clock
+// at its start, once its latent queries are packed (the prologue), once the
+// key loop's last products have landed, and after its last store; wave 0
+// writes the four stamps to p.clk. Stamps follow register dependencies of
+// the phase results, so the compiler cannot move a phase's work past them.
+template <int R, int EPW, int DK, bool FUSED, typename CT, bool PH = false>
 __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnParams p, AttnCfg cfg) {
   constexpr int kAttnThreads = 64 * attn_waves(R);
   constexpr int BN = kAttnBN;        // keys per tile
@@ -171,21 +186,49 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
 
   __shared__ __attribute__((aligned(16))) f16 Cs[2][BN * R];
 
-  const int nitems = min(*p.n_items, p.items_cap);
-  if ((int)blockIdx.x >= nitems) return;
-  const i32x4 it = p.items[blockIdx.x];
+  unsigned long long clk0 = 0, clk1 = 0, clk2 = 0;
+  if constexpr (PH) clk0 = __builtin_amdgcn_s_memrealtime();
+  const int tid = lid_x();
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int h0 = gid_y() * cfg.HG;
+  // The item count and the work item come in one round trip of scalar
+  // loads (constant address space; the workgroup index is below items_cap, so the item is in
+  // bounds either way, and both were written by an earlier launch).
+  // Workgroups past the count then leave with no vector load outstanding:
+  // every launch's grid covers the largest layer's item bound, so late
+  // layers have thousands of such workgroups.
+  using cint = __attribute__((address_space(4))) const int;
+  using ci32x4 = __attribute__((address_space(4))) const i32x4;
+  const int nitems_raw = *(cint*)p.n_items;
+  const i32x4 it = ((ci32x4*)p.items)[gid_x()];
+  // the item is read here, with the count: one wait for both scalar loads
+  // (the branch needs the count anyway), not a second round trip after it
+  asm volatile("" ::"s"(it[0]), "s"(it[1]), "s"(it[2]), "s"(it[3]));
+  if (gid_x() >= min(nitems_raw, p.items_cap)) return;
+  constexpr int KD = DK / 32;
+  constexpr int NRB_ = R / 16;
+  constexpr int RBC = NRB_ * KD <= 16 ? NRB_ : 16 / KD;
+  const int hd = p.h * DK;
+  const int head_w = h0 + (wave * EPW) / cfg.BQ;  // every block of a wave: one head
+  // W_uk in fragment order (attn_pack_weights): fragment (rb, kd) of the
+  // wave's head is 512 values, this lane's eight at lane * 8
+  const bf16* wp = FUSED ? (const bf16*)p.w_uk + (size_t)head_w * NRB_ * KD * 512 + lane * 8 : nullptr;
+  bf16x8 wa0[FUSED ? RBC : 1][KD];
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int r = 0; r < RBC; ++r)
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd) wa0[r][kd] = *(const bf16x8*)(wp + (size_t)(r * KD + kd) * 512);
+  }
   const int qrow0 = it[0], kvb = it[1];
   const bool cand = it[2] < 0;
   const int nr = it[2] & 0x7fffffff;
   const int pos0 = it[3];
-  const int h0 = blockIdx.y * cfg.HG;
   const int max_pos = cand ? pos0 : pos0 + nr - 1;
   const int nkeys = max_pos + 1;
   const int ntiles = (nkeys + BN - 1) / BN;
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, l16 = lane & 15;
   const float sc = p.scale * kLog2e;   // scores in log2 units
   const CT* Cg = (const CT*)p.c + (size_t)kvb * R;
   // Standalone path: C and the scaled latent queries enter fp16 as
@@ -274,18 +317,16 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
   if constexpr (FUSED) {
     // q_lat^T[r][e] = sum_k W_uk[r][head*DK + k] * q[e][head*DK + k]. All
     // blocks of a wave belong to one head: each W_uk fragment is loaded once
-    // per wave, in batches of at most 16 fragments all in flight together.
-    constexpr int KD = DK / 32;
-    constexpr int RBC = NRB * KD <= 16 ? NRB : 16 / KD;
-    const int hd = p.h * DK;
+    // per wave, in batches of at most 16 fragments all in flight together
+    // (the first batch was issued at the start).
+    static_assert(NRB_ == NRB, "r blocks");
     bf16x8 bq[NEB][KD];
 #pragma unroll
     for (int eb = 0; eb < NEB; ++eb) {
-      const bf16* qp = (const bf16*)p.q + (size_t)qrow[eb] * hd + head[0] * DK + g * 8;
+      const bf16* qp = (const bf16*)p.q + (size_t)qrow[eb] * hd + head_w * DK + g * 8;
 #pragma unroll
       for (int kd = 0; kd < KD; ++kd) bq[eb][kd] = *(const bf16x8*)(qp + kd * 32);
     }
-    const bf16* wp = (const bf16*)p.w_uk + (size_t)l16 * hd + head[0] * DK + g * 8;
     f32x4 acc[NEB][NRB];
 #pragma unroll
     for (int rb0 = 0; rb0 < NRB; rb0 += RBC) {
@@ -294,7 +335,8 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
       for (int r = 0; r < RBC; ++r)
 #pragma unroll
         for (int kd = 0; kd < KD; ++kd)
-          a[r][kd] = *(const bf16x8*)(wp + (size_t)(rb0 + r) * 16 * hd + kd * 32);
+          a[r][kd] = rb0 == 0 ? wa0[r][kd]
+                              : *(const bf16x8*)(wp + (size_t)((rb0 + r) * KD + kd) * 512);
 #pragma unroll
       for (int r = 0; r < RBC; ++r)
 #pragma unroll
@@ -321,6 +363,14 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
                            __builtin_ldexpf(sc, -eq));
       }
     }
+  }
+
+  if constexpr (PH) {
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) asm volatile("" ::"v"(qf[eb][ks]));
+    clk1 = __builtin_amdgcn_s_memrealtime();
   }
 
   // S^T operand reads: row kb*16 + l16; lane group g takes the r-chunks g
@@ -534,13 +584,25 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
     iter(t + 1, std::integral_constant<int, 1>{});
   }
   if (t < ntiles) iter(t, std::integral_constant<int, 0>{});
+  if constexpr (PH) {
+    // a read of the last products' results waits for them to land
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb) {
+      float d;
+      asm volatile("v_mov_b32 %0, %1" : "=v"(d) : "v"(acc_l[eb][0]));
+      asm volatile("" ::"v"(d));
+    }
+    clk2 = __builtin_amdgcn_s_memrealtime();
+  }
 
   if constexpr (FUSED) {
     // o^T[k][e] = sum_r W_uv^T[head][k][r] * o_lat^T[r][e]: the head's W_uv^T
     // fragments once per wave, in batches of at most 16 in flight together
     constexpr int NB = DK / 16;
     constexpr int NBC = NB * NKS <= 16 ? NB : 16 / NKS;
-    const f16* wv = (const f16*)p.w_uv_t + ((size_t)head[0] * DK + l16) * R + g * 4;
+    // W_uv in fragment order (attn_pack_weights): fragment (nb, kk) of the
+    // head is 512 values, this lane's eight at lane * 8
+    const f16* wv = (const f16*)p.w_uv_t + (size_t)head[0] * NB * NKS * 512 + lane * 8;
     f16x8 ob[NEB][NKS];
 #pragma unroll
     for (int eb = 0; eb < NEB; ++eb) {
@@ -556,8 +618,7 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
       for (int n = 0; n < NBC; ++n)
 #pragma unroll
         for (int kk = 0; kk < NKS; ++kk) {
-          const f16* q = wv + (size_t)(nb0 + n) * 16 * R + kk * 32;
-          w[n][kk] = cat(*(const f16x4*)q, *(const f16x4*)(q + 16));
+          w[n][kk] = *(const f16x8*)(wv + (size_t)((nb0 + n) * NKS + kk) * 512);
         }
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) {
@@ -587,6 +648,17 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
       if (p.lse && g == 0) p.lse[orow] = (m_run[eb] + log2f(acc_l[eb][0])) * kLn2;
     }
   }
+  if constexpr (PH) {
+    const unsigned long long clk3 = __builtin_amdgcn_s_memrealtime();
+    if (tid == 0) {
+      // the grid is items_cap workgroups wide
+      unsigned long long* o = p.clk + ((size_t)gid_y() * p.items_cap + gid_x()) * 4;
+      o[0] = clk0;
+      o[1] = clk1;
+      o[2] = clk2;
+      o[3] = clk3;
+    }
+  }
 }
 
 // fp32: one wave per (query row, head).
@@ -594,7 +666,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
   constexpr int RV = 4;  // r <= 256
   __shared__ float sq[256];
   __shared__ float sp[64];
-  const int i = blockIdx.x, hh = blockIdx.y, lane = threadIdx.x;
+  const int i = gid_x(), hh = gid_y(), lane = lid_x();
   if (i >= dev_count(p.M_dev, p.M_cap)) return;
   const int r = p.r;
   const int2 info = p.qinfo[i];
@@ -669,8 +741,12 @@ template <int R, int EPW, int DK, bool FUSED, typename CT>
 static void launch_mfma(const AttnParams& p, hipStream_t s) {
   const AttnCfg c = attn_cfg(p.h, R);
   dim3 grid(p.items_cap, p.h / c.HG);
-  hipLaunchKernelGGL((attn_mfma_kernel<R, EPW, DK, FUSED, CT>), grid, dim3(64 * attn_waves(R)),
-                     0, s, p, c);
+  if (p.clk)
+    hipLaunchKernelGGL((attn_mfma_kernel<R, EPW, DK, FUSED, CT, true>), grid,
+                       dim3(64 * attn_waves(R)), 0, s, p, c);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<R, EPW, DK, FUSED, CT>), grid, dim3(64 * attn_waves(R)),
+                       0, s, p, c);
 }
 
 template <int R, int EPW>
@@ -718,41 +794,43 @@ __global__ __launch_bounds__(256) void attn_absmax_kernel(const bf16* q, long lo
                                                           const bf16* c, long long nc,
                                                           unsigned* part) {
   __shared__ float red[2][4];
-  const long long stride = (long long)gridDim.x * blockDim.x;
-  const long long t = blockIdx.x * (long long)blockDim.x + threadIdx.x;
+  const int tid = lid_x(), b = gid_x();
+  const long long stride = (long long)__builtin_amdgcn_grid_size_x();
+  const long long t = b * 256ll + tid;
   float mq = wave_max(absmax_scan(q, nq, t, stride));
   float mc = wave_max(absmax_scan(c, nc, t, stride));
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
+  const int w = tid >> 6;
+  if ((tid & 63) == 0) {
     red[0][w] = mq;
     red[1][w] = mc;
   }
   __syncthreads();
-  if (threadIdx.x < 2) {
-    const float* r = red[threadIdx.x];
-    part[2 * blockIdx.x + threadIdx.x] = __float_as_uint(fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3])));
+  if (tid < 2) {
+    const float* r = red[tid];
+    part[2 * b + tid] = __float_as_uint(fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3])));
   }
 }
 __global__ __launch_bounds__(256) void attn_absmax_fold(const unsigned* part, int nb, float sc,
                                                         unsigned* amax) {
   __shared__ float red[2][4];
+  const int tid = lid_x();
   float mq = 0.f, mc = 0.f;
-  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+  for (int b = tid; b < nb; b += 256) {
     mq = fmaxf(mq, __uint_as_float(part[2 * b]));
     mc = fmaxf(mc, __uint_as_float(part[2 * b + 1]));
   }
   mq = wave_max(mq);
   mc = wave_max(mc);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
+  const int w = tid >> 6;
+  if ((tid & 63) == 0) {
     red[0][w] = mq;
     red[1][w] = mc;
   }
   __syncthreads();
-  if (threadIdx.x < 2) {
-    const float* r = red[threadIdx.x];
+  if (tid < 2) {
+    const float* r = red[tid];
     const float m = fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3]));
-    amax[threadIdx.x] = __float_as_uint(threadIdx.x == 0 ? m * sc : m);
+    amax[tid] = __float_as_uint(tid == 0 ? m * sc : m);
   }
 }
 
@@ -769,17 +847,144 @@ hipError_t attn_absmax(const void* q, long long nq, const void* c, long long nc,
   return hipGetLastError();
 }
 
+// Fragment-order weight packing (attn_pack_weights). Output index o =
+// ((head * nrb + rb) * nks + ks) * 512 + lane * 8 + e, with lane = 16 g + l16:
+//   W_uk: row rb * 16 + l16 of r, column head * dk + 32 ks + 8 g + e (the
+//         prologue's A operand: 16 rows of r, 8 consecutive k per lane);
+//   W_uv: row rb * 16 + l16 of the head's dk, stored latent position 32 ks +
+//         4 g + e (e < 4) or 32 ks + 16 + 4 g + (e - 4) (e >= 4), i.e. the
+//         r-chunks g and 4 + g of the step, mapped back to the original r
+//         index through attn_slot_chunk (the epilogue's A operand).
+__global__ void attn_pack_uk_kernel(const bf16* W, int r, int h, int dk, bf16* out) {
+  const long long n = (long long)r * h * dk;
+  const int nks = dk / 32, nrb = r / 16;
+  for (long long o = (long long)gid_x() * 256 + lid_x(); o < n;
+       o += (long long)__builtin_amdgcn_grid_size_x()) {
+    const int e = (int)(o & 7), lane = (int)((o >> 3) & 63);
+    long long t = o >> 9;
+    const int ks = (int)(t % nks);
+    t /= nks;
+    const int rb = (int)(t % nrb), head = (int)(t / nrb);
+    const int row = rb * 16 + (lane & 15);
+    const int col = head * dk + ks * 32 + (lane >> 4) * 8 + e;
+    out[o] = W[(size_t)row * h * dk + col];
+  }
+}
+__global__ void attn_pack_uv_kernel(const bf16* W, int r, int h, int dk, f16* out) {
+  const long long n = (long long)r * h * dk;
+  const int nks = r / 32, nrb = dk / 16;
+  for (long long o = (long long)gid_x() * 256 + lid_x(); o < n;
+       o += (long long)__builtin_amdgcn_grid_size_x()) {
+    const int e = (int)(o & 7), lane = (int)((o >> 3) & 63);
+    long long t = o >> 9;
+    const int ks = (int)(t % nks);
+    t /= nks;
+    const int rb = (int)(t % nrb), head = (int)(t / nrb);
+    const int k = rb * 16 + (lane & 15), g = lane >> 4;
+    const int sp = ks * 32 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));  // stored position
+    const int rr = (sp & ~31) + 4 * attn_slot_chunk((sp & 31) >> 2) + (sp & 3);
+    out[o] = (f16)from_bf16(W[(size_t)rr * h * dk + head * dk + k]);
+  }
+}
+
+hipError_t attn_pack_weights(const void* W_uk, const void* W_uv, int r, int h, int dk,
+                             void* uk_frag, void* uv_frag, hipStream_t s) {
+  if (dk % 32 || r % 32 || r <= 0 || h <= 0) return hipErrorInvalidValue;
+  const long long n = (long long)r * h * dk;
+  const int blocks = (int)std::min<long long>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(attn_pack_uk_kernel, dim3(blocks), dim3(256), 0, s, (const bf16*)W_uk, r,
+                     h, dk, (bf16*)uk_frag);
+  hipLaunchKernelGGL(attn_pack_uv_kernel, dim3(blocks), dim3(256), 0, s, (const bf16*)W_uv, r,
+                     h, dk, (f16*)uv_frag);
+  return hipGetLastError();
+}
+
+// Phase diagnostics (attn_phases_enable): the stamp buffer of this thread's
+// device and the records taken so far.
+struct PhaseState {
+  unsigned long long* buf = nullptr;
+  int cap = 0;
+  std::vector<double> rec;
+};
+static thread_local PhaseState t_phase;
+
+hipError_t attn_phases_enable(int max_wg) {
+  if (t_phase.buf) {
+    hipError_t e = hipFree(t_phase.buf);
+    t_phase.buf = nullptr;
+    t_phase.cap = 0;
+    if (e != hipSuccess) return e;
+  }
+  t_phase.rec.clear();
+  if (max_wg <= 0) return hipSuccess;
+  hipError_t e = hipMalloc(&t_phase.buf, (size_t)max_wg * 4 * sizeof(unsigned long long));
+  if (e != hipSuccess) {
+    t_phase.buf = nullptr;
+    return e;
+  }
+  t_phase.cap = max_wg;
+  return hipSuccess;
+}
+
+int attn_phases_read(double* out, int cap) {
+  const int n = (int)(t_phase.rec.size() / kAttnPhaseFields);
+  if (out)
+    for (int i = 0; i < std::min(n, cap) * kAttnPhaseFields; ++i) out[i] = t_phase.rec[i];
+  return n;
+}
+
+// The stamps of one instrumented launch, reduced on the host (clock ticks
+// are 10 ns).
+static hipError_t phase_collect(int nwg, hipStream_t s) {
+  std::vector<unsigned long long> h((size_t)nwg * 4);
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipMemcpy(h.data(), t_phase.buf, h.size() * sizeof(h[0]), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  double wg = 0, pro = 0, loop = 0, epi = 0, longest = 0;
+  unsigned long long first = ~0ull, last = 0;
+  for (int i = 0; i < nwg; ++i) {
+    const unsigned long long* c = &h[(size_t)i * 4];
+    if (c[0] == 0) continue;  // workgroup without a work item
+    wg += 1;
+    pro += (double)(c[1] - c[0]);
+    loop += (double)(c[2] - c[1]);
+    epi += (double)(c[3] - c[2]);
+    longest = std::max(longest, (double)(c[3] - c[0]));
+    first = std::min(first, c[0]);
+    last = std::max(last, c[3]);
+  }
+  const double us = 0.01;
+  const double rec[kAttnPhaseFields] = {wg, pro * us, loop * us, epi * us,
+                                        wg > 0 ? (double)(last - first) * us : 0.0, longest * us};
+  t_phase.rec.insert(t_phase.rec.end(), rec, rec + kAttnPhaseFields);
+  return hipSuccess;
+}
+
 hipError_t attention(const AttnParams& p, bool is_bf16, hipStream_t s) {
   if (p.M_cap <= 0) return hipSuccess;
   hipError_t e = hipSuccess;
   timing_begin(is_bf16 ? "attention_mfma" : "attention_f32", s);
   if (is_bf16) {
     if (p.items_cap > 0) {
+      AttnParams q = p;
+      int nwg = 0;
+      if (t_phase.buf && (p.r == 64 || p.r == 128 || p.r == 256)) {
+        nwg = p.items_cap * (p.h / attn_cfg(p.h, p.r).HG);
+        if (nwg <= t_phase.cap) {
+          q.clk = t_phase.buf;
+          e = hipMemsetAsync(q.clk, 0, (size_t)nwg * 4 * sizeof(unsigned long long), s);
+          if (e != hipSuccess) return e;
+        }
+      }
       switch (p.r) {
-        case 64: e = launch_r<64, 32>(p, s); break;
-        case 128: e = launch_r<128, 32>(p, s); break;
-        case 256: e = launch_r<256, 16>(p, s); break;
+        case 64: e = launch_r<64, 32>(q, s); break;
+        case 128: e = launch_r<128, 32>(q, s); break;
+        case 256: e = launch_r<256, 16>(q, s); break;
         default: e = hipErrorInvalidValue;
+      }
+      if (e == hipSuccess && q.clk) {
+        e = hipGetLastError();
+        if (e == hipSuccess) e = phase_collect(nwg, s);
       }
     }
   } else {

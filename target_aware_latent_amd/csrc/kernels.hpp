@@ -150,13 +150,11 @@ hipError_t norm_rows(RowSrc src, int rows_cap, const int* rows_dev,
 // dst [cols, rows] = transpose(src [rows, cols]) for a batch of `batch`
 // matrices laid out with the given element strides; src has kind s_kind,
 // dst kind d_kind (bf16 -> f16 and same-kind copies).
-// row_scale (optional, float [src_rows]) multiplies source row i first;
-// slot_rows places source row i at dst column attn_r_slot(i) (src_rows a
-// multiple of 32).
+// row_scale (optional, float [src_rows]) multiplies source row i first.
 hipError_t transpose(const void* src, int src_rows, int src_cols, int ld_src,
                      long long s_src, void* dst, int ld_dst, long long s_dst,
                      int batch, int s_kind, int d_kind, hipStream_t s,
-                     const float* row_scale = nullptr, bool slot_rows = false);
+                     const float* row_scale = nullptr);
 
 // xc (dtype) [B*n_q, d + d_c]: row u*n_q + j = [cand[u*n_q+j] ; ctx[u]].
 hipError_t concat_queries(const float* cand, const float* ctx, int B, int n_q,
@@ -292,20 +290,20 @@ struct AttnParams {
   // (attn_absmax); the kernel scales both by powers of two into fp16 range
   // and undoes the scaling exactly. nullptr: no scaling.
   const unsigned* amax = nullptr;
+  // diagnostics only (attn_phases_enable): four real-time clock stamps per
+  // workgroup, at [(blockIdx.y * gridDim.x + blockIdx.x) * 4]; nullptr in
+  // normal operation.
+  unsigned long long* clk = nullptr;
 };
 
 // LDS layout of the latent rows in the MFMA attention kernel: within each
 // 32-element block of r, the 4-element chunk q (r = 4q .. 4q+3) is stored at
 // chunk position slot(q) = 2q (q < 4) or 2(q-4) + 1 (q >= 4), so that chunks
 // g and 4 + g (one lane group's k values of a 32-wide MFMA step) sit side by
-// side. The kernel's output rows come in this stored order; W_uv^T is packed
-// with its r columns in the same order.
+// side. The kernel's output rows come in this stored order; the W_uv
+// fragments (attn_pack_weights) take r in the same order.
 __host__ __device__ constexpr int attn_chunk_slot(int q) { return q < 4 ? 2 * q : 2 * (q - 4) + 1; }
 __host__ __device__ constexpr int attn_slot_chunk(int c) { return (c & 1) ? 4 + (c >> 1) : c >> 1; }
-// stored position of latent index r (r of any 32-element block)
-__host__ __device__ constexpr int attn_r_slot(int r) {
-  return (r & ~31) + 4 * attn_chunk_slot((r & 31) >> 2) + (r & 3);
-}
 
 // Query rows per work item for the bf16 kernel at these sizes (0 if the
 // shape is not supported by the MFMA kernel).
@@ -313,6 +311,25 @@ int attn_bq(int h, int r);
 bool attn_fused_supported(int h, int r, int dk);
 constexpr int kAttnBN = 64;
 hipError_t attention(const AttnParams& p, bool bf16, hipStream_t s);
+// Packs W_uk ([r, h*dk] bf16) and W_uv ([r, h*dk] bf16) for the fused bf16
+// kernel in fragment order: per head, per 16-row block and 32-wide k step
+// of the MFMA operand, the 64 lanes' eight values in lane order (one
+// 16-byte load per lane, 1 KB per wave). uk_frag: bf16, A operand of the
+// W_uk product (rows r, k over the head's dk). uv_frag: fp16, A operand of
+// the W_uv product (rows dk, k over r in the kernel's stored latent order).
+// Both hold r * h * dk values; needs dk % 32 == 0 and r % 32 == 0.
+hipError_t attn_pack_weights(const void* W_uk, const void* W_uv, int r, int h, int dk,
+                             void* uk_frag, void* uv_frag, hipStream_t s);
+// Phase diagnostics of the bf16 attention kernel, per calling thread:
+// enable with room for max_wg workgroups (allocates on the current device;
+// 0 frees and disables). While enabled, each bf16 attention launch runs the
+// instrumented kernel copy, synchronises and appends one record of
+// kAttnPhaseFields doubles: workgroups, summed prologue / key-loop /
+// epilogue microseconds over workgroups, the launch span from the first
+// start to the last end, and the longest workgroup.
+constexpr int kAttnPhaseFields = 6;
+hipError_t attn_phases_enable(int max_wg);
+int attn_phases_read(double* out, int cap);
 // amax[0] = max |q| * scale * log2 e, amax[1] = max |c| (bf16 inputs, float
 // bits), followed by two words per scan block for the partial maxima: the
 // buffer holds kAbsmaxWords unsigned, all written by this call (two launches,

@@ -197,6 +197,8 @@ _SIGS = {
         ctypes.c_char_p, _c_int, ctypes.POINTER(_c_int),
         ctypes.POINTER(ctypes.c_double), _c_int]),
     "llatte_kernel_timing_reset": (None, []),
+    "llatte_attention_phases_enable": (_c_int, [_c_int]),
+    "llatte_attention_phases_read": (_c_int, [ctypes.POINTER(ctypes.c_double), _c_int]),
 }
 
 _lib = None
@@ -479,3 +481,21 @@ def llatte_kernel_timing_read(cap=64):
         nm = names.raw[i * stride:(i + 1) * stride].split(b"\0", 1)[0].decode()
         out[nm] = (counts[i], ms[i])
     return out
+
+
+LLATTE_ATTN_PHASE_FIELDS = 6
+ATTN_PHASE_KEYS = ("workgroups", "prologue_us", "loop_us", "epilogue_us", "span_us", "longest_us")
+
+
+def llatte_attention_phases_enable(max_workgroups):
+    _check(lib().llatte_attention_phases_enable(int(max_workgroups)),
+           "llatte_attention_phases_enable")
+
+
+def llatte_attention_phases_read():
+    """One dict per instrumented attention launch, in launch order."""
+    n = lib().llatte_attention_phases_read(None, 0)
+    buf = (ctypes.c_double * (max(n, 1) * LLATTE_ATTN_PHASE_FIELDS))()
+    n = lib().llatte_attention_phases_read(buf, n)
+    f = LLATTE_ATTN_PHASE_FIELDS
+    return [dict(zip(ATTN_PHASE_KEYS, buf[i * f:(i + 1) * f])) for i in range(n)]

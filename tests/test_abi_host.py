@@ -337,3 +337,11 @@ def test_stack_backward_host_validation(L):
     dr.n_seeds, dr.d_out = 2, 64
     assert call(desc=dr, grads=nog) == L.LLATTE_ERR_INVALID_ARG  # readout: the seeds' gradient
     assert "seeds" in L.llatte_last_error()
+
+
+def test_attention_phase_diagnostic_off_by_default(L):
+    # no GPU needed: nothing is allocated while the diagnostic is off
+    assert L.llatte_attention_phases_read() == []
+    L.llatte_attention_phases_enable(0)
+    assert L.llatte_attention_phases_read() == []
+    assert L.LLATTE_ATTN_PHASE_FIELDS == len(L.ATTN_PHASE_KEYS)

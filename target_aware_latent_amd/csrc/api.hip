@@ -619,7 +619,12 @@ static hipError_t run_layer(const Shapes& S, const FwdWS& w, int l,
   a.scale = 1.f / sqrtf((float)S.dk);
   a.items = P.items;
   a.n_items = P.n_items;
-  a.items_cap = S.icap;
+  // the grid: this layer's item bound (the plan's buffer holds S.icap per
+  // layer, the largest layer's); late layers launch far fewer workgroups
+  a.items_cap = S.bq > 0 ? (int)std::min<long long>(cdiv(S.UBn[l], S.bq) + S.B +
+                                                        (long long)S.B * cdiv(nql, S.bq),
+                                                    S.icap)
+                         : S.icap;
   a.qinfo = P.qinfo;
   a.M_cap = UBM;
   a.M_dev = P.counts + 3;

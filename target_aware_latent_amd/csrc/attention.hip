@@ -310,7 +310,10 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
     }
   };
 
-  load_tile(0);  // in flight during the prologue
+  // the first key tile is in flight during the prologue; fused, it is
+  // issued after the query rows (below), so that the W_uk products, which
+  // wait for those rows, do not also wait for it (loads retire in order)
+  if constexpr (!FUSED) load_tile(0);
 
   // latent queries, B operand of S^T, scaled into log2 units
   f16x8 qf[NEB][NKS];
@@ -327,6 +330,7 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
 #pragma unroll
       for (int kd = 0; kd < KD; ++kd) bq[eb][kd] = *(const bf16x8*)(qp + kd * 32);
     }
+    load_tile(0);
     f32x4 acc[NEB][NRB];
 #pragma unroll
     for (int rb0 = 0; rb0 < NRB; rb0 += RBC) {

@@ -231,22 +231,32 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
 
   const float sc = p.scale * kLog2e;   // scores in log2 units
   const CT* Cg = (const CT*)p.c + (size_t)kvb * R;
-  // Standalone path: C and the scaled latent queries enter fp16 as
-  // C 2^-ec and q sc 2^-eq, each exponent chosen so that the largest
-  // magnitude lies in [2^13, 2^14): far from fp16's overflow (65504) and, for
-  // all values within 2^-24 of the largest, from its subnormals. The MFMAs
-  // then give scores times 2^-(ec+eq), scaled back before the softmax, and
-  // the output is scaled by 2^ec at the end; powers of two are exact, so for
-  // values that fp16 represents either way the results equal the unscaled
-  // computation's. Exponents are clamped to +-60 (all-zero inputs).
+  // Standalone path: C and the scaled latent queries enter fp16 as C 2^-ec
+  // and q sc 2^-eq (powers of two: exact). Preferred is eq = -ec, where the
+  // MFMAs give the scores themselves: ec (0 where possible) puts both
+  // largest magnitudes in [2^-3, 2^14), below fp16's overflow (65504) and,
+  // for all values within 2^-11 of the largest, above its subnormals. Where
+  // no such ec exists (the two maxima's product below about 2^-6 or above
+  // 2^28), each exponent puts its largest magnitude in [2^13, 2^14) and the
+  // scores are scaled back by 2^(ec+eq) before the softmax. The output is
+  // scaled by 2^ec at the end. For values that fp16 represents either way
+  // the results equal the unscaled computation's. Exponents are clamped to
+  // +-60 (all-zero inputs).
   int ec = 0, eq = 0;
   if constexpr (!FUSED) {
     if (p.amax) {
       const auto e_of = [](unsigned bits) {  // x < 2^e for finite x > 0
         return (int)((bits >> 23) & 0xff) - 126;
       };
-      eq = min(max(-60, e_of(p.amax[0]) - 14), 60);
-      ec = min(max(-60, e_of(p.amax[1]) - 14), 60);
+      const int e_q = e_of(p.amax[0]), e_c = e_of(p.amax[1]);
+      const int lo = max(e_c - 14, -2 - e_q), hi = min(14 - e_q, e_c + 2);
+      if (lo <= hi) {
+        ec = min(max(0, lo), hi);
+        eq = -ec;
+      } else {
+        eq = min(max(-60, e_q - 14), 60);
+        ec = min(max(-60, e_c - 14), 60);
+      }
     }
   }
   const float c_pre = __builtin_ldexpf(1.f, -ec);       // applied to C on staging

@@ -3,7 +3,9 @@ ABI. The kernel computes in fp16 (more mantissa than bf16); the standalone
 entry scales its bf16 inputs by powers of two into range first, so finite
 inputs of any magnitude give finite results equal to the oracle's. The
 cases keep the scores moderate (large latent rows with small queries, and
-the reverse), so that what is checked is the range handling."""
+the reverse) or near zero (both small), so that what is checked is the
+range handling: the common exponent that gives the scores exactly, and the
+separate scaling of each side where there is none."""
 import math
 
 import numpy as np
@@ -29,6 +31,10 @@ CASES = [
     ("large_scaled_queries", 1.8e-6, 4e5, "workspace"),
     ("large_latent_noalloc", 2e6, 3.5e-7, "noalloc"),
     ("tiny_inputs", 1e-6, 7e5, "workspace"),
+    # both small: the product of the two largest magnitudes (~2^-16) leaves
+    # no common exponent for exact scores, so each side is scaled on its own
+    # and the scores are scaled back (near-uniform softmax)
+    ("tiny_product", 2e-3, 2e-3, "workspace"),
 ]
 
 
@@ -46,9 +52,11 @@ def test_large_finite_inputs_match_oracle(name, cs, qs, entry):
     C = synth.round_bf16(rng.standard_normal((int(kv_off[-1]), r)) * cs).astype(np.float32)
     scale = 1.0 / math.sqrt(64)
     big = max(np.abs(C).max(), np.abs(q).max() * scale * 1.4427)
-    assert big > 65504 or name == "tiny_inputs"  # beyond fp16's range
+    assert big > 65504 or name in ("tiny_inputs", "tiny_product")  # beyond fp16's range
     if name == "tiny_inputs":
         assert np.abs(C).max() < 6.1e-5            # fp16 subnormals unscaled
+    if name == "tiny_product":
+        assert np.abs(C).max() * np.abs(q).max() * scale * 1.4427 < 2.0 ** -6
     ad = L().llatte_attn_desc(h, r, nc, L().LLATTE_BF16, scale)
     qd = torch.from_numpy(q).cuda().to(torch.bfloat16)
     Cd = torch.from_numpy(C).cuda().to(torch.bfloat16)

@@ -1,11 +1,17 @@
 """Summaries of rocprofv3 output for the measurement records (host-side).
 
     python -m target_aware_latent_amd.profsum stats KERNEL_STATS_CSV
+    python -m target_aware_latent_amd.profsum phases BENCH_JSON_LINE_FILE
     python -m target_aware_latent_amd.profsum traffic --fetch FETCH_CSV \\
         --write WRITE_CSV --kernel attn_mfma_kernel --label attention_mfma \\
         --source target_aware_latent_amd/csrc/attention.hip [--out FILE]
 
 `stats` prints the per-kernel table of a `--kernel-trace --stats` run.
+
+`phases` prints the attention kernel's phase table from the JSON line of
+`bench.py --attn-phases` (one row per attention launch: workgroups, launch
+span, each phase's share of workgroup time, its share of the span in
+microseconds and the rate of its algorithmic FLOPs over that estimate).
 
 `counters` sums the SQ counters of `--pmc` runs per kernel and prints the
 derived ratios: MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES over the SIMD-cycles of
@@ -157,6 +163,24 @@ def launches(path, first="plan_layer_kernel"):
              statistics.median(dur(p[j]) for p in passes)) for j in range(n)]
 
 
+def phases(path):
+    """The attention phase table of a bench.py --attn-phases line."""
+    with open(path) as f:
+        rec = json.loads(f.read().strip().splitlines()[-1])
+    rows = ["                       | share of workgroup time | us (span x share)     | TFLOP/s",
+            "launch  workgroups   span_us | prologue loop epilogue | prologue loop epilogue | "
+            "prologue loop epilogue"]
+    for e in rec.get("attention_phases") or []:
+        layer = e.get("layer", "?")
+        name = f"L{layer}" if isinstance(layer, int) else str(layer)
+        rows.append(
+            f"{name:8s}{int(e['workgroups']):6d} {e['span_us']:9.1f} |"
+            f" {100 * e['prologue_share']:7.1f}% {100 * e['loop_share']:4.1f}% {100 * e['epilogue_share']:6.1f}% |"
+            f" {e['prologue_us_est']:8.1f} {e['loop_us_est']:5.1f} {e['epilogue_us_est']:8.1f} |"
+            f" {e['prologue_tflops_est']:8.0f} {e['loop_tflops_est']:4.0f} {e['epilogue_tflops_est']:8.0f}")
+    return "\n".join(rows)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -167,6 +191,8 @@ def main(argv=None):
     c.add_argument("--kernel", action="append", required=True)
     t = sub.add_parser("launches")
     t.add_argument("csv")
+    ph = sub.add_parser("phases")
+    ph.add_argument("json")
     b = sub.add_parser("traffic")
     b.add_argument("--fetch", required=True)
     b.add_argument("--write", required=True)
@@ -179,6 +205,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         print(stats(args.csv))
+    elif args.cmd == "phases":
+        print(phases(args.json))
     elif args.cmd == "launches":
         for j, name, grid, us in launches(args.csv):
             print(f"{j:4d} {us:9.1f} us  grid {grid:>9s}  {name[:100]}")

@@ -36,6 +36,8 @@ def _run(m, prob):
     ("c2", [5, 40, 17, 300, 1], dict(N=3, n_seeds=2, d_out=64,
                                      pyramid=synth.PyramidRule("fixed", (200, 20, 10)))),
     ("c3", [64, 700, 3], dict(B=3)),
+    # r = 256: the eight-wave kernel (16 rows per wave, two W_uk batches)
+    ("c3", [40, 300], dict(N=2, r=256, n_seeds=0, pyramid=synth.PyramidRule("fixed", (300, 40)))),
 ])
 def test_phase_stamps_change_nothing_and_cover_every_launch(name, lengths, kw):
     from target_aware_latent_amd.model import DeviceModel

@@ -946,9 +946,16 @@ static TileCfg select_tile(const GemmParams& p, bool is_bf16) {
   if (p.epi == EPI_ROWNORM && p.gain) {
     if (!is_bf16) return p.N <= 64 ? F128x64 : p.N <= 128 ? F128x128 : T_NONE;
     if (p.N <= 64) return ntiles(p, 128, 64) < 256 ? T64x64 : T128x64;
-    // fewer 128-row tiles than one round of the GPU (two per CU): 64-row
-    // tiles spread the rows over more CUs
-    if (p.N <= 128) return ntiles(p, 128, 128) < 512 ? T64x128 : T128x128;
+    // 64-row tiles spread the rows over more CUs where that takes no more
+    // rounds of the GPU: 128 x 128 tiles run two per CU (512 at once), the
+    // 64 x 128 ones three (LDS: 768 at once). Each round costs about the
+    // same (the K loop's latency), so 400 large tiles (one round) beat 800
+    // small ones (two).
+    if (p.N <= 128) {
+      const long long r128 = (ntiles(p, 128, 128) + 511) / 512;
+      const long long r64 = (ntiles(p, 64, 128) + 767) / 768;
+      return r64 <= r128 ? T64x128 : T128x128;
+    }
     if (p.N <= 256) return T128x256;
     return T_NONE;
   }

@@ -946,7 +946,11 @@ llatte_status llatte_mla_forward(
       src = RowSrc{w.Q0, hist_values, (int)nc, S.d};
     else
       src = RowSrc{last, last + nc * S.d, (int)nc, S.d};
-    float* out = w.Rb[l & 1];
+    // with no candidate rows ahead of them, the last layer's rows are the
+    // caller's history rows: written there directly (only the W2 product
+    // and the post-norm pass write a layer's output, both within the
+    // device-side row count, which out_hist holds)
+    float* out = (l == S.N - 1 && out_hist && nc == 0) ? out_hist : w.Rb[l & 1];
     io.next = S.fnorm && l + 1 < S.N;
     HIP_TRY(run_layer(S, w, l, PK.L[l], src, out, io, s));
     if (S.dump)
@@ -958,7 +962,7 @@ llatte_status llatte_mla_forward(
   }
   const LayerPlan PN = w.plan.layer(S.N - 1);
   if (S.nq) HIP_TRY(copy_rows_f32(last, S.d, out_cand, (int)nc, nullptr, S.d, s));
-  if (out_hist)
+  if (out_hist && last != out_hist)
     HIP_TRY(copy_rows_f32(last + nc * S.d, S.d, out_hist, (int)S.UBn[S.N - 1],
                           PN.counts + 1, S.d, s));
   if (S.ns) {

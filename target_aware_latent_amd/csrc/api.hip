@@ -1031,7 +1031,7 @@ static llatte_status mla_attention_impl(
     const llatte_attn_desc* a, const void* q_lat, const void* c_lat,
     const int32_t* kv_offsets, const int32_t* hq_offsets, int32_t B,
     int32_t Mtot, int32_t Ktot, void* out, float* lse, void* workspace,
-    size_t workspace_bytes, void* stream, bool fixed_scratch) {
+    size_t workspace_bytes, void* stream, bool fixed_scratch, bf16* out_bf16 = nullptr) {
   if (!a) return fail(LLATTE_ERR_INVALID_ARG, "desc is NULL");
   if (a->dtype != LLATTE_F32 && a->dtype != LLATTE_BF16)
     return fail(LLATTE_ERR_UNSUPPORTED, "dtype %d", a->dtype);
@@ -1081,6 +1081,7 @@ static llatte_status mla_attention_impl(
   ap.q = q_lat;
   ap.c = c_lat;
   ap.out = out;
+  ap.out_bf16 = a->dtype == LLATTE_BF16 ? out_bf16 : nullptr;
   ap.lse = lse;
   ap.fused = false;
   ap.w_uk = nullptr;
@@ -1703,11 +1704,11 @@ static llatte_status sublayer_backward_run(
   HIP_TRY(mm(Hq, d, 0, WuqT, d, 0, M, hd, d, q, hd, 0, 1, false, false, "gemm_sub_q"));
   HIP_TRY(mm(q, hd, dk, W->w_uk, hd, dk, M, r, dk, qt, hr, r, h, false, false, "gemm_sub_qlat"));
   {
-    const llatte_status st = llatte_mla_attention(&ad, qt, Cb, kv_off, hq_off, B, Mtot, Ktot, ot, lse,
-                                                  attn_ws, aws, s);
+    // õ in fp32 (the core backward's D) and as bf16 (the operand of its products)
+    const llatte_status st = mla_attention_impl(&ad, qt, Cb, kv_off, hq_off, B, Mtot, Ktot, ot, lse,
+                                                attn_ws, aws, s, false, otb);
     if (st != LLATTE_OK) return st;
   }
-  HIP_TRY(cast_f32(ot, otb, M * hr, true, s));  // õ as bf16
   HIP_TRY(transpose(W->w_uv, r, hd, hd, 0, WuvT, r, 0, 1, K_BF16, K_BF16, s));
   HIP_TRY(transpose(W->w_uk, r, hd, hd, 0, WukT, r, 0, 1, K_BF16, K_BF16, s));
   HIP_TRY(mm(otb, hr, r, WuvT, r, (long long)dk * r, M, dk, r, o, hd, dk, h, false, false, "gemm_sub_o"));

@@ -657,8 +657,13 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
       // O^T rows come in stored order: rows 16 rb + 4g .. +3 hold the chunk
       // attn_slot_chunk(4 (rb % 2) + g) of the 32-element block rb / 2
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
-        *(f32x4*)(op + 32 * (rb / 2) + 4 * attn_slot_chunk(4 * (rb % 2) + g)) = acc_o[rb][eb] * inv;
+      for (int rb = 0; rb < NRB; ++rb) {
+        const int col = 32 * (rb / 2) + 4 * attn_slot_chunk(4 * (rb % 2) + g);
+        const f32x4 v = acc_o[rb][eb] * inv;
+        *(f32x4*)(op + col) = v;
+        if (p.out_bf16)
+          *(bf16x4*)(p.out_bf16 + orow * R + col) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+      }
       if (p.lse && g == 0) p.lse[orow] = (m_run[eb] + log2f(acc_l[eb][0])) * kLn2;
     }
   }

@@ -290,6 +290,8 @@ struct AttnParams {
   // (attn_absmax); the kernel scales both by powers of two into fp16 range
   // and undoes the scaling exactly. nullptr: no scaling.
   const unsigned* amax = nullptr;
+  // standalone bf16 path: also the output as bf16 ([M, h, r]), or nullptr
+  bf16* out_bf16 = nullptr;
   // diagnostics only (attn_phases_enable): four real-time clock stamps per
   // workgroup, at [(blockIdx.y * gridDim.x + blockIdx.x) * 4]; nullptr in
   // normal operation.

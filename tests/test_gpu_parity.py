@@ -334,6 +334,9 @@ SMALL_CASES = {
                                       latent_norm=False, gain_jitter=0.1),
     "c3_small": lambda: small("c3", [300, 150, 64, 1],
                               pyramid=synth.PyramidRule("fixed", (300, 129, 64, 33, 17, 5))),
+    # the upstream widths under the halving rule, without the latent norm
+    "c3_small_halving_nolatent": lambda: small("c3", [300, 150, 64, 1], latent_norm=False,
+                                               pyramid=synth.PyramidRule("halving", floor=8)),
     "c4_small": lambda: small("c4", [1, 64, 65, 129, 300, 513, 200]),
     "c4_cross_last": lambda: small("c4", [90, 12, 300], N=2,
                                    pyramid=synth.PyramidRule("fixed", (200, 0))),

@@ -377,7 +377,8 @@ template <int BM, int BN, int NW> constexpr int gemm_min_waves3() {
 // synchronisation). SA: LDS stages of the A operand (DMA staging). With 3
 // the A copies run two K steps ahead of the MFMAs and B's one (A streams
 // from HBM, the weights mostly hit L2); the 128 x 128 tile's LDS is then
-// exactly half a CU's, and there is no room for fused row scales.
+// exactly half a CU's, and fused row scales wait in a register until the
+// output tile's LDS is laid out.
 template <typename T, int BM, int BN, int WM, int WN, int NW, int PF, int SK, int SA = 2,
           int MINW = gemm_min_waves3<BM, BN, NW>()>
 __global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
@@ -393,15 +394,17 @@ __global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
   constexpr int TM = WM / 16, TN = WN / 16;
 
   // One LDS block: the operand tile stages during the main loop, then
-  // (kShuffle) the fp32 output tile for the row-major epilogue; after the
-  // operands, the row scales of a fused RMSNorm of A (not with SA = 3).
+  // (kShuffle) the fp32 output tile for the row-major epilogue. The row
+  // scales of a fused RMSNorm of A follow the operands; with SA = 3 (no room
+  // there) they follow the output tile, written once the main loop is done.
   static_assert(SA == 2 || (SA == 3 && PF == 0), "A stages");
   constexpr int kOpBytes = (SA * BM + 2 * BN) * LDK * (int)sizeof(T);
   constexpr bool kShuffle = BM * BN * 4 <= kOpBytes;
+  static_assert(SA == 2 || (kShuffle && BM * BN * 4 + BM * 4 <= kOpBytes), "row scales with SA = 3");
   __shared__ __attribute__((aligned(16))) char smem[kOpBytes + (SA == 3 ? 0 : BM * 4)];
   T (*As)[BM * LDK] = (T (*)[BM * LDK])smem;
   T (*Bs)[BN * LDK] = (T (*)[BN * LDK])(smem + SA * BM * LDK * sizeof(T));
-  float* rs_lds = (float*)(smem + kOpBytes);
+  float* rs_lds = (float*)(smem + (SA == 3 ? BM * BN * 4 : kOpBytes));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -629,8 +632,10 @@ __global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
     }
   }
   // Row scales of a fused RMSNorm of the A rows, one thread per tile row:
-  // their loads wait together with the first tile's.
-  if (SA == 2 && p.rs.ss && tid < BM) {
+  // their loads wait together with the first tile's. With SA = 3 the value
+  // waits in a register until the operand stages are free.
+  float rs_reg = 1.f;
+  if (p.rs.ss && tid < BM) {
     const int m = m0 + tid;
     float sc = 1.f;
     if (m < M) {
@@ -646,7 +651,8 @@ __global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
       }
       sc = 1.f / sqrtf(t / (float)p.rs.n + p.rs.eps);
     }
-    rs_lds[tid] = sc;
+    if constexpr (SA == 2) rs_lds[tid] = sc;
+    else rs_reg = sc;
   }
   if constexpr (DMA && SA == 3) {
     // at step kt's top only A(kt + 1) may still be in flight (copies retire
@@ -664,6 +670,8 @@ __global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
       bc ^= 1;
     }
     __syncthreads();  // operand LDS before the epilogue reuses it
+    // past the output tile; the epilogue's barrier publishes them
+    if (p.rs.ss && tid < BM) rs_lds[tid] = rs_reg;
   } else if constexpr (DMA) {
     // one barrier per K step: it publishes step kt's tile (every wave has
     // waited for its own copies) and frees the other buffer, into which the
@@ -1002,12 +1010,10 @@ hipError_t gemm(const GemmParams& p, bool is_bf16, hipStream_t s) {
     case T64x128:
       return dma ? launch_gemm<bf16, 64, 128, 32, 64, 4, 0>(p, s) : launch_gemm<bf16, 64, 128, 32, 64, 4>(p, s);
     case T128x128:
-      // three A stages for long contractions without a fused row scale
-      // (measured on the layer-1/2 W2 products, K = 2048: 3-6 % faster;
-      // no gain at K = 512)
-      if (dma && !p.rs.ss && p.K >= 1024)
-        return launch_gemm<bf16, 128, 128, 32, 64, 8, 0, 3>(p, s);
-      return dma ? launch_gemm<bf16, 128, 128, 32, 64, 8, 0>(p, s) : launch_gemm<bf16, 128, 128, 32, 64, 8>(p, s);
+      // three A stages (A copies two K steps ahead): measured on the c3
+      // forward, 1.7 % per step over two stages (W1 and W_o 3 %, W2 1 %)
+      return dma ? launch_gemm<bf16, 128, 128, 32, 64, 8, 0, 3>(p, s)
+                 : launch_gemm<bf16, 128, 128, 32, 64, 8>(p, s);
     case T128x256:
       return dma ? launch_gemm<bf16, 128, 256, 64, 64, 8, 0>(p, s) : launch_gemm<bf16, 128, 256, 64, 64, 8>(p, s);
     case F128x64: return launch_gemm<float, 128, 64, 64, 32, 4>(p, s);

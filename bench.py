@@ -10,6 +10,7 @@
     python bench.py --workload stack_backward (the whole-stack training backward)
     python bench.py --config c5            (the 12-layer stack with the token build)
     python bench.py --attn-phases          (adds the attention kernel's phase breakdown)
+    python bench.py --gemm-phases          (adds the 128x128 GEMM tile's phase breakdown)
 
 One step is one llatte_mla_forward over one batch of the workload (all
 layers, the pyramid, the readout), inputs and weights already resident in
@@ -148,6 +149,54 @@ def non_absorbed_flops(cfg, lengths):
     if cfg.semantic is not None:
         t += 2 * (int(np.sum(lengths)) + cfg.B * cfg.n_q) * cfg.semantic.d_sem * d
     return t
+
+
+def gemm_phases(cfg, lengths, step):
+    """One forward with the phase stamps of the 128 x 128 GEMM tile: per
+    instrumented product launch (W_dkv, W_uq, W_o, W1, W2 of the large
+    layers, in launch order) the workgroups' summed wait for their first
+    operands, K loop and epilogue, the launch span, and each phase's share
+    of workgroup time. `*_us_est` spreads the span over the phases by those
+    shares (two workgroups share a CU); `loop_tflops_est` divides the
+    product's 2MNK by the loop's estimate."""
+    import torch
+    from target_aware_latent_amd import llatte as C
+    d, hd, r, dff = cfg.d, cfg.h * cfg.dk, cfg.r, 4 * cfg.d
+    # products by shape; W_uq and W_o share one when h d_k = d, and each
+    # layer launches W_uq first, so equal shapes alternate in launch order
+    names = {}
+    for shape, name in (((r, d), "down"), ((hd, d), "q"), ((d, hd), "out"), ((dff, d), "ffn1"),
+                        ((d, dff), "ffn2")):
+        names.setdefault(shape, []).append(name)
+    count = {}
+    torch.cuda.synchronize()
+    C.llatte_gemm_phases_enable(1 << 20)
+    try:
+        step()
+        torch.cuda.synchronize()
+        recs = C.llatte_gemm_phases_read()
+    finally:
+        C.llatte_gemm_phases_enable(0)
+    seen, out = {}, []
+    for rc in recs:
+        shape = (int(rc["N"]), int(rc["K"]))
+        cands = names.get(shape, ["other"])
+        count[shape] = count.get(shape, 0) + 1
+        name = cands[(count[shape] - 1) % len(cands)]
+        seen[name] = seen.get(name, 0) + 1
+        e = {k: round(v, 2) for k, v in rc.items()}
+        e["product"], e["layer"] = name, seen[name]
+        tot = rc["first_us"] + rc["loop_us"] + rc["epilogue_us"]
+        if tot > 0:
+            for ph in ("first", "loop", "epilogue"):
+                share = rc[ph + "_us"] / tot
+                e[ph + "_share"] = round(share, 4)
+                e[ph + "_us_est"] = round(rc["span_us"] * share, 2)
+            est = e["loop_us_est"]
+            e["loop_tflops_est"] = round(2 * rc["M"] * rc["N"] * rc["K"] / (est * 1e-6) / 1e12, 1) \
+                if est > 0 else None
+        out.append(e)
+    return out
 
 
 def attention_phases(cfg, lengths, step):
@@ -1074,6 +1123,10 @@ def main():
     ap.add_argument("--config", default="c3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-times", action="store_true")
+    ap.add_argument("--gemm-phases", action="store_true",
+                    help="after the timed steps, one more forward with the 128x128 GEMM tile's "
+                         "phase stamps (first operands, K loop, epilogue) per launch; adds "
+                         "gemm_phases to the line")
     ap.add_argument("--attn-phases", action="store_true",
                     help="after the timed steps, one more forward with the attention "
                          "kernel's phase stamps (W_uk prologue, key loop, W_uv "
@@ -1254,6 +1307,7 @@ def main():
                     "avg_launch_ms": round(tot / cnt, 4)}
 
     phases = attention_phases(cfg, lengths, step) if args.attn_phases and cfg.dtype == "bf16" else None
+    gphases = gemm_phases(cfg, lengths, step) if args.gemm_phases and cfg.dtype == "bf16" else None
 
     token_build = None
     if build_tokens is not None and "gemm_token_embed" in kernels:
@@ -1293,6 +1347,8 @@ def main():
         rec["token_build"] = token_build
     if phases is not None:
         rec["attention_phases"] = phases
+    if gphases is not None:
+        rec["gemm_phases"] = gphases
     emit(rec)
 
 

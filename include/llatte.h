@@ -764,6 +764,31 @@ void llatte_kernel_timing_reset(void);
 llatte_status llatte_attention_phases_enable(int32_t max_workgroups);
 int32_t llatte_attention_phases_read(double* out, int32_t cap);
 
+/* Phase breakdown of the bf16 matrix products on the 128 x 128 tile staged
+ * by LDS DMA (a diagnostic; the products of [LLaTTE] App. A.2's layer
+ * equation and App. A.3's projections that run on it: the large W_dkv,
+ * W_uq, W_o, W1 and W2 launches).
+ *   llatte_gemm_phases_enable(max_workgroups) allocates room for that many
+ *   workgroups' stamps on the current device (0 frees and turns the
+ *   diagnostic off; LLATTE_ERR_HIP if the allocation fails). While it is on,
+ *   every such product of this thread whose K is not split runs an
+ *   instrumented copy of the kernel whose workgroups stamp the 100 MHz
+ *   real-time clock at their start, once their first operands have landed,
+ *   once their last products have landed and after their last store; the
+ *   library then synchronises the stream and reduces the stamps. Launches
+ *   with more workgroups than the room, and the other tiles, are not
+ *   instrumented. Not for throughput runs.
+ *   llatte_gemm_phases_read(out, cap) writes up to cap records of
+ *   LLATTE_GEMM_PHASE_FIELDS doubles to out (host), one per instrumented
+ *   launch in launch order: workgroups with rows; the row bound M, N and K
+ *   of the product; summed wait for the first operands, K loop and
+ *   epilogue microseconds over those workgroups; the launch span (us); the
+ *   longest workgroup (us). Returns the number of records taken since the
+ *   last enable (out may be NULL to count). */
+#define LLATTE_GEMM_PHASE_FIELDS 9
+llatte_status llatte_gemm_phases_enable(int32_t max_workgroups);
+int32_t llatte_gemm_phases_read(double* out, int32_t cap);
+
 #ifdef __cplusplus
 }
 #endif

@@ -800,6 +800,16 @@ int32_t llatte_attention_phases_read(double* out, int32_t cap) {
   return attn_phases_read(out, cap < 0 ? 0 : cap);
 }
 
+llatte_status llatte_gemm_phases_enable(int32_t max_workgroups) {
+  static_assert(kGemmPhaseFields == LLATTE_GEMM_PHASE_FIELDS, "record width");
+  HIP_TRY(gemm_phases_enable(max_workgroups));
+  return LLATTE_OK;
+}
+
+int32_t llatte_gemm_phases_read(double* out, int32_t cap) {
+  return gemm_phases_read(out, cap < 0 ? 0 : cap);
+}
+
 size_t llatte_mla_forward_workspace_size(const llatte_model_desc* desc,
                                          int32_t B, int32_t total_rows,
                                          int32_t max_len) {

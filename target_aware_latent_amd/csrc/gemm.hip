@@ -15,6 +15,7 @@
 // v_mfma_f32_16x16x4_f32. Accumulation is fp32 in both cases.
 #include <algorithm>
 #include <type_traits>
+#include <vector>
 
 #include "kernels.hpp"
 
@@ -379,9 +380,18 @@ template <int BM, int BN, int NW> constexpr int gemm_min_waves3() {
 // from HBM, the weights mostly hit L2); the 128 x 128 tile's LDS is then
 // exactly half a CU's, and fused row scales wait in a register until the
 // output tile's LDS is laid out.
+//
+// PH: the diagnostic copy (SK = 0, LDS DMA). Each workgroup stamps the 100 MHz
+// real-time clock at its start, once its first operands have landed (the
+// first K step's barrier), once its last products have landed, and after
+// its last store; thread 0 writes the four stamps to p.clk at the
+// workgroup's launch index. Workgroups past the row count write none.
 template <typename T, int BM, int BN, int WM, int WN, int NW, int PF, int SK, int SA = 2,
-          int MINW = gemm_min_waves3<BM, BN, NW>()>
+          bool PH = false, int MINW = gemm_min_waves3<BM, BN, NW>()>
 __global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
+  static_assert(!PH || (SK == 0 && PF == 0), "phase stamps: whole products, LDS DMA");
+  unsigned long long clk0 = 0, clk1 = 0, clk2 = 0;
+  if constexpr (PH) clk0 = clk1 = __builtin_amdgcn_s_memrealtime();
   using MF = Mfma<T>;
   constexpr int NT = 64 * NW;              // threads
   constexpr int CE = 16 / sizeof(T);       // elements per 16-byte chunk
@@ -663,6 +673,9 @@ __global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
       if (kt + 1 < nk) dma_wait_but<AI>();
       else dma_wait_all();
       __syncthreads();
+      if constexpr (PH) {
+        if (kt == 0) clk1 = __builtin_amdgcn_s_memrealtime();
+      }
       if (kt + 1 < nk) dma_b(kt + 1, bc ^ 1);
       if (kt + 2 < nk) dma_a(kt + 2, ac == 0 ? 2 : ac - 1);
       compute2(ac, bc);
@@ -679,6 +692,9 @@ __global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
     for (int kt = 0; kt < nk; ++kt) {
       dma_wait_all();
       __syncthreads();
+      if constexpr (PH) {
+        if (kt == 0) clk1 = __builtin_amdgcn_s_memrealtime();
+      }
       if (kt + 1 < nk) dma_tile(kt + 1, (kt + 1) & 1);
       compute(kt & 1);
     }
@@ -718,6 +734,13 @@ __global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
     }
   }
 
+  if constexpr (PH) {
+    // a read of the last products' results waits for them to land
+    float d;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(d) : "v"(acc[TM - 1][TN - 1][3]));
+    asm volatile("" ::"v"(d));
+    clk2 = __builtin_amdgcn_s_memrealtime();
+  }
   if constexpr (kShuffle) {
     if (p.nt)
       epilogue_rowmajor<T, BM, BN, WM, WN, NW, true>(p, acc, (float*)smem, rs_lds, rrow, m0, n0,
@@ -725,6 +748,16 @@ __global__ __launch_bounds__(64 * NW, MINW) void gemm_kernel(GemmParams p) {
     else
       epilogue_rowmajor<T, BM, BN, WM, WN, NW, false>(p, acc, (float*)smem, rs_lds, rrow, m0, n0,
                                                       M, wm0, wn0, lane, tid);
+    if constexpr (PH) {
+      const unsigned long long clk3 = __builtin_amdgcn_s_memrealtime();
+      if (tid == 0) {
+        unsigned long long* o = p.clk + ((size_t)blockIdx.z * gridDim.x + blockIdx.x) * 4;
+        o[0] = clk0;
+        o[1] = clk1;
+        o[2] = clk2;
+        o[3] = clk3;
+      }
+    }
     return;
   }
   // Direct epilogue (tiles whose fp32 output does not fit the LDS block):
@@ -940,6 +973,80 @@ static hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Phase diagnostics (gemm_phases_enable): the stamp buffer of this thread's
+// device and the records taken so far.
+struct GemmPhaseState {
+  unsigned long long* buf = nullptr;
+  int cap = 0;
+  std::vector<double> rec;
+};
+static thread_local GemmPhaseState t_gph;
+
+hipError_t gemm_phases_enable(int max_wg) {
+  if (t_gph.buf) {
+    hipError_t e = hipFree(t_gph.buf);
+    t_gph.buf = nullptr;
+    t_gph.cap = 0;
+    if (e != hipSuccess) return e;
+  }
+  t_gph.rec.clear();
+  if (max_wg <= 0) return hipSuccess;
+  hipError_t e = hipMalloc(&t_gph.buf, (size_t)max_wg * 4 * sizeof(unsigned long long));
+  if (e != hipSuccess) {
+    t_gph.buf = nullptr;
+    return e;
+  }
+  t_gph.cap = max_wg;
+  return hipSuccess;
+}
+
+int gemm_phases_read(double* out, int cap) {
+  const int n = (int)(t_gph.rec.size() / kGemmPhaseFields);
+  if (out)
+    for (int i = 0; i < std::min(n, cap) * kGemmPhaseFields; ++i) out[i] = t_gph.rec[i];
+  return n;
+}
+
+// One instrumented launch of the 128 x 128 LDS-staged tile: stamps, then the
+// host reduction (clock ticks are 10 ns). Record: workgroups with rows, M
+// bound, N, K, summed wait for the first operands, K loop and epilogue (us),
+// launch span and longest workgroup (us).
+static hipError_t launch_gemm_phases(const GemmParams& p, int tiles, hipStream_t s) {
+  const int nwg = tiles * p.batch;
+  GemmParams q = p;
+  q.clk = t_gph.buf;
+  hipError_t e = hipMemsetAsync(q.clk, 0, (size_t)nwg * 4 * sizeof(unsigned long long), s);
+  if (e != hipSuccess) return e;
+  timing_begin(p.name, s);
+  hipLaunchKernelGGL((gemm_kernel<bf16, 128, 128, 32, 64, 8, 0, 0, 3, true>), dim3(tiles, 1, p.batch),
+                     dim3(512), 0, s, q);
+  timing_end(s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  std::vector<unsigned long long> h((size_t)nwg * 4);
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+  if ((e = hipMemcpy(h.data(), q.clk, h.size() * sizeof(h[0]), hipMemcpyDeviceToHost)) != hipSuccess)
+    return e;
+  double wg = 0, first = 0, loop = 0, epi = 0, longest = 0;
+  unsigned long long t0 = ~0ull, t1 = 0;
+  for (int i = 0; i < nwg; ++i) {
+    const unsigned long long* c = &h[(size_t)i * 4];
+    if (c[0] == 0) continue;  // a workgroup past the row count
+    wg += 1;
+    first += (double)(c[1] - c[0]);
+    loop += (double)(c[2] - c[1]);
+    epi += (double)(c[3] - c[2]);
+    longest = std::max(longest, (double)(c[3] - c[0]));
+    t0 = std::min(t0, c[0]);
+    t1 = std::max(t1, c[3]);
+  }
+  const double us = 0.01;
+  const double rec[kGemmPhaseFields] = {wg, (double)p.M_cap, (double)p.N, (double)p.K,
+                                        first * us, loop * us, epi * us,
+                                        wg > 0 ? (double)(t1 - t0) * us : 0.0, longest * us};
+  t_gph.rec.insert(t_gph.rec.end(), rec, rec + kGemmPhaseFields);
+  return hipSuccess;
+}
+
 static long long ntiles(const GemmParams& p, int bm, int bn) {
   return (long long)((p.M_cap + bm - 1) / bm) * ((p.N + bn - 1) / bn) * p.batch;
 }
@@ -1012,6 +1119,9 @@ hipError_t gemm(const GemmParams& p, bool is_bf16, hipStream_t s) {
     case T128x128:
       // three A stages (A copies two K steps ahead): measured on the c3
       // forward, 1.7 % per step over two stages (W1 and W_o 3 %, W2 1 %)
+      if (dma && t_gph.buf && p.batch >= 1 && ntiles(p, 128, 128) <= t_gph.cap &&
+          k_splits(p, ntiles(p, 128, 128), 128, 128, 64) == 1)
+        return launch_gemm_phases(p, (int)(ntiles(p, 128, 128) / std::max(p.batch, 1)), s);
       return dma ? launch_gemm<bf16, 128, 128, 32, 64, 8, 0, 3>(p, s)
                  : launch_gemm<bf16, 128, 128, 32, 64, 8>(p, s);
     case T128x256:

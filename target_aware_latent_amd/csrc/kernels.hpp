@@ -96,12 +96,19 @@ struct GemmParams {
   float* sk_part = nullptr;
   long long sk_part_cap = 0;
   int sk_splits = 1;
+  // Phase stamps of the diagnostic kernel copy (gemm_phases_enable): four
+  // 64-bit clock values per workgroup, in launch order.
+  unsigned long long* clk = nullptr;
 };
 
 // Partial sums of squares per row that an EPI_RESID_F32 launch with these
 // parameters writes to ss_out.
 int gemm_ss_slots(const GemmParams& p, bool bf16);
 hipError_t gemm(const GemmParams& p, bool bf16, hipStream_t s);
+// Phase diagnostic of the 128 x 128 LDS-staged tile (llatte_gemm_phases_*).
+hipError_t gemm_phases_enable(int max_wg);
+int gemm_phases_read(double* out, int cap);
+constexpr int kGemmPhaseFields = 9;
 
 // ------------------------------------------------------------------ actions
 // U[row] = [E_type(type) | E_item(item) | E_surf(surf) | E_time(bucket) |

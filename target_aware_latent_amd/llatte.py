@@ -199,6 +199,8 @@ _SIGS = {
     "llatte_kernel_timing_reset": (None, []),
     "llatte_attention_phases_enable": (_c_int, [_c_int]),
     "llatte_attention_phases_read": (_c_int, [ctypes.POINTER(ctypes.c_double), _c_int]),
+    "llatte_gemm_phases_enable": (_c_int, [_c_int]),
+    "llatte_gemm_phases_read": (_c_int, [ctypes.POINTER(ctypes.c_double), _c_int]),
 }
 
 _lib = None
@@ -499,3 +501,21 @@ def llatte_attention_phases_read():
     n = lib().llatte_attention_phases_read(buf, n)
     f = LLATTE_ATTN_PHASE_FIELDS
     return [dict(zip(ATTN_PHASE_KEYS, buf[i * f:(i + 1) * f])) for i in range(n)]
+
+
+LLATTE_GEMM_PHASE_FIELDS = 9
+GEMM_PHASE_KEYS = ("workgroups", "M", "N", "K", "first_us", "loop_us", "epilogue_us", "span_us",
+                   "longest_us")
+
+
+def llatte_gemm_phases_enable(max_workgroups):
+    _check(lib().llatte_gemm_phases_enable(int(max_workgroups)), "llatte_gemm_phases_enable")
+
+
+def llatte_gemm_phases_read():
+    """One dict per instrumented matrix-product launch, in launch order."""
+    n = lib().llatte_gemm_phases_read(None, 0)
+    buf = (ctypes.c_double * (max(n, 1) * LLATTE_GEMM_PHASE_FIELDS))()
+    n = lib().llatte_gemm_phases_read(buf, n)
+    f = LLATTE_GEMM_PHASE_FIELDS
+    return [dict(zip(GEMM_PHASE_KEYS, buf[i * f:(i + 1) * f])) for i in range(n)]

@@ -164,7 +164,7 @@ def launches(path, first="plan_layer_kernel"):
 
 
 def phases(path):
-    """The attention phase table of a bench.py --attn-phases line."""
+    """The phase tables of a bench.py --attn-phases / --gemm-phases line."""
     with open(path) as f:
         rec = json.loads(f.read().strip().splitlines()[-1])
     rows = ["                       | share of workgroup time | us (span x share)     | TFLOP/s",
@@ -178,6 +178,16 @@ def phases(path):
             f" {100 * e['prologue_share']:7.1f}% {100 * e['loop_share']:4.1f}% {100 * e['epilogue_share']:6.1f}% |"
             f" {e['prologue_us_est']:8.1f} {e['loop_us_est']:5.1f} {e['epilogue_us_est']:8.1f} |"
             f" {e['prologue_tflops_est']:8.0f} {e['loop_tflops_est']:4.0f} {e['epilogue_tflops_est']:8.0f}")
+    g = rec.get("gemm_phases") or []
+    if g:
+        rows += ["", "                                | share of workgroup time  | us (span x share)      | K loop",
+                 "product layer  workgroups span_us | first   loop   epilogue | first   loop  epilogue | TFLOP/s"]
+        for e in g:
+            rows.append(
+                f"{e['product']:8s}{e['layer']:3d} {int(e['workgroups']):9d} {e['span_us']:8.1f} |"
+                f" {100 * e['first_share']:5.1f}% {100 * e['loop_share']:5.1f}% {100 * e['epilogue_share']:7.1f}% |"
+                f" {e['first_us_est']:6.1f} {e['loop_us_est']:6.1f} {e['epilogue_us_est']:8.1f} |"
+                f" {e['loop_tflops_est']:7.0f}")
     return "\n".join(rows)
 
 

@@ -345,3 +345,11 @@ def test_attention_phase_diagnostic_off_by_default(L):
     L.llatte_attention_phases_enable(0)
     assert L.llatte_attention_phases_read() == []
     assert L.LLATTE_ATTN_PHASE_FIELDS == len(L.ATTN_PHASE_KEYS)
+
+
+def test_gemm_phase_diagnostic_off_by_default(L):
+    # no GPU needed: nothing is allocated while the diagnostic is off
+    assert L.llatte_gemm_phases_read() == []
+    L.llatte_gemm_phases_enable(0)
+    assert L.llatte_gemm_phases_read() == []
+    assert L.LLATTE_GEMM_PHASE_FIELDS == len(L.GEMM_PHASE_KEYS)

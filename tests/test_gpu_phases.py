@@ -68,3 +68,39 @@ def test_phase_stamps_change_nothing_and_cover_every_launch(name, lengths, kw):
     assert C.llatte_attention_phases_read() == []
     for k in ref:
         assert np.array_equal(again[k], ref[k], equal_nan=True), k
+
+
+def test_gemm_phase_stamps_change_nothing():
+    """The matrix products' phase stamps (llatte_gemm_phases_enable / _read):
+    the instrumented copy of the 128 x 128 tile computes the same outputs bit
+    for bit, and every launch on that tile gives one record whose shape is
+    one of the layer's products and whose phases add up within the span."""
+    from target_aware_latent_amd.model import DeviceModel
+    lengths = [1600, 1500, 1600, 1400, 1600, 1600]
+    cfg = synth.get_config("c3", B=len(lengths), N=2,
+                           pyramid=synth.PyramidRule("fixed", (1600, 700)))
+    prob = synth.generate(cfg, seed=7, lengths=lengths)
+    m = DeviceModel(cfg, prob["weights"])
+    m.pack()
+    print(f"gemm phases c3 lengths={lengths}", flush=True)
+    ref = _run(m, prob)
+    C = L()
+    C.llatte_gemm_phases_enable(1 << 16)
+    try:
+        got = _run(m, prob)
+        recs = C.llatte_gemm_phases_read()
+    finally:
+        C.llatte_gemm_phases_enable(0)
+    for k in ref:
+        assert np.array_equal(got[k], ref[k], equal_nan=True), k
+    d, hd, r, dff = cfg.d, cfg.h * cfg.dk, cfg.r, 4 * cfg.d
+    shapes = {(r, d), (hd, d), (d, hd), (dff, d), (d, dff)}
+    # layer 1 has 9300 rows: its W_uq, W_o, W1 and W2 launches are on the tile
+    assert len(recs) >= 4, recs
+    for rc in recs:
+        assert (int(rc["N"]), int(rc["K"])) in shapes, rc
+        assert rc["workgroups"] >= 1
+        assert min(rc["first_us"], rc["loop_us"], rc["epilogue_us"]) >= 0, rc
+        assert 0 < rc["longest_us"] <= rc["span_us"] + 1e-6, rc
+        per_wg = (rc["first_us"] + rc["loop_us"] + rc["epilogue_us"]) / rc["workgroups"]
+        assert per_wg <= rc["longest_us"] + 1e-6, rc

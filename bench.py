@@ -7,6 +7,7 @@
     python bench.py --workload ffn_backward (the FFN-sublayer backward)
     python bench.py --workload sublayer_backward (the attention-sublayer backward)
     python bench.py --workload compact     (the pyramid compaction, HBM-bound)
+    python bench.py --workload vendor_gemm (hipBLASLt on the c3 layer-1 shapes, a reference)
     python bench.py --workload stack_backward (the whole-stack training backward)
     python bench.py --config c5            (the 12-layer stack with the token build)
     python bench.py --attn-phases          (adds the attention kernel's phase breakdown)
@@ -1035,6 +1036,53 @@ COMPACT_TEXT = ("c3 layer-2 compaction: 64 users x 1600 fp32 rows of 512, the la
                 "kept (values, offsets and source indices out)")
 
 
+def bench_vendor_gemm(args):
+    """A reference point, not the product path: the vendor GEMM (hipBLASLt,
+    through torch.matmul on bf16 operands, fp32 accumulation, no epilogue)
+    on the five product shapes of the c3 forward's first layer (M = 102,400
+    rows: W_dkv, W_uq, W_o, W1, W2). `value` is the FLOP-weighted rate over
+    the five; `products` gives each one's. The library's own rates for the
+    same launches come from its per-launch table (profiles/)."""
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    M, d, r, hd, dff = 102400, 512, 128, 512, 2048
+    shapes = [("down", r, d), ("q", hd, d), ("out", d, hd), ("ffn1", dff, d), ("ffn2", d, dff)]
+    g = torch.Generator(device="cuda").manual_seed(0)
+    prods, tot_f, tot_t = {}, 0.0, 0.0
+    for name, N, K in shapes:
+        A = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+        Bt = (torch.randn(K, N, device="cuda", generator=g) / K ** 0.5).to(torch.bfloat16)
+        C = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+        for _ in range(args.warmup):
+            torch.matmul(A, Bt, out=C)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(args.steps):
+            torch.matmul(A, Bt, out=C)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / args.steps
+        f = 2.0 * M * N * K
+        prods[name] = {"N": N, "K": K, "ms": round(ms, 4), "tflops": round(f / (ms / 1e3) / 1e12, 1)}
+        tot_f += f
+        tot_t += ms
+        del A, Bt, C
+    tf = tot_f / (tot_t / 1e3) / 1e12
+    rec = {"metric": "vendor GEMM TFLOP/s (hipBLASLt via torch.matmul) on the c3 layer-1 product shapes",
+           "value": round(tf, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(tot_t, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1))",
+           "config": {"workload": "c3 layer-1 product shapes, M=102400: W_dkv 512->128, W_uq 512->512, "
+                                  "W_o 512->512, W1 512->2048, W2 2048->512; one step = the five products"},
+           "roofline": {"bound": "mfma", "kernel": "vendor GEMM", "achieved": round(tf, 1),
+                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+           "cpu_baseline": None, "products": prods,
+           "note": "reference measurement of the vendor library; the library does not use it"}
+    print(json.dumps(rec))
+
+
 def bench_compact(args):
     import torch
     from oracle import llatte_oracle as O
@@ -1140,7 +1188,7 @@ def main():
                          "by target_aware_latent_amd.profsum traffic); by "
                          "default the c3 records under profiles/")
     ap.add_argument("--workload", default="stack", choices=["stack", "actions", "summaries", "backward", "ffn_backward",
-                             "sublayer_backward", "stack_backward", "compact"],
+                             "sublayer_backward", "stack_backward", "compact", "vendor_gemm"],
                     help="stack: the MLA forward (default); actions: the action "
                          "tokenization that builds the history tokens; summaries: the "
                          "LoRAMLP sequence summaries of the readout; backward: the attention-core "
@@ -1148,7 +1196,8 @@ def main():
                          "backward (GEMM gradients) of every layer; sublayer_backward: the "
                          "attention-sublayer backward of every layer; stack_backward: the "
                          "whole-stack training backward; compact: the pyramid compaction "
-                         "(HBM-bound)")
+                         "(HBM-bound); vendor_gemm: hipBLASLt on the c3 layer-1 product "
+                         "shapes, a reference point only")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
@@ -1175,6 +1224,9 @@ def main():
         return
     if args.workload == "compact":
         bench_compact(args)
+        return
+    if args.workload == "vendor_gemm":
+        bench_vendor_gemm(args)
         return
 
     import torch

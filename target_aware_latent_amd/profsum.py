@@ -2,6 +2,7 @@
 
     python -m target_aware_latent_amd.profsum stats KERNEL_STATS_CSV
     python -m target_aware_latent_amd.profsum phases BENCH_JSON_LINE_FILE
+    python -m target_aware_latent_amd.profsum layers KERNEL_TRACE_CSV   (c3 forward)
     python -m target_aware_latent_amd.profsum traffic --fetch FETCH_CSV \\
         --write WRITE_CSV --kernel attn_mfma_kernel --label attention_mfma \\
         --source target_aware_latent_amd/csrc/attention.hip [--out FILE]
@@ -163,6 +164,57 @@ def launches(path, first="plan_layer_kernel"):
              statistics.median(dur(p[j]) for p in passes)) for j in range(n)]
 
 
+def layers(path):
+    """Per-layer table of one c3 forward (B=64, L=1600, d=512, 8x64 heads,
+    r=128, pyramid 1600-800-400-200-100-50, 4-seed readout, no candidates)
+    from the median dispatch durations of `launches`. The dispatches of a
+    pass are: the plan and the query map, the layer-1 norm; per layer W_dkv,
+    W_uq, the attention, W_o, W1, W2; then the seeds' broadcast and the
+    readout's pre-norm, its six launches (W2 a split-K pair) and W_p (a
+    split-K pair). Rates are each launch's algorithmic FLOPs (2MNK; for the
+    attention the allowed pairs x 8 heads x 4r plus both absorptions) over
+    its median duration."""
+    rows = launches(path)
+    t = [r[3] for r in rows]
+    names = [r[1] for r in rows]
+    B, d, h, dk, r, dff = 64, 512, 8, 64, 128, 2048
+    shapes = [(1600, 1600), (1600, 800), (800, 400), (400, 200), (200, 100), (100, 50), (50, 4)]
+    att = [3 + 6 * l + 2 for l in range(6)] + [3 + 6 * 6 + 2 + 2]
+    if len(t) != 50 or any("attn_mfma_kernel" not in names[i] for i in att):
+        raise SystemExit("not the c3 forward's dispatch sequence")
+    out, idx, total, pre = [], 3, 0.0, []
+    for li, (K, n) in enumerate(shapes):
+        ro = li == 6
+        if ro:
+            pre = t[idx:idx + 2]
+            idx += 2
+        times = []
+        for j in range(6):
+            if ro and j == 5:
+                times.append(t[idx] + t[idx + 1])
+                idx += 2
+            else:
+                times.append(t[idx])
+                idx += 1
+        pairs = n * K if ro else n * K - n * (n - 1) // 2
+        fl = [2 * B * K * d * r, 2 * B * n * d * h * dk,
+              B * pairs * h * 4 * r + 2 * 2 * B * n * h * dk * r,
+              2 * B * n * h * dk * d, 2 * B * n * d * dff, 2 * B * n * dff * d]
+        rates = [f / (x * 1e-6) / 1e12 for f, x in zip(fl, times)]
+        total += sum(times)
+        lab = "readout" if ro else f"L{li + 1}"
+        out.append(f"{lab:<7}{K:>9}/{n:>6}          | " + " ".join(f"{x:6.1f}" for x in times[:2]) +
+                   f"  {times[2]:7.1f}  " + " ".join(f"{x:6.1f}" for x in times[3:]) +
+                   f" | {sum(times):8.1f} us")
+        out.append(" " * 9 + "TFLOP/s              | " + " ".join(f"{x:6.0f}" for x in rates[:2]) +
+                   f"  {rates[2]:7.0f}  " + " ".join(f"{x:6.0f}" for x in rates[3:]) + " |")
+    out.append(f"stack + readout layers: {total:.1f} us; plan {t[0] + t[1]:.1f} us, layer-1 norm "
+               f"{t[2]:.1f} us, readout broadcast {pre[0]:.1f} us and pre-norm {pre[1]:.1f} us, "
+               f"W_p {t[idx] + t[idx + 1]:.1f} us")
+    out.append(f"all launches of the pass: {sum(t):.1f} us")
+    return "\n".join(out)
+
+
 def phases(path):
     """The phase tables of a bench.py --attn-phases / --gemm-phases line."""
     with open(path) as f:
@@ -201,6 +253,8 @@ def main(argv=None):
     c.add_argument("--kernel", action="append", required=True)
     t = sub.add_parser("launches")
     t.add_argument("csv")
+    ly = sub.add_parser("layers")
+    ly.add_argument("csv")
     ph = sub.add_parser("phases")
     ph.add_argument("json")
     b = sub.add_parser("traffic")
@@ -217,6 +271,8 @@ def main(argv=None):
         print(stats(args.csv))
     elif args.cmd == "phases":
         print(phases(args.json))
+    elif args.cmd == "layers":
+        print(layers(args.csv))
     elif args.cmd == "launches":
         for j, name, grid, us in launches(args.csv):
             print(f"{j:4d} {us:9.1f} us  grid {grid:>9s}  {name[:100]}")

@@ -191,7 +191,27 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
   const int tid = lid_x();
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, l16 = lane & 15;
-  const int h0 = gid_y() * cfg.HG;
+  // Work item and head group from the workgroup's place in dispatch order:
+  // workgroups go to the eight XCDs in turn, so in each run of 8 x nhg
+  // workgroups the head groups of the same eight items sit eight apart, on
+  // one XCD and close in time, and the latent tiles one group stages are
+  // still in that XCD's L2 for the other. Items keep their (longest-first)
+  // order; a last run with fewer than eight items is laid out the same way.
+  const int nhg = (int)__builtin_amdgcn_readfirstlane(p.h / cfg.HG);
+  int item, hgrp;
+  {
+    const int lin = gid_x() + p.items_cap * gid_y();
+    const int full = (p.items_cap / 8) * 8;  // items in complete runs of eight
+    if (lin < full * nhg) {
+      item = (lin / (8 * nhg)) * 8 + lin % 8;
+      hgrp = (lin / 8) % nhg;
+    } else {
+      const int r = lin - full * nhg, tail = p.items_cap - full;
+      item = full + r % tail;
+      hgrp = r / tail;
+    }
+  }
+  const int h0 = hgrp * cfg.HG;
   // The item count and the work item come in one round trip of scalar
   // loads (constant address space; the workgroup index is below items_cap, so the item is in
   // bounds either way, and both were written by an earlier launch).
@@ -201,11 +221,11 @@ __global__ __launch_bounds__(64 * attn_waves(R), 2) void attn_mfma_kernel(AttnPa
   using cint = __attribute__((address_space(4))) const int;
   using ci32x4 = __attribute__((address_space(4))) const i32x4;
   const int nitems_raw = *(cint*)p.n_items;
-  const i32x4 it = ((ci32x4*)p.items)[gid_x()];
+  const i32x4 it = ((ci32x4*)p.items)[item];
   // the item is read here, with the count: one wait for both scalar loads
   // (the branch needs the count anyway), not a second round trip after it
   asm volatile("" ::"s"(it[0]), "s"(it[1]), "s"(it[2]), "s"(it[3]));
-  if (gid_x() >= min(nitems_raw, p.items_cap)) return;
+  if (item >= min(nitems_raw, p.items_cap)) return;
   constexpr int KD = DK / 32;
   constexpr int NRB_ = R / 16;
   constexpr int RBC = NRB_ * KD <= 16 ? NRB_ : 16 / KD;
